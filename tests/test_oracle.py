@@ -1,0 +1,272 @@
+"""Pins for the float64 CPU oracle.
+
+The pages print no formula, worked example or value for the mixer, so the
+oracle is pinned to facts fixed by the mathematics of the gated delta rule:
+special cases with a closed form, exact (bitwise) reductions, invariants, an
+exact rational computation on a tiny case, and the agreement of three
+independently written forms (token-by-token C, chunked C, dense NumPy).
+Several cases use dk != dv so that a transposed state or an operand applied
+on the wrong axis cannot pass.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _rand_case(B=2, T=37, H=3, dk=5, dv=7, kda=False, seed=0, s0=True, unit_k=True):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, T, H, dk))
+    k = r.standard_normal((B, T, H, dk))
+    if unit_k:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, T, H, dv))
+    ashape = (B, T, H, dk) if kda else (B, T, H)
+    alpha = 1.0 / (1.0 + np.exp(-(2.0 + 0.5 * r.standard_normal(ashape))))
+    beta = 1.0 / (1.0 + np.exp(-r.standard_normal((B, T, H))))
+    S0 = 0.3 * r.standard_normal((B, H, dk, dv)) if s0 else None
+    return q, k, v, alpha, beta, S0
+
+
+def _close(a, b, tol):
+    a, b = np.asarray(a), np.asarray(b)
+    scale = max(1.0, float(np.abs(b).max()) if b.size else 1.0)
+    err = float(np.abs(a - b).max()) if b.size else 0.0
+    assert err <= tol * scale, "max abs err %.3e > %.1e * %.3e" % (err, tol, scale)
+
+
+# --- F1: beta = 0, alpha = 1 leaves the state unchanged --------------------
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_identity_when_beta0_alpha1(kda):
+    q, k, v, alpha, beta, S0 = _rand_case(kda=kda, seed=1)
+    alpha = np.ones_like(alpha)
+    beta = np.zeros_like(beta)
+    o, sT = oracle.recurrent(q, k, v, alpha, beta, S0)
+    assert np.array_equal(sT, S0)  # bitwise
+    # o_t = S_0^T q_t, computed with a library contraction.
+    expect = np.einsum("bhij,bthi->bthj", S0, q)
+    _close(o, expect, 1e-14)
+    oc, sc = oracle.chunked(q, k, v, alpha, beta, S0, chunk=8)
+    _close(sc, S0, 1e-14)
+    _close(oc, expect, 1e-14)
+
+
+# --- F2: alpha = 1, beta = 1, unit k: the delta rule recalls v exactly -----
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_exact_recall(kda):
+    q, k, v, alpha, beta, S0 = _rand_case(kda=kda, seed=2, dk=6, dv=4)
+    alpha = np.ones_like(alpha)
+    beta = np.ones_like(beta)
+    # With q_t = k_t the output is S_t^T k_t, which must equal v_t.
+    o, _ = oracle.recurrent(k, k, v, alpha, beta, S0)
+    _close(o, v, 1e-13)
+
+
+# --- F3: alpha = 0 reduces every step to a single rank-one write -----------
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_zero_gate_is_rank_one(kda):
+    q, k, v, alpha, beta, S0 = _rand_case(kda=kda, seed=3, T=1)
+    alpha = np.zeros_like(alpha)
+    o, sT = oracle.recurrent(q, k, v, alpha, beta, S0)
+    expect = (beta[:, 0, :, None] * k[:, 0])[..., None] * v[:, 0][:, :, None, :]
+    assert np.array_equal(sT, expect)  # bitwise: a single write of beta k v^T
+    kq = (k[:, 0] * q[:, 0]).sum(-1)
+    _close(o[:, 0], (beta[:, 0] * kq)[..., None] * v[:, 0], 1e-14)
+
+
+def test_zero_gate_mid_sequence_forgets_history():
+    q, k, v, alpha, beta, S0 = _rand_case(seed=4, T=9)
+    alpha[:, 4] = 0.0
+    o_full, s_full = oracle.recurrent(q, k, v, alpha, beta, S0)
+    # After the zero gate, the state no longer depends on anything before it.
+    q2, k2, v2, a2, b2 = (x[:, 4:].copy() for x in (q, k, v, alpha, beta))
+    o_tail, s_tail = oracle.recurrent(q2, k2, v2, a2, b2, None)
+    _close(o_full[:, 4:], o_tail, 1e-14)
+    _close(s_full, s_tail, 1e-14)
+
+
+# --- F4: the chunked refactoring equals the definition ---------------------
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("chunk", [1, 2, 4, 8, 16, 64])
+@pytest.mark.parametrize("T", [1, 37, 64, 130])
+def test_chunked_equals_recurrent(kda, chunk, T):
+    q, k, v, alpha, beta, S0 = _rand_case(kda=kda, seed=5 + T, T=T, B=1, H=2)
+    if T > 10:
+        alpha[:, 10] = 0.0  # a zero gate inside a chunk must be legal
+    o1, s1 = oracle.recurrent(q, k, v, alpha, beta, S0, scale=0.7)
+    o2, s2 = oracle.chunked(q, k, v, alpha, beta, S0, scale=0.7, chunk=chunk)
+    _close(o2, o1, 1e-12)
+    _close(s2, s1, 1e-12)
+
+
+# --- F5: dense brute force equals the rank-one form ------------------------
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_brute_force_matches(kda):
+    q, k, v, alpha, beta, S0 = _rand_case(kda=kda, seed=6, B=1, T=8, H=2, dk=4, dv=3,
+                                          unit_k=False)
+    o1, s1 = oracle.recurrent(q, k, v, alpha, beta, S0, scale=1.3)
+    o2, s2 = oracle.brute(q, k, v, alpha, beta, S0, scale=1.3)
+    _close(o1, o2, 1e-13)
+    _close(s1, s2, 1e-13)
+
+
+def _exact_dense(q, k, v, alpha, beta):
+    """Exact rational arithmetic, dense matrices, one (b, h), zero S_0."""
+    T, dk = len(q), len(q[0])
+    dv = len(v[0])
+    S = [[Fraction(0)] * dv for _ in range(dk)]
+    outs = []
+    for t in range(T):
+        D = [[(alpha[t][i] if i == j else Fraction(0)) for j in range(dk)] for i in range(dk)]
+        E = [[(Fraction(1) if i == j else Fraction(0)) - beta[t] * k[t][i] * k[t][j]
+              for j in range(dk)] for i in range(dk)]
+        M = [[sum(E[i][m] * D[m][j] for m in range(dk)) for j in range(dk)] for i in range(dk)]
+        S = [[sum(M[i][m] * S[m][j] for m in range(dk)) + beta[t] * k[t][i] * v[t][j]
+              for j in range(dv)] for i in range(dk)]
+        outs.append([sum(S[i][j] * q[t][i] for i in range(dk)) for j in range(dv)])
+    return outs, S
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_exact_rational_tiny(kda):
+    # Dyadic inputs: exactly representable in float64, exact in Fraction.
+    r = np.random.default_rng(7)
+    T, dk, dv = 4, 3, 2
+    q = r.integers(-4, 5, (T, dk)) / 4.0
+    k = r.integers(-4, 5, (T, dk)) / 4.0
+    v = r.integers(-8, 9, (T, dv)) / 8.0
+    beta = r.integers(1, 8, T) / 8.0
+    alpha = (r.integers(1, 16, (T, dk)) / 16.0) if kda else (r.integers(1, 16, T) / 16.0)
+    F = lambda a: [[Fraction(x) for x in row] for row in a]
+    if kda:
+        al = F(alpha)
+    else:
+        al = [[Fraction(a)] * dk for a in alpha]
+    outs, S = _exact_dense(F(q), F(k), F(v), al, [Fraction(b) for b in beta])
+    o, sT = oracle.recurrent(q[None, :, None], k[None, :, None], v[None, :, None],
+                             alpha[None, :, None], beta[None, :, None])
+    _close(o[0, :, 0], np.array([[float(x) for x in row] for row in outs]), 1e-15)
+    _close(sT[0, 0], np.array([[float(x) for x in row] for row in S]), 1e-15)
+
+
+# --- F6: a channel gate that is constant across channels is the scalar gate
+
+def test_kda_with_constant_gate_equals_gdn():
+    q, k, v, alpha, beta, S0 = _rand_case(seed=8)
+    alpha_kda = np.repeat(alpha[..., None], q.shape[-1], axis=-1)
+    o1, s1 = oracle.recurrent(q, k, v, alpha, beta, S0)
+    o2, s2 = oracle.recurrent(q, k, v, alpha_kda, beta, S0)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+    o3, s3 = oracle.chunked(q, k, v, alpha_kda, beta, S0, chunk=16)
+    _close(o3, o1, 1e-12)
+    _close(s3, s1, 1e-12)
+
+
+# --- F7: splitting the sequence and stepping token by token ----------------
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_split_and_decode_steps(kda):
+    q, k, v, alpha, beta, S0 = _rand_case(kda=kda, seed=9, T=20)
+    o, s = oracle.recurrent(q, k, v, alpha, beta, S0)
+    o_a, s_a = oracle.recurrent(q[:, :7], k[:, :7], v[:, :7], alpha[:, :7], beta[:, :7], S0)
+    o_b, s_b = oracle.recurrent(q[:, 7:], k[:, 7:], v[:, 7:], alpha[:, 7:], beta[:, 7:], s_a)
+    assert np.array_equal(np.concatenate([o_a, o_b], axis=1), o)
+    assert np.array_equal(s_b, s)
+    st = S0.copy()
+    for t in range(q.shape[1]):
+        ot, st = oracle.decode_step(q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t], st)
+        assert np.array_equal(ot, o[:, t])
+    assert np.array_equal(st, s)
+
+
+# --- F8: value columns are independent -------------------------------------
+
+def test_value_columns_independent():
+    q, k, v, alpha, beta, S0 = _rand_case(seed=10, dv=9, kda=True)
+    o, s = oracle.recurrent(q, k, v, alpha, beta, S0)
+    cols = [1, 4, 8]
+    o2, s2 = oracle.recurrent(q, k, v[..., cols], alpha, beta, S0[..., cols])
+    _close(o2, o[..., cols], 1e-15)
+    _close(s2, s[..., cols], 1e-15)
+
+
+# --- F9: (S_0, v) -> (o, S_T) is linear -------------------------------------
+
+def test_linear_in_state_and_values():
+    q, k, v1, alpha, beta, S1 = _rand_case(seed=11, kda=True)
+    _, _, v2, _, _, S2 = _rand_case(seed=12, kda=True)
+    a, b = 0.75, -1.5
+    o1, s1 = oracle.recurrent(q, k, v1, alpha, beta, S1)
+    o2, s2 = oracle.recurrent(q, k, v2, alpha, beta, S2)
+    o3, s3 = oracle.recurrent(q, k, a * v1 + b * v2, alpha, beta, a * S1 + b * S2)
+    _close(o3, a * o1 + b * o2, 1e-13)
+    _close(s3, a * s1 + b * s2, 1e-13)
+
+
+# --- F10: scalar closed form at dk = dv = 1 --------------------------------
+
+def test_scalar_closed_form():
+    r = np.random.default_rng(13)
+    T = 25
+    q = r.standard_normal(T)
+    k = r.choice([-1.0, 1.0], T)
+    v = r.standard_normal(T)
+    alpha = r.uniform(0, 1, T)
+    beta = r.uniform(0, 1, T)
+    s, outs = 0.4, []
+    for t in range(T):
+        s = alpha[t] * (1 - beta[t]) * s + beta[t] * k[t] * v[t]
+        outs.append(q[t] * s)
+    o, sT = oracle.recurrent(q.reshape(1, T, 1, 1), k.reshape(1, T, 1, 1),
+                             v.reshape(1, T, 1, 1), alpha.reshape(1, T, 1),
+                             beta.reshape(1, T, 1), np.full((1, 1, 1, 1), 0.4))
+    _close(o.ravel(), np.array(outs), 1e-14)
+    _close(sT.ravel(), [s], 1e-14)
+
+
+# --- F11: contraction bound --------------------------------------------------
+
+def test_state_norm_bound():
+    q, k, v, alpha, beta, S0 = _rand_case(seed=14, kda=True, T=1, B=4, H=4, dk=8, dv=8)
+    _, sT = oracle.recurrent(q, k, v, alpha, beta, S0)
+    for b in range(4):
+        for h in range(4):
+            lhs = np.linalg.norm(sT[b, h], 2)
+            rhs = np.linalg.norm(S0[b, h], 2) + beta[b, 0, h] * np.linalg.norm(v[b, 0, h])
+            assert lhs <= rhs * (1 + 1e-12)
+
+
+# --- scale and threading -----------------------------------------------------
+
+def test_scale_is_a_pure_output_factor():
+    q, k, v, alpha, beta, S0 = _rand_case(seed=15)
+    o1, s1 = oracle.recurrent(q, k, v, alpha, beta, S0, scale=1.0)
+    o2, s2 = oracle.recurrent(q, k, v, alpha, beta, S0, scale=0.125)
+    assert np.array_equal(s1, s2)
+    _close(o2, 0.125 * o1, 1e-15)
+
+
+def test_thread_count_does_not_change_results():
+    q, k, v, alpha, beta, S0 = _rand_case(seed=16, B=3, H=5, kda=True)
+    a = oracle.recurrent(q, k, v, alpha, beta, S0, nthreads=1)
+    b = oracle.recurrent(q, k, v, alpha, beta, S0, nthreads=7)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    c = oracle.chunked(q, k, v, alpha, beta, S0, chunk=4, nthreads=1)
+    d = oracle.chunked(q, k, v, alpha, beta, S0, chunk=4, nthreads=6)
+    assert all(np.array_equal(x, y) for x, y in zip(c, d))
+
+
+def test_empty_sequence_copies_state():
+    q, k, v, alpha, beta, S0 = _rand_case(seed=17, T=0)
+    o, s = oracle.recurrent(q, k, v, alpha, beta, S0)
+    assert o.shape[1] == 0 and np.array_equal(s, S0)
+    o, s = oracle.chunked(q, k, v, alpha, beta, S0)
+    assert np.array_equal(s, S0)
