@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Throughput of the gated delta-rule mixer on one MI355X.
+
+Headline (the JSON line's ``value``): decode state-stream bandwidth of the GDN
+decode step, B=64 sequences x H=32 heads x dk=dv=128, over 48 independent
+layer states (6 GiB of fp32 state, far beyond the on-chip caches).  One
+"step" is one decoded token for every sequence: 48 back-to-back
+``gdr_decode_step`` calls on one stream, each streaming its 128 MiB state
+in and out.  ``value`` = algorithmic bytes moved per step x steps / elapsed.
+
+Also measured in the same run (under ``workloads``): KDA decode (B=256,
+20 in-place steps), GDN chunked prefill (B=4, T=8192) and KDA chunked
+prefill (B=1, T=32768), each with its roofline fractions.
+
+Roofline: algorithmic bytes (or flops) per launch divided by the average
+launch duration, measured with HIP events recorded around every launch on the
+stream the kernel runs on.  ``cpu_baseline`` times the float64 CPU oracle on a
+bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+       [--no-cpu-baseline] [--launches N]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode state-stream GB/s vs HBM peak; chunked-prefill tokens/s vs MFMA peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector peak
+CHUNK = 64
+
+
+def decode_bytes_per_head(gate, dk, dv, elt=2):
+    """Read + write the fp32 state, read q, k, v, write o, read the gates."""
+    return 8 * dk * dv + elt * (2 * dk + 2 * dv) + 4 + (4 * dk if gate == "kda" else 4)
+
+
+def decode_flops_per_head(dk, dv):
+    return 7 * dk * dv
+
+
+def prefill_bytes(gate, B, T, H, dk, dv, has_s0, elt=2):
+    per_tok = elt * (2 * dk + 2 * dv) + 4 + (4 * dk if gate == "kda" else 4)
+    return B * T * H * per_tok + B * H * 4 * dk * dv * (2 if has_s0 else 1)
+
+
+def prefill_flops(B, T, H, dk, dv):
+    """Matrix-core flops of the chunked algorithm per token-head (C = 64): the
+    intra-chunk products (A, P, W, U-tilde) 2C(3dk + 2dv) plus the inter-chunk
+    state products (W S, Qhat S, Ktil^T U) 6 dk dv."""
+    return B * T * H * (2 * CHUNK * (3 * dk + 2 * dv) + 6 * dk * dv)
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_08_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, sha):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on this exact kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        e = d.get(kernel_key)
+        if e and e.get("source_sha256") == sha:
+            return e.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+class LaunchTimer:
+    """HIP events around every launch on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __call__(self, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.append((a, b))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else 0.0
+
+
+def timed_region(torch, steps, body):
+    """Barrier + synchronize on both sides of exactly `steps` calls to body()."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        body()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def bench_gdn_decode(torch, gdr, synth, steps, warmup, want_cpu):
+    w = synth.WORKLOADS["gdn_decode_b64_h32_d128"]
+    B, H, dk, dv, L = w.B, w.H, w.dk, w.dv, w.layers
+    g = torch.Generator(device="cuda")
+    layers = []
+    for layer in range(L):
+        inp = synth.make_inputs(w, layer=layer, s0="zero")
+        g.manual_seed(1000 + layer)
+        state = torch.randn(B, H, dk, dv, device="cuda", generator=g) * 0.02
+        d = {k: torch.from_numpy(np.ascontiguousarray(inp[k][:, 0])).to(
+            torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()
+            for k in ("q", "k", "v", "alpha", "beta")}
+        d["state"] = state
+        d["o"] = torch.empty(B, H, dv, device="cuda", dtype=torch.bfloat16)
+        layers.append(d)
+
+    def step(timer=None):
+        for d in layers:
+            call = lambda d=d: gdr.gdr_decode_step("gdn", d["q"], d["k"], d["v"], d["alpha"],
+                                                    d["beta"], d["state"], d["o"])
+            if timer is None:
+                call()
+            else:
+                timer(call)
+
+    for _ in range(warmup):
+        step()
+    elapsed = timed_region(torch, steps, step)
+    timer = LaunchTimer(torch)
+    for _ in range(max(1, min(steps, 4))):
+        step(timer)
+    launch_ms = timer.mean_ms()
+    per_launch = B * H * decode_bytes_per_head("gdn", dk, dv)
+    step_bytes = per_launch * L
+    res = {
+        "elapsed_s": elapsed,
+        "ms_per_step": 1e3 * elapsed / steps,
+        "gbs": step_bytes * steps / elapsed / 1e9,
+        "tokens_per_s": B * steps / elapsed,
+        "launch_ms": launch_ms,
+        "bytes_per_launch": per_launch,
+    }
+    if want_cpu:
+        res["cpu"] = cpu_baseline_decode(torch, synth, w, layers)
+    return res
+
+
+def cpu_baseline_decode(torch, synth, w, layers, budget_s=12.0):
+    """The float64 oracle on whole layers of the same workload until ~budget_s."""
+    import oracle
+    nt = oracle.default_threads()
+    done, t_total = 0, 0.0
+    for layer, d in enumerate(layers):
+        inp = synth.make_inputs(w, layer=layer, s0="zero")
+        s0 = d["state"].double().cpu().numpy()
+        x = {k: inp[k][:, 0] for k in ("q", "k", "v", "alpha", "beta")}
+        t0 = time.perf_counter()
+        oracle.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], s0, nthreads=nt)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    per_layer = w.B * w.H * decode_bytes_per_head("gdn", w.dk, w.dv)
+    return {
+        "value": round(per_layer * done / t_total / 1e9, 3),
+        "unit": "GB/s",
+        "cores": nt,
+        "kind": "oracle",
+        "sample": "%d of %d layers, one decode step each (B=%d, H=%d, d=%d), float64" % (
+            done, w.layers, w.B, w.H, w.dk),
+        "seconds": round(t_total, 3),
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def bench_kda_decode(torch, gdr, synth, steps, warmup):
+    w = synth.WORKLOADS["kda_decode_b256_h32_d128"]
+    B, H, dk, dv = w.B, w.H, w.dk, w.dv
+    inp = synth.make_inputs(w, s0="zero")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2000)
+    state = torch.randn(B, H, dk, dv, device="cuda", generator=g) * 0.02
+    d = {k: torch.from_numpy(np.ascontiguousarray(inp[k][:, 0])).to(
+        torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()
+        for k in ("q", "k", "v", "alpha", "beta")}
+    o = torch.empty(B, H, dv, device="cuda", dtype=torch.bfloat16)
+    call = lambda: gdr.gdr_decode_step("kda", d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                       state, o)
+    for _ in range(warmup):
+        call()
+    n = max(steps, 20)
+    elapsed = timed_region(torch, n, call)
+    timer = LaunchTimer(torch)
+    for _ in range(n):
+        timer(call)
+    launch_ms = timer.mean_ms()
+    per_launch = B * H * decode_bytes_per_head("kda", dk, dv)
+    return {"workload": w.name, "steps": n, "ms_per_step": 1e3 * elapsed / n,
+            "gbs": per_launch * n / elapsed / 1e9, "tokens_per_s": B * n / elapsed,
+            "roofline": roofline_hbm(per_launch, launch_ms)}
+
+
+def bench_prefill(torch, gdr, synth, name, steps, warmup):
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    d = {k: (None if v is None else torch.from_numpy(v).to(
+        torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()) for k, v in inp.items()}
+    del inp
+    s_out = torch.empty(B, H, dk, dv, device="cuda")
+    o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.bfloat16)
+    call = lambda: gdr.gdr_chunk_prefill(w.gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                         d["s0"], s_out, o)
+    for _ in range(warmup):
+        call()
+    elapsed = timed_region(torch, steps, call)
+    timer = LaunchTimer(torch)
+    for _ in range(steps):
+        timer(call)
+    launch_ms = timer.mean_ms()
+    nbytes = prefill_bytes(w.gate, B, T, H, dk, dv, d["s0"] is not None)
+    flops = prefill_flops(B, T, H, dk, dv)
+    sec = launch_ms / 1e3
+    return {
+        "workload": name, "steps": steps, "ms_per_step": 1e3 * elapsed / steps,
+        "tokens_per_s": B * T * steps / elapsed,
+        "launch_ms": launch_ms,
+        "roofline": {
+            "bound": "hbm", "achieved": round(nbytes / sec / 1e9, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("prefill_" + w.gate, src_hash("prefill_bf16.hip")),
+        },
+        "mfma": {"achieved": round(flops / sec / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "algorithmic_flops": flops},
+        "algorithmic_bytes": nbytes,
+    }
+
+
+def roofline_hbm(per_launch_bytes, launch_ms, traffic=None):
+    a = per_launch_bytes / (launch_ms / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": round(a, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default=None,
+                    help="gdn_decode | kda_decode | gdn_prefill | kda_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_08_amd as gdr
+    import synth
+    if not os.path.exists(gdr.library_path()):
+        from gated_delta_rule_08_amd import build
+        build.build()
+    gdr.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+
+    only = args.only
+    extra = {}
+    head = None
+    if only in (None, "gdn_decode"):
+        head = bench_gdn_decode(torch, gdr, synth, args.steps, args.warmup,
+                                want_cpu=(only is None and not args.no_cpu_baseline))
+    if only in (None, "kda_decode"):
+        extra["kda_decode_b256_h32_d128"] = bench_kda_decode(torch, gdr, synth, args.steps,
+                                                             args.warmup)
+    if only in (None, "gdn_prefill"):
+        extra["gdn_prefill_b4_t8192_h32_d128"] = bench_prefill(
+            torch, gdr, synth, "gdn_prefill_b4_t8192_h32_d128", max(5, args.steps // 2), 2)
+    if only in (None, "kda_prefill"):
+        extra["kda_prefill_b1_t32768_h32_d128"] = bench_prefill(
+            torch, gdr, synth, "kda_prefill_b1_t32768_h32_d128", max(5, args.steps // 2), 2)
+
+    if head is None:
+        print(json.dumps({"workloads": extra}))
+        return
+    line = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gdn_decode_b64_h32_d128", "gate": "gdn", "B": 64, "H": 32,
+                   "dk": 128, "dv": 128, "layers": 48, "qkv": "bf16", "state": "fp32",
+                   "tokens_per_s": round(head["tokens_per_s"], 1)},
+        "roofline": roofline_hbm(head["bytes_per_launch"], head["launch_ms"],
+                                 load_traffic("decode_gdn", src_hash("decode.hip"))),
+    }
+    if "cpu" in head:
+        line["cpu_baseline"] = head["cpu"]
+    if extra:
+        line["workloads"] = extra
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

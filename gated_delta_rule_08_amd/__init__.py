@@ -1,0 +1,166 @@
+"""Python binding of libgdr, the gated delta-rule mixer for MI355X (gfx950).
+
+Argument marshalling only: each function checks that the torch tensors it is
+given agree with one another (device, dtype, contiguity, shapes), passes their
+device pointers and the current HIP stream to the C ABI declared in
+``include/gdr.h``, and raises :class:`GdrError` on a non-zero status.  All
+arithmetic runs in the library's HIP kernels.  If ``libgdr.so`` has not been
+built, importing works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "GdrError", "GATES", "library_path", "load_library", "gdr_decode_step",
+    "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
+    "gdr_abi_version", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+GATES = {"gdn": 0, "kda": 1}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_chunk_prefill",
+                    "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
+                    "gdr_abi_version")
+CHUNK = 64
+_lib = None
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("GDR_LIBRARY", os.path.join(_PKG, "libgdr.so"))
+
+
+def load_library():
+    """Load libgdr.so and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise GdrError(-100, "libgdr.so is not built (%s); run "
+                       "`python -m gated_delta_rule_08_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.gdr_decode_step.argtypes = [i, i, i, i, i, i, f] + [vp] * 8
+    lib.gdr_decode_step.restype = i
+    lib.gdr_chunk_prefill.argtypes = [i] * 8 + [f] + [vp] * 9 + [ctypes.c_size_t, vp]
+    lib.gdr_chunk_prefill.restype = i
+    lib.gdr_chunk_prefill_workspace_bytes.argtypes = [i] * 8
+    lib.gdr_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdr_status_string.argtypes = [i]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_abi_version.argtypes = []
+    lib.gdr_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def gdr_status_string(status: int) -> str:
+    return load_library().gdr_status_string(int(status)).decode()
+
+
+def gdr_abi_version() -> int:
+    return load_library().gdr_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise GdrError(status, gdr_status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _same_device(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+
+
+def gdr_decode_step(gate: str, q, k, v, alpha, beta, state, o, scale: float = 1.0,
+                    stream=None) -> None:
+    """One decode step; ``state`` [B,H,dk,dv] fp32 is updated in place.
+
+    q, k [B,H,dk] and v, o [B,H,dv] share a dtype (fp32 or bf16); alpha is
+    [B,H] (gate "gdn") or [B,H,dk] (gate "kda"); beta [B,H]; fp32 gates.
+    """
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, H, dv) or o.shape != (B, H, dv):
+        raise ValueError("q, k, v, o shapes disagree")
+    if alpha.shape != ((B, H, dk) if gate == "kda" else (B, H)) or beta.shape != (B, H):
+        raise ValueError("alpha / beta shapes disagree with the gate mode")
+    if state.shape != (B, H, dk, dv) or state.dtype != torch.float32:
+        raise ValueError("state must be fp32 [B,H,dk,dv]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, o must share dtype fp32 or bf16")
+    if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise ValueError("alpha and beta must be fp32")
+    _same_device(q, k, v, alpha, beta, state, o)
+    _check(load_library().gdr_decode_step(
+        GATES[gate], _DTYPES[q.dtype], B, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _stream(stream)))
+
+
+def gdr_chunk_prefill_workspace_bytes(gate: str, dtype, B: int, T: int, H: int, dk: int,
+                                      dv: int, chunk: int = CHUNK) -> int:
+    return int(load_library().gdr_chunk_prefill_workspace_bytes(
+        GATES[gate], _DTYPES[dtype], B, T, H, dk, dv, chunk))
+
+
+def gdr_chunk_prefill(gate: str, q, k, v, alpha, beta, state_in, state_out, o,
+                      scale: float = 1.0, workspace=None, chunk: int = CHUNK,
+                      stream=None) -> None:
+    """Chunked prefill; writes o [B,T,H,dv] and state_out [B,H,dk,dv] (fp32).
+
+    q, k [B,T,H,dk] and v, o [B,T,H,dv] share a dtype; alpha [B,T,H] (gdn) or
+    [B,T,H,dk] (kda) and beta [B,T,H] are fp32; state_in may be None.
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or o.shape != (B, T, H, dv):
+        raise ValueError("q, k, v, o shapes disagree")
+    if alpha.shape != ((B, T, H, dk) if gate == "kda" else (B, T, H)) or beta.shape != (B, T, H):
+        raise ValueError("alpha / beta shapes disagree with the gate mode")
+    for s in (state_in, state_out):
+        if s is not None and (s.shape != (B, H, dk, dv) or s.dtype != torch.float32):
+            raise ValueError("states must be fp32 [B,H,dk,dv]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, o must share dtype fp32 or bf16")
+    if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise ValueError("alpha and beta must be fp32")
+    _same_device(q, k, v, alpha, beta, state_in, state_out, o, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().gdr_chunk_prefill(
+        GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k),
+        _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o),
+        _ptr(workspace), ws_bytes, _stream(stream)))

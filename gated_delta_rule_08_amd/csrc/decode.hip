@@ -1,0 +1,184 @@
+// Decode step of the gated delta rule: one token per head, state streamed
+// through registers once (read 4*dk*dv bytes, write 4*dk*dv bytes).
+//
+// Per head (b, h), with a = alpha (scalar for GDN, vector over the key axis
+// for KDA), the step S_t = (I - beta k k^T) D S + beta k v^T, o = S_t^T q
+// ("Super Apriel: One Checkpoint, Many Speeds", §2.A: GDN and KDA are
+// recurrent mixers with scalar and channel-wise gates) is evaluated in one
+// pass over the state as
+//     S' = D S;   p = S'^T k;   r = S'^T q;   e = v - p
+//     S  = S' + beta k e^T;     o = scale * (r + beta (k . q) e)
+// (o = S^T q expanded, so no second pass over the new state is needed).
+//
+// Mapping.  The state of one head is dk rows of dv fp32.  Each wavefront owns
+// a slice of up to 32 value columns over all dk rows: a lane holds one float4
+// (4 columns) of every (64/LPR)-th row, LPR = columns/4 lanes covering a row
+// segment, so one wavefront load instruction fetches 64/LPR full 128-byte
+// row segments.  The dk-reductions of p, r and k.q are in-lane sums over the
+// lane's rows followed by a butterfly over the lanes that share columns.  No
+// LDS, no barriers: waves are independent.  With dv = 128 the four waves of a
+// workgroup cover the four column slices of one head, so a workgroup streams
+// one contiguous 64 KiB state.
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+template <typename InT> struct Vec4Out;
+template <> struct Vec4Out<float> {
+    __device__ __forceinline__ static void store(float* p, float a, float b, float c, float d) {
+        *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+    }
+};
+template <> struct Vec4Out<bf16_t> {
+    __device__ __forceinline__ static void store(bf16_t* p, float a, float b, float c, float d) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+        w.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+        *reinterpret_cast<uint2*>(p) = w;
+    }
+};
+
+template <typename InT>
+__device__ __forceinline__ float4 load4(const InT* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
+template <int DK, int DV, typename InT, bool KDA>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    int n_units, float scale, const InT* __restrict__ q, const InT* __restrict__ k,
+    const InT* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
+    float* __restrict__ state, InT* __restrict__ o) {
+    constexpr int COLS = DV < 32 ? DV : 32;  // value columns per wavefront
+    constexpr int NSLICE = DV / COLS;
+    constexpr int LPR = COLS / 4;            // lanes per row segment
+    constexpr int RPI = 64 / LPR;            // rows per load instruction
+    constexpr int NI = DK / RPI;             // rows per lane
+    static_assert(NI >= 1 && NI * RPI == DK, "head size does not tile the wavefront");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int unit = wave / NSLICE;
+    if (unit >= n_units) return;  // no barriers below: whole waves retire
+    const int slice = wave - unit * NSLICE;
+    const int rg = lane / LPR;
+    const int col = slice * COLS + (lane % LPR) * 4;
+
+    float* S = state + static_cast<size_t>(unit) * DK * DV + col;
+    float4 s[NI];
+#pragma unroll
+    for (int m = 0; m < NI; ++m)
+        s[m] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(m * RPI + rg) * DV);
+
+    const InT* qu = q + static_cast<size_t>(unit) * DK;
+    const InT* ku = k + static_cast<size_t>(unit) * DK;
+    float qv[NI], kv[NI];
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        qv[m] = Elem<InT>::load(qu + m * RPI + rg);
+        kv[m] = Elem<InT>::load(ku + m * RPI + rg);
+    }
+    float av[KDA ? NI : 1];
+    if constexpr (KDA) {
+#pragma unroll
+        for (int m = 0; m < NI; ++m) av[m] = alpha[static_cast<size_t>(unit) * DK + m * RPI + rg];
+    } else {
+        av[0] = alpha[unit];
+    }
+    const float b = beta[unit];
+    const float4 vv = load4<InT>(v + static_cast<size_t>(unit) * DV + col);
+
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        const float a = KDA ? av[m] : av[0];
+        s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
+        p0 += kv[m] * s[m].x; p1 += kv[m] * s[m].y; p2 += kv[m] * s[m].z; p3 += kv[m] * s[m].w;
+        r0 += qv[m] * s[m].x; r1 += qv[m] * s[m].y; r2 += qv[m] * s[m].z; r3 += qv[m] * s[m].w;
+        kq += kv[m] * qv[m];
+    }
+    // Butterfly over the lanes that hold the same columns (lane bits >= log2(LPR)).
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+        p0 += __shfl_xor(p0, off); p1 += __shfl_xor(p1, off);
+        p2 += __shfl_xor(p2, off); p3 += __shfl_xor(p3, off);
+        r0 += __shfl_xor(r0, off); r1 += __shfl_xor(r1, off);
+        r2 += __shfl_xor(r2, off); r3 += __shfl_xor(r3, off);
+        kq += __shfl_xor(kq, off);
+    }
+    const float e0 = vv.x - p0, e1 = vv.y - p1, e2 = vv.z - p2, e3 = vv.w - p3;
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        const float bk = b * kv[m];
+        s[m].x += bk * e0; s[m].y += bk * e1; s[m].z += bk * e2; s[m].w += bk * e3;
+        *reinterpret_cast<float4*>(S + static_cast<size_t>(m * RPI + rg) * DV) = s[m];
+    }
+    if (rg == 0) {
+        const float bkq = b * kq;
+        Vec4Out<InT>::store(o + static_cast<size_t>(unit) * DV + col,
+                            scale * (r0 + bkq * e0), scale * (r1 + bkq * e1),
+                            scale * (r2 + bkq * e2), scale * (r3 + bkq * e3));
+    }
+}
+
+template <int DK, int DV, typename InT, bool KDA>
+hipError_t launch(int n_units, float scale, const void* q, const void* k, const void* v,
+                  const float* alpha, const float* beta, float* state, void* o, hipStream_t s) {
+    constexpr int COLS = DV < 32 ? DV : 32;
+    const long long waves = static_cast<long long>(n_units) * (DV / COLS);
+    const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, InT, KDA>), dim3(blocks), dim3(256), 0, s,
+                       n_units, scale, static_cast<const InT*>(q), static_cast<const InT*>(k),
+                       static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o));
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t dispatch_type(int kda, int dtype, int n, float scale, const void* q, const void* k,
+                         const void* v, const float* alpha, const float* beta, float* state,
+                         void* o, hipStream_t s) {
+    if (dtype == GDR_DTYPE_BF16) {
+        return kda ? launch<DK, DV, bf16_t, true>(n, scale, q, k, v, alpha, beta, state, o, s)
+                   : launch<DK, DV, bf16_t, false>(n, scale, q, k, v, alpha, beta, state, o, s);
+    }
+    return kda ? launch<DK, DV, float, true>(n, scale, q, k, v, alpha, beta, state, o, s)
+               : launch<DK, DV, float, false>(n, scale, q, k, v, alpha, beta, state, o, s);
+}
+
+template <int DK>
+hipError_t dispatch_dv(int kda, int dtype, int dv, int n, float scale, const void* q,
+                       const void* k, const void* v, const float* alpha, const float* beta,
+                       float* state, void* o, hipStream_t s) {
+    switch (dv) {
+        case 16: return dispatch_type<DK, 16>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s);
+        case 32: return dispatch_type<DK, 32>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s);
+        case 64: return dispatch_type<DK, 64>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s);
+        default: return dispatch_type<DK, 128>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float scale,
+                         const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, float* state, void* o, hipStream_t s) {
+    const int n = B * H;
+    switch (dk) {
+        case 16: return dispatch_dv<16>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
+        case 32: return dispatch_dv<32>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
+        case 64: return dispatch_dv<64>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
+        default: return dispatch_dv<128>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
+    }
+}
+
+}  // namespace gdr

@@ -1,0 +1,148 @@
+// C ABI of libgdr: argument validation and dispatch.  Every check runs before
+// the first HIP call, so invalid calls never touch the device.
+#include <limits.h>
+#include <stdint.h>
+
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+__global__ __launch_bounds__(256) void state_copy_kernel(const float4* __restrict__ in,
+                                                         float4* __restrict__ out, size_t n4) {
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+         i += static_cast<size_t>(gridDim.x) * 256)
+        out[i] = in ? in[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+}  // namespace
+
+hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s) {
+    if (state_in == state_out || n == 0) return hipSuccess;
+    const size_t n4 = n / 4;  // n = B*H*dk*dv is a multiple of 256
+    const size_t want = (n4 + 255) / 256;
+    const unsigned blocks = static_cast<unsigned>(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(state_copy_kernel, dim3(blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(state_in),
+                       reinterpret_cast<float4*>(state_out), n4);
+    return hipGetLastError();
+}
+
+}  // namespace gdr
+
+namespace {
+
+inline bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Largest element count of any tensor must fit comfortably in size_t and
+// every grid dimension in an int.
+inline bool sizes_ok(long long B, long long T, long long H, long long dk, long long dv) {
+    const long long lim = 1LL << 40;
+    if (B * H > INT_MAX / 8) return false;
+    if (B * H * dk * dv > lim) return false;
+    if (B * T > lim / (H > 0 ? H : 1)) return false;
+    if (B * T * H > lim / 128) return false;
+    return true;
+}
+
+int check_enums(int gate, int dtype) {
+    if (gate != GDR_GATE_GDN && gate != GDR_GATE_KDA) return GDR_ERR_BAD_ENUM;
+    if (dtype != GDR_DTYPE_F32 && dtype != GDR_DTYPE_BF16) return GDR_ERR_BAD_ENUM;
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char* gdr_status_string(int status) {
+    switch (status) {
+        case GDR_OK: return "GDR_OK: success";
+        case GDR_ERR_NULL_PTR: return "GDR_ERR_NULL_PTR: a required pointer is NULL";
+        case GDR_ERR_BAD_SHAPE: return "GDR_ERR_BAD_SHAPE: a size is negative or too large";
+        case GDR_ERR_UNSUPPORTED:
+            return "GDR_ERR_UNSUPPORTED: dk and dv must be 16, 32, 64 or 128 and chunk must be 64";
+        case GDR_ERR_MISALIGNED:
+            return "GDR_ERR_MISALIGNED: tensors need 16-byte alignment (beta and GDN alpha 4-byte)";
+        case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace missing or too small";
+        case GDR_ERR_BAD_ENUM: return "GDR_ERR_BAD_ENUM: unknown gate mode or dtype";
+        case GDR_ERR_HIP: return "GDR_ERR_HIP: the HIP runtime rejected a launch";
+        case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: state_in and state_out partially overlap";
+        default: return "unknown gdr status";
+    }
+}
+
+int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float scale,
+                    const void* q, const void* k, const void* v, const float* alpha,
+                    const float* beta, float* state, void* o, void* stream) {
+    int st = check_enums(gate, dtype);
+    if (st != GDR_OK) return st;
+    if (B < 0 || H < 0) return GDR_ERR_BAD_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDR_ERR_UNSUPPORTED;
+    if (!sizes_ok(B, 1, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
+    if (B == 0 || H == 0) return GDR_OK;
+    if (!q || !k || !v || !alpha || !beta || !state || !o) return GDR_ERR_NULL_PTR;
+    const int kda = gate == GDR_GATE_KDA;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(state, 16) || !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4))
+        return GDR_ERR_MISALIGNED;
+    hipError_t e = gdr::launch_decode(kda, dtype, B, H, dk, dv, scale, q, k, v, alpha, beta,
+                                      state, o, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+size_t gdr_chunk_prefill_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
+                                         int dv, int chunk) {
+    (void)gate; (void)dtype; (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)chunk;
+    return 0;  // every prefill kernel keeps its intermediates on chip
+}
+
+int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                      float scale, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const float* state_in,
+                      float* state_out, void* o, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    int st = check_enums(gate, dtype);
+    if (st != GDR_OK) return st;
+    if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
+    if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
+    const size_t need = gdr_chunk_prefill_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
+    if (B == 0 || H == 0) return GDR_OK;
+    if (!state_out) return GDR_ERR_NULL_PTR;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !o)) return GDR_ERR_NULL_PTR;
+    const int kda = gate == GDR_GATE_KDA;
+    if (!aligned(state_out, 16) || (state_in && !aligned(state_in, 16))) return GDR_ERR_MISALIGNED;
+    if (T > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+                  !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4)))
+        return GDR_ERR_MISALIGNED;
+    const size_t n_state = static_cast<size_t>(B) * H * dk * dv;
+    if (state_in && state_in != state_out) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(state_in);
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(state_out);
+        const uintptr_t len = n_state * sizeof(float);
+        if (a0 < b0 + len && b0 < a0 + len) return GDR_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (T == 0) {
+        e = gdr::launch_state_copy(state_in, state_out, n_state, s);
+    } else if (dtype == GDR_DTYPE_F32) {
+        e = gdr::launch_prefill_f32(kda, B, T, H, dk, dv, scale, static_cast<const float*>(q),
+                                    static_cast<const float*>(k), static_cast<const float*>(v),
+                                    alpha, beta, state_in, state_out, static_cast<float*>(o), s);
+    } else {
+        e = gdr::launch_prefill_bf16(kda, B, T, H, dk, dv, scale,
+                                     static_cast<const gdr::bf16_t*>(q),
+                                     static_cast<const gdr::bf16_t*>(k),
+                                     static_cast<const gdr::bf16_t*>(v), alpha, beta, state_in,
+                                     state_out, static_cast<gdr::bf16_t*>(o), s);
+    }
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal declarations shared by the translation units of libgdr.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr.h"
+
+namespace gdr {
+
+// bfloat16 is carried as its 16-bit pattern.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round to nearest even; NaN is kept a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float* p) { return *p; }
+    __device__ __forceinline__ static void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<bf16_t> {
+    __device__ __forceinline__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+    __device__ __forceinline__ static void store(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// Launchers, one per kernel family.  They assume validated arguments and
+// return the hipError_t of the launch.
+hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float scale,
+                         const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, float* state, void* o, hipStream_t s);
+
+hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, float scale,
+                              const float* q, const float* k, const float* v,
+                              const float* alpha, const float* beta, const float* state_in,
+                              float* state_out, float* o, hipStream_t s);
+
+hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
+                               const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                               const float* alpha, const float* beta, const float* state_in,
+                               float* state_out, bf16_t* o, hipStream_t s);
+
+// state_out <- state_in (or zeros when state_in is NULL), n floats.
+hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
+
+}  // namespace gdr

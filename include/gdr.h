@@ -1,0 +1,134 @@
+/*
+ * gdr.h -- C ABI of the gated delta-rule token mixer for AMD MI355X (gfx950).
+ *
+ * The mixer.  "Super Apriel: One Checkpoint, Many Speeds"
+ * (gist.science/paper/2604.19877), §2.A "The Supernet Architecture", lists
+ * two recurrent token mixers with a fixed-size state and O(n) time: Gated
+ * DeltaNet (GDN), a delta rule with a scalar gate, and Kimi Delta Attention
+ * (KDA), delta attention with a channel-wise gate; §2.D "Inference &
+ * Serving" runs them in decode (including an all-GDN speculative draft).
+ * The pages print no update rule; this library computes the gated delta rule
+ * in its usual form, per batch entry b and head h, with an fp32 state
+ * S in R^{dk x dv} (row i = key channel, column j = value channel):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) D_t S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * D_t = alpha_t I for GDN (one scalar gate per token and head) and
+ * D_t = diag(alpha_t) for KDA (alpha_t in R^dk, acting on the key axis).
+ * The gate is applied before the delta correction; the output reads the
+ * post-update state.  alpha and beta are given in linear space (already
+ * passed through their activations); alpha is expected in [0, 1].
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer to a dense, row-major buffer
+ *    owned by the caller.  The library allocates and frees nothing and keeps
+ *    no mutable global state; concurrent calls on different streams are safe
+ *    as long as their output buffers do not overlap.
+ *  - q, k, v, o share one element type, selected by `dtype`: GDR_DTYPE_F32
+ *    (IEEE fp32) or GDR_DTYPE_BF16 (bfloat16, outputs rounded to nearest
+ *    even).  alpha, beta and the state are always fp32.
+ *  - Supported head sizes: dk, dv in {16, 32, 64, 128}.  The chunk size of
+ *    the prefill is 64.
+ *  - Alignment: q, k, v, o, the state buffers and KDA alpha must be 16-byte
+ *    aligned; beta and GDN alpha 4-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it; no call synchronises the host.
+ *  - Arguments are validated completely before any HIP call, so an invalid
+ *    call returns an error without touching the device.  Faults inside a
+ *    kernel surface at the caller's next synchronisation; launch failures
+ *    return GDR_ERR_HIP.
+ *  - Zero-sized problems (B == 0 or H == 0) are no-ops that return GDR_OK;
+ *    their pointers may then be NULL.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+/* Gate mode: scalar gate (Gated DeltaNet) or channel-wise gate (Kimi Delta
+ * Attention), the two mixers of the pages' §2.A. */
+typedef enum { GDR_GATE_GDN = 0, GDR_GATE_KDA = 1 } gdr_gate_t;
+
+/* Element type of q, k, v and o. */
+typedef enum { GDR_DTYPE_F32 = 0, GDR_DTYPE_BF16 = 1 } gdr_dtype_t;
+
+/* Status codes.  0 is success; errors are negative. */
+enum {
+    GDR_OK = 0,
+    GDR_ERR_NULL_PTR = -1,    /* a required pointer is NULL                 */
+    GDR_ERR_BAD_SHAPE = -2,   /* a size is negative or overflows            */
+    GDR_ERR_UNSUPPORTED = -3, /* dk, dv or chunk outside the supported set  */
+    GDR_ERR_MISALIGNED = -4,  /* a pointer violates the alignment rule      */
+    GDR_ERR_WORKSPACE = -5,   /* workspace missing or too small             */
+    GDR_ERR_BAD_ENUM = -6,    /* gate or dtype is not a known enumerator    */
+    GDR_ERR_HIP = -7,         /* the HIP runtime rejected a launch          */
+    GDR_ERR_ALIAS = -8        /* state_in and state_out partially overlap   */
+};
+
+/*
+ * One decode step for B x H independent heads, updating the state in place
+ * (the per-token step of §2.D's decode; one token per head).
+ *
+ *   q, k   [B, H, dk]   dtype         v, o   [B, H, dv]   dtype
+ *   alpha  [B, H] (GDN) or [B, H, dk] (KDA), fp32
+ *   beta   [B, H], fp32
+ *   state  [B, H, dk, dv], fp32, read and overwritten with S_t
+ *
+ * o may not overlap any input.  Returns a GDR_* status.
+ */
+int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float scale,
+                    const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta,
+                    float* state, void* o, void* stream);
+
+/*
+ * Chunked prefill of T tokens for B x H independent heads (the prompt pass
+ * of the same recurrence), in chunks of `chunk` = 64 tokens; T need not be a
+ * multiple of the chunk.
+ *
+ *   q, k      [B, T, H, dk]   dtype     v, o   [B, T, H, dv]   dtype
+ *   alpha     [B, T, H] (GDN) or [B, T, H, dk] (KDA), fp32
+ *   beta      [B, T, H], fp32
+ *   state_in  [B, H, dk, dv] fp32, or NULL for a zero initial state
+ *   state_out [B, H, dk, dv] fp32, receives S_T; may equal state_in (in
+ *             place) but may not partially overlap it
+ *   workspace device scratch of at least
+ *             gdr_chunk_prefill_workspace_bytes(...) bytes (NULL if that is 0)
+ *
+ * T == 0 copies state_in (or zeros) to state_out.  With dtype BF16 the
+ * contractions run on bf16 matrix cores with fp32 accumulation and an fp32
+ * state; with dtype F32 every operation is fp32.  KDA with bf16 inputs
+ * requires the cumulative log-gate inside any chunk to stay above -80 per
+ * channel (exp of its half-range must not overflow); GDN and the F32 path
+ * have no such limit.  Returns a GDR_* status.
+ */
+int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                      float scale,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta,
+                      const float* state_in, float* state_out, void* o,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gdr_chunk_prefill needs for these arguments (0 when the
+ * arguments are invalid or no scratch is needed). */
+size_t gdr_chunk_prefill_workspace_bytes(int gate, int dtype, int B, int T, int H,
+                                         int dk, int dv, int chunk);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* gdr_status_string(int status);
+
+/* GDR_ABI_VERSION of the loaded library. */
+int gdr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

@@ -1,0 +1,142 @@
+"""C-ABI contract of libgdr on the CPU: exports, status strings, validation.
+
+Every call here fails validation (or is a zero-sized no-op), which the
+library guarantees happens before any HIP call, so no device is touched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_08_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+OK, NULL, SHAPE, UNSUP, MISAL, WS, ENUM, HIP, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdr.library_path()):
+        from gated_delta_rule_08_amd import build
+        build.build()
+    return gdr.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gdr_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_what_binding_lists():
+    assert _declared_functions() == sorted(gdr.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", gdr.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define GDR_ABI_VERSION (\d+)", text).group(1))
+    assert gdr.gdr_abi_version() == ver
+
+
+def test_status_strings(lib):
+    for code, tag in [(OK, "GDR_OK"), (NULL, "NULL_PTR"), (SHAPE, "BAD_SHAPE"),
+                      (UNSUP, "UNSUPPORTED"), (MISAL, "MISALIGNED"), (WS, "WORKSPACE"),
+                      (ENUM, "BAD_ENUM"), (HIP, "GDR_ERR_HIP"), (ALIAS, "ALIAS")]:
+        assert tag in gdr.gdr_status_string(code)
+    assert gdr.gdr_status_string(12345) == "unknown gdr status"
+
+
+# Fake, non-NULL, 256-byte aligned "device" addresses: only ever passed to
+# calls that are rejected by validation.
+P = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(12)]
+
+
+def decode(lib, gate=0, dtype=1, B=2, H=3, dk=128, dv=128, ptrs=None):
+    p = list(P[:8]) if ptrs is None else ptrs
+    return lib.gdr_decode_step(gate, dtype, B, H, dk, dv, 1.0, *p)
+
+
+def prefill(lib, gate=0, dtype=1, B=2, T=70, H=3, dk=128, dv=128, chunk=64, ptrs=None,
+            ws=None, ws_bytes=0):
+    p = list(P[:8]) if ptrs is None else ptrs
+    return lib.gdr_chunk_prefill(gate, dtype, B, T, H, dk, dv, chunk, 1.0, *p,
+                                 ws, ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, gate=2) == ENUM
+    assert decode(lib, dtype=7) == ENUM
+    assert decode(lib, B=-1) == SHAPE
+    assert decode(lib, H=-5) == SHAPE
+    assert decode(lib, dk=96) == UNSUP
+    assert decode(lib, dv=8) == UNSUP
+    assert decode(lib, B=1 << 30, H=1 << 10) == SHAPE
+    for i in range(7):  # q k v alpha beta state o
+        ptrs = list(P[:8])
+        ptrs[i] = None
+        assert decode(lib, ptrs=ptrs) == NULL, i
+    for i in (0, 1, 2, 5, 6):  # q k v state o need 16-byte alignment
+        ptrs = list(P[:8])
+        ptrs[i] = ctypes.c_void_p(P[i].value + 8)
+        assert decode(lib, ptrs=ptrs) == MISAL, i
+    ptrs = list(P[:8])
+    ptrs[3] = ctypes.c_void_p(P[3].value + 4)  # KDA alpha needs 16-byte alignment
+    assert decode(lib, gate=1, ptrs=ptrs) == MISAL
+    ptrs = list(P[:8])
+    ptrs[4] = ctypes.c_void_p(P[4].value + 2)  # beta needs 4-byte alignment
+    assert decode(lib, ptrs=ptrs) == MISAL
+
+
+def test_decode_zero_size_is_noop(lib):
+    assert decode(lib, B=0, ptrs=[None] * 8) == OK
+    assert decode(lib, H=0, ptrs=[None] * 8) == OK
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, gate=-1) == ENUM
+    assert prefill(lib, dtype=2) == ENUM
+    assert prefill(lib, T=-1) == SHAPE
+    assert prefill(lib, chunk=32) == UNSUP
+    assert prefill(lib, dk=256) == UNSUP
+    ptrs = list(P[:8])
+    ptrs[6] = None  # state_out
+    assert prefill(lib, ptrs=ptrs) == NULL
+    for i in (0, 1, 2, 3, 4, 7):  # q k v alpha beta o
+        ptrs = list(P[:8])
+        ptrs[i] = None
+        assert prefill(lib, ptrs=ptrs) == NULL, i
+    ptrs = list(P[:8])
+    ptrs[5] = ctypes.c_void_p(P[6].value + 64)  # state_in overlaps state_out partially
+    assert prefill(lib, ptrs=ptrs) == ALIAS
+    ptrs = list(P[:8])
+    ptrs[2] = ctypes.c_void_p(P[2].value + 2)
+    assert prefill(lib, ptrs=ptrs) == MISAL
+    assert prefill(lib, B=0, ptrs=[None] * 8) == OK
+
+
+def test_workspace(lib):
+    n = lib.gdr_chunk_prefill_workspace_bytes(0, 1, 4, 8192, 32, 128, 128, 64)
+    assert n == 0
+    assert gdr.gdr_chunk_prefill_workspace_bytes("kda", __import__("torch").bfloat16,
+                                                 1, 32768, 32, 128, 128) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 16)
+    with pytest.raises(ValueError):
+        gdr.gdr_decode_step("gdn", q, q, q, torch.zeros(1, 1), torch.zeros(1, 1),
+                            torch.zeros(1, 1, 16, 16), torch.zeros(1, 1, 16))
