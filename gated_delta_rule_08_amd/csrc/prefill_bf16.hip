@@ -1,174 +1,162 @@
 // Chunked prefill with bf16 inputs: every contraction on bf16 matrix cores
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation), the state in fp32.
+// (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16, fp32 accumulation), the state
+// in fp32 registers for the whole sequence.
 //
 // Method ("Super Apriel: One Checkpoint, Many Speeds", §2.A: GDN and KDA are
-// recurrent mixers with a fixed-size state, scalar resp. channel-wise gate).
-// For a chunk of n <= 64 tokens entering with state S, G_t is the cumulative
-// log-gate from the chunk start (per key channel for KDA), beta_t the write
-// strength, and the recurrence S_t = (I - beta_t k_t k_t^T) D_t S_{t-1} +
-// beta_t k_t v_t^T unrolls to
-//     A_tj = beta_t sum_c k_tc k_jc exp(G_tc - G_jc)     j <  t   (else 0)
-//     P_tj =        sum_c q_tc k_jc exp(G_tc - G_jc)     j <= t   (else 0)
-//     T    = (I + A)^{-1}                                (UT transform)
-//     X    = diag(beta) (V - Khat S),  Khat_t = k_t exp(G_t)
-//     U    = T X
-//     O    = scale (Qhat S + P U),     Qhat_t = q_t exp(G_t)
-//     S   <- diag(exp(G_end)) S + Ktil^T U,  Ktil_t = k_t exp(G_end - G_t)
-// (the WY form with W = T diag(beta) Khat is never materialised: U = T X
-// folds W S into Khat S).
+// recurrent mixers with a fixed-size state and a scalar resp. channel-wise
+// gate).  For a chunk of n <= 64 tokens entering with state S, G_t is the
+// cumulative log2-gate from the chunk start (per key channel for KDA) and the
+// recurrence S_t = (I - beta_t k_t k_t^T) D_t S_{t-1} + beta_t k_t v_t^T
+// unrolls exactly to
+//     A_tj = beta_t sum_c k_tc k_jc 2^(G_tc - G_jc)     j <  t   (else 0)
+//     P_tj =        sum_c q_tc k_jc 2^(G_tc - G_jc)     j <= t   (else 0)
+//     X    = diag(beta) (V - Khat S),  Khat_t = k_t 2^G_t
+//     U    = (I + A)^{-1} X
+//     O    = scale (Qhat S + P U),     Qhat_t = q_t 2^G_t
+//     S   <- diag(2^G_end) S + Ktil^T U,  Ktil_t = k_t 2^(G_end - G_t)
+// (the WY form W = (I + A)^{-1} diag(beta) Khat is folded into X).
 //
-// Gates inside the contractions.  GDN: the decay is one scalar per token, so
-// the MFMAs run on raw q, k and exp(G_t - G_j) (always <= 1) scales their
-// outputs.  KDA: the decay differs per channel and must be folded into the
-// operands; with a per-channel reference R = G_end / 2 the factors
-// exp(G_t - R) and exp(R - G_j) both stay within exp(|G_end| / 2), and S is
-// scaled by exp(R) when it is rounded to bf16 for the products.  log(alpha)
-// is floored at -80 (exp(-80) ~ 2e-35), so alpha == 0 is legal; KDA needs
-// the total log-decay of a channel within one chunk above about -170.
+// U = (I + A)^{-1} X is a blocked forward substitution over the four 16-token
+// blocks, U_r = D_r^{-1} (X_r - sum_{k<r} A_rk U_k), with the inverses D_r^{-1}
+// of the unit lower triangular 16x16 diagonal blocks of I + A computed in fp32
+// by forward substitution (one lane per column).
 //
-// UT transform in fp32.  The four 16x16 diagonal blocks of I + A are inverted
-// by forward substitution (one lane per column), then the off-diagonal blocks
-// follow from two doubling levels,
-//     T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,
-//     T_[23][01] = -T_[23][23] A_[23][01] T_[01][01],
-// on fp32 matrix cores (v_mfma_f32_16x16x4_f32).  T is rounded to bf16 once.
+// Gates inside the contractions.  GDN: one scalar per token, so the MFMAs run
+// on raw q and k and the factors 2^(G_t - G_j) <= 1, 2^G_t, 2^(G_end - G_t)
+// scale their outputs.  KDA: the decay differs per channel and is folded into
+// the operands around a per-channel reference R = G_end / 2, so every factor
+// stays within 2^(|G_end| / 2); S is scaled by 2^R where it is rounded to bf16.
+// log2(alpha) is floored at -115.4 (alpha ~ e^-80), so alpha == 0 is legal;
+// KDA needs the total log-decay of a channel within one chunk above about -170.
 //
-// Mapping.  One workgroup of four wavefronts per (b, h, slice of DVS value
-// columns); the value columns of S are independent, so slices of one head
-// run on different CUs (sharing q/k/gates through L2: the slices of a head
-// are placed on one XCD).  The fp32 state slice lives in MFMA accumulators
-// for the whole sequence; only a bf16 copy goes through LDS per chunk.
+// Mapping.  One workgroup per (b, h, slice of 16*NSW value columns); the value
+// columns of S are independent, so the slices of a head run on different CUs
+// (their block ids are congruent mod 8: one XCD, shared L2).  Waves 0..3 are
+// "prep" waves, waves 4.. are "serial" waves owning 16 value columns each:
+//   iteration i, phase 1: prep gates chunk i+1 into LDS buffer (i+1)&1 and
+//                         prefetches chunk i+2; serial computes Khat S, X and
+//                         U for chunk i from buffer i&1;
+//   phase 2:              prep forms A, P and the D_r^{-1} of chunk i+1;
+//                         serial forms O and updates S for chunk i.
+// Two workgroup barriers per chunk.  The serial chain keeps S, X and U in
+// MFMA registers: an fp32 accumulator tile holds rows 4g..4g+3 of column l%16
+// in lane l (g = l/16), so two row tiles together are the B operand of a
+// K=32 step whose k order is {4g..4g+3, 16+4g..16+4g+3}; the LDS operand of
+// that step is read in the same k order, which keeps every product exact
+// without any register shuffle.
 #include "gdr_internal.h"
 
 namespace gdr {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kC = 64;             // chunk
-constexpr float kLogFloor = -80.0f;
-constexpr int kThreads = 256;
+constexpr int kC = 64;                 // chunk
+constexpr int kPrepWaves = 4;
+constexpr float kLog2Floor = -115.4f;  // log2(alpha) floor, alpha ~ e^-80
 
-__device__ __forceinline__ bf16x8 ld_op(const bf16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
-__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// but leaves global loads in flight (a full __syncthreads also drains vmcnt,
+// which would stall the prefetch of the next chunk).  Waves exchange data
+// only through LDS in this kernel.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+__device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x4 cvt4(const f32x4& x) {
+    bf16x4 r;
+    r[0] = static_cast<__bf16>(x[0]);
+    r[1] = static_cast<__bf16>(x[1]);
+    r[2] = static_cast<__bf16>(x[2]);
+    r[3] = static_cast<__bf16>(x[3]);
+    return r;
+}
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x4 lds4(const bf16_t* p) {
+    return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(p));
+}
+__device__ __forceinline__ bf16x8 lds8(const bf16_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+// k order {0..3, 16..19} relative to p: matches two stacked accumulator tiles.
+__device__ __forceinline__ bf16x8 lds_perm(const bf16_t* p) { return cat8(lds4(p), lds4(p + 16)); }
+__device__ __forceinline__ void st4(bf16_t* p, const f32x4& x) {
+    *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, cvt4(x));
+}
+__device__ __forceinline__ uint32_t bf_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// acc(16x16) += A[0:16, k0:k0+32*steps] * Bt[0:16, k0:...]^T, both K-contiguous.
-// Lane l holds row (l & 15) of A / of Bt and k-octet (l >> 4); the output
-// element acc[i] is C[4 * (l >> 4) + i][l & 15].
-template <int STEPS>
-__device__ __forceinline__ void mma_nt(f32x4& acc, const bf16_t* A, int pa, const bf16_t* Bt,
-                                       int pb, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s)
-        acc = mfma_bf16(ld_op(A + r * pa + s * 32 + g * 8), ld_op(Bt + r * pb + s * 32 + g * 8), acc);
-}
-__device__ __forceinline__ void mma_nt_dyn(f32x4& acc, const bf16_t* A, int pa, const bf16_t* Bt,
-                                           int pb, int lane, int steps) {
-    const int r = lane & 15, g = lane >> 4;
-    for (int s = 0; s < steps; ++s)
-        acc = mfma_bf16(ld_op(A + r * pa + s * 32 + g * 8), ld_op(Bt + r * pb + s * 32 + g * 8), acc);
-}
-
-// fp32 16x16 block product X * Y (row-major in LDS with pitches px, py),
-// accumulated into `acc` in the accumulator layout described above.
-__device__ __forceinline__ f32x4 mm16_f32(const float* X, int px, const float* Y, int py,
-                                          int lane, f32x4 acc) {
-    const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[r * px + 4 * s + g], Y[(4 * s + g) * py + r],
-                                                   acc, 0, 0, 0);
-    return acc;
-}
-
-template <int DK, int DVS, bool KDA>
+template <int DK, int NSW, bool KDA>
 struct Layout {
-    static constexpr int DKP = DK < 32 ? 32 : DK;  // contraction pad for dk = 16
+    static constexpr int DKP = DK < 32 ? 32 : DK;  // contraction pad (dk = 16)
     static constexpr int PK = DKP + 8;             // pitch of [token][channel] tiles (bf16)
-    static constexpr int PT = kC + 8;              // pitch of [*][token] tiles (bf16)
-    static constexpr int PF = kC + 4;              // pitch of fp32 64x64 tiles
-    static constexpr int PY = 16 + 4;              // pitch of fp32 16x16 scratch
+    static constexpr int PT = kC + 4;              // pitch of [channel][token] tiles (bf16)
+    static constexpr int PD = 16 + 8;              // pitch of packed 16x16 tiles (bf16)
+    static constexpr int TILE = 16 * PD * 2;       // bytes of one packed tile
     static constexpr int NPAIR = DK / 2;           // channel pairs
-    static constexpr int TPP = kThreads / NPAIR;   // threads per channel pair
-    static constexpr int TPT = kC / TPP;           // tokens per thread
-    // byte offsets
-    static constexpr int oKh = 0;
-    static constexpr int oQh = oKh + kC * PK * 2;
-    static constexpr int oKc = oQh + kC * PK * 2;
-    static constexpr int oKtT = oKc + (KDA ? kC * PK * 2 : 0);
-    static constexpr int oTb = oKtT + DK * PT * 2;
-    static constexpr int oPb = oTb + kC * PT * 2;
-    static constexpr int oR0 = oPb + kC * PT * 2;
-    // region R0: serial-phase tiles, aliased with the fp32 solve scratch
-    static constexpr int oSt = oR0;
-    static constexpr int oXt = oSt + DVS * PK * 2;
-    static constexpr int oUt = oXt + DVS * PT * 2;
-    static constexpr int oU2t = oUt + DVS * PT * 2;
-    static constexpr int endSerial = oU2t + (KDA ? 0 : DVS * PT * 2);
-    static constexpr int oAf = oR0;
-    static constexpr int oTf = oAf + kC * PF * 4;
-    static constexpr int oYf = oTf + kC * PF * 4;
-    static constexpr int endSolve = oYf + 4 * 16 * PY * 4;
-    static constexpr int oBeta = endSerial > endSolve ? endSerial : endSolve;  // beta_t
-    static constexpr int oGl = oBeta + kC * 4;         // GDN: G_t
-    static constexpr int oGend = oGl + kC * 4;         // exp(G_end) per channel
-    static constexpr int oGref = oGend + DK * 4;       // KDA: exp(R) per channel
-    static constexpr int oPart = oGref + DK * 4;       // cumsum partials [TPP][DK]
-    static constexpr int bytes = oPart + TPP * DK * 4;
+    static constexpr int TPP = 256 / NPAIR;        // lanes per pair (one wave segment)
+    static constexpr int PPW = 64 / TPP;           // pairs per prep wave
+    static constexpr int TPT = kC / TPP;           // tokens per lane
+    // one chunk buffer (byte offsets)
+    static constexpr int oKh = 0;                         // Khat [64][PK]
+    static constexpr int oQh = oKh + kC * PK * 2;         // Qhat [64][PK]
+    static constexpr int oKt = oQh + kC * PK * 2;         // Ktil^T [DK][PT]
+    static constexpr int oP = oKt + DK * PT * 2;          // P, 10 lower tiles
+    static constexpr int oA = oP + 10 * TILE;             // -A, 6 off-diagonal tiles
+    static constexpr int oD = oA + 6 * TILE;              // D_r^{-1}, 4 tiles
+    static constexpr int oBeta = oD + 4 * TILE;           // beta_t [64]
+    static constexpr int oEg = oBeta + kC * 4;            // GDN 2^G_t [64]
+    static constexpr int oEk = oEg + kC * 4;              // GDN 2^(G_end - G_t) [64]
+    static constexpr int oGend = oEk + kC * 4;            // 2^G_end per channel (GDN: [0])
+    static constexpr int oSref = oGend + DK * 4;          // KDA 2^R per channel
+    static constexpr int BUF = ((oSref + DK * 4) + 15) / 16 * 16;
+    // prep-private
+    static constexpr int oKc = 2 * BUF;                   // KDA Kcheck [64][PK]
+    static constexpr int oG = oKc + (KDA ? kC * PK * 2 : 0);  // GDN G_t [64]
+    static constexpr int PS = 20;                         // pitch of the fp32 scratch tiles
+    static constexpr int oScr = oG + kC * 4;              // fp32 diagonal tiles [4][16][PS]
+    static constexpr int bytes = oScr + kPrepWaves * 16 * PS * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
-    static_assert(TPT >= 2 && TPT % 2 == 0, "token split");
+    static_assert(TPT >= 2 && TPT % 2 == 0 && TPP <= 64, "token split");
 };
 
-template <int DK, int DVS, bool KDA>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
+__device__ __forceinline__ int ptile(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }  // ct <= rt
+__device__ __forceinline__ int atile(int rt, int ct) { return rt * (rt - 1) / 2 + ct; }  // ct < rt
+
+template <int DK, int NSW, bool KDA>
+__global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     int B, int T, int H, int DV, int NS, float scale, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ state_in,
     float* __restrict__ state_out, bf16_t* __restrict__ o) {
-    using L = Layout<DK, DVS, KDA>;
-    constexpr int NCT = DVS / 16;            // value-column tiles
-    constexpr int NRT = DK / 16;             // key-row tiles of S
-    constexpr int NST = NRT * NCT;           // S tiles
-    constexpr int MST = (NST + 3) / 4;       // S tiles per wave (max)
-    constexpr int KSTEPS = L::DKP / 32;      // contraction steps over dk
+    using L = Layout<DK, NSW, KDA>;
+    constexpr int DVS = 16 * NSW;
+    constexpr int NRT = DK / 16;          // 16-row tiles of S
+    constexpr int NKS = L::DKP / 32;      // K=32 steps over dk
+    constexpr int TPT = L::TPT;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    bf16_t* Kh = reinterpret_cast<bf16_t*>(smem + L::oKh);
-    bf16_t* Qh = reinterpret_cast<bf16_t*>(smem + L::oQh);
-    bf16_t* Kc = KDA ? reinterpret_cast<bf16_t*>(smem + L::oKc) : Kh;
-    bf16_t* KtT = reinterpret_cast<bf16_t*>(smem + L::oKtT);
-    bf16_t* Tb = reinterpret_cast<bf16_t*>(smem + L::oTb);
-    bf16_t* Pb = reinterpret_cast<bf16_t*>(smem + L::oPb);
-    bf16_t* St = reinterpret_cast<bf16_t*>(smem + L::oSt);
-    bf16_t* Xt = reinterpret_cast<bf16_t*>(smem + L::oXt);
-    bf16_t* Ut = reinterpret_cast<bf16_t*>(smem + L::oUt);
-    bf16_t* U2t = KDA ? Ut : reinterpret_cast<bf16_t*>(smem + L::oU2t);
-    float* Af = reinterpret_cast<float*>(smem + L::oAf);
-    float* Tf = reinterpret_cast<float*>(smem + L::oTf);
-    float* Yf = reinterpret_cast<float*>(smem + L::oYf);
-    float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
-    float* sGl = reinterpret_cast<float*>(smem + L::oGl);
-    float* sGend = reinterpret_cast<float*>(smem + L::oGend);
-    float* sGref = reinterpret_cast<float*>(smem + L::oGref);
-    float* sPart = reinterpret_cast<float*>(smem + L::oPart);
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // Block -> (head, slice): the NS slices of a head get block ids that are
-    // congruent mod 8, i.e. land on one XCD and share its L2.
     const int BH = B * H;
     const int grp = blockIdx.x / (8 * NS);
     const int rem = blockIdx.x - grp * 8 * NS;
@@ -176,372 +164,413 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     const int slice = rem >> 3;
     if (bh >= BH) return;  // whole block exits before any barrier
     const int b = bh / H, h = bh - b * H;
-    const int c0 = slice * DVS;
+    const int nch = (T + kC - 1) / kC;
+    const bool prep = wave < kPrepWaves;
 
-    // ---- constant zeros: upper tiles of T and P, dk padding -----------------
-    for (int idx = tid; idx < kC * kC; idx += kThreads) {
-        const int t = idx / kC, j = idx % kC;
-        if ((j >> 4) > (t >> 4)) { Tb[t * L::PT + j] = 0; Pb[t * L::PT + j] = 0; }
-    }
-    if constexpr (L::DKP != DK) {
-        for (int idx = tid; idx < kC * (L::DKP - DK); idx += kThreads) {
-            const int t = idx / (L::DKP - DK), c = DK + idx % (L::DKP - DK);
-            Kh[t * L::PK + c] = 0; Qh[t * L::PK + c] = 0;
-            if constexpr (KDA) Kc[t * L::PK + c] = 0;
+    auto bfp = [&](int c, int off) { return reinterpret_cast<bf16_t*>(smem + (c & 1) * L::BUF + off); };
+    auto f32p = [&](int c, int off) { return reinterpret_cast<float*>(smem + (c & 1) * L::BUF + off); };
+    bf16_t* Kc = reinterpret_cast<bf16_t*>(smem + L::oKc);  // used by KDA only
+    float* sG = reinterpret_cast<float*>(smem + L::oG);
+
+    if constexpr (L::DKP != DK) {  // zero the contraction padding once (both buffers, Kc)
+        constexpr int W = L::DKP - DK;
+        for (int idx = tid; idx < 2 * kC * W; idx += blockDim.x) {
+            const int c = idx / (kC * W), r = idx % (kC * W);
+            const int t = r / W, col = DK + r % W;
+            bfp(c, L::oKh)[t * L::PK + col] = 0;
+            bfp(c, L::oQh)[t * L::PK + col] = 0;
+            if (KDA && c == 0) Kc[t * L::PK + col] = 0;
         }
     }
 
-    // ---- fp32 state slice in accumulators -----------------------------------
-    // owned tile index s = wave + 4 m: key-row tile s / NCT, column tile s % NCT.
-    f32x4 S[MST];
-    const size_t sbase = static_cast<size_t>(bh) * DK * DV;
+    // ================= prep-wave work =================
+    const int pl = lane / L::TPP, tg = lane % L::TPP;
+    const int ch = 2 * (wave * L::PPW + pl);
+    const int tlo = tg * TPT;
+    struct PrepIn {
+        float a0[TPT], a1[TPT], bt[TPT];
+        uint32_t kw[TPT], qw[TPT];
+    };
+    auto prep_load = [&](int c, PrepIn& R) {
+        const int t0 = c * kC, nn = min(kC, T - t0);
 #pragma unroll
-    for (int m = 0; m < MST; ++m) {
-        const int s = wave + 4 * m;
-        S[m] = zero4();
-        if (s < NST && state_in) {
-            const int rt = s / NCT, ct = s % NCT;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[m][i] = state_in[sbase + static_cast<size_t>(16 * rt + 4 * lg + i) * DV + c0 +
-                                   16 * ct + lr];
+        for (int u = 0; u < TPT; ++u) {
+            const int tc = min(tlo + u, nn - 1);
+            const size_t gi = (static_cast<size_t>(b) * T + t0 + tc) * H + h;
+            if constexpr (KDA) {
+                const float2 a2 = *reinterpret_cast<const float2*>(alpha + gi * DK + ch);
+                R.a0[u] = a2.x;
+                R.a1[u] = a2.y;
+            } else {
+                R.a0[u] = R.a1[u] = alpha[gi];
+            }
+            R.bt[u] = beta[gi];
+            R.kw[u] = *reinterpret_cast<const uint32_t*>(k + gi * DK + ch);
+            R.qw[u] = *reinterpret_cast<const uint32_t*>(q + gi * DK + ch);
         }
-    }
+    };
 
-    const int pair = tid % L::NPAIR;
-    const int tgrp = tid / L::NPAIR;
-    const int ch = 2 * pair;
-    const int tlo = tgrp * L::TPT;
-
-    for (int t0 = 0; t0 < T; t0 += kC) {
-        const int n = min(kC, T - t0);
-        __syncthreads();  // previous chunk finished reading every tile
-
-        // ---- gates and gated operands: thread = (channel pair, token run) ---
-        float g0[L::TPT], g1[L::TPT];
-        {
-            float acc0 = 0.f, acc1 = 0.f;
+    // Gates and gated operands of chunk c into buffer c & 1.  Lane = (channel
+    // pair, run of TPT tokens); the TPP lanes of a pair are one wave segment,
+    // so the cumulative sum over the chunk is an in-wave scan.
+    auto prep_gate = [&](int c, const PrepIn& R) {
+        const int n = min(kC, T - c * kC);
+        float g0[TPT], g1[TPT];
+        float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-            for (int u = 0; u < L::TPT; ++u) {
+        for (int u = 0; u < TPT; ++u) {
+            const bool valid = tlo + u < n;
+            const float l0 = valid ? fmaxf(__log2f(R.a0[u]), kLog2Floor) : 0.f;
+            const float l1 = KDA ? (valid ? fmaxf(__log2f(R.a1[u]), kLog2Floor) : 0.f) : l0;
+            acc0 += l0;
+            acc1 += l1;
+            g0[u] = acc0;
+            g1[u] = acc1;
+        }
+        float inc0 = acc0, inc1 = acc1;
+#pragma unroll
+        for (int d = 1; d < L::TPP; d <<= 1) {
+            const float y0 = __shfl_up(inc0, d, L::TPP), y1 = __shfl_up(inc1, d, L::TPP);
+            if (tg >= d) { inc0 += y0; inc1 += y1; }
+        }
+        const float off0 = inc0 - acc0, off1 = inc1 - acc1;
+        const float end0 = __shfl(inc0, L::TPP - 1, L::TPP), end1 = __shfl(inc1, L::TPP - 1, L::TPP);
+        bf16_t* Kh = bfp(c, L::oKh);
+        bf16_t* Qh = bfp(c, L::oQh);
+        bf16_t* Kt = bfp(c, L::oKt);
+        const bool lead = (wave == 0 && pl == 0);  // one pair writes the per-token vectors
+        if (lead) {
+            float* sb = f32p(c, L::oBeta);
+#pragma unroll
+            for (int u = 0; u < TPT; ++u) sb[tlo + u] = tlo + u < n ? R.bt[u] : 0.f;
+        }
+        uint32_t kt0[TPT / 2], kt1[TPT / 2];
+        if constexpr (KDA) {
+            const float ref0 = 0.5f * end0, ref1 = 0.5f * end1;
+            const float ce0 = exp2f(end0 - ref0), ce1 = exp2f(end1 - ref1);
+            if (tg == 0) {
+                f32p(c, L::oGend)[ch] = exp2f(end0);
+                f32p(c, L::oGend)[ch + 1] = exp2f(end1);
+                f32p(c, L::oSref)[ch] = exp2f(ref0);
+                f32p(c, L::oSref)[ch + 1] = exp2f(ref1);
+            }
+#pragma unroll
+            for (int u = 0; u < TPT; ++u) {
                 const int t = tlo + u;
-                float l0 = 0.f, l1 = 0.f;
-                if (t < n) {
-                    const size_t gi = (static_cast<size_t>(b) * T + t0 + t) * H + h;
-                    if constexpr (KDA) {
-                        const float2 a2 = *reinterpret_cast<const float2*>(alpha + gi * DK + ch);
-                        l0 = fmaxf(__logf(a2.x), kLogFloor);
-                        l1 = fmaxf(__logf(a2.y), kLogFloor);
-                    } else {
-                        l0 = l1 = fmaxf(__logf(alpha[gi]), kLogFloor);
-                    }
+                const bool valid = t < n;
+                const uint32_t kw = valid ? R.kw[u] : 0u, qw = valid ? R.qw[u] : 0u;
+                const float k0 = bf_lo(kw), k1 = bf_hi(kw), q0 = bf_lo(qw), q1 = bf_hi(qw);
+                const float up0 = exp2f(off0 + g0[u] - ref0), up1 = exp2f(off1 + g1[u] - ref1);
+                const float dn0 = __builtin_amdgcn_rcpf(up0), dn1 = __builtin_amdgcn_rcpf(up1);
+                bf16x2 x;
+                x[0] = static_cast<__bf16>(k0 * up0);
+                x[1] = static_cast<__bf16>(k1 * up1);
+                *reinterpret_cast<bf16x2*>(Kh + t * L::PK + ch) = x;
+                x[0] = static_cast<__bf16>(q0 * up0);
+                x[1] = static_cast<__bf16>(q1 * up1);
+                *reinterpret_cast<bf16x2*>(Qh + t * L::PK + ch) = x;
+                x[0] = static_cast<__bf16>(k0 * dn0);
+                x[1] = static_cast<__bf16>(k1 * dn1);
+                *reinterpret_cast<bf16x2*>(Kc + t * L::PK + ch) = x;
+                const uint32_t b0 = bf_bits(k0 * dn0 * ce0), b1 = bf_bits(k1 * dn1 * ce1);
+                if (u & 1) { kt0[u >> 1] |= b0 << 16; kt1[u >> 1] |= b1 << 16; }
+                else { kt0[u >> 1] = b0; kt1[u >> 1] = b1; }
+            }
+        } else {
+            if (lead) {
+                float* eg = f32p(c, L::oEg);
+                float* ek = f32p(c, L::oEk);
+#pragma unroll
+                for (int u = 0; u < TPT; ++u) {
+                    const float G = off0 + g0[u];
+                    sG[tlo + u] = G;
+                    eg[tlo + u] = exp2f(G);
+                    ek[tlo + u] = exp2f(end0 - G);
                 }
-                acc0 += l0;
-                acc1 += l1;
-                g0[u] = acc0;
-                g1[u] = acc1;
+                if (tg == 0) f32p(c, L::oGend)[0] = exp2f(end0);
             }
-            sPart[tgrp * DK + ch] = acc0;
-            sPart[tgrp * DK + ch + 1] = acc1;
-        }
-        if (pair == 0) {
 #pragma unroll
-            for (int u = 0; u < L::TPT; ++u) {
+            for (int u = 0; u < TPT; ++u) {
                 const int t = tlo + u;
-                sBeta[t] = t < n ? beta[(static_cast<size_t>(b) * T + t0 + t) * H + h] : 0.f;
+                const bool valid = t < n;
+                const uint32_t kw = valid ? R.kw[u] : 0u, qw = valid ? R.qw[u] : 0u;
+                *reinterpret_cast<uint32_t*>(Kh + t * L::PK + ch) = kw;
+                *reinterpret_cast<uint32_t*>(Qh + t * L::PK + ch) = qw;
+                if (u & 1) { kt0[u >> 1] |= kw << 16; kt1[u >> 1] |= kw & 0xffff0000u; }
+                else { kt0[u >> 1] = kw & 0xffffu; kt1[u >> 1] = kw >> 16; }
             }
         }
-        __syncthreads();  // partial sums visible
-        {
-            float off0 = 0.f, off1 = 0.f, end0 = 0.f, end1 = 0.f;
-            for (int gq = 0; gq < L::TPP; ++gq) {
-                const float p0 = sPart[gq * DK + ch], p1 = sPart[gq * DK + ch + 1];
-                if (gq < tgrp) { off0 += p0; off1 += p1; }
-                end0 += p0;
-                end1 += p1;
-            }
-            const float ref0 = KDA ? 0.5f * end0 : 0.f, ref1 = KDA ? 0.5f * end1 : 0.f;
-            if (tgrp == 0) {
-                sGend[ch] = __expf(end0);
-                sGend[ch + 1] = __expf(end1);
-                if constexpr (KDA) { sGref[ch] = __expf(ref0); sGref[ch + 1] = __expf(ref1); }
-            }
-            uint32_t kt0[L::TPT / 2], kt1[L::TPT / 2];
 #pragma unroll
-            for (int u = 0; u < L::TPT; ++u) {
-                const int t = tlo + u;
-                const float G0 = off0 + g0[u], G1 = off1 + g1[u];
-                float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
-                if (t < n) {
-                    const size_t ri = ((static_cast<size_t>(b) * T + t0 + t) * H + h) * DK + ch;
-                    const uint32_t kw = *reinterpret_cast<const uint32_t*>(k + ri);
-                    const uint32_t qw = *reinterpret_cast<const uint32_t*>(q + ri);
-                    k0 = __uint_as_float(kw << 16);
-                    k1 = __uint_as_float(kw & 0xffff0000u);
-                    q0 = __uint_as_float(qw << 16);
-                    q1 = __uint_as_float(qw & 0xffff0000u);
-                }
-                if (!KDA && pair == 0) sGl[t] = G0;
-                float kt_0, kt_1;
-                if constexpr (KDA) {
-                    const float up0 = __expf(G0 - ref0), up1 = __expf(G1 - ref1);
-                    const float dn0 = __expf(ref0 - G0), dn1 = __expf(ref1 - G1);
-                    *reinterpret_cast<uint32_t*>(Kh + t * L::PK + ch) = pack2(k0 * up0, k1 * up1);
-                    *reinterpret_cast<uint32_t*>(Qh + t * L::PK + ch) = pack2(q0 * up0, q1 * up1);
-                    *reinterpret_cast<uint32_t*>(Kc + t * L::PK + ch) = pack2(k0 * dn0, k1 * dn1);
-                    kt_0 = k0 * __expf(end0 - G0);
-                    kt_1 = k1 * __expf(end1 - G1);
+        for (int u = 0; u < TPT / 2; ++u) {
+            *reinterpret_cast<uint32_t*>(Kt + ch * L::PT + tlo + 2 * u) = kt0[u];
+            *reinterpret_cast<uint32_t*>(Kt + (ch + 1) * L::PT + tlo + 2 * u) = kt1[u];
+        }
+    };
+
+    // A, P and the diagonal-block inverses of chunk c (buffer c & 1).  The
+    // tile products run transposed, C^T = Kr M^T, so a lane ends up with 4
+    // consecutive j of one row t and stores 8 bytes.
+    auto prep_ap = [&](int c) {
+        const bf16_t* Kh = bfp(c, L::oKh);
+        const bf16_t* Qh = bfp(c, L::oQh);
+        const bf16_t* Kr = KDA ? Kc : Kh;  // right factor (j side)
+        const float* sb = f32p(c, L::oBeta);
+        bf16_t* Pt = bfp(c, L::oP);
+        bf16_t* At = bfp(c, L::oA);
+        bf16_t* Dt = bfp(c, L::oD);
+        float* scr = reinterpret_cast<float*>(smem + L::oScr) + wave * 16 * L::PS;
+        // tile 0: this wave's diagonal A tile; then 4 of the 16 others
+        // (6 off-diagonal A tiles, then 10 P tiles), round-robin over waves
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            bool isP;
+            int rt, ct;
+            if (m == 0) {
+                isP = false;
+                rt = ct = wave;
+            } else {
+                const int x = wave + 4 * (m - 1);  // 0..15
+                if (x < 6) {
+                    isP = false;
+                    rt = x < 1 ? 1 : (x < 3 ? 2 : 3);
+                    ct = x - rt * (rt - 1) / 2;
                 } else {
-                    *reinterpret_cast<uint32_t*>(Kh + t * L::PK + ch) = pack2(k0, k1);
-                    *reinterpret_cast<uint32_t*>(Qh + t * L::PK + ch) = pack2(q0, q1);
-                    kt_0 = k0;
-                    kt_1 = k1;
-                }
-                if (u & 1) {
-                    kt0[u >> 1] |= static_cast<uint32_t>(f32_to_bf16(kt_0)) << 16;
-                    kt1[u >> 1] |= static_cast<uint32_t>(f32_to_bf16(kt_1)) << 16;
-                } else {
-                    kt0[u >> 1] = f32_to_bf16(kt_0);
-                    kt1[u >> 1] = f32_to_bf16(kt_1);
+                    isP = true;
+                    const int y = x - 6;
+                    rt = y < 1 ? 0 : (y < 3 ? 1 : (y < 6 ? 2 : 3));
+                    ct = y - rt * (rt + 1) / 2;
                 }
             }
-#pragma unroll
-            for (int u = 0; u < L::TPT / 2; ++u) {
-                *reinterpret_cast<uint32_t*>(KtT + ch * L::PT + tlo + 2 * u) = kt0[u];
-                *reinterpret_cast<uint32_t*>(KtT + (ch + 1) * L::PT + tlo + 2 * u) = kt1[u];
-            }
-        }
-        __syncthreads();  // operands ready
-
-        // ---- A and P: 10 lower tiles each, 5 tiles per wave ------------------
-        for (int tix = wave; tix < 20; tix += 4) {
-            const bool isP = tix >= 10;
-            int rem2 = isP ? tix - 10 : tix, rt = 0;
-            while (rem2 > rt) { rem2 -= rt + 1; ++rt; }
-            const int ct = rem2;
             f32x4 acc = zero4();
-            mma_nt<KSTEPS>(acc, (isP ? Qh : Kh) + 16 * rt * L::PK, L::PK, Kc + 16 * ct * L::PK,
-                           L::PK, lane);
-            const int j = 16 * ct + lr;
+            const bf16_t* M = isP ? Qh : Kh;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                acc = mfma32(lds8(Kr + (16 * ct + lr) * L::PK + 32 * s + 8 * lg),
+                             lds8(M + (16 * rt + lr) * L::PK + 32 * s + 8 * lg), acc);
+            const int t = 16 * rt + lr;
+            const float bt = sb[t];
+            f32x4 val;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * rt + 4 * lg + i;
+                const int j = 16 * ct + 4 * lg + i;
                 float x = acc[i];
-                if constexpr (!KDA) x *= __expf(sGl[t] - sGl[j]);
-                if (isP) {
-                    Pb[t * L::PT + j] = f32_to_bf16(j <= t ? x : 0.f);
-                } else {
-                    Af[t * L::PF + j] = j < t ? sBeta[t] * x : 0.f;
-                }
+                if constexpr (!KDA) x *= exp2f(fminf(sG[t] - sG[j], 0.f));
+                val[i] = isP ? (j <= t ? x : 0.f) : (j < t ? bt * x : 0.f);
+            }
+            if (m == 0) {
+                *reinterpret_cast<float4*>(scr + lr * L::PS + 4 * lg) =
+                    make_float4(val[0], val[1], val[2], val[3]);
+            } else if (isP) {
+                st4(Pt + ptile(rt, ct) * 16 * L::PD + lr * L::PD + 4 * lg, val);
+            } else {
+                st4(At + atile(rt, ct) * 16 * L::PD + lr * L::PD + 4 * lg, -val);
             }
         }
-        __syncthreads();  // A in LDS
-
-        // ---- UT transform, level 0: diagonal blocks, one lane per column -----
+        // D_w^{-1} = (I + A_ww)^{-1}: lane c solves column c by forward substitution.
         if (lane < 16) {
-            const int base = 16 * wave;
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float acc = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc -= Af[(base + i) * L::PF + base + j] * x[j];
+                for (int j = 0; j < i; ++j) acc -= scr[i * L::PS + j] * x[j];
                 x[i] = acc;
             }
+            bf16_t* Dw = Dt + wave * 16 * L::PD;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                Tf[(base + i) * L::PF + base + lane] = x[i];
-                Tb[(base + i) * L::PT + base + lane] = f32_to_bf16(x[i]);
-            }
+            for (int i = 0; i < 16; ++i) Dw[i * L::PD + lane] = static_cast<bf16_t>(bf_bits(x[i]));
         }
-        __syncthreads();
-        // level 1a: Y0 = A_10 T_00 (wave 0), Y1 = A_32 T_22 (wave 1)
-        if (wave < 2) {
-            const int d = 32 * wave;
-            const f32x4 y = mm16_f32(Af + (d + 16) * L::PF + d, L::PF, Tf + d * L::PF + d, L::PF,
-                                     lane, zero4());
+    };
+
+    // ================= serial-wave work =================
+    const int sw = wave - kPrepWaves;
+    const int col0 = slice * DVS + 16 * sw;  // first value column of this wave
+    f32x4 S[NRT];
+    f32x4 Uf[4];
+    bf16x4 Ub[4];
+    bf16x8 bS[NKS];
+    const size_t sbase = static_cast<size_t>(bh) * DK * DV;
+    auto serial_vload = [&](int c, bf16_t (&V)[4][4]) {
+        const int t0 = c * kC, nn = min(kC, T - t0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Yf[(16 * wave + 4 * lg + i) * L::PY + lr] = y[i];
-        }
-        __syncthreads();
-        // level 1b: T_10 = -T_11 Y0, T_32 = -T_33 Y1
-        if (wave < 2) {
-            const int d = 32 * wave;
-            const f32x4 y = mm16_f32(Tf + (d + 16) * L::PF + d + 16, L::PF, Yf + 16 * wave * L::PY,
-                                     L::PY, lane, zero4());
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = d + 16 + 4 * lg + i, j = d + lr;
-                Tf[t * L::PF + j] = -y[i];
-                Tb[t * L::PT + j] = f32_to_bf16(-y[i]);
+                const int tc = min(16 * rt + 4 * lg + i, nn - 1);
+                V[rt][i] = v[((static_cast<size_t>(b) * T + t0 + tc) * H + h) * DV + col0 + lr];
+            }
+    };
+    // B operands of S for the K=32 steps over dk (KDA: scaled by 2^R per row).
+    auto build_bS = [&](int c) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            f32x4 lo = S[2 * s];
+            f32x4 hi = (2 * s + 1 < NRT) ? S[2 * s + 1] : zero4();
+            if constexpr (KDA) {
+                const float* sr = f32p(c, L::oSref);
+                const float4 f0 = *reinterpret_cast<const float4*>(sr + 32 * s + 4 * lg);
+                lo[0] *= f0.x; lo[1] *= f0.y; lo[2] *= f0.z; lo[3] *= f0.w;
+                if (2 * s + 1 < NRT) {
+                    const float4 f1 = *reinterpret_cast<const float4*>(sr + 32 * s + 16 + 4 * lg);
+                    hi[0] *= f1.x; hi[1] *= f1.y; hi[2] *= f1.z; hi[3] *= f1.w;
+                }
+            }
+            bS[s] = cat8(cvt4(lo), cvt4(hi));
+        }
+    };
+    // phase 1: Khat S -> X -> U (blocked forward substitution)
+    auto serial_a = [&](int c, const bf16_t (&V)[4][4]) {
+        build_bS(c);
+        const bf16_t* Kh = bfp(c, L::oKh);
+        const float* sb = f32p(c, L::oBeta);
+        const float* eg = f32p(c, L::oEg);
+        const bf16_t* At = bfp(c, L::oA);
+        const bf16_t* Dt = bfp(c, L::oD);
+        f32x4 X[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                acc = mfma32(lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg), bS[s], acc);
+            const float4 b4 = *reinterpret_cast<const float4*>(sb + 16 * rt + 4 * lg);
+            float4 e4 = make_float4(1.f, 1.f, 1.f, 1.f);
+            if constexpr (!KDA) e4 = *reinterpret_cast<const float4*>(eg + 16 * rt + 4 * lg);
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ee[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[rt][i] = bb[i] * (bf16_to_f32(V[rt][i]) - ee[i] * acc[i]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 w = X[rt];
+#pragma unroll
+            for (int kb = 0; kb < rt; ++kb)
+                w = mfma16(lds4(At + atile(rt, kb) * 16 * L::PD + lr * L::PD + 4 * lg), Ub[kb], w);
+            Uf[rt] = mfma16(lds4(Dt + rt * 16 * L::PD + lr * L::PD + 4 * lg), cvt4(w), zero4());
+            Ub[rt] = cvt4(Uf[rt]);
+        }
+    };
+    // phase 2: O = scale (Qhat S + P U) (computed transposed), and
+    // S <- diag(2^G_end) S + Ktil^T U
+    auto serial_b = [&](int c) {
+        const int t0 = c * kC, n = min(kC, T - t0);
+        const bf16_t* Qh = bfp(c, L::oQh);
+        const bf16_t* Pt = bfp(c, L::oP);
+        const bf16_t* Kt = bfp(c, L::oKt);
+        const float* eg = f32p(c, L::oEg);
+        const float* ek = f32p(c, L::oEk);
+        const float* ge = f32p(c, L::oGend);
+        const bf16x4 z4 = cvt4(zero4());
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            // O^T tile: rows = this wave's 16 value columns, columns = tokens 16 rt..
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                acc = mfma32(bS[s], lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg), acc);
+            if constexpr (!KDA) acc *= eg[16 * rt + lr];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (2 * s <= rt) {
+                    const bf16x4 plo = lds4(Pt + ptile(rt, 2 * s) * 16 * L::PD + lr * L::PD + 4 * lg);
+                    const bf16x4 phi = (2 * s + 1 <= rt)
+                        ? lds4(Pt + ptile(rt, 2 * s + 1) * 16 * L::PD + lr * L::PD + 4 * lg) : z4;
+                    acc = mfma32(cat8(Ub[2 * s], Ub[2 * s + 1]), cat8(plo, phi), acc);
+                }
+            }
+            const int t = 16 * rt + lr;
+            if (t < n)
+                st4(o + ((static_cast<size_t>(b) * T + t0 + t) * H + h) * DV + col0 + 4 * lg, acc * scale);
+        }
+        bf16x8 bU[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if constexpr (KDA) {
+                bU[s] = cat8(Ub[2 * s], Ub[2 * s + 1]);
+            } else {
+                const float4 k0 = *reinterpret_cast<const float4*>(ek + 32 * s + 4 * lg);
+                const float4 k1 = *reinterpret_cast<const float4*>(ek + 32 * s + 16 + 4 * lg);
+                f32x4 lo = Uf[2 * s], hi = Uf[2 * s + 1];
+                lo[0] *= k0.x; lo[1] *= k0.y; lo[2] *= k0.z; lo[3] *= k0.w;
+                hi[0] *= k1.x; hi[1] *= k1.y; hi[2] *= k1.z; hi[3] *= k1.w;
+                bU[s] = cat8(cvt4(lo), cvt4(hi));
             }
         }
-        __syncthreads();
-        // level 2a: Z_rc = sum_{kb=c..1} A_[2+r][kb] T_[kb][c]   (wave = 2 r + c)
-        {
-            const int r = wave >> 1, c = wave & 1;
-            f32x4 z = zero4();
-            for (int kb = c; kb < 2; ++kb)
-                z = mm16_f32(Af + (32 + 16 * r) * L::PF + 16 * kb, L::PF,
-                             Tf + 16 * kb * L::PF + 16 * c, L::PF, lane, z);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Yf[(16 * wave + 4 * lg + i) * L::PY + lr] = z[i];
+        for (int r = 0; r < NRT; ++r) {
+            if constexpr (KDA) {
+                const float4 g4 = *reinterpret_cast<const float4*>(ge + 16 * r + 4 * lg);
+                S[r][0] *= g4.x; S[r][1] *= g4.y; S[r][2] *= g4.z; S[r][3] *= g4.w;
+            } else {
+                S[r] *= ge[0];
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                S[r] = mfma32(lds_perm(Kt + (16 * r + lr) * L::PT + 32 * s + 4 * lg), bU[s], S[r]);
         }
-        __syncthreads();
-        // level 2b: T_[2+r][c] = -sum_{kb=0..r} T_[2+r][2+kb] Z_[kb][c]
-        {
-            const int r = wave >> 1, c = wave & 1;
-            f32x4 y = zero4();
-            for (int kb = 0; kb <= r; ++kb)
-                y = mm16_f32(Tf + (32 + 16 * r) * L::PF + 32 + 16 * kb, L::PF,
-                             Yf + 16 * (2 * kb + c) * L::PY, L::PY, lane, y);
+    };
+
+    // ================= pipeline =================
+    // Each role runs its own loop: nch + 1 iterations with exactly two
+    // workgroup barriers each, so the barriers pair up across roles while the
+    // compiler keeps only one role's loop-carried registers live.
+    if (prep) {
+        PrepIn pin;
+        if (nch > 0) prep_load(0, pin);
+        for (int i = -1; i < nch; ++i) {
+            if (i + 1 < nch) {
+                prep_gate(i + 1, pin);
+                if (i + 2 < nch) prep_load(i + 2, pin);  // in flight until the next iteration
+            }
+            lds_barrier();
+            if (i + 1 < nch) prep_ap(i + 1);
+            lds_barrier();
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < NRT; ++r) {
+            S[r] = zero4();
+            if (state_in) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[r][i] = state_in[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr];
+            }
+        }
+        bf16_t vin[4][4];
+        if (nch > 0) serial_vload(0, vin);
+        for (int i = -1; i < nch; ++i) {
+            if (i >= 0) {
+                serial_a(i, vin);
+                if (i + 1 < nch) serial_vload(i + 1, vin);  // in flight until the next iteration
+            }
+            lds_barrier();
+            if (i >= 0) serial_b(i);
+            lds_barrier();
+        }
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                Tb[(32 + 16 * r + 4 * lg + i) * L::PT + 16 * c + lr] = f32_to_bf16(-y[i]);
-        }
-        __syncthreads();  // T complete; solve scratch is dead from here
-
-        // ---- S (fp32 accumulators) -> bf16 S^T in LDS -------------------------
-#pragma unroll
-        for (int m = 0; m < MST; ++m) {
-            const int s = wave + 4 * m;
-            if (s < NST) {
-                const int rt = s / NCT, ct = s % NCT;
-                float x[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[i] = S[m][i];
-                    if constexpr (KDA) x[i] *= sGref[16 * rt + 4 * lg + i];
-                }
-                uint2 w;
-                w.x = pack2(x[0], x[1]);
-                w.y = pack2(x[2], x[3]);
-                *reinterpret_cast<uint2*>(St + (16 * ct + lr) * L::PK + 16 * rt + 4 * lg) = w;
-            }
-        }
-        if constexpr (L::DKP != DK) {
-            for (int idx = tid; idx < DVS * (L::DKP - DK); idx += kThreads)
-                St[(idx / (L::DKP - DK)) * L::PK + DK + idx % (L::DKP - DK)] = 0;
-        }
-        __syncthreads();
-
-        // ---- Khat S -> X = diag(beta)(V - Khat S); Qhat S kept in registers --
-        f32x4 Oacc[NCT];
-        {
-            const int t_base = 16 * wave + 4 * lg;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 ak = zero4(), aq = zero4();
-                mma_nt<KSTEPS>(ak, Kh + 16 * wave * L::PK, L::PK, St + 16 * ct * L::PK, L::PK, lane);
-                mma_nt<KSTEPS>(aq, Qh + 16 * wave * L::PK, L::PK, St + 16 * ct * L::PK, L::PK, lane);
-                float x[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = t_base + i;
-                    float kS = ak[i], qS = aq[i];
-                    if constexpr (!KDA) {
-                        const float e = __expf(sGl[t]);
-                        kS *= e;
-                        qS *= e;
-                    }
-                    aq[i] = qS;
-                    float vv = 0.f;
-                    if (t < n)
-                        vv = bf16_to_f32(v[((static_cast<size_t>(b) * T + t0 + t) * H + h) * DV + c0 +
-                                           16 * ct + lr]);
-                    x[i] = sBeta[t] * (vv - kS);
-                }
-                Oacc[ct] = aq;
-                uint2 w;
-                w.x = pack2(x[0], x[1]);
-                w.y = pack2(x[2], x[3]);
-                *reinterpret_cast<uint2*>(Xt + (16 * ct + lr) * L::PT + t_base) = w;
-            }
-        }
-        __syncthreads();
-
-        // ---- U = T X ------------------------------------------------------------
-        const int tsteps = wave < 2 ? 1 : 2;  // T is lower triangular
-        {
-            const int t_base = 16 * wave + 4 * lg;
-            const float gl_end = KDA ? 0.f : sGl[kC - 1];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 u = zero4();
-                mma_nt_dyn(u, Tb + 16 * wave * L::PT, L::PT, Xt + 16 * ct * L::PT, L::PT, lane, tsteps);
-                uint2 w;
-                w.x = pack2(u[0], u[1]);
-                w.y = pack2(u[2], u[3]);
-                *reinterpret_cast<uint2*>(Ut + (16 * ct + lr) * L::PT + t_base) = w;
-                if constexpr (!KDA) {
-                    float y[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) y[i] = u[i] * __expf(gl_end - sGl[t_base + i]);
-                    w.x = pack2(y[0], y[1]);
-                    w.y = pack2(y[2], y[3]);
-                    *reinterpret_cast<uint2*>(U2t + (16 * ct + lr) * L::PT + t_base) = w;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- O = scale (Qhat S + P U) -------------------------------------------
-        {
-            const int t_base = 16 * wave + 4 * lg;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                mma_nt_dyn(Oacc[ct], Pb + 16 * wave * L::PT, L::PT, Ut + 16 * ct * L::PT, L::PT, lane,
-                           tsteps);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = t_base + i;
-                    if (t < n)
-                        o[((static_cast<size_t>(b) * T + t0 + t) * H + h) * DV + c0 + 16 * ct + lr] =
-                            f32_to_bf16(scale * Oacc[ct][i]);
-                }
-            }
-        }
-        // ---- S <- diag(exp(G_end)) S + Ktil^T U ----------------------------------
-#pragma unroll
-        for (int m = 0; m < MST; ++m) {
-            const int s = wave + 4 * m;
-            if (s < NST) {
-                const int rt = s / NCT, ct = s % NCT;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[m][i] *= sGend[KDA ? 16 * rt + 4 * lg + i : 0];
-                mma_nt<2>(S[m], KtT + 16 * rt * L::PT, L::PT, U2t + 16 * ct * L::PT, L::PT, lane);
-            }
-        }
-    }
-
-#pragma unroll
-    for (int m = 0; m < MST; ++m) {
-        const int s = wave + 4 * m;
-        if (s < NST) {
-            const int rt = s / NCT, ct = s % NCT;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                state_out[sbase + static_cast<size_t>(16 * rt + 4 * lg + i) * DV + c0 + 16 * ct + lr] =
-                    S[m][i];
-        }
+                state_out[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr] = S[r][i];
     }
 }
 
-template <int DK, int DVS, bool KDA>
+template <int DK, int NSW, bool KDA>
 hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, const bf16_t* k,
                   const bf16_t* v, const float* alpha, const float* beta, const float* s_in,
                   float* s_out, bf16_t* o, hipStream_t s) {
-    using L = Layout<DK, DVS, KDA>;
-    auto kern = prefill_bf16_kernel<DK, DVS, KDA>;
+    using L = Layout<DK, NSW, KDA>;
+    auto kern = prefill_bf16_kernel<DK, NSW, KDA>;
     if (L::bytes > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
         if (e != hipSuccess) return e;
     }
-    const int NS = DV / DVS;
+    const int NS = DV / (16 * NSW);
     const int groups = (B * H + 7) / 8;
     const unsigned blocks = static_cast<unsigned>(groups) * 8u * static_cast<unsigned>(NS);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), L::bytes, s, B, T, H, DV, NS, scale, q,
-                       k, v, alpha, beta, s_in, s_out, o);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (kPrepWaves + NSW)), L::bytes, s, B, T, H, DV,
+                       NS, scale, q, k, v, alpha, beta, s_in, s_out, o);
     return hipGetLastError();
 }
 
@@ -550,9 +579,9 @@ hipError_t dispatch_dvs(int dvs, int B, int T, int H, int DV, float scale, const
                         const bf16_t* k, const bf16_t* v, const float* alpha, const float* beta,
                         const float* s_in, float* s_out, bf16_t* o, hipStream_t s) {
     switch (dvs) {
-        case 16: return launch<DK, 16, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
-        case 32: return launch<DK, 32, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
-        default: return launch<DK, 64, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
+        case 16: return launch<DK, 1, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
+        case 32: return launch<DK, 2, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
+        default: return launch<DK, 4, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
     }
 }
 
@@ -567,9 +596,9 @@ hipError_t dispatch_gate(int kda, int dvs, int B, int T, int H, int DV, float sc
 
 }  // namespace
 
-// Value-column slice width: at most 64 columns (LDS budget), and heads are
-// split further until the grid covers the 256 CUs (the slices are exact:
-// columns of S never interact), down to 16 columns.
+// Value-column slice width per workgroup: at most 64 columns (four serial
+// waves), and heads are split further until the grid covers the 256 CUs
+// (exact: columns of S never interact), down to 16 columns.
 int prefill_bf16_slice_width(int B, int H, int dv) {
     int ns = dv > 64 ? dv / 64 : 1;
     while (static_cast<long long>(B) * H * ns < 256 && dv / ns > 16) ns *= 2;
