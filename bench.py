@@ -12,9 +12,11 @@ Also measured in the same run (under ``workloads``): KDA decode (B=256,
 20 in-place steps), GDN chunked prefill (B=4, T=8192) and KDA chunked
 prefill (B=1, T=32768), each with its roofline fractions.
 
-Roofline: algorithmic bytes (or flops) per launch divided by the average
-launch duration, measured with HIP events recorded around every launch on the
-stream the kernel runs on.  ``cpu_baseline`` times the float64 CPU oracle on a
+The headline step is captured once as a HIP graph (48 kernel launches) and
+replayed, so the timed region holds GPU work only.  Roofline: algorithmic
+bytes (or flops) per launch divided by the average launch duration, from HIP
+events recorded around the timed region on the stream the kernels run on
+(GPU time / launches in the region).  ``cpu_baseline`` times the float64 CPU oracle on a
 bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
@@ -86,35 +88,52 @@ def load_traffic(kernel_key, sha):
     return None
 
 
-class LaunchTimer:
-    """HIP events around every launch on the current stream."""
+def c_decode_call(torch, gdr, gate, d, scale=1.0):
+    """A zero-argument callable that enqueues one gdr_decode_step through the C
+    ABI with pre-marshalled pointers on the current stream (no per-call Python
+    checks, so the host stays ahead of the GPU)."""
+    import ctypes
+    lib = gdr.load_library()
+    B, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    dtype = 1 if d["q"].dtype == torch.bfloat16 else 0
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (gdr.GATES[gate], dtype, B, H, dk, dv, ctypes.c_float(scale), ptr(d["q"]), ptr(d["k"]),
+            ptr(d["v"]), ptr(d["alpha"]), ptr(d["beta"]), ptr(d["state"]), ptr(d["o"]))
 
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
+    def call():
+        st = lib.gdr_decode_step(*args, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(gdr.gdr_status_string(st))
+    return call
 
-    def __call__(self, fn):
-        t = self.torch
-        a = t.cuda.Event(enable_timing=True)
-        b = t.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        self.pairs.append((a, b))
 
-    def mean_ms(self):
-        self.torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else 0.0
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of nbytes (read + write), for context."""
+    a = torch.empty(nbytes // 4, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    _, dt = timed_region(torch, reps, lambda: b.copy_(a))
+    del a, b
+    return 2 * nbytes * reps / dt / 1e9
 
 
 def timed_region(torch, steps, body):
-    """Barrier + synchronize on both sides of exactly `steps` calls to body()."""
+    """Synchronize on both sides of exactly `steps` calls to body(); returns
+    (wall seconds, GPU seconds between HIP events recorded on the current
+    stream -- the stream every launch goes to -- around the region)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     for _ in range(steps):
         body()
+    e1.record()
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) / 1e3
 
 
 def bench_gdn_decode(torch, gdr, synth, steps, warmup, want_cpu):
@@ -133,22 +152,29 @@ def bench_gdn_decode(torch, gdr, synth, steps, warmup, want_cpu):
         d["o"] = torch.empty(B, H, dv, device="cuda", dtype=torch.bfloat16)
         layers.append(d)
 
-    def step(timer=None):
-        for d in layers:
-            call = lambda d=d: gdr.gdr_decode_step("gdn", d["q"], d["k"], d["v"], d["alpha"],
-                                                    d["beta"], d["state"], d["o"])
-            if timer is None:
-                call()
-            else:
-                timer(call)
+    calls = [c_decode_call(torch, gdr, "gdn", d) for d in layers]
 
+    def step():
+        for c in calls:
+            c()
+
+    # One step (48 launches) captured as a HIP graph and replayed: the
+    # timed region is GPU work only, with no host launch gaps.
     for _ in range(warmup):
         step()
-    elapsed = timed_region(torch, steps, step)
-    timer = LaunchTimer(torch)
-    for _ in range(max(1, min(steps, 4))):
-        step(timer)
-    launch_ms = timer.mean_ms()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(2):
+        graph.replay()
+    elapsed, gpu_s = timed_region(torch, steps, graph.replay)
+    launch_ms = 1e3 * gpu_s / (steps * L)
     per_launch = B * H * decode_bytes_per_head("gdn", dk, dv)
     step_bytes = per_launch * L
     res = {
@@ -202,21 +228,19 @@ def bench_kda_decode(torch, gdr, synth, steps, warmup):
     d = {k: torch.from_numpy(np.ascontiguousarray(inp[k][:, 0])).to(
         torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()
         for k in ("q", "k", "v", "alpha", "beta")}
-    o = torch.empty(B, H, dv, device="cuda", dtype=torch.bfloat16)
-    call = lambda: gdr.gdr_decode_step("kda", d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                       state, o)
+    d["state"] = state
+    d["o"] = torch.empty(B, H, dv, device="cuda", dtype=torch.bfloat16)
+    call = c_decode_call(torch, gdr, "kda", d)
     for _ in range(warmup):
         call()
     n = max(steps, 20)
-    elapsed = timed_region(torch, n, call)
-    timer = LaunchTimer(torch)
-    for _ in range(n):
-        timer(call)
-    launch_ms = timer.mean_ms()
+    elapsed, gpu_s = timed_region(torch, n, call)
+    launch_ms = 1e3 * gpu_s / n
     per_launch = B * H * decode_bytes_per_head("kda", dk, dv)
     return {"workload": w.name, "steps": n, "ms_per_step": 1e3 * elapsed / n,
             "gbs": per_launch * n / elapsed / 1e9, "tokens_per_s": B * n / elapsed,
-            "roofline": roofline_hbm(per_launch, launch_ms)}
+            "roofline": roofline_hbm(per_launch, launch_ms,
+                                     load_traffic("decode_kda", src_hash("decode.hip")))}
 
 
 def bench_prefill(torch, gdr, synth, name, steps, warmup):
@@ -232,11 +256,8 @@ def bench_prefill(torch, gdr, synth, name, steps, warmup):
                                          d["s0"], s_out, o)
     for _ in range(warmup):
         call()
-    elapsed = timed_region(torch, steps, call)
-    timer = LaunchTimer(torch)
-    for _ in range(steps):
-        timer(call)
-    launch_ms = timer.mean_ms()
+    elapsed, gpu_s = timed_region(torch, steps, call)
+    launch_ms = 1e3 * gpu_s / steps
     nbytes = prefill_bytes(w.gate, B, T, H, dk, dv, d["s0"] is not None)
     flops = prefill_flops(B, T, H, dk, dv)
     sec = launch_ms / 1e3
@@ -268,7 +289,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None,
-                    help="gdn_decode | kda_decode | gdn_prefill | kda_prefill")
+                    help="gdn_decode | kda_decode | gdn_prefill | kda_prefill | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -288,6 +309,10 @@ def main():
         sys.exit(3)
 
     only = args.only
+    if only == "copy":  # plain copy kernel of known size, for counter calibration
+        print(json.dumps({"copy_gbs_measured": round(copy_bandwidth(torch), 1),
+                          "bytes_per_copy": 1 << 30}))
+        return
     extra = {}
     head = None
     if only in (None, "gdn_decode"):
@@ -327,6 +352,8 @@ def main():
     }
     if "cpu" in head:
         line["cpu_baseline"] = head["cpu"]
+    line["context"] = {"copy_gbs_measured": round(copy_bandwidth(torch), 1),
+                       "note": "device-to-device copy of 1 GiB on the same GPU, same run"}
     if extra:
         line["workloads"] = extra
     print(json.dumps(line))

@@ -111,3 +111,39 @@ def test_decode_deterministic():
     a = _run_decode("kda", "bf16", inp)
     b = _run_decode("kda", "bf16", inp)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_decode_graph_replays_match_eager():
+    """A decode step captured in a HIP graph, replayed several times with eager
+    work and synchronisations in between; every replay matches eager steps."""
+    w = synth.WORKLOADS["gdn_decode_b64_h32_d128"]
+    inp = _decode_inputs(w, B=8, H=32)
+    dev = {k: to_dev(v, "bf16" if k in ("q", "k", "v") else "f32") for k, v in inp.items()}
+    B, H, dv = inp["v"].shape
+    s_graph = dev["s0"].clone()
+    s_eager = dev["s0"].clone()
+    o_graph = torch.empty(B, H, dv, device="cuda", dtype=torch.bfloat16)
+    o_eager = torch.empty_like(o_graph)
+    step = lambda st, o: gdr.gdr_decode_step("gdn", dev["q"], dev["k"], dev["v"], dev["alpha"],
+                                             dev["beta"], st, o)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        warm = dev["s0"].clone()
+        step(warm, torch.empty_like(o_graph))
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(s_graph, o_graph)
+    # capture does not execute: restore the starting state
+    s_graph.copy_(dev["s0"])
+    announce("decode graph replays")
+    for rep in range(4):
+        g.replay()
+        step(s_eager, o_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph, o_eager), rep
+        assert torch.equal(s_graph, s_eager), rep
+        junk = torch.randn(1024, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del junk
