@@ -44,6 +44,8 @@
 // K=32 step whose k order is {4g..4g+3, 16+4g..16+4g+3}; the LDS operand of
 // that step is read in the same k order, which keeps every product exact
 // without any register shuffle.
+#include <type_traits>
+
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -57,7 +59,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;                 // chunk
 constexpr int kPrepWaves = 4;
-constexpr float kLog2Floor = -115.4f;  // log2(alpha) floor, alpha ~ e^-80
+constexpr float kLog2Floor = -115.4f;  // GDN: log2(alpha) floor, alpha ~ e^-80
+constexpr float kMinGate = 3.7252903e-09f;  // KDA: alpha floor 2^-28 (4-token products stay normal)
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
 // but leaves global loads in flight (a full __syncthreads also drains vmcnt,
@@ -99,7 +102,18 @@ __device__ __forceinline__ void st4(bf16_t* p, const f32x4& x) {
 __device__ __forceinline__ uint32_t bf_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
+// Hardware 2^x and log2 (v_exp_f32 / v_log_f32).  Every exponent here is a
+// difference of cumulative log-gates bounded by the chunk's total decay, so
+// the plain instructions suffice (results below 2^-126 may flush to zero,
+// which is the intended limit of a vanishing decay).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+// 16-bit element e (0..7) of eight packed bf16
+__device__ __forceinline__ uint32_t bf16_half(const uint4& w, int e) {
+    const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+    return (e & 1) ? (x >> 16) : (x & 0xffffu);
+}
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <int DK, int NSW, bool KDA>
@@ -109,10 +123,6 @@ struct Layout {
     static constexpr int PT = kC + 4;              // pitch of [channel][token] tiles (bf16)
     static constexpr int PD = 16 + 8;              // pitch of packed 16x16 tiles (bf16)
     static constexpr int TILE = 16 * PD * 2;       // bytes of one packed tile
-    static constexpr int NPAIR = DK / 2;           // channel pairs
-    static constexpr int TPP = 256 / NPAIR;        // lanes per pair (one wave segment)
-    static constexpr int PPW = 64 / TPP;           // pairs per prep wave
-    static constexpr int TPT = kC / TPP;           // tokens per lane
     // one chunk buffer (byte offsets)
     static constexpr int oKh = 0;                         // Khat [64][PK]
     static constexpr int oQh = oKh + kC * PK * 2;         // Qhat [64][PK]
@@ -133,7 +143,6 @@ struct Layout {
     static constexpr int oScr = oG + kC * 4;              // fp32 diagonal tiles [4][16][PS]
     static constexpr int bytes = oScr + kPrepWaves * 16 * PS * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
-    static_assert(TPT >= 2 && TPT % 2 == 0 && TPP <= 64, "token split");
 };
 
 __device__ __forceinline__ int ptile(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }  // ct <= rt
@@ -149,7 +158,6 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     constexpr int DVS = 16 * NSW;
     constexpr int NRT = DK / 16;          // 16-row tiles of S
     constexpr int NKS = L::DKP / 32;      // K=32 steps over dk
-    constexpr int TPT = L::TPT;
 
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
@@ -184,132 +192,177 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     }
 
     // ================= prep-wave work =================
-    const int pl = lane / L::TPP, tg = lane % L::TPP;
-    const int ch = 2 * (wave * L::PPW + pl);
-    const int tlo = tg * TPT;
+    // Gating layout: lane = (channel octet o, run of 4 tokens tg); the 16
+    // lanes of an octet are one DPP row, so the chunk's cumulative sum is an
+    // in-row scan.  Loads and LDS writes are 16 bytes (8 channels).
+    const int oct = tid >> 4, tg = tid & 15;
+    const bool gater = tid < 2 * DK;  // DK/8 octets x 16 lanes
+    const int c8 = 8 * oct;           // first channel of this lane's octet
+    constexpr int NA = KDA ? 32 : 4;  // gate values per lane
     struct PrepIn {
-        float a0[TPT], a1[TPT], bt[TPT];
-        uint32_t kw[TPT], qw[TPT];
+        uint4 kr[4], qr[4];
+        float a[NA];
+        float bt[4];
     };
+    const size_t tok0 = static_cast<size_t>(b) * T * H + h;  // token (b, 0, h)
     auto prep_load = [&](int c, PrepIn& R) {
         const int t0 = c * kC, nn = min(kC, T - t0);
+        const size_t rb = tok0 + static_cast<size_t>(t0) * H;  // row of token t0 (uniform)
+        const bf16_t* kb = k + rb * DK;
+        const bf16_t* qb = q + rb * DK;
+        const float* ab = KDA ? alpha + rb * DK : alpha + rb;
+        const float* bb = beta + rb;
 #pragma unroll
-        for (int u = 0; u < TPT; ++u) {
-            const int tc = min(tlo + u, nn - 1);
-            const size_t gi = (static_cast<size_t>(b) * T + t0 + tc) * H + h;
+        for (int u = 0; u < 4; ++u) {
+            const int tc = nn == kC ? 4 * tg + u : min(4 * tg + u, nn - 1);
+            const unsigned ro = static_cast<unsigned>(tc * H);  // row offset inside the chunk
+            R.kr[u] = *reinterpret_cast<const uint4*>(kb + (ro * DK + c8));
+            R.qr[u] = *reinterpret_cast<const uint4*>(qb + (ro * DK + c8));
             if constexpr (KDA) {
-                const float2 a2 = *reinterpret_cast<const float2*>(alpha + gi * DK + ch);
-                R.a0[u] = a2.x;
-                R.a1[u] = a2.y;
+                const float4 x0 = *reinterpret_cast<const float4*>(ab + (ro * DK + c8));
+                const float4 x1 = *reinterpret_cast<const float4*>(ab + (ro * DK + c8 + 4));
+                R.a[8 * u + 0] = x0.x; R.a[8 * u + 1] = x0.y; R.a[8 * u + 2] = x0.z; R.a[8 * u + 3] = x0.w;
+                R.a[8 * u + 4] = x1.x; R.a[8 * u + 5] = x1.y; R.a[8 * u + 6] = x1.z; R.a[8 * u + 7] = x1.w;
             } else {
-                R.a0[u] = R.a1[u] = alpha[gi];
+                R.a[u] = ab[ro];
             }
-            R.bt[u] = beta[gi];
-            R.kw[u] = *reinterpret_cast<const uint32_t*>(k + gi * DK + ch);
-            R.qw[u] = *reinterpret_cast<const uint32_t*>(q + gi * DK + ch);
+            R.bt[u] = bb[ro];
         }
     };
+    // inclusive scan over the 16 lanes of a DPP row (row_shr by 1, 2, 4, 8)
+    auto row_scan = [](float x) {
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+        return x;
+    };
+    auto bf_at = [](const uint4& w, int e) {  // element e of 8 packed bf16
+        const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+        return (e & 1) ? bf_hi(x) : bf_lo(x);
+    };
 
-    // Gates and gated operands of chunk c into buffer c & 1.  Lane = (channel
-    // pair, run of TPT tokens); the TPP lanes of a pair are one wave segment,
-    // so the cumulative sum over the chunk is an in-wave scan.
+    // Gates and gated operands of chunk c into buffer c & 1.
     auto prep_gate = [&](int c, const PrepIn& R) {
         const int n = min(kC, T - c * kC);
-        float g0[TPT], g1[TPT];
-        float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int u = 0; u < TPT; ++u) {
-            const bool valid = tlo + u < n;
-            const float l0 = valid ? fmaxf(__log2f(R.a0[u]), kLog2Floor) : 0.f;
-            const float l1 = KDA ? (valid ? fmaxf(__log2f(R.a1[u]), kLog2Floor) : 0.f) : l0;
-            acc0 += l0;
-            acc1 += l1;
-            g0[u] = acc0;
-            g1[u] = acc1;
-        }
-        float inc0 = acc0, inc1 = acc1;
-#pragma unroll
-        for (int d = 1; d < L::TPP; d <<= 1) {
-            const float y0 = __shfl_up(inc0, d, L::TPP), y1 = __shfl_up(inc1, d, L::TPP);
-            if (tg >= d) { inc0 += y0; inc1 += y1; }
-        }
-        const float off0 = inc0 - acc0, off1 = inc1 - acc1;
-        const float end0 = __shfl(inc0, L::TPP - 1, L::TPP), end1 = __shfl(inc1, L::TPP - 1, L::TPP);
         bf16_t* Kh = bfp(c, L::oKh);
         bf16_t* Qh = bfp(c, L::oQh);
         bf16_t* Kt = bfp(c, L::oKt);
-        const bool lead = (wave == 0 && pl == 0);  // one pair writes the per-token vectors
-        if (lead) {
-            float* sb = f32p(c, L::oBeta);
+        if (!gater) return;
+        // a full chunk (every chunk but a ragged last one) needs no row masks
+        auto body = [&](auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            bool valid[4];
 #pragma unroll
-            for (int u = 0; u < TPT; ++u) sb[tlo + u] = tlo + u < n ? R.bt[u] : 0.f;
-        }
-        uint32_t kt0[TPT / 2], kt1[TPT / 2];
-        if constexpr (KDA) {
-            const float ref0 = 0.5f * end0, ref1 = 0.5f * end1;
-            const float ce0 = exp2f(end0 - ref0), ce1 = exp2f(end1 - ref1);
-            if (tg == 0) {
-                f32p(c, L::oGend)[ch] = exp2f(end0);
-                f32p(c, L::oGend)[ch + 1] = exp2f(end1);
-                f32p(c, L::oSref)[ch] = exp2f(ref0);
-                f32p(c, L::oSref)[ch + 1] = exp2f(ref1);
+            for (int u = 0; u < 4; ++u) valid[u] = FULL || 4 * tg + u < n;
+            if (oct == 0) {
+                float4 b4;
+                b4.x = valid[0] ? R.bt[0] : 0.f; b4.y = valid[1] ? R.bt[1] : 0.f;
+                b4.z = valid[2] ? R.bt[2] : 0.f; b4.w = valid[3] ? R.bt[3] : 0.f;
+                *reinterpret_cast<float4*>(f32p(c, L::oBeta) + 4 * tg) = b4;
             }
+            uint4 kz[4], qz[4];
 #pragma unroll
-            for (int u = 0; u < TPT; ++u) {
-                const int t = tlo + u;
-                const bool valid = t < n;
-                const uint32_t kw = valid ? R.kw[u] : 0u, qw = valid ? R.qw[u] : 0u;
-                const float k0 = bf_lo(kw), k1 = bf_hi(kw), q0 = bf_lo(qw), q1 = bf_hi(qw);
-                const float up0 = exp2f(off0 + g0[u] - ref0), up1 = exp2f(off1 + g1[u] - ref1);
-                const float dn0 = __builtin_amdgcn_rcpf(up0), dn1 = __builtin_amdgcn_rcpf(up1);
-                bf16x2 x;
-                x[0] = static_cast<__bf16>(k0 * up0);
-                x[1] = static_cast<__bf16>(k1 * up1);
-                *reinterpret_cast<bf16x2*>(Kh + t * L::PK + ch) = x;
-                x[0] = static_cast<__bf16>(q0 * up0);
-                x[1] = static_cast<__bf16>(q1 * up1);
-                *reinterpret_cast<bf16x2*>(Qh + t * L::PK + ch) = x;
-                x[0] = static_cast<__bf16>(k0 * dn0);
-                x[1] = static_cast<__bf16>(k1 * dn1);
-                *reinterpret_cast<bf16x2*>(Kc + t * L::PK + ch) = x;
-                const uint32_t b0 = bf_bits(k0 * dn0 * ce0), b1 = bf_bits(k1 * dn1 * ce1);
-                if (u & 1) { kt0[u >> 1] |= b0 << 16; kt1[u >> 1] |= b1 << 16; }
-                else { kt0[u >> 1] = b0; kt1[u >> 1] = b1; }
+            for (int u = 0; u < 4; ++u) {
+                kz[u] = valid[u] ? R.kr[u] : make_uint4(0, 0, 0, 0);
+                qz[u] = valid[u] ? R.qr[u] : make_uint4(0, 0, 0, 0);
             }
-        } else {
-            if (lead) {
-                float* eg = f32p(c, L::oEg);
-                float* ek = f32p(c, L::oEk);
+            if constexpr (KDA) {
+                // Pass 1, per channel: product of this lane's 4 gates, its log2
+                // scanned across the 16 lanes, and the lane's base factor
+                // 2^(off - R) with R = G_end / 2.  Pass 2 walks the tokens with
+                // a running product (2^(G_t - R)) and writes each row at once.
+                float run[8], ce[8];
 #pragma unroll
-                for (int u = 0; u < TPT; ++u) {
-                    const float G = off0 + g0[u];
-                    sG[tlo + u] = G;
-                    eg[tlo + u] = exp2f(G);
-                    ek[tlo + u] = exp2f(end0 - G);
+                for (int e = 0; e < 8; ++e) {
+                    float p = 1.f;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) p *= valid[u] ? fmaxf(R.a[8 * u + e], kMinGate) : 1.f;
+                    const float tot = lg2(p);
+                    const float inc = row_scan(tot);
+                    const float end = __shfl(inc, 15, 16);
+                    run[e] = ex2(inc - tot - 0.5f * end);
+                    ce[e] = ex2(0.5f * end);  // 2^(G_end - R) = 2^R
+                    if (tg == 0) {
+                        f32p(c, L::oGend)[c8 + e] = ex2(end);
+                        f32p(c, L::oSref)[c8 + e] = ce[e];
+                    }
                 }
-                if (tg == 0) f32p(c, L::oGend)[0] = exp2f(end0);
-            }
+                uint32_t ktw[8][2];
 #pragma unroll
-            for (int u = 0; u < TPT; ++u) {
-                const int t = tlo + u;
-                const bool valid = t < n;
-                const uint32_t kw = valid ? R.kw[u] : 0u, qw = valid ? R.qw[u] : 0u;
-                *reinterpret_cast<uint32_t*>(Kh + t * L::PK + ch) = kw;
-                *reinterpret_cast<uint32_t*>(Qh + t * L::PK + ch) = qw;
-                if (u & 1) { kt0[u >> 1] |= kw << 16; kt1[u >> 1] |= kw & 0xffff0000u; }
-                else { kt0[u >> 1] = kw & 0xffffu; kt1[u >> 1] = kw >> 16; }
-            }
-        }
+                for (int u = 0; u < 4; ++u) {
+                    const int t = 4 * tg + u;
+                    bf16x8 kh, qh, kc;
 #pragma unroll
-        for (int u = 0; u < TPT / 2; ++u) {
-            *reinterpret_cast<uint32_t*>(Kt + ch * L::PT + tlo + 2 * u) = kt0[u];
-            *reinterpret_cast<uint32_t*>(Kt + (ch + 1) * L::PT + tlo + 2 * u) = kt1[u];
-        }
+                    for (int e = 0; e < 8; ++e) {
+                        run[e] *= valid[u] ? fmaxf(R.a[8 * u + e], kMinGate) : 1.f;  // 2^(G_t - R)
+                        const float kv = bf_at(kz[u], e), qv = bf_at(qz[u], e);
+                        const float dn = __builtin_amdgcn_rcpf(run[e]);
+                        kh[e] = static_cast<__bf16>(kv * run[e]);
+                        qh[e] = static_cast<__bf16>(qv * run[e]);
+                        const float kcv = kv * dn;
+                        kc[e] = static_cast<__bf16>(kcv);
+                        const uint32_t kt = bf_bits(kcv * ce[e]);
+                        if (u & 1) ktw[e][u >> 1] |= kt << 16;
+                        else ktw[e][u >> 1] = kt;
+                    }
+                    *reinterpret_cast<bf16x8*>(Kh + t * L::PK + c8) = kh;
+                    *reinterpret_cast<bf16x8*>(Qh + t * L::PK + c8) = qh;
+                    *reinterpret_cast<bf16x8*>(Kc + t * L::PK + c8) = kc;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<uint2*>(Kt + (c8 + e) * L::PT + 4 * tg) = make_uint2(ktw[e][0], ktw[e][1]);
+            } else {
+                float acc = 0.f, G[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    acc += valid[u] ? fmaxf(lg2(R.a[u]), kLog2Floor) : 0.f;
+                    G[u] = acc;
+                }
+                const float inc = row_scan(acc);
+                const float off = inc - acc;
+                const float end = __shfl(inc, 15, 16);
+                if (oct == 0) {
+                    float4 g4, e4, k4;
+                    g4.x = off + G[0]; g4.y = off + G[1]; g4.z = off + G[2]; g4.w = off + G[3];
+                    e4.x = ex2(g4.x); e4.y = ex2(g4.y); e4.z = ex2(g4.z); e4.w = ex2(g4.w);
+                    k4.x = ex2(end - g4.x); k4.y = ex2(end - g4.y);
+                    k4.z = ex2(end - g4.z); k4.w = ex2(end - g4.w);
+                    *reinterpret_cast<float4*>(sG + 4 * tg) = g4;
+                    *reinterpret_cast<float4*>(f32p(c, L::oEg) + 4 * tg) = e4;
+                    *reinterpret_cast<float4*>(f32p(c, L::oEk) + 4 * tg) = k4;
+                    if (tg == 0) f32p(c, L::oGend)[0] = ex2(end);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int t = 4 * tg + u;
+                    *reinterpret_cast<uint4*>(Kh + t * L::PK + c8) = kz[u];
+                    *reinterpret_cast<uint4*>(Qh + t * L::PK + c8) = qz[u];
+                }
+                // K^T: channel c8 + e, tokens 4 tg .. 4 tg + 3
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t x0 = bf16_half(kz[0], e), x1 = bf16_half(kz[1], e);
+                    const uint32_t x2 = bf16_half(kz[2], e), x3 = bf16_half(kz[3], e);
+                    *reinterpret_cast<uint2*>(Kt + (c8 + e) * L::PT + 4 * tg) =
+                        make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
+                }
+            }
+    
+        };
+        if (n == kC) body(std::true_type{});
+        else body(std::false_type{});
     };
 
     // A, P and the diagonal-block inverses of chunk c (buffer c & 1).  The
     // tile products run transposed, C^T = Kr M^T, so a lane ends up with 4
-    // consecutive j of one row t and stores 8 bytes.
+    // consecutive j of one row t and stores 8 bytes.  Tiles per wave (row
+    // tile rt of M = Khat for A, Qhat for P; column tiles ct <= rt of Kr):
+    //   wave 0: A rows 3 and 0;  wave 1: P rows 3 and 0;
+    //   wave 2: A rows 2 and 1;  wave 3: P rows 2 and 1     (5 tiles each),
+    // so each K step loads the Kr fragments once for both rows.  Waves 0 and
+    // 2 hold the diagonal A tiles and invert them, two blocks per wave.
     auto prep_ap = [&](int c) {
         const bf16_t* Kh = bfp(c, L::oKh);
         const bf16_t* Qh = bfp(c, L::oQh);
@@ -318,67 +371,85 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
         bf16_t* Pt = bfp(c, L::oP);
         bf16_t* At = bfp(c, L::oA);
         bf16_t* Dt = bfp(c, L::oD);
-        float* scr = reinterpret_cast<float*>(smem + L::oScr) + wave * 16 * L::PS;
-        // tile 0: this wave's diagonal A tile; then 4 of the 16 others
-        // (6 off-diagonal A tiles, then 10 P tiles), round-robin over waves
+        float* scr0 = reinterpret_cast<float*>(smem + L::oScr);
+        const bool isP = wave & 1;
+        const int rA = wave < 2 ? 3 : 2;  // first row tile: ct = 0..rA
+        const int rB = wave < 2 ? 0 : 1;  // second row tile: ct = 0..rB
+        const bf16_t* M = isP ? Qh : Kh;
+        f32x4 accA[4] = {zero4(), zero4(), zero4(), zero4()};
+        f32x4 accB[2] = {zero4(), zero4()};
 #pragma unroll
-        for (int m = 0; m < 5; ++m) {
-            bool isP;
-            int rt, ct;
-            if (m == 0) {
-                isP = false;
-                rt = ct = wave;
-            } else {
-                const int x = wave + 4 * (m - 1);  // 0..15
-                if (x < 6) {
-                    isP = false;
-                    rt = x < 1 ? 1 : (x < 3 ? 2 : 3);
-                    ct = x - rt * (rt - 1) / 2;
-                } else {
-                    isP = true;
-                    const int y = x - 6;
-                    rt = y < 1 ? 0 : (y < 3 ? 1 : (y < 6 ? 2 : 3));
-                    ct = y - rt * (rt + 1) / 2;
-                }
-            }
-            f32x4 acc = zero4();
-            const bf16_t* M = isP ? Qh : Kh;
+        for (int s = 0; s < NKS; ++s) {
+            bf16x8 kr[4];
 #pragma unroll
-            for (int s = 0; s < NKS; ++s)
-                acc = mfma32(lds8(Kr + (16 * ct + lr) * L::PK + 32 * s + 8 * lg),
-                             lds8(M + (16 * rt + lr) * L::PK + 32 * s + 8 * lg), acc);
+            for (int ct = 0; ct < 4; ++ct)
+                if (ct <= rA) kr[ct] = lds8(Kr + (16 * ct + lr) * L::PK + 32 * s + 8 * lg);
+            const bf16x8 mA = lds8(M + (16 * rA + lr) * L::PK + 32 * s + 8 * lg);
+            const bf16x8 mB = lds8(M + (16 * rB + lr) * L::PK + 32 * s + 8 * lg);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                if (ct <= rA) accA[ct] = mfma32(kr[ct], mA, accA[ct]);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                if (ct <= rB) accB[ct] = mfma32(kr[ct], mB, accB[ct]);
+        }
+        auto epilogue = [&](int rt, int ct, const f32x4& acc) {
             const int t = 16 * rt + lr;
             const float bt = sb[t];
+            float gt = 0.f, gj[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (!KDA) {
+                gt = sG[t];
+                const float4 g4 = *reinterpret_cast<const float4*>(sG + 16 * ct + 4 * lg);
+                gj[0] = g4.x; gj[1] = g4.y; gj[2] = g4.z; gj[3] = g4.w;
+            }
             f32x4 val;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = 16 * ct + 4 * lg + i;
                 float x = acc[i];
-                if constexpr (!KDA) x *= exp2f(fminf(sG[t] - sG[j], 0.f));
+                if constexpr (!KDA) x *= ex2(fminf(gt - gj[i], 0.f));
                 val[i] = isP ? (j <= t ? x : 0.f) : (j < t ? bt * x : 0.f);
             }
-            if (m == 0) {
-                *reinterpret_cast<float4*>(scr + lr * L::PS + 4 * lg) =
-                    make_float4(val[0], val[1], val[2], val[3]);
-            } else if (isP) {
+            if (isP) {
                 st4(Pt + ptile(rt, ct) * 16 * L::PD + lr * L::PD + 4 * lg, val);
-            } else {
+            } else if (ct < rt) {
                 st4(At + atile(rt, ct) * 16 * L::PD + lr * L::PD + 4 * lg, -val);
+            } else {  // diagonal tile, stored transposed: scr[j][t] = A[t][j]
+                float* scr = scr0 + rt * 16 * L::PS;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) scr[(4 * lg + i) * L::PS + lr] = val[i];
             }
-        }
-        // D_w^{-1} = (I + A_ww)^{-1}: lane c solves column c by forward substitution.
-        if (lane < 16) {
+        };
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+            if (ct <= rA) epilogue(rA, ct, accA[ct]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+            if (ct <= rB) epilogue(rB, ct, accB[ct]);
+        // D_r^{-1} = (I + A_rr)^{-1}: lanes 0..15 invert block rA, lanes 16..31
+        // block rB; lane c solves column c by right-looking forward
+        // substitution (x_i -= A_ij x_j for all i > j at step j).
+        if (!isP && lane < 32) {
+            const int blk = lane < 16 ? rA : rB;
+            const int cl = lane & 15;
+            const float* scr = scr0 + blk * 16 * L::PS;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == lane) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = (i == cl) ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc -= scr[i * L::PS + j] * x[j];
-                x[i] = acc;
+            for (int j = 0; j < 15; ++j) {
+                float a[16];
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const float4 r = *reinterpret_cast<const float4*>(scr + j * L::PS + 4 * i4);
+                    a[4 * i4] = r.x; a[4 * i4 + 1] = r.y; a[4 * i4 + 2] = r.z; a[4 * i4 + 3] = r.w;
+                }
+#pragma unroll
+                for (int i = j + 1; i < 16; ++i) x[i] -= a[i] * x[j];
             }
-            bf16_t* Dw = Dt + wave * 16 * L::PD;
+            bf16_t* Dw = Dt + blk * 16 * L::PD;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) Dw[i * L::PD + lane] = static_cast<bf16_t>(bf_bits(x[i]));
+            for (int i = 0; i < 16; ++i) Dw[i * L::PD + cl] = static_cast<bf16_t>(bf_bits(x[i]));
         }
     };
 
@@ -390,14 +461,17 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     bf16x4 Ub[4];
     bf16x8 bS[NKS];
     const size_t sbase = static_cast<size_t>(bh) * DK * DV;
+    const size_t vrow0 = static_cast<size_t>(b) * T * H + h;  // token (b, 0, h)
     auto serial_vload = [&](int c, bf16_t (&V)[4][4]) {
         const int t0 = c * kC, nn = min(kC, T - t0);
+        const bf16_t* vb = v + (vrow0 + static_cast<size_t>(t0) * H) * DV + col0;  // uniform
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int tc = min(16 * rt + 4 * lg + i, nn - 1);
-                V[rt][i] = v[((static_cast<size_t>(b) * T + t0 + tc) * H + h) * DV + col0 + lr];
+                const int t = 16 * rt + 4 * lg + i;
+                const int tc = nn == kC ? t : min(t, nn - 1);
+                V[rt][i] = vb[static_cast<unsigned>(tc * H * DV + lr)];
             }
     };
     // B operands of S for the K=32 steps over dk (KDA: scaled by 2^R per row).
@@ -418,35 +492,55 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
             bS[s] = cat8(cvt4(lo), cvt4(hi));
         }
     };
-    // phase 1: Khat S -> X -> U (blocked forward substitution)
-    auto serial_a = [&](int c, const bf16_t (&V)[4][4]) {
-        build_bS(c);
+    // LDS operands of every MFMA of a phase are read in one batch before the
+    // products (one exposed LDS latency per batch instead of one per product);
+    // Khat of the next chunk is fetched during the current chunk's phase 2.
+    typedef bf16x8 KFrag[4][NKS];
+    auto load_kf = [&](int c, KFrag& kf) {
         const bf16_t* Kh = bfp(c, L::oKh);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                kf[rt][s] = lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
+    };
+    // phase 1: Khat S -> X -> U (blocked forward substitution)
+    auto serial_a = [&](int c, const bf16_t (&V)[4][4], const KFrag& kf) {
         const float* sb = f32p(c, L::oBeta);
         const float* eg = f32p(c, L::oEg);
         const bf16_t* At = bfp(c, L::oA);
         const bf16_t* Dt = bfp(c, L::oD);
+        float4 b4[4], e4[4];
+        bf16x4 Af[6], Df[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            b4[rt] = *reinterpret_cast<const float4*>(sb + 16 * rt + 4 * lg);
+            e4[rt] = KDA ? make_float4(1.f, 1.f, 1.f, 1.f)
+                         : *reinterpret_cast<const float4*>(eg + 16 * rt + 4 * lg);
+            Df[rt] = lds4(Dt + rt * 16 * L::PD + lr * L::PD + 4 * lg);
+        }
+#pragma unroll
+        for (int x = 0; x < 6; ++x) Af[x] = lds4(At + x * 16 * L::PD + lr * L::PD + 4 * lg);
+        build_bS(c);
+        f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(kf[rt][s], bS[s], acc[rt]);
         f32x4 X[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            f32x4 acc = zero4();
+            const float bb[4] = {b4[rt].x, b4[rt].y, b4[rt].z, b4[rt].w};
+            const float ee[4] = {e4[rt].x, e4[rt].y, e4[rt].z, e4[rt].w};
 #pragma unroll
-            for (int s = 0; s < NKS; ++s)
-                acc = mfma32(lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg), bS[s], acc);
-            const float4 b4 = *reinterpret_cast<const float4*>(sb + 16 * rt + 4 * lg);
-            float4 e4 = make_float4(1.f, 1.f, 1.f, 1.f);
-            if constexpr (!KDA) e4 = *reinterpret_cast<const float4*>(eg + 16 * rt + 4 * lg);
-            const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ee[4] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[rt][i] = bb[i] * (bf16_to_f32(V[rt][i]) - ee[i] * acc[i]);
+            for (int i = 0; i < 4; ++i) X[rt][i] = bb[i] * (bf16_to_f32(V[rt][i]) - ee[i] * acc[rt][i]);
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             f32x4 w = X[rt];
 #pragma unroll
-            for (int kb = 0; kb < rt; ++kb)
-                w = mfma16(lds4(At + atile(rt, kb) * 16 * L::PD + lr * L::PD + 4 * lg), Ub[kb], w);
-            Uf[rt] = mfma16(lds4(Dt + rt * 16 * L::PD + lr * L::PD + 4 * lg), cvt4(w), zero4());
+            for (int kb = 0; kb < rt; ++kb) w = mfma16(Af[atile(rt, kb)], Ub[kb], w);
+            Uf[rt] = mfma16(Df[rt], cvt4(w), zero4());
             Ub[rt] = cvt4(Uf[rt]);
         }
     };
@@ -454,6 +548,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     // S <- diag(2^G_end) S + Ktil^T U
     auto serial_b = [&](int c) {
         const int t0 = c * kC, n = min(kC, T - t0);
+        bf16_t* ob = o + (vrow0 + static_cast<size_t>(t0) * H) * DV + col0;  // uniform
         const bf16_t* Qh = bfp(c, L::oQh);
         const bf16_t* Pt = bfp(c, L::oP);
         const bf16_t* Kt = bfp(c, L::oKt);
@@ -461,27 +556,47 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
         const float* ek = f32p(c, L::oEk);
         const float* ge = f32p(c, L::oGend);
         const bf16x4 z4 = cvt4(zero4());
+        // batch 1: Qhat fragments and the P tiles
+        bf16x8 qf[4][NKS], pf[6];
+        float egt[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            // O^T tile: rows = this wave's 16 value columns, columns = tokens 16 rt..
-            f32x4 acc = zero4();
 #pragma unroll
             for (int s = 0; s < NKS; ++s)
-                acc = mfma32(bS[s], lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg), acc);
-            if constexpr (!KDA) acc *= eg[16 * rt + lr];
+                qf[rt][s] = lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
+            egt[rt] = KDA ? 1.f : eg[16 * rt + lr];
+        }
+        // P pieces: (rt, s) for 2 s <= rt -> 6 pieces
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+        for (int rt = 0, x = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
                 if (2 * s <= rt) {
                     const bf16x4 plo = lds4(Pt + ptile(rt, 2 * s) * 16 * L::PD + lr * L::PD + 4 * lg);
                     const bf16x4 phi = (2 * s + 1 <= rt)
                         ? lds4(Pt + ptile(rt, 2 * s + 1) * 16 * L::PD + lr * L::PD + 4 * lg) : z4;
-                    acc = mfma32(cat8(Ub[2 * s], Ub[2 * s + 1]), cat8(plo, phi), acc);
+                    pf[x++] = cat8(plo, phi);
                 }
-            }
+        f32x4 oacc[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) oacc[rt] = mfma32(bS[s], qf[rt][s], oacc[rt]);
+        const bf16x8 u01 = cat8(Ub[0], Ub[1]), u23 = cat8(Ub[2], Ub[3]);
+#pragma unroll
+        for (int rt = 0, x = 0; rt < 4; ++rt) {
+            if constexpr (!KDA) oacc[rt] *= egt[rt];
+            oacc[rt] = mfma32(u01, pf[x++], oacc[rt]);
+            if (rt >= 2) oacc[rt] = mfma32(u23, pf[x++], oacc[rt]);
             const int t = 16 * rt + lr;
-            if (t < n)
-                st4(o + ((static_cast<size_t>(b) * T + t0 + t) * H + h) * DV + col0 + 4 * lg, acc * scale);
+            if (t < n) st4(ob + static_cast<unsigned>(t * H * DV + 4 * lg), oacc[rt] * scale);
         }
+        // batch 2: Ktil^T fragments
+        bf16x8 kt[NRT][2];
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) kt[r][s] = lds_perm(Kt + (16 * r + lr) * L::PT + 32 * s + 4 * lg);
         bf16x8 bU[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -504,10 +619,11 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
             } else {
                 S[r] *= ge[0];
             }
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                S[r] = mfma32(lds_perm(Kt + (16 * r + lr) * L::PT + 32 * s + 4 * lg), bU[s], S[r]);
         }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) S[r] = mfma32(kt[r][s], bU[s], S[r]);
     };
 
     // ================= pipeline =================
@@ -515,12 +631,14 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     // workgroup barriers each, so the barriers pair up across roles while the
     // compiler keeps only one role's loop-carried registers live.
     if (prep) {
+        // Inputs of chunk i+2 are loaded into registers while chunk i+1 is
+        // gated, so the global loads overlap one whole step.
         PrepIn pin;
-        if (nch > 0) prep_load(0, pin);
+        if (nch > 0 && gater) prep_load(0, pin);
         for (int i = -1; i < nch; ++i) {
             if (i + 1 < nch) {
                 prep_gate(i + 1, pin);
-                if (i + 2 < nch) prep_load(i + 2, pin);  // in flight until the next iteration
+                if (i + 2 < nch && gater) prep_load(i + 2, pin);
             }
             lds_barrier();
             if (i + 1 < nch) prep_ap(i + 1);
@@ -536,15 +654,17 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
                     S[r][i] = state_in[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr];
             }
         }
-        bf16_t vin[4][4];
-        if (nch > 0) serial_vload(0, vin);
+        bf16_t vr[4][4];  // v of the next chunk, prefetched one step ahead
+        KFrag kf;
+        if (nch > 0) serial_vload(0, vr);
         for (int i = -1; i < nch; ++i) {
             if (i >= 0) {
-                serial_a(i, vin);
-                if (i + 1 < nch) serial_vload(i + 1, vin);  // in flight until the next iteration
+                serial_a(i, vr, kf);
+                if (i + 1 < nch) serial_vload(i + 1, vr);
             }
             lds_barrier();
             if (i >= 0) serial_b(i);
+            if (i + 1 < nch) load_kf(i + 1, kf);  // Khat of chunk i+1 is complete since barrier 1
             lds_barrier();
         }
 #pragma unroll
