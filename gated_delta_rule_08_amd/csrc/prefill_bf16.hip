@@ -116,6 +116,16 @@ __device__ __forceinline__ uint32_t bf16_half(const uint4& w, int e) {
 }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Raw buffer access (SGPR base and range, 32-bit lane offsets).  Loads beyond
+// the range return zero and stores beyond it are dropped, so the rows past the
+// end of a ragged chunk need neither clamped addresses nor branches (and the
+// memory-counter waits stay exact).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr uint32_t kOOB = 0x80000000u;  // a lane offset past every range used here
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
 template <int DK, int NSW, bool KDA>
 struct Layout {
     static constexpr int DKP = DK < 32 ? 32 : DK;  // contraction pad (dk = 16)
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int lr = lane & 15, lg = lane >> 4;
 
     const int BH = B * H;
@@ -462,16 +472,20 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     bf16x8 bS[NKS];
     const size_t sbase = static_cast<size_t>(bh) * DK * DV;
     const size_t vrow0 = static_cast<size_t>(b) * T * H + h;  // token (b, 0, h)
-    auto serial_vload = [&](int c, bf16_t (&V)[4][4]) {
+    // v of a chunk: the 32-bit word holding this lane's column for each of its
+    // 16 rows (two lanes share a word; the half is picked where it is used),
+    // so the loaded registers themselves carry the prefetch across the barrier.
+    auto serial_vload = [&](int c, uint32_t (&V)[4][4]) {
         const int t0 = c * kC, nn = min(kC, T - t0);
         const bf16_t* vb = v + (vrow0 + static_cast<size_t>(t0) * H) * DV + col0;  // uniform
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(vb, static_cast<uint32_t>(nn * H * DV * 2));
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * rt + 4 * lg + i;
-                const int tc = nn == kC ? t : min(t, nn - 1);
-                V[rt][i] = vb[static_cast<unsigned>(tc * H * DV + lr)];
+                const uint32_t off = t < nn ? static_cast<uint32_t>((t * H * DV + (lr & ~1)) * 2) : kOOB;
+                V[rt][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
             }
     };
     // B operands of S for the K=32 steps over dk (KDA: scaled by 2^R per row).
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
                 kf[rt][s] = lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
     };
     // phase 1: Khat S -> X -> U (blocked forward substitution)
-    auto serial_a = [&](int c, const bf16_t (&V)[4][4], const KFrag& kf) {
+    auto serial_a = [&](int c, const uint32_t (&V)[4][4], const KFrag& kf) {
         const float* sb = f32p(c, L::oBeta);
         const float* eg = f32p(c, L::oEg);
         const bf16_t* At = bfp(c, L::oA);
@@ -533,7 +547,10 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
             const float bb[4] = {b4[rt].x, b4[rt].y, b4[rt].z, b4[rt].w};
             const float ee[4] = {e4[rt].x, e4[rt].y, e4[rt].z, e4[rt].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) X[rt][i] = bb[i] * (bf16_to_f32(V[rt][i]) - ee[i] * acc[rt][i]);
+            for (int i = 0; i < 4; ++i) {
+                const float vv = (lr & 1) ? bf_hi(V[rt][i]) : bf_lo(V[rt][i]);
+                X[rt][i] = bb[i] * (vv - ee[i] * acc[rt][i]);
+            }
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -548,7 +565,8 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     // S <- diag(2^G_end) S + Ktil^T U
     auto serial_b = [&](int c) {
         const int t0 = c * kC, n = min(kC, T - t0);
-        bf16_t* ob = o + (vrow0 + static_cast<size_t>(t0) * H) * DV + col0;  // uniform
+        const bf16_t* ob = o + (vrow0 + static_cast<size_t>(t0) * H) * DV + col0;  // uniform
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob, static_cast<uint32_t>(n * H * DV * 2));
         const bf16_t* Qh = bfp(c, L::oQh);
         const bf16_t* Pt = bfp(c, L::oP);
         const bf16_t* Kt = bfp(c, L::oKt);
@@ -589,7 +607,9 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
             oacc[rt] = mfma32(u01, pf[x++], oacc[rt]);
             if (rt >= 2) oacc[rt] = mfma32(u23, pf[x++], oacc[rt]);
             const int t = 16 * rt + lr;
-            if (t < n) st4(ob + static_cast<unsigned>(t * H * DV + 4 * lg), oacc[rt] * scale);
+            const uint32_t off = t < n ? static_cast<uint32_t>((t * H * DV + 4 * lg) * 2) : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(oacc[rt] * scale)), ors,
+                                                  off, 0, 0);
         }
         // batch 2: Ktil^T fragments
         bf16x8 kt[NRT][2];
@@ -654,17 +674,32 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
                     S[r][i] = state_in[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr];
             }
         }
-        bf16_t vr[4][4];  // v of the next chunk, prefetched one step ahead
-        KFrag kf;
+        // Wait for the initial state here, so that no load into S is pending
+        // at the loop head (otherwise every iteration would wait for all
+        // memory operations, including the previous chunk's output stores).
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        uint32_t vr[4][4];  // v of the next chunk, prefetched one step ahead
         if (nch > 0) serial_vload(0, vr);
-        for (int i = -1; i < nch; ++i) {
-            if (i >= 0) {
-                serial_a(i, vr, kf);
-                if (i + 1 < nch) serial_vload(i + 1, vr);
-            }
+        {
+            // Four dropped (out-of-range) stores: the loop head is then reached
+            // with the same memory-op order from both sides (v loads, then the
+            // four output stores), so the wait for v there does not also wait
+            // for the output stores to complete.
+            const __amdgpu_buffer_rsrc_t nul = make_rsrc(o, 0);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, nul, kOOB + 8 * x, 0, 0);
+        }
+        // iteration -1 (prep gates and forms chunk 0) has no serial work; it
+        // is peeled so that every loop iteration issues its output stores
+        lds_barrier();
+        lds_barrier();
+        for (int i = 0; i < nch; ++i) {
+            KFrag kf;
+            load_kf(i, kf);
+            serial_a(i, vr, kf);
+            if (i + 1 < nch) serial_vload(i + 1, vr);
             lds_barrier();
-            if (i >= 0) serial_b(i);
-            if (i + 1 < nch) load_kf(i + 1, kf);  // Khat of chunk i+1 is complete since barrier 1
+            serial_b(i);
             lds_barrier();
         }
 #pragma unroll
