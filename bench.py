@@ -252,8 +252,10 @@ def bench_prefill(torch, gdr, synth, name, steps, warmup):
     del inp
     s_out = torch.empty(B, H, dk, dv, device="cuda")
     o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.bfloat16)
+    need = gdr.gdr_chunk_prefill_workspace_bytes(w.gate, torch.bfloat16, B, T, H, dk, dv)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     call = lambda: gdr.gdr_chunk_prefill(w.gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                         d["s0"], s_out, o)
+                                         d["s0"], s_out, o, workspace=ws)
     for _ in range(warmup):
         call()
     elapsed, gpu_s = timed_region(torch, steps, call)
@@ -264,6 +266,7 @@ def bench_prefill(torch, gdr, synth, name, steps, warmup):
     return {
         "workload": name, "steps": steps, "ms_per_step": 1e3 * elapsed / steps,
         "tokens_per_s": B * T * steps / elapsed,
+        "schedule": "split" if need else "fused", "workspace_bytes": need,
         "launch_ms": launch_ms,
         "roofline": {
             "bound": "hbm", "achieved": round(nbytes / sec / 1e9, 2), "peak": HBM_PEAK_GBS,

@@ -144,6 +144,8 @@ def gdr_chunk_prefill(gate: str, q, k, v, alpha, beta, state_in, state_out, o,
 
     q, k [B,T,H,dk] and v, o [B,T,H,dv] share a dtype; alpha [B,T,H] (gdn) or
     [B,T,H,dk] (kda) and beta [B,T,H] are fp32; state_in may be None.
+    workspace: a device tensor of at least gdr_chunk_prefill_workspace_bytes
+    bytes, or None to have one allocated for this call.
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -159,6 +161,10 @@ def gdr_chunk_prefill(gate: str, q, k, v, alpha, beta, state_in, state_out, o,
     if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
         raise ValueError("alpha and beta must be fp32")
     _same_device(q, k, v, alpha, beta, state_in, state_out, o, workspace)
+    if workspace is None:  # allocate what this call needs (callers that time or capture pass their own)
+        need = gdr_chunk_prefill_workspace_bytes(gate, q.dtype, B, T, H, dk, dv, chunk)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().gdr_chunk_prefill(
         GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k),

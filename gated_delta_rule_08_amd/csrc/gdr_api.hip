@@ -96,8 +96,13 @@ int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float sca
 
 size_t gdr_chunk_prefill_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
                                          int dv, int chunk) {
-    (void)gate; (void)dtype; (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)chunk;
-    return 0;  // every prefill kernel keeps its intermediates on chip
+    if (check_enums(gate, dtype) != GDR_OK || chunk != 64 || B < 0 || H < 0 || T < 0 ||
+        !head_dim_ok(dk) || !head_dim_ok(dv) || !sizes_ok(B, T, H, dk, dv))
+        return 0;
+    // The fp32 path keeps its intermediates on chip; the bf16 path may stage
+    // per-chunk images of its chunk-local products.
+    if (dtype != GDR_DTYPE_BF16) return 0;
+    return gdr::prefill_bf16_workspace(gate == GDR_GATE_KDA, B, T, H, dk);
 }
 
 int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
@@ -140,7 +145,7 @@ int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, 
                                      static_cast<const gdr::bf16_t*>(q),
                                      static_cast<const gdr::bf16_t*>(k),
                                      static_cast<const gdr::bf16_t*>(v), alpha, beta, state_in,
-                                     state_out, static_cast<gdr::bf16_t*>(o), s);
+                                     state_out, static_cast<gdr::bf16_t*>(o), workspace, s);
     }
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

@@ -44,10 +44,14 @@ hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, floa
                               const float* alpha, const float* beta, const float* state_in,
                               float* state_out, float* o, hipStream_t s);
 
+// The bf16 prefill uses `workspace` (at least prefill_bf16_workspace(...)
+// bytes) when its split schedule is selected, and ignores it otherwise.
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, bf16_t* o, hipStream_t s);
+                               float* state_out, bf16_t* o, void* workspace, hipStream_t s);
+bool prefill_bf16_split(int kda);
+size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk);
 
 // state_out <- state_in (or zeros when state_in is NULL), n floats.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);

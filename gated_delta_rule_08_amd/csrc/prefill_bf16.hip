@@ -44,6 +44,8 @@
 // K=32 step whose k order is {4g..4g+3, 16+4g..16+4g+3}; the LDS operand of
 // that step is read in the same k order, which keeps every product exact
 // without any register shuffle.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "gdr_internal.h"
@@ -59,6 +61,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;                 // chunk
 constexpr int kPrepWaves = 4;
+constexpr int kLoadWaves = 1;          // chain kernel: waves that stream chunk images into LDS
+
+// One kernel body, three launch modes:
+//   kFused  one workgroup per (b, h, value slice); prep waves form chunk i+1
+//           in LDS while the serial waves advance the state through chunk i;
+//   kPrep   one workgroup per (b, h, chunk): only the prep work, writing the
+//           chunk's LDS buffer image (gated operands, A, P, D_r^{-1}, gates)
+//           to a workspace;
+//   kChain  one workgroup per (b, h, value slice): a loader wave copies the
+//           images into two LDS buffers (direct global-to-LDS loads) while the
+//           serial waves run the state recurrence.
+// kPrep + kChain do the chunk-local work once per (head, chunk) instead of
+// once per value slice, and run it at full occupancy.
+enum : int { kFused = 0, kPrep = 1, kChain = 2 };
 constexpr float kLog2Floor = -115.4f;  // GDN: log2(alpha) floor, alpha ~ e^-80
 constexpr float kMinGate = 3.7252903e-09f;  // KDA: alpha floor 2^-28 (4-token products stay normal)
 
@@ -146,6 +162,7 @@ struct Layout {
     static constexpr int oGend = oEk + kC * 4;            // 2^G_end per channel (GDN: [0])
     static constexpr int oSref = oGend + DK * 4;          // KDA 2^R per channel
     static constexpr int BUF = ((oSref + DK * 4) + 15) / 16 * 16;
+    static constexpr int IMG = (BUF + 1023) / 1024 * 1024;  // image stride (1 KB per copy instruction)
     // prep-private
     static constexpr int oKc = 2 * BUF;                   // KDA Kcheck [64][PK]
     static constexpr int oG = oKc + (KDA ? kC * PK * 2 : 0);  // GDN G_t [64]
@@ -153,17 +170,33 @@ struct Layout {
     static constexpr int oScr = oG + kC * 4;              // fp32 diagonal tiles [4][16][PS]
     static constexpr int bytes = oScr + kPrepWaves * 16 * PS * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
+    // kPrep: only what the A/P products and the inverses read stays in LDS
+    static constexpr int pKh = 0;
+    static constexpr int pQh = kC * PK * 2;
+    static constexpr int pBeta = 2 * kC * PK * 2;
+    static constexpr int pKc = pBeta + kC * 4;
+    static constexpr int pG = pKc + (KDA ? kC * PK * 2 : 0);
+    static constexpr int pScr = pG + kC * 4;
+    static constexpr int pBytes = pScr + kPrepWaves * 16 * PS * 4;
+    // kChain: two image buffers
+    static constexpr int cBytes = 2 * IMG;
+    static_assert(cBytes <= 160 * 1024, "LDS budget exceeded");
 };
+
+template <int NSW, int MODE>
+constexpr int block_threads() {
+    return 64 * (MODE == kPrep ? kPrepWaves : MODE == kChain ? kLoadWaves + NSW : kPrepWaves + NSW);
+}
 
 __device__ __forceinline__ int ptile(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }  // ct <= rt
 __device__ __forceinline__ int atile(int rt, int ct) { return rt * (rt - 1) / 2 + ct; }  // ct < rt
 
-template <int DK, int NSW, bool KDA>
-__global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
+template <int DK, int NSW, bool KDA, int MODE>
+__global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_kernel(
     int B, int T, int H, int DV, int NS, float scale, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ state_in,
-    float* __restrict__ state_out, bf16_t* __restrict__ o) {
+    float* __restrict__ state_out, bf16_t* __restrict__ o, unsigned char* __restrict__ img) {
     using L = Layout<DK, NSW, KDA>;
     constexpr int DVS = 16 * NSW;
     constexpr int NRT = DK / 16;          // 16-row tiles of S
@@ -176,28 +209,61 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     const int lr = lane & 15, lg = lane >> 4;
 
     const int BH = B * H;
-    const int grp = blockIdx.x / (8 * NS);
-    const int rem = blockIdx.x - grp * 8 * NS;
-    const int bh = grp * 8 + (rem & 7);
-    const int slice = rem >> 3;
-    if (bh >= BH) return;  // whole block exits before any barrier
-    const int b = bh / H, h = bh - b * H;
     const int nch = (T + kC - 1) / kC;
-    const bool prep = wave < kPrepWaves;
+    int bh, slice = 0, pc = 0;  // pc: the chunk of a kPrep block
+    if constexpr (MODE == kPrep) {
+        pc = blockIdx.x / BH;
+        bh = blockIdx.x - pc * BH;
+    } else {
+        const int grp = blockIdx.x / (8 * NS);
+        const int rem = blockIdx.x - grp * 8 * NS;
+        bh = grp * 8 + (rem & 7);
+        slice = rem >> 3;
+        if (bh >= BH) return;  // whole block exits before any barrier
+    }
+    const int b = bh / H, h = bh - b * H;
+    constexpr int kLead = MODE == kChain ? kLoadWaves : kPrepWaves;  // waves before the serial ones
+    const bool prep = MODE == kPrep || (MODE == kFused && wave < kPrepWaves);
 
-    auto bfp = [&](int c, int off) { return reinterpret_cast<bf16_t*>(smem + (c & 1) * L::BUF + off); };
-    auto f32p = [&](int c, int off) { return reinterpret_cast<float*>(smem + (c & 1) * L::BUF + off); };
-    bf16_t* Kc = reinterpret_cast<bf16_t*>(smem + L::oKc);  // used by KDA only
-    float* sG = reinterpret_cast<float*>(smem + L::oG);
+    // Chunk buffers: kFused / kChain keep two in LDS (chunk c uses c & 1).
+    constexpr int kStride = MODE == kChain ? L::IMG : L::BUF;
+    auto bfp = [&](int c, int off) { return reinterpret_cast<bf16_t*>(smem + (c & 1) * kStride + off); };
+    auto f32p = [&](int c, int off) { return reinterpret_cast<float*>(smem + (c & 1) * kStride + off); };
+    // The image of chunk c of this head (kPrep writes it, kChain reads it).
+    auto imgp = [&](int c) { return img + (static_cast<size_t>(bh) * nch + c) * L::IMG; };
+    // Where the prep work reads and writes.  kFused: the LDS buffer of the
+    // chunk.  kPrep: what the A/P products and the inverses read sits in LDS
+    // (and Khat, Qhat, beta are also written to the image); everything else
+    // goes to the image only.
+    auto prep_lds_b = [&](int c, int off_fused, int off_prep) {
+        if constexpr (MODE == kPrep) return reinterpret_cast<bf16_t*>(smem + off_prep);
+        else return bfp(c, off_fused);
+    };
+    auto prep_out_b = [&](int c, int off) {
+        if constexpr (MODE == kPrep) return reinterpret_cast<bf16_t*>(imgp(c) + off);
+        else return bfp(c, off);
+    };
+    auto prep_out_f = [&](int c, int off) {
+        if constexpr (MODE == kPrep) return reinterpret_cast<float*>(imgp(c) + off);
+        else return f32p(c, off);
+    };
+    bf16_t* Kc = reinterpret_cast<bf16_t*>(smem + (MODE == kPrep ? L::pKc : L::oKc));  // KDA only
+    float* sG = reinterpret_cast<float*>(smem + (MODE == kPrep ? L::pG : L::oG));
+    float* scr0 = reinterpret_cast<float*>(smem + (MODE == kPrep ? L::pScr : L::oScr));
 
-    if constexpr (L::DKP != DK) {  // zero the contraction padding once (both buffers, Kc)
+    if constexpr (L::DKP != DK && MODE != kChain) {  // zero the contraction padding
         constexpr int W = L::DKP - DK;
-        for (int idx = tid; idx < 2 * kC * W; idx += blockDim.x) {
+        constexpr int NB = MODE == kPrep ? 1 : 2;
+        for (int idx = tid; idx < NB * kC * W; idx += blockDim.x) {
             const int c = idx / (kC * W), r = idx % (kC * W);
             const int t = r / W, col = DK + r % W;
-            bfp(c, L::oKh)[t * L::PK + col] = 0;
-            bfp(c, L::oQh)[t * L::PK + col] = 0;
+            prep_lds_b(c, L::oKh, L::pKh)[t * L::PK + col] = 0;
+            prep_lds_b(c, L::oQh, L::pQh)[t * L::PK + col] = 0;
             if (KDA && c == 0) Kc[t * L::PK + col] = 0;
+            if constexpr (MODE == kPrep) {  // and in the image, which the chain reads
+                reinterpret_cast<bf16_t*>(imgp(pc) + L::oKh)[t * L::PK + col] = 0;
+                reinterpret_cast<bf16_t*>(imgp(pc) + L::oQh)[t * L::PK + col] = 0;
+            }
         }
     }
 
@@ -255,9 +321,13 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     // Gates and gated operands of chunk c into buffer c & 1.
     auto prep_gate = [&](int c, const PrepIn& R) {
         const int n = min(kC, T - c * kC);
-        bf16_t* Kh = bfp(c, L::oKh);
-        bf16_t* Qh = bfp(c, L::oQh);
-        bf16_t* Kt = bfp(c, L::oKt);
+        bf16_t* Kh = prep_lds_b(c, L::oKh, L::pKh);
+        bf16_t* Qh = prep_lds_b(c, L::oQh, L::pQh);
+        bf16_t* Kt = prep_out_b(c, L::oKt);
+        float* sBeta = reinterpret_cast<float*>(prep_lds_b(c, L::oBeta, L::pBeta));
+        // kPrep: copies of Khat, Qhat and beta for the image
+        bf16_t* KhI = reinterpret_cast<bf16_t*>(MODE == kPrep ? imgp(c) + L::oKh : nullptr);
+        bf16_t* QhI = reinterpret_cast<bf16_t*>(MODE == kPrep ? imgp(c) + L::oQh : nullptr);
         if (!gater) return;
         // a full chunk (every chunk but a ragged last one) needs no row masks
         auto body = [&](auto full_tag) {
@@ -269,7 +339,8 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
                 float4 b4;
                 b4.x = valid[0] ? R.bt[0] : 0.f; b4.y = valid[1] ? R.bt[1] : 0.f;
                 b4.z = valid[2] ? R.bt[2] : 0.f; b4.w = valid[3] ? R.bt[3] : 0.f;
-                *reinterpret_cast<float4*>(f32p(c, L::oBeta) + 4 * tg) = b4;
+                *reinterpret_cast<float4*>(sBeta + 4 * tg) = b4;
+                if constexpr (MODE == kPrep) *reinterpret_cast<float4*>(prep_out_f(c, L::oBeta) + 4 * tg) = b4;
             }
             uint4 kz[4], qz[4];
 #pragma unroll
@@ -294,8 +365,8 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
                     run[e] = ex2(inc - tot - 0.5f * end);
                     ce[e] = ex2(0.5f * end);  // 2^(G_end - R) = 2^R
                     if (tg == 0) {
-                        f32p(c, L::oGend)[c8 + e] = ex2(end);
-                        f32p(c, L::oSref)[c8 + e] = ce[e];
+                        prep_out_f(c, L::oGend)[c8 + e] = ex2(end);
+                        prep_out_f(c, L::oSref)[c8 + e] = ce[e];
                     }
                 }
                 uint32_t ktw[8][2];
@@ -319,6 +390,10 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
                     *reinterpret_cast<bf16x8*>(Kh + t * L::PK + c8) = kh;
                     *reinterpret_cast<bf16x8*>(Qh + t * L::PK + c8) = qh;
                     *reinterpret_cast<bf16x8*>(Kc + t * L::PK + c8) = kc;
+                    if constexpr (MODE == kPrep) {
+                        *reinterpret_cast<bf16x8*>(KhI + t * L::PK + c8) = kh;
+                        *reinterpret_cast<bf16x8*>(QhI + t * L::PK + c8) = qh;
+                    }
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -340,15 +415,19 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
                     k4.x = ex2(end - g4.x); k4.y = ex2(end - g4.y);
                     k4.z = ex2(end - g4.z); k4.w = ex2(end - g4.w);
                     *reinterpret_cast<float4*>(sG + 4 * tg) = g4;
-                    *reinterpret_cast<float4*>(f32p(c, L::oEg) + 4 * tg) = e4;
-                    *reinterpret_cast<float4*>(f32p(c, L::oEk) + 4 * tg) = k4;
-                    if (tg == 0) f32p(c, L::oGend)[0] = ex2(end);
+                    *reinterpret_cast<float4*>(prep_out_f(c, L::oEg) + 4 * tg) = e4;
+                    *reinterpret_cast<float4*>(prep_out_f(c, L::oEk) + 4 * tg) = k4;
+                    if (tg == 0) prep_out_f(c, L::oGend)[0] = ex2(end);
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int t = 4 * tg + u;
                     *reinterpret_cast<uint4*>(Kh + t * L::PK + c8) = kz[u];
                     *reinterpret_cast<uint4*>(Qh + t * L::PK + c8) = qz[u];
+                    if constexpr (MODE == kPrep) {
+                        *reinterpret_cast<uint4*>(KhI + t * L::PK + c8) = kz[u];
+                        *reinterpret_cast<uint4*>(QhI + t * L::PK + c8) = qz[u];
+                    }
                 }
                 // K^T: channel c8 + e, tokens 4 tg .. 4 tg + 3
 #pragma unroll
@@ -374,14 +453,13 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     // so each K step loads the Kr fragments once for both rows.  Waves 0 and
     // 2 hold the diagonal A tiles and invert them, two blocks per wave.
     auto prep_ap = [&](int c) {
-        const bf16_t* Kh = bfp(c, L::oKh);
-        const bf16_t* Qh = bfp(c, L::oQh);
+        const bf16_t* Kh = prep_lds_b(c, L::oKh, L::pKh);
+        const bf16_t* Qh = prep_lds_b(c, L::oQh, L::pQh);
         const bf16_t* Kr = KDA ? Kc : Kh;  // right factor (j side)
-        const float* sb = f32p(c, L::oBeta);
-        bf16_t* Pt = bfp(c, L::oP);
-        bf16_t* At = bfp(c, L::oA);
-        bf16_t* Dt = bfp(c, L::oD);
-        float* scr0 = reinterpret_cast<float*>(smem + L::oScr);
+        const float* sb = reinterpret_cast<const float*>(prep_lds_b(c, L::oBeta, L::pBeta));
+        bf16_t* Pt = prep_out_b(c, L::oP);
+        bf16_t* At = prep_out_b(c, L::oA);
+        bf16_t* Dt = prep_out_b(c, L::oD);
         const bool isP = wave & 1;
         const int rA = wave < 2 ? 3 : 2;  // first row tile: ct = 0..rA
         const int rB = wave < 2 ? 0 : 1;  // second row tile: ct = 0..rB
@@ -464,7 +542,7 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     };
 
     // ================= serial-wave work =================
-    const int sw = wave - kPrepWaves;
+    const int sw = wave - kLead;
     const int col0 = slice * DVS + 16 * sw;  // first value column of this wave
     f32x4 S[NRT];
     f32x4 Uf[4];
@@ -647,10 +725,82 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
     };
 
     // ================= pipeline =================
-    // Each role runs its own loop: nch + 1 iterations with exactly two
-    // workgroup barriers each, so the barriers pair up across roles while the
-    // compiler keeps only one role's loop-carried registers live.
-    if (prep) {
+    auto serial_init = [&]() {
+#pragma unroll
+        for (int r = 0; r < NRT; ++r) {
+            S[r] = zero4();
+            if (state_in) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[r][i] = state_in[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr];
+            }
+        }
+        // Wait for the initial state here, so that no load into S is pending
+        // at the loop head (otherwise every iteration would wait for all
+        // memory operations, including the previous chunk's output stores).
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    };
+    auto serial_fini = [&]() {
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                state_out[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr] = S[r][i];
+    };
+    // Four dropped (out-of-range) stores: the loop head is then reached with
+    // the same memory-op order from both sides (v loads, then the four output
+    // stores), so the wait for v there does not also wait for output stores.
+    auto dummy_stores = [&]() {
+        const __amdgpu_buffer_rsrc_t nul = make_rsrc(o, 0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, nul, kOOB + 8 * x, 0, 0);
+    };
+
+    if constexpr (MODE == kPrep) {
+        // One chunk per workgroup; the outputs go straight to the image.
+        PrepIn pin;
+        if (gater) prep_load(pc, pin);
+        prep_gate(pc, pin);
+        lds_barrier();
+        prep_ap(pc);
+    } else if constexpr (MODE == kChain) {
+        if (wave < kLoadWaves) {
+            // Loader: image of chunk c -> LDS buffer c & 1, 1 KB per instruction
+            // (lane l moves bytes [16 l, 16 l + 16) of each kilobyte).
+            auto copy_in = [&](int c) {
+                const unsigned char* src = imgp(c) + 16 * lane;
+                auto dst = (__attribute__((address_space(3))) unsigned char*)(smem + (c & 1) * L::IMG);
+                for (int j = wave; j < L::IMG / 1024; j += kLoadWaves)
+                    __builtin_amdgcn_global_load_lds(src + 1024 * j, dst + 1024 * j, 16, 0, 0);
+            };
+            copy_in(0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copy has landed in LDS
+            lds_barrier();
+            for (int i = 0; i < nch; ++i) {
+                if (i + 1 < nch) copy_in(i + 1);
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+                lds_barrier();
+            }
+        } else {
+            serial_init();
+            uint32_t vr[4][4];  // v of the next chunk, prefetched one step ahead
+            if (nch > 0) serial_vload(0, vr);
+            dummy_stores();
+            lds_barrier();  // chunk 0 is in buffer 0
+            for (int i = 0; i < nch; ++i) {
+                KFrag kf;
+                load_kf(i, kf);
+                serial_a(i, vr, kf);
+                if (i + 1 < nch) serial_vload(i + 1, vr);
+                serial_b(i);
+                lds_barrier();  // chunk i + 1 has landed; buffer i & 1 is free
+            }
+            serial_fini();
+        }
+    } else if (prep) {
+        // Each role runs its own loop: nch + 1 iterations with exactly two
+        // workgroup barriers each, so the barriers pair up across roles while
+        // the compiler keeps only one role's loop-carried registers live.
         // Inputs of chunk i+2 are loaded into registers while chunk i+1 is
         // gated, so the global loads overlap one whole step.
         PrepIn pin;
@@ -665,30 +815,10 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
             lds_barrier();
         }
     } else {
-#pragma unroll
-        for (int r = 0; r < NRT; ++r) {
-            S[r] = zero4();
-            if (state_in) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[r][i] = state_in[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr];
-            }
-        }
-        // Wait for the initial state here, so that no load into S is pending
-        // at the loop head (otherwise every iteration would wait for all
-        // memory operations, including the previous chunk's output stores).
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        serial_init();
         uint32_t vr[4][4];  // v of the next chunk, prefetched one step ahead
         if (nch > 0) serial_vload(0, vr);
-        {
-            // Four dropped (out-of-range) stores: the loop head is then reached
-            // with the same memory-op order from both sides (v loads, then the
-            // four output stores), so the wait for v there does not also wait
-            // for the output stores to complete.
-            const __amdgpu_buffer_rsrc_t nul = make_rsrc(o, 0);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, nul, kOOB + 8 * x, 0, 0);
-        }
+        dummy_stores();
         // iteration -1 (prep gates and forms chunk 0) has no serial work; it
         // is peeled so that every loop iteration issues its output stores
         lds_barrier();
@@ -702,41 +832,54 @@ __global__ __launch_bounds__(64 * (kPrepWaves + NSW)) void prefill_bf16_kernel(
             serial_b(i);
             lds_barrier();
         }
-#pragma unroll
-        for (int r = 0; r < NRT; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                state_out[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr] = S[r][i];
+        serial_fini();
     }
 }
 
 template <int DK, int NSW, bool KDA>
 hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, const bf16_t* k,
                   const bf16_t* v, const float* alpha, const float* beta, const float* s_in,
-                  float* s_out, bf16_t* o, hipStream_t s) {
+                  float* s_out, bf16_t* o, unsigned char* img, hipStream_t s) {
     using L = Layout<DK, NSW, KDA>;
-    auto kern = prefill_bf16_kernel<DK, NSW, KDA>;
-    if (L::bytes > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
-        if (e != hipSuccess) return e;
-    }
     const int NS = DV / (16 * NSW);
     const int groups = (B * H + 7) / 8;
     const unsigned blocks = static_cast<unsigned>(groups) * 8u * static_cast<unsigned>(NS);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (kPrepWaves + NSW)), L::bytes, s, B, T, H, DV,
-                       NS, scale, q, k, v, alpha, beta, s_in, s_out, o);
+    auto set_lds = [](const void* kern, int bytes) {
+        return bytes > 64 * 1024 ? hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
+                                 : hipSuccess;
+    };
+    hipError_t e;
+    if (!img) {
+        auto kern = prefill_bf16_kernel<DK, NSW, KDA, kFused>;
+        if ((e = set_lds(reinterpret_cast<const void*>(kern), L::bytes)) != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(block_threads<NSW, kFused>()), L::bytes, s, B, T,
+                           H, DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, nullptr);
+        return hipGetLastError();
+    }
+    // chunk-local work of every (b, h, chunk), then the recurrence
+    using LP = Layout<DK, 1, KDA>;
+    auto prep = prefill_bf16_kernel<DK, 1, KDA, kPrep>;
+    if ((e = set_lds(reinterpret_cast<const void*>(prep), LP::pBytes)) != hipSuccess) return e;
+    const unsigned nch = static_cast<unsigned>((T + kC - 1) / kC);
+    hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(B * H) * nch), dim3(block_threads<1, kPrep>()),
+                       LP::pBytes, s, B, T, H, DV, 1, scale, q, k, v, alpha, beta, s_in, s_out, o, img);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    auto chain = prefill_bf16_kernel<DK, NSW, KDA, kChain>;
+    if ((e = set_lds(reinterpret_cast<const void*>(chain), L::cBytes)) != hipSuccess) return e;
+    hipLaunchKernelGGL(chain, dim3(blocks), dim3(block_threads<NSW, kChain>()), L::cBytes, s, B, T, H,
+                       DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, img);
     return hipGetLastError();
 }
 
 template <int DK, bool KDA>
 hipError_t dispatch_dvs(int dvs, int B, int T, int H, int DV, float scale, const bf16_t* q,
                         const bf16_t* k, const bf16_t* v, const float* alpha, const float* beta,
-                        const float* s_in, float* s_out, bf16_t* o, hipStream_t s) {
+                        const float* s_in, float* s_out, bf16_t* o, unsigned char* img,
+                        hipStream_t s) {
     switch (dvs) {
-        case 16: return launch<DK, 1, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
-        case 32: return launch<DK, 2, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
-        default: return launch<DK, 4, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
+        case 16: return launch<DK, 1, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s);
+        case 32: return launch<DK, 2, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s);
+        default: return launch<DK, 4, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s);
     }
 }
 
@@ -744,10 +887,13 @@ template <int DK>
 hipError_t dispatch_gate(int kda, int dvs, int B, int T, int H, int DV, float scale,
                          const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* alpha,
                          const float* beta, const float* s_in, float* s_out, bf16_t* o,
-                         hipStream_t s) {
-    return kda ? dispatch_dvs<DK, true>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s)
-               : dispatch_dvs<DK, false>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
+                         unsigned char* img, hipStream_t s) {
+    return kda ? dispatch_dvs<DK, true>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s)
+               : dispatch_dvs<DK, false>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s);
 }
+
+template <int DK>
+constexpr size_t image_bytes() { return static_cast<size_t>(Layout<DK, 1, false>::IMG); }
 
 }  // namespace
 
@@ -760,16 +906,41 @@ int prefill_bf16_slice_width(int B, int H, int dv) {
     return dv / ns;
 }
 
+// Which bf16 prefill schedule runs: the split one (chunk-local kernel + chain
+// kernel, needs a workspace) or the fused one.  GDR_PREFILL_PATH=fused|split
+// overrides the default, which is split for KDA (its chunk-local work is the
+// expensive part, and the fused kernel would repeat it for every value
+// slice) and fused for GDN.
+bool prefill_bf16_split(int kda) {
+    const char* env = getenv("GDR_PREFILL_PATH");
+    if (env && !strcmp(env, "fused")) return false;
+    if (env && !strcmp(env, "split")) return true;
+    return kda != 0;
+}
+
+size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk) {
+    if (!prefill_bf16_split(kda) || T <= 0 || B <= 0 || H <= 0) return 0;
+    size_t img;
+    switch (dk) {
+        case 16: img = image_bytes<16>(); break;
+        case 32: img = image_bytes<32>(); break;
+        case 64: img = image_bytes<64>(); break;
+        default: img = image_bytes<128>(); break;
+    }
+    return static_cast<size_t>(B) * H * ((T + kC - 1) / kC) * img;
+}
+
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, bf16_t* o, hipStream_t s) {
+                               float* state_out, bf16_t* o, void* workspace, hipStream_t s) {
     const int dvs = prefill_bf16_slice_width(B, H, dv);
+    unsigned char* img = prefill_bf16_split(kda) ? static_cast<unsigned char*>(workspace) : nullptr;
     switch (dk) {
-        case 16: return dispatch_gate<16>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s);
-        case 32: return dispatch_gate<32>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s);
-        case 64: return dispatch_gate<64>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s);
-        default: return dispatch_gate<128>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s);
+        case 16: return dispatch_gate<16>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s);
+        case 32: return dispatch_gate<32>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s);
+        case 64: return dispatch_gate<64>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s);
+        default: return dispatch_gate<128>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s);
     }
 }
 

@@ -127,11 +127,28 @@ def test_prefill_validation(lib):
     assert prefill(lib, B=0, ptrs=[None] * 8) == OK
 
 
-def test_workspace(lib):
-    n = lib.gdr_chunk_prefill_workspace_bytes(0, 1, 4, 8192, 32, 128, 128, 64)
-    assert n == 0
-    assert gdr.gdr_chunk_prefill_workspace_bytes("kda", __import__("torch").bfloat16,
-                                                 1, 32768, 32, 128, 128) == 0
+def test_workspace(lib, monkeypatch):
+    import torch
+    monkeypatch.delenv("GDR_PREFILL_PATH", raising=False)
+    # GDN bf16 and every fp32 prefill keep their intermediates on chip
+    assert lib.gdr_chunk_prefill_workspace_bytes(0, 1, 4, 8192, 32, 128, 128, 64) == 0
+    assert lib.gdr_chunk_prefill_workspace_bytes(1, 0, 1, 256, 2, 128, 128, 64) == 0
+    # KDA bf16 stages one image per (b, h, chunk): a whole number of KiB each
+    n = gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 32768, 32, 128, 128)
+    n1 = gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 64, 1, 128, 128)
+    assert n1 > 0 and n1 % 1024 == 0 and n == 32 * 512 * n1
+    assert gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 65, 1, 128, 128) == 2 * n1
+    assert gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 0, 1, 128, 128) == 0
+    # invalid arguments need nothing
+    assert lib.gdr_chunk_prefill_workspace_bytes(1, 1, 1, 64, 1, 96, 128, 64) == 0
+    # a missing or short workspace is rejected before any device work
+    assert prefill(lib, gate=1) == WS
+    assert prefill(lib, gate=1, ws=P[8], ws_bytes=1024) == WS
+    # the schedule can be forced either way
+    monkeypatch.setenv("GDR_PREFILL_PATH", "fused")
+    assert gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 64, 1, 128, 128) == 0
+    monkeypatch.setenv("GDR_PREFILL_PATH", "split")
+    assert gdr.gdr_chunk_prefill_workspace_bytes("gdn", torch.bfloat16, 1, 64, 1, 128, 128) == n1
 
 
 def test_binding_rejects_cpu_tensors():
