@@ -44,6 +44,7 @@
 // K=32 step whose k order is {4g..4g+3, 16+4g..16+4g+3}; the LDS operand of
 // that step is read in the same k order, which keeps every product exact
 // without any register shuffle.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -61,7 +62,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;                 // chunk
 constexpr int kPrepWaves = 4;
-constexpr int kLoadWaves = 1;          // chain kernel: waves that stream chunk images into LDS
 
 // One kernel body, three launch modes:
 //   kFused  one workgroup per (b, h, value slice); prep waves form chunk i+1
@@ -177,26 +177,45 @@ struct Layout {
     static constexpr int pKc = pBeta + kC * 4;
     static constexpr int pG = pKc + (KDA ? kC * PK * 2 : 0);
     static constexpr int pScr = pG + kC * 4;
-    static constexpr int pBytes = pScr + kPrepWaves * 16 * PS * 4;
+    static constexpr int pA = pScr + kPrepWaves * 16 * PS * 4;  // -A_rk tiles (6)
+    static constexpr int pD = pA + 6 * TILE;                     // D_r^{-1} tiles (4)
+    static constexpr int pT = pD + 4 * TILE;                     // T_rk tiles, k < r (6)
+    static constexpr int pBytes = pT + 6 * TILE;
     // kChain: two image buffers
     static constexpr int cBytes = 2 * IMG;
     static_assert(cBytes <= 160 * 1024, "LDS budget exceeded");
 };
 
+// Chain kernel: waves that copy chunk images into LDS (they fill the SIMDs
+// the serial waves leave free; the copies of one chunk are split among them).
+template <int NSW>
+constexpr int load_waves() { return NSW >= 4 ? 1 : 4 - NSW; }
 template <int NSW, int MODE>
 constexpr int block_threads() {
-    return 64 * (MODE == kPrep ? kPrepWaves : MODE == kChain ? kLoadWaves + NSW : kPrepWaves + NSW);
+    return 64 * (MODE == kPrep ? kPrepWaves : MODE == kChain ? load_waves<NSW>() + NSW : kPrepWaves + NSW);
+}
+// Waves per SIMD the register allocation is sized for: a chain workgroup of
+// at most four waves has a SIMD per wave (its LDS keeps it alone on the CU),
+// so each wave may use the whole register file.
+template <int NSW, int MODE>
+constexpr int waves_per_simd() {
+    return (MODE == kChain && load_waves<NSW>() + NSW <= 4) ? 1 : 2;
 }
 
 __device__ __forceinline__ int ptile(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }  // ct <= rt
 __device__ __forceinline__ int atile(int rt, int ct) { return rt * (rt - 1) / 2 + ct; }  // ct < rt
 
 template <int DK, int NSW, bool KDA, int MODE>
-__global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_kernel(
+__global__ __launch_bounds__((block_threads<NSW, MODE>()))
+__attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefill_bf16_kernel(
     int B, int T, int H, int DV, int NS, float scale, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ state_in,
-    float* __restrict__ state_out, bf16_t* __restrict__ o, unsigned char* __restrict__ img) {
+    float* __restrict__ state_out, bf16_t* __restrict__ o, unsigned char* __restrict__ img,
+    int c0, int c1) {
+    // Chunks c0 .. c1-1 of every sequence (the split schedule runs a long
+    // sequence as consecutive ranges, chaining the state through state_in /
+    // state_out, so that one range's images stay cache resident).
     using L = Layout<DK, NSW, KDA>;
     constexpr int DVS = 16 * NSW;
     constexpr int NRT = DK / 16;          // 16-row tiles of S
@@ -209,11 +228,11 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
     const int lr = lane & 15, lg = lane >> 4;
 
     const int BH = B * H;
-    const int nch = (T + kC - 1) / kC;
+    const int nch = c1;         // chunks run by this launch: c0 .. nch-1
     int bh, slice = 0, pc = 0;  // pc: the chunk of a kPrep block
     if constexpr (MODE == kPrep) {
-        pc = blockIdx.x / BH;
-        bh = blockIdx.x - pc * BH;
+        pc = c0 + static_cast<int>(blockIdx.x) / BH;
+        bh = static_cast<int>(blockIdx.x) - (pc - c0) * BH;
     } else {
         const int grp = blockIdx.x / (8 * NS);
         const int rem = blockIdx.x - grp * 8 * NS;
@@ -222,7 +241,8 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
         if (bh >= BH) return;  // whole block exits before any barrier
     }
     const int b = bh / H, h = bh - b * H;
-    constexpr int kLead = MODE == kChain ? kLoadWaves : kPrepWaves;  // waves before the serial ones
+    constexpr int kLoad = load_waves<NSW>();
+    constexpr int kLead = MODE == kChain ? kLoad : kPrepWaves;  // waves before the serial ones
     const bool prep = MODE == kPrep || (MODE == kFused && wave < kPrepWaves);
 
     // Chunk buffers: kFused / kChain keep two in LDS (chunk c uses c & 1).
@@ -230,7 +250,7 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
     auto bfp = [&](int c, int off) { return reinterpret_cast<bf16_t*>(smem + (c & 1) * kStride + off); };
     auto f32p = [&](int c, int off) { return reinterpret_cast<float*>(smem + (c & 1) * kStride + off); };
     // The image of chunk c of this head (kPrep writes it, kChain reads it).
-    auto imgp = [&](int c) { return img + (static_cast<size_t>(bh) * nch + c) * L::IMG; };
+    auto imgp = [&](int c) { return img + (static_cast<size_t>(bh) * (c1 - c0) + (c - c0)) * L::IMG; };
     // Where the prep work reads and writes.  kFused: the LDS buffer of the
     // chunk.  kPrep: what the A/P products and the inverses read sits in LDS
     // (and Khat, Qhat, beta are also written to the image); everything else
@@ -458,8 +478,9 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
         const bf16_t* Kr = KDA ? Kc : Kh;  // right factor (j side)
         const float* sb = reinterpret_cast<const float*>(prep_lds_b(c, L::oBeta, L::pBeta));
         bf16_t* Pt = prep_out_b(c, L::oP);
-        bf16_t* At = prep_out_b(c, L::oA);
-        bf16_t* Dt = prep_out_b(c, L::oD);
+        // kPrep keeps -A and D_r^{-1} in LDS: the image gets (I + A)^{-1} instead
+        bf16_t* At = MODE == kPrep ? reinterpret_cast<bf16_t*>(smem + L::pA) : prep_out_b(c, L::oA);
+        bf16_t* Dt = MODE == kPrep ? reinterpret_cast<bf16_t*>(smem + L::pD) : prep_out_b(c, L::oD);
         const bool isP = wave & 1;
         const int rA = wave < 2 ? 3 : 2;  // first row tile: ct = 0..rA
         const int rB = wave < 2 ? 0 : 1;  // second row tile: ct = 0..rB
@@ -541,6 +562,45 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
         }
     };
 
+    // kPrep: the 16x16 blocks of T = (I + A)^{-1} from -A and the D_r^{-1}
+    // (one wave):  T_rr = D_r^{-1},  T_rk = D_r^{-1} sum_{k<=m<r} (-A_rm) T_mk.
+    // Z = sum_m (-A_rm) T_mk is formed in the accumulator layout, which is
+    // the A-operand layout of Z^T, so the second product gives (D_r^{-1} Z)^T,
+    // whose accumulator layout is the row-fragment layout the chain reads.
+    auto prep_t = [&](int c) {
+        const bf16_t* Ab = reinterpret_cast<const bf16_t*>(smem + L::pA);
+        const bf16_t* Dl = reinterpret_cast<const bf16_t*>(smem + L::pD);
+        bf16_t* Tl = reinterpret_cast<bf16_t*>(smem + L::pT);
+        bf16_t* Ti = prep_out_b(c, L::oA);  // T_rk, k < r, in the slots of -A_rk
+        bf16_t* Di = prep_out_b(c, L::oD);  // T_rr
+        auto row_frag = [&](const bf16_t* t) { return lds4(t + lr * L::PD + 4 * lg); };
+        auto col_frag = [&](const bf16_t* t) {  // t[4 lg + i][lr], i = 0..3 (transposing read)
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            const bf16_t* p = t + (4 * lg + (lr >> 2)) * L::PD + 4 * (lr & 3);
+            return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+        };
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<uint2*>(Di + r * 16 * L::PD + lr * L::PD + 4 * lg) =
+                *reinterpret_cast<const uint2*>(Dl + r * 16 * L::PD + lr * L::PD + 4 * lg);
+#pragma unroll
+        for (int r = 1; r < 4; ++r) {
+            const bf16x4 dr = row_frag(Dl + r * 16 * L::PD);
+#pragma unroll
+            for (int kk = 0; kk < r; ++kk) {
+                f32x4 z = zero4();
+#pragma unroll
+                for (int m = kk; m < r; ++m) {
+                    const bf16_t* tmk = m == kk ? Dl + kk * 16 * L::PD : Tl + atile(m, kk) * 16 * L::PD;
+                    z = mfma16(row_frag(Ab + atile(r, m) * 16 * L::PD), col_frag(tmk), z);
+                }
+                const f32x4 tt = mfma16(cvt4(z), dr, zero4());  // lane: T_rk[lr][4 lg + i]
+                st4(Tl + atile(r, kk) * 16 * L::PD + lr * L::PD + 4 * lg, tt);
+                st4(Ti + atile(r, kk) * 16 * L::PD + lr * L::PD + 4 * lg, tt);
+            }
+        }
+    };
+
     // ================= serial-wave work =================
     const int sw = wave - kLead;
     const int col0 = slice * DVS + 16 * sw;  // first value column of this wave
@@ -566,101 +626,63 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
                 V[rt][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
             }
     };
-    // B operands of S for the K=32 steps over dk (KDA: scaled by 2^R per row).
-    auto build_bS = [&](int c) {
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            f32x4 lo = S[2 * s];
-            f32x4 hi = (2 * s + 1 < NRT) ? S[2 * s + 1] : zero4();
-            if constexpr (KDA) {
-                const float* sr = f32p(c, L::oSref);
-                const float4 f0 = *reinterpret_cast<const float4*>(sr + 32 * s + 4 * lg);
-                lo[0] *= f0.x; lo[1] *= f0.y; lo[2] *= f0.z; lo[3] *= f0.w;
-                if (2 * s + 1 < NRT) {
-                    const float4 f1 = *reinterpret_cast<const float4*>(sr + 32 * s + 16 + 4 * lg);
-                    hi[0] *= f1.x; hi[1] *= f1.y; hi[2] *= f1.z; hi[3] *= f1.w;
-                }
-            }
-            bS[s] = cat8(cvt4(lo), cvt4(hi));
-        }
-    };
-    // LDS operands of every MFMA of a phase are read in one batch before the
-    // products (one exposed LDS latency per batch instead of one per product);
-    // Khat of the next chunk is fetched during the current chunk's phase 2.
+    // ---- operands of one chunk, grouped by the phase that consumes them ----
+    // kFused loads each group right before its phase; kChain issues the next
+    // group's LDS reads before each phase's products (scheduling barriers keep
+    // that order), so LDS latency overlaps the matrix-core work.
     typedef bf16x8 KFrag[4][NKS];
-    auto load_kf = [&](int c, KFrag& kf) {
+    struct OpsA {
+        KFrag kf;                     // Khat rows 16 rt + lr, permuted k
+        float4 sr[KDA ? NRT : 1];     // KDA: 2^R of S rows 16 r + 4 lg + i
+        float4 b4[4], e4[4];          // beta_t, GDN 2^G_t, rows t = 16 rt + 4 lg + i
+        bf16x4 Df[4], Af[6];          // kFused: D_r^{-1} and -A_rk; kChain: blocks of (I + A)^{-1}
+    };
+    struct OpsB {
+        bf16x8 qf[4][NKS], pf[6];     // Qhat rows 16 rt + lr; P pieces (rt, s) with 2 s <= rt
+        float egt[4];                 // GDN 2^G_t of row t = 16 rt + lr
+        bf16x8 kt[NRT][2];            // Ktil^T rows 16 r + lr, permuted k (tokens)
+        float4 ek[2][2];              // GDN 2^(G_end - G_t), U rows 32 s + 16 h + 4 lg + i
+        float4 ge[KDA ? NRT : 1];     // 2^G_end (KDA: of S rows 16 r + 4 lg + i)
+    };
+    auto load_a1 = [&](int c, OpsA& A) {
         const bf16_t* Kh = bfp(c, L::oKh);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int s = 0; s < NKS; ++s)
-                kf[rt][s] = lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
+                A.kf[rt][s] = lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
+        if constexpr (KDA) {
+            const float* sr = f32p(c, L::oSref);
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) A.sr[r] = *reinterpret_cast<const float4*>(sr + 16 * r + 4 * lg);
+        }
     };
-    // phase 1: Khat S -> X -> U (blocked forward substitution)
-    auto serial_a = [&](int c, const uint32_t (&V)[4][4], const KFrag& kf) {
+    auto load_a2 = [&](int c, OpsA& A) {
         const float* sb = f32p(c, L::oBeta);
         const float* eg = f32p(c, L::oEg);
         const bf16_t* At = bfp(c, L::oA);
         const bf16_t* Dt = bfp(c, L::oD);
-        float4 b4[4], e4[4];
-        bf16x4 Af[6], Df[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            b4[rt] = *reinterpret_cast<const float4*>(sb + 16 * rt + 4 * lg);
-            e4[rt] = KDA ? make_float4(1.f, 1.f, 1.f, 1.f)
-                         : *reinterpret_cast<const float4*>(eg + 16 * rt + 4 * lg);
-            Df[rt] = lds4(Dt + rt * 16 * L::PD + lr * L::PD + 4 * lg);
+            A.b4[rt] = *reinterpret_cast<const float4*>(sb + 16 * rt + 4 * lg);
+            A.e4[rt] = KDA ? make_float4(1.f, 1.f, 1.f, 1.f)
+                           : *reinterpret_cast<const float4*>(eg + 16 * rt + 4 * lg);
+            A.Df[rt] = lds4(Dt + rt * 16 * L::PD + lr * L::PD + 4 * lg);
         }
 #pragma unroll
-        for (int x = 0; x < 6; ++x) Af[x] = lds4(At + x * 16 * L::PD + lr * L::PD + 4 * lg);
-        build_bS(c);
-        f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-        for (int s = 0; s < NKS; ++s)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(kf[rt][s], bS[s], acc[rt]);
-        f32x4 X[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const float bb[4] = {b4[rt].x, b4[rt].y, b4[rt].z, b4[rt].w};
-            const float ee[4] = {e4[rt].x, e4[rt].y, e4[rt].z, e4[rt].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float vv = (lr & 1) ? bf_hi(V[rt][i]) : bf_lo(V[rt][i]);
-                X[rt][i] = bb[i] * (vv - ee[i] * acc[rt][i]);
-            }
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x4 w = X[rt];
-#pragma unroll
-            for (int kb = 0; kb < rt; ++kb) w = mfma16(Af[atile(rt, kb)], Ub[kb], w);
-            Uf[rt] = mfma16(Df[rt], cvt4(w), zero4());
-            Ub[rt] = cvt4(Uf[rt]);
-        }
+        for (int x = 0; x < 6; ++x) A.Af[x] = lds4(At + x * 16 * L::PD + lr * L::PD + 4 * lg);
     };
-    // phase 2: O = scale (Qhat S + P U) (computed transposed), and
-    // S <- diag(2^G_end) S + Ktil^T U
-    auto serial_b = [&](int c) {
-        const int t0 = c * kC, n = min(kC, T - t0);
-        const bf16_t* ob = o + (vrow0 + static_cast<size_t>(t0) * H) * DV + col0;  // uniform
-        const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob, static_cast<uint32_t>(n * H * DV * 2));
+    auto load_b1 = [&](int c, OpsB& Bo) {
         const bf16_t* Qh = bfp(c, L::oQh);
         const bf16_t* Pt = bfp(c, L::oP);
-        const bf16_t* Kt = bfp(c, L::oKt);
         const float* eg = f32p(c, L::oEg);
-        const float* ek = f32p(c, L::oEk);
-        const float* ge = f32p(c, L::oGend);
         const bf16x4 z4 = cvt4(zero4());
-        // batch 1: Qhat fragments and the P tiles
-        bf16x8 qf[4][NKS], pf[6];
-        float egt[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
             for (int s = 0; s < NKS; ++s)
-                qf[rt][s] = lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
-            egt[rt] = KDA ? 1.f : eg[16 * rt + lr];
+                Bo.qf[rt][s] = lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
+            Bo.egt[rt] = KDA ? 1.f : eg[16 * rt + lr];
         }
         // P pieces: (rt, s) for 2 s <= rt -> 6 pieces
 #pragma unroll
@@ -671,39 +693,124 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
                     const bf16x4 plo = lds4(Pt + ptile(rt, 2 * s) * 16 * L::PD + lr * L::PD + 4 * lg);
                     const bf16x4 phi = (2 * s + 1 <= rt)
                         ? lds4(Pt + ptile(rt, 2 * s + 1) * 16 * L::PD + lr * L::PD + 4 * lg) : z4;
-                    pf[x++] = cat8(plo, phi);
+                    Bo.pf[x++] = cat8(plo, phi);
                 }
+    };
+    auto load_b2 = [&](int c, OpsB& Bo) {
+        const bf16_t* Kt = bfp(c, L::oKt);
+        const float* ek = f32p(c, L::oEk);
+        const float* ge = f32p(c, L::oGend);
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) Bo.kt[r][s] = lds_perm(Kt + (16 * r + lr) * L::PT + 32 * s + 4 * lg);
+        if constexpr (KDA) {
+#pragma unroll
+            for (int r = 0; r < NRT; ++r) Bo.ge[r] = *reinterpret_cast<const float4*>(ge + 16 * r + 4 * lg);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    Bo.ek[s][hh] = *reinterpret_cast<const float4*>(ek + 32 * s + 16 * hh + 4 * lg);
+            Bo.ge[0] = make_float4(ge[0], 0.f, 0.f, 0.f);
+        }
+    };
+
+    // phase 1: Khat S (the B operands are S rounded to bf16; KDA: rows scaled by 2^R)
+    auto phase_ks = [&](const OpsA& A, f32x4 (&acc)[4]) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            f32x4 lo = S[2 * s];
+            f32x4 hi = (2 * s + 1 < NRT) ? S[2 * s + 1] : zero4();
+            if constexpr (KDA) {
+                const float4 f0 = A.sr[2 * s];
+                lo[0] *= f0.x; lo[1] *= f0.y; lo[2] *= f0.z; lo[3] *= f0.w;
+                if (2 * s + 1 < NRT) {
+                    const float4 f1 = A.sr[2 * s + 1 < NRT ? 2 * s + 1 : 0];
+                    hi[0] *= f1.x; hi[1] *= f1.y; hi[2] *= f1.z; hi[3] *= f1.w;
+                }
+            }
+            bS[s] = cat8(cvt4(lo), cvt4(hi));
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = zero4();
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(A.kf[rt][s], bS[s], acc[rt]);
+    };
+    // phase 2: X = diag(beta) (V - Khat S), U = (I + A)^{-1} X
+    auto phase_u = [&](const OpsA& A, const f32x4 (&acc)[4], const uint32_t (&V)[4][4]) {
+        f32x4 X[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const float bb[4] = {A.b4[rt].x, A.b4[rt].y, A.b4[rt].z, A.b4[rt].w};
+            const float ee[4] = {A.e4[rt].x, A.e4[rt].y, A.e4[rt].z, A.e4[rt].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float vv = (lr & 1) ? bf_hi(V[rt][i]) : bf_lo(V[rt][i]);
+                X[rt][i] = bb[i] * (vv - ee[i] * acc[rt][i]);
+            }
+        }
+        if constexpr (MODE == kChain) {
+            // U_r = sum_{k <= r} T_rk X_k: independent products (no chain)
+            bf16x4 Xb[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) Xb[rt] = cvt4(X[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 w = mfma16(A.Df[rt], Xb[rt], zero4());
+#pragma unroll
+                for (int kb = 0; kb < rt; ++kb) w = mfma16(A.Af[atile(rt, kb)], Xb[kb], w);
+                Uf[rt] = w;
+                Ub[rt] = cvt4(w);
+            }
+        } else {
+            // blocked forward substitution: U_r = D_r^{-1} (X_r - sum_{k<r} A_rk U_k)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 w = X[rt];
+#pragma unroll
+                for (int kb = 0; kb < rt; ++kb) w = mfma16(A.Af[atile(rt, kb)], Ub[kb], w);
+                Uf[rt] = mfma16(A.Df[rt], cvt4(w), zero4());
+                Ub[rt] = cvt4(Uf[rt]);
+            }
+        }
+    };
+    // phase 3: O = scale (Qhat S + P U), computed transposed (a lane holds 4
+    // consecutive columns of one token row)
+    auto phase_o = [&](int c, const OpsB& Bo) {
+        const int t0 = c * kC, n = min(kC, T - t0);
+        const bf16_t* ob = o + (vrow0 + static_cast<size_t>(t0) * H) * DV + col0;  // uniform
+        const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob, static_cast<uint32_t>(n * H * DV * 2));
         f32x4 oacc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
         for (int s = 0; s < NKS; ++s)
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) oacc[rt] = mfma32(bS[s], qf[rt][s], oacc[rt]);
+            for (int rt = 0; rt < 4; ++rt) oacc[rt] = mfma32(bS[s], Bo.qf[rt][s], oacc[rt]);
         const bf16x8 u01 = cat8(Ub[0], Ub[1]), u23 = cat8(Ub[2], Ub[3]);
 #pragma unroll
         for (int rt = 0, x = 0; rt < 4; ++rt) {
-            if constexpr (!KDA) oacc[rt] *= egt[rt];
-            oacc[rt] = mfma32(u01, pf[x++], oacc[rt]);
-            if (rt >= 2) oacc[rt] = mfma32(u23, pf[x++], oacc[rt]);
+            if constexpr (!KDA) oacc[rt] *= Bo.egt[rt];
+            oacc[rt] = mfma32(u01, Bo.pf[x++], oacc[rt]);
+            if (rt >= 2) oacc[rt] = mfma32(u23, Bo.pf[x++], oacc[rt]);
             const int t = 16 * rt + lr;
             const uint32_t off = t < n ? static_cast<uint32_t>((t * H * DV + 4 * lg) * 2) : kOOB;
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(oacc[rt] * scale)), ors,
                                                   off, 0, 0);
         }
-        // batch 2: Ktil^T fragments
-        bf16x8 kt[NRT][2];
-#pragma unroll
-        for (int r = 0; r < NRT; ++r)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) kt[r][s] = lds_perm(Kt + (16 * r + lr) * L::PT + 32 * s + 4 * lg);
+    };
+    // phase 4: S <- diag(2^G_end) S + Ktil^T U
+    auto phase_s = [&](const OpsB& Bo) {
         bf16x8 bU[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             if constexpr (KDA) {
                 bU[s] = cat8(Ub[2 * s], Ub[2 * s + 1]);
             } else {
-                const float4 k0 = *reinterpret_cast<const float4*>(ek + 32 * s + 4 * lg);
-                const float4 k1 = *reinterpret_cast<const float4*>(ek + 32 * s + 16 + 4 * lg);
                 f32x4 lo = Uf[2 * s], hi = Uf[2 * s + 1];
+                const float4 k0 = Bo.ek[s][0], k1 = Bo.ek[s][1];
                 lo[0] *= k0.x; lo[1] *= k0.y; lo[2] *= k0.z; lo[3] *= k0.w;
                 hi[0] *= k1.x; hi[1] *= k1.y; hi[2] *= k1.z; hi[3] *= k1.w;
                 bU[s] = cat8(cvt4(lo), cvt4(hi));
@@ -712,16 +819,15 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
 #pragma unroll
         for (int r = 0; r < NRT; ++r) {
             if constexpr (KDA) {
-                const float4 g4 = *reinterpret_cast<const float4*>(ge + 16 * r + 4 * lg);
-                S[r][0] *= g4.x; S[r][1] *= g4.y; S[r][2] *= g4.z; S[r][3] *= g4.w;
+                S[r][0] *= Bo.ge[r].x; S[r][1] *= Bo.ge[r].y; S[r][2] *= Bo.ge[r].z; S[r][3] *= Bo.ge[r].w;
             } else {
-                S[r] *= ge[0];
+                S[r] *= Bo.ge[0].x;
             }
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int r = 0; r < NRT; ++r) S[r] = mfma32(kt[r][s], bU[s], S[r]);
+            for (int r = 0; r < NRT; ++r) S[r] = mfma32(Bo.kt[r][s], bU[s], S[r]);
     };
 
     // ================= pipeline =================
@@ -763,20 +869,22 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
         prep_gate(pc, pin);
         lds_barrier();
         prep_ap(pc);
+        lds_barrier();
+        if (wave == 0) prep_t(pc);
     } else if constexpr (MODE == kChain) {
-        if (wave < kLoadWaves) {
+        if (wave < kLoad) {
             // Loader: image of chunk c -> LDS buffer c & 1, 1 KB per instruction
             // (lane l moves bytes [16 l, 16 l + 16) of each kilobyte).
             auto copy_in = [&](int c) {
                 const unsigned char* src = imgp(c) + 16 * lane;
                 auto dst = (__attribute__((address_space(3))) unsigned char*)(smem + (c & 1) * L::IMG);
-                for (int j = wave; j < L::IMG / 1024; j += kLoadWaves)
+                for (int j = wave; j < L::IMG / 1024; j += kLoad)
                     __builtin_amdgcn_global_load_lds(src + 1024 * j, dst + 1024 * j, 16, 0, 0);
             };
-            copy_in(0);
+            copy_in(c0);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copy has landed in LDS
             lds_barrier();
-            for (int i = 0; i < nch; ++i) {
+            for (int i = c0; i < nch; ++i) {
                 if (i + 1 < nch) copy_in(i + 1);
                 __builtin_amdgcn_s_waitcnt(0x0F70);
                 lds_barrier();
@@ -784,15 +892,26 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
         } else {
             serial_init();
             uint32_t vr[4][4];  // v of the next chunk, prefetched one step ahead
-            if (nch > 0) serial_vload(0, vr);
+            if (c0 < nch) serial_vload(c0, vr);
             dummy_stores();
-            lds_barrier();  // chunk 0 is in buffer 0
-            for (int i = 0; i < nch; ++i) {
-                KFrag kf;
-                load_kf(i, kf);
-                serial_a(i, vr, kf);
+            lds_barrier();  // chunk c0 is in its buffer
+            for (int i = c0; i < nch; ++i) {
+                OpsA A;
+                OpsB Bo;
+                f32x4 acc[4];
+                load_a1(i, A);
+                __builtin_amdgcn_sched_barrier(0);
+                load_a2(i, A);
+                phase_ks(A, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                load_b1(i, Bo);
+                phase_u(A, acc, vr);
                 if (i + 1 < nch) serial_vload(i + 1, vr);
-                serial_b(i);
+                __builtin_amdgcn_sched_barrier(0);
+                load_b2(i, Bo);
+                phase_o(i, Bo);
+                __builtin_amdgcn_sched_barrier(0);
+                phase_s(Bo);
                 lds_barrier();  // chunk i + 1 has landed; buffer i & 1 is free
             }
             serial_fini();
@@ -824,16 +943,37 @@ __global__ __launch_bounds__((block_threads<NSW, MODE>())) void prefill_bf16_ker
         lds_barrier();
         lds_barrier();
         for (int i = 0; i < nch; ++i) {
-            KFrag kf;
-            load_kf(i, kf);
-            serial_a(i, vr, kf);
+            {
+                OpsA A;
+                f32x4 acc[4];
+                load_a1(i, A);
+                load_a2(i, A);
+                phase_ks(A, acc);
+                phase_u(A, acc, vr);
+            }
             if (i + 1 < nch) serial_vload(i + 1, vr);
             lds_barrier();
-            serial_b(i);
+            {
+                OpsB Bo;
+                load_b1(i, Bo);
+                phase_o(i, Bo);
+                load_b2(i, Bo);
+                phase_s(Bo);
+            }
             lds_barrier();
         }
         serial_fini();
     }
+}
+
+// Chunks per range of the split schedule: the images of one range (all heads)
+// stay within about 96 MiB, well inside the 256 MB last-level cache, so the
+// chain kernel reads what the chunk-local kernel has just written from cache.
+constexpr size_t kRangeBytes = size_t(96) << 20;
+inline int split_range_chunks(int BH, int nch, size_t img_bytes) {
+    const size_t per_chunk = static_cast<size_t>(BH) * img_bytes;
+    const size_t r = per_chunk ? kRangeBytes / per_chunk : 0;
+    return static_cast<int>(std::max<size_t>(1, std::min<size_t>(static_cast<size_t>(nch), r)));
 }
 
 template <int DK, int NSW, bool KDA>
@@ -853,22 +993,31 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
         auto kern = prefill_bf16_kernel<DK, NSW, KDA, kFused>;
         if ((e = set_lds(reinterpret_cast<const void*>(kern), L::bytes)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(block_threads<NSW, kFused>()), L::bytes, s, B, T,
-                           H, DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, nullptr);
+                           H, DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, nullptr, 0,
+                           (T + kC - 1) / kC);
         return hipGetLastError();
     }
-    // chunk-local work of every (b, h, chunk), then the recurrence
+    // Per range of chunks: the chunk-local work of every (b, h, chunk), then
+    // the recurrence through the range (state carried in state_out).
     using LP = Layout<DK, 1, KDA>;
     auto prep = prefill_bf16_kernel<DK, 1, KDA, kPrep>;
-    if ((e = set_lds(reinterpret_cast<const void*>(prep), LP::pBytes)) != hipSuccess) return e;
-    const unsigned nch = static_cast<unsigned>((T + kC - 1) / kC);
-    hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(B * H) * nch), dim3(block_threads<1, kPrep>()),
-                       LP::pBytes, s, B, T, H, DV, 1, scale, q, k, v, alpha, beta, s_in, s_out, o, img);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     auto chain = prefill_bf16_kernel<DK, NSW, KDA, kChain>;
+    if ((e = set_lds(reinterpret_cast<const void*>(prep), LP::pBytes)) != hipSuccess) return e;
     if ((e = set_lds(reinterpret_cast<const void*>(chain), L::cBytes)) != hipSuccess) return e;
-    hipLaunchKernelGGL(chain, dim3(blocks), dim3(block_threads<NSW, kChain>()), L::cBytes, s, B, T, H,
-                       DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, img);
-    return hipGetLastError();
+    const int nch = (T + kC - 1) / kC;
+    const int rc = split_range_chunks(B * H, nch, L::IMG);
+    for (int c0 = 0; c0 < nch; c0 += rc) {
+        const int c1 = std::min(nch, c0 + rc);
+        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(B * H * (c1 - c0))),
+                           dim3(block_threads<1, kPrep>()), LP::pBytes, s, B, T, H, DV, 1, scale, q, k, v,
+                           alpha, beta, s_in, s_out, o, img, c0, c1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(chain, dim3(blocks), dim3(block_threads<NSW, kChain>()), L::cBytes, s, B, T,
+                           H, DV, NS, scale, q, k, v, alpha, beta, c0 == 0 ? s_in : s_out, s_out, o,
+                           img, c0, c1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int DK, bool KDA>
@@ -927,7 +1076,8 @@ size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk) {
         case 64: img = image_bytes<64>(); break;
         default: img = image_bytes<128>(); break;
     }
-    return static_cast<size_t>(B) * H * ((T + kC - 1) / kC) * img;
+    const int nch = (T + kC - 1) / kC;
+    return static_cast<size_t>(B) * H * split_range_chunks(B * H, nch, img) * img;
 }
 
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,

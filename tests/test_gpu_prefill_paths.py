@@ -1,5 +1,8 @@
 """The two bf16 prefill schedules (fused; chunk-local kernel + chain kernel)
-give bitwise identical results, and each matches the oracle."""
+each match the oracle; they round differently (the chain kernel applies the
+block inverse (I + A)^{-1} formed by the chunk-local kernel, the fused one
+substitutes block by block), so they are compared to the oracle, not to each
+other bit for bit."""
 from dataclasses import replace
 
 import pytest
@@ -24,18 +27,32 @@ def _run(monkeypatch, path, gate, inp, scale=1.0):
 
 
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("T,dk,dv", [(1, 128, 128), (64, 128, 128), (130, 128, 128),
-                                     (1000, 128, 128), (200, 16, 16), (150, 32, 64),
-                                     (150, 64, 32), (100, 128, 16), (100, 16, 128)])
-def test_paths_bitwise_equal(monkeypatch, gate, T, dk, dv):
+                                     (200, 16, 16), (150, 32, 64), (150, 64, 32),
+                                     (100, 128, 16), (100, 16, 128)])
+def test_paths_against_oracle(monkeypatch, gate, path, T, dk, dv):
     w = replace(synth.WORKLOADS["kda_prefill_b1_t32768_h32_d128"], gate=gate, dtype="bf16",
                 dk=dk, dv=dv)
-    inp = synth.make_inputs(w, B=2, T=T, H=3, seed=300 + T + dk)
-    announce("prefill paths %s T=%d dk=%d dv=%d" % (gate, T, dk, dv))
-    o_f, s_f = _run(monkeypatch, "fused", gate, inp, scale=0.8)
-    o_s, s_s = _run(monkeypatch, "split", gate, inp, scale=0.8)
-    assert torch.equal(o_f, o_s)
-    assert torch.equal(s_f, s_s)
+    monkeypatch.setenv("GDR_PREFILL_PATH", path)
+    announce("prefill %s %s T=%d dk=%d dv=%d" % (path, gate, T, dk, dv))
+    check(gate, "bf16", synth.make_inputs(w, B=2, T=T, H=3, seed=300 + T + dk), scale=0.8)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_paths_agree_long(monkeypatch, gate):
+    """1000 tokens (16 chunks): both schedules against the oracle and each other."""
+    w = replace(synth.WORKLOADS["kda_prefill_b1_t32768_h32_d128"], gate=gate, dtype="bf16")
+    inp = synth.make_inputs(w, B=1, T=1000, H=3, seed=77)
+    announce("prefill paths %s T=1000" % gate)
+    o_f, s_f = _run(monkeypatch, "fused", gate, inp)
+    o_s, s_s = _run(monkeypatch, "split", gate, inp)
+    scale_o = float(o_f.float().abs().max())
+    scale_s = float(s_f.float().abs().max())
+    assert float((o_f.float() - o_s.float()).abs().max()) <= 2e-2 * scale_o
+    assert float((s_f - s_s).abs().max()) <= 2e-2 * scale_s
+    monkeypatch.setenv("GDR_PREFILL_PATH", "split")
+    check(gate, "bf16", inp)
 
 
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
