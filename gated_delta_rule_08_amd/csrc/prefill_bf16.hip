@@ -207,7 +207,7 @@ __device__ __forceinline__ int atile(int rt, int ct) { return rt * (rt - 1) / 2 
 
 template <int DK, int NSW, bool KDA, int MODE>
 __global__ __launch_bounds__((block_threads<NSW, MODE>()))
-__attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefill_bf16_kernel(
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<NSW, MODE>()))) void prefill_bf16_kernel(
     int B, int T, int H, int DV, int NS, float scale, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ state_in,
@@ -229,10 +229,12 @@ __attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefil
 
     const int BH = B * H;
     const int nch = c1;         // chunks run by this launch: c0 .. nch-1
-    int bh, slice = 0, pc = 0;  // pc: the chunk of a kPrep block
+    int bh, slice = 0, pc = 0, pc_end = 0;  // kPrep: chunks pc .. pc_end-1 of one head
     if constexpr (MODE == kPrep) {
-        pc = c0 + static_cast<int>(blockIdx.x) / BH;
-        bh = static_cast<int>(blockIdx.x) - (pc - c0) * BH;
+        const int g = static_cast<int>(blockIdx.x) / BH;  // NS = chunks per workgroup
+        bh = static_cast<int>(blockIdx.x) - g * BH;
+        pc = c0 + g * NS;
+        pc_end = min(c1, pc + NS);
     } else {
         const int grp = blockIdx.x / (8 * NS);
         const int rem = blockIdx.x - grp * 8 * NS;
@@ -280,19 +282,32 @@ __attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefil
             prep_lds_b(c, L::oKh, L::pKh)[t * L::PK + col] = 0;
             prep_lds_b(c, L::oQh, L::pQh)[t * L::PK + col] = 0;
             if (KDA && c == 0) Kc[t * L::PK + col] = 0;
-            if constexpr (MODE == kPrep) {  // and in the image, which the chain reads
-                reinterpret_cast<bf16_t*>(imgp(pc) + L::oKh)[t * L::PK + col] = 0;
-                reinterpret_cast<bf16_t*>(imgp(pc) + L::oQh)[t * L::PK + col] = 0;
-            }
         }
     }
+    // kPrep: the same padding in the image of chunk c, which the chain reads
+    auto zero_image_pad = [&](int c) {
+        if constexpr (L::DKP != DK && MODE == kPrep) {
+            constexpr int W = L::DKP - DK;
+            for (int idx = tid; idx < kC * W; idx += blockDim.x) {
+                const int t = idx / W, col = DK + idx % W;
+                reinterpret_cast<bf16_t*>(imgp(c) + L::oKh)[t * L::PK + col] = 0;
+                reinterpret_cast<bf16_t*>(imgp(c) + L::oQh)[t * L::PK + col] = 0;
+            }
+        }
+    };
 
     // ================= prep-wave work =================
-    // Gating layout: lane = (channel octet o, run of 4 tokens tg); the 16
-    // lanes of an octet are one DPP row, so the chunk's cumulative sum is an
-    // in-row scan.  Loads and LDS writes are 16 bytes (8 channels).
-    const int oct = tid >> 4, tg = tid & 15;
-    const bool gater = tid < 2 * DK;  // DK/8 octets x 16 lanes
+    // Lane layout for q and k: lane = (channel octet oct, run of 4 tokens
+    // tg); loads and LDS writes are 16 bytes (8 channels).
+    //  KDA: the 16 lanes of an octet are one DPP row, so each channel's
+    //       cumulative log-gate over the chunk is an in-row scan.
+    //  GDN: the octets of a row are adjacent lanes (a wave load instruction
+    //       reads whole 256-byte rows); the scalar gates of the 64 tokens are
+    //       scanned by wave 0 alone, one token per lane.
+    constexpr int OPR = DK / 8;  // octets per row
+    const int oct = KDA ? tid >> 4 : tid % OPR;
+    const int tg = KDA ? tid & 15 : tid / OPR;
+    const bool gater = tid < 2 * DK;  // DK/8 octets x 16 token runs
     const int c8 = 8 * oct;           // first channel of this lane's octet
     constexpr int NA = KDA ? 32 : 4;  // gate values per lane
     struct PrepIn {
@@ -308,6 +323,7 @@ __attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefil
         const bf16_t* qb = q + rb * DK;
         const float* ab = KDA ? alpha + rb * DK : alpha + rb;
         const float* bb = beta + rb;
+        if (gater) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tc = nn == kC ? 4 * tg + u : min(4 * tg + u, nn - 1);
@@ -319,10 +335,17 @@ __attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefil
                 const float4 x1 = *reinterpret_cast<const float4*>(ab + (ro * DK + c8 + 4));
                 R.a[8 * u + 0] = x0.x; R.a[8 * u + 1] = x0.y; R.a[8 * u + 2] = x0.z; R.a[8 * u + 3] = x0.w;
                 R.a[8 * u + 4] = x1.x; R.a[8 * u + 5] = x1.y; R.a[8 * u + 6] = x1.z; R.a[8 * u + 7] = x1.w;
-            } else {
-                R.a[u] = ab[ro];
+                R.bt[u] = bb[ro];
             }
-            R.bt[u] = bb[ro];
+        }
+        }
+        if constexpr (!KDA) {
+            if (wave == 0) {  // token = lane
+                const int tc = nn == kC ? lane : min(lane, nn - 1);
+                const unsigned ro = static_cast<unsigned>(tc * H);
+                R.a[0] = ab[ro];
+                R.bt[0] = bb[ro];
+            }
         }
     };
     // inclusive scan over the 16 lanes of a DPP row (row_shr by 1, 2, 4, 8)
@@ -348,14 +371,14 @@ __attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefil
         // kPrep: copies of Khat, Qhat and beta for the image
         bf16_t* KhI = reinterpret_cast<bf16_t*>(MODE == kPrep ? imgp(c) + L::oKh : nullptr);
         bf16_t* QhI = reinterpret_cast<bf16_t*>(MODE == kPrep ? imgp(c) + L::oQh : nullptr);
-        if (!gater) return;
+        if (KDA && !gater) return;
         // a full chunk (every chunk but a ragged last one) needs no row masks
         auto body = [&](auto full_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
             bool valid[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) valid[u] = FULL || 4 * tg + u < n;
-            if (oct == 0) {
+            if (KDA && oct == 0) {
                 float4 b4;
                 b4.x = valid[0] ? R.bt[0] : 0.f; b4.y = valid[1] ? R.bt[1] : 0.f;
                 b4.z = valid[2] ? R.bt[2] : 0.f; b4.w = valid[3] ? R.bt[3] : 0.f;
@@ -419,26 +442,25 @@ __attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefil
                 for (int e = 0; e < 8; ++e)
                     *reinterpret_cast<uint2*>(Kt + (c8 + e) * L::PT + 4 * tg) = make_uint2(ktw[e][0], ktw[e][1]);
             } else {
-                float acc = 0.f, G[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    acc += valid[u] ? fmaxf(lg2(R.a[u]), kLog2Floor) : 0.f;
-                    G[u] = acc;
+                if (wave == 0) {
+                    // scalar gates: token t = lane; inclusive scan of log2 alpha
+                    // over the wave (in-row DPP scan, then the row totals)
+                    const bool vt = FULL || lane < n;
+                    float x = vt ? fmaxf(lg2(R.a[0]), kLog2Floor) : 0.f;
+                    x = row_scan(x);
+                    const float r0 = __shfl(x, 15), r1 = __shfl(x, 31), r2 = __shfl(x, 47);
+                    const int row = lane >> 4;
+                    x += (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+                    const float end = __shfl(x, 63);
+                    sG[lane] = x;
+                    prep_out_f(c, L::oEg)[lane] = ex2(x);
+                    prep_out_f(c, L::oEk)[lane] = ex2(end - x);
+                    const float bv = vt ? R.bt[0] : 0.f;
+                    sBeta[lane] = bv;
+                    if constexpr (MODE == kPrep) prep_out_f(c, L::oBeta)[lane] = bv;
+                    if (lane == 0) prep_out_f(c, L::oGend)[0] = ex2(end);
                 }
-                const float inc = row_scan(acc);
-                const float off = inc - acc;
-                const float end = __shfl(inc, 15, 16);
-                if (oct == 0) {
-                    float4 g4, e4, k4;
-                    g4.x = off + G[0]; g4.y = off + G[1]; g4.z = off + G[2]; g4.w = off + G[3];
-                    e4.x = ex2(g4.x); e4.y = ex2(g4.y); e4.z = ex2(g4.z); e4.w = ex2(g4.w);
-                    k4.x = ex2(end - g4.x); k4.y = ex2(end - g4.y);
-                    k4.z = ex2(end - g4.z); k4.w = ex2(end - g4.w);
-                    *reinterpret_cast<float4*>(sG + 4 * tg) = g4;
-                    *reinterpret_cast<float4*>(prep_out_f(c, L::oEg) + 4 * tg) = e4;
-                    *reinterpret_cast<float4*>(prep_out_f(c, L::oEk) + 4 * tg) = k4;
-                    if (tg == 0) prep_out_f(c, L::oGend)[0] = ex2(end);
-                }
+                if (!gater) return;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int t = 4 * tg + u;
@@ -863,14 +885,22 @@ __attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefil
     };
 
     if constexpr (MODE == kPrep) {
-        // One chunk per workgroup; the outputs go straight to the image.
+        // A few consecutive chunks of one head per workgroup; the inputs of
+        // chunk c+1 are loaded into registers while chunk c is gated and
+        // multiplied, and the outputs go straight to the image.  prep_t of
+        // chunk c (wave 0) only touches its own LDS tiles, which the next
+        // chunk's products overwrite after the next barrier.
         PrepIn pin;
-        if (gater) prep_load(pc, pin);
-        prep_gate(pc, pin);
-        lds_barrier();
-        prep_ap(pc);
-        lds_barrier();
-        if (wave == 0) prep_t(pc);
+        prep_load(pc, pin);
+        for (int c = pc; c < pc_end; ++c) {
+            zero_image_pad(c);
+            prep_gate(c, pin);
+            if (c + 1 < pc_end) prep_load(c + 1, pin);
+            lds_barrier();
+            prep_ap(c);
+            lds_barrier();
+            if (wave == 0) prep_t(c);
+        }
     } else if constexpr (MODE == kChain) {
         if (wave < kLoad) {
             // Loader: image of chunk c -> LDS buffer c & 1, 1 KB per instruction
@@ -923,11 +953,11 @@ __attribute__((amdgpu_waves_per_eu(1, waves_per_simd<NSW, MODE>()))) void prefil
         // Inputs of chunk i+2 are loaded into registers while chunk i+1 is
         // gated, so the global loads overlap one whole step.
         PrepIn pin;
-        if (nch > 0 && gater) prep_load(0, pin);
+        if (nch > 0) prep_load(0, pin);
         for (int i = -1; i < nch; ++i) {
             if (i + 1 < nch) {
                 prep_gate(i + 1, pin);
-                if (i + 2 < nch && gater) prep_load(i + 2, pin);
+                if (i + 2 < nch) prep_load(i + 2, pin);
             }
             lds_barrier();
             if (i + 1 < nch) prep_ap(i + 1);
@@ -1008,9 +1038,12 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     const int rc = split_range_chunks(B * H, nch, L::IMG);
     for (int c0 = 0; c0 < nch; c0 += rc) {
         const int c1 = std::min(nch, c0 + rc);
-        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(B * H * (c1 - c0))),
-                           dim3(block_threads<1, kPrep>()), LP::pBytes, s, B, T, H, DV, 1, scale, q, k, v,
-                           alpha, beta, s_in, s_out, o, img, c0, c1);
+        // chunks per chunk-local workgroup: about two workgroups per CU
+        const int cpw = std::max(1, (B * H * (c1 - c0) + 511) / 512);
+        const int groups_per_head = (c1 - c0 + cpw - 1) / cpw;
+        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(B * H * groups_per_head)),
+                           dim3(block_threads<1, kPrep>()), LP::pBytes, s, B, T, H, DV, cpw, scale, q, k,
+                           v, alpha, beta, s_in, s_out, o, img, c0, c1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(chain, dim3(blocks), dim3(block_threads<NSW, kChain>()), L::cBytes, s, B, T,
                            H, DV, NS, scale, q, k, v, alpha, beta, c0 == 0 ? s_in : s_out, s_out, o,
