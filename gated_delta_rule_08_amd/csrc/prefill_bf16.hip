@@ -184,30 +184,48 @@ struct Layout {
     // kChain: two image buffers
     static constexpr int cBytes = 2 * IMG;
     static_assert(cBytes <= 160 * 1024, "LDS budget exceeded");
+    // GDN split: the image holds only the tiles and gate factors (the BUF
+    // range from oP on); the chain stages raw k and q rows itself, in rows of
+    // DKP bf16 whose 16-byte units are permuted by a row-dependent XOR (swz)
+    // so that 16 rows read at one column hit distinct LDS banks.
+    static constexpr int TIMG = ((BUF - oP) + 15) / 16 * 16;
+    static constexpr int lK = 0;
+    static constexpr int lQ = kC * DKP * 2;
+    static constexpr int lT = 2 * kC * DKP * 2;
+    static constexpr int lBUF = ((lT + TIMG) + 15) / 16 * 16;
+    static constexpr int lBytes = 2 * lBUF;
+    static_assert(lBytes <= 160 * 1024, "LDS budget exceeded");
+    static constexpr int U = DKP / 8;  // 16-byte units per staged row
 };
+// Unit permutation of staged row r (see Layout): position = unit ^ swz(r).
+template <int U>
+__device__ __forceinline__ int swz(int r) { return ((2 * r) | ((r >> 3) & 1)) & (U - 1); }
 
 // Chain kernel: waves that copy chunk images into LDS (they fill the SIMDs
 // the serial waves leave free; the copies of one chunk are split among them).
-template <int NSW>
-constexpr int load_waves() { return NSW >= 4 ? 1 : 4 - NSW; }
-template <int NSW, int MODE>
+// (KDA: the image holds everything; GDN ("lite"): the serial waves stage
+// the raw rows and the small tile image through their registers instead.)
+template <int NSW, bool KDA>
+constexpr int load_waves() { return !KDA ? 0 : NSW >= 4 ? 1 : 4 - NSW; }
+template <int NSW, bool KDA, int MODE>
 constexpr int block_threads() {
-    return 64 * (MODE == kPrep ? kPrepWaves : MODE == kChain ? load_waves<NSW>() + NSW : kPrepWaves + NSW);
+    return 64 * (MODE == kPrep ? kPrepWaves
+                 : MODE == kChain ? load_waves<NSW, KDA>() + NSW : kPrepWaves + NSW);
 }
 // Waves per SIMD the register allocation is sized for: a chain workgroup of
 // at most four waves has a SIMD per wave (its LDS keeps it alone on the CU),
 // so each wave may use the whole register file.
-template <int NSW, int MODE>
+template <int NSW, bool KDA, int MODE>
 constexpr int waves_per_simd() {
-    return (MODE == kChain && load_waves<NSW>() + NSW <= 4) ? 1 : 2;
+    return (MODE == kChain && load_waves<NSW, KDA>() + NSW <= 4) ? 1 : 2;
 }
 
 __device__ __forceinline__ int ptile(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }  // ct <= rt
 __device__ __forceinline__ int atile(int rt, int ct) { return rt * (rt - 1) / 2 + ct; }  // ct < rt
 
 template <int DK, int NSW, bool KDA, int MODE>
-__global__ __launch_bounds__((block_threads<NSW, MODE>()))
-__attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<NSW, MODE>()))) void prefill_bf16_kernel(
+__global__ __launch_bounds__((block_threads<NSW, KDA, MODE>()))
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_simd<NSW, KDA, MODE>()))) void prefill_bf16_kernel(
     int B, int T, int H, int DV, int NS, float scale, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ state_in,
@@ -243,16 +261,24 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
         if (bh >= BH) return;  // whole block exits before any barrier
     }
     const int b = bh / H, h = bh - b * H;
-    constexpr int kLoad = load_waves<NSW>();
+    constexpr int kLoad = load_waves<NSW, KDA>();
+    constexpr bool LITE = !KDA && MODE != kFused;  // GDN split
     constexpr int kLead = MODE == kChain ? kLoad : kPrepWaves;  // waves before the serial ones
     const bool prep = MODE == kPrep || (MODE == kFused && wave < kPrepWaves);
 
     // Chunk buffers: kFused / kChain keep two in LDS (chunk c uses c & 1).
-    constexpr int kStride = MODE == kChain ? L::IMG : L::BUF;
-    auto bfp = [&](int c, int off) { return reinterpret_cast<bf16_t*>(smem + (c & 1) * kStride + off); };
-    auto f32p = [&](int c, int off) { return reinterpret_cast<float*>(smem + (c & 1) * kStride + off); };
+    constexpr int kStride = MODE == kChain ? (LITE ? L::lBUF : L::IMG) : L::BUF;
+    // LITE chain buffers keep the tile image at lT (image offset = BUF offset - oP)
+    constexpr int kTileShift = (LITE && MODE == kChain) ? L::lT - L::oP : 0;
+    auto bfp = [&](int c, int off) {
+        return reinterpret_cast<bf16_t*>(smem + (c & 1) * kStride + off + kTileShift);
+    };
+    auto f32p = [&](int c, int off) {
+        return reinterpret_cast<float*>(smem + (c & 1) * kStride + off + kTileShift);
+    };
     // The image of chunk c of this head (kPrep writes it, kChain reads it).
-    auto imgp = [&](int c) { return img + (static_cast<size_t>(bh) * (c1 - c0) + (c - c0)) * L::IMG; };
+    constexpr int kImg = LITE ? L::TIMG : L::IMG;  // image bytes per (head, chunk)
+    auto imgp = [&](int c) { return img + (static_cast<size_t>(bh) * (c1 - c0) + (c - c0)) * kImg; };
     // Where the prep work reads and writes.  kFused: the LDS buffer of the
     // chunk.  kPrep: what the A/P products and the inverses read sits in LDS
     // (and Khat, Qhat, beta are also written to the image); everything else
@@ -262,11 +288,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
         else return bfp(c, off_fused);
     };
     auto prep_out_b = [&](int c, int off) {
-        if constexpr (MODE == kPrep) return reinterpret_cast<bf16_t*>(imgp(c) + off);
+        if constexpr (MODE == kPrep) return reinterpret_cast<bf16_t*>(imgp(c) + off - (LITE ? L::oP : 0));
         else return bfp(c, off);
     };
     auto prep_out_f = [&](int c, int off) {
-        if constexpr (MODE == kPrep) return reinterpret_cast<float*>(imgp(c) + off);
+        if constexpr (MODE == kPrep) return reinterpret_cast<float*>(imgp(c) + off - (LITE ? L::oP : 0));
         else return f32p(c, off);
     };
     bf16_t* Kc = reinterpret_cast<bf16_t*>(smem + (MODE == kPrep ? L::pKc : L::oKc));  // KDA only
@@ -286,7 +312,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
     }
     // kPrep: the same padding in the image of chunk c, which the chain reads
     auto zero_image_pad = [&](int c) {
-        if constexpr (L::DKP != DK && MODE == kPrep) {
+        if constexpr (L::DKP != DK && MODE == kPrep && !LITE) {
             constexpr int W = L::DKP - DK;
             for (int idx = tid; idx < kC * W; idx += blockDim.x) {
                 const int t = idx / W, col = DK + idx % W;
@@ -366,11 +392,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
         const int n = min(kC, T - c * kC);
         bf16_t* Kh = prep_lds_b(c, L::oKh, L::pKh);
         bf16_t* Qh = prep_lds_b(c, L::oQh, L::pQh);
-        bf16_t* Kt = prep_out_b(c, L::oKt);
+        bf16_t* Kt = LITE ? nullptr : prep_out_b(c, L::oKt);  // the lite image has no K^T
         float* sBeta = reinterpret_cast<float*>(prep_lds_b(c, L::oBeta, L::pBeta));
         // kPrep: copies of Khat, Qhat and beta for the image
-        bf16_t* KhI = reinterpret_cast<bf16_t*>(MODE == kPrep ? imgp(c) + L::oKh : nullptr);
-        bf16_t* QhI = reinterpret_cast<bf16_t*>(MODE == kPrep ? imgp(c) + L::oQh : nullptr);
+        bf16_t* KhI = reinterpret_cast<bf16_t*>(MODE == kPrep && !LITE ? imgp(c) + L::oKh : nullptr);
+        bf16_t* QhI = reinterpret_cast<bf16_t*>(MODE == kPrep && !LITE ? imgp(c) + L::oQh : nullptr);
         if (KDA && !gater) return;
         // a full chunk (every chunk but a ragged last one) needs no row masks
         auto body = [&](auto full_tag) {
@@ -466,14 +492,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
                     const int t = 4 * tg + u;
                     *reinterpret_cast<uint4*>(Kh + t * L::PK + c8) = kz[u];
                     *reinterpret_cast<uint4*>(Qh + t * L::PK + c8) = qz[u];
-                    if constexpr (MODE == kPrep) {
+                    if constexpr (MODE == kPrep && !LITE) {
                         *reinterpret_cast<uint4*>(KhI + t * L::PK + c8) = kz[u];
                         *reinterpret_cast<uint4*>(QhI + t * L::PK + c8) = qz[u];
                     }
                 }
                 // K^T: channel c8 + e, tokens 4 tg .. 4 tg + 3
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
+                for (int e = 0; e < 8 && !LITE; ++e) {
                     const uint32_t x0 = bf16_half(kz[0], e), x1 = bf16_half(kz[1], e);
                     const uint32_t x2 = bf16_half(kz[2], e), x3 = bf16_half(kz[3], e);
                     *reinterpret_cast<uint2*>(Kt + (c8 + e) * L::PT + 4 * tg) =
@@ -507,6 +533,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
         const int rA = wave < 2 ? 3 : 2;  // first row tile: ct = 0..rA
         const int rB = wave < 2 ? 0 : 1;  // second row tile: ct = 0..rB
         const bf16_t* M = isP ? Qh : Kh;
+        // scalars of the epilogues, read before the products
+        const float btA = sb[16 * rA + lr], btB = sb[16 * rB + lr];
+        float gtA = 0.f, gtB = 0.f;
+        float4 gj4[4];
+        if constexpr (!KDA) {
+            gtA = sG[16 * rA + lr];
+            gtB = sG[16 * rB + lr];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) gj4[ct] = *reinterpret_cast<const float4*>(sG + 16 * ct + 4 * lg);
+        }
         f32x4 accA[4] = {zero4(), zero4(), zero4(), zero4()};
         f32x4 accB[2] = {zero4(), zero4()};
 #pragma unroll
@@ -524,14 +560,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
             for (int ct = 0; ct < 2; ++ct)
                 if (ct <= rB) accB[ct] = mfma32(kr[ct], mB, accB[ct]);
         }
-        auto epilogue = [&](int rt, int ct, const f32x4& acc) {
+        auto epilogue = [&](int rt, int ct, const f32x4& acc, float bt, float gt) {
             const int t = 16 * rt + lr;
-            const float bt = sb[t];
-            float gt = 0.f, gj[4] = {0.f, 0.f, 0.f, 0.f};
+            float gj[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (!KDA) {
-                gt = sG[t];
-                const float4 g4 = *reinterpret_cast<const float4*>(sG + 16 * ct + 4 * lg);
-                gj[0] = g4.x; gj[1] = g4.y; gj[2] = g4.z; gj[3] = g4.w;
+                gj[0] = gj4[ct].x; gj[1] = gj4[ct].y; gj[2] = gj4[ct].z; gj[3] = gj4[ct].w;
             }
             f32x4 val;
 #pragma unroll
@@ -553,10 +586,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
         };
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
-            if (ct <= rA) epilogue(rA, ct, accA[ct]);
+            if (ct <= rA) epilogue(rA, ct, accA[ct], btA, gtA);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
-            if (ct <= rB) epilogue(rB, ct, accB[ct]);
+            if (ct <= rB) epilogue(rB, ct, accB[ct], btB, gtB);
         // D_r^{-1} = (I + A_rr)^{-1}: lanes 0..15 invert block rA, lanes 16..31
         // block rB; lane c solves column c by right-looking forward
         // substitution (x_i -= A_ij x_j for all i > j at step j).
@@ -567,14 +600,26 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = (i == cl) ? 1.f : 0.f;
+            // columns of A_rr are read three steps ahead of their use (only
+            // the float4 groups holding rows below the diagonal)
+            float4 col[3][4];
+            auto load_col = [&](int j, float4 (&dst)[4]) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4)
+                    if (4 * i4 + 3 > j) dst[i4] = *reinterpret_cast<const float4*>(scr + j * L::PS + 4 * i4);
+            };
+            load_col(0, col[0]);
+            load_col(1, col[1]);
+            load_col(2, col[2]);
 #pragma unroll
             for (int j = 0; j < 15; ++j) {
                 float a[16];
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
-                    const float4 r = *reinterpret_cast<const float4*>(scr + j * L::PS + 4 * i4);
+                    const float4 r = col[j % 3][i4];
                     a[4 * i4] = r.x; a[4 * i4 + 1] = r.y; a[4 * i4 + 2] = r.z; a[4 * i4 + 3] = r.w;
                 }
+                if (j + 3 < 15) load_col(j + 3, col[j % 3]);
 #pragma unroll
                 for (int i = j + 1; i < 16; ++i) x[i] -= a[i] * x[j];
             }
@@ -666,7 +711,31 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
         float4 ek[2][2];              // GDN 2^(G_end - G_t), U rows 32 s + 16 h + 4 lg + i
         float4 ge[KDA ? NRT : 1];     // 2^G_end (KDA: of S rows 16 r + 4 lg + i)
     };
+    // LITE chain: fragments of the staged raw rows (unit-permuted, see swz)
+    auto stg = [&](int c, int region) { return smem + (c & 1) * kStride + region; };
+    auto perm_frag = [&](const unsigned char* base, int t, int e) {  // elements e..e+3, e+16..e+19 of row t
+        const int sw = swz<L::U>(t);
+        const unsigned char* row = base + t * (L::DKP * 2);
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 16 * ((e >> 3) ^ sw) + 2 * (e & 7));
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 * (((e + 16) >> 3) ^ sw) + 2 * (e & 7));
+        return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
+    };
+    // transposing read: the 16 lanes of a group address 4 rows (lr >> 2) at
+    // 4 column quads (lr & 3); lane m receives column e0 + m of the 4 rows
+    auto tr_frag = [&](const unsigned char* base, int t, int e) {
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const unsigned char* p = base + t * (L::DKP * 2) + 16 * ((e >> 3) ^ swz<L::U>(t)) + 2 * (e & 7);
+        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+    };
     auto load_a1 = [&](int c, OpsA& A) {
+        if constexpr (LITE && MODE == kChain) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int s = 0; s < NKS; ++s)
+                    A.kf[rt][s] = perm_frag(stg(c, L::lK), 16 * rt + lr, 32 * s + 4 * lg);
+            return;
+        }
         const bf16_t* Kh = bfp(c, L::oKh);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -703,7 +772,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
         for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
             for (int s = 0; s < NKS; ++s)
-                Bo.qf[rt][s] = lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
+                Bo.qf[rt][s] = (LITE && MODE == kChain)
+                    ? perm_frag(stg(c, L::lQ), 16 * rt + lr, 32 * s + 4 * lg)
+                    : lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
             Bo.egt[rt] = KDA ? 1.f : eg[16 * rt + lr];
         }
         // P pieces: (rt, s) for 2 s <= rt -> 6 pieces
@@ -725,7 +796,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
 #pragma unroll
         for (int r = 0; r < NRT; ++r)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) Bo.kt[r][s] = lds_perm(Kt + (16 * r + lr) * L::PT + 32 * s + 4 * lg);
+            for (int s = 0; s < 2; ++s) {
+                if constexpr (LITE && MODE == kChain) {
+                    const int t = 32 * s + 4 * lg + (lr >> 2), e = 16 * r + 4 * (lr & 3);
+                    Bo.kt[r][s] = cat8(tr_frag(stg(c, L::lK), t, e), tr_frag(stg(c, L::lK), t + 16, e));
+                } else {
+                    Bo.kt[r][s] = lds_perm(Kt + (16 * r + lr) * L::PT + 32 * s + 4 * lg);
+                }
+            }
         if constexpr (KDA) {
 #pragma unroll
             for (int r = 0; r < NRT; ++r) Bo.ge[r] = *reinterpret_cast<const float4*>(ge + 16 * r + 4 * lg);
@@ -921,11 +999,85 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
             }
         } else {
             serial_init();
+            // LITE: each serial wave stages its share of the next chunk's raw
+            // k and q rows (range-checked buffer loads: rows past a ragged end
+            // read as zeros) and of its tile image through registers
+            constexpr int NUK = kC * (DK / 8);  // 16-byte units of k (or q) rows
+            constexpr int NUI = L::TIMG / 16;
+            constexpr int NT = NSW * 64;
+            constexpr int XK = LITE ? (NUK + NT - 1) / NT : 1, XI = LITE ? (NUI + NT - 1) / NT : 1;
+            const int sl = sw * 64 + lane;
+            // (register vectors, not arrays, so the staging stays in registers)
+            typedef unsigned int VK __attribute__((ext_vector_type(4 * XK)));
+            typedef unsigned int VI __attribute__((ext_vector_type(4 * XI)));
+            VK stk, stq;
+            VI sti;
+            auto stage_load = [&](int c) {
+                if constexpr (LITE) {
+                    const int t0 = c * kC, nn = min(kC, T - t0);
+                    const size_t rb = tok0 + static_cast<size_t>(t0) * H;
+                    const uint32_t range = static_cast<uint32_t>(((nn - 1) * H * DK + DK) * 2);
+                    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + rb * DK, range);
+                    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + rb * DK, range);
+#pragma unroll
+                    for (int x = 0; x < XK; ++x) {
+                        const int g = x * NT + sl, r = g / (DK / 8), u = g % (DK / 8);
+                        const uint32_t off = g < NUK ? static_cast<uint32_t>((r * H * DK + 8 * u) * 2) : kOOB;
+                        const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                        const uint4 bq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+                        stk[4 * x] = a.x; stk[4 * x + 1] = a.y; stk[4 * x + 2] = a.z; stk[4 * x + 3] = a.w;
+                        stq[4 * x] = bq.x; stq[4 * x + 1] = bq.y; stq[4 * x + 2] = bq.z; stq[4 * x + 3] = bq.w;
+                    }
+                    const uint4* src = reinterpret_cast<const uint4*>(imgp(c));
+#pragma unroll
+                    for (int x = 0; x < XI; ++x) {
+                        const int m = x * NT + sl;
+                        const uint4 a = src[m < NUI ? m : 0];
+                        sti[4 * x] = a.x; sti[4 * x + 1] = a.y; sti[4 * x + 2] = a.z; sti[4 * x + 3] = a.w;
+                    }
+                }
+            };
+            auto stage_store = [&](int c) {
+                if constexpr (LITE) {
+                    unsigned char* base = smem + (c & 1) * kStride;
+#pragma unroll
+                    for (int x = 0; x < XK; ++x) {
+                        const int g = x * NT + sl, r = g / (DK / 8), u = g % (DK / 8);
+                        if (g < NUK) {
+                            const int pos = (r * L::DKP + 8 * (u ^ swz<L::U>(r))) * 2;
+                            *reinterpret_cast<uint4*>(base + L::lK + pos) =
+                                make_uint4(stk[4 * x], stk[4 * x + 1], stk[4 * x + 2], stk[4 * x + 3]);
+                            *reinterpret_cast<uint4*>(base + L::lQ + pos) =
+                                make_uint4(stq[4 * x], stq[4 * x + 1], stq[4 * x + 2], stq[4 * x + 3]);
+                        }
+                    }
+#pragma unroll
+                    for (int x = 0; x < XI; ++x) {
+                        const int m = x * NT + sl;
+                        if (m < NUI)
+                            *reinterpret_cast<uint4*>(base + L::lT + 16 * m) =
+                                make_uint4(sti[4 * x], sti[4 * x + 1], sti[4 * x + 2], sti[4 * x + 3]);
+                    }
+                }
+            };
+            if constexpr (LITE && L::DKP != DK) {
+                // staged rows are DKP wide: zero both buffers once (pad units are never written)
+                for (int idx = tid; idx < 2 * L::lT / 16; idx += blockDim.x) {
+                    const int bsel = idx / (L::lT / 16), rem16 = idx % (L::lT / 16);
+                    *reinterpret_cast<uint4*>(smem + bsel * kStride + 16 * rem16) = make_uint4(0, 0, 0, 0);
+                }
+                lds_barrier();
+            }
+            if (c0 < nch) {
+                stage_load(c0);
+                stage_store(c0);
+            }
             uint32_t vr[4][4];  // v of the next chunk, prefetched one step ahead
             if (c0 < nch) serial_vload(c0, vr);
             dummy_stores();
             lds_barrier();  // chunk c0 is in its buffer
             for (int i = c0; i < nch; ++i) {
+                if (i + 1 < nch) stage_load(i + 1);
                 OpsA A;
                 OpsB Bo;
                 f32x4 acc[4];
@@ -942,6 +1094,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, MODE>(), waves_per_simd<N
                 phase_o(i, Bo);
                 __builtin_amdgcn_sched_barrier(0);
                 phase_s(Bo);
+                if (i + 1 < nch) stage_store(i + 1);
                 lds_barrier();  // chunk i + 1 has landed; buffer i & 1 is free
             }
             serial_fini();
@@ -1022,7 +1175,7 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     if (!img) {
         auto kern = prefill_bf16_kernel<DK, NSW, KDA, kFused>;
         if ((e = set_lds(reinterpret_cast<const void*>(kern), L::bytes)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(blocks), dim3(block_threads<NSW, kFused>()), L::bytes, s, B, T,
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(block_threads<NSW, KDA, kFused>()), L::bytes, s, B, T,
                            H, DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, nullptr, 0,
                            (T + kC - 1) / kC);
         return hipGetLastError();
@@ -1032,20 +1185,21 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     using LP = Layout<DK, 1, KDA>;
     auto prep = prefill_bf16_kernel<DK, 1, KDA, kPrep>;
     auto chain = prefill_bf16_kernel<DK, NSW, KDA, kChain>;
+    constexpr int chain_lds = KDA ? L::cBytes : L::lBytes;
     if ((e = set_lds(reinterpret_cast<const void*>(prep), LP::pBytes)) != hipSuccess) return e;
-    if ((e = set_lds(reinterpret_cast<const void*>(chain), L::cBytes)) != hipSuccess) return e;
+    if ((e = set_lds(reinterpret_cast<const void*>(chain), chain_lds)) != hipSuccess) return e;
     const int nch = (T + kC - 1) / kC;
-    const int rc = split_range_chunks(B * H, nch, L::IMG);
+    const int rc = split_range_chunks(B * H, nch, KDA ? L::IMG : L::TIMG);
     for (int c0 = 0; c0 < nch; c0 += rc) {
         const int c1 = std::min(nch, c0 + rc);
         // chunks per chunk-local workgroup: about two workgroups per CU
         const int cpw = std::max(1, (B * H * (c1 - c0) + 511) / 512);
         const int groups_per_head = (c1 - c0 + cpw - 1) / cpw;
         hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(B * H * groups_per_head)),
-                           dim3(block_threads<1, kPrep>()), LP::pBytes, s, B, T, H, DV, cpw, scale, q, k,
+                           dim3(block_threads<1, KDA, kPrep>()), LP::pBytes, s, B, T, H, DV, cpw, scale, q, k,
                            v, alpha, beta, s_in, s_out, o, img, c0, c1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(chain, dim3(blocks), dim3(block_threads<NSW, kChain>()), L::cBytes, s, B, T,
+        hipLaunchKernelGGL(chain, dim3(blocks), dim3(block_threads<NSW, KDA, kChain>()), chain_lds, s, B, T,
                            H, DV, NS, scale, q, k, v, alpha, beta, c0 == 0 ? s_in : s_out, s_out, o,
                            img, c0, c1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1075,7 +1229,9 @@ hipError_t dispatch_gate(int kda, int dvs, int B, int T, int H, int DV, float sc
 }
 
 template <int DK>
-constexpr size_t image_bytes() { return static_cast<size_t>(Layout<DK, 1, false>::IMG); }
+constexpr size_t image_bytes(int kda) {
+    return static_cast<size_t>(kda ? Layout<DK, 1, true>::IMG : Layout<DK, 1, false>::TIMG);
+}
 
 }  // namespace
 
@@ -1104,10 +1260,10 @@ size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk) {
     if (!prefill_bf16_split(kda) || T <= 0 || B <= 0 || H <= 0) return 0;
     size_t img;
     switch (dk) {
-        case 16: img = image_bytes<16>(); break;
-        case 32: img = image_bytes<32>(); break;
-        case 64: img = image_bytes<64>(); break;
-        default: img = image_bytes<128>(); break;
+        case 16: img = image_bytes<16>(kda); break;
+        case 32: img = image_bytes<32>(kda); break;
+        case 64: img = image_bytes<64>(kda); break;
+        default: img = image_bytes<128>(kda); break;
     }
     const int nch = (T + kC - 1) / kC;
     return static_cast<size_t>(B) * H * split_range_chunks(B * H, nch, img) * img;
