@@ -196,6 +196,16 @@ struct Layout {
     static constexpr int lBytes = 2 * lBUF;
     static_assert(lBytes <= 160 * 1024, "LDS budget exceeded");
     static constexpr int U = DKP / 8;  // 16-byte units per staged row
+    // Per serial wave, a 2 KiB tile of the chunk's v (64 rows x 16 columns),
+    // after the mode's other LDS, when it fits: v then arrives with two
+    // 16-byte loads per lane and is transposed by an LDS read.
+    static constexpr int VST = kC * 16 * 2;
+    static constexpr int vFused = bytes, vChain = cBytes, vLite = lBytes;
+    static constexpr bool vstage(int mode, bool kda) {
+        return (mode == 0 ? bytes : mode == 2 ? (kda ? cBytes : lBytes) : 0) + NSW * VST <= 160 * 1024 &&
+               mode != 1;
+    }
+    static constexpr int vbase(int mode, bool kda) { return mode == 0 ? bytes : kda ? cBytes : lBytes; }
 };
 // Unit permutation of staged row r (see Layout): position = unit ^ swz(r).
 template <int U>
@@ -677,21 +687,36 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     bf16x8 bS[NKS];
     const size_t sbase = static_cast<size_t>(bh) * DK * DV;
     const size_t vrow0 = static_cast<size_t>(b) * T * H + h;  // token (b, 0, h)
-    // v of a chunk: the 32-bit word holding this lane's column for each of its
-    // 16 rows (two lanes share a word; the half is picked where it is used),
-    // so the loaded registers themselves carry the prefetch across the barrier.
-    auto serial_vload = [&](int c, uint32_t (&V)[4][4]) {
+    // v of a chunk, loaded a chunk ahead so the registers carry the prefetch
+    // across the barrier.  Staged (VSTAGE): two 16-byte loads per lane (rows
+    // 32 x + lane / 2, 8 columns each), later written to the wave's LDS tile
+    // and read back transposed into the accumulator layout.  Otherwise: the
+    // 32-bit word holding this lane's column for each of its 16 rows (two
+    // lanes share a word; the half is picked where it is used).
+    constexpr bool VSTAGE = L::vstage(MODE, KDA);
+    typedef unsigned int VIn __attribute__((ext_vector_type(VSTAGE ? 8 : 16)));
+    auto serial_vload = [&](int c, VIn& V) {
         const int t0 = c * kC, nn = min(kC, T - t0);
         const bf16_t* vb = v + (vrow0 + static_cast<size_t>(t0) * H) * DV + col0;  // uniform
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(vb, static_cast<uint32_t>(nn * H * DV * 2));
+        if constexpr (VSTAGE) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * rt + 4 * lg + i;
-                const uint32_t off = t < nn ? static_cast<uint32_t>((t * H * DV + (lr & ~1)) * 2) : kOOB;
-                V[rt][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+            for (int x = 0; x < 2; ++x) {
+                const int t = 32 * x + (lane >> 1);
+                const uint32_t off = t < nn ? static_cast<uint32_t>((t * H * DV + 8 * (lane & 1)) * 2) : kOOB;
+                const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                V[4 * x] = w.x; V[4 * x + 1] = w.y; V[4 * x + 2] = w.z; V[4 * x + 3] = w.w;
             }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * rt + 4 * lg + i;
+                    const uint32_t off = t < nn ? static_cast<uint32_t>((t * H * DV + (lr & ~1)) * 2) : kOOB;
+                    V[4 * rt + i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+                }
+        }
     };
     // ---- operands of one chunk, grouped by the phase that consumes them ----
     // kFused loads each group right before its phase; kChain issues the next
@@ -841,17 +866,37 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(A.kf[rt][s], bS[s], acc[rt]);
     };
     // phase 2: X = diag(beta) (V - Khat S), U = (I + A)^{-1} X
-    auto phase_u = [&](const OpsA& A, const f32x4 (&acc)[4], const uint32_t (&V)[4][4]) {
+    auto phase_u = [&](const OpsA& A, const f32x4 (&acc)[4], const VIn& V) {
+        float vv[4][4];  // v[16 rt + 4 lg + i][col0 + lr]
+        if constexpr (VSTAGE) {
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            unsigned char* vt = smem + L::vbase(MODE, KDA) + sw * L::VST;
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                *reinterpret_cast<uint4*>(vt + 1024 * x + 16 * lane) =
+                    make_uint4(V[4 * x], V[4 * x + 1], V[4 * x + 2], V[4 * x + 3]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const unsigned char* p = vt + (16 * rt + 4 * lg + (lr >> 2)) * 32 + 8 * (lr & 3);
+                const s16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vv[rt][i] = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(w[i])) << 16);
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vv[rt][i] = (lr & 1) ? bf_hi(V[4 * rt + i]) : bf_lo(V[4 * rt + i]);
+        }
         f32x4 X[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const float bb[4] = {A.b4[rt].x, A.b4[rt].y, A.b4[rt].z, A.b4[rt].w};
             const float ee[4] = {A.e4[rt].x, A.e4[rt].y, A.e4[rt].z, A.e4[rt].w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float vv = (lr & 1) ? bf_hi(V[rt][i]) : bf_lo(V[rt][i]);
-                X[rt][i] = bb[i] * (vv - ee[i] * acc[rt][i]);
-            }
+            for (int i = 0; i < 4; ++i) X[rt][i] = bb[i] * (vv[rt][i] - ee[i] * acc[rt][i]);
         }
         if constexpr (MODE == kChain) {
             // U_r = sum_{k <= r} T_rk X_k: independent products (no chain)
@@ -1072,7 +1117,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 stage_load(c0);
                 stage_store(c0);
             }
-            uint32_t vr[4][4];  // v of the next chunk, prefetched one step ahead
+            VIn vr;  // v of the next chunk, prefetched one step ahead
             if (c0 < nch) serial_vload(c0, vr);
             dummy_stores();
             lds_barrier();  // chunk c0 is in its buffer
@@ -1118,7 +1163,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         }
     } else {
         serial_init();
-        uint32_t vr[4][4];  // v of the next chunk, prefetched one step ahead
+        VIn vr;  // v of the next chunk, prefetched one step ahead
         if (nch > 0) serial_vload(0, vr);
         dummy_stores();
         // iteration -1 (prep gates and forms chunk 0) has no serial work; it
@@ -1174,8 +1219,9 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     hipError_t e;
     if (!img) {
         auto kern = prefill_bf16_kernel<DK, NSW, KDA, kFused>;
-        if ((e = set_lds(reinterpret_cast<const void*>(kern), L::bytes)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(blocks), dim3(block_threads<NSW, KDA, kFused>()), L::bytes, s, B, T,
+        constexpr int fused_lds = L::bytes + (L::vstage(kFused, KDA) ? NSW * L::VST : 0);
+        if ((e = set_lds(reinterpret_cast<const void*>(kern), fused_lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(block_threads<NSW, KDA, kFused>()), fused_lds, s, B, T,
                            H, DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, nullptr, 0,
                            (T + kC - 1) / kC);
         return hipGetLastError();
@@ -1185,7 +1231,7 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     using LP = Layout<DK, 1, KDA>;
     auto prep = prefill_bf16_kernel<DK, 1, KDA, kPrep>;
     auto chain = prefill_bf16_kernel<DK, NSW, KDA, kChain>;
-    constexpr int chain_lds = KDA ? L::cBytes : L::lBytes;
+    constexpr int chain_lds = (KDA ? L::cBytes : L::lBytes) + (L::vstage(kChain, KDA) ? NSW * L::VST : 0);
     if ((e = set_lds(reinterpret_cast<const void*>(prep), LP::pBytes)) != hipSuccess) return e;
     if ((e = set_lds(reinterpret_cast<const void*>(chain), chain_lds)) != hipSuccess) return e;
     const int nch = (T + kC - 1) / kC;
