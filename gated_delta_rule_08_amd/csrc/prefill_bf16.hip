@@ -1163,23 +1163,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         }
     } else {
         serial_init();
-        VIn vr;  // v of the next chunk, prefetched one step ahead
-        if (nch > 0) serial_vload(0, vr);
-        dummy_stores();
-        // iteration -1 (prep gates and forms chunk 0) has no serial work; it
-        // is peeled so that every loop iteration issues its output stores
-        lds_barrier();
-        lds_barrier();
-        for (int i = 0; i < nch; ++i) {
+        // v alternates between two register sets (even / odd chunks): the
+        // loads of chunk i+1 go out at the start of chunk i, independent of
+        // the set chunk i consumes
+        auto body = [&](int i, VIn& cur, VIn& nxt) {
+            if (i + 1 < nch) serial_vload(i + 1, nxt);
             {
                 OpsA A;
                 f32x4 acc[4];
                 load_a1(i, A);
                 load_a2(i, A);
                 phase_ks(A, acc);
-                phase_u(A, acc, vr);
+                phase_u(A, acc, cur);
             }
-            if (i + 1 < nch) serial_vload(i + 1, vr);
             lds_barrier();
             {
                 OpsB Bo;
@@ -1189,6 +1185,17 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 phase_s(Bo);
             }
             lds_barrier();
+        };
+        VIn va, vb;
+        if (nch > 0) serial_vload(0, va);
+        dummy_stores();
+        // iteration -1 (prep gates and forms chunk 0) has no serial work; it
+        // is peeled so that every loop iteration issues its output stores
+        lds_barrier();
+        lds_barrier();
+        for (int i = 0; i < nch; i += 2) {
+            body(i, va, vb);
+            if (i + 1 < nch) body(i + 1, vb, va);
         }
         serial_fini();
     }
