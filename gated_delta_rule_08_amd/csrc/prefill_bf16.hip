@@ -507,13 +507,38 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                         *reinterpret_cast<uint4*>(QhI + t * L::PK + c8) = qz[u];
                     }
                 }
-                // K^T: channel c8 + e, tokens 4 tg .. 4 tg + 3
+                // K^T: channel c8 + e, tokens 4 tg .. 4 tg + 3.  The 16 lanes
+                // of a token run hold 16 octets, whose rows lie 8 apart: with
+                // the row pitch they would meet on a quarter of the banks.  A
+                // lane therefore walks its octet from a lane-dependent start
+                // (rot, distinct across the 16 octets modulo 8 together with
+                // the octet's parity) after rotating its 8 channels by rot.
+                if constexpr (!LITE) {
+                    const int rot = (oct + (oct >> 3)) & 7;
+                    const uint32_t sh = static_cast<uint32_t>(rot & 1) * 16u;
+                    uint4 rz[4];
 #pragma unroll
-                for (int e = 0; e < 8 && !LITE; ++e) {
-                    const uint32_t x0 = bf16_half(kz[0], e), x1 = bf16_half(kz[1], e);
-                    const uint32_t x2 = bf16_half(kz[2], e), x3 = bf16_half(kz[3], e);
-                    *reinterpret_cast<uint2*>(Kt + (c8 + e) * L::PT + 4 * tg) =
-                        make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t d[4] = {kz[u].x, kz[u].y, kz[u].z, kz[u].w};
+                        uint32_t t1[4], t2[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) t1[j] = (rot & 2) ? d[(j + 1) & 3] : d[j];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) t2[j] = (rot & 4) ? t1[(j + 2) & 3] : t1[j];
+                        // halves: rz half e = kz half (e + rot) & 7
+                        rz[u] = make_uint4(__builtin_amdgcn_alignbit(t2[1], t2[0], sh),
+                                           __builtin_amdgcn_alignbit(t2[2], t2[1], sh),
+                                           __builtin_amdgcn_alignbit(t2[3], t2[2], sh),
+                                           __builtin_amdgcn_alignbit(t2[0], t2[3], sh));
+                    }
+                    bf16_t* ktl = Kt + c8 * L::PT + 4 * tg;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t x0 = bf16_half(rz[0], e), x1 = bf16_half(rz[1], e);
+                        const uint32_t x2 = bf16_half(rz[2], e), x3 = bf16_half(rz[3], e);
+                        *reinterpret_cast<uint2*>(ktl + ((e + rot) & 7) * L::PT) =
+                            make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
+                    }
                 }
             }
     
