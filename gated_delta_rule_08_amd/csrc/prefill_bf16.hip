@@ -181,6 +181,24 @@ struct Layout {
     static constexpr int pD = pA + 6 * TILE;                     // D_r^{-1} tiles (4)
     static constexpr int pT = pD + 4 * TILE;                     // T_rk tiles, k < r (6)
     static constexpr int pBytes = pT + 6 * TILE;
+    // GDN kFused, one barrier per chunk: three operand sets (Khat, Qhat and
+    // the per-token scalars: prep gates chunk i+2 while the serial waves read
+    // chunk i) and two tile sets (P, -A, D_r^{-1}: prep forms chunk i+1).
+    // The serial waves read K^T through transposing LDS reads of Khat (GDN
+    // contracts raw k), so there is no K^T copy.
+    static constexpr int uKh = 0;
+    static constexpr int uQh = kC * PK * 2;
+    static constexpr int uBeta = 2 * kC * PK * 2;
+    static constexpr int uEg = uBeta + kC * 4;
+    static constexpr int uEk = uEg + kC * 4;
+    static constexpr int uG = uEk + kC * 4;
+    static constexpr int uGend = uG + kC * 4;
+    static constexpr int OPS = (uGend + 16 + 15) / 16 * 16;  // operand set stride
+    static constexpr int uTB = 3 * OPS;                      // first tile set
+    static constexpr int TLS = 20 * TILE;                    // tile set: P (10), -A (6), D (4)
+    static constexpr int uScr = uTB + 2 * TLS;
+    static constexpr int ubytes = uScr + kPrepWaves * 16 * PS * 4;
+    static_assert(ubytes <= 160 * 1024, "LDS budget exceeded");
     // kChain: two image buffers
     static constexpr int cBytes = 2 * IMG;
     static_assert(cBytes <= 160 * 1024, "LDS budget exceeded");
@@ -200,12 +218,13 @@ struct Layout {
     // after the mode's other LDS, when it fits: v then arrives with two
     // 16-byte loads per lane and is transposed by an LDS read.
     static constexpr int VST = kC * 16 * 2;
-    static constexpr int vFused = bytes, vChain = cBytes, vLite = lBytes;
+    // LDS of the fused mode before the v tiles (GDN: the one-barrier layout)
+    static constexpr int fBytes(bool kda) { return kda ? bytes : ubytes; }
     static constexpr bool vstage(int mode, bool kda) {
-        return (mode == 0 ? bytes : mode == 2 ? (kda ? cBytes : lBytes) : 0) + NSW * VST <= 160 * 1024 &&
+        return (mode == 0 ? fBytes(kda) : mode == 2 ? (kda ? cBytes : lBytes) : 0) + NSW * VST <= 160 * 1024 &&
                mode != 1;
     }
-    static constexpr int vbase(int mode, bool kda) { return mode == 0 ? bytes : kda ? cBytes : lBytes; }
+    static constexpr int vbase(int mode, bool kda) { return mode == 0 ? fBytes(kda) : kda ? cBytes : lBytes; }
 };
 // Unit permutation of staged row r (see Layout): position = unit ^ swz(r).
 template <int U>
@@ -280,12 +299,25 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     constexpr int kStride = MODE == kChain ? (LITE ? L::lBUF : L::IMG) : L::BUF;
     // LITE chain buffers keep the tile image at lT (image offset = BUF offset - oP)
     constexpr int kTileShift = (LITE && MODE == kChain) ? L::lT - L::oP : 0;
-    auto bfp = [&](int c, int off) {
-        return reinterpret_cast<bf16_t*>(smem + (c & 1) * kStride + off + kTileShift);
+    // GDN kFused: one barrier per chunk (three operand sets, two tile sets);
+    // the buffer offsets (BUF layout) are mapped to the set holding them.
+    constexpr bool ONEBAR = MODE == kFused && !KDA;
+    auto at = [&](int c, int off) -> unsigned char* {
+        if constexpr (ONEBAR) {
+            unsigned char* ops = smem + (c % 3) * L::OPS;
+            if (off == L::oKh) return ops + L::uKh;
+            if (off == L::oQh) return ops + L::uQh;
+            if (off == L::oBeta) return ops + L::uBeta;
+            if (off == L::oEg) return ops + L::uEg;
+            if (off == L::oEk) return ops + L::uEk;
+            if (off == L::oGend) return ops + L::uGend;
+            return smem + L::uTB + (c & 1) * L::TLS + (off - L::oP);  // P, -A, D_r^{-1}
+        } else {
+            return smem + (c & 1) * kStride + off + kTileShift;
+        }
     };
-    auto f32p = [&](int c, int off) {
-        return reinterpret_cast<float*>(smem + (c & 1) * kStride + off + kTileShift);
-    };
+    auto bfp = [&](int c, int off) { return reinterpret_cast<bf16_t*>(at(c, off)); };
+    auto f32p = [&](int c, int off) { return reinterpret_cast<float*>(at(c, off)); };
     // The image of chunk c of this head (kPrep writes it, kChain reads it).
     constexpr int kImg = LITE ? L::TIMG : L::IMG;  // image bytes per (head, chunk)
     auto imgp = [&](int c) { return img + (static_cast<size_t>(bh) * (c1 - c0) + (c - c0)) * kImg; };
@@ -306,12 +338,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         else return f32p(c, off);
     };
     bf16_t* Kc = reinterpret_cast<bf16_t*>(smem + (MODE == kPrep ? L::pKc : L::oKc));  // KDA only
-    float* sG = reinterpret_cast<float*>(smem + (MODE == kPrep ? L::pG : L::oG));
-    float* scr0 = reinterpret_cast<float*>(smem + (MODE == kPrep ? L::pScr : L::oScr));
+    // G_t of the chunk being gated / formed (ONEBAR: one per operand set)
+    auto sGp = [&](int c) {
+        if constexpr (ONEBAR) return reinterpret_cast<float*>(smem + (c % 3) * L::OPS + L::uG);
+        else return reinterpret_cast<float*>(smem + (MODE == kPrep ? L::pG : L::oG));
+    };
+    float* scr0 = reinterpret_cast<float*>(smem + (MODE == kPrep ? L::pScr : ONEBAR ? L::uScr : L::oScr));
 
     if constexpr (L::DKP != DK && MODE != kChain) {  // zero the contraction padding
         constexpr int W = L::DKP - DK;
-        constexpr int NB = MODE == kPrep ? 1 : 2;
+        constexpr int NB = MODE == kPrep ? 1 : ONEBAR ? 3 : 2;
         for (int idx = tid; idx < NB * kC * W; idx += blockDim.x) {
             const int c = idx / (kC * W), r = idx % (kC * W);
             const int t = r / W, col = DK + r % W;
@@ -402,7 +438,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         const int n = min(kC, T - c * kC);
         bf16_t* Kh = prep_lds_b(c, L::oKh, L::pKh);
         bf16_t* Qh = prep_lds_b(c, L::oQh, L::pQh);
-        bf16_t* Kt = LITE ? nullptr : prep_out_b(c, L::oKt);  // the lite image has no K^T
+        bf16_t* Kt = (LITE || ONEBAR) ? nullptr : prep_out_b(c, L::oKt);  // lite image / ONEBAR: no K^T
         float* sBeta = reinterpret_cast<float*>(prep_lds_b(c, L::oBeta, L::pBeta));
         // kPrep: copies of Khat, Qhat and beta for the image
         bf16_t* KhI = reinterpret_cast<bf16_t*>(MODE == kPrep && !LITE ? imgp(c) + L::oKh : nullptr);
@@ -488,7 +524,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     const int row = lane >> 4;
                     x += (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
                     const float end = __shfl(x, 63);
-                    sG[lane] = x;
+                    sGp(c)[lane] = x;
                     prep_out_f(c, L::oEg)[lane] = ex2(x);
                     prep_out_f(c, L::oEk)[lane] = ex2(end - x);
                     const float bv = vt ? R.bt[0] : 0.f;
@@ -513,7 +549,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 // lane therefore walks its octet from a lane-dependent start
                 // (rot, distinct across the 16 octets modulo 8 together with
                 // the octet's parity) after rotating its 8 channels by rot.
-                if constexpr (!LITE) {
+                if constexpr (!LITE && !ONEBAR) {
                     const int rot = (oct + (oct >> 3)) & 7;
                     const uint32_t sh = static_cast<uint32_t>(rot & 1) * 16u;
                     uint4 rz[4];
@@ -573,6 +609,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         float gtA = 0.f, gtB = 0.f;
         float4 gj4[4];
         if constexpr (!KDA) {
+            const float* sG = sGp(c);
             gtA = sG[16 * rA + lr];
             gtB = sG[16 * rB + lr];
 #pragma unroll
@@ -840,7 +877,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 }
     };
     auto load_b2 = [&](int c, OpsB& Bo) {
-        const bf16_t* Kt = bfp(c, L::oKt);
+        const bf16_t* Kt = ONEBAR ? bfp(c, L::oKh) : bfp(c, L::oKt);  // ONEBAR: Khat rows, read transposed
         const float* ek = f32p(c, L::oEk);
         const float* ge = f32p(c, L::oGend);
 #pragma unroll
@@ -850,6 +887,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 if constexpr (LITE && MODE == kChain) {
                     const int t = 32 * s + 4 * lg + (lr >> 2), e = 16 * r + 4 * (lr & 3);
                     Bo.kt[r][s] = cat8(tr_frag(stg(c, L::lK), t, e), tr_frag(stg(c, L::lK), t + 16, e));
+                } else if constexpr (ONEBAR) {
+                    // lane m of a 16-lane group receives K[t0 + i][16 r + m], i = 0..3,
+                    // from 4 rows x 4 column quads addressed by the group
+                    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                    const bf16_t* p = Kt + (32 * s + 4 * lg + (lr >> 2)) * L::PK + 16 * r + 4 * (lr & 3);
+                    const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+                    const bf16x4 hi = __builtin_bit_cast(
+                        bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * L::PK)));
+                    Bo.kt[r][s] = cat8(lo, hi);
                 } else {
                     Bo.kt[r][s] = lds_perm(Kt + (16 * r + lr) * L::PT + 32 * s + 4 * lg);
                 }
@@ -1177,15 +1223,66 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         // gated, so the global loads overlap one whole step.
         PrepIn pin;
         if (nch > 0) prep_load(0, pin);
-        for (int i = -1; i < nch; ++i) {
-            if (i + 1 < nch) {
-                prep_gate(i + 1, pin);
-                if (i + 2 < nch) prep_load(i + 2, pin);
+        if constexpr (ONEBAR) {
+            // one barrier per step: gate chunk i+2 (operand set (i+2) % 3)
+            // and form A, P, D_r^{-1} of chunk i+1 (gated a step earlier)
+            // while the serial waves run chunk i; nch + 2 barriers in all
+            for (int i = -2; i < nch; ++i) {
+                if (i + 2 < nch) {
+                    prep_gate(i + 2, pin);
+                    if (i + 3 < nch) prep_load(i + 3, pin);
+                }
+                if (i + 1 >= 0 && i + 1 < nch) prep_ap(i + 1);
+                lds_barrier();
+            }
+        } else {
+            for (int i = -1; i < nch; ++i) {
+                if (i + 1 < nch) {
+                    prep_gate(i + 1, pin);
+                    if (i + 2 < nch) prep_load(i + 2, pin);
+                }
+                lds_barrier();
+                if (i + 1 < nch) prep_ap(i + 1);
+                lds_barrier();
+            }
+        }
+    } else if constexpr (ONEBAR) {
+        serial_init();
+        // a whole chunk between barriers (the prep waves never write the
+        // operand set or tile set of the chunk being run); v alternates
+        // between two register sets as below
+        auto body = [&](int i, VIn& cur, VIn& nxt) {
+            if (i + 1 < nch) serial_vload(i + 1, nxt);
+            {
+                OpsA A;
+                f32x4 acc[4];
+                load_a1(i, A);
+                load_a2(i, A);
+                phase_ks(A, acc);
+                phase_u(A, acc, cur);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                OpsB Bo;
+                load_b1(i, Bo);
+                phase_o(i, Bo);
+                load_b2(i, Bo);
+                phase_s(Bo);
             }
             lds_barrier();
-            if (i + 1 < nch) prep_ap(i + 1);
-            lds_barrier();
+        };
+        VIn va, vb;
+        if (nch > 0) serial_vload(0, va);
+        dummy_stores();
+        // prep steps -2 and -1 (gate chunks 0 and 1, form chunk 0) have no
+        // serial work
+        lds_barrier();
+        lds_barrier();
+        for (int i = 0; i < nch; i += 2) {
+            body(i, va, vb);
+            if (i + 1 < nch) body(i + 1, vb, va);
         }
+        serial_fini();
     } else {
         serial_init();
         // v alternates between two register sets (even / odd chunks): the
@@ -1251,7 +1348,7 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     hipError_t e;
     if (!img) {
         auto kern = prefill_bf16_kernel<DK, NSW, KDA, kFused>;
-        constexpr int fused_lds = L::bytes + (L::vstage(kFused, KDA) ? NSW * L::VST : 0);
+        constexpr int fused_lds = L::fBytes(KDA) + (L::vstage(kFused, KDA) ? NSW * L::VST : 0);
         if ((e = set_lds(reinterpret_cast<const void*>(kern), fused_lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(block_threads<NSW, KDA, kFused>()), fused_lds, s, B, T,
                            H, DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, nullptr, 0,
