@@ -112,6 +112,12 @@ __device__ __forceinline__ bf16x8 lds8(const bf16_t* p) {
 }
 // k order {0..3, 16..19} relative to p: matches two stacked accumulator tiles.
 __device__ __forceinline__ bf16x8 lds_perm(const bf16_t* p) { return cat8(lds4(p), lds4(p + 16)); }
+// Channel-permuted rows: channel 16 h + 4 g + i of each 32-channel group sits
+// at position 8 g + 4 h + i, so the k order {4g..4g+3, 16+4g..16+4g+3} of a
+// fragment is 8 contiguous elements (one 16-byte read).
+__device__ __forceinline__ constexpr int perm_pos(int c) {
+    return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
+}
 __device__ __forceinline__ void st4(bf16_t* p, const f32x4& x) {
     *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, cvt4(x));
 }
@@ -350,7 +356,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         constexpr int NB = MODE == kPrep ? 1 : ONEBAR ? 3 : 2;
         for (int idx = tid; idx < NB * kC * W; idx += blockDim.x) {
             const int c = idx / (kC * W), r = idx % (kC * W);
-            const int t = r / W, col = DK + r % W;
+            const int t = r / W, col = ONEBAR ? perm_pos(DK + r % W) : DK + r % W;
             prep_lds_b(c, L::oKh, L::pKh)[t * L::PK + col] = 0;
             prep_lds_b(c, L::oQh, L::pQh)[t * L::PK + col] = 0;
             if (KDA && c == 0) Kc[t * L::PK + col] = 0;
@@ -375,13 +381,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     //       cumulative log-gate over the chunk is an in-row scan.
     //  GDN: the octets of a row are adjacent lanes (a wave load instruction
     //       reads whole 256-byte rows); the scalar gates of the 64 tokens are
-    //       scanned by wave 0 alone, one token per lane.
+    //       scanned by one wave alone, one token per lane.
     constexpr int OPR = DK / 8;  // octets per row
     const int oct = KDA ? tid >> 4 : tid % OPR;
     const int tg = KDA ? tid & 15 : tid / OPR;
     const bool gater = tid < 2 * DK;  // DK/8 octets x 16 token runs
     const int c8 = 8 * oct;           // first channel of this lane's octet
     constexpr int NA = KDA ? 32 : 4;  // gate values per lane
+    // GDN: the wave that scans the scalar gates (a P wave: the A waves also
+    // invert the diagonal blocks)
+    constexpr int kScanWave = 1;
     struct PrepIn {
         uint4 kr[4], qr[4];
         float a[NA];
@@ -412,7 +421,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         }
         }
         if constexpr (!KDA) {
-            if (wave == 0) {  // token = lane
+            if (wave == kScanWave) {  // token = lane
                 const int tc = nn == kC ? lane : min(lane, nn - 1);
                 const unsigned ro = static_cast<unsigned>(tc * H);
                 R.a[0] = ab[ro];
@@ -514,16 +523,20 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 for (int e = 0; e < 8; ++e)
                     *reinterpret_cast<uint2*>(Kt + (c8 + e) * L::PT + 4 * tg) = make_uint2(ktw[e][0], ktw[e][1]);
             } else {
-                if (wave == 0) {
+                if (wave == kScanWave) {
                     // scalar gates: token t = lane; inclusive scan of log2 alpha
-                    // over the wave (in-row DPP scan, then the row totals)
+                    // over the wave (in-row DPP scan, then the row totals,
+                    // read into scalar registers)
                     const bool vt = FULL || lane < n;
                     float x = vt ? fmaxf(lg2(R.a[0]), kLog2Floor) : 0.f;
                     x = row_scan(x);
-                    const float r0 = __shfl(x, 15), r1 = __shfl(x, 31), r2 = __shfl(x, 47);
+                    auto lane_at = [](float y, int l) {
+                        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y), l));
+                    };
+                    const float r0 = lane_at(x, 15), r1 = lane_at(x, 31), r2 = lane_at(x, 47);
                     const int row = lane >> 4;
                     x += (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
-                    const float end = __shfl(x, 63);
+                    const float end = lane_at(x, 63);
                     sGp(c)[lane] = x;
                     prep_out_f(c, L::oEg)[lane] = ex2(x);
                     prep_out_f(c, L::oEk)[lane] = ex2(end - x);
@@ -533,6 +546,46 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     if (lane == 0) prep_out_f(c, L::oGend)[0] = ex2(end);
                 }
                 if (!gater) return;
+                if constexpr (ONEBAR && DK >= 32) {
+                    // channel-permuted rows (see perm_pos).  Octets o and o^2
+                    // of a 32-channel group (lanes of one DPP quad) swap one
+                    // 8-byte half, after which each lane holds 16 contiguous
+                    // bytes of the permuted row: octet 4j + o4 writes
+                    // positions 32 j + 16 (o4 & 1) + 8 (o4 >> 1) .. + 7 (the
+                    // same 256 bytes per row as unpermuted 16-byte stores)
+                    const int o4 = oct & 3;
+                    const bool up = o4 >= 2;  // keeps its high half, receives the partner's
+                    bf16_t* kr0 = Kh + 32 * (oct >> 2) + 16 * (o4 & 1) + 8 * (o4 >> 1);
+                    bf16_t* qr0 = Qh + 32 * (oct >> 2) + 16 * (o4 & 1) + 8 * (o4 >> 1);
+                    auto xch = [&](uint32_t x) {  // value of quad lane o4 ^ 2
+                        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x4E, 0xF, 0xF, false));
+                    };
+                    auto perm16 = [&](const uint4& w) {
+                        const uint32_t s0 = up ? w.x : w.z, s1 = up ? w.y : w.w;  // half sent to the partner
+                        const uint32_t r0 = xch(s0), r1 = xch(s1);
+                        return up ? make_uint4(r0, r1, w.z, w.w) : make_uint4(w.x, w.y, r0, r1);
+                    };
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int t = 4 * tg + u;
+                        *reinterpret_cast<uint4*>(kr0 + t * L::PK) = perm16(kz[u]);
+                        *reinterpret_cast<uint4*>(qr0 + t * L::PK) = perm16(qz[u]);
+                    }
+                    return;
+                } else if constexpr (ONEBAR) {
+                    // dk = 16 (one octet pair per row): the two halves go to
+                    // positions p0 and p0 + 8 (p0 = perm_pos of the octet)
+                    const int p0 = perm_pos(c8);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int t = 4 * tg + u;
+                        *reinterpret_cast<uint2*>(Kh + t * L::PK + p0) = make_uint2(kz[u].x, kz[u].y);
+                        *reinterpret_cast<uint2*>(Kh + t * L::PK + p0 + 8) = make_uint2(kz[u].z, kz[u].w);
+                        *reinterpret_cast<uint2*>(Qh + t * L::PK + p0) = make_uint2(qz[u].x, qz[u].y);
+                        *reinterpret_cast<uint2*>(Qh + t * L::PK + p0 + 8) = make_uint2(qz[u].z, qz[u].w);
+                    }
+                    return;
+                }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int t = 4 * tg + u;
@@ -828,7 +881,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int s = 0; s < NKS; ++s)
-                A.kf[rt][s] = lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
+                A.kf[rt][s] = ONEBAR ? lds8(Kh + (16 * rt + lr) * L::PK + 32 * s + 8 * lg)  // permuted rows
+                                     : lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
         if constexpr (KDA) {
             const float* sr = f32p(c, L::oSref);
 #pragma unroll
@@ -861,7 +915,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             for (int s = 0; s < NKS; ++s)
                 Bo.qf[rt][s] = (LITE && MODE == kChain)
                     ? perm_frag(stg(c, L::lQ), 16 * rt + lr, 32 * s + 4 * lg)
-                    : lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
+                    : ONEBAR ? lds8(Qh + (16 * rt + lr) * L::PK + 32 * s + 8 * lg)  // permuted rows
+                             : lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
             Bo.egt[rt] = KDA ? 1.f : eg[16 * rt + lr];
         }
         // P pieces: (rt, s) for 2 s <= rt -> 6 pieces
@@ -889,9 +944,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     Bo.kt[r][s] = cat8(tr_frag(stg(c, L::lK), t, e), tr_frag(stg(c, L::lK), t + 16, e));
                 } else if constexpr (ONEBAR) {
                     // lane m of a 16-lane group receives K[t0 + i][16 r + m], i = 0..3,
-                    // from 4 rows x 4 column quads addressed by the group
+                    // from 4 rows x 4 channel quads addressed by the group (the
+                    // quad of channels 16 r + 4 q .. + 3 sits at perm_pos(16 r + 4 q))
                     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-                    const bf16_t* p = Kt + (32 * s + 4 * lg + (lr >> 2)) * L::PK + 16 * r + 4 * (lr & 3);
+                    const bf16_t* p = Kt + (32 * s + 4 * lg + (lr >> 2)) * L::PK + 32 * (r >> 1) + 8 * (lr & 3) + 4 * (r & 1);
                     const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
                     const bf16x4 hi = __builtin_bit_cast(
                         bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * L::PK)));
