@@ -199,7 +199,13 @@ struct Layout {
     static constexpr int uEk = uEg + kC * 4;
     static constexpr int uG = uEk + kC * 4;
     static constexpr int uGend = uG + kC * 4;
-    static constexpr int OPS = (uGend + 16 + 15) / 16 * 16;  // operand set stride
+    // factors of 2^(G_t - G_j) for t, j in different 16-token blocks:
+    // 2^(G_t - Gb_{b(t)-1}) 2^(Gb_{b(t)-1} - Gb_{b(j)}) 2^(Gb_{b(j)} - G_j),
+    // Gb_b = G at the last token of block b (each factor <= 1)
+    static constexpr int uU = uGend + 16;   // [64] row factors
+    static constexpr int uW = uU + kC * 4;  // [64] column factors
+    static constexpr int uC = uW + kC * 4;  // [4][4] block-pair factors (r > c)
+    static constexpr int OPS = (uC + 64 + 15) / 16 * 16;  // operand set stride
     static constexpr int uTB = 3 * OPS;                      // first tile set
     static constexpr int TLS = 20 * TILE;                    // tile set: P (10), -A (6), D (4)
     static constexpr int uScr = uTB + 2 * TLS;
@@ -537,6 +543,18 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     const int row = lane >> 4;
                     x += (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
                     const float end = lane_at(x, 63);
+                    if constexpr (ONEBAR) {
+                        // block-factored gate products (each factor <= 1)
+                        const float gb0 = r0, gb1 = r0 + r1, gb2 = r0 + r1 + r2;
+                        auto gb = [&](int bb) { return bb == 0 ? gb0 : bb == 1 ? gb1 : bb == 2 ? gb2 : end; };
+                        float* ops = reinterpret_cast<float*>(smem + (c % 3) * L::OPS);
+                        ops[L::uU / 4 + lane] = ex2(x - (row == 0 ? 0.f : gb(row - 1)));
+                        ops[L::uW / 4 + lane] = ex2(gb(row) - x);
+                        if (lane < 16) {
+                            const int br = lane >> 2, bc = lane & 3;
+                            ops[L::uC / 4 + lane] = br > bc ? ex2(gb(br - 1) - gb(bc)) : 0.f;
+                        }
+                    }
                     sGp(c)[lane] = x;
                     prep_out_f(c, L::oEg)[lane] = ex2(x);
                     prep_out_f(c, L::oEk)[lane] = ex2(end - x);
@@ -661,12 +679,27 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         const float btA = sb[16 * rA + lr], btB = sb[16 * rB + lr];
         float gtA = 0.f, gtB = 0.f;
         float4 gj4[4];
+        // ONEBAR: factored off-diagonal gates (row, block-pair, column factors)
+        float uA = 0.f, uB = 0.f;
+        float4 cA4 = make_float4(0.f, 0.f, 0.f, 0.f), cB4 = cA4, w4[3];
         if constexpr (!KDA) {
             const float* sG = sGp(c);
             gtA = sG[16 * rA + lr];
             gtB = sG[16 * rB + lr];
+            if constexpr (ONEBAR) {
+                const float* ops = reinterpret_cast<const float*>(smem + (c % 3) * L::OPS);
+                gj4[0] = *reinterpret_cast<const float4*>(sG + 16 * rA + 4 * lg);  // diagonal tiles only
+                gj4[1] = *reinterpret_cast<const float4*>(sG + 16 * rB + 4 * lg);
+                uA = ops[L::uU / 4 + 16 * rA + lr];
+                uB = ops[L::uU / 4 + 16 * rB + lr];
+                cA4 = *reinterpret_cast<const float4*>(ops + L::uC / 4 + 4 * rA);
+                cB4 = *reinterpret_cast<const float4*>(ops + L::uC / 4 + 4 * rB);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) gj4[ct] = *reinterpret_cast<const float4*>(sG + 16 * ct + 4 * lg);
+                for (int ct = 0; ct < 3; ++ct) w4[ct] = *reinterpret_cast<const float4*>(ops + L::uW / 4 + 16 * ct + 4 * lg);
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) gj4[ct] = *reinterpret_cast<const float4*>(sG + 16 * ct + 4 * lg);
+            }
         }
         f32x4 accA[4] = {zero4(), zero4(), zero4(), zero4()};
         f32x4 accB[2] = {zero4(), zero4()};
@@ -685,19 +718,33 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             for (int ct = 0; ct < 2; ++ct)
                 if (ct <= rB) accB[ct] = mfma32(kr[ct], mB, accB[ct]);
         }
-        auto epilogue = [&](int rt, int ct, const f32x4& acc, float bt, float gt) {
+        auto epilogue = [&](int rt, int ct, const f32x4& acc, float bt, float gt, float ur, const float4& cr) {
             const int t = 16 * rt + lr;
             float gj[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (!KDA) {
-                gj[0] = gj4[ct].x; gj[1] = gj4[ct].y; gj[2] = gj4[ct].z; gj[3] = gj4[ct].w;
-            }
             f32x4 val;
+            if (ONEBAR && ct < rt) {
+                // off-diagonal tile: row x block-pair x column factors
+                const float cf = ct == 0 ? cr.x : ct == 1 ? cr.y : cr.z;
+                const float4 wj = w4[ct < 3 ? ct : 0];
+                const float f = ur * cf;
+                const float wv[4] = {wj.x, wj.y, wj.z, wj.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 16 * ct + 4 * lg + i;
-                float x = acc[i];
-                if constexpr (!KDA) x *= ex2(fminf(gt - gj[i], 0.f));
-                val[i] = isP ? (j <= t ? x : 0.f) : (j < t ? bt * x : 0.f);
+                for (int i = 0; i < 4; ++i) {
+                    const float x = acc[i] * f * wv[i];
+                    val[i] = isP ? x : bt * x;
+                }
+            } else {
+                if constexpr (!KDA) {
+                    const float4 g = ONEBAR ? gj4[rt == rA ? 0 : 1] : gj4[ct];
+                    gj[0] = g.x; gj[1] = g.y; gj[2] = g.z; gj[3] = g.w;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = 16 * ct + 4 * lg + i;
+                    float x = acc[i];
+                    if constexpr (!KDA) x *= ex2(fminf(gt - gj[i], 0.f));
+                    val[i] = isP ? (j <= t ? x : 0.f) : (j < t ? bt * x : 0.f);
+                }
             }
             if (isP) {
                 st4(Pt + ptile(rt, ct) * 16 * L::PD + lr * L::PD + 4 * lg, val);
@@ -711,10 +758,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         };
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
-            if (ct <= rA) epilogue(rA, ct, accA[ct], btA, gtA);
+            if (ct <= rA) epilogue(rA, ct, accA[ct], btA, gtA, uA, cA4);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
-            if (ct <= rB) epilogue(rB, ct, accB[ct], btB, gtB);
+            if (ct <= rB) epilogue(rB, ct, accB[ct], btB, gtB, uB, cB4);
         // D_r^{-1} = (I + A_rr)^{-1}: lanes 0..15 invert block rA, lanes 16..31
         // block rB; lane c solves column c by right-looking forward
         // substitution (x_i -= A_ij x_j for all i > j at step j).
