@@ -1325,20 +1325,29 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         // Inputs of chunk i+2 are loaded into registers while chunk i+1 is
         // gated, so the global loads overlap one whole step.
         PrepIn pin;
-        if (nch > 0) prep_load(0, pin);
         if constexpr (ONEBAR) {
             // one barrier per step: gate chunk i+2 (operand set (i+2) % 3)
             // and form A, P, D_r^{-1} of chunk i+1 (gated a step earlier)
-            // while the serial waves run chunk i; nch + 2 barriers in all
-            for (int i = -2; i < nch; ++i) {
+            // while the serial waves run chunk i; nch + 2 barriers in all.
+            // The inputs alternate between two register sets (even / odd
+            // chunks) and are loaded two steps ahead.
+            PrepIn pin2;
+            if (nch > 0) prep_load(0, pin);
+            if (nch > 1) prep_load(1, pin2);
+            auto step = [&](int i, PrepIn& cur) {  // cur holds chunk i + 2
                 if (i + 2 < nch) {
-                    prep_gate(i + 2, pin);
-                    if (i + 3 < nch) prep_load(i + 3, pin);
+                    prep_gate(i + 2, cur);
+                    if (i + 4 < nch) prep_load(i + 4, cur);
                 }
                 if (i + 1 >= 0 && i + 1 < nch) prep_ap(i + 1);
                 lds_barrier();
+            };
+            for (int i = -2; i < nch; i += 2) {
+                step(i, pin);
+                if (i + 1 < nch) step(i + 1, pin2);
             }
         } else {
+            if (nch > 0) prep_load(0, pin);
             for (int i = -1; i < nch; ++i) {
                 if (i + 1 < nch) {
                     prep_gate(i + 1, pin);
