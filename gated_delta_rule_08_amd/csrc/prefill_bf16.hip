@@ -263,6 +263,14 @@ constexpr int waves_per_simd() {
 
 __device__ __forceinline__ int ptile(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }  // ct <= rt
 __device__ __forceinline__ int atile(int rt, int ct) { return rt * (rt - 1) / 2 + ct; }  // ct < rt
+// A compile-time list of A/P tiles: code = 16 isP + 4 row + column (column <= row).
+template <int... T>
+struct Tiles {
+    static constexpr int n = sizeof...(T);
+    static constexpr int code[n] = {T...};
+};
+constexpr int tA(int r, int c) { return 4 * r + c; }
+constexpr int tP(int r, int c) { return 16 + 4 * r + c; }
 
 template <int DK, int NSW, bool KDA, int MODE>
 __global__ __launch_bounds__((block_threads<NSW, KDA, MODE>()))
@@ -394,9 +402,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     const bool gater = tid < 2 * DK;  // DK/8 octets x 16 token runs
     const int c8 = 8 * oct;           // first channel of this lane's octet
     constexpr int NA = KDA ? 32 : 4;  // gate values per lane
-    // GDN: the wave that scans the scalar gates (a P wave: the A waves also
-    // invert the diagonal blocks)
-    constexpr int kScanWave = 1;
+    // GDN: the wave that scans the scalar gates (one with a light tile load:
+    // see the tile lists of prep_ap)
+    constexpr int kScanWave = ONEBAR ? 2 : 1;
     struct PrepIn {
         uint4 kr[4], qr[4];
         float a[NA];
@@ -675,31 +683,128 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         const int rA = wave < 2 ? 3 : 2;  // first row tile: ct = 0..rA
         const int rB = wave < 2 ? 0 : 1;  // second row tile: ct = 0..rB
         const bf16_t* M = isP ? Qh : Kh;
+        if constexpr (ONEBAR) {
+            // GDN fused: per-wave tile lists.  Waves 0 and 2 also invert the
+            // diagonal blocks (3, 0) and (2, 1), so they form only those A
+            // tiles and one more; waves 1 and 3 form the other 14.  Each wave
+            // loads every right-hand (Kr) and left-hand (Khat / Qhat rows)
+            // fragment it needs once per K step.  Gates: diagonal tiles take
+            // 2^(G_t - G_j) per element, the others row x block-pair x column
+            // factors.
+            const float* sG = sGp(c);
+            const float* ops = reinterpret_cast<const float*>(smem + (c % 3) * L::OPS);
+            auto run = [&](auto tag) {
+                using TL = decltype(tag);
+                constexpr int NT = TL::n;
+                auto uses_col = [&](int cc, int diag) {  // diag: -1 any, 0 off-diagonal, 1 diagonal
+                    bool u = false;
+#pragma unroll
+                    for (int x = 0; x < NT; ++x) {
+                        const int cd = TL::code[x], r = (cd >> 2) & 3, cl = cd & 3;
+                        u |= cl == cc && (diag < 0 || (diag == 1) == (cl == r));
+                    }
+                    return u;
+                };
+                auto uses_row = [&](int rr, int what) {  // what: 0 any, 1 A tile, 2 diagonal, 3 off-diagonal
+                    bool u = false;
+#pragma unroll
+                    for (int x = 0; x < NT; ++x) {
+                        const int cd = TL::code[x], r = (cd >> 2) & 3, cl = cd & 3;
+                        u |= r == rr && (what == 0 || (what == 1 && cd < 16) || (what == 2 && cl == r) ||
+                                         (what == 3 && cl < r));
+                    }
+                    return u;
+                };
+                auto uses_m = [&](int key) {  // key = 4 isP + row
+                    bool u = false;
+#pragma unroll
+                    for (int x = 0; x < NT; ++x) u |= (TL::code[x] >> 2) == key;
+                    return u;
+                };
+                // epilogue scalars, read before the products
+                float bt[4], gt[4], ut[4];
+                float4 gj[4], wj[4], cr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (uses_row(r, 1)) bt[r] = sb[16 * r + lr];
+                    if (uses_row(r, 2)) gt[r] = sG[16 * r + lr];
+                    if (uses_row(r, 3)) {
+                        ut[r] = ops[L::uU / 4 + 16 * r + lr];
+                        cr[r] = *reinterpret_cast<const float4*>(ops + L::uC / 4 + 4 * r);
+                    }
+                }
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    if (uses_col(cc, 1)) gj[cc] = *reinterpret_cast<const float4*>(sG + 16 * cc + 4 * lg);
+                    if (uses_col(cc, 0)) wj[cc] = *reinterpret_cast<const float4*>(ops + L::uW / 4 + 16 * cc + 4 * lg);
+                }
+                f32x4 acc[NT];
+#pragma unroll
+                for (int x = 0; x < NT; ++x) acc[x] = zero4();
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) {
+                    bf16x8 kr[4], mf[8];
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+                        if (uses_col(cc, -1)) kr[cc] = lds8(Kr + (16 * cc + lr) * L::PK + 32 * s + 8 * lg);
+#pragma unroll
+                    for (int key = 0; key < 8; ++key)
+                        if (uses_m(key))
+                            mf[key] = lds8((key >= 4 ? Qh : Kh) + (16 * (key & 3) + lr) * L::PK + 32 * s + 8 * lg);
+#pragma unroll
+                    for (int x = 0; x < NT; ++x) acc[x] = mfma32(kr[TL::code[x] & 3], mf[TL::code[x] >> 2], acc[x]);
+                }
+#pragma unroll
+                for (int x = 0; x < NT; ++x) {
+                    const int cd = TL::code[x], tP_ = cd >> 4, r = (cd >> 2) & 3, cl = cd & 3;
+                    const int t = 16 * r + lr;
+                    f32x4 val;
+                    if (cl < r) {
+                        const float4 w = wj[cl];
+                        const float cf = cl == 0 ? cr[r].x : cl == 1 ? cr[r].y : cr[r].z;
+                        const float f = ut[r] * cf;
+                        const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float xx = acc[x][i] * f * wv[i];
+                            val[i] = tP_ ? xx : bt[r] * xx;
+                        }
+                    } else {
+                        const float4 g = gj[cl];
+                        const float gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int j = 16 * cl + 4 * lg + i;
+                            const float xx = acc[x][i] * ex2(fminf(gt[r] - gv[i], 0.f));
+                            val[i] = tP_ ? (j <= t ? xx : 0.f) : (j < t ? bt[r] * xx : 0.f);
+                        }
+                    }
+                    if (tP_) {
+                        st4(Pt + ptile(r, cl) * 16 * L::PD + lr * L::PD + 4 * lg, val);
+                    } else if (cl < r) {
+                        st4(At + atile(r, cl) * 16 * L::PD + lr * L::PD + 4 * lg, -val);
+                    } else {  // diagonal tile, stored transposed: scr[j][t] = A[t][j]
+                        float* scr = scr0 + r * 16 * L::PS;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) scr[(4 * lg + i) * L::PS + lr] = val[i];
+                    }
+                }
+            };
+            if (wave == 0) run(Tiles<tA(3, 3), tA(0, 0), tA(3, 2)>{});
+            else if (wave == 1) run(Tiles<tP(3, 0), tP(3, 1), tP(3, 2), tP(3, 3), tA(3, 0), tA(3, 1), tP(0, 0)>{});
+            else if (wave == 2) run(Tiles<tA(2, 2), tA(1, 1), tA(2, 1)>{});
+            else run(Tiles<tP(2, 0), tP(2, 1), tP(2, 2), tP(1, 0), tP(1, 1), tA(2, 0), tA(1, 0)>{});
+        } else {
         // scalars of the epilogues, read before the products
         const float btA = sb[16 * rA + lr], btB = sb[16 * rB + lr];
         float gtA = 0.f, gtB = 0.f;
         float4 gj4[4];
-        // ONEBAR: factored off-diagonal gates (row, block-pair, column factors)
-        float uA = 0.f, uB = 0.f;
-        float4 cA4 = make_float4(0.f, 0.f, 0.f, 0.f), cB4 = cA4, w4[3];
         if constexpr (!KDA) {
             const float* sG = sGp(c);
             gtA = sG[16 * rA + lr];
             gtB = sG[16 * rB + lr];
-            if constexpr (ONEBAR) {
-                const float* ops = reinterpret_cast<const float*>(smem + (c % 3) * L::OPS);
-                gj4[0] = *reinterpret_cast<const float4*>(sG + 16 * rA + 4 * lg);  // diagonal tiles only
-                gj4[1] = *reinterpret_cast<const float4*>(sG + 16 * rB + 4 * lg);
-                uA = ops[L::uU / 4 + 16 * rA + lr];
-                uB = ops[L::uU / 4 + 16 * rB + lr];
-                cA4 = *reinterpret_cast<const float4*>(ops + L::uC / 4 + 4 * rA);
-                cB4 = *reinterpret_cast<const float4*>(ops + L::uC / 4 + 4 * rB);
 #pragma unroll
-                for (int ct = 0; ct < 3; ++ct) w4[ct] = *reinterpret_cast<const float4*>(ops + L::uW / 4 + 16 * ct + 4 * lg);
-            } else {
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) gj4[ct] = *reinterpret_cast<const float4*>(sG + 16 * ct + 4 * lg);
-            }
+            for (int ct = 0; ct < 4; ++ct) gj4[ct] = *reinterpret_cast<const float4*>(sG + 16 * ct + 4 * lg);
         }
         f32x4 accA[4] = {zero4(), zero4(), zero4(), zero4()};
         f32x4 accB[2] = {zero4(), zero4()};
@@ -718,33 +823,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             for (int ct = 0; ct < 2; ++ct)
                 if (ct <= rB) accB[ct] = mfma32(kr[ct], mB, accB[ct]);
         }
-        auto epilogue = [&](int rt, int ct, const f32x4& acc, float bt, float gt, float ur, const float4& cr) {
+        auto epilogue = [&](int rt, int ct, const f32x4& acc, float bt, float gt) {
             const int t = 16 * rt + lr;
             float gj[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (!KDA) {
+                gj[0] = gj4[ct].x; gj[1] = gj4[ct].y; gj[2] = gj4[ct].z; gj[3] = gj4[ct].w;
+            }
             f32x4 val;
-            if (ONEBAR && ct < rt) {
-                // off-diagonal tile: row x block-pair x column factors
-                const float cf = ct == 0 ? cr.x : ct == 1 ? cr.y : cr.z;
-                const float4 wj = w4[ct < 3 ? ct : 0];
-                const float f = ur * cf;
-                const float wv[4] = {wj.x, wj.y, wj.z, wj.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = acc[i] * f * wv[i];
-                    val[i] = isP ? x : bt * x;
-                }
-            } else {
-                if constexpr (!KDA) {
-                    const float4 g = ONEBAR ? gj4[rt == rA ? 0 : 1] : gj4[ct];
-                    gj[0] = g.x; gj[1] = g.y; gj[2] = g.z; gj[3] = g.w;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = 16 * ct + 4 * lg + i;
-                    float x = acc[i];
-                    if constexpr (!KDA) x *= ex2(fminf(gt - gj[i], 0.f));
-                    val[i] = isP ? (j <= t ? x : 0.f) : (j < t ? bt * x : 0.f);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int j = 16 * ct + 4 * lg + i;
+                float x = acc[i];
+                if constexpr (!KDA) x *= ex2(fminf(gt - gj[i], 0.f));
+                val[i] = isP ? (j <= t ? x : 0.f) : (j < t ? bt * x : 0.f);
             }
             if (isP) {
                 st4(Pt + ptile(rt, ct) * 16 * L::PD + lr * L::PD + 4 * lg, val);
@@ -758,10 +849,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         };
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
-            if (ct <= rA) epilogue(rA, ct, accA[ct], btA, gtA, uA, cA4);
+            if (ct <= rA) epilogue(rA, ct, accA[ct], btA, gtA);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
-            if (ct <= rB) epilogue(rB, ct, accB[ct], btB, gtB, uB, cB4);
+            if (ct <= rB) epilogue(rB, ct, accB[ct], btB, gtB);
+        }
         // D_r^{-1} = (I + A_rr)^{-1}: lanes 0..15 invert block rA, lanes 16..31
         // block rB; lane c solves column c by right-looking forward
         // substitution (x_i -= A_ij x_j for all i > j at step j).
