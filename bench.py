@@ -49,6 +49,13 @@ def decode_bytes_per_head(gate, dk, dv, elt=2):
     return 8 * dk * dv + elt * (2 * dk + 2 * dv) + 4 + (4 * dk if gate == "kda" else 4)
 
 
+def verify_bytes_per_head(gate, dk, dv, T, save, elt=2):
+    """Multi-token decode of T tokens: read + write the fp32 state once, write
+    the T intermediate states if kept, and each token's q, k, v, o and gates."""
+    per_tok = elt * (2 * dk + 2 * dv) + 4 + (4 * dk if gate == "kda" else 4)
+    return 8 * dk * dv + (4 * dk * dv * T if save else 0) + T * per_tok
+
+
 def decode_flops_per_head(dk, dv):
     return 7 * dk * dv
 
@@ -243,6 +250,46 @@ def bench_kda_decode(torch, gdr, synth, steps, warmup):
                                      load_traffic("decode_kda", src_hash("decode.hip")))}
 
 
+def bench_gdn_verify(torch, gdr, synth, steps, warmup, T=4, save=True):
+    """The verify step of speculative decoding at the decode workload's shape:
+    T draft tokens per head in one gdr_decode_multi call, keeping the state
+    after every token (for rollback) when ``save``."""
+    import ctypes
+    w = synth.WORKLOADS["gdn_decode_b64_h32_d128"]
+    B, H, dk, dv = w.B, w.H, w.dk, w.dv
+    inp = synth.make_inputs(w, T=T, s0="zero")
+    d = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(
+        torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()
+        for k in ("q", "k", "v", "alpha", "beta")}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3000)
+    state = torch.randn(B, H, dk, dv, device="cuda", generator=g) * 0.02
+    o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.bfloat16)
+    states = torch.empty(B, T, H, dk, dv, device="cuda") if save else None
+    lib = gdr.load_library()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    args = (gdr.GATES["gdn"], 1, B, T, H, dk, dv, ctypes.c_float(1.0), ptr(d["q"]), ptr(d["k"]),
+            ptr(d["v"]), ptr(d["alpha"]), ptr(d["beta"]), ptr(state), ptr(o), ptr(states))
+
+    def call():
+        st = lib.gdr_decode_multi(*args, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(gdr.gdr_status_string(st))
+    for _ in range(warmup):
+        call()
+    n = max(steps, 20)
+    elapsed, gpu_s = timed_region(torch, n, call)
+    launch_ms = 1e3 * gpu_s / n
+    per_launch = B * H * verify_bytes_per_head("gdn", dk, dv, T, save)
+    return {"workload": "gdn_verify_b64_h32_d128_t%d%s" % (T, "" if save else "_nostates"),
+            "steps": n, "ms_per_step": 1e3 * elapsed / n, "launch_ms": launch_ms,
+            "tokens_per_s": B * T * n / elapsed, "gbs": per_launch * n / elapsed / 1e9,
+            "bytes_per_launch": per_launch,
+            "roofline": roofline_hbm(per_launch, launch_ms,
+                                     load_traffic("verify_gdn" + ("" if save else "_nostates"),
+                                                  src_hash("decode.hip")))}
+
+
 def bench_prefill(torch, gdr, synth, name, steps, warmup):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w)
@@ -292,7 +339,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None,
-                    help="gdn_decode | kda_decode | gdn_prefill | kda_prefill | copy")
+                    help="gdn_decode | kda_decode | gdn_verify | gdn_prefill | kda_prefill | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -324,6 +371,10 @@ def main():
     if only in (None, "kda_decode"):
         extra["kda_decode_b256_h32_d128"] = bench_kda_decode(torch, gdr, synth, args.steps,
                                                              args.warmup)
+    if only in (None, "gdn_verify"):
+        for save in (True, False):
+            r = bench_gdn_verify(torch, gdr, synth, args.steps, args.warmup, T=4, save=save)
+            extra[r["workload"]] = r
     if only in (None, "gdn_prefill"):
         extra["gdn_prefill_b4_t8192_h32_d128"] = bench_prefill(
             torch, gdr, synth, "gdn_prefill_b4_t8192_h32_d128", max(5, args.steps // 2), 2)

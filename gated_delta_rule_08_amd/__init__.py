@@ -17,14 +17,14 @@ import torch
 
 __all__ = [
     "GdrError", "GATES", "library_path", "load_library", "gdr_decode_step",
-    "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
+    "gdr_decode_multi", "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
     "gdr_abi_version", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 GATES = {"gdn": 0, "kda": 1}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
-EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_chunk_prefill",
+EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_multi", "gdr_chunk_prefill",
                     "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
                     "gdr_abi_version")
 CHUNK = 64
@@ -54,6 +54,8 @@ def load_library():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.gdr_decode_step.argtypes = [i, i, i, i, i, i, f] + [vp] * 8
     lib.gdr_decode_step.restype = i
+    lib.gdr_decode_multi.argtypes = [i] * 7 + [f] + [vp] * 9
+    lib.gdr_decode_multi.restype = i
     lib.gdr_chunk_prefill.argtypes = [i] * 8 + [f] + [vp] * 9 + [ctypes.c_size_t, vp]
     lib.gdr_chunk_prefill.restype = i
     lib.gdr_chunk_prefill_workspace_bytes.argtypes = [i] * 8
@@ -129,6 +131,35 @@ def gdr_decode_step(gate: str, q, k, v, alpha, beta, state, o, scale: float = 1.
     _check(load_library().gdr_decode_step(
         GATES[gate], _DTYPES[q.dtype], B, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
         _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _stream(stream)))
+
+
+def gdr_decode_multi(gate: str, q, k, v, alpha, beta, state, o, states=None,
+                     scale: float = 1.0, stream=None) -> None:
+    """T decode steps per head (the verify step of speculative decoding).
+
+    q, k [B,T,H,dk] and v, o [B,T,H,dv] share a dtype; alpha [B,T,H] (gdn) or
+    [B,T,H,dk] (kda) and beta [B,T,H] are fp32; ``state`` [B,H,dk,dv] fp32 is
+    read as S_0 and overwritten with S_T.  ``states`` (optional, fp32
+    [B,T,H,dk,dv]) receives the state after every token.  T <= 64.
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or o.shape != (B, T, H, dv):
+        raise ValueError("q, k, v, o shapes disagree")
+    if alpha.shape != ((B, T, H, dk) if gate == "kda" else (B, T, H)) or beta.shape != (B, T, H):
+        raise ValueError("alpha / beta shapes disagree with the gate mode")
+    if state.shape != (B, H, dk, dv) or state.dtype != torch.float32:
+        raise ValueError("state must be fp32 [B,H,dk,dv]")
+    if states is not None and (states.shape != (B, T, H, dk, dv) or states.dtype != torch.float32):
+        raise ValueError("states must be fp32 [B,T,H,dk,dv]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, o must share dtype fp32 or bf16")
+    if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise ValueError("alpha and beta must be fp32")
+    _same_device(q, k, v, alpha, beta, state, o, states)
+    _check(load_library().gdr_decode_multi(
+        GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _ptr(states), _stream(stream)))
 
 
 def gdr_chunk_prefill_workspace_bytes(gate: str, dtype, B: int, T: int, H: int, dk: int,

@@ -182,6 +182,148 @@ hipError_t dispatch_dv(int kda, int dtype, int dv, int n, float scale, const voi
     }
 }
 
+
+// T decode steps per head in one launch (the verify step of speculative
+// decoding): the state stays in registers across the T tokens, so it is read
+// and written once; token t's inputs are loaded while token t-1 is applied.
+// Token tensors are [B, T, H, .]; with SAVE the state after each token goes to
+// states[b, t, h] (the caller rolls back to an accepted prefix from there).
+// The per-token arithmetic is the decode step's, in the same order.
+template <int DK, int DV, typename InT, bool KDA, bool SAVE>
+__global__ __launch_bounds__(256) void decode_multi_kernel(
+    int n_units, int T, int H, float scale, const InT* __restrict__ q, const InT* __restrict__ k,
+    const InT* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
+    float* __restrict__ state, InT* __restrict__ o, float* __restrict__ states) {
+    constexpr int COLS = DV < 32 ? DV : 32;
+    constexpr int NSLICE = DV / COLS;
+    constexpr int LPR = COLS / 4;
+    constexpr int RPI = 64 / LPR;
+    constexpr int NI = DK / RPI;
+    static_assert(NI >= 1 && NI * RPI == DK, "head size does not tile the wavefront");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int unit = wave / NSLICE;
+    if (unit >= n_units) return;  // no barriers below: whole waves retire
+    const int slice = wave - unit * NSLICE;
+    const int rg = lane / LPR;
+    const int col = slice * COLS + (lane % LPR) * 4;
+    const int b = unit / H, h = unit - (unit / H) * H;
+
+    float* S = state + static_cast<size_t>(unit) * DK * DV + col;
+    float4 s[NI];
+#pragma unroll
+    for (int m = 0; m < NI; ++m)
+        s[m] = ld_state(S + static_cast<size_t>(m * RPI + rg) * DV);
+
+    struct In {
+        float qv[NI], kv[NI], av[KDA ? NI : 1], b;
+        float4 vv;
+    };
+    auto load_in = [&](int t, In& x) {
+        const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;  // row of token (b, t, h)
+        const InT* qu = q + tok * DK;
+        const InT* ku = k + tok * DK;
+#pragma unroll
+        for (int m = 0; m < NI; ++m) {
+            x.qv[m] = Elem<InT>::load(qu + m * RPI + rg);
+            x.kv[m] = Elem<InT>::load(ku + m * RPI + rg);
+        }
+        if constexpr (KDA) {
+#pragma unroll
+            for (int m = 0; m < NI; ++m) x.av[m] = alpha[tok * DK + m * RPI + rg];
+        } else {
+            x.av[0] = alpha[tok];
+        }
+        x.b = beta[tok];
+        x.vv = load4<InT>(v + tok * DV + col);
+    };
+    In cur, nxt;
+    load_in(0, cur);
+    for (int t = 0; t < T; ++t) {
+        load_in(t + 1 < T ? t + 1 : t, nxt);  // the next token's inputs (the last one reloads)
+        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+        float kq = 0.f;
+#pragma unroll
+        for (int m = 0; m < NI; ++m) {
+            const float a = KDA ? cur.av[m] : cur.av[0];
+            s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
+            p0 += cur.kv[m] * s[m].x; p1 += cur.kv[m] * s[m].y; p2 += cur.kv[m] * s[m].z; p3 += cur.kv[m] * s[m].w;
+            r0 += cur.qv[m] * s[m].x; r1 += cur.qv[m] * s[m].y; r2 += cur.qv[m] * s[m].z; r3 += cur.qv[m] * s[m].w;
+            kq += cur.kv[m] * cur.qv[m];
+        }
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) {
+            p0 += __shfl_xor(p0, off); p1 += __shfl_xor(p1, off);
+            p2 += __shfl_xor(p2, off); p3 += __shfl_xor(p3, off);
+            r0 += __shfl_xor(r0, off); r1 += __shfl_xor(r1, off);
+            r2 += __shfl_xor(r2, off); r3 += __shfl_xor(r3, off);
+            kq += __shfl_xor(kq, off);
+        }
+        const float e0 = cur.vv.x - p0, e1 = cur.vv.y - p1, e2 = cur.vv.z - p2, e3 = cur.vv.w - p3;
+        const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
+#pragma unroll
+        for (int m = 0; m < NI; ++m) {
+            const float bk = cur.b * cur.kv[m];
+            s[m].x += bk * e0; s[m].y += bk * e1; s[m].z += bk * e2; s[m].w += bk * e3;
+            if constexpr (SAVE)
+                st_state(states + tok * DK * DV + col + static_cast<size_t>(m * RPI + rg) * DV, s[m]);
+        }
+        if (rg == 0) {
+            const float bkq = cur.b * kq;
+            Vec4Out<InT>::store(o + tok * DV + col, scale * (r0 + bkq * e0), scale * (r1 + bkq * e1),
+                                scale * (r2 + bkq * e2), scale * (r3 + bkq * e3));
+        }
+        cur = nxt;
+    }
+#pragma unroll
+    for (int m = 0; m < NI; ++m) st_state(S + static_cast<size_t>(m * RPI + rg) * DV, s[m]);
+}
+
+template <int DK, int DV, typename InT, bool KDA>
+hipError_t launch_multi(int n_units, int T, int H, float scale, const void* q, const void* k,
+                        const void* v, const float* alpha, const float* beta, float* state,
+                        void* o, float* states, hipStream_t s) {
+    constexpr int COLS = DV < 32 ? DV : 32;
+    const long long waves = static_cast<long long>(n_units) * (DV / COLS);
+    const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
+    if (states) {
+        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, InT, KDA, true>), dim3(blocks), dim3(256), 0, s,
+                           n_units, T, H, scale, static_cast<const InT*>(q), static_cast<const InT*>(k),
+                           static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o), states);
+    } else {
+        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, InT, KDA, false>), dim3(blocks), dim3(256), 0, s,
+                           n_units, T, H, scale, static_cast<const InT*>(q), static_cast<const InT*>(k),
+                           static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o), states);
+    }
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t multi_type(int kda, int dtype, int n, int T, int H, float scale, const void* q,
+                      const void* k, const void* v, const float* alpha, const float* beta,
+                      float* state, void* o, float* states, hipStream_t s) {
+    if (dtype == GDR_DTYPE_BF16) {
+        return kda ? launch_multi<DK, DV, bf16_t, true>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s)
+                   : launch_multi<DK, DV, bf16_t, false>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+    }
+    return kda ? launch_multi<DK, DV, float, true>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s)
+               : launch_multi<DK, DV, float, false>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+}
+
+template <int DK>
+hipError_t multi_dv(int kda, int dtype, int dv, int n, int T, int H, float scale, const void* q,
+                    const void* k, const void* v, const float* alpha, const float* beta,
+                    float* state, void* o, float* states, hipStream_t s) {
+    switch (dv) {
+        case 16: return multi_type<DK, 16>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        case 32: return multi_type<DK, 32>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        case 64: return multi_type<DK, 64>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        default: return multi_type<DK, 128>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float scale,
@@ -193,6 +335,19 @@ hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float
         case 32: return dispatch_dv<32>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
         case 64: return dispatch_dv<64>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
         default: return dispatch_dv<128>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
+    }
+}
+
+hipError_t launch_decode_multi(int kda, int dtype, int B, int T, int H, int dk, int dv,
+                               float scale, const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, float* state, void* o,
+                               float* states, hipStream_t s) {
+    const int n = B * H;
+    switch (dk) {
+        case 16: return multi_dv<16>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        case 32: return multi_dv<32>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        case 64: return multi_dv<64>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        default: return multi_dv<128>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
     }
 }
 

@@ -33,6 +33,7 @@ hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, 
 namespace {
 
 inline bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+constexpr int kMaxMultiTokens = 64;  // gdr_decode_multi: a verify window, not a prompt
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Largest element count of any tensor must fit comfortably in size_t and
@@ -70,7 +71,7 @@ const char* gdr_status_string(int status) {
         case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace missing or too small";
         case GDR_ERR_BAD_ENUM: return "GDR_ERR_BAD_ENUM: unknown gate mode or dtype";
         case GDR_ERR_HIP: return "GDR_ERR_HIP: the HIP runtime rejected a launch";
-        case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: state_in and state_out partially overlap";
+        case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: two state buffers (partially) overlap";
         default: return "unknown gdr status";
     }
 }
@@ -91,6 +92,34 @@ int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float sca
         return GDR_ERR_MISALIGNED;
     hipError_t e = gdr::launch_decode(kda, dtype, B, H, dk, dv, scale, q, k, v, alpha, beta,
                                       state, o, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int gdr_decode_multi(int gate, int dtype, int B, int T, int H, int dk, int dv, float scale,
+                     const void* q, const void* k, const void* v, const float* alpha,
+                     const float* beta, float* state, void* o, float* states, void* stream) {
+    int st = check_enums(gate, dtype);
+    if (st != GDR_OK) return st;
+    if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || T > kMaxMultiTokens) return GDR_ERR_UNSUPPORTED;
+    if (!sizes_ok(B, T, H, dk, dv) || static_cast<long long>(B) * T * H * dk * dv > (1LL << 40))
+        return GDR_ERR_BAD_SHAPE;
+    if (B == 0 || H == 0 || T == 0) return GDR_OK;
+    if (!q || !k || !v || !alpha || !beta || !state || !o) return GDR_ERR_NULL_PTR;
+    const int kda = gate == GDR_GATE_KDA;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(state, 16) || (states && !aligned(states, 16)) || !aligned(beta, 4) ||
+        !aligned(alpha, kda ? 16 : 4))
+        return GDR_ERR_MISALIGNED;
+    if (states) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(state);
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(states);
+        const uintptr_t la = static_cast<uintptr_t>(B) * H * dk * dv * sizeof(float);
+        const uintptr_t lb = la * static_cast<uintptr_t>(T);
+        if (a0 < b0 + lb && b0 < a0 + la) return GDR_ERR_ALIAS;
+    }
+    hipError_t e = gdr::launch_decode_multi(kda, dtype, B, T, H, dk, dv, scale, q, k, v, alpha,
+                                            beta, state, o, states, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

@@ -38,6 +38,12 @@ template <> struct Elem<bf16_t> {
 hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float scale,
                          const void* q, const void* k, const void* v, const float* alpha,
                          const float* beta, float* state, void* o, hipStream_t s);
+// T decode steps per head; token tensors [B, T, H, .]; states (optional)
+// receives the state after every token, [B, T, H, dk, dv].
+hipError_t launch_decode_multi(int kda, int dtype, int B, int T, int H, int dk, int dv,
+                               float scale, const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, float* state, void* o,
+                               float* states, hipStream_t s);
 
 hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, float scale,
                               const float* q, const float* k, const float* v,

@@ -69,7 +69,7 @@ enum {
     GDR_ERR_WORKSPACE = -5,   /* workspace missing or too small             */
     GDR_ERR_BAD_ENUM = -6,    /* gate or dtype is not a known enumerator    */
     GDR_ERR_HIP = -7,         /* the HIP runtime rejected a launch          */
-    GDR_ERR_ALIAS = -8        /* state_in and state_out partially overlap   */
+    GDR_ERR_ALIAS = -8        /* two state buffers (partially) overlap      */
 };
 
 /*
@@ -87,6 +87,33 @@ int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float sca
                     const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta,
                     float* state, void* o, void* stream);
+
+/*
+ * T consecutive decode steps per head in one call, the verify step of
+ * speculative decoding (§2.D of the pages runs an all-GDN draft whose tokens
+ * the target then checks): the T draft tokens go through the recurrence in
+ * order, and the state after every token can be kept so that the caller can
+ * roll back to any accepted prefix.
+ *
+ *   q, k    [B, T, H, dk]   dtype        v, o   [B, T, H, dv]   dtype
+ *   alpha   [B, T, H] (GDN) or [B, T, H, dk] (KDA), fp32
+ *   beta    [B, T, H], fp32
+ *   state   [B, H, dk, dv], fp32, read as S_0 and overwritten with S_T
+ *   states  [B, T, H, dk, dv], fp32, or NULL: receives S_t, the state after
+ *           token t (t = 1 .. T at index t - 1); accepting the first a
+ *           tokens means continuing from states[:, a - 1]
+ *
+ * o_t and every S_t are exactly what T calls of gdr_decode_step would give
+ * (same arithmetic, same order); the state is read and written once.
+ * 0 <= T <= 64 (longer runs belong to gdr_chunk_prefill; larger T returns
+ * GDR_ERR_UNSUPPORTED); T == 0 is a no-op.  o and states may not overlap any
+ * input, and states may not overlap state (GDR_ERR_ALIAS).  Returns a GDR_*
+ * status.
+ */
+int gdr_decode_multi(int gate, int dtype, int B, int T, int H, int dk, int dv, float scale,
+                     const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta,
+                     float* state, void* o, float* states, void* stream);
 
 /*
  * Chunked prefill of T tokens for B x H independent heads (the prompt pass

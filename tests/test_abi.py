@@ -100,6 +100,50 @@ def test_decode_validation(lib):
     assert decode(lib, ptrs=ptrs) == MISAL
 
 
+def multi(lib, gate=0, dtype=1, B=2, T=4, H=3, dk=128, dv=128, ptrs=None):
+    # q k v alpha beta state o states; the states buffer (T x the state) is
+    # placed far from the rest unless a case moves it
+    p = list(P[:7]) + [ctypes.c_void_p(0x7000000)] if ptrs is None else ptrs
+    return lib.gdr_decode_multi(gate, dtype, B, T, H, dk, dv, 1.0, *p, None)
+
+
+def _mptrs():
+    return list(P[:7]) + [ctypes.c_void_p(0x7000000)]
+
+
+def test_decode_multi_validation(lib):
+    assert multi(lib, gate=3) == ENUM
+    assert multi(lib, dtype=-1) == ENUM
+    assert multi(lib, T=-1) == SHAPE
+    assert multi(lib, B=-2) == SHAPE
+    assert multi(lib, T=65) == UNSUP  # a verify window, not a prompt
+    assert multi(lib, dk=48) == UNSUP
+    for i in range(7):  # q k v alpha beta state o (states may be NULL)
+        ptrs = _mptrs()
+        ptrs[i] = None
+        assert multi(lib, ptrs=ptrs) == NULL, i
+    ptrs = _mptrs()
+    ptrs[7] = ctypes.c_void_p(0x7000000 + 8)  # states need 16-byte alignment
+    assert multi(lib, ptrs=ptrs) == MISAL
+    ptrs = _mptrs()
+    ptrs[3] = ctypes.c_void_p(P[3].value + 4)  # KDA alpha needs 16-byte alignment
+    assert multi(lib, gate=1, ptrs=ptrs) == MISAL
+    la = 2 * 3 * 128 * 128 * 4  # bytes of the state
+    base = 0x40000000
+    ptrs = _mptrs()
+    ptrs[5] = ctypes.c_void_p(base)
+    ptrs[7] = ctypes.c_void_p(base + 1024)  # states start inside the state
+    assert multi(lib, ptrs=ptrs) == ALIAS
+    ptrs[7] = ctypes.c_void_p(base - 4 * la + 256)  # states end inside it
+    assert multi(lib, ptrs=ptrs) == ALIAS
+
+
+def test_decode_multi_empty_is_noop(lib):
+    assert multi(lib, T=0, ptrs=[None] * 8) == OK
+    assert multi(lib, B=0, ptrs=[None] * 8) == OK
+    assert multi(lib, H=0, ptrs=[None] * 8) == OK
+
+
 def test_decode_zero_size_is_noop(lib):
     assert decode(lib, B=0, ptrs=[None] * 8) == OK
     assert decode(lib, H=0, ptrs=[None] * 8) == OK
