@@ -290,6 +290,50 @@ def bench_gdn_verify(torch, gdr, synth, steps, warmup, T=4, save=True):
                                                   src_hash("decode.hip")))}
 
 
+def varlen_lengths(N=32, lo=128, hi=4096, seed=7):
+    """Prompt lengths of the packed variable-length workload (seeded, log-uniform)."""
+    rng = np.random.default_rng(seed)
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), N)).astype(np.int64).tolist()
+
+
+def bench_gdn_varlen(torch, gdr, synth, steps, warmup, N=32, slots=64):
+    """Packed variable-length GDN prefill of N prompts (a serving batch): every
+    prompt reads its state from a pooled row and writes it back."""
+    w = synth.WORKLOADS["gdn_prefill_b4_t8192_h32_d128"]
+    H, dk, dv = w.H, w.dk, w.dv
+    lens = varlen_lengths(N)
+    total = int(sum(lens))
+    inp = synth.make_inputs(w, B=1, T=total, s0="zero")
+    d = {k: torch.from_numpy(np.ascontiguousarray(inp[k][0])).to(
+        torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()
+        for k in ("q", "k", "v", "alpha", "beta")}
+    del inp
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    perm = np.random.default_rng(11).permutation(slots)[:N]
+    sl = torch.tensor(perm, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4000)
+    pool = torch.randn(slots, H, dk, dv, device="cuda", generator=g) * 0.02
+    o = torch.empty(total, H, dv, device="cuda", dtype=torch.bfloat16)
+    max_t = int(max(lens))
+    need = gdr.gdr_chunk_prefill_varlen_workspace_bytes("gdn", torch.bfloat16, N, max_t, H, dk, dv)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    call = lambda: gdr.gdr_chunk_prefill_varlen("gdn", d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                                cu, sl, pool, o, max_seqlen=max_t, workspace=ws)
+    for _ in range(warmup):
+        call()
+    n = max(5, steps // 2)
+    elapsed, gpu_s = timed_region(torch, n, call)
+    launch_ms = 1e3 * gpu_s / n
+    # every token's q, k, v, o and gates, and each prompt's state read and written once
+    per_launch = prefill_bytes("gdn", 1, total, H, dk, dv, False) - H * 4 * dk * dv + 2 * N * H * 4 * dk * dv
+    return {"workload": "gdn_prefill_varlen_n%d_h%d_d%d" % (N, H, dk), "steps": n,
+            "ms_per_step": 1e3 * elapsed / n, "launch_ms": launch_ms,
+            "tokens_per_s": total * n / elapsed, "tokens": total, "lengths": "%d prompts, %d..%d tokens" % (N, min(lens), max(lens)),
+            "algorithmic_bytes": per_launch,
+            "roofline": roofline_hbm(per_launch, launch_ms, None)}
+
+
 def bench_prefill(torch, gdr, synth, name, steps, warmup):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w)
@@ -339,7 +383,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None,
-                    help="gdn_decode | kda_decode | gdn_verify | gdn_prefill | kda_prefill | copy")
+                    help="gdn_decode | kda_decode | gdn_verify | gdn_prefill | gdn_varlen | kda_prefill | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -378,6 +422,9 @@ def main():
     if only in (None, "gdn_prefill"):
         extra["gdn_prefill_b4_t8192_h32_d128"] = bench_prefill(
             torch, gdr, synth, "gdn_prefill_b4_t8192_h32_d128", max(5, args.steps // 2), 2)
+    if only in (None, "gdn_varlen"):
+        r = bench_gdn_varlen(torch, gdr, synth, args.steps, 2)
+        extra[r["workload"]] = r
     if only in (None, "kda_prefill"):
         extra["kda_prefill_b1_t32768_h32_d128"] = bench_prefill(
             torch, gdr, synth, "kda_prefill_b1_t32768_h32_d128", max(5, args.steps // 2), 2)

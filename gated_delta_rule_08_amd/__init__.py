@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "GdrError", "GATES", "library_path", "load_library", "gdr_decode_step",
-    "gdr_decode_multi", "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
+    "gdr_decode_multi", "gdr_chunk_prefill", "gdr_chunk_prefill_varlen",
+    "gdr_chunk_prefill_varlen_workspace_bytes", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
     "gdr_abi_version", "EXPORTED_SYMBOLS",
 ]
 
@@ -25,6 +26,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 GATES = {"gdn": 0, "kda": 1}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_multi", "gdr_chunk_prefill",
+                    "gdr_chunk_prefill_varlen", "gdr_chunk_prefill_varlen_workspace_bytes",
                     "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
                     "gdr_abi_version")
 CHUNK = 64
@@ -60,6 +62,10 @@ def load_library():
     lib.gdr_chunk_prefill.restype = i
     lib.gdr_chunk_prefill_workspace_bytes.argtypes = [i] * 8
     lib.gdr_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdr_chunk_prefill_varlen.argtypes = [i] * 9 + [f] + [vp] * 9 + [i, vp, vp, ctypes.c_size_t, vp]
+    lib.gdr_chunk_prefill_varlen.restype = i
+    lib.gdr_chunk_prefill_varlen_workspace_bytes.argtypes = [i] * 8
+    lib.gdr_chunk_prefill_varlen_workspace_bytes.restype = ctypes.c_size_t
     lib.gdr_status_string.argtypes = [i]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_abi_version.argtypes = []
@@ -201,3 +207,55 @@ def gdr_chunk_prefill(gate: str, q, k, v, alpha, beta, state_in, state_out, o,
         GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k),
         _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def gdr_chunk_prefill_varlen_workspace_bytes(gate: str, dtype, N: int, max_T: int, H: int,
+                                             dk: int, dv: int, chunk: int = CHUNK) -> int:
+    return int(load_library().gdr_chunk_prefill_varlen_workspace_bytes(
+        GATES[gate], _DTYPES[dtype], N, max_T, H, dk, dv, chunk))
+
+
+def gdr_chunk_prefill_varlen(gate: str, q, k, v, alpha, beta, cu_seqlens, state_slots, states, o,
+                             has_state=None, max_seqlen: Optional[int] = None, scale: float = 1.0,
+                             workspace=None, chunk: int = CHUNK, stream=None) -> None:
+    """Chunked prefill of packed variable-length sequences with pooled states.
+
+    q, k [total_T,H,dk] and v, o [total_T,H,dv] share a dtype; alpha
+    [total_T,H] (gdn) or [total_T,H,dk] (kda) and beta [total_T,H] are fp32;
+    cu_seqlens [N+1], state_slots [N] and has_state [N] (optional) are int32
+    device tensors; states [n_slots,H,dk,dv] fp32 is read and written in
+    place.  max_seqlen bounds every sequence length; if None it is read from
+    cu_seqlens (one device-to-host copy).
+    """
+    total_T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    if N < 0 or state_slots.shape != (N,) or (has_state is not None and has_state.shape != (N,)):
+        raise ValueError("cu_seqlens must be [N+1], state_slots and has_state [N]")
+    for t in (cu_seqlens, state_slots, has_state):
+        if t is not None and t.dtype != torch.int32:
+            raise ValueError("cu_seqlens, state_slots and has_state must be int32")
+    if k.shape != q.shape or v.shape != (total_T, H, dv) or o.shape != (total_T, H, dv):
+        raise ValueError("q, k, v, o shapes disagree")
+    if alpha.shape != ((total_T, H, dk) if gate == "kda" else (total_T, H)) or beta.shape != (total_T, H):
+        raise ValueError("alpha / beta shapes disagree with the gate mode")
+    if states.dim() != 4 or states.shape[1:] != (H, dk, dv) or states.dtype != torch.float32:
+        raise ValueError("states must be fp32 [n_slots,H,dk,dv]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, o must share dtype fp32 or bf16")
+    if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise ValueError("alpha and beta must be fp32")
+    _same_device(q, k, v, alpha, beta, cu_seqlens, state_slots, has_state, states, o, workspace)
+    if max_seqlen is None:
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max()) if N > 0 else 0
+    if workspace is None:
+        need = gdr_chunk_prefill_varlen_workspace_bytes(gate, q.dtype, N, max_seqlen, H, dk, dv, chunk)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().gdr_chunk_prefill_varlen(
+        GATES[gate], _DTYPES[q.dtype], N, total_T, int(max_seqlen), H, dk, dv, chunk, float(scale),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), _ptr(state_slots),
+        _ptr(has_state), _ptr(states), states.shape[0], _ptr(o), _ptr(workspace), ws_bytes,
+        _stream(stream)))

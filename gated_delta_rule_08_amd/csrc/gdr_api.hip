@@ -179,4 +179,56 @@ int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, 
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
+size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int max_T, int H,
+                                                int dk, int dv, int chunk) {
+    return gdr_chunk_prefill_workspace_bytes(gate, dtype, N, max_T, H, dk, dv, chunk);
+}
+
+int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T, int H, int dk,
+                             int dv, int chunk, float scale, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta,
+                             const int* cu_seqlens, const int* state_slots, const int* has_state,
+                             float* states, int n_slots, void* o, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    int st = check_enums(gate, dtype);
+    if (st != GDR_OK) return st;
+    if (N < 0 || total_T < 0 || max_T < 0 || H < 0 || n_slots < 0) return GDR_ERR_BAD_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
+    if (!sizes_ok(1, total_T, H, dk, dv) || !sizes_ok(N, max_T, H, dk, dv) ||
+        !sizes_ok(n_slots, 1, H, dk, dv))
+        return GDR_ERR_BAD_SHAPE;
+    const size_t need = gdr_chunk_prefill_varlen_workspace_bytes(gate, dtype, N, max_T, H, dk, dv, chunk);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
+    if (N == 0 || H == 0) return GDR_OK;
+    if (!cu_seqlens || !state_slots || !states) return GDR_ERR_NULL_PTR;
+    if (total_T > 0 && (!q || !k || !v || !alpha || !beta || !o)) return GDR_ERR_NULL_PTR;
+    const int kda = gate == GDR_GATE_KDA;
+    if (!aligned(states, 16) || !aligned(cu_seqlens, 4) || !aligned(state_slots, 4) ||
+        (has_state && !aligned(has_state, 4)))
+        return GDR_ERR_MISALIGNED;
+    if (total_T > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+                        !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4)))
+        return GDR_ERR_MISALIGNED;
+    gdr::VarLen vl;
+    vl.cu = cu_seqlens;
+    vl.slot = state_slots;
+    vl.has = has_state;
+    vl.n_slots = n_slots;
+    vl.total = total_T;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == GDR_DTYPE_F32) {
+        e = gdr::launch_prefill_f32(kda, N, max_T, H, dk, dv, scale, static_cast<const float*>(q),
+                                    static_cast<const float*>(k), static_cast<const float*>(v),
+                                    alpha, beta, states, states, static_cast<float*>(o), s, vl);
+    } else {
+        e = gdr::launch_prefill_bf16(kda, N, max_T, H, dk, dv, scale,
+                                     static_cast<const gdr::bf16_t*>(q),
+                                     static_cast<const gdr::bf16_t*>(k),
+                                     static_cast<const gdr::bf16_t*>(v), alpha, beta, states,
+                                     states, static_cast<gdr::bf16_t*>(o), workspace, s, vl);
+    }
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
 }  // extern "C"

@@ -33,6 +33,19 @@ template <> struct Elem<bf16_t> {
     __device__ __forceinline__ static void store(bf16_t* p, float x) { *p = f32_to_bf16(x); }
 };
 
+// Packed variable-length sequences (all pointers device memory; all null for
+// the uniform [B, T, H, .] layout).  Sequence b holds tokens cu[b] .. cu[b+1]-1
+// of the packed token tensors and its state is row slot[b] of the state pool;
+// has[b] == 0 starts it from zeros.  A kernel skips (writes nothing for) a
+// sequence whose offsets or slot are out of range.
+struct VarLen {
+    const int* cu = nullptr;
+    const int* slot = nullptr;
+    const int* has = nullptr;
+    int n_slots = 0;  // rows of the state pool
+    int total = 0;    // tokens of the packed tensors
+};
+
 // Launchers, one per kernel family.  They assume validated arguments and
 // return the hipError_t of the launch.
 hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float scale,
@@ -48,14 +61,15 @@ hipError_t launch_decode_multi(int kda, int dtype, int B, int T, int H, int dk, 
 hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, float scale,
                               const float* q, const float* k, const float* v,
                               const float* alpha, const float* beta, const float* state_in,
-                              float* state_out, float* o, hipStream_t s);
+                              float* state_out, float* o, hipStream_t s, const VarLen& vl = VarLen());
 
 // The bf16 prefill uses `workspace` (at least prefill_bf16_workspace(...)
 // bytes) when its split schedule is selected, and ignores it otherwise.
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, bf16_t* o, void* workspace, hipStream_t s);
+                               float* state_out, bf16_t* o, void* workspace, hipStream_t s,
+                               const VarLen& vl = VarLen());
 bool prefill_bf16_split(int kda);
 size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk);
 

@@ -275,14 +275,15 @@ constexpr int tP(int r, int c) { return 16 + 4 * r + c; }
 template <int DK, int NSW, bool KDA, int MODE>
 __global__ __launch_bounds__((block_threads<NSW, KDA, MODE>()))
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_simd<NSW, KDA, MODE>()))) void prefill_bf16_kernel(
-    int B, int T, int H, int DV, int NS, float scale, const bf16_t* __restrict__ q,
+    int B, int Tmax, int H, int DV, int NS, float scale, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ state_in,
     float* __restrict__ state_out, bf16_t* __restrict__ o, unsigned char* __restrict__ img,
-    int c0, int c1) {
+    int c0, int c1, VarLen vl) {
     // Chunks c0 .. c1-1 of every sequence (the split schedule runs a long
     // sequence as consecutive ranges, chaining the state through state_in /
-    // state_out, so that one range's images stay cache resident).
+    // state_out, so that one range's images stay cache resident).  Packed
+    // variable-length sequences (vl.cu) end at their own chunk count.
     using L = Layout<DK, NSW, KDA>;
     constexpr int DVS = 16 * NSW;
     constexpr int NRT = DK / 16;          // 16-row tiles of S
@@ -295,13 +296,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     const int lr = lane & 15, lg = lane >> 4;
 
     const int BH = B * H;
-    const int nch = c1;         // chunks run by this launch: c0 .. nch-1
-    int bh, slice = 0, pc = 0, pc_end = 0;  // kPrep: chunks pc .. pc_end-1 of one head
+    int bh, slice = 0, g = 0;
     if constexpr (MODE == kPrep) {
-        const int g = static_cast<int>(blockIdx.x) / BH;  // NS = chunks per workgroup
+        g = static_cast<int>(blockIdx.x) / BH;  // NS = chunks per workgroup
         bh = static_cast<int>(blockIdx.x) - g * BH;
-        pc = c0 + g * NS;
-        pc_end = min(c1, pc + NS);
     } else {
         const int grp = blockIdx.x / (8 * NS);
         const int rem = blockIdx.x - grp * 8 * NS;
@@ -310,6 +308,32 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         if (bh >= BH) return;  // whole block exits before any barrier
     }
     const int b = bh / H, h = bh - b * H;
+    // This sequence: its length, first token row, state row, and whether it
+    // reads an initial state (later ranges of the split schedule always read
+    // the state carried from the previous range).
+    int T = Tmax;
+    size_t tseq = static_cast<size_t>(b) * Tmax;
+    int srow = bh;
+    bool init = state_in != nullptr;
+    if (vl.cu) {
+        const int s0 = vl.cu[b], s1 = vl.cu[b + 1];
+        if (s0 < 0 || s1 < s0 || s1 - s0 > Tmax || s1 > vl.total) return;  // whole block, no barrier yet
+        T = s1 - s0;
+        tseq = static_cast<size_t>(s0);
+        if (T == 0) return;  // an empty sequence leaves its state row untouched
+    }
+    if (vl.slot) {
+        const int r = vl.slot[b];
+        if (r < 0 || r >= vl.n_slots) return;
+        srow = r * H + h;
+    }
+    if (vl.has && c0 == 0 && vl.has[b] == 0) init = false;
+    const int nch = min(c1, (T + kC - 1) / kC);  // chunks run by this launch: c0 .. nch-1
+    int pc = 0, pc_end = 0;                       // kPrep: chunks pc .. pc_end-1 of one head
+    if constexpr (MODE == kPrep) {
+        pc = c0 + g * NS;
+        pc_end = min(nch, pc + NS);
+    }
     constexpr int kLoad = load_waves<NSW, KDA>();
     constexpr bool LITE = !KDA && MODE != kFused;  // GDN split
     constexpr int kLead = MODE == kChain ? kLoad : kPrepWaves;  // waves before the serial ones
@@ -410,7 +434,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         float a[NA];
         float bt[4];
     };
-    const size_t tok0 = static_cast<size_t>(b) * T * H + h;  // token (b, 0, h)
+    const size_t tok0 = tseq * H + h;  // token (b, 0, h)
     auto prep_load = [&](int c, PrepIn& R) {
         const int t0 = c * kC, nn = min(kC, T - t0);
         const size_t rb = tok0 + static_cast<size_t>(t0) * H;  // row of token t0 (uniform)
@@ -939,8 +963,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     f32x4 Uf[4];
     bf16x4 Ub[4];
     bf16x8 bS[NKS];
-    const size_t sbase = static_cast<size_t>(bh) * DK * DV;
-    const size_t vrow0 = static_cast<size_t>(b) * T * H + h;  // token (b, 0, h)
+    const size_t sbase = static_cast<size_t>(srow) * DK * DV;
+    const size_t vrow0 = tseq * H + h;  // token (b, 0, h)
     // v of a chunk, loaded a chunk ahead so the registers carry the prefetch
     // across the barrier.  Staged (VSTAGE): two 16-byte loads per lane (rows
     // 32 x + lane / 2, 8 columns each), later written to the wave's LDS tile
@@ -1246,7 +1270,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
 #pragma unroll
         for (int r = 0; r < NRT; ++r) {
             S[r] = zero4();
-            if (state_in) {
+            if (init) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     S[r][i] = state_in[sbase + static_cast<size_t>(16 * r + 4 * lg + i) * DV + col0 + lr];
@@ -1280,7 +1304,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         // chunk c (wave 0) only touches its own LDS tiles, which the next
         // chunk's products overwrite after the next barrier.
         PrepIn pin;
-        prep_load(pc, pin);
+        // (a packed sequence may end before this workgroup's chunks begin)
+        if (pc < pc_end) prep_load(pc, pin);
         for (int c = pc; c < pc_end; ++c) {
             zero_image_pad(c);
             prep_gate(c, pin);
@@ -1540,7 +1565,7 @@ inline int split_range_chunks(int BH, int nch, size_t img_bytes) {
 template <int DK, int NSW, bool KDA>
 hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, const bf16_t* k,
                   const bf16_t* v, const float* alpha, const float* beta, const float* s_in,
-                  float* s_out, bf16_t* o, unsigned char* img, hipStream_t s) {
+                  float* s_out, bf16_t* o, unsigned char* img, hipStream_t s, const VarLen& vl) {
     using L = Layout<DK, NSW, KDA>;
     const int NS = DV / (16 * NSW);
     const int groups = (B * H + 7) / 8;
@@ -1556,7 +1581,7 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
         if ((e = set_lds(reinterpret_cast<const void*>(kern), fused_lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(block_threads<NSW, KDA, kFused>()), fused_lds, s, B, T,
                            H, DV, NS, scale, q, k, v, alpha, beta, s_in, s_out, o, nullptr, 0,
-                           (T + kC - 1) / kC);
+                           (T + kC - 1) / kC, vl);
         return hipGetLastError();
     }
     // Per range of chunks: the chunk-local work of every (b, h, chunk), then
@@ -1576,11 +1601,11 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
         const int groups_per_head = (c1 - c0 + cpw - 1) / cpw;
         hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(B * H * groups_per_head)),
                            dim3(block_threads<1, KDA, kPrep>()), LP::pBytes, s, B, T, H, DV, cpw, scale, q, k,
-                           v, alpha, beta, s_in, s_out, o, img, c0, c1);
+                           v, alpha, beta, s_in, s_out, o, img, c0, c1, vl);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(chain, dim3(blocks), dim3(block_threads<NSW, KDA, kChain>()), chain_lds, s, B, T,
                            H, DV, NS, scale, q, k, v, alpha, beta, c0 == 0 ? s_in : s_out, s_out, o,
-                           img, c0, c1);
+                           img, c0, c1, vl);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1590,11 +1615,11 @@ template <int DK, bool KDA>
 hipError_t dispatch_dvs(int dvs, int B, int T, int H, int DV, float scale, const bf16_t* q,
                         const bf16_t* k, const bf16_t* v, const float* alpha, const float* beta,
                         const float* s_in, float* s_out, bf16_t* o, unsigned char* img,
-                        hipStream_t s) {
+                        hipStream_t s, const VarLen& vl) {
     switch (dvs) {
-        case 16: return launch<DK, 1, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s);
-        case 32: return launch<DK, 2, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s);
-        default: return launch<DK, 4, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s);
+        case 16: return launch<DK, 1, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
+        case 32: return launch<DK, 2, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
+        default: return launch<DK, 4, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
     }
 }
 
@@ -1602,9 +1627,9 @@ template <int DK>
 hipError_t dispatch_gate(int kda, int dvs, int B, int T, int H, int DV, float scale,
                          const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* alpha,
                          const float* beta, const float* s_in, float* s_out, bf16_t* o,
-                         unsigned char* img, hipStream_t s) {
-    return kda ? dispatch_dvs<DK, true>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s)
-               : dispatch_dvs<DK, false>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s);
+                         unsigned char* img, hipStream_t s, const VarLen& vl) {
+    return kda ? dispatch_dvs<DK, true>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl)
+               : dispatch_dvs<DK, false>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
 }
 
 template <int DK>
@@ -1651,14 +1676,15 @@ size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk) {
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, bf16_t* o, void* workspace, hipStream_t s) {
+                               float* state_out, bf16_t* o, void* workspace, hipStream_t s,
+                               const VarLen& vl) {
     const int dvs = prefill_bf16_slice_width(B, H, dv);
     unsigned char* img = prefill_bf16_split(kda) ? static_cast<unsigned char*>(workspace) : nullptr;
     switch (dk) {
-        case 16: return dispatch_gate<16>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s);
-        case 32: return dispatch_gate<32>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s);
-        case 64: return dispatch_gate<64>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s);
-        default: return dispatch_gate<128>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s);
+        case 16: return dispatch_gate<16>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
+        case 32: return dispatch_gate<32>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
+        case 64: return dispatch_gate<64>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
+        default: return dispatch_gate<128>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
     }
 }
 

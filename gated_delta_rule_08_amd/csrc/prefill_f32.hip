@@ -42,9 +42,10 @@ struct F32Smem {
 
 template <int DK, int DVS, bool KDA>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
-    int T, int H, int DV, float scale, const float* __restrict__ q, const float* __restrict__ k,
+    int Tmax, int H, int DV, float scale, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
-    const float* __restrict__ state_in, float* __restrict__ state_out, float* __restrict__ o) {
+    const float* __restrict__ state_in, float* __restrict__ state_out, float* __restrict__ o,
+    VarLen vl) {
     using L = F32Smem<DK, DVS, KDA>;
     extern __shared__ float smem[];
     float* Qs = smem + L::kQ;
@@ -63,11 +64,30 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const int b = bh / H;
     const int c0 = slice * DVS;
     const int tid = threadIdx.x;
-    const size_t sbase = static_cast<size_t>(bh) * DK * DV;
+    // This sequence (packed variable-length input: its own length, first
+    // token row and state row; skipped, before any barrier, if out of range).
+    int T = Tmax;
+    size_t tb = static_cast<size_t>(b) * Tmax;  // row of the sequence's first token (before x H)
+    int srow = bh;
+    bool init = state_in != nullptr;
+    if (vl.cu) {
+        const int s0 = vl.cu[b], s1 = vl.cu[b + 1];
+        if (s0 < 0 || s1 < s0 || s1 - s0 > Tmax || s1 > vl.total) return;
+        T = s1 - s0;
+        tb = static_cast<size_t>(s0);
+        if (T == 0) return;  // an empty sequence leaves its state row untouched
+    }
+    if (vl.slot) {
+        const int r = vl.slot[b];
+        if (r < 0 || r >= vl.n_slots) return;
+        srow = r * H + h;
+    }
+    if (vl.has && vl.has[b] == 0) init = false;
+    const size_t sbase = static_cast<size_t>(srow) * DK * DV;
 
     for (int idx = tid; idx < DK * DVS; idx += 256) {
         const int i = idx / DVS, j = idx % DVS;
-        Ss[idx] = state_in ? state_in[sbase + static_cast<size_t>(i) * DV + c0 + j] : 0.0f;
+        Ss[idx] = init ? state_in[sbase + static_cast<size_t>(i) * DV + c0 + j] : 0.0f;
     }
 
     for (int t0 = 0; t0 < T; t0 += kChunk) {
@@ -75,16 +95,16 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
         __syncthreads();  // previous chunk done with every buffer
         for (int idx = tid; idx < kChunk * DK; idx += 256) {
             const int t = idx / DK, c = idx % DK;
-            const size_t g = ((static_cast<size_t>(b) * T + t0 + t) * H + h) * DK + c;
+            const size_t g = ((tb + t0 + t) * H + h) * DK + c;
             Qs[idx] = t < n ? q[g] : 0.0f;
             Ks[idx] = t < n ? k[g] : 0.0f;
         }
         for (int idx = tid; idx < kChunk * DVS; idx += 256) {
             const int t = idx / DVS, j = idx % DVS;
-            Xs[idx] = t < n ? v[((static_cast<size_t>(b) * T + t0 + t) * H + h) * DV + c0 + j] : 0.0f;
+            Xs[idx] = t < n ? v[((tb + t0 + t) * H + h) * DV + c0 + j] : 0.0f;
         }
         if (tid < kChunk) {
-            const size_t g = (static_cast<size_t>(b) * T + t0 + tid) * H + h;
+            const size_t g = (tb + t0 + tid) * H + h;
             Bs[tid] = tid < n ? beta[g] : 0.0f;
             if constexpr (!KDA) Gs[tid] = tid < n ? fmaxf(__logf(alpha[g]), kLogFloor) : 0.0f;
         }
@@ -96,7 +116,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
                 for (int t = 0; t < kChunk; ++t) {
                     float g = 0.0f;
                     if (t < n)
-                        g = fmaxf(__logf(alpha[((static_cast<size_t>(b) * T + t0 + t) * H + h) * DK + tid]),
+                        g = fmaxf(__logf(alpha[((tb + t0 + t) * H + h) * DK + tid]),
                                   kLogFloor);
                     acc += g;
                     Gs[t * DK + tid] = acc;
@@ -163,7 +183,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
                 acc += Qs[t * DK + c] * __expf(g) * Ss[c * DVS + j];
             }
             for (int jj = 0; jj <= t; ++jj) acc += Ps[t * kChunk + jj] * Xs[jj * DVS + j];
-            o[((static_cast<size_t>(b) * T + t0 + t) * H + h) * DV + c0 + j] = scale * acc;
+            o[((tb + t0 + t) * H + h) * DV + c0 + j] = scale * acc;
         }
         __syncthreads();
         // S <- diag(exp(G_end)) S + Ktil^T U.
@@ -188,7 +208,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 template <int DK, int DVS, bool KDA>
 hipError_t launch(int B, int T, int H, int DV, float scale, const float* q, const float* k,
                   const float* v, const float* alpha, const float* beta, const float* s_in,
-                  float* s_out, float* o, hipStream_t s) {
+                  float* s_out, float* o, hipStream_t s, const VarLen& vl) {
     using L = F32Smem<DK, DVS, KDA>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
     auto kern = prefill_f32_kernel<DK, DVS, KDA>;
@@ -200,25 +220,25 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const float* q, cons
     }
     const unsigned blocks = static_cast<unsigned>(B) * H * (DV / DVS);
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), L::bytes, s, T, H, DV, scale, q, k, v,
-                       alpha, beta, s_in, s_out, o);
+                       alpha, beta, s_in, s_out, o, vl);
     return hipGetLastError();
 }
 
 template <int DK, bool KDA>
 hipError_t dispatch_dv(int B, int T, int H, int dv, float scale, const float* q,
                        const float* k, const float* v, const float* alpha, const float* beta,
-                       const float* s_in, float* s_out, float* o, hipStream_t s) {
+                       const float* s_in, float* s_out, float* o, hipStream_t s, const VarLen& vl) {
     if (dv == 16)
-        return launch<DK, 16, KDA>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
-    return launch<DK, 32, KDA>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
+        return launch<DK, 16, KDA>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s, vl);
+    return launch<DK, 32, KDA>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s, vl);
 }
 
 template <int DK>
 hipError_t dispatch_gate(int kda, int B, int T, int H, int dv, float scale, const float* q,
                          const float* k, const float* v, const float* alpha, const float* beta,
-                         const float* s_in, float* s_out, float* o, hipStream_t s) {
-    return kda ? dispatch_dv<DK, true>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s)
-               : dispatch_dv<DK, false>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s);
+                         const float* s_in, float* s_out, float* o, hipStream_t s, const VarLen& vl) {
+    return kda ? dispatch_dv<DK, true>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s, vl)
+               : dispatch_dv<DK, false>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s, vl);
 }
 
 }  // namespace
@@ -226,12 +246,12 @@ hipError_t dispatch_gate(int kda, int B, int T, int H, int dv, float scale, cons
 hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, float scale,
                               const float* q, const float* k, const float* v,
                               const float* alpha, const float* beta, const float* state_in,
-                              float* state_out, float* o, hipStream_t s) {
+                              float* state_out, float* o, hipStream_t s, const VarLen& vl) {
     switch (dk) {
-        case 16: return dispatch_gate<16>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s);
-        case 32: return dispatch_gate<32>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s);
-        case 64: return dispatch_gate<64>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s);
-        default: return dispatch_gate<128>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s);
+        case 16: return dispatch_gate<16>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s, vl);
+        case 32: return dispatch_gate<32>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s, vl);
+        case 64: return dispatch_gate<64>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s, vl);
+        default: return dispatch_gate<128>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s, vl);
     }
 }
 

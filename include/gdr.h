@@ -148,6 +148,45 @@ int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, 
 size_t gdr_chunk_prefill_workspace_bytes(int gate, int dtype, int B, int T, int H,
                                          int dk, int dv, int chunk);
 
+/*
+ * Chunked prefill of N packed variable-length sequences whose states live in
+ * a pool of state rows (the call a serving engine makes for a batch of
+ * prompts of different lengths; the pages' §2.D serves the mixers through
+ * such an engine).  Sequence n holds tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
+ * of the packed token tensors; its initial state is row state_slots[n] of
+ * `states` (or zeros where has_state[n] == 0), and its final state is written
+ * back to the same row.  The same kernels as gdr_chunk_prefill run every
+ * sequence independently.
+ *
+ *   q, k         [total_T, H, dk]   dtype    v, o   [total_T, H, dv]   dtype
+ *   alpha        [total_T, H] (GDN) or [total_T, H, dk] (KDA), fp32
+ *   beta         [total_T, H], fp32
+ *   cu_seqlens   [N + 1] int32, DEVICE: non-decreasing token offsets
+ *   state_slots  [N] int32, DEVICE: distinct rows of `states`
+ *   has_state    [N] int32, DEVICE, or NULL (every sequence reads its row)
+ *   states       [n_slots, H, dk, dv] fp32, DEVICE, read and written in place
+ *   max_T        an upper bound of every sequence length (sizes the launch
+ *                and the workspace, gdr_chunk_prefill_varlen_workspace_bytes)
+ *
+ * The offsets and slots are device data the host does not read: a sequence
+ * whose offsets are out of order, longer than max_T or beyond total_T, or
+ * whose slot is outside [0, n_slots), is skipped (nothing of it is written);
+ * a sequence of length 0 leaves its row untouched.  Two sequences with the
+ * same slot race.  Returns a GDR_* status.
+ */
+int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T, int H, int dk,
+                             int dv, int chunk, float scale,
+                             const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta,
+                             const int* cu_seqlens, const int* state_slots, const int* has_state,
+                             float* states, int n_slots, void* o,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gdr_chunk_prefill_varlen needs (0 when the arguments are
+ * invalid or no scratch is needed). */
+size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int max_T, int H,
+                                                int dk, int dv, int chunk);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* gdr_status_string(int status);
 

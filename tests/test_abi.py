@@ -171,6 +171,41 @@ def test_prefill_validation(lib):
     assert prefill(lib, B=0, ptrs=[None] * 8) == OK
 
 
+def varlen(lib, gate=0, dtype=1, N=3, total_T=100, max_T=64, H=2, dk=64, dv=64, chunk=64,
+           ptrs=None, n_slots=4, ws=None, ws_bytes=0):
+    # q k v alpha beta cu slots has states o
+    p = list(P[:10]) if ptrs is None else ptrs
+    return lib.gdr_chunk_prefill_varlen(gate, dtype, N, total_T, max_T, H, dk, dv, chunk, 1.0,
+                                        *p[:9], n_slots, p[9], ws, ws_bytes, None)
+
+
+def test_prefill_varlen_validation(lib, monkeypatch):
+    monkeypatch.setenv("GDR_PREFILL_PATH", "fused")  # no workspace needed for GDN bf16
+    assert varlen(lib, gate=5) == ENUM
+    assert varlen(lib, N=-1) == SHAPE
+    assert varlen(lib, max_T=-1) == SHAPE
+    assert varlen(lib, n_slots=-1) == SHAPE
+    assert varlen(lib, chunk=16) == UNSUP
+    assert varlen(lib, dv=24) == UNSUP
+    for i in (0, 1, 2, 3, 4, 5, 6, 8, 9):  # every pointer but has_state is required
+        ptrs = list(P[:10])
+        ptrs[i] = None
+        assert varlen(lib, ptrs=ptrs) == NULL, i
+    ptrs = list(P[:10])
+    ptrs[5] = ctypes.c_void_p(P[5].value + 2)  # cu_seqlens: 4-byte alignment
+    assert varlen(lib, ptrs=ptrs) == MISAL
+    ptrs = list(P[:10])
+    ptrs[8] = ctypes.c_void_p(P[8].value + 4)  # states: 16-byte alignment
+    assert varlen(lib, ptrs=ptrs) == MISAL
+    assert varlen(lib, N=0, ptrs=[None] * 10) == OK
+    monkeypatch.setenv("GDR_PREFILL_PATH", "split")
+    import torch
+    need = gdr.gdr_chunk_prefill_varlen_workspace_bytes("kda", torch.bfloat16, 3, 64, 2, 64, 64)
+    assert need > 0
+    assert varlen(lib, gate=1) == WS
+    assert varlen(lib, gate=1, ws=ctypes.c_void_p(0x100000), ws_bytes=need - 1) == WS
+
+
 def test_workspace(lib, monkeypatch):
     import torch
     monkeypatch.delenv("GDR_PREFILL_PATH", raising=False)
