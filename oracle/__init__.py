@@ -10,7 +10,9 @@ definition and the chunked algebra):
 * :func:`recurrent`  -- plain C, token by token (the main oracle);
 * :func:`chunked`    -- plain C, the exact chunked (WY/UT) refactoring;
 * :func:`brute`      -- NumPy, dense per-token transition matrices
-  ``M_t = (I - beta_t k_t k_t^T) D_t``, for tiny inputs only.
+  ``M_t = (I - beta_t k_t k_t^T) D_t``, for tiny inputs only;
+* :func:`prologue`   -- NumPy, the input steps before the mixer (q/k L2
+  normalisation, sigmoid of the gate logits).
 
 Pins: every function here is checked against facts fixed by the mathematics
 (identity and rank-one special cases, the delta rule's exact recall, a scalar
@@ -135,6 +137,28 @@ def decode_step(q, k, v, alpha, beta, state, scale: float = 1.0,
     alpha = np.asarray(alpha)[:, None]
     o, s = recurrent(q, k, v, alpha, beta, state, scale, nthreads)
     return o[:, 0], s
+
+
+def prologue(q, k, alpha, beta, norm_qk: bool = True, sigmoid_gates: bool = True,
+             eps: float = 1e-12):
+    """The input steps on the near side of the mixer, in float64.
+
+    ``norm_qk``: every q and k vector (last axis, length dk) is divided by its
+    Euclidean norm, the norm clamped below at ``eps`` (a zero vector stays
+    zero).  ``sigmoid_gates``: alpha and beta are logits and become
+    1 / (1 + exp(-x)), evaluated without overflow for either sign.
+    Returns (q, k, alpha, beta) ready for :func:`recurrent`.
+    """
+    q, k, alpha, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, alpha, beta))
+    if norm_qk:
+        q = q / np.maximum(np.sqrt(np.sum(q * q, axis=-1, keepdims=True)), eps)
+        k = k / np.maximum(np.sqrt(np.sum(k * k, axis=-1, keepdims=True)), eps)
+    if sigmoid_gates:
+        def sig(x):
+            e = np.exp(-np.abs(x))  # <= 1, never overflows
+            return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+        alpha, beta = sig(alpha), sig(beta)
+    return q, k, alpha, beta
 
 
 def brute(q, k, v, alpha, beta, s0=None, scale: float = 1.0):

@@ -42,6 +42,7 @@ __all__ = [
     "bf16_round",
     "bf16_bits",
     "make_inputs",
+    "make_raw_inputs",
     "make_state",
 ]
 
@@ -163,3 +164,31 @@ def make_inputs(w: Workload, layer: int = 0, *, B: Optional[int] = None,
     beta = _sigmoid(rb.standard_normal((B, T, H), dtype=np.float32))
     s0 = make_state(rs, B, H, dk, dv) if s0_kind == "normal" else None
     return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta, "s0": s0}
+
+
+def make_raw_inputs(w: Workload, layer: int = 0, *, B: Optional[int] = None,
+                    T: Optional[int] = None, H: Optional[int] = None,
+                    seed: Optional[int] = None, s0: Optional[str] = None,
+                    round_bf16: bool = True) -> dict:
+    """The same draws as :func:`make_inputs` before its two transforms: q and
+    k are the raw normal draws (not normalised) and ``alpha``, ``beta`` are the
+    logits (before the sigmoid).  With a bf16 workload and ``round_bf16`` the
+    raw q, k, v are rounded to bf16 (what a caller would pass)."""
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    H = w.H if H is None else H
+    seed = w.seed if seed is None else seed
+    s0_kind = w.s0 if s0 is None else s0
+    rq, rk, rv, ra, rb, rs = _streams(seed, layer)
+    dk, dv = w.dk, w.dv
+    q = rq.standard_normal((B, T, H, dk), dtype=np.float32)
+    k = rk.standard_normal((B, T, H, dk), dtype=np.float32)
+    v = rv.standard_normal((B, T, H, dv), dtype=np.float32)
+    if w.dtype == "bf16" and round_bf16:
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    ashape = (B, T, H) if w.gate == "gdn" else (B, T, H, dk)
+    alpha = (2.0 + 0.5 * ra.standard_normal(ashape, dtype=np.float32)).astype(np.float32)
+    beta = rb.standard_normal((B, T, H), dtype=np.float32)
+    s0 = make_state(rs, B, H, dk, dv) if s0_kind == "normal" else None
+    return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta, "s0": s0}
+

@@ -270,3 +270,47 @@ def test_empty_sequence_copies_state():
     assert o.shape[1] == 0 and np.array_equal(s, S0)
     o, s = oracle.chunked(q, k, v, alpha, beta, S0)
     assert np.array_equal(s, S0)
+
+
+# ---- prologue (q/k L2 normalisation, gate sigmoids) ----
+
+def test_prologue_unit_norm_parallel_and_scale_invariant():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((2, 5, 3, 16))
+    k = rng.standard_normal((2, 5, 3, 16)) * 7.0
+    qn, kn, _, _ = oracle.prologue(q, k, np.zeros((2, 5, 3)), np.zeros((2, 5, 3)))
+    for x, xn in ((q, qn), (k, kn)):
+        assert np.allclose(np.linalg.norm(xn, axis=-1), 1.0, atol=1e-14)
+        cos = np.sum(x * xn, axis=-1) / np.linalg.norm(x, axis=-1)
+        assert np.allclose(cos, 1.0, atol=1e-14)  # same direction, positive factor
+    q2, k2, _, _ = oracle.prologue(3.5 * q, 0.25 * k, np.zeros((2, 5, 3)), np.zeros((2, 5, 3)))
+    assert np.allclose(q2, qn, atol=1e-15) and np.allclose(k2, kn, atol=1e-15)
+
+
+def test_prologue_zero_vector_stays_zero():
+    q = np.zeros((1, 1, 1, 8))
+    q[0, 0, 0, 3] = 0.0
+    qn, _, _, _ = oracle.prologue(q, q, np.zeros((1, 1, 1)), np.zeros((1, 1, 1)))
+    assert np.all(qn == 0.0) and np.all(np.isfinite(qn))
+
+
+def test_prologue_sigmoid_values():
+    x = np.array([0.0, np.log(3.0), -np.log(3.0), 40.0, -40.0, 1000.0, -1000.0])
+    _, _, a, b = oracle.prologue(np.ones((1, 8)), np.ones((1, 8)), x, -x, norm_qk=False)
+    assert a[0] == 0.5
+    assert abs(a[1] - 0.75) < 1e-15 and abs(a[2] - 0.25) < 1e-15  # 1/(1+1/3), 1/(1+3)
+    assert np.allclose(a + b, 1.0, atol=1e-15)  # sigma(x) + sigma(-x) = 1
+    assert a[5] == 1.0 and 0.0 <= a[6] < 1e-300 and np.all(np.isfinite(a))
+    assert np.all((a >= 0.0) & (a <= 1.0))
+
+
+def test_prologue_matches_the_input_generator():
+    """The generator applies the same two steps to its raw draws (its own code)."""
+    import synth
+    w = synth.WORKLOADS["gdn_tiny_f32"]
+    raw = synth.make_raw_inputs(w)
+    qn, kn, a, b = oracle.prologue(raw["q"], raw["k"], raw["alpha"], raw["beta"])
+    inp = synth.make_inputs(w)
+    assert np.allclose(qn, inp["q"], atol=1e-6) and np.allclose(kn, inp["k"], atol=1e-6)
+    assert np.allclose(a, inp["alpha"], atol=1e-6) and np.allclose(b, inp["beta"], atol=1e-6)
+
