@@ -250,6 +250,48 @@ def bench_kda_decode(torch, gdr, synth, steps, warmup):
                                      load_traffic("decode_kda", src_hash("decode.hip")))}
 
 
+def bench_decode_prologue(torch, gdr, synth, steps, warmup, gate="gdn"):
+    """The decode step with the fused input prologue (raw q, k normalised and
+    gate logits through the sigmoid inside the kernel) beside the plain step,
+    same shapes and memory, launches alternating in one region each."""
+    import ctypes
+    w = synth.WORKLOADS["gdn_decode_b64_h32_d128" if gate == "gdn" else "kda_decode_b256_h32_d128"]
+    B, H, dk, dv = w.B, w.H, w.dk, w.dv
+    lib = gdr.load_library()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5000)
+    args = {}
+    # raw inputs for the prologue, the usual (transformed) ones for the plain step
+    for f, inp in ((1, synth.make_raw_inputs(w, s0="zero")), (0, synth.make_inputs(w, s0="zero"))):
+        d = {k: torch.from_numpy(np.ascontiguousarray(inp[k][:, 0])).to(
+            torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()
+            for k in ("q", "k", "v", "alpha", "beta")}
+        d["state"] = torch.randn(B, H, dk, dv, device="cuda", generator=g) * 0.02
+        d["o"] = torch.empty(B, H, dv, device="cuda", dtype=torch.bfloat16)
+        args[f] = (d, (B, H, dk, dv, ctypes.c_float(1.0), ptr(d["q"]), ptr(d["k"]), ptr(d["v"]),
+                       ptr(d["alpha"]), ptr(d["beta"]), ptr(d["state"]), ptr(d["o"])))
+    flags = gdr.PRO_L2NORM_QK | gdr.PRO_SIGMOID
+
+    def call(f):
+        st = lib.gdr_decode_step_ex(gdr.GATES[gate], 1, f, *args[1 if f else 0][1],
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(gdr.gdr_status_string(st))
+    for _ in range(warmup):
+        call(flags)
+        call(0)
+    n = max(steps, 20)
+    per_launch = B * H * decode_bytes_per_head(gate, dk, dv)
+    res = {"workload": w.name + "_prologue", "steps": n, "bytes_per_launch": per_launch}
+    for tag, f in (("prologue", flags), ("plain", 0)):
+        _, gpu_s = timed_region(torch, n, lambda: call(f))
+        res[tag + "_launch_ms"] = 1e3 * gpu_s / n
+    res["overhead"] = round(res["prologue_launch_ms"] / res["plain_launch_ms"] - 1.0, 4)
+    res["roofline"] = roofline_hbm(per_launch, res["prologue_launch_ms"], None)
+    return res
+
+
 def bench_gdn_verify(torch, gdr, synth, steps, warmup, T=4, save=True):
     """The verify step of speculative decoding at the decode workload's shape:
     T draft tokens per head in one gdr_decode_multi call, keeping the state
@@ -334,9 +376,11 @@ def bench_gdn_varlen(torch, gdr, synth, steps, warmup, N=32, slots=64):
             "roofline": roofline_hbm(per_launch, launch_ms, None)}
 
 
-def bench_prefill(torch, gdr, synth, name, steps, warmup):
+def bench_prefill(torch, gdr, synth, name, steps, warmup, flags=0):
+    """One chunked prefill per step; with ``flags`` the inputs are raw (q, k
+    not normalised, gate logits) and the kernels run the input prologue."""
     w = synth.WORKLOADS[name]
-    inp = synth.make_inputs(w)
+    inp = synth.make_raw_inputs(w) if flags else synth.make_inputs(w)
     B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
     d = {k: (None if v is None else torch.from_numpy(v).to(
         torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()) for k, v in inp.items()}
@@ -345,8 +389,8 @@ def bench_prefill(torch, gdr, synth, name, steps, warmup):
     o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.bfloat16)
     need = gdr.gdr_chunk_prefill_workspace_bytes(w.gate, torch.bfloat16, B, T, H, dk, dv)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
-    call = lambda: gdr.gdr_chunk_prefill(w.gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                         d["s0"], s_out, o, workspace=ws)
+    call = lambda: gdr.gdr_chunk_prefill_ex(w.gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                            d["s0"], s_out, o, flags=flags, workspace=ws)
     for _ in range(warmup):
         call()
     elapsed, gpu_s = timed_region(torch, steps, call)
@@ -355,14 +399,15 @@ def bench_prefill(torch, gdr, synth, name, steps, warmup):
     flops = prefill_flops(B, T, H, dk, dv)
     sec = launch_ms / 1e3
     return {
-        "workload": name, "steps": steps, "ms_per_step": 1e3 * elapsed / steps,
+        "workload": name + ("_prologue" if flags else ""), "steps": steps,
+        "ms_per_step": 1e3 * elapsed / steps,
         "tokens_per_s": B * T * steps / elapsed,
         "schedule": "split" if need else "fused", "workspace_bytes": need,
         "launch_ms": launch_ms,
         "roofline": {
             "bound": "hbm", "achieved": round(nbytes / sec / 1e9, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": load_traffic("prefill_" + w.gate, src_hash("prefill_bf16.hip")),
+            "traffic": None if flags else load_traffic("prefill_" + w.gate, src_hash("prefill_bf16.hip")),
         },
         "mfma": {"achieved": round(flops / sec / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -383,7 +428,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None,
-                    help="gdn_decode | kda_decode | gdn_verify | gdn_prefill | gdn_varlen | kda_prefill | copy")
+                    help="gdn_decode | kda_decode | gdn_verify | gdn_prefill | gdn_varlen | kda_prefill | prologue | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -428,6 +473,14 @@ def main():
     if only in (None, "kda_prefill"):
         extra["kda_prefill_b1_t32768_h32_d128"] = bench_prefill(
             torch, gdr, synth, "kda_prefill_b1_t32768_h32_d128", max(5, args.steps // 2), 2)
+    if only in (None, "prologue"):  # the same paths with the fused input prologue
+        for gate in ("gdn", "kda"):
+            r = bench_decode_prologue(torch, gdr, synth, args.steps, args.warmup, gate)
+            extra[r["workload"]] = r
+        pro = gdr.PRO_L2NORM_QK | gdr.PRO_SIGMOID
+        for name in ("gdn_prefill_b4_t8192_h32_d128", "kda_prefill_b1_t32768_h32_d128"):
+            r = bench_prefill(torch, gdr, synth, name, max(5, args.steps // 2), 2, flags=pro)
+            extra[r["workload"]] = r
 
     if head is None:
         print(json.dumps({"workloads": extra}))

@@ -19,13 +19,18 @@ __all__ = [
     "GdrError", "GATES", "library_path", "load_library", "gdr_decode_step",
     "gdr_decode_multi", "gdr_chunk_prefill", "gdr_chunk_prefill_varlen",
     "gdr_chunk_prefill_varlen_workspace_bytes", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
-    "gdr_abi_version", "EXPORTED_SYMBOLS",
+    "gdr_abi_version", "EXPORTED_SYMBOLS", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
+    "PRO_L2NORM_QK", "PRO_SIGMOID",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 GATES = {"gdn": 0, "kda": 1}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
-EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_multi", "gdr_chunk_prefill",
+# input prologue flags of the *_ex calls (include/gdr.h: GDR_PRO_*)
+PRO_L2NORM_QK = 1
+PRO_SIGMOID = 2
+EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
+                    "gdr_decode_multi", "gdr_chunk_prefill",
                     "gdr_chunk_prefill_varlen", "gdr_chunk_prefill_varlen_workspace_bytes",
                     "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
                     "gdr_abi_version")
@@ -56,6 +61,10 @@ def load_library():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.gdr_decode_step.argtypes = [i, i, i, i, i, i, f] + [vp] * 8
     lib.gdr_decode_step.restype = i
+    lib.gdr_decode_step_ex.argtypes = [i] * 7 + [f] + [vp] * 8
+    lib.gdr_decode_step_ex.restype = i
+    lib.gdr_chunk_prefill_ex.argtypes = [i] * 9 + [f] + [vp] * 9 + [ctypes.c_size_t, vp]
+    lib.gdr_chunk_prefill_ex.restype = i
     lib.gdr_decode_multi.argtypes = [i] * 7 + [f] + [vp] * 9
     lib.gdr_decode_multi.restype = i
     lib.gdr_chunk_prefill.argtypes = [i] * 8 + [f] + [vp] * 9 + [ctypes.c_size_t, vp]
@@ -121,6 +130,18 @@ def gdr_decode_step(gate: str, q, k, v, alpha, beta, state, o, scale: float = 1.
     q, k [B,H,dk] and v, o [B,H,dv] share a dtype (fp32 or bf16); alpha is
     [B,H] (gate "gdn") or [B,H,dk] (gate "kda"); beta [B,H]; fp32 gates.
     """
+    _decode_step(None, gate, q, k, v, alpha, beta, state, o, scale, stream)
+
+
+def gdr_decode_step_ex(gate: str, q, k, v, alpha, beta, state, o, flags: int = 0,
+                       scale: float = 1.0, stream=None) -> None:
+    """:func:`gdr_decode_step` with an input prologue: ``flags`` ORs
+    PRO_L2NORM_QK (q, k are raw and get L2-normalised) and PRO_SIGMOID
+    (alpha, beta are logits)."""
+    _decode_step(int(flags), gate, q, k, v, alpha, beta, state, o, scale, stream)
+
+
+def _decode_step(flags, gate, q, k, v, alpha, beta, state, o, scale, stream):
     B, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape != (B, H, dv) or o.shape != (B, H, dv):
@@ -134,9 +155,13 @@ def gdr_decode_step(gate: str, q, k, v, alpha, beta, state, o, scale: float = 1.
     if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
         raise ValueError("alpha and beta must be fp32")
     _same_device(q, k, v, alpha, beta, state, o)
-    _check(load_library().gdr_decode_step(
-        GATES[gate], _DTYPES[q.dtype], B, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
-        _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _stream(stream)))
+    lib = load_library()
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _stream(stream))
+    if flags is None:
+        _check(lib.gdr_decode_step(GATES[gate], _DTYPES[q.dtype], B, H, dk, dv, float(scale), *ptrs))
+    else:
+        _check(lib.gdr_decode_step_ex(GATES[gate], _DTYPES[q.dtype], flags, B, H, dk, dv, float(scale),
+                                      *ptrs))
 
 
 def gdr_decode_multi(gate: str, q, k, v, alpha, beta, state, o, states=None,
@@ -184,6 +209,21 @@ def gdr_chunk_prefill(gate: str, q, k, v, alpha, beta, state_in, state_out, o,
     workspace: a device tensor of at least gdr_chunk_prefill_workspace_bytes
     bytes, or None to have one allocated for this call.
     """
+    _chunk_prefill(None, gate, q, k, v, alpha, beta, state_in, state_out, o, scale, workspace,
+                   chunk, stream)
+
+
+def gdr_chunk_prefill_ex(gate: str, q, k, v, alpha, beta, state_in, state_out, o, flags: int = 0,
+                         scale: float = 1.0, workspace=None, chunk: int = CHUNK,
+                         stream=None) -> None:
+    """:func:`gdr_chunk_prefill` with an input prologue (``flags`` as in
+    :func:`gdr_decode_step_ex`)."""
+    _chunk_prefill(int(flags), gate, q, k, v, alpha, beta, state_in, state_out, o, scale,
+                   workspace, chunk, stream)
+
+
+def _chunk_prefill(flags, gate, q, k, v, alpha, beta, state_in, state_out, o, scale, workspace,
+                   chunk, stream):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape != (B, T, H, dv) or o.shape != (B, T, H, dv):
@@ -203,10 +243,14 @@ def gdr_chunk_prefill(gate: str, q, k, v, alpha, beta, state_in, state_out, o,
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().gdr_chunk_prefill(
-        GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k),
-        _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o),
-        _ptr(workspace), ws_bytes, _stream(stream)))
+    lib = load_library()
+    rest = (float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
+            _ptr(state_out), _ptr(o), _ptr(workspace), ws_bytes, _stream(stream))
+    if flags is None:
+        _check(lib.gdr_chunk_prefill(GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, chunk, *rest))
+    else:
+        _check(lib.gdr_chunk_prefill_ex(GATES[gate], _DTYPES[q.dtype], flags, B, T, H, dk, dv, chunk,
+                                        *rest))
 
 
 def gdr_chunk_prefill_varlen_workspace_bytes(gate: str, dtype, N: int, max_T: int, H: int,

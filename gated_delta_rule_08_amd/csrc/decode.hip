@@ -19,6 +19,11 @@
 // LDS, no barriers: waves are independent.  With dv = 128 the four waves of a
 // workgroup cover the four column slices of one head, so a workgroup streams
 // one contiguous 64 KiB state.
+//
+// Input prologue (GDR_PRO_*): sigmoid of the gate logits on load; raw q and
+// k enter the dk-sums unchanged, their squared norms take one more butterfly,
+// and the sums are rescaled by 1/||k||, 1/||q|| afterwards (no extra pass
+// over the state).
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -71,7 +76,7 @@ template <int DK, int DV, typename InT, bool KDA>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     int n_units, float scale, const InT* __restrict__ q, const InT* __restrict__ k,
     const InT* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
-    float* __restrict__ state, InT* __restrict__ o) {
+    float* __restrict__ state, InT* __restrict__ o, int pro) {
     constexpr int COLS = DV < 32 ? DV : 32;  // value columns per wavefront
     constexpr int NSLICE = DV / COLS;
     constexpr int LPR = COLS / 4;            // lanes per row segment
@@ -108,8 +113,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     } else {
         av[0] = alpha[unit];
     }
-    const float b = beta[unit];
+    float b = beta[unit];
     const float4 vv = load4<InT>(v + static_cast<size_t>(unit) * DV + col);
+    if (pro & GDR_PRO_SIGMOID) {  // gates given as logits
+        b = sigmoid_f(b);
+#pragma unroll
+        for (int m = 0; m < (KDA ? NI : 1); ++m) av[m] = sigmoid_f(av[m]);
+    }
 
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
@@ -131,10 +141,33 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         r2 += __shfl_xor(r2, off); r3 += __shfl_xor(r3, off);
         kq += __shfl_xor(kq, off);
     }
+    // Raw q, k: the sums above used them as given; with ik = 1/||k|| and
+    // iq = 1/||q|| the normalised step has p * ik, r * iq, (k.q) ik iq, and
+    // the update adds beta (ik k) e^T.
+    float ik = 1.f;
+    if (pro & GDR_PRO_L2NORM_QK) {
+        float kk = 0.f, qq = 0.f;
+#pragma unroll
+        for (int m = 0; m < NI; ++m) {
+            kk += kv[m] * kv[m];
+            qq += qv[m] * qv[m];
+        }
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) {
+            kk += __shfl_xor(kk, off);
+            qq += __shfl_xor(qq, off);
+        }
+        ik = inv_norm(kk);
+        const float iq = inv_norm(qq);
+        p0 *= ik; p1 *= ik; p2 *= ik; p3 *= ik;
+        r0 *= iq; r1 *= iq; r2 *= iq; r3 *= iq;
+        kq *= ik * iq;
+    }
     const float e0 = vv.x - p0, e1 = vv.y - p1, e2 = vv.z - p2, e3 = vv.w - p3;
+    const float bn = b * ik;
 #pragma unroll
     for (int m = 0; m < NI; ++m) {
-        const float bk = b * kv[m];
+        const float bk = bn * kv[m];
         s[m].x += bk * e0; s[m].y += bk * e1; s[m].z += bk * e2; s[m].w += bk * e3;
         st_state(S + static_cast<size_t>(m * RPI + rg) * DV, s[m]);
     }
@@ -148,37 +181,38 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
 template <int DK, int DV, typename InT, bool KDA>
 hipError_t launch(int n_units, float scale, const void* q, const void* k, const void* v,
-                  const float* alpha, const float* beta, float* state, void* o, hipStream_t s) {
+                  const float* alpha, const float* beta, float* state, void* o, hipStream_t s,
+                  int pro) {
     constexpr int COLS = DV < 32 ? DV : 32;
     const long long waves = static_cast<long long>(n_units) * (DV / COLS);
     const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
     hipLaunchKernelGGL((decode_step_kernel<DK, DV, InT, KDA>), dim3(blocks), dim3(256), 0, s,
                        n_units, scale, static_cast<const InT*>(q), static_cast<const InT*>(k),
-                       static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o));
+                       static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o), pro);
     return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t dispatch_type(int kda, int dtype, int n, float scale, const void* q, const void* k,
                          const void* v, const float* alpha, const float* beta, float* state,
-                         void* o, hipStream_t s) {
+                         void* o, hipStream_t s, int pro) {
     if (dtype == GDR_DTYPE_BF16) {
-        return kda ? launch<DK, DV, bf16_t, true>(n, scale, q, k, v, alpha, beta, state, o, s)
-                   : launch<DK, DV, bf16_t, false>(n, scale, q, k, v, alpha, beta, state, o, s);
+        return kda ? launch<DK, DV, bf16_t, true>(n, scale, q, k, v, alpha, beta, state, o, s, pro)
+                   : launch<DK, DV, bf16_t, false>(n, scale, q, k, v, alpha, beta, state, o, s, pro);
     }
-    return kda ? launch<DK, DV, float, true>(n, scale, q, k, v, alpha, beta, state, o, s)
-               : launch<DK, DV, float, false>(n, scale, q, k, v, alpha, beta, state, o, s);
+    return kda ? launch<DK, DV, float, true>(n, scale, q, k, v, alpha, beta, state, o, s, pro)
+               : launch<DK, DV, float, false>(n, scale, q, k, v, alpha, beta, state, o, s, pro);
 }
 
 template <int DK>
 hipError_t dispatch_dv(int kda, int dtype, int dv, int n, float scale, const void* q,
                        const void* k, const void* v, const float* alpha, const float* beta,
-                       float* state, void* o, hipStream_t s) {
+                       float* state, void* o, hipStream_t s, int pro) {
     switch (dv) {
-        case 16: return dispatch_type<DK, 16>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s);
-        case 32: return dispatch_type<DK, 32>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s);
-        case 64: return dispatch_type<DK, 64>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s);
-        default: return dispatch_type<DK, 128>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s);
+        case 16: return dispatch_type<DK, 16>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s, pro);
+        case 32: return dispatch_type<DK, 32>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s, pro);
+        case 64: return dispatch_type<DK, 64>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s, pro);
+        default: return dispatch_type<DK, 128>(kda, dtype, n, scale, q, k, v, alpha, beta, state, o, s, pro);
     }
 }
 
@@ -328,13 +362,13 @@ hipError_t multi_dv(int kda, int dtype, int dv, int n, int T, int H, float scale
 
 hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float scale,
                          const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, float* state, void* o, hipStream_t s) {
+                         const float* beta, float* state, void* o, hipStream_t s, int pro) {
     const int n = B * H;
     switch (dk) {
-        case 16: return dispatch_dv<16>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
-        case 32: return dispatch_dv<32>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
-        case 64: return dispatch_dv<64>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
-        default: return dispatch_dv<128>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s);
+        case 16: return dispatch_dv<16>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s, pro);
+        case 32: return dispatch_dv<32>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s, pro);
+        case 64: return dispatch_dv<64>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s, pro);
+        default: return dispatch_dv<128>(kda, dtype, dv, n, scale, q, k, v, alpha, beta, state, o, s, pro);
     }
 }
 

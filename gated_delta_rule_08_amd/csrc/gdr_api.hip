@@ -47,6 +47,8 @@ inline bool sizes_ok(long long B, long long T, long long H, long long dk, long l
     return true;
 }
 
+inline bool flags_ok(int flags) { return (flags & ~(GDR_PRO_L2NORM_QK | GDR_PRO_SIGMOID)) == 0; }
+
 int check_enums(int gate, int dtype) {
     if (gate != GDR_GATE_GDN && gate != GDR_GATE_KDA) return GDR_ERR_BAD_ENUM;
     if (dtype != GDR_DTYPE_F32 && dtype != GDR_DTYPE_BF16) return GDR_ERR_BAD_ENUM;
@@ -69,7 +71,7 @@ const char* gdr_status_string(int status) {
         case GDR_ERR_MISALIGNED:
             return "GDR_ERR_MISALIGNED: tensors need 16-byte alignment (beta and GDN alpha 4-byte)";
         case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace missing or too small";
-        case GDR_ERR_BAD_ENUM: return "GDR_ERR_BAD_ENUM: unknown gate mode or dtype";
+        case GDR_ERR_BAD_ENUM: return "GDR_ERR_BAD_ENUM: unknown gate mode, dtype or prologue flag";
         case GDR_ERR_HIP: return "GDR_ERR_HIP: the HIP runtime rejected a launch";
         case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: two state buffers (partially) overlap";
         default: return "unknown gdr status";
@@ -79,8 +81,16 @@ const char* gdr_status_string(int status) {
 int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float scale,
                     const void* q, const void* k, const void* v, const float* alpha,
                     const float* beta, float* state, void* o, void* stream) {
+    return gdr_decode_step_ex(gate, dtype, 0, B, H, dk, dv, scale, q, k, v, alpha, beta, state, o,
+                              stream);
+}
+
+int gdr_decode_step_ex(int gate, int dtype, int flags, int B, int H, int dk, int dv, float scale,
+                       const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, float* state, void* o, void* stream) {
     int st = check_enums(gate, dtype);
     if (st != GDR_OK) return st;
+    if (!flags_ok(flags)) return GDR_ERR_BAD_ENUM;
     if (B < 0 || H < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDR_ERR_UNSUPPORTED;
     if (!sizes_ok(B, 1, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
@@ -91,7 +101,7 @@ int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float sca
         !aligned(state, 16) || !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4))
         return GDR_ERR_MISALIGNED;
     hipError_t e = gdr::launch_decode(kda, dtype, B, H, dk, dv, scale, q, k, v, alpha, beta,
-                                      state, o, static_cast<hipStream_t>(stream));
+                                      state, o, static_cast<hipStream_t>(stream), flags);
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
@@ -139,10 +149,25 @@ int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, 
                       const float* alpha, const float* beta, const float* state_in,
                       float* state_out, void* o, void* workspace, size_t workspace_bytes,
                       void* stream) {
+    return gdr_chunk_prefill_ex(gate, dtype, 0, B, T, H, dk, dv, chunk, scale, q, k, v, alpha,
+                                beta, state_in, state_out, o, workspace, workspace_bytes, stream);
+}
+
+int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
+                         int chunk, float scale, const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta, const float* state_in,
+                         float* state_out, void* o, void* workspace, size_t workspace_bytes,
+                         void* stream) {
     int st = check_enums(gate, dtype);
     if (st != GDR_OK) return st;
+    if (!flags_ok(flags)) return GDR_ERR_BAD_ENUM;
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
+    // the bf16 schedules normalise q, k where the chunk-local products are
+    // formed: the fused GDN kernel and the split KDA kernels
+    if ((flags & GDR_PRO_L2NORM_QK) && dtype == GDR_DTYPE_BF16 &&
+        gdr::prefill_bf16_split(gate == GDR_GATE_KDA) != (gate == GDR_GATE_KDA))
+        return GDR_ERR_UNSUPPORTED;
     if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
     const size_t need = gdr_chunk_prefill_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
@@ -162,19 +187,21 @@ int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, 
         if (a0 < b0 + len && b0 < a0 + len) return GDR_ERR_ALIAS;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    gdr::Opts opt;
+    opt.pro = flags;
     hipError_t e;
     if (T == 0) {
         e = gdr::launch_state_copy(state_in, state_out, n_state, s);
     } else if (dtype == GDR_DTYPE_F32) {
         e = gdr::launch_prefill_f32(kda, B, T, H, dk, dv, scale, static_cast<const float*>(q),
                                     static_cast<const float*>(k), static_cast<const float*>(v),
-                                    alpha, beta, state_in, state_out, static_cast<float*>(o), s);
+                                    alpha, beta, state_in, state_out, static_cast<float*>(o), s, opt);
     } else {
         e = gdr::launch_prefill_bf16(kda, B, T, H, dk, dv, scale,
                                      static_cast<const gdr::bf16_t*>(q),
                                      static_cast<const gdr::bf16_t*>(k),
                                      static_cast<const gdr::bf16_t*>(v), alpha, beta, state_in,
-                                     state_out, static_cast<gdr::bf16_t*>(o), workspace, s);
+                                     state_out, static_cast<gdr::bf16_t*>(o), workspace, s, opt);
     }
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
@@ -209,7 +236,7 @@ int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T,
     if (total_T > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
                         !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4)))
         return GDR_ERR_MISALIGNED;
-    gdr::VarLen vl;
+    gdr::Opts vl;
     vl.cu = cu_seqlens;
     vl.slot = state_slots;
     vl.has = has_state;

@@ -33,24 +33,41 @@ template <> struct Elem<bf16_t> {
     __device__ __forceinline__ static void store(bf16_t* p, float x) { *p = f32_to_bf16(x); }
 };
 
-// Packed variable-length sequences (all pointers device memory; all null for
-// the uniform [B, T, H, .] layout).  Sequence b holds tokens cu[b] .. cu[b+1]-1
-// of the packed token tensors and its state is row slot[b] of the state pool;
-// has[b] == 0 starts it from zeros.  A kernel skips (writes nothing for) a
-// sequence whose offsets or slot are out of range.
-struct VarLen {
+// Per-launch options of the prefill kernels.
+//  Packed variable-length sequences (all pointers device memory; all null for
+//  the uniform [B, T, H, .] layout): sequence b holds tokens cu[b] .. cu[b+1]-1
+//  of the packed token tensors and its state is row slot[b] of the state pool;
+//  has[b] == 0 starts it from zeros.  A kernel skips (writes nothing for) a
+//  sequence whose offsets or slot are out of range.
+//  pro: input prologue flags (GDR_PRO_*), applied where q, k and the gates are
+//  loaded.
+struct Opts {
     const int* cu = nullptr;
     const int* slot = nullptr;
     const int* has = nullptr;
     int n_slots = 0;  // rows of the state pool
     int total = 0;    // tokens of the packed tensors
+    int pro = 0;
 };
+
+// Input prologue helpers (fp32).  A row is divided by max(||x||, 1e-12), i.e.
+// multiplied by rsqrt(max(sum x^2, 1e-24)); sigmoid and log2(sigmoid) in a
+// form that neither overflows nor loses the small-gate end.
+constexpr float kNormEps2 = 1e-24f;
+__device__ __forceinline__ float inv_norm(float sumsq) { return rsqrtf(fmaxf(sumsq, kNormEps2)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+__device__ __forceinline__ float log2_sigmoid(float z) {
+    // log2 sigma(z) = -(max(-z, 0) log2 e + log2(1 + 2^(-|z| log2 e)))
+    constexpr float kLog2e = 1.4426950408889634f;
+    return -(fmaxf(-z, 0.f) * kLog2e + __log2f(1.f + exp2f(-fabsf(z) * kLog2e)));
+}
 
 // Launchers, one per kernel family.  They assume validated arguments and
 // return the hipError_t of the launch.
+// pro: input prologue flags (GDR_PRO_*).
 hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float scale,
                          const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, float* state, void* o, hipStream_t s);
+                         const float* beta, float* state, void* o, hipStream_t s, int pro = 0);
 // T decode steps per head; token tensors [B, T, H, .]; states (optional)
 // receives the state after every token, [B, T, H, dk, dv].
 hipError_t launch_decode_multi(int kda, int dtype, int B, int T, int H, int dk, int dv,
@@ -61,7 +78,7 @@ hipError_t launch_decode_multi(int kda, int dtype, int B, int T, int H, int dk, 
 hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, float scale,
                               const float* q, const float* k, const float* v,
                               const float* alpha, const float* beta, const float* state_in,
-                              float* state_out, float* o, hipStream_t s, const VarLen& vl = VarLen());
+                              float* state_out, float* o, hipStream_t s, const Opts& vl = Opts());
 
 // The bf16 prefill uses `workspace` (at least prefill_bf16_workspace(...)
 // bytes) when its split schedule is selected, and ignores it otherwise.
@@ -69,7 +86,7 @@ hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, flo
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
                                float* state_out, bf16_t* o, void* workspace, hipStream_t s,
-                               const VarLen& vl = VarLen());
+                               const Opts& vl = Opts());
 bool prefill_bf16_split(int kda);
 size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk);
 

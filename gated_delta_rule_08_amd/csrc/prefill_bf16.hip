@@ -137,6 +137,36 @@ __device__ __forceinline__ uint32_t bf16_half(const uint4& w, int e) {
     return (e & 1) ? (x >> 16) : (x & 0xffffu);
 }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Input prologue on eight packed bf16: sum of squares, and the values scaled
+// by s and rounded to bf16 again.
+__device__ __forceinline__ float sumsq8(const uint4& w) {
+    float a = bf_lo(w.x) * bf_lo(w.x) + bf_hi(w.x) * bf_hi(w.x);
+    float b = bf_lo(w.y) * bf_lo(w.y) + bf_hi(w.y) * bf_hi(w.y);
+    a += bf_lo(w.z) * bf_lo(w.z) + bf_hi(w.z) * bf_hi(w.z);
+    b += bf_lo(w.w) * bf_lo(w.w) + bf_hi(w.w) * bf_hi(w.w);
+    return a + b;
+}
+__device__ __forceinline__ uint4 scale8(const uint4& w, float s) {
+    auto sc = [&](uint32_t x) {
+        return static_cast<uint32_t>(bf_bits(bf_lo(x) * s)) | (static_cast<uint32_t>(bf_bits(bf_hi(x) * s)) << 16);
+    };
+    return make_uint4(sc(w.x), sc(w.y), sc(w.z), sc(w.w));
+}
+// Sum over each group of N adjacent lanes (N = 2, 4, 8, 16), by DPP moves:
+// quad permutations, then the half-row and row mirrors.  Every lane of a
+// group ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    x += dpp_f<0xB1>(x);                         // quad_perm [1, 0, 3, 2]
+    if constexpr (N >= 4) x += dpp_f<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    if constexpr (N >= 8) x += dpp_f<0x141>(x);  // row_half_mirror
+    if constexpr (N >= 16) x += dpp_f<0x140>(x); // row_mirror
+    return x;
+}
 
 // Raw buffer access (SGPR base and range, 32-bit lane offsets).  Loads beyond
 // the range return zero and stores beyond it are dropped, so the rows past the
@@ -186,7 +216,8 @@ struct Layout {
     static constexpr int pA = pScr + kPrepWaves * 16 * PS * 4;  // -A_rk tiles (6)
     static constexpr int pD = pA + 6 * TILE;                     // D_r^{-1} tiles (4)
     static constexpr int pT = pD + 4 * TILE;                     // T_rk tiles, k < r (6)
-    static constexpr int pBytes = pT + 6 * TILE;
+    static constexpr int pNrm = pT + 6 * TILE;  // KDA prologue: per-wave sums of squares [4][64][2]
+    static constexpr int pBytes = pNrm + (KDA ? kPrepWaves * kC * 2 * 4 : 0);
     // GDN kFused, one barrier per chunk: three operand sets (Khat, Qhat and
     // the per-token scalars: prep gates chunk i+2 while the serial waves read
     // chunk i) and two tile sets (P, -A, D_r^{-1}: prep forms chunk i+1).
@@ -279,7 +310,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ state_in,
     float* __restrict__ state_out, bf16_t* __restrict__ o, unsigned char* __restrict__ img,
-    int c0, int c1, VarLen vl) {
+    int c0, int c1, Opts vl) {
     // Chunks c0 .. c1-1 of every sequence (the split schedule runs a long
     // sequence as consecutive ranges, chaining the state through state_in /
     // state_out, so that one range's images stay cache resident).  Packed
@@ -490,6 +521,47 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         // kPrep: copies of Khat, Qhat and beta for the image
         bf16_t* KhI = reinterpret_cast<bf16_t*>(MODE == kPrep && !LITE ? imgp(c) + L::oKh : nullptr);
         bf16_t* QhI = reinterpret_cast<bf16_t*>(MODE == kPrep && !LITE ? imgp(c) + L::oQh : nullptr);
+        // Input prologue.  Sigmoid gates (logits given); inverse norms of the
+        // raw q, k rows, nk[u], nq[u] for token 4 tg + u.  GDN: a row is OPR
+        // adjacent lanes (a DPP sum).  KDA (chunk-local kernel): a row is the
+        // lanes tg, tg+16, tg+32, tg+48 of every wave, so the per-wave sums
+        // meet in LDS behind one barrier, which every wave reaches.
+        const bool sig = (vl.pro & GDR_PRO_SIGMOID) != 0;
+        const bool nrm = (vl.pro & GDR_PRO_L2NORM_QK) != 0;
+        float nk[4] = {1.f, 1.f, 1.f, 1.f}, nq[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (KDA && MODE == kPrep) {
+            if (nrm) {
+                float* part = reinterpret_cast<float*>(smem + L::pNrm);  // [wave][token][k, q]
+                float sk[4], sq[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    sk[u] = gater ? sumsq8(R.kr[u]) : 0.f;
+                    sq[u] = gater ? sumsq8(R.qr[u]) : 0.f;
+                    sk[u] += __shfl_xor(sk[u], 16);
+                    sq[u] += __shfl_xor(sq[u], 16);
+                    sk[u] += __shfl_xor(sk[u], 32);
+                    sq[u] += __shfl_xor(sq[u], 32);
+                }
+                if (lane < 16) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        *reinterpret_cast<float2*>(part + 2 * (wave * kC + 4 * tg + u)) = make_float2(sk[u], sq[u]);
+                }
+                lds_barrier();
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float a = 0.f, bq = 0.f;
+#pragma unroll
+                    for (int w = 0; w < kPrepWaves; ++w) {
+                        const float2 x = *reinterpret_cast<const float2*>(part + 2 * (w * kC + 4 * tg + u));
+                        a += x.x;
+                        bq += x.y;
+                    }
+                    nk[u] = inv_norm(a);
+                    nq[u] = inv_norm(bq);
+                }
+            }
+        }
         if (KDA && !gater) return;
         // a full chunk (every chunk but a ragged last one) needs no row masks
         auto body = [&](auto full_tag) {
@@ -498,9 +570,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
 #pragma unroll
             for (int u = 0; u < 4; ++u) valid[u] = FULL || 4 * tg + u < n;
             if (KDA && oct == 0) {
+                auto bt = [&](int u) { return valid[u] ? (sig ? sigmoid_f(R.bt[u]) : R.bt[u]) : 0.f; };
                 float4 b4;
-                b4.x = valid[0] ? R.bt[0] : 0.f; b4.y = valid[1] ? R.bt[1] : 0.f;
-                b4.z = valid[2] ? R.bt[2] : 0.f; b4.w = valid[3] ? R.bt[3] : 0.f;
+                b4.x = bt(0); b4.y = bt(1); b4.z = bt(2); b4.w = bt(3);
                 *reinterpret_cast<float4*>(sBeta + 4 * tg) = b4;
                 if constexpr (MODE == kPrep) *reinterpret_cast<float4*>(prep_out_f(c, L::oBeta) + 4 * tg) = b4;
             }
@@ -515,12 +587,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 // scanned across the 16 lanes, and the lane's base factor
                 // 2^(off - R) with R = G_end / 2.  Pass 2 walks the tokens with
                 // a running product (2^(G_t - R)) and writes each row at once.
-                float run[8], ce[8];
+                float run[8], ce[8], ga[NA];
+#pragma unroll
+                for (int i = 0; i < NA; ++i) ga[i] = fmaxf(sig ? sigmoid_f(R.a[i]) : R.a[i], kMinGate);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     float p = 1.f;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) p *= valid[u] ? fmaxf(R.a[8 * u + e], kMinGate) : 1.f;
+                    for (int u = 0; u < 4; ++u) p *= valid[u] ? ga[8 * u + e] : 1.f;
                     const float tot = lg2(p);
                     const float inc = row_scan(tot);
                     const float end = __shfl(inc, 15, 16);
@@ -538,8 +612,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     bf16x8 kh, qh, kc;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        run[e] *= valid[u] ? fmaxf(R.a[8 * u + e], kMinGate) : 1.f;  // 2^(G_t - R)
-                        const float kv = bf_at(kz[u], e), qv = bf_at(qz[u], e);
+                        run[e] *= valid[u] ? ga[8 * u + e] : 1.f;  // 2^(G_t - R)
+                        const float kv = bf_at(kz[u], e) * nk[u], qv = bf_at(qz[u], e) * nq[u];
                         const float dn = __builtin_amdgcn_rcpf(run[e]);
                         kh[e] = static_cast<__bf16>(kv * run[e]);
                         qh[e] = static_cast<__bf16>(qv * run[e]);
@@ -566,7 +640,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     // over the wave (in-row DPP scan, then the row totals,
                     // read into scalar registers)
                     const bool vt = FULL || lane < n;
-                    float x = vt ? fmaxf(lg2(R.a[0]), kLog2Floor) : 0.f;
+                    float x = vt ? fmaxf(sig ? log2_sigmoid(R.a[0]) : lg2(R.a[0]), kLog2Floor) : 0.f;
                     x = row_scan(x);
                     auto lane_at = [](float y, int l) {
                         return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y), l));
@@ -590,12 +664,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     sGp(c)[lane] = x;
                     prep_out_f(c, L::oEg)[lane] = ex2(x);
                     prep_out_f(c, L::oEk)[lane] = ex2(end - x);
-                    const float bv = vt ? R.bt[0] : 0.f;
+                    const float bv = vt ? (sig ? sigmoid_f(R.bt[0]) : R.bt[0]) : 0.f;
                     sBeta[lane] = bv;
                     if constexpr (MODE == kPrep) prep_out_f(c, L::oBeta)[lane] = bv;
                     if (lane == 0) prep_out_f(c, L::oGend)[0] = ex2(end);
                 }
                 if (!gater) return;
+                if (MODE == kFused && nrm) {  // a row is the OPR adjacent lanes of one token run
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        kz[u] = scale8(kz[u], inv_norm(lane_group_sum<OPR>(sumsq8(kz[u]))));
+                        qz[u] = scale8(qz[u], inv_norm(lane_group_sum<OPR>(sumsq8(qz[u]))));
+                    }
+                }
                 if constexpr (ONEBAR && DK >= 32) {
                     // channel-permuted rows (see perm_pos).  Octets o and o^2
                     // of a 32-channel group (lanes of one DPP quad) swap one
@@ -1565,7 +1646,7 @@ inline int split_range_chunks(int BH, int nch, size_t img_bytes) {
 template <int DK, int NSW, bool KDA>
 hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, const bf16_t* k,
                   const bf16_t* v, const float* alpha, const float* beta, const float* s_in,
-                  float* s_out, bf16_t* o, unsigned char* img, hipStream_t s, const VarLen& vl) {
+                  float* s_out, bf16_t* o, unsigned char* img, hipStream_t s, const Opts& vl) {
     using L = Layout<DK, NSW, KDA>;
     const int NS = DV / (16 * NSW);
     const int groups = (B * H + 7) / 8;
@@ -1615,7 +1696,7 @@ template <int DK, bool KDA>
 hipError_t dispatch_dvs(int dvs, int B, int T, int H, int DV, float scale, const bf16_t* q,
                         const bf16_t* k, const bf16_t* v, const float* alpha, const float* beta,
                         const float* s_in, float* s_out, bf16_t* o, unsigned char* img,
-                        hipStream_t s, const VarLen& vl) {
+                        hipStream_t s, const Opts& vl) {
     switch (dvs) {
         case 16: return launch<DK, 1, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
         case 32: return launch<DK, 2, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
@@ -1627,7 +1708,7 @@ template <int DK>
 hipError_t dispatch_gate(int kda, int dvs, int B, int T, int H, int DV, float scale,
                          const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* alpha,
                          const float* beta, const float* s_in, float* s_out, bf16_t* o,
-                         unsigned char* img, hipStream_t s, const VarLen& vl) {
+                         unsigned char* img, hipStream_t s, const Opts& vl) {
     return kda ? dispatch_dvs<DK, true>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl)
                : dispatch_dvs<DK, false>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
 }
@@ -1677,7 +1758,7 @@ hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, flo
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
                                float* state_out, bf16_t* o, void* workspace, hipStream_t s,
-                               const VarLen& vl) {
+                               const Opts& vl) {
     const int dvs = prefill_bf16_slice_width(B, H, dv);
     unsigned char* img = prefill_bf16_split(kda) ? static_cast<unsigned char*>(workspace) : nullptr;
     switch (dk) {

@@ -14,6 +14,9 @@
 //     S   <- diag(exp(G_end)) S + Ktil^T U,  Ktil_t = k_t * exp(G_end - G_t)
 // Every exponent is a difference G_a - G_b with a >= b, so no factor exceeds 1.
 // log(alpha) is floored at -40 (exp(-40) ~ 4e-18), which makes alpha == 0 legal.
+// Input prologue (GDR_PRO_*): beta and the log-gates are formed from logits
+// as they are loaded, and the staged q, k rows are scaled by their inverse
+// norms before any product.
 //
 // Mapping: one workgroup (256 threads) per (b, h, slice of up to 32 value
 // columns); the state slice stays in LDS for the whole sequence.
@@ -36,7 +39,8 @@ struct F32Smem {
     static constexpr int kP = kA + kChunk * kChunk;
     static constexpr int kS = kP + kChunk * kChunk;
     static constexpr int kX = kS + DK * DVS;
-    static constexpr int kTotal = kX + kChunk * DVS;
+    static constexpr int kN = kX + kChunk * DVS;  // prologue: 1/||q_t||, 1/||k_t||
+    static constexpr int kTotal = kN + 2 * kChunk;
     static constexpr size_t bytes = sizeof(float) * kTotal;
 };
 
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     int Tmax, int H, int DV, float scale, const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ state_in, float* __restrict__ state_out, float* __restrict__ o,
-    VarLen vl) {
+    Opts vl) {
     using L = F32Smem<DK, DVS, KDA>;
     extern __shared__ float smem[];
     float* Qs = smem + L::kQ;
@@ -56,6 +60,10 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     float* Ps = smem + L::kP;
     float* Ss = smem + L::kS;
     float* Xs = smem + L::kX;
+    float* Ns = smem + L::kN;
+    const bool sig = (vl.pro & GDR_PRO_SIGMOID) != 0;
+    // natural log of a gate (of sigmoid(logit) with the prologue)
+    auto log_gate = [&](float a) { return sig ? 0.6931471805599453f * log2_sigmoid(a) : __logf(a); };
 
     const int nslice = DV / DVS;
     const int slice = blockIdx.x % nslice;
@@ -105,10 +113,28 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
         }
         if (tid < kChunk) {
             const size_t g = (tb + t0 + tid) * H + h;
-            Bs[tid] = tid < n ? beta[g] : 0.0f;
-            if constexpr (!KDA) Gs[tid] = tid < n ? fmaxf(__logf(alpha[g]), kLogFloor) : 0.0f;
+            Bs[tid] = tid < n ? (sig ? sigmoid_f(beta[g]) : beta[g]) : 0.0f;
+            if constexpr (!KDA) Gs[tid] = tid < n ? fmaxf(log_gate(alpha[g]), kLogFloor) : 0.0f;
         }
         __syncthreads();
+        if (vl.pro & GDR_PRO_L2NORM_QK) {
+            // inverse norms of the 64 q rows and 64 k rows (each thread walks
+            // its row from its own start, so the 64 rows hit distinct banks)
+            if (tid < 2 * kChunk) {
+                const float* row = (tid < kChunk ? Qs : Ks) + (tid % kChunk) * DK;
+                float ss = 0.0f;
+                for (int c = 0; c < DK; ++c) {
+                    const float x = row[(c + tid) % DK];
+                    ss += x * x;
+                }
+                Ns[tid] = inv_norm(ss);
+            }
+            __syncthreads();
+            for (int idx = tid; idx < kChunk * DK; idx += 256) {
+                Qs[idx] *= Ns[idx / DK];
+                Ks[idx] *= Ns[kChunk + idx / DK];
+            }
+        }
         // Cumulative log-gate inside the chunk.
         if constexpr (KDA) {
             if (tid < DK) {
@@ -116,7 +142,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
                 for (int t = 0; t < kChunk; ++t) {
                     float g = 0.0f;
                     if (t < n)
-                        g = fmaxf(__logf(alpha[((tb + t0 + t) * H + h) * DK + tid]),
+                        g = fmaxf(log_gate(alpha[((tb + t0 + t) * H + h) * DK + tid]),
                                   kLogFloor);
                     acc += g;
                     Gs[t * DK + tid] = acc;
@@ -208,7 +234,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 template <int DK, int DVS, bool KDA>
 hipError_t launch(int B, int T, int H, int DV, float scale, const float* q, const float* k,
                   const float* v, const float* alpha, const float* beta, const float* s_in,
-                  float* s_out, float* o, hipStream_t s, const VarLen& vl) {
+                  float* s_out, float* o, hipStream_t s, const Opts& vl) {
     using L = F32Smem<DK, DVS, KDA>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
     auto kern = prefill_f32_kernel<DK, DVS, KDA>;
@@ -227,7 +253,7 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const float* q, cons
 template <int DK, bool KDA>
 hipError_t dispatch_dv(int B, int T, int H, int dv, float scale, const float* q,
                        const float* k, const float* v, const float* alpha, const float* beta,
-                       const float* s_in, float* s_out, float* o, hipStream_t s, const VarLen& vl) {
+                       const float* s_in, float* s_out, float* o, hipStream_t s, const Opts& vl) {
     if (dv == 16)
         return launch<DK, 16, KDA>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s, vl);
     return launch<DK, 32, KDA>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s, vl);
@@ -236,7 +262,7 @@ hipError_t dispatch_dv(int B, int T, int H, int dv, float scale, const float* q,
 template <int DK>
 hipError_t dispatch_gate(int kda, int B, int T, int H, int dv, float scale, const float* q,
                          const float* k, const float* v, const float* alpha, const float* beta,
-                         const float* s_in, float* s_out, float* o, hipStream_t s, const VarLen& vl) {
+                         const float* s_in, float* s_out, float* o, hipStream_t s, const Opts& vl) {
     return kda ? dispatch_dv<DK, true>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s, vl)
                : dispatch_dv<DK, false>(B, T, H, dv, scale, q, k, v, alpha, beta, s_in, s_out, o, s, vl);
 }
@@ -246,7 +272,7 @@ hipError_t dispatch_gate(int kda, int B, int T, int H, int dv, float scale, cons
 hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, float scale,
                               const float* q, const float* k, const float* v,
                               const float* alpha, const float* beta, const float* state_in,
-                              float* state_out, float* o, hipStream_t s, const VarLen& vl) {
+                              float* state_out, float* o, hipStream_t s, const Opts& vl) {
     switch (dk) {
         case 16: return dispatch_gate<16>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s, vl);
         case 32: return dispatch_gate<32>(kda, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, s, vl);

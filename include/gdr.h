@@ -67,7 +67,7 @@ enum {
     GDR_ERR_UNSUPPORTED = -3, /* dk, dv or chunk outside the supported set  */
     GDR_ERR_MISALIGNED = -4,  /* a pointer violates the alignment rule      */
     GDR_ERR_WORKSPACE = -5,   /* workspace missing or too small             */
-    GDR_ERR_BAD_ENUM = -6,    /* gate or dtype is not a known enumerator    */
+    GDR_ERR_BAD_ENUM = -6,    /* gate, dtype or flags not known             */
     GDR_ERR_HIP = -7,         /* the HIP runtime rejected a launch          */
     GDR_ERR_ALIAS = -8        /* two state buffers (partially) overlap      */
 };
@@ -87,6 +87,33 @@ int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float sca
                     const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta,
                     float* state, void* o, void* stream);
+
+/*
+ * Input prologue flags of the *_ex entry points (bitwise OR; 0 = none).  The
+ * mixers' inputs usually come out of a projection followed by two cheap
+ * transforms; these flags run them inside the kernels, where q, k and the
+ * gates are loaded, instead of as separate passes over HBM:
+ *   GDR_PRO_L2NORM_QK   q and k are raw: each dk-vector q[b,t,h,:] and
+ *                       k[b,t,h,:] is divided by max(||x||_2, 1e-12) in fp32
+ *                       (bf16 inputs: the normalised values feed the bf16
+ *                       matrix products rounded to bf16 again).
+ *   GDR_PRO_SIGMOID     alpha and beta are logits: the kernels use
+ *                       sigmoid(alpha) and sigmoid(beta) (the chunked paths
+ *                       take log2 sigmoid(alpha) directly, so very negative
+ *                       logits keep their size instead of underflowing).
+ * Other bits return GDR_ERR_BAD_ENUM.
+ */
+enum { GDR_PRO_L2NORM_QK = 1, GDR_PRO_SIGMOID = 2 };
+
+/*
+ * gdr_decode_step with an input prologue (flags: GDR_PRO_*): the same step
+ * on normalised q, k and sigmoid gates.  flags == 0 is gdr_decode_step
+ * exactly (the same kernel and arithmetic).
+ */
+int gdr_decode_step_ex(int gate, int dtype, int flags, int B, int H, int dk, int dv, float scale,
+                       const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta,
+                       float* state, void* o, void* stream);
 
 /*
  * T consecutive decode steps per head in one call, the verify step of
@@ -147,6 +174,21 @@ int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, 
  * arguments are invalid or no scratch is needed). */
 size_t gdr_chunk_prefill_workspace_bytes(int gate, int dtype, int B, int T, int H,
                                          int dk, int dv, int chunk);
+
+/*
+ * gdr_chunk_prefill with an input prologue (flags: GDR_PRO_*), same
+ * arguments and workspace.  flags == 0 is gdr_chunk_prefill exactly.
+ * GDR_PRO_SIGMOID runs in every schedule; GDR_PRO_L2NORM_QK runs in the fp32
+ * path and in the default bf16 schedules (the fused GDN kernel, the split KDA
+ * kernels), and returns GDR_ERR_UNSUPPORTED when GDR_PREFILL_PATH selects
+ * the other bf16 schedule.
+ */
+int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
+                         int chunk, float scale,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta,
+                         const float* state_in, float* state_out, void* o,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Chunked prefill of N packed variable-length sequences whose states live in

@@ -240,3 +240,29 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         gdr.gdr_decode_step("gdn", q, q, q, torch.zeros(1, 1), torch.zeros(1, 1),
                             torch.zeros(1, 1, 16, 16), torch.zeros(1, 1, 16))
+
+
+def test_prologue_flag_validation(lib, monkeypatch):
+    """Unknown prologue bits are BAD_ENUM; the normalising prologue in a bf16
+    schedule that does not form the chunk-local products itself is
+    UNSUPPORTED; everything is checked before the device is touched."""
+    p = list(P[:8])
+    assert lib.gdr_decode_step_ex(0, 1, 4, 2, 3, 128, 128, 1.0, *p) == ENUM
+    assert lib.gdr_decode_step_ex(0, 1, -1, 2, 3, 128, 128, 1.0, *p) == ENUM
+    assert lib.gdr_decode_step_ex(0, 1, 3, 0, 3, 128, 128, 1.0, *([None] * 8)) == OK
+    assert lib.gdr_decode_step_ex(0, 1, 3, 2, 3, 100, 128, 1.0, *p) == UNSUP
+
+    def pre(gate, dtype, flags, T=70):
+        return lib.gdr_chunk_prefill_ex(gate, dtype, flags, 2, T, 3, 128, 128, 64, 1.0,
+                                        *([None] * 8), None, 0, None)
+
+    assert pre(0, 1, 8) == ENUM
+    for path in ("fused", "split"):
+        monkeypatch.setenv("GDR_PREFILL_PATH", path)
+        # GDN normalises in the fused kernel, KDA in the split one
+        assert pre(0, 1, 1) == (NULL if path == "fused" else UNSUP)
+        assert pre(1, 1, 1) == (UNSUP if path == "fused" else WS)
+        assert pre(0, 1, 2) in (NULL, WS)  # the sigmoid runs in every schedule
+        assert pre(1, 0, 3) == NULL        # fp32 path: both
+    monkeypatch.delenv("GDR_PREFILL_PATH")
+    assert pre(0, 1, 3) == NULL and pre(1, 1, 3) == WS
