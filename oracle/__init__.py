@@ -12,7 +12,10 @@ definition and the chunked algebra):
 * :func:`brute`      -- NumPy, dense per-token transition matrices
   ``M_t = (I - beta_t k_t k_t^T) D_t``, for tiny inputs only;
 * :func:`prologue`   -- NumPy, the input steps before the mixer (q/k L2
-  normalisation, sigmoid of the gate logits).
+  normalisation, sigmoid of the gate logits);
+* :func:`backward`   -- NumPy, reverse-mode gradients of the token recurrence
+  (pinned by central finite differences of :func:`recurrent` and by closed
+  forms; see tests/test_oracle.py).
 
 Pins: every function here is checked against facts fixed by the mathematics
 (identity and rank-one special cases, the delta rule's exact recall, a scalar
@@ -188,3 +191,64 @@ def brute(q, k, v, alpha, beta, s0=None, scale: float = 1.0):
                 o[b, t, h] = scale * (S.T @ q[b, t, h])
             sT[b, h] = S
     return o, sT
+
+
+def backward(q, k, v, alpha, beta, s0, do, ds_t=None, scale: float = 1.0):
+    """Gradients of L = sum(do * o) + sum(ds_t * S_T) through the token
+    recurrence, float64.
+
+    Forward, per (b, h) and token t (D_t = alpha_t I or diag(alpha_t)):
+        S'_t = D_t S_{t-1},  u_t = S'_t^T k_t,  e_t = v_t - u_t,
+        S_t = S'_t + beta_t k_t e_t^T,  o_t = scale S_t^T q_t.
+    Reverse, with G the gradient of L with respect to S_t (starting from
+    ds_t) and each forward step undone in the opposite order:
+        G += scale q_t do_t^T;           dq_t = scale S_t do_t
+        g = G^T k_t (d/d e_t = beta_t g): dv_t = beta_t g,
+                                           dbeta_t = e_t . g,
+                                           dk_t = beta_t G e_t
+        du_t = -beta_t g;  G' = G + k_t du_t^T;  dk_t += S'_t du_t
+        dalpha_t = sum_j G'[:, j] * S_{t-1}[:, j]   (summed over i for GDN)
+        G = D_t G'
+    and dS_0 = G at the end.  Returns a dict with dq, dk, dv, dalpha, dbeta,
+    ds0 shaped like the inputs (ds0 like s0, zeros-state when s0 is None).
+    """
+    q, k, v, alpha, beta, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, alpha, beta, do))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    kda = alpha.ndim == 4
+    s = np.zeros((B, H, dk, dv)) if s0 is None else np.array(s0, dtype=np.float64)
+    # forward, keeping S_{t-1} and S'_t
+    prev, decayed, states = [], [], []
+    for t in range(T):
+        a = alpha[:, t][..., None] if kda else alpha[:, t][..., None, None]   # [B,H,dk,1] or [B,H,1,1]
+        prev.append(s)
+        sp = a * s
+        u = np.einsum("bhij,bhi->bhj", sp, k[:, t])
+        e = v[:, t] - u
+        s = sp + beta[:, t][..., None, None] * k[:, t][..., :, None] * e[..., None, :]
+        decayed.append((sp, e))
+        states.append(s)
+    G = np.zeros((B, H, dk, dv)) if ds_t is None else np.array(ds_t, dtype=np.float64)
+    dq, dkk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    da, db = np.zeros_like(alpha), np.zeros_like(beta)
+    for t in reversed(range(T)):
+        sp, e = decayed[t]
+        bt = beta[:, t][..., None]                                  # [B,H,1]
+        G = G + scale * q[:, t][..., :, None] * do[:, t][..., None, :]
+        dq[:, t] = scale * np.einsum("bhij,bhj->bhi", states[t], do[:, t])
+        g = np.einsum("bhij,bhi->bhj", G, k[:, t])                  # G^T k
+        dvv[:, t] = bt * g
+        db[:, t] = np.sum(e * g, axis=-1)
+        dkk[:, t] = bt * np.einsum("bhij,bhj->bhi", G, e)
+        du = -bt * g
+        Gp = G + k[:, t][..., :, None] * du[..., None, :]
+        dkk[:, t] += np.einsum("bhij,bhj->bhi", sp, du)
+        row = np.sum(Gp * prev[t], axis=-1)                         # [B,H,dk]
+        if kda:
+            da[:, t] = row
+            G = alpha[:, t][..., None] * Gp
+        else:
+            da[:, t] = np.sum(row, axis=-1)
+            G = alpha[:, t][..., None, None] * Gp
+    return {"dq": dq, "dk": dkk, "dv": dvv, "dalpha": da, "dbeta": db, "ds0": G}
+

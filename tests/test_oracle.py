@@ -314,3 +314,96 @@ def test_prologue_matches_the_input_generator():
     assert np.allclose(qn, inp["q"], atol=1e-6) and np.allclose(kn, inp["k"], atol=1e-6)
     assert np.allclose(a, inp["alpha"], atol=1e-6) and np.allclose(b, inp["beta"], atol=1e-6)
 
+
+
+# ---------------------------------------------------------------- backward
+
+def _bwd_case(kda, B=1, T=5, H=2, dk=3, dv=4, seed=0, with_s0=True, with_dst=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((B, T, H, dv))
+    alpha = rng.uniform(0.5, 1.0, (B, T, H, dk) if kda else (B, T, H))
+    beta = rng.uniform(0.1, 0.9, (B, T, H))
+    s0 = rng.standard_normal((B, H, dk, dv)) if with_s0 else None
+    do = rng.standard_normal((B, T, H, dv))
+    dst = rng.standard_normal((B, H, dk, dv)) if with_dst else None
+    return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, s0=s0, do=do, dst=dst)
+
+
+def _loss(c, scale, **over):
+    x = dict(c, **over)
+    o, sT = oracle.recurrent(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["s0"], scale=scale)
+    val = float(np.sum(c["do"] * o))
+    if c["dst"] is not None:
+        val += float(np.sum(c["dst"] * sT))
+    return val
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_backward_matches_central_differences(kda):
+    """Every gradient entry against (L(x + h) - L(x - h)) / 2h of the C
+    token recurrence (a code path the backward does not share)."""
+    c = _bwd_case(kda, seed=3 + kda)
+    scale = 0.7
+    g = oracle.backward(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["s0"], c["do"], c["dst"],
+                        scale=scale)
+    h = 1e-6
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("alpha", "dalpha"),
+                      ("beta", "dbeta"), ("s0", "ds0")):
+        x = c[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd[idx] = (_loss(c, scale, **{name: xp}) - _loss(c, scale, **{name: xm})) / (2 * h)
+        err = np.abs(g[key] - fd).max() / max(np.abs(fd).max(), 1e-12)
+        assert err < 1e-6, (name, err)
+
+
+def test_backward_single_token_closed_form():
+    """T = 1 from a zero state: o = scale beta (k.q) v and S_1 = beta k v^T,
+    so every gradient has a closed form."""
+    c = _bwd_case(False, B=2, T=1, H=3, dk=4, dv=5, seed=9, with_s0=False)
+    scale = 1.3
+    g = oracle.backward(c["q"], c["k"], c["v"], c["alpha"], c["beta"], None, c["do"], c["dst"], scale=scale)
+    q, k, v, b, do, dst = c["q"][:, 0], c["k"][:, 0], c["v"][:, 0], c["beta"][:, 0], c["do"][:, 0], c["dst"]
+    kq = np.sum(k * q, -1)
+    vdo = np.sum(v * do, -1)
+    dstk = np.einsum("bhij,bhi->bhj", dst, k)          # dst^T k
+    dstv = np.einsum("bhij,bhj->bhi", dst, v)          # dst v
+    np.testing.assert_allclose(g["dv"][:, 0], (scale * b * kq)[..., None] * do + b[..., None] * dstk, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dbeta"][:, 0], scale * kq * vdo + np.sum(k * dstv, -1), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dq"][:, 0], (scale * b * vdo)[..., None] * k, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dk"][:, 0], (scale * b * vdo)[..., None] * q + b[..., None] * dstv, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dalpha"], 0.0, atol=1e-15)   # the gate multiplies the zero state
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_backward_pure_decay_closed_form(kda):
+    """beta = 0: S_t = (prod of the gates up to t) S_0, so dS_0 and the gate
+    gradients are sums of decayed outer products."""
+    c = _bwd_case(kda, B=1, T=4, H=2, dk=3, dv=2, seed=5)
+    c["beta"] = np.zeros_like(c["beta"])
+    scale = 0.9
+    g = oracle.backward(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["s0"], c["do"], c["dst"], scale=scale)
+    a = c["alpha"] if kda else c["alpha"][..., None] * np.ones(c["q"].shape)   # [B,T,H,dk]
+    cum = np.cumprod(a, axis=1)                                                 # prod_{s<=t}
+    want = cum[:, -1][..., None] * c["dst"]
+    for t in range(4):
+        want += scale * cum[:, t][..., None] * c["q"][:, t][..., :, None] * c["do"][:, t][..., None, :]
+    np.testing.assert_allclose(g["ds0"], want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dv"], 0.0, atol=1e-15)
+    np.testing.assert_allclose(g["dk"], 0.0, atol=1e-15)
+
+
+def test_backward_is_linear_in_the_output_gradient():
+    c = _bwd_case(True, B=1, T=6, H=1, dk=4, dv=3, seed=8)
+    d2 = np.random.default_rng(1).standard_normal(c["do"].shape)
+    args = (c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["s0"])
+    g1 = oracle.backward(*args, c["do"], None)
+    g2 = oracle.backward(*args, d2, None)
+    g3 = oracle.backward(*args, c["do"] + 2.0 * d2, None)
+    for key in g1:
+        np.testing.assert_allclose(g3[key], g1[key] + 2.0 * g2[key], rtol=1e-10, atol=1e-10)
