@@ -20,7 +20,7 @@ __all__ = [
     "gdr_decode_multi", "gdr_chunk_prefill", "gdr_chunk_prefill_varlen",
     "gdr_chunk_prefill_varlen_workspace_bytes", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
     "gdr_abi_version", "EXPORTED_SYMBOLS", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
-    "PRO_L2NORM_QK", "PRO_SIGMOID",
+    "PRO_L2NORM_QK", "PRO_SIGMOID", "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +30,7 @@ _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 PRO_L2NORM_QK = 1
 PRO_SIGMOID = 2
 EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
+                    "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
                     "gdr_decode_multi", "gdr_chunk_prefill",
                     "gdr_chunk_prefill_varlen", "gdr_chunk_prefill_varlen_workspace_bytes",
                     "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
@@ -65,6 +66,10 @@ def load_library():
     lib.gdr_decode_step_ex.restype = i
     lib.gdr_chunk_prefill_ex.argtypes = [i] * 9 + [f] + [vp] * 9 + [ctypes.c_size_t, vp]
     lib.gdr_chunk_prefill_ex.restype = i
+    lib.gdr_chunk_backward.argtypes = [i] * 8 + [f] + [vp] * 15 + [ctypes.c_size_t, vp]
+    lib.gdr_chunk_backward.restype = i
+    lib.gdr_chunk_backward_workspace_bytes.argtypes = [i] * 8
+    lib.gdr_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.gdr_decode_multi.argtypes = [i] * 7 + [f] + [vp] * 9
     lib.gdr_decode_multi.restype = i
     lib.gdr_chunk_prefill.argtypes = [i] * 8 + [f] + [vp] * 9 + [ctypes.c_size_t, vp]
@@ -303,3 +308,50 @@ def gdr_chunk_prefill_varlen(gate: str, q, k, v, alpha, beta, cu_seqlens, state_
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), _ptr(state_slots),
         _ptr(has_state), _ptr(states), states.shape[0], _ptr(o), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def gdr_chunk_backward_workspace_bytes(gate: str, dtype, B: int, T: int, H: int, dk: int, dv: int,
+                                       chunk: int = CHUNK) -> int:
+    return int(load_library().gdr_chunk_backward_workspace_bytes(
+        GATES[gate], _DTYPES[dtype], B, T, H, dk, dv, chunk))
+
+
+def gdr_chunk_backward(gate: str, q, k, v, alpha, beta, state_in, grad_o, grad_state_out,
+                       grad_q, grad_k, grad_v, grad_alpha, grad_beta, grad_state_in=None,
+                       scale: float = 1.0, workspace=None, chunk: int = CHUNK, stream=None) -> None:
+    """Gradients of sum(grad_o * o) + sum(grad_state_out * S_T) through the
+    chunked prefill, written into grad_* (shapes and dtypes of the inputs;
+    grad_alpha, grad_beta, grad_state_in fp32).  state_in, grad_state_out and
+    grad_state_in may be None.  workspace: a device tensor of at least
+    gdr_chunk_backward_workspace_bytes bytes, or None to allocate one."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or grad_o.shape != (B, T, H, dv):
+        raise ValueError("q, k, v, grad_o shapes disagree")
+    if grad_q.shape != q.shape or grad_k.shape != q.shape or grad_v.shape != v.shape:
+        raise ValueError("gradient shapes must match the inputs")
+    ash = (B, T, H, dk) if gate == "kda" else (B, T, H)
+    if alpha.shape != ash or beta.shape != (B, T, H) or grad_alpha.shape != ash or grad_beta.shape != (B, T, H):
+        raise ValueError("alpha / beta (or their gradients) disagree with the gate mode")
+    for st in (state_in, grad_state_out, grad_state_in):
+        if st is not None and (st.shape != (B, H, dk, dv) or st.dtype != torch.float32):
+            raise ValueError("states must be fp32 [B,H,dk,dv]")
+    if not (q.dtype == k.dtype == v.dtype == grad_o.dtype == grad_q.dtype == grad_k.dtype == grad_v.dtype) \
+            or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, grad_o and grad_q/k/v must share dtype fp32 or bf16")
+    for t in (alpha, beta, grad_alpha, grad_beta):
+        if t.dtype != torch.float32:
+            raise ValueError("gates and their gradients must be fp32")
+    _same_device(q, k, v, alpha, beta, state_in, grad_o, grad_state_out, grad_q, grad_k, grad_v,
+                 grad_alpha, grad_beta, grad_state_in, workspace)
+    if workspace is None:
+        need = gdr_chunk_backward_workspace_bytes(gate, q.dtype, B, T, H, dk, dv, chunk)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().gdr_chunk_backward(
+        GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(grad_o), _ptr(grad_state_out), _ptr(grad_q),
+        _ptr(grad_k), _ptr(grad_v), _ptr(grad_alpha), _ptr(grad_beta), _ptr(grad_state_in),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+

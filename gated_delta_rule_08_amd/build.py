@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdr.so")
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gdr_api.hip", "decode.hip", "prefill_f32.hip", "prefill_bf16.hip"]
+SOURCES = ["gdr_api.hip", "decode.hip", "prefill_f32.hip", "prefill_bf16.hip", "backward.hip"]
 
 HIPFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

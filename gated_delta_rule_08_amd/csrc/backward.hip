@@ -1,0 +1,697 @@
+// Backward pass of the chunked gated delta rule (dq, dk, dv, dalpha, dbeta,
+// dS_0 from dO and dS_T), in fp32 on the vector ALUs.
+//
+// The mixers ("Super Apriel: One Checkpoint, Many Speeds", §2.A: GDN and KDA,
+// recurrent mixers with scalar and channel-wise gates) are trained in the
+// pages' stages §2.B, so their recurrence is differentiated here.  Per chunk
+// of n <= 64 tokens entering with state S (rows t, s; key channel c; value
+// column j), with G the cumulative log-gate inside the chunk (per channel for
+// KDA, floored per token at -40 as in the forward) and
+//   E(t,s,c) = exp(G_tc - G_sc)  (s <= t),   e0 = exp(G_t),
+//   ek = exp(G_end - G_t),                    eE = exp(G_end),
+// the forward is
+//   Ahat_ts = sum_c k_tc k_sc E (s < t),  A = diag(beta) Ahat,
+//   P_ts    = sum_c q_tc k_sc E (s <= t), Tinv = (I + A)^{-1}
+//   Xr = V - (k e0) S,  U = Tinv diag(beta) Xr
+//   O  = scale ((q e0) S + P U),  S_end = eE S + (k ek)^T U.
+// Reverse, given dO and dS_end (chunk by chunk from the last):
+//   dU = scale P^T dO + (k ek) dS_end,   dX = Tinv^T dU,   dV = beta dX
+//   dS = eE dS_end + scale (q e0)^T dO - (k e0)^T diag(beta) dX
+//   dA = -dX U^T (s < t),  dP = scale dO U^T (s <= t)
+//   dQ0 = scale dO S^T,  dK0 = -diag(beta) dX S^T,  dKt = U dS_end^T
+//   dbeta_t = sum_j Xr_tj dX_tj + sum_s dA_ts Ahat_ts
+// and, with M = diag(beta) dA, N = dP and the four sums
+//   a1 = sum_{s<t} M_ts k_sc E(t,s,c),   a2 = sum_{s<=t} N_ts k_sc E(t,s,c),
+//   a3 = sum_{r>t} M_rt k_rc E(r,t,c),   a4 = sum_{r>=t} N_rt q_rc E(r,t,c),
+//   dq = dQ0 e0 + a2,   dk = dK0 e0 + dKt ek + a1 + a3 + a4,
+//   dG = q (dQ0 e0 + a2) + k (dK0 e0 - dKt ek + a1 - a3 - a4),
+//   dG_end = eE sum_j dS_end S + sum_t dKt k ek   (added to the last token),
+// dlog alpha_s = sum_{t >= s} dG_t inside the chunk, dalpha = dlog alpha / alpha
+// (zero where the floor is active).
+//
+// Kernels (one head per (b, h); 16-column value slices where the work
+// separates by value column):
+//   bwd_prep   (b, h, chunk)  Ahat, P and Tinv of every chunk -> image
+//   bwd_fwd    (b, h, slice)  forward chain: S at every chunk start
+//                             (checkpoints) and Xr
+//   bwd_chain  (b, h, slice)  reverse chain: dS_end of every chunk, U, dX,
+//                             dV and the Xr.dX part of dbeta
+//   bwd_local  (b, h, chunk)  the contractions over all value columns and
+//                             everything that maps back to q, k, beta, alpha
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+constexpr int kC = 64;
+constexpr int kSl = 16;  // value columns per slice
+constexpr float kFloor = -40.0f;
+constexpr int kTP = kC + 1;  // pitch of 64 x 64 tiles in LDS
+
+template <typename T> __device__ __forceinline__ float ld(const T* p);
+template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+
+__device__ __forceinline__ float log_gate(float a) { return fmaxf(__logf(a), kFloor); }
+
+// Per-chunk image (floats): Ahat, P, Tinv [64][64] each, then K0 = k e0,
+// Kt = k ek, Q0 = q e0 [64][dk] each, then eE [dk].
+enum { iA = 0, iP = kC * kC, iT = 2 * kC * kC, iK0 = 3 * kC * kC };
+__host__ __device__ constexpr size_t img_floats(int dk) { return 3 * kC * kC + 3 * kC * dk + dk; }
+
+// Workspace layout (floats), shared by the host sizing and the kernels.
+struct Ws {
+    size_t img, ck, dck, xr, u, dx, dbp, total;
+    __host__ __device__ Ws(int B, int T, int H, int dk, int dv) {
+        const size_t bh = static_cast<size_t>(B) * H;
+        const size_t nch = (static_cast<size_t>(T) + kC - 1) / kC;
+        const size_t tok = static_cast<size_t>(B) * T * H;
+        img = 0;                                  // [bh][chunk][img_floats(dk)]
+        ck = img + bh * nch * img_floats(dk);     // [bh][chunk][dk][dv]: S at chunk start
+        dck = ck + bh * nch * dk * dv;            // [bh][chunk][dk][dv]: dS at chunk end
+        xr = dck + bh * nch * dk * dv;            // [B,T,H,dv]
+        u = xr + tok * dv;
+        dx = u + tok * dv;
+        dbp = dx + tok * dv;                      // [dv/16][B,T,H]
+        total = dbp + tok * (dv / kSl);
+    }
+};
+
+struct Args {
+    int B, T, H, DV, nch;
+    float scale;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* s0;
+    const void* dO;
+    const float* dsT;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dalpha;
+    float* dbeta;
+    float* ds0;
+    float* ws;
+};
+
+// ---------------------------------------------------------------- bwd_prep
+// Chunk-local quantities of one chunk: its gates (all threads stage the
+// log-gates, one thread per channel sums them in LDS), Ahat and P, the
+// factored rows K0, Kt, Q0 and eE, and Tinv by forward substitution.
+template <int DK, bool KDA, typename InT>
+__global__ __launch_bounds__(256) void bwd_prep(Args a) {
+    constexpr int KP = DK + 1;
+    constexpr int GW = KDA ? DK : 1;
+    constexpr int GP = GW + 1;
+    extern __shared__ float sm[];
+    float* Ks = sm;                 // [64][KP]
+    float* Qs = Ks + kC * KP;       // [64][KP]
+    float* Gs = Qs + kC * KP;       // [64][GP]
+    float* As = Gs + kC * GP;       // [64][kTP]  beta-scaled A
+    float* Tl = As + kC * kTP;      // [64][kTP]  Tinv
+    float* Bs = Tl + kC * kTP;      // [64]
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int t0 = ch * kC, n = min(kC, a.T - t0);
+    const InT* q = static_cast<const InT*>(a.q);
+    const InT* k = static_cast<const InT*>(a.k);
+    auto tok = [&](int t) { return (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h; };
+    for (int i = tid; i < kC * DK; i += 256) {
+        const int t = i / DK, c = i - t * DK;
+        Ks[t * KP + c] = t < n ? ld(k + tok(t) * DK + c) : 0.f;
+        Qs[t * KP + c] = t < n ? ld(q + tok(t) * DK + c) : 0.f;
+    }
+    for (int i = tid; i < kC * GW; i += 256) {
+        const int t = i / GW, c = i - t * GW;
+        Gs[t * GP + c] = t < n ? log_gate(KDA ? a.alpha[tok(t) * DK + c] : a.alpha[tok(t)]) : 0.f;
+    }
+    if (tid < kC) Bs[tid] = tid < n ? a.beta[tok(tid)] : 0.f;
+    __syncthreads();
+    if (tid < GW) {  // cumulative log-gate (padded tokens add nothing)
+        float acc = 0.f;
+        for (int t = 0; t < kC; ++t) {
+            acc += Gs[t * GP + tid];
+            Gs[t * GP + tid] = acc;
+        }
+    }
+    __syncthreads();
+    float* img = a.ws + Ws(a.B, a.T, a.H, DK, a.DV).img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+    for (int i = tid; i < kC * kC; i += 256) {
+        const int t = i >> 6, s = i & 63;
+        float sa = 0.f, sp = 0.f;
+        if (s <= t) {
+            for (int c = 0; c < DK; ++c) {
+                const float e = __expf(Gs[t * GP + (KDA ? c : 0)] - Gs[s * GP + (KDA ? c : 0)]);
+                const float kse = Ks[s * KP + c] * e;
+                sa += Ks[t * KP + c] * kse;
+                sp += Qs[t * KP + c] * kse;
+            }
+        }
+        if (s == t) sa = 0.f;
+        img[iA + i] = sa;
+        img[iP + i] = sp;
+        As[t * kTP + s] = Bs[t] * sa;
+    }
+    for (int i = tid; i < kC * DK; i += 256) {
+        const int t = i / DK, c = i - t * DK;
+        const float g = Gs[t * GP + (KDA ? c : 0)], ge = Gs[(kC - 1) * GP + (KDA ? c : 0)];
+        const float e0 = __expf(g);
+        img[iK0 + i] = Ks[t * KP + c] * e0;
+        img[iK0 + kC * DK + i] = Ks[t * KP + c] * __expf(ge - g);
+        img[iK0 + 2 * kC * DK + i] = Qs[t * KP + c] * e0;
+        if (t == 0) img[iK0 + 3 * kC * DK + c] = __expf(ge);
+    }
+    __syncthreads();
+    // Tinv = (I + A)^{-1}, unit lower triangular: column s by forward
+    // substitution, one thread per column (each reads only its own column).
+    if (tid < kC) {
+        const int s = tid;
+        for (int t = 0; t < kC; ++t) {
+            float v = t == s ? 1.f : 0.f;
+            for (int r = s; r < t; ++r) v -= As[t * kTP + r] * Tl[r * kTP + s];
+            Tl[t * kTP + s] = v;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < kC * kC; i += 256) img[iT + i] = Tl[(i >> 6) * kTP + (i & 63)];
+}
+
+// The factored rows, eE and beta of one chunk from its image (all threads,
+// coalesced).  Q0 is skipped when null.
+template <int DK>
+__device__ __forceinline__ void load_factors(const Args& a, const float* im, int b, int h, int t0, int n,
+                                             float* K0, float* Kt, float* Q0, float* eE, float* Bs) {
+    constexpr int KP = DK + 1;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kC * DK; i += 256) {
+        const int t = i / DK, c = i - t * DK;
+        K0[t * KP + c] = im[iK0 + i];
+        Kt[t * KP + c] = im[iK0 + kC * DK + i];
+        if (Q0) Q0[t * KP + c] = im[iK0 + 2 * kC * DK + i];
+    }
+    if (tid < DK) eE[tid] = im[iK0 + 3 * kC * DK + tid];
+    if (tid < kC) Bs[tid] = tid < n ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
+}
+
+// ---------------------------------------------------------------- bwd_fwd
+template <int DK, bool KDA, typename InT>
+__global__ __launch_bounds__(256) void bwd_fwd(Args a) {
+    constexpr int KP = DK + 1;
+    extern __shared__ float sm[];
+    float* K0 = sm;                  // [64][KP]
+    float* Kt = K0 + kC * KP;        // [64][KP]
+    float* Ti = Kt + kC * KP;        // [64][kTP]
+    float* Ss = Ti + kC * kTP;       // [DK][kSl]
+    float* Xs = Ss + DK * kSl;       // [64][kSl]  Xr
+    float* Us = Xs + kC * kSl;       // [64][kSl]
+    float* eE = Us + kC * kSl;       // [DK]
+    float* Bs = eE + DK;             // [64]
+    const int tid = threadIdx.x;
+    const int nsl = a.DV / kSl;
+    const int bh = blockIdx.x / nsl, sl = blockIdx.x - (blockIdx.x / nsl) * nsl;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int j0 = sl * kSl;
+    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    const InT* v = static_cast<const InT*>(a.v);
+    for (int i = tid; i < DK * kSl; i += 256) {
+        const int c = i / kSl, j = i - c * kSl;
+        Ss[i] = a.s0 ? a.s0[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
+    }
+    for (int ch = 0; ch < a.nch; ++ch) {
+        const int t0 = ch * kC, n = min(kC, a.T - t0);
+        __syncthreads();  // the previous chunk is done with every buffer
+        float* ck = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+        for (int i = tid; i < DK * kSl; i += 256) {
+            const int c = i / kSl, j = i - c * kSl;
+            ck[static_cast<size_t>(c) * a.DV + j0 + j] = Ss[i];
+        }
+        const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, nullptr, eE, Bs);
+        for (int i = tid; i < kC * kC; i += 256) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
+        __syncthreads();
+        // Xr = V - K0 S
+        for (int i = tid; i < kC * kSl; i += 256) {
+            const int t = i / kSl, j = i - t * kSl;
+            float acc = 0.f;
+            for (int c = 0; c < DK; ++c) acc += K0[t * KP + c] * Ss[c * kSl + j];
+            const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
+            const float x = t < n ? ld(v + r * a.DV + j0 + j) - acc : 0.f;
+            Xs[i] = x;
+            if (t < n) a.ws[W.xr + r * a.DV + j0 + j] = x;
+        }
+        __syncthreads();
+        // U = Tinv diag(beta) Xr
+        for (int i = tid; i < kC * kSl; i += 256) {
+            const int t = i / kSl, j = i - t * kSl;
+            float acc = 0.f;
+            for (int s = 0; s <= t; ++s) acc += Ti[t * kTP + s] * Bs[s] * Xs[s * kSl + j];
+            Us[i] = acc;
+        }
+        __syncthreads();
+        // S <- eE S + Kt^T U
+        for (int i = tid; i < DK * kSl; i += 256) {
+            const int c = i / kSl, j = i - c * kSl;
+            float acc = eE[c] * Ss[i];
+            for (int t = 0; t < kC; ++t) acc += Kt[t * KP + c] * Us[t * kSl + j];
+            Ss[i] = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bwd_chain
+template <int DK, bool KDA, typename InT>
+__global__ __launch_bounds__(256) void bwd_chain(Args a) {
+    constexpr int KP = DK + 1;
+    extern __shared__ float sm[];
+    float* K0 = sm;                  // [64][KP]
+    float* Kt = K0 + kC * KP;        // [64][KP]
+    float* Q0 = Kt + kC * KP;        // [64][KP]
+    float* Ti = Q0 + kC * KP;        // [64][kTP]
+    float* Ps = Ti + kC * kTP;       // [64][kTP]
+    float* dS = Ps + kC * kTP;       // [DK][kSl]
+    float* Xs = dS + DK * kSl;       // [64][kSl]  Xr
+    float* Os = Xs + kC * kSl;       // [64][kSl]  dO
+    float* Us = Os + kC * kSl;       // [64][kSl]  U
+    float* dU = Us + kC * kSl;       // [64][kSl]  dU, then dX
+    float* eE = dU + kC * kSl;       // [DK]
+    float* Bs = eE + DK;             // [64]
+    const int tid = threadIdx.x;
+    const int nsl = a.DV / kSl;
+    const int bh = blockIdx.x / nsl, sl = blockIdx.x - (blockIdx.x / nsl) * nsl;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int j0 = sl * kSl;
+    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    const InT* dO = static_cast<const InT*>(a.dO);
+    InT* dv = static_cast<InT*>(a.dv);
+    for (int i = tid; i < DK * kSl; i += 256) {
+        const int c = i / kSl, j = i - c * kSl;
+        dS[i] = a.dsT ? a.dsT[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
+    }
+    for (int ch = a.nch - 1; ch >= 0; --ch) {
+        const int t0 = ch * kC, n = min(kC, a.T - t0);
+        __syncthreads();
+        float* dck = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+        for (int i = tid; i < DK * kSl; i += 256) {
+            const int c = i / kSl, j = i - c * kSl;
+            dck[static_cast<size_t>(c) * a.DV + j0 + j] = dS[i];
+        }
+        const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, Q0, eE, Bs);
+        for (int i = tid; i < kC * kC; i += 256) {
+            Ps[(i >> 6) * kTP + (i & 63)] = im[iP + i];
+            Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
+        }
+        for (int i = tid; i < kC * kSl; i += 256) {
+            const int t = i / kSl, j = i - t * kSl;
+            const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
+            Xs[i] = t < n ? a.ws[W.xr + r * a.DV + j0 + j] : 0.f;
+            Os[i] = t < n ? ld(dO + r * a.DV + j0 + j) : 0.f;
+        }
+        __syncthreads();
+        // U = Tinv diag(beta) Xr;  dU = scale P^T dO + Kt dS_end
+        for (int i = tid; i < kC * kSl; i += 256) {
+            const int t = i / kSl, j = i - t * kSl;
+            float u = 0.f;
+            for (int s = 0; s <= t; ++s) u += Ti[t * kTP + s] * Bs[s] * Xs[s * kSl + j];
+            Us[i] = u;
+            float du = 0.f;
+            for (int r = t; r < kC; ++r) du += Ps[r * kTP + t] * Os[r * kSl + j];
+            du *= a.scale;
+            for (int c = 0; c < DK; ++c) du += Kt[t * KP + c] * dS[c * kSl + j];
+            dU[i] = du;
+        }
+        __syncthreads();
+        // dX = Tinv^T dU (kept in registers until every thread has read dU)
+        float dxr[kC * kSl / 256];
+#pragma unroll
+        for (int m = 0; m < kC * kSl / 256; ++m) {
+            const int i = tid + 256 * m;
+            const int t = i / kSl, j = i - t * kSl;
+            float acc = 0.f;
+            for (int r = t; r < kC; ++r) acc += Ti[r * kTP + t] * dU[r * kSl + j];
+            dxr[m] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < kC * kSl / 256; ++m) dU[tid + 256 * m] = dxr[m];
+        __syncthreads();
+        float* dX = dU;
+        for (int i = tid; i < kC * kSl; i += 256) {
+            const int t = i / kSl, j = i - t * kSl;
+            if (t < n) {
+                const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
+                Elem<InT>::store(dv + r * a.DV + j0 + j, Bs[t] * dX[i]);
+                a.ws[W.u + r * a.DV + j0 + j] = Us[i];
+                a.ws[W.dx + r * a.DV + j0 + j] = dX[i];
+            }
+        }
+        if (tid < kC) {  // this slice's part of sum_j Xr dX
+            float acc = 0.f;
+            for (int j = 0; j < kSl; ++j) acc += Xs[tid * kSl + j] * dX[tid * kSl + j];
+            if (tid < n) {
+                const size_t tok = (static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h;
+                a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok] = acc;
+            }
+        }
+        // dS <- eE dS + scale Q0^T dO - K0^T diag(beta) dX
+        for (int i = tid; i < DK * kSl; i += 256) {
+            const int c = i / kSl, j = i - c * kSl;
+            float acc = 0.f;
+            for (int t = 0; t < kC; ++t)
+                acc += a.scale * Q0[t * KP + c] * Os[t * kSl + j] - K0[t * KP + c] * Bs[t] * dX[t * kSl + j];
+            dS[i] = eE[c] * dS[i] + acc;
+        }
+    }
+    __syncthreads();
+    if (a.ds0) {
+        for (int i = tid; i < DK * kSl; i += 256) {
+            const int c = i / kSl, j = i - c * kSl;
+            a.ds0[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] = dS[i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bwd_local
+// Thread tiles: rows t0 .. t0+3 (t0 = 4 (tid % 16)) of the [64 x DK]
+// gradients, columns c0 .. c0+CW-1 (CW = DK/16, c0 = CW (tid / 16)); of the
+// [64 x 64] ones, rows t0 .. t0+3 and columns s0 .. s0+3 (s0 = 4 (tid / 16)).
+template <int DK, bool KDA, typename InT>
+__global__ __launch_bounds__(256) void bwd_local(Args a) {
+    constexpr int KP = DK + 1;
+    constexpr int GW = KDA ? DK : 1;
+    constexpr int GP = GW + 1;
+    constexpr int CW = DK / 16;
+    constexpr int CB = 16;             // value columns per block
+    constexpr int SP = CB + 1;
+    extern __shared__ float sm[];
+    float* Ks = sm;                    // [64][KP]  raw k; later dG
+    float* Qs = Ks + kC * KP;          // [64][KP]  raw q
+    float* Gs = Qs + kC * KP;          // [64][GP]
+    float* Ah = Gs + kC * GP;          // [64][kTP] Ahat
+    float* X = Ah + kC * kTP;          // union: column blocks / M, N
+    float* Sb = X;                     // [DK][SP]  S
+    float* Db = Sb + DK * SP;          // [DK][SP]  dS_end
+    float* Ub = Db + DK * SP;          // [64][SP]  U
+    float* Xb = Ub + kC * SP;          // [64][SP]  dX
+    float* Ob = Xb + kC * SP;          // [64][SP]  dO
+    float* Mm = X;                     // [64][kTP] M = beta dA
+    float* Nm = Mm + kC * kTP;         // [64][kTP] N = dP
+    constexpr int UNION = (2 * DK * SP + 3 * kC * SP) > 2 * kC * kTP ? (2 * DK * SP + 3 * kC * SP) : 2 * kC * kTP;
+    float* Bs = X + UNION;             // [64] beta
+    float* dB = Bs + kC;               // [64] dbeta
+    float* eE = dB + kC;               // [DK]
+    float* dGe = eE + DK;              // [DK] dG_end
+    float* dGt = dGe + DK;             // [64] GDN: dG per token
+
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int t0c = ch * kC, n = min(kC, a.T - t0c);
+    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    const InT* q = static_cast<const InT*>(a.q);
+    const InT* k = static_cast<const InT*>(a.k);
+    const InT* dO = static_cast<const InT*>(a.dO);
+    auto tok = [&](int t) { return (static_cast<size_t>(b) * a.T + t0c + t) * a.H + h; };
+
+    for (int i = tid; i < kC * DK; i += 256) {
+        const int t = i / DK, c = i - t * DK;
+        Ks[t * KP + c] = t < n ? ld(k + tok(t) * DK + c) : 0.f;
+        Qs[t * KP + c] = t < n ? ld(q + tok(t) * DK + c) : 0.f;
+    }
+    for (int i = tid; i < kC * GW; i += 256) {
+        const int t = i / GW, c = i - t * GW;
+        Gs[t * GP + c] = t < n ? log_gate(KDA ? a.alpha[tok(t) * DK + c] : a.alpha[tok(t)]) : 0.f;
+    }
+    if (tid < kC) {
+        Bs[tid] = tid < n ? a.beta[tok(tid)] : 0.f;
+        dB[tid] = 0.f;
+        dGt[tid] = 0.f;
+    }
+    if (tid < DK) dGe[tid] = 0.f;
+    const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+    for (int i = tid; i < kC * kC; i += 256) Ah[(i >> 6) * kTP + (i & 63)] = im[iA + i];
+    __syncthreads();
+    if (tid < GW) {  // cumulative log-gate in place
+        float acc = 0.f;
+        for (int t = 0; t < kC; ++t) {
+            acc += Gs[t * GP + tid];
+            Gs[t * GP + tid] = acc;
+        }
+        eE[tid] = __expf(acc);  // acc = G_end
+    }
+
+    const int t0 = 4 * (tid & 15);
+    const int c0 = CW * (tid >> 4);
+    const int s0 = 4 * (tid >> 4);
+    float aQ[4][CW], aK[4][CW], aT[4][CW], aA[4][4], aP[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+#pragma unroll
+        for (int y = 0; y < CW; ++y) aQ[x][y] = aK[x][y] = aT[x][y] = 0.f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) aA[x][y] = aP[x][y] = 0.f;
+    }
+    float ge = 0.f;  // tid < DK: sum_j dS_end S of channel tid
+    const float* Sg = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    const float* Dg = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    for (int jb = 0; jb < a.DV; jb += CB) {
+        __syncthreads();  // previous block consumed (first pass: staging above done)
+        for (int i = tid; i < DK * CB; i += 256) {
+            const int c = i / CB, j = i - c * CB;
+            Sb[c * SP + j] = Sg[static_cast<size_t>(c) * a.DV + jb + j];
+            Db[c * SP + j] = Dg[static_cast<size_t>(c) * a.DV + jb + j];
+        }
+        for (int i = tid; i < kC * CB; i += 256) {
+            const int t = i / CB, j = i - t * CB;
+            const bool ok = t < n;
+            const size_t r = tok(t) * a.DV + jb + j;
+            Ub[t * SP + j] = ok ? a.ws[W.u + r] : 0.f;
+            Xb[t * SP + j] = ok ? a.ws[W.dx + r] : 0.f;
+            Ob[t * SP + j] = ok ? ld(dO + r) : 0.f;
+        }
+        __syncthreads();
+        for (int j = 0; j < CB; ++j) {
+            float o[4], x[4], u[4], us[4], sv[CW], dv[CW];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                o[m] = Ob[(t0 + m) * SP + j];
+                x[m] = Xb[(t0 + m) * SP + j];
+                u[m] = Ub[(t0 + m) * SP + j];
+                us[m] = Ub[(s0 + m) * SP + j];
+            }
+#pragma unroll
+            for (int y = 0; y < CW; ++y) {
+                sv[y] = Sb[(c0 + y) * SP + j];
+                dv[y] = Db[(c0 + y) * SP + j];
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int y = 0; y < CW; ++y) {
+                    aQ[m][y] += o[m] * sv[y];
+                    aK[m][y] += x[m] * sv[y];
+                    aT[m][y] += u[m] * dv[y];
+                }
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    aA[m][y] += x[m] * us[y];
+                    aP[m][y] += o[m] * us[y];
+                }
+            }
+        }
+        if (tid < DK) {
+            for (int j = 0; j < CB; ++j) ge += Db[tid * SP + j] * Sb[tid * SP + j];
+        }
+    }
+    __syncthreads();  // the column blocks are consumed: M, N take their place
+    // dA = -dX U^T (s < t), M = beta dA;  dP = scale dO U^T (s <= t);
+    // dbeta_t += sum_s dA_ts Ahat_ts
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int t = t0 + m;
+        float db = 0.f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const int s = s0 + y;
+            const float dA = s < t ? -aA[m][y] : 0.f;
+            db += dA * Ah[t * kTP + s];
+            Mm[t * kTP + s] = Bs[t] * dA;
+            Nm[t * kTP + s] = s <= t ? a.scale * aP[m][y] : 0.f;
+        }
+        atomicAdd(&dB[t], db);
+    }
+    if (tid < DK) {
+        if (KDA) dGe[tid] = eE[tid] * ge;
+        else atomicAdd(&dGe[0], eE[0] * ge);
+    }
+    __syncthreads();
+    // the four gate-weighted sums and the gradients of the thread's tile
+    float dq[4][CW], dk[4][CW], dg[4][CW];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int t = t0 + m;
+#pragma unroll
+        for (int y = 0; y < CW; ++y) {
+            const int c = c0 + y;
+            const float gt = Gs[t * GP + (KDA ? c : 0)];
+            float a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
+            for (int s = 0; s < kC; ++s) {
+                const float gs = Gs[s * GP + (KDA ? c : 0)];
+                if (s <= t) {
+                    const float e = __expf(gt - gs);
+                    const float kse = Ks[s * KP + c] * e;
+                    a1 += Mm[t * kTP + s] * kse;  // M is zero on and above the diagonal
+                    a2 += Nm[t * kTP + s] * kse;
+                }
+                if (s >= t) {
+                    const float e = __expf(gs - gt);
+                    a3 += Mm[s * kTP + t] * Ks[s * KP + c] * e;
+                    a4 += Nm[s * kTP + t] * Qs[s * KP + c] * e;
+                }
+            }
+            const float e0 = __expf(gt);
+            const float ek = __expf(Gs[(kC - 1) * GP + (KDA ? c : 0)] - gt);  // exp(G_end - G_t) <= 1
+            const float kv = Ks[t * KP + c], qv = Qs[t * KP + c];
+            const float dQ0 = a.scale * aQ[m][y], dK0 = -Bs[t] * aK[m][y], dKt = aT[m][y];
+            dq[m][y] = dQ0 * e0 + a2;
+            dk[m][y] = dK0 * e0 + dKt * ek + a1 + a3 + a4;
+            dg[m][y] = qv * (dQ0 * e0 + a2) + kv * (dK0 * e0 - dKt * ek + a1 - a3 - a4);
+            // G_end = G_{n-1}: its gradient through Kt (and, below, eE)
+            const float ge_t = dKt * kv * ek;
+            if (KDA) atomicAdd(&dGe[c], ge_t);
+            else atomicAdd(&dGe[0], ge_t);
+        }
+    }
+    __syncthreads();  // k, q no longer read: dG goes where k was
+    float* dG = Ks;
+    if constexpr (KDA) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int y = 0; y < CW; ++y) dG[(t0 + m) * KP + c0 + y] = dg[m][y];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float s = 0.f;
+#pragma unroll
+            for (int y = 0; y < CW; ++y) s += dg[m][y];
+            atomicAdd(&dGt[t0 + m], s);
+        }
+    }
+    InT* dqo = static_cast<InT*>(a.dq);
+    InT* dko = static_cast<InT*>(a.dk);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int t = t0 + m;
+        if (t < n) {
+#pragma unroll
+            for (int y = 0; y < CW; ++y) {
+                Elem<InT>::store(dqo + tok(t) * DK + c0 + y, dq[m][y]);
+                Elem<InT>::store(dko + tok(t) * DK + c0 + y, dk[m][y]);
+            }
+        }
+    }
+    __syncthreads();
+    // dlog alpha_s = sum_{t >= s} dG_t inside the chunk (G_end's gradient on
+    // the last token); dalpha = dlog alpha / alpha unless the floor is active.
+    float* dL = KDA ? dG : dGt;  // dlog alpha, in place
+    constexpr int LP = KDA ? KP : 1;
+    if (tid < GW) {
+        const int c = tid;
+        float acc = dGe[c];
+        for (int t = n - 1; t >= 0; --t) {
+            acc += dL[t * LP + c];
+            dL[t * LP + c] = acc;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < n * GW; i += 256) {
+        const int t = i / GW, c = i - t * GW;
+        const size_t r = KDA ? tok(t) * DK + c : tok(t);
+        const float al = a.alpha[r];
+        a.dalpha[r] = __logf(al) > kFloor ? dL[t * LP + c] / al : 0.f;
+    }
+    if (tid < n) {
+        float db = dB[tid];
+        const int nsl = a.DV / kSl;
+        for (int sl = 0; sl < nsl; ++sl) db += a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok(tid)];
+        a.dbeta[tok(tid)] = db;
+    }
+}
+
+template <int DK, bool KDA>
+constexpr int prep_lds() { return 4 * (2 * kC * (DK + 1) + kC * ((KDA ? DK : 1) + 1) + 2 * kC * kTP + kC); }
+template <int DK>
+constexpr int fwd_lds() { return 4 * (2 * kC * (DK + 1) + kC * kTP + DK * kSl + 2 * kC * kSl + DK + kC); }
+template <int DK>
+constexpr int chain_lds() { return 4 * (3 * kC * (DK + 1) + 2 * kC * kTP + DK * kSl + 4 * kC * kSl + DK + kC); }
+template <int DK, bool KDA>
+constexpr int local_lds() {
+    constexpr int SP = 17;
+    constexpr int un = (2 * DK * SP + 3 * kC * SP) > 2 * kC * kTP ? (2 * DK * SP + 3 * kC * SP) : 2 * kC * kTP;
+    return 4 * (2 * kC * (DK + 1) + kC * ((KDA ? DK : 1) + 1) + kC * kTP + un + 3 * kC + 2 * DK);
+}
+
+template <int DK, bool KDA, typename InT>
+hipError_t run(const Args& a, hipStream_t s) {
+    static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK>() <= 160 * 1024 &&
+                  prep_lds<DK, KDA>() <= 160 * 1024, "LDS budget");
+    auto set = [](const void* f, int bytes) {
+        return bytes > 64 * 1024 ? hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
+                                 : hipSuccess;
+    };
+    hipError_t e;
+    const unsigned per_chunk = static_cast<unsigned>(a.B * a.H * a.nch);
+    const unsigned per_slice = static_cast<unsigned>(a.B * a.H * (a.DV / kSl));
+    if ((e = set(reinterpret_cast<const void*>(bwd_prep<DK, KDA, InT>), prep_lds<DK, KDA>())) != hipSuccess) return e;
+    if ((e = set(reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT>), fwd_lds<DK>())) != hipSuccess) return e;
+    if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT>), chain_lds<DK>())) != hipSuccess) return e;
+    if ((e = set(reinterpret_cast<const void*>(bwd_local<DK, KDA, InT>), local_lds<DK, KDA>())) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(256), (prep_lds<DK, KDA>()), s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT>), dim3(per_slice), dim3(256), fwd_lds<DK>(), s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_chain<DK, KDA, InT>), dim3(per_slice), dim3(256), chain_lds<DK>(), s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_local<DK, KDA, InT>), dim3(per_chunk), dim3(256), (local_lds<DK, KDA>()), s, a);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t run_dk(int kda, int dtype, const Args& a, hipStream_t s) {
+    if (dtype == GDR_DTYPE_BF16)
+        return kda ? run<DK, true, bf16_t>(a, s) : run<DK, false, bf16_t>(a, s);
+    return kda ? run<DK, true, float>(a, s) : run<DK, false, float>(a, s);
+}
+
+}  // namespace
+
+size_t backward_workspace_floats(int B, int T, int H, int dk, int dv) {
+    return Ws(B, T, H, dk, dv).total;
+}
+
+hipError_t launch_backward(int kda, int dtype, int B, int T, int H, int dk, int dv, float scale,
+                           const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* state_in, const void* d_o,
+                           const float* d_state_out, void* dq, void* dkk, void* dvv, float* dalpha,
+                           float* dbeta, float* d_state_in, float* ws, hipStream_t s) {
+    Args a;
+    a.B = B; a.T = T; a.H = H; a.DV = dv; a.nch = (T + kC - 1) / kC;
+    a.scale = scale;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.s0 = state_in;
+    a.dO = d_o; a.dsT = d_state_out;
+    a.dq = dq; a.dk = dkk; a.dv = dvv; a.dalpha = dalpha; a.dbeta = dbeta; a.ds0 = d_state_in;
+    a.ws = ws;
+    switch (dk) {
+        case 16: return run_dk<16>(kda, dtype, a, s);
+        case 32: return run_dk<32>(kda, dtype, a, s);
+        case 64: return run_dk<64>(kda, dtype, a, s);
+        default: return run_dk<128>(kda, dtype, a, s);
+    }
+}
+
+}  // namespace gdr

@@ -258,4 +258,54 @@ int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T,
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
+size_t gdr_chunk_backward_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
+                                          int dv, int chunk) {
+    if (check_enums(gate, dtype) != GDR_OK || chunk != 64 || B < 0 || H < 0 || T < 0 ||
+        !head_dim_ok(dk) || !head_dim_ok(dv) || !sizes_ok(B, T, H, dk, dv))
+        return 0;
+    if (B == 0 || H == 0 || T == 0) return 0;
+    return gdr::backward_workspace_floats(B, T, H, dk, dv) * sizeof(float);
+}
+
+int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                       float scale, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, const float* state_in,
+                       const void* grad_o, const float* grad_state_out, void* grad_q,
+                       void* grad_k, void* grad_v, float* grad_alpha, float* grad_beta,
+                       float* grad_state_in, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    int st = check_enums(gate, dtype);
+    if (st != GDR_OK) return st;
+    if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
+    if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
+    const size_t need = gdr_chunk_backward_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
+    if (B == 0 || H == 0) return GDR_OK;
+    const int kda = gate == GDR_GATE_KDA;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !grad_o || !grad_q || !grad_k || !grad_v ||
+                  !grad_alpha || !grad_beta))
+        return GDR_ERR_NULL_PTR;
+    if ((state_in && !aligned(state_in, 16)) || (grad_state_out && !aligned(grad_state_out, 16)) ||
+        (grad_state_in && !aligned(grad_state_in, 16)) || (workspace && !aligned(workspace, 16)))
+        return GDR_ERR_MISALIGNED;
+    if (T > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(grad_o, 16) ||
+                  !aligned(grad_q, 16) || !aligned(grad_k, 16) || !aligned(grad_v, 16) ||
+                  !aligned(beta, 4) || !aligned(grad_beta, 4) || !aligned(alpha, kda ? 16 : 4) ||
+                  !aligned(grad_alpha, kda ? 16 : 4)))
+        return GDR_ERR_MISALIGNED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (T == 0) {
+        e = grad_state_in ? gdr::launch_state_copy(grad_state_out, grad_state_in,
+                                                    static_cast<size_t>(B) * H * dk * dv, s)
+                          : hipSuccess;
+    } else {
+        e = gdr::launch_backward(kda, dtype, B, T, H, dk, dv, scale, q, k, v, alpha, beta, state_in,
+                                 grad_o, grad_state_out, grad_q, grad_k, grad_v, grad_alpha,
+                                 grad_beta, grad_state_in, static_cast<float*>(workspace), s);
+    }
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
 }  // extern "C"

@@ -90,6 +90,15 @@ hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, flo
 bool prefill_bf16_split(int kda);
 size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk);
 
+// Backward of the chunked recurrence (fp32 arithmetic; q, k, v, d_o, dq, dk,
+// dv in the element type `dtype`).  ws: backward_workspace_floats(...) floats.
+size_t backward_workspace_floats(int B, int T, int H, int dk, int dv);
+hipError_t launch_backward(int kda, int dtype, int B, int T, int H, int dk, int dv, float scale,
+                           const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* state_in, const void* d_o,
+                           const float* d_state_out, void* dq, void* dkk, void* dvv, float* dalpha,
+                           float* dbeta, float* d_state_in, float* ws, hipStream_t s);
+
 // state_out <- state_in (or zeros when state_in is NULL), n floats.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);
 

@@ -229,6 +229,42 @@ int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T,
 size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int max_T, int H,
                                                 int dk, int dv, int chunk);
 
+/*
+ * Backward pass of the chunked prefill (the training step of the mixers; the
+ * pages' §2.B trains the supernet's mixers in its distillation stages):
+ * gradients of L = sum(grad_o * o) + sum(grad_state_out * S_T) with respect
+ * to every input of gdr_chunk_prefill, same shapes and layouts.
+ *
+ *   inputs     q, k, v, alpha, beta, state_in (NULL = zeros): as given to
+ *              the forward (alpha, beta in linear space)
+ *   grad_o     [B, T, H, dv]    dtype
+ *   grad_state_out [B, H, dk, dv] fp32, or NULL (S_T unused by the loss)
+ *   grad_q, grad_k [B, T, H, dk] dtype;  grad_v [B, T, H, dv] dtype
+ *   grad_alpha [B, T, H] (GDN) or [B, T, H, dk] (KDA) fp32
+ *   grad_beta  [B, T, H] fp32
+ *   grad_state_in [B, H, dk, dv] fp32, or NULL (not wanted)
+ *   workspace  device scratch of at least gdr_chunk_backward_workspace_bytes
+ *
+ * Every product runs in fp32 (bf16 inputs are widened, bf16 gradients rounded
+ * to nearest even).  The gate enters through log(alpha), floored at -40 per
+ * token as in the fp32 forward: where the floor is active, grad_alpha is 0.
+ * T == 0 copies grad_state_out (or zeros) to grad_state_in.  Outputs may not
+ * overlap inputs.  Returns a GDR_* status.
+ */
+int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                       float scale,
+                       const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, const float* state_in,
+                       const void* grad_o, const float* grad_state_out,
+                       void* grad_q, void* grad_k, void* grad_v,
+                       float* grad_alpha, float* grad_beta, float* grad_state_in,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gdr_chunk_backward needs (0 when the arguments are
+ * invalid). */
+size_t gdr_chunk_backward_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
+                                          int dv, int chunk);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* gdr_status_string(int status);
 

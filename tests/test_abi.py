@@ -266,3 +266,32 @@ def test_prologue_flag_validation(lib, monkeypatch):
         assert pre(1, 0, 3) == NULL        # fp32 path: both
     monkeypatch.delenv("GDR_PREFILL_PATH")
     assert pre(0, 1, 3) == NULL and pre(1, 1, 3) == WS
+
+
+def test_backward_validation(lib):
+    """Validation of gdr_chunk_backward before any device work."""
+    nul = [None] * 14
+
+    def bwd(gate=0, dtype=1, B=2, T=70, H=3, dk=128, dv=128, chunk=64, ptrs=None, ws=None, ws_bytes=0):
+        p = nul if ptrs is None else ptrs
+        return lib.gdr_chunk_backward(gate, dtype, B, T, H, dk, dv, chunk, 1.0, *p, ws, ws_bytes, None)
+
+    assert bwd(gate=3) == ENUM
+    assert bwd(dtype=7) == ENUM
+    assert bwd(B=-1) == SHAPE
+    assert bwd(dk=48) == UNSUP
+    assert bwd(chunk=32) == UNSUP
+    need = lib.gdr_chunk_backward_workspace_bytes(0, 1, 2, 70, 3, 128, 128, 64)
+    assert need > 0
+    assert lib.gdr_chunk_backward_workspace_bytes(0, 1, 2, 0, 3, 128, 128, 64) == 0
+    assert bwd() == WS                                        # workspace missing
+    ws = ctypes.c_void_p(0x40000000)
+    assert bwd(ws=ws, ws_bytes=need) == NULL                  # inputs missing
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(14)]
+    p[5] = None                                               # state_in may be NULL
+    p[7] = None                                               # grad_state_out may be NULL
+    p[13] = None                                              # grad_state_in may be NULL
+    bad = list(p)
+    bad[8] = ctypes.c_void_p(0x10008)                         # grad_q misaligned
+    assert bwd(ptrs=bad, ws=ws, ws_bytes=need) == MISAL
+    assert bwd(B=0, ptrs=nul) == OK                           # empty batch: no-op

@@ -1,0 +1,105 @@
+"""GPU parity of the chunked backward pass (gdr_chunk_backward).
+
+Reference: the float64 token-recurrence backward of the oracle (itself pinned
+by central finite differences), on the same seeded inputs, output gradient
+and final-state gradient.  Each gradient is compared element by element,
+relative to its own largest magnitude.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_08_amd as gdr
+import oracle
+import synth
+from gpu_util import TOL, announce, assert_close, ensure_built, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+def _case(gate, dtype, B, T, H, dk, dv, seed, s0=True, dst=True):
+    base = synth.WORKLOADS["gdn_prefill_b4_t8192_h32_d128" if gate == "gdn" else "kda_prefill_b1_t32768_h32_d128"]
+    w = replace(base, dtype=dtype, dk=dk, dv=dv)
+    inp = synth.make_inputs(w, B=B, T=T, H=H, seed=seed, s0="normal" if s0 else "zero")
+    rng = np.random.default_rng(seed + 100)
+    do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    if dtype == "bf16":
+        do = synth.bf16_round(do)
+    dst_arr = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32) if dst else None
+    return inp, do, dst_arr
+
+
+def _run(gate, dtype, inp, do, dst, scale, want_ds0=True):
+    d = {key: to_dev(val, dtype if key in ("q", "k", "v") else "f32") for key, val in inp.items()}
+    g_o = to_dev(do, dtype)
+    g_st = None if dst is None else to_dev(dst, "f32")
+    out = {"dq": torch.full_like(d["q"], 7.0), "dk": torch.full_like(d["k"], 7.0),
+           "dv": torch.full_like(d["v"], 7.0), "dalpha": torch.full_like(d["alpha"], 7.0),
+           "dbeta": torch.full_like(d["beta"], 7.0)}
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[-1]
+    out["ds0"] = torch.full((B, H, dk, dv), 7.0, device="cuda") if want_ds0 else None
+    gdr.gdr_chunk_backward(gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["s0"], g_o, g_st,
+                           out["dq"], out["dk"], out["dv"], out["dalpha"], out["dbeta"], out["ds0"],
+                           scale=scale)
+    torch.cuda.synchronize()
+    return {key: (None if val is None else to_host64(val)) for key, val in out.items()}
+
+
+def _check(gate, dtype, B, T, H, dk, dv, seed=1, s0=True, dst=True, scale=0.8):
+    inp, do, dst_arr = _case(gate, dtype, B, T, H, dk, dv, seed, s0, dst)
+    got = _run(gate, dtype, inp, do, dst_arr, scale)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["s0"], do,
+                          dst_arr, scale=scale)
+    tol = TOL[dtype]
+    for key in ("dq", "dk", "dv", "dalpha", "dbeta", "ds0"):
+        assert_close(got[key], ref[key], tol, key)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_matches_oracle_ragged(gate, dtype):
+    """Three chunks with a ragged tail, from a given state, with dS_T."""
+    announce("backward %s %s B=2 T=150 H=2 d=64" % (gate, dtype))
+    _check(gate, dtype, B=2, T=150, H=2, dk=64, dv=64)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (16, 32), (32, 16), (128, 64)])
+def test_backward_head_sizes(gate, dk, dv):
+    announce("backward %s f32 dk=%d dv=%d" % (gate, dk, dv))
+    _check(gate, "f32", B=1, T=130, H=2, dk=dk, dv=dv, seed=4)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_backward_without_states(gate):
+    """No initial state, no final-state gradient, one partial chunk."""
+    announce("backward %s no states T=37" % gate)
+    _check(gate, "f32", B=2, T=37, H=3, dk=32, dv=32, seed=6, s0=False, dst=False)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_backward_exact_chunks_bf16_d128(gate):
+    announce("backward %s bf16 T=256 d=128" % gate)
+    _check(gate, "bf16", B=1, T=256, H=2, dk=128, dv=128, seed=8)
+
+
+def test_backward_t0_copies_the_state_gradient():
+    B, H, dk, dv = 2, 3, 32, 32
+    dst = torch.randn(B, H, dk, dv, device="cuda")
+    e = torch.empty(B, 0, H, dk, device="cuda")
+    ev = torch.empty(B, 0, H, dv, device="cuda")
+    ea = torch.empty(B, 0, H, device="cuda")
+    ds0 = torch.full((B, H, dk, dv), 7.0, device="cuda")
+    announce("backward T=0")
+    gdr.gdr_chunk_backward("gdn", e, e, ev, ea, ea, None, ev, dst, e.clone(), e.clone(), ev.clone(),
+                           ea.clone(), ea.clone(), ds0)
+    torch.cuda.synchronize()
+    assert torch.equal(ds0, dst)
