@@ -376,6 +376,67 @@ def bench_gdn_varlen(torch, gdr, synth, steps, warmup, N=32, slots=64):
             "roofline": roofline_hbm(per_launch, launch_ms, None)}
 
 
+def backward_flops(B, T, H, dk, dv):
+    """Flops of the chunked backward as computed (per 64-token chunk and
+    head; a fused multiply-add counts 2): the chunk-local prep (Ahat, P over
+    the lower triangle, the triangular inverse), the forward checkpoint chain
+    (Xr, U, S), the reverse chain (U, dU, dX, dS) and the chunk-local
+    contractions (dQ0, dK0, dKt, dA, dP and the four gate-weighted sums)."""
+    C, tri = CHUNK, CHUNK * (CHUNK + 1) // 2
+    per = (2 * tri * dk * 2 + C ** 3 // 3 * 2                          # prep
+           + (C * dk * dv + tri * dv + dk * C * dv) * 2                # forward chain
+           + (tri * dv + tri * dv + C * dk * dv + tri * dv + 2 * C * dk * dv) * 2  # reverse chain
+           + (3 * C * dk * dv + 2 * C * C * dv + 4 * tri * dk) * 2)    # local
+    nch = (T + CHUNK - 1) // CHUNK
+    return B * H * nch * per
+
+
+def backward_bytes(gate, B, T, H, dk, dv, elt=2):
+    """Algorithmic HBM bytes: read q, k, v, dO and the gates, write dq, dk, dv
+    and the gate gradients; read S_0 and dS_T, write dS_0."""
+    g = 4 * dk if gate == "kda" else 4
+    per_tok = elt * (2 * dk + 2 * dv) + g + 4 + elt * (2 * dk + dv) + g + 4
+    return B * T * H * per_tok + 3 * B * H * 4 * dk * dv
+
+
+def bench_backward(torch, gdr, synth, name, steps, warmup):
+    """One gdr_chunk_backward per step on the prefill workload's shape (bf16
+    inputs and output gradient, fp32 state and state gradient)."""
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    d = {k: torch.from_numpy(v).to(torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()
+         for k, v in inp.items() if v is not None}
+    del inp
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6000)
+    do = torch.randn(B, T, H, dv, device="cuda", generator=g).to(torch.bfloat16)
+    dst = torch.randn(B, H, dk, dv, device="cuda", generator=g) * 0.1
+    s0 = d.get("s0")
+    out = [torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
+           torch.empty_like(d["alpha"]), torch.empty_like(d["beta"]),
+           torch.empty(B, H, dk, dv, device="cuda")]
+    need = gdr.gdr_chunk_backward_workspace_bytes(w.gate, torch.bfloat16, B, T, H, dk, dv)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    call = lambda: gdr.gdr_chunk_backward(w.gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], s0, do,
+                                          dst, *out, workspace=ws)
+    for _ in range(warmup):
+        call()
+    elapsed, gpu_s = timed_region(torch, steps, call)
+    launch_ms = 1e3 * gpu_s / steps
+    flops = backward_flops(B, T, H, dk, dv)
+    nbytes = backward_bytes(w.gate, B, T, H, dk, dv)
+    sec = launch_ms / 1e3
+    return {"workload": name.replace("prefill", "backward"), "steps": steps,
+            "ms_per_step": 1e3 * elapsed / steps, "launch_ms": launch_ms,
+            "tokens_per_s": B * T * steps / elapsed, "workspace_bytes": need,
+            "roofline": {"bound": "alu", "achieved": round(flops / sec / 1e12, 2), "peak": FP32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(flops / sec / 1e12 / FP32_PEAK_TFLOPS, 4),
+                         "traffic": None, "algorithmic_flops": flops},
+            "hbm": {"achieved": round(nbytes / sec / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
+
+
 def bench_prefill(torch, gdr, synth, name, steps, warmup, flags=0):
     """One chunked prefill per step; with ``flags`` the inputs are raw (q, k
     not normalised, gate logits) and the kernels run the input prologue."""
@@ -428,7 +489,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None,
-                    help="gdn_decode | kda_decode | gdn_verify | gdn_prefill | gdn_varlen | kda_prefill | prologue | copy")
+                    help="gdn_decode | kda_decode | gdn_verify | gdn_prefill | gdn_varlen | kda_prefill | backward | prologue | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -473,6 +534,10 @@ def main():
     if only in (None, "kda_prefill"):
         extra["kda_prefill_b1_t32768_h32_d128"] = bench_prefill(
             torch, gdr, synth, "kda_prefill_b1_t32768_h32_d128", max(5, args.steps // 2), 2)
+    if only in (None, "backward"):
+        for name in ("gdn_prefill_b4_t8192_h32_d128", "kda_prefill_b1_t32768_h32_d128"):
+            r = bench_backward(torch, gdr, synth, name, max(3, args.steps // 4), 1)
+            extra[r["workload"]] = r
     if only in (None, "prologue"):  # the same paths with the fused input prologue
         for gate in ("gdn", "kda"):
             r = bench_decode_prologue(torch, gdr, synth, args.steps, args.warmup, gate)
