@@ -47,6 +47,9 @@ constexpr int kC = 64;
 constexpr int kSl = 16;  // value columns per slice
 constexpr float kFloor = -40.0f;
 constexpr int kTP = kC + 1;  // pitch of 64 x 64 tiles in LDS
+constexpr int kNT = 1024;    // threads per workgroup: the LDS use allows one
+                             // workgroup per CU, so four waves per SIMD come
+                             // from one workgroup (latency hiding)
 
 template <typename T> __device__ __forceinline__ float ld(const T* p);
 template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
@@ -102,7 +105,7 @@ struct Args {
 // log-gates, one thread per channel sums them in LDS), Ahat and P, the
 // factored rows K0, Kt, Q0 and eE, and Tinv by forward substitution.
 template <int DK, bool KDA, typename InT>
-__global__ __launch_bounds__(256) void bwd_prep(Args a) {
+__global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
     constexpr int KP = DK + 1;
     constexpr int GW = KDA ? DK : 1;
     constexpr int GP = GW + 1;
@@ -120,12 +123,12 @@ __global__ __launch_bounds__(256) void bwd_prep(Args a) {
     const InT* q = static_cast<const InT*>(a.q);
     const InT* k = static_cast<const InT*>(a.k);
     auto tok = [&](int t) { return (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h; };
-    for (int i = tid; i < kC * DK; i += 256) {
+    for (int i = tid; i < kC * DK; i += kNT) {
         const int t = i / DK, c = i - t * DK;
         Ks[t * KP + c] = t < n ? ld(k + tok(t) * DK + c) : 0.f;
         Qs[t * KP + c] = t < n ? ld(q + tok(t) * DK + c) : 0.f;
     }
-    for (int i = tid; i < kC * GW; i += 256) {
+    for (int i = tid; i < kC * GW; i += kNT) {
         const int t = i / GW, c = i - t * GW;
         Gs[t * GP + c] = t < n ? log_gate(KDA ? a.alpha[tok(t) * DK + c] : a.alpha[tok(t)]) : 0.f;
     }
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(256) void bwd_prep(Args a) {
     }
     __syncthreads();
     float* img = a.ws + Ws(a.B, a.T, a.H, DK, a.DV).img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-    for (int i = tid; i < kC * kC; i += 256) {
+    for (int i = tid; i < kC * kC; i += kNT) {
         const int t = i >> 6, s = i & 63;
         float sa = 0.f, sp = 0.f;
         if (s <= t) {
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void bwd_prep(Args a) {
         img[iP + i] = sp;
         As[t * kTP + s] = Bs[t] * sa;
     }
-    for (int i = tid; i < kC * DK; i += 256) {
+    for (int i = tid; i < kC * DK; i += kNT) {
         const int t = i / DK, c = i - t * DK;
         const float g = Gs[t * GP + (KDA ? c : 0)], ge = Gs[(kC - 1) * GP + (KDA ? c : 0)];
         const float e0 = __expf(g);
@@ -165,19 +168,27 @@ __global__ __launch_bounds__(256) void bwd_prep(Args a) {
         img[iK0 + 2 * kC * DK + i] = Qs[t * KP + c] * e0;
         if (t == 0) img[iK0 + 3 * kC * DK + c] = __expf(ge);
     }
+    for (int i = tid; i < kC * kC; i += kNT) Tl[(i >> 6) * kTP + (i & 63)] = (i >> 6) == (i & 63) ? 1.f : 0.f;
     __syncthreads();
-    // Tinv = (I + A)^{-1}, unit lower triangular: column s by forward
-    // substitution, one thread per column (each reads only its own column).
+    // Tinv = (I + A)^{-1}, unit lower triangular, row by row: row t is
+    // -sum_{r<t} A_tr Tinv_r (Tinv_r zero right of its diagonal, so every
+    // lane s runs the same r range and A_tr is a broadcast read).  One wave.
+    // Each lane reads and writes only its own column.
     if (tid < kC) {
         const int s = tid;
-        for (int t = 0; t < kC; ++t) {
-            float v = t == s ? 1.f : 0.f;
-            for (int r = s; r < t; ++r) v -= As[t * kTP + r] * Tl[r * kTP + s];
-            Tl[t * kTP + s] = v;
+        for (int t = 1; t < kC; ++t) {
+            float v0 = 0.f, v1 = 0.f;
+            int r = 0;
+            for (; r + 1 < t; r += 2) {
+                v0 -= As[t * kTP + r] * Tl[r * kTP + s];
+                v1 -= As[t * kTP + r + 1] * Tl[(r + 1) * kTP + s];
+            }
+            if (r < t) v0 -= As[t * kTP + r] * Tl[r * kTP + s];
+            if (s < t) Tl[t * kTP + s] = v0 + v1;
         }
     }
     __syncthreads();
-    for (int i = tid; i < kC * kC; i += 256) img[iT + i] = Tl[(i >> 6) * kTP + (i & 63)];
+    for (int i = tid; i < kC * kC; i += kNT) img[iT + i] = Tl[(i >> 6) * kTP + (i & 63)];
 }
 
 // The factored rows, eE and beta of one chunk from its image (all threads,
@@ -187,7 +198,7 @@ __device__ __forceinline__ void load_factors(const Args& a, const float* im, int
                                              float* K0, float* Kt, float* Q0, float* eE, float* Bs) {
     constexpr int KP = DK + 1;
     const int tid = threadIdx.x;
-    for (int i = tid; i < kC * DK; i += 256) {
+    for (int i = tid; i < kC * DK; i += kNT) {
         const int t = i / DK, c = i - t * DK;
         K0[t * KP + c] = im[iK0 + i];
         Kt[t * KP + c] = im[iK0 + kC * DK + i];
@@ -199,7 +210,7 @@ __device__ __forceinline__ void load_factors(const Args& a, const float* im, int
 
 // ---------------------------------------------------------------- bwd_fwd
 template <int DK, bool KDA, typename InT>
-__global__ __launch_bounds__(256) void bwd_fwd(Args a) {
+__global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
     constexpr int KP = DK + 1;
     extern __shared__ float sm[];
     float* K0 = sm;                  // [64][KP]
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(256) void bwd_fwd(Args a) {
     const int j0 = sl * kSl;
     const Ws W(a.B, a.T, a.H, DK, a.DV);
     const InT* v = static_cast<const InT*>(a.v);
-    for (int i = tid; i < DK * kSl; i += 256) {
+    for (int i = tid; i < DK * kSl; i += kNT) {
         const int c = i / kSl, j = i - c * kSl;
         Ss[i] = a.s0 ? a.s0[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
     }
@@ -225,16 +236,16 @@ __global__ __launch_bounds__(256) void bwd_fwd(Args a) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();  // the previous chunk is done with every buffer
         float* ck = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
-        for (int i = tid; i < DK * kSl; i += 256) {
+        for (int i = tid; i < DK * kSl; i += kNT) {
             const int c = i / kSl, j = i - c * kSl;
             ck[static_cast<size_t>(c) * a.DV + j0 + j] = Ss[i];
         }
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
         load_factors<DK>(a, im, b, h, t0, n, K0, Kt, nullptr, eE, Bs);
-        for (int i = tid; i < kC * kC; i += 256) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
+        for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
         __syncthreads();
         // Xr = V - K0 S
-        for (int i = tid; i < kC * kSl; i += 256) {
+        for (int i = tid; i < kC * kSl; i += kNT) {
             const int t = i / kSl, j = i - t * kSl;
             float acc = 0.f;
             for (int c = 0; c < DK; ++c) acc += K0[t * KP + c] * Ss[c * kSl + j];
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(256) void bwd_fwd(Args a) {
         }
         __syncthreads();
         // U = Tinv diag(beta) Xr
-        for (int i = tid; i < kC * kSl; i += 256) {
+        for (int i = tid; i < kC * kSl; i += kNT) {
             const int t = i / kSl, j = i - t * kSl;
             float acc = 0.f;
             for (int s = 0; s <= t; ++s) acc += Ti[t * kTP + s] * Bs[s] * Xs[s * kSl + j];
@@ -253,7 +264,7 @@ __global__ __launch_bounds__(256) void bwd_fwd(Args a) {
         }
         __syncthreads();
         // S <- eE S + Kt^T U
-        for (int i = tid; i < DK * kSl; i += 256) {
+        for (int i = tid; i < DK * kSl; i += kNT) {
             const int c = i / kSl, j = i - c * kSl;
             float acc = eE[c] * Ss[i];
             for (int t = 0; t < kC; ++t) acc += Kt[t * KP + c] * Us[t * kSl + j];
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(256) void bwd_fwd(Args a) {
 
 // ---------------------------------------------------------------- bwd_chain
 template <int DK, bool KDA, typename InT>
-__global__ __launch_bounds__(256) void bwd_chain(Args a) {
+__global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
     constexpr int KP = DK + 1;
     extern __shared__ float sm[];
     float* K0 = sm;                  // [64][KP]
@@ -287,7 +298,7 @@ __global__ __launch_bounds__(256) void bwd_chain(Args a) {
     const Ws W(a.B, a.T, a.H, DK, a.DV);
     const InT* dO = static_cast<const InT*>(a.dO);
     InT* dv = static_cast<InT*>(a.dv);
-    for (int i = tid; i < DK * kSl; i += 256) {
+    for (int i = tid; i < DK * kSl; i += kNT) {
         const int c = i / kSl, j = i - c * kSl;
         dS[i] = a.dsT ? a.dsT[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
     }
@@ -295,17 +306,17 @@ __global__ __launch_bounds__(256) void bwd_chain(Args a) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();
         float* dck = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
-        for (int i = tid; i < DK * kSl; i += 256) {
+        for (int i = tid; i < DK * kSl; i += kNT) {
             const int c = i / kSl, j = i - c * kSl;
             dck[static_cast<size_t>(c) * a.DV + j0 + j] = dS[i];
         }
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
         load_factors<DK>(a, im, b, h, t0, n, K0, Kt, Q0, eE, Bs);
-        for (int i = tid; i < kC * kC; i += 256) {
+        for (int i = tid; i < kC * kC; i += kNT) {
             Ps[(i >> 6) * kTP + (i & 63)] = im[iP + i];
             Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
         }
-        for (int i = tid; i < kC * kSl; i += 256) {
+        for (int i = tid; i < kC * kSl; i += kNT) {
             const int t = i / kSl, j = i - t * kSl;
             const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
             Xs[i] = t < n ? a.ws[W.xr + r * a.DV + j0 + j] : 0.f;
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(256) void bwd_chain(Args a) {
         }
         __syncthreads();
         // U = Tinv diag(beta) Xr;  dU = scale P^T dO + Kt dS_end
-        for (int i = tid; i < kC * kSl; i += 256) {
+        for (int i = tid; i < kC * kSl; i += kNT) {
             const int t = i / kSl, j = i - t * kSl;
             float u = 0.f;
             for (int s = 0; s <= t; ++s) u += Ti[t * kTP + s] * Bs[s] * Xs[s * kSl + j];
@@ -326,10 +337,12 @@ __global__ __launch_bounds__(256) void bwd_chain(Args a) {
         }
         __syncthreads();
         // dX = Tinv^T dU (kept in registers until every thread has read dU)
-        float dxr[kC * kSl / 256];
+        constexpr int ND = (kC * kSl + kNT - 1) / kNT;
+        float dxr[ND];
 #pragma unroll
-        for (int m = 0; m < kC * kSl / 256; ++m) {
-            const int i = tid + 256 * m;
+        for (int m = 0; m < ND; ++m) {
+            const int i = tid + kNT * m;
+            if (i >= kC * kSl) break;
             const int t = i / kSl, j = i - t * kSl;
             float acc = 0.f;
             for (int r = t; r < kC; ++r) acc += Ti[r * kTP + t] * dU[r * kSl + j];
@@ -337,10 +350,11 @@ __global__ __launch_bounds__(256) void bwd_chain(Args a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int m = 0; m < kC * kSl / 256; ++m) dU[tid + 256 * m] = dxr[m];
+        for (int m = 0; m < ND; ++m)
+            if (tid + kNT * m < kC * kSl) dU[tid + kNT * m] = dxr[m];
         __syncthreads();
         float* dX = dU;
-        for (int i = tid; i < kC * kSl; i += 256) {
+        for (int i = tid; i < kC * kSl; i += kNT) {
             const int t = i / kSl, j = i - t * kSl;
             if (t < n) {
                 const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
@@ -358,7 +372,7 @@ __global__ __launch_bounds__(256) void bwd_chain(Args a) {
             }
         }
         // dS <- eE dS + scale Q0^T dO - K0^T diag(beta) dX
-        for (int i = tid; i < DK * kSl; i += 256) {
+        for (int i = tid; i < DK * kSl; i += kNT) {
             const int c = i / kSl, j = i - c * kSl;
             float acc = 0.f;
             for (int t = 0; t < kC; ++t)
@@ -368,7 +382,7 @@ __global__ __launch_bounds__(256) void bwd_chain(Args a) {
     }
     __syncthreads();
     if (a.ds0) {
-        for (int i = tid; i < DK * kSl; i += 256) {
+        for (int i = tid; i < DK * kSl; i += kNT) {
             const int c = i / kSl, j = i - c * kSl;
             a.ds0[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] = dS[i];
         }
@@ -376,15 +390,20 @@ __global__ __launch_bounds__(256) void bwd_chain(Args a) {
 }
 
 // ---------------------------------------------------------------- bwd_local
-// Thread tiles: rows t0 .. t0+3 (t0 = 4 (tid % 16)) of the [64 x DK]
-// gradients, columns c0 .. c0+CW-1 (CW = DK/16, c0 = CW (tid / 16)); of the
-// [64 x 64] ones, rows t0 .. t0+3 and columns s0 .. s0+3 (s0 = 4 (tid / 16)).
+// Thread tiles: of the [64 x DK] gradients, RT rows from t0 = RT (tid % NRG)
+// and CW columns from c0 = CW (tid / NRG) (NRG = 64 / RT row groups); of the
+// [64 x 64] ones, rows tb .. tb+1 and columns s0 .. s0+1 (tb = 2 (tid % 32),
+// s0 = 2 (tid / 32)).
 template <int DK, bool KDA, typename InT>
-__global__ __launch_bounds__(256) void bwd_local(Args a) {
+__global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     constexpr int KP = DK + 1;
     constexpr int GW = KDA ? DK : 1;
     constexpr int GP = GW + 1;
-    constexpr int CW = DK / 16;
+    constexpr int PER = kC * DK / kNT;              // [64 x DK] elements per thread
+    constexpr int RT = PER >= 4 ? 4 : PER;          // rows of the tile
+    constexpr int CW = PER / RT;                    // columns of the tile
+    constexpr int NRG = kC / RT;
+    static_assert(RT * CW * kNT == kC * DK && (kNT / NRG) * CW == DK, "tile mapping");
     constexpr int CB = 16;             // value columns per block
     constexpr int SP = CB + 1;
     extern __shared__ float sm[];
@@ -417,12 +436,12 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
     const InT* dO = static_cast<const InT*>(a.dO);
     auto tok = [&](int t) { return (static_cast<size_t>(b) * a.T + t0c + t) * a.H + h; };
 
-    for (int i = tid; i < kC * DK; i += 256) {
+    for (int i = tid; i < kC * DK; i += kNT) {
         const int t = i / DK, c = i - t * DK;
         Ks[t * KP + c] = t < n ? ld(k + tok(t) * DK + c) : 0.f;
         Qs[t * KP + c] = t < n ? ld(q + tok(t) * DK + c) : 0.f;
     }
-    for (int i = tid; i < kC * GW; i += 256) {
+    for (int i = tid; i < kC * GW; i += kNT) {
         const int t = i / GW, c = i - t * GW;
         Gs[t * GP + c] = t < n ? log_gate(KDA ? a.alpha[tok(t) * DK + c] : a.alpha[tok(t)]) : 0.f;
     }
@@ -433,7 +452,7 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
     }
     if (tid < DK) dGe[tid] = 0.f;
     const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-    for (int i = tid; i < kC * kC; i += 256) Ah[(i >> 6) * kTP + (i & 63)] = im[iA + i];
+    for (int i = tid; i < kC * kC; i += kNT) Ah[(i >> 6) * kTP + (i & 63)] = im[iA + i];
     __syncthreads();
     if (tid < GW) {  // cumulative log-gate in place
         float acc = 0.f;
@@ -444,28 +463,30 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
         eE[tid] = __expf(acc);  // acc = G_end
     }
 
-    const int t0 = 4 * (tid & 15);
-    const int c0 = CW * (tid >> 4);
-    const int s0 = 4 * (tid >> 4);
-    float aQ[4][CW], aK[4][CW], aT[4][CW], aA[4][4], aP[4][4];
+    const int t0 = RT * (tid % NRG);
+    const int c0 = CW * (tid / NRG);
+    const int tb = 2 * (tid & 31);
+    const int s0 = 2 * (tid >> 5);
+    float aQ[RT][CW], aK[RT][CW], aT[RT][CW], aA[2][2], aP[2][2];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < RT; ++x)
 #pragma unroll
         for (int y = 0; y < CW; ++y) aQ[x][y] = aK[x][y] = aT[x][y] = 0.f;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) aA[x][y] = aP[x][y] = 0.f;
-    }
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) aA[x][y] = aP[x][y] = 0.f;
     float ge = 0.f;  // tid < DK: sum_j dS_end S of channel tid
     const float* Sg = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
     const float* Dg = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
     for (int jb = 0; jb < a.DV; jb += CB) {
         __syncthreads();  // previous block consumed (first pass: staging above done)
-        for (int i = tid; i < DK * CB; i += 256) {
+        for (int i = tid; i < DK * CB; i += kNT) {
             const int c = i / CB, j = i - c * CB;
             Sb[c * SP + j] = Sg[static_cast<size_t>(c) * a.DV + jb + j];
             Db[c * SP + j] = Dg[static_cast<size_t>(c) * a.DV + jb + j];
         }
-        for (int i = tid; i < kC * CB; i += 256) {
+        for (int i = tid; i < kC * CB; i += kNT) {
             const int t = i / CB, j = i - t * CB;
             const bool ok = t < n;
             const size_t r = tok(t) * a.DV + jb + j;
@@ -475,12 +496,17 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
         }
         __syncthreads();
         for (int j = 0; j < CB; ++j) {
-            float o[4], x[4], u[4], us[4], sv[CW], dv[CW];
+            float o[RT], x[RT], u[RT], sv[CW], dv[CW], ob[2], xb[2], us[2];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < RT; ++m) {
                 o[m] = Ob[(t0 + m) * SP + j];
                 x[m] = Xb[(t0 + m) * SP + j];
                 u[m] = Ub[(t0 + m) * SP + j];
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                ob[m] = Ob[(tb + m) * SP + j];
+                xb[m] = Xb[(tb + m) * SP + j];
                 us[m] = Ub[(s0 + m) * SP + j];
             }
 #pragma unroll
@@ -489,19 +515,21 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
                 dv[y] = Db[(c0 + y) * SP + j];
             }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < RT; ++m) {
 #pragma unroll
                 for (int y = 0; y < CW; ++y) {
                     aQ[m][y] += o[m] * sv[y];
                     aK[m][y] += x[m] * sv[y];
                     aT[m][y] += u[m] * dv[y];
                 }
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    aA[m][y] += x[m] * us[y];
-                    aP[m][y] += o[m] * us[y];
-                }
             }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    aA[m][y] += xb[m] * us[y];
+                    aP[m][y] += ob[m] * us[y];
+                }
         }
         if (tid < DK) {
             for (int j = 0; j < CB; ++j) ge += Db[tid * SP + j] * Sb[tid * SP + j];
@@ -511,11 +539,11 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
     // dA = -dX U^T (s < t), M = beta dA;  dP = scale dO U^T (s <= t);
     // dbeta_t += sum_s dA_ts Ahat_ts
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int t = t0 + m;
+    for (int m = 0; m < 2; ++m) {
+        const int t = tb + m;
         float db = 0.f;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
+        for (int y = 0; y < 2; ++y) {
             const int s = s0 + y;
             const float dA = s < t ? -aA[m][y] : 0.f;
             db += dA * Ah[t * kTP + s];
@@ -530,9 +558,9 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
     }
     __syncthreads();
     // the four gate-weighted sums and the gradients of the thread's tile
-    float dq[4][CW], dk[4][CW], dg[4][CW];
+    float dq[RT][CW], dk[RT][CW], dg[RT][CW];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < RT; ++m) {
         const int t = t0 + m;
 #pragma unroll
         for (int y = 0; y < CW; ++y) {
@@ -570,12 +598,12 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
     float* dG = Ks;
     if constexpr (KDA) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < RT; ++m)
 #pragma unroll
             for (int y = 0; y < CW; ++y) dG[(t0 + m) * KP + c0 + y] = dg[m][y];
     } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < RT; ++m) {
             float s = 0.f;
 #pragma unroll
             for (int y = 0; y < CW; ++y) s += dg[m][y];
@@ -585,7 +613,7 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
     InT* dqo = static_cast<InT*>(a.dq);
     InT* dko = static_cast<InT*>(a.dk);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < RT; ++m) {
         const int t = t0 + m;
         if (t < n) {
 #pragma unroll
@@ -609,7 +637,7 @@ __global__ __launch_bounds__(256) void bwd_local(Args a) {
         }
     }
     __syncthreads();
-    for (int i = tid; i < n * GW; i += 256) {
+    for (int i = tid; i < n * GW; i += kNT) {
         const int t = i / GW, c = i - t * GW;
         const size_t r = KDA ? tok(t) * DK + c : tok(t);
         const float al = a.alpha[r];
@@ -651,13 +679,13 @@ hipError_t run(const Args& a, hipStream_t s) {
     if ((e = set(reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT>), fwd_lds<DK>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT>), chain_lds<DK>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_local<DK, KDA, InT>), local_lds<DK, KDA>())) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(256), (prep_lds<DK, KDA>()), s, a);
+    hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (prep_lds<DK, KDA>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT>), dim3(per_slice), dim3(256), fwd_lds<DK>(), s, a);
+    hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT>), dim3(per_slice), dim3(kNT), fwd_lds<DK>(), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chain<DK, KDA, InT>), dim3(per_slice), dim3(256), chain_lds<DK>(), s, a);
+    hipLaunchKernelGGL((bwd_chain<DK, KDA, InT>), dim3(per_slice), dim3(kNT), chain_lds<DK>(), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_local<DK, KDA, InT>), dim3(per_chunk), dim3(256), (local_lds<DK, KDA>()), s, a);
+    hipLaunchKernelGGL((bwd_local<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (local_lds<DK, KDA>()), s, a);
     return hipGetLastError();
 }
 
