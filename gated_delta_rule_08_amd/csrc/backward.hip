@@ -100,6 +100,16 @@ struct Args {
     float* ws;
 };
 
+// Workgroup -> (head, value slice) of the two chains.  Consecutive workgroups
+// go to the eight XCDs in turn, so the slices of one head are placed eight
+// workgroups apart: they share an XCD and its L2, where they all read the
+// head's chunk images.  The grid is padded to a multiple of eight heads.
+__device__ __forceinline__ void slice_of(const Args& a, int nsl, int& bh, int& sl) {
+    const int x = blockIdx.x, xcd = x & 7, k = x >> 3;
+    sl = k % nsl;
+    bh = (k / nsl) * 8 + xcd;
+}
+
 // ---------------------------------------------------------------- bwd_prep
 // Chunk-local quantities of one chunk: its gates (all threads stage the
 // log-gates, one thread per channel sums them in LDS), Ahat and P, the
@@ -223,7 +233,9 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
     float* Bs = eE + DK;             // [64]
     const int tid = threadIdx.x;
     const int nsl = a.DV / kSl;
-    const int bh = blockIdx.x / nsl, sl = blockIdx.x - (blockIdx.x / nsl) * nsl;
+    int bh, sl;
+    slice_of(a, nsl, bh, sl);
+    if (bh >= a.B * a.H) return;  // padding of the grid (whole block, before any barrier)
     const int b = bh / a.H, h = bh - b * a.H;
     const int j0 = sl * kSl;
     const Ws W(a.B, a.T, a.H, DK, a.DV);
@@ -244,31 +256,55 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
         load_factors<DK>(a, im, b, h, t0, n, K0, Kt, nullptr, eE, Bs);
         for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
         __syncthreads();
-        // Xr = V - K0 S
-        for (int i = tid; i < kC * kSl; i += kNT) {
-            const int t = i / kSl, j = i - t * kSl;
-            float acc = 0.f;
-            for (int c = 0; c < DK; ++c) acc += K0[t * KP + c] * Ss[c * kSl + j];
-            const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
-            const float x = t < n ? ld(v + r * a.DV + j0 + j) - acc : 0.f;
-            Xs[i] = x;
-            if (t < n) a.ws[W.xr + r * a.DV + j0 + j] = x;
+        // Xr = V - K0 S  (2 x 2 tiles of (t, j))
+        if (tid < kC * kSl / 4) {
+            const int t = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
+            float x00 = 0.f, x01 = 0.f, x10 = 0.f, x11 = 0.f;
+#pragma unroll 4
+            for (int c = 0; c < DK; ++c) {
+                const float k0 = K0[t * KP + c], k1 = K0[(t + 1) * KP + c];
+                const float s0 = Ss[c * kSl + j], s1 = Ss[c * kSl + j + 1];
+                x00 += k0 * s0; x01 += k0 * s1; x10 += k1 * s0; x11 += k1 * s1;
+            }
+            const float acc[2][2] = {{x00, x01}, {x10, x11}};
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    const size_t r = (static_cast<size_t>(b) * a.T + t0 + t + m) * a.H + h;
+                    const bool ok = t + m < n;
+                    const float x = ok ? ld(v + r * a.DV + j0 + j + y) - acc[m][y] : 0.f;
+                    Xs[(t + m) * kSl + j + y] = x;
+                    if (ok) a.ws[W.xr + r * a.DV + j0 + j + y] = x;
+                }
         }
         __syncthreads();
-        // U = Tinv diag(beta) Xr
-        for (int i = tid; i < kC * kSl; i += kNT) {
-            const int t = i / kSl, j = i - t * kSl;
-            float acc = 0.f;
-            for (int s = 0; s <= t; ++s) acc += Ti[t * kTP + s] * Bs[s] * Xs[s * kSl + j];
-            Us[i] = acc;
+        // U = Tinv diag(beta) Xr  (Tinv is zero above its diagonal)
+        if (tid < kC * kSl / 4) {
+            const int t = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
+            float u00 = 0.f, u01 = 0.f, u10 = 0.f, u11 = 0.f;
+            for (int q = 0; q <= t + 1; ++q) {
+                const float b0 = Bs[q] * Xs[q * kSl + j], b1 = Bs[q] * Xs[q * kSl + j + 1];
+                const float i0 = Ti[t * kTP + q], i1 = Ti[(t + 1) * kTP + q];
+                u00 += i0 * b0; u01 += i0 * b1; u10 += i1 * b0; u11 += i1 * b1;
+            }
+            Us[t * kSl + j] = u00; Us[t * kSl + j + 1] = u01;
+            Us[(t + 1) * kSl + j] = u10; Us[(t + 1) * kSl + j + 1] = u11;
         }
         __syncthreads();
-        // S <- eE S + Kt^T U
-        for (int i = tid; i < DK * kSl; i += kNT) {
-            const int c = i / kSl, j = i - c * kSl;
-            float acc = eE[c] * Ss[i];
-            for (int t = 0; t < kC; ++t) acc += Kt[t * KP + c] * Us[t * kSl + j];
-            Ss[i] = acc;
+        // S <- eE S + Kt^T U  (2 x 2 tiles of (c, j))
+        if (tid < DK * kSl / 4) {
+            const int c = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
+            float s00 = eE[c] * Ss[c * kSl + j], s01 = eE[c] * Ss[c * kSl + j + 1];
+            float s10 = eE[c + 1] * Ss[(c + 1) * kSl + j], s11 = eE[c + 1] * Ss[(c + 1) * kSl + j + 1];
+#pragma unroll 4
+            for (int t = 0; t < kC; ++t) {
+                const float k0 = Kt[t * KP + c], k1 = Kt[t * KP + c + 1];
+                const float u0 = Us[t * kSl + j], u1 = Us[t * kSl + j + 1];
+                s00 += k0 * u0; s01 += k0 * u1; s10 += k1 * u0; s11 += k1 * u1;
+            }
+            Ss[c * kSl + j] = s00; Ss[c * kSl + j + 1] = s01;
+            Ss[(c + 1) * kSl + j] = s10; Ss[(c + 1) * kSl + j + 1] = s11;
         }
     }
 }
@@ -292,7 +328,9 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
     float* Bs = eE + DK;             // [64]
     const int tid = threadIdx.x;
     const int nsl = a.DV / kSl;
-    const int bh = blockIdx.x / nsl, sl = blockIdx.x - (blockIdx.x / nsl) * nsl;
+    int bh, sl;
+    slice_of(a, nsl, bh, sl);
+    if (bh >= a.B * a.H) return;  // padding of the grid (whole block, before any barrier)
     const int b = bh / a.H, h = bh - b * a.H;
     const int j0 = sl * kSl;
     const Ws W(a.B, a.T, a.H, DK, a.DV);
@@ -323,35 +361,50 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
             Os[i] = t < n ? ld(dO + r * a.DV + j0 + j) : 0.f;
         }
         __syncthreads();
-        // U = Tinv diag(beta) Xr;  dU = scale P^T dO + Kt dS_end
-        for (int i = tid; i < kC * kSl; i += kNT) {
-            const int t = i / kSl, j = i - t * kSl;
-            float u = 0.f;
-            for (int s = 0; s <= t; ++s) u += Ti[t * kTP + s] * Bs[s] * Xs[s * kSl + j];
-            Us[i] = u;
-            float du = 0.f;
-            for (int r = t; r < kC; ++r) du += Ps[r * kTP + t] * Os[r * kSl + j];
-            du *= a.scale;
-            for (int c = 0; c < DK; ++c) du += Kt[t * KP + c] * dS[c * kSl + j];
-            dU[i] = du;
+        // U = Tinv diag(beta) Xr;  dU = scale P^T dO + Kt dS_end  (2 x 2 tiles;
+        // Tinv and P are zero above their diagonals)
+        if (tid < kC * kSl / 4) {
+            const int t = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
+            float u00 = 0.f, u01 = 0.f, u10 = 0.f, u11 = 0.f;
+            for (int q = 0; q <= t + 1; ++q) {
+                const float b0 = Bs[q] * Xs[q * kSl + j], b1 = Bs[q] * Xs[q * kSl + j + 1];
+                const float i0 = Ti[t * kTP + q], i1 = Ti[(t + 1) * kTP + q];
+                u00 += i0 * b0; u01 += i0 * b1; u10 += i1 * b0; u11 += i1 * b1;
+            }
+            Us[t * kSl + j] = u00; Us[t * kSl + j + 1] = u01;
+            Us[(t + 1) * kSl + j] = u10; Us[(t + 1) * kSl + j + 1] = u11;
+            float d00 = 0.f, d01 = 0.f, d10 = 0.f, d11 = 0.f;
+            for (int r = t; r < kC; ++r) {
+                const float p0 = Ps[r * kTP + t], p1 = Ps[r * kTP + t + 1];
+                const float o0 = Os[r * kSl + j], o1 = Os[r * kSl + j + 1];
+                d00 += p0 * o0; d01 += p0 * o1; d10 += p1 * o0; d11 += p1 * o1;
+            }
+            d00 *= a.scale; d01 *= a.scale; d10 *= a.scale; d11 *= a.scale;
+#pragma unroll 4
+            for (int c = 0; c < DK; ++c) {
+                const float k0 = Kt[t * KP + c], k1 = Kt[(t + 1) * KP + c];
+                const float s0 = dS[c * kSl + j], s1 = dS[c * kSl + j + 1];
+                d00 += k0 * s0; d01 += k0 * s1; d10 += k1 * s0; d11 += k1 * s1;
+            }
+            dU[t * kSl + j] = d00; dU[t * kSl + j + 1] = d01;
+            dU[(t + 1) * kSl + j] = d10; dU[(t + 1) * kSl + j + 1] = d11;
         }
         __syncthreads();
-        // dX = Tinv^T dU (kept in registers until every thread has read dU)
-        constexpr int ND = (kC * kSl + kNT - 1) / kNT;
-        float dxr[ND];
-#pragma unroll
-        for (int m = 0; m < ND; ++m) {
-            const int i = tid + kNT * m;
-            if (i >= kC * kSl) break;
-            const int t = i / kSl, j = i - t * kSl;
-            float acc = 0.f;
-            for (int r = t; r < kC; ++r) acc += Ti[r * kTP + t] * dU[r * kSl + j];
-            dxr[m] = acc;
+        // dX = Tinv^T dU, kept in registers until every tile has read dU
+        float x00 = 0.f, x01 = 0.f, x10 = 0.f, x11 = 0.f;
+        const int xt = 2 * (tid / (kSl / 2)), xj = 2 * (tid % (kSl / 2));
+        if (tid < kC * kSl / 4) {
+            for (int r = xt; r < kC; ++r) {
+                const float i0 = Ti[r * kTP + xt], i1 = Ti[r * kTP + xt + 1];
+                const float g0 = dU[r * kSl + xj], g1 = dU[r * kSl + xj + 1];
+                x00 += i0 * g0; x01 += i0 * g1; x10 += i1 * g0; x11 += i1 * g1;
+            }
         }
         __syncthreads();
-#pragma unroll
-        for (int m = 0; m < ND; ++m)
-            if (tid + kNT * m < kC * kSl) dU[tid + kNT * m] = dxr[m];
+        if (tid < kC * kSl / 4) {
+            dU[xt * kSl + xj] = x00; dU[xt * kSl + xj + 1] = x01;
+            dU[(xt + 1) * kSl + xj] = x10; dU[(xt + 1) * kSl + xj + 1] = x11;
+        }
         __syncthreads();
         float* dX = dU;
         for (int i = tid; i < kC * kSl; i += kNT) {
@@ -371,13 +424,26 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
                 a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok] = acc;
             }
         }
-        // dS <- eE dS + scale Q0^T dO - K0^T diag(beta) dX
-        for (int i = tid; i < DK * kSl; i += kNT) {
-            const int c = i / kSl, j = i - c * kSl;
-            float acc = 0.f;
-            for (int t = 0; t < kC; ++t)
-                acc += a.scale * Q0[t * KP + c] * Os[t * kSl + j] - K0[t * KP + c] * Bs[t] * dX[t * kSl + j];
-            dS[i] = eE[c] * dS[i] + acc;
+        // dS <- eE dS + scale Q0^T dO - K0^T diag(beta) dX  (2 x 2 tiles of (c, j))
+        if (tid < DK * kSl / 4) {
+            const int c = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
+            float q00 = 0.f, q01 = 0.f, q10 = 0.f, q11 = 0.f;
+            float k00 = 0.f, k01 = 0.f, k10 = 0.f, k11 = 0.f;
+#pragma unroll 4
+            for (int t = 0; t < kC; ++t) {
+                const float qa = Q0[t * KP + c], qb = Q0[t * KP + c + 1];
+                const float ka = K0[t * KP + c], kb = K0[t * KP + c + 1];
+                const float o0 = Os[t * kSl + j], o1 = Os[t * kSl + j + 1];
+                const float bt = Bs[t];
+                const float g0 = bt * dX[t * kSl + j], g1 = bt * dX[t * kSl + j + 1];
+                q00 += qa * o0; q01 += qa * o1; q10 += qb * o0; q11 += qb * o1;
+                k00 += ka * g0; k01 += ka * g1; k10 += kb * g0; k11 += kb * g1;
+            }
+            const float sc = a.scale;
+            dS[c * kSl + j] = eE[c] * dS[c * kSl + j] + sc * q00 - k00;
+            dS[c * kSl + j + 1] = eE[c] * dS[c * kSl + j + 1] + sc * q01 - k01;
+            dS[(c + 1) * kSl + j] = eE[c + 1] * dS[(c + 1) * kSl + j] + sc * q10 - k10;
+            dS[(c + 1) * kSl + j + 1] = eE[c + 1] * dS[(c + 1) * kSl + j + 1] + sc * q11 - k11;
         }
     }
     __syncthreads();
@@ -557,7 +623,54 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         else atomicAdd(&dGe[0], eE[0] * ge);
     }
     __syncthreads();
-    // the four gate-weighted sums and the gradients of the thread's tile
+    // the four gate-weighted sums of the thread's tile, s outermost so that
+    // each LDS value feeds the whole tile.  G decreases along the chunk, so
+    // G_t - G_s <= 0 exactly where M_ts, N_ts can be nonzero (s <= t) and
+    // G_s - G_t <= 0 where M_st, N_st can (s >= t); clamping the exponents
+    // at 0 leaves the other products at 0 * 1.
+    float a1[RT][CW], a2[RT][CW], a3[RT][CW], a4[RT][CW], gt[RT][CW];
+#pragma unroll
+    for (int m = 0; m < RT; ++m)
+#pragma unroll
+        for (int y = 0; y < CW; ++y) {
+            a1[m][y] = a2[m][y] = a3[m][y] = a4[m][y] = 0.f;
+            gt[m][y] = Gs[(t0 + m) * GP + (KDA ? c0 + y : 0)];
+        }
+#pragma unroll 2
+    for (int s = 0; s < kC; ++s) {
+        float mts[RT], nts[RT], mst[RT], nst[RT], ks[CW], qs[CW], gs[CW];
+#pragma unroll
+        for (int m = 0; m < RT; ++m) {
+            mts[m] = Mm[(t0 + m) * kTP + s];
+            nts[m] = Nm[(t0 + m) * kTP + s];
+            mst[m] = Mm[s * kTP + t0 + m];
+            nst[m] = Nm[s * kTP + t0 + m];
+        }
+#pragma unroll
+        for (int y = 0; y < CW; ++y) {
+            ks[y] = Ks[s * KP + c0 + y];
+            qs[y] = Qs[s * KP + c0 + y];
+            gs[y] = Gs[s * GP + (KDA ? c0 + y : 0)];
+        }
+#pragma unroll
+        for (int m = 0; m < RT; ++m) {
+            float e1g = 0.f, e2g = 0.f;
+            if constexpr (!KDA) {
+                e1g = __expf(fminf(gt[m][0] - gs[0], 0.f));
+                e2g = __expf(fminf(gs[0] - gt[m][0], 0.f));
+            }
+#pragma unroll
+            for (int y = 0; y < CW; ++y) {
+                const float e1 = KDA ? __expf(fminf(gt[m][y] - gs[y], 0.f)) : e1g;
+                const float e2 = KDA ? __expf(fminf(gs[y] - gt[m][y], 0.f)) : e2g;
+                const float k1 = ks[y] * e1, k2 = ks[y] * e2;
+                a1[m][y] += mts[m] * k1;
+                a2[m][y] += nts[m] * k1;
+                a3[m][y] += mst[m] * k2;
+                a4[m][y] += nst[m] * qs[y] * e2;
+            }
+        }
+    }
     float dq[RT][CW], dk[RT][CW], dg[RT][CW];
 #pragma unroll
     for (int m = 0; m < RT; ++m) {
@@ -565,30 +678,14 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
 #pragma unroll
         for (int y = 0; y < CW; ++y) {
             const int c = c0 + y;
-            const float gt = Gs[t * GP + (KDA ? c : 0)];
-            float a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
-            for (int s = 0; s < kC; ++s) {
-                const float gs = Gs[s * GP + (KDA ? c : 0)];
-                if (s <= t) {
-                    const float e = __expf(gt - gs);
-                    const float kse = Ks[s * KP + c] * e;
-                    a1 += Mm[t * kTP + s] * kse;  // M is zero on and above the diagonal
-                    a2 += Nm[t * kTP + s] * kse;
-                }
-                if (s >= t) {
-                    const float e = __expf(gs - gt);
-                    a3 += Mm[s * kTP + t] * Ks[s * KP + c] * e;
-                    a4 += Nm[s * kTP + t] * Qs[s * KP + c] * e;
-                }
-            }
-            const float e0 = __expf(gt);
-            const float ek = __expf(Gs[(kC - 1) * GP + (KDA ? c : 0)] - gt);  // exp(G_end - G_t) <= 1
+            const float e0 = __expf(gt[m][y]);
+            const float ek = __expf(Gs[(kC - 1) * GP + (KDA ? c : 0)] - gt[m][y]);  // exp(G_end - G_t) <= 1
             const float kv = Ks[t * KP + c], qv = Qs[t * KP + c];
             const float dQ0 = a.scale * aQ[m][y], dK0 = -Bs[t] * aK[m][y], dKt = aT[m][y];
-            dq[m][y] = dQ0 * e0 + a2;
-            dk[m][y] = dK0 * e0 + dKt * ek + a1 + a3 + a4;
-            dg[m][y] = qv * (dQ0 * e0 + a2) + kv * (dK0 * e0 - dKt * ek + a1 - a3 - a4);
-            // G_end = G_{n-1}: its gradient through Kt (and, below, eE)
+            dq[m][y] = dQ0 * e0 + a2[m][y];
+            dk[m][y] = dK0 * e0 + dKt * ek + a1[m][y] + a3[m][y] + a4[m][y];
+            dg[m][y] = qv * (dQ0 * e0 + a2[m][y]) + kv * (dK0 * e0 - dKt * ek + a1[m][y] - a3[m][y] - a4[m][y]);
+            // G_end = G_{n-1}: its gradient through Kt (and, above, eE)
             const float ge_t = dKt * kv * ek;
             if (KDA) atomicAdd(&dGe[c], ge_t);
             else atomicAdd(&dGe[0], ge_t);
@@ -674,7 +771,7 @@ hipError_t run(const Args& a, hipStream_t s) {
     };
     hipError_t e;
     const unsigned per_chunk = static_cast<unsigned>(a.B * a.H * a.nch);
-    const unsigned per_slice = static_cast<unsigned>(a.B * a.H * (a.DV / kSl));
+    const unsigned per_slice = static_cast<unsigned>((a.B * a.H + 7) / 8 * 8 * (a.DV / kSl));
     if ((e = set(reinterpret_cast<const void*>(bwd_prep<DK, KDA, InT>), prep_lds<DK, KDA>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT>), fwd_lds<DK>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT>), chain_lds<DK>())) != hipSuccess) return e;
