@@ -217,25 +217,26 @@ def backward(q, k, v, alpha, beta, s0, do, ds_t=None, scale: float = 1.0):
     dv = v.shape[-1]
     kda = alpha.ndim == 4
     s = np.zeros((B, H, dk, dv)) if s0 is None else np.array(s0, dtype=np.float64)
-    # forward, keeping S_{t-1} and S'_t
-    prev, decayed, states = [], [], []
-    for t in range(T):
+
+    def step(t, s_prev):  # the forward step from S_{t-1}: (S'_t, e_t, S_t)
         a = alpha[:, t][..., None] if kda else alpha[:, t][..., None, None]   # [B,H,dk,1] or [B,H,1,1]
+        sp = a * s_prev
+        e = v[:, t] - np.einsum("bhij,bhi->bhj", sp, k[:, t])
+        return sp, e, sp + beta[:, t][..., None, None] * k[:, t][..., :, None] * e[..., None, :]
+
+    # forward, keeping S_{t-1} only (the rest of a step is recomputed from it)
+    prev = []
+    for t in range(T):
         prev.append(s)
-        sp = a * s
-        u = np.einsum("bhij,bhi->bhj", sp, k[:, t])
-        e = v[:, t] - u
-        s = sp + beta[:, t][..., None, None] * k[:, t][..., :, None] * e[..., None, :]
-        decayed.append((sp, e))
-        states.append(s)
+        s = step(t, s)[2]
     G = np.zeros((B, H, dk, dv)) if ds_t is None else np.array(ds_t, dtype=np.float64)
     dq, dkk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     da, db = np.zeros_like(alpha), np.zeros_like(beta)
     for t in reversed(range(T)):
-        sp, e = decayed[t]
+        sp, e, s_t = step(t, prev[t])
         bt = beta[:, t][..., None]                                  # [B,H,1]
         G = G + scale * q[:, t][..., :, None] * do[:, t][..., None, :]
-        dq[:, t] = scale * np.einsum("bhij,bhj->bhi", states[t], do[:, t])
+        dq[:, t] = scale * np.einsum("bhij,bhj->bhi", s_t, do[:, t])
         g = np.einsum("bhij,bhi->bhj", G, k[:, t])                  # G^T k
         dvv[:, t] = bt * g
         db[:, t] = np.sum(e * g, axis=-1)
