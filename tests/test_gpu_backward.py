@@ -103,3 +103,33 @@ def test_backward_t0_copies_the_state_gradient():
                            ea.clone(), ea.clone(), ds0)
     torch.cuda.synchronize()
     assert torch.equal(ds0, dst)
+
+
+def _full_size(gate, name, heads, seed=31):
+    """The backward at the prefill workload's full shape, in the launch
+    configuration the benchmark times; the oracle runs on sampled heads over
+    the whole length."""
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    rng = np.random.default_rng(seed)
+    do = synth.bf16_round(rng.standard_normal((B, T, H, dv)).astype(np.float32))
+    dst = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    announce("backward %s bf16 full size %s" % (gate, name))
+    got = _run(gate, "bf16", inp, do, dst, 1.0)
+    for (b, h) in heads:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+        s0 = None if inp["s0"] is None else np.ascontiguousarray(inp["s0"][b:b + 1, h:h + 1])
+        ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]), sl(inp["beta"]),
+                              s0, sl(do), np.ascontiguousarray(dst[b:b + 1, h:h + 1]))
+        for key in ("dq", "dk", "dv", "dalpha", "dbeta"):
+            assert_close(got[key][b:b + 1, :, h:h + 1], ref[key], TOL["bf16"], "%s[b=%d,h=%d]" % (key, b, h))
+        assert_close(got["ds0"][b:b + 1, h:h + 1], ref["ds0"], TOL["bf16"], "ds0[b=%d,h=%d]" % (b, h))
+
+
+def test_backward_gdn_full_size():
+    _full_size("gdn", "gdn_prefill_b4_t8192_h32_d128", [(0, 0), (3, 31)])
+
+
+def test_backward_kda_full_size():
+    _full_size("kda", "kda_prefill_b1_t32768_h32_d128", [(0, 7)])

@@ -110,7 +110,7 @@ def test_decode_flags_zero_is_the_plain_step_bitwise(gate):
 
 
 def _prefill(gate, dtype, d, flags, B, T, H, dv):
-    s_out = torch.empty_like(d["s0"])
+    s_out = torch.empty(B, H, d["q"].shape[-1], dv, device="cuda")
     o = torch.empty(B, T, H, dv, device="cuda", dtype=d["q"].dtype)
     gdr.gdr_chunk_prefill_ex(gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["s0"], s_out, o,
                              flags=flags, scale=0.75)
@@ -182,3 +182,24 @@ def test_prefill_flags_zero_is_the_plain_call_bitwise(gate):
     gdr.gdr_chunk_prefill_ex(gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["s0"], s2, o2, flags=0)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("gate,name,heads", [
+    ("gdn", "gdn_prefill_b4_t8192_h32_d128", [(0, 3), (3, 30)]),
+    ("kda", "kda_prefill_b1_t32768_h32_d128", [(0, 11)]),
+])
+def test_prefill_prologue_full_size(gate, name, heads):
+    """The prologue at the prefill workload's full shape (the benchmark's
+    launch configuration); the oracle on sampled heads over the whole length."""
+    w = synth.WORKLOADS[name]
+    raw = synth.make_raw_inputs(w)
+    B, T, H, dv = w.B, w.T, w.H, w.dv
+    announce("prefill prologue full size %s" % name)
+    o, s = _prefill(gate, "bf16", _dev(raw, "bf16"), NORM | SIG, B, T, H, dv)
+    for (b, h) in heads:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+        s0 = None if raw["s0"] is None else np.ascontiguousarray(raw["s0"][b:b + 1, h:h + 1])
+        q, k, a, bt = oracle.prologue(sl(raw["q"]), sl(raw["k"]), sl(raw["alpha"]), sl(raw["beta"]))
+        o_ref, s_ref = oracle.recurrent(q, k, sl(raw["v"]), a, bt, s0, scale=0.75)
+        assert_close(o[b:b + 1, :, h:h + 1], o_ref, TOL["bf16"], "o[b=%d,h=%d]" % (b, h))
+        assert_close(s[b:b + 1, h:h + 1], s_ref, TOL["bf16"], "S_T[b=%d,h=%d]" % (b, h))
