@@ -57,6 +57,29 @@ template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p) { retur
 
 __device__ __forceinline__ float log_gate(float a) { return fmaxf(__logf(a), kFloor); }
 
+// fp32 matrix-core tile product, v_mfma_f32_16x16x4f32: D[16x16] += A[16x4] B[4x16].
+// Lane l (li = l % 16, lk = l / 16) supplies A[li][lk] and B[lk][li] and holds
+// D[4 lk + r][li] in component r.  A 16-row tile of a product over K is K/4
+// such steps; two accumulators alternate so that consecutive steps do not
+// wait on each other.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+template <typename FA, typename FB>
+__device__ __forceinline__ f32x4 tile_product(int k0, int k1, FA fa, FB fb) {
+    const int lk = (threadIdx.x & 63) >> 4;
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    int k = k0;
+#pragma unroll 2
+    for (; k + 8 <= k1; k += 8) {
+        c0 = mma4(fa(k + lk), fb(k + lk), c0);
+        c1 = mma4(fa(k + 4 + lk), fb(k + 4 + lk), c1);
+    }
+    if (k < k1) c0 = mma4(fa(k + lk), fb(k + lk), c0);
+    return c0 + c1;
+}
+
 // Per-chunk image (floats): Ahat, P, Tinv [64][64] each, then K0 = k e0,
 // Kt = k ek, Q0 = q e0 [64][dk] each, then eE [dk].
 enum { iA = 0, iP = kC * kC, iT = 2 * kC * kC, iK0 = 3 * kC * kC };
@@ -256,55 +279,45 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
         load_factors<DK>(a, im, b, h, t0, n, K0, Kt, nullptr, eE, Bs);
         for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
         __syncthreads();
-        // Xr = V - K0 S  (2 x 2 tiles of (t, j))
-        if (tid < kC * kSl / 4) {
-            const int t = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
-            float x00 = 0.f, x01 = 0.f, x10 = 0.f, x11 = 0.f;
-#pragma unroll 4
-            for (int c = 0; c < DK; ++c) {
-                const float k0 = K0[t * KP + c], k1 = K0[(t + 1) * KP + c];
-                const float s0 = Ss[c * kSl + j], s1 = Ss[c * kSl + j + 1];
-                x00 += k0 * s0; x01 += k0 * s1; x10 += k1 * s0; x11 += k1 * s1;
+        // Matrix-core phases: wave w takes 16-row tile w of each product
+        // (rows t for Xr and U, rows c for S); li = lane % 16 is the value
+        // column of the slice.
+        const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+        // Xr = V - K0 S
+        if (wave < kC / 16) {
+            const int R = 16 * wave;
+            const f32x4 acc = tile_product(0, DK, [&](int k) { return K0[(R + li) * KP + k]; },
+                                           [&](int k) { return Ss[k * kSl + li]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = R + 4 * l4 + r;
+                const size_t row = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
+                const bool ok = t < n;
+                const float x = ok ? ld(v + row * a.DV + j0 + li) - acc[r] : 0.f;
+                Xs[t * kSl + li] = x;
+                if (ok) a.ws[W.xr + row * a.DV + j0 + li] = x;
             }
-            const float acc[2][2] = {{x00, x01}, {x10, x11}};
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    const size_t r = (static_cast<size_t>(b) * a.T + t0 + t + m) * a.H + h;
-                    const bool ok = t + m < n;
-                    const float x = ok ? ld(v + r * a.DV + j0 + j + y) - acc[m][y] : 0.f;
-                    Xs[(t + m) * kSl + j + y] = x;
-                    if (ok) a.ws[W.xr + r * a.DV + j0 + j + y] = x;
-                }
         }
         __syncthreads();
         // U = Tinv diag(beta) Xr  (Tinv is zero above its diagonal)
-        if (tid < kC * kSl / 4) {
-            const int t = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
-            float u00 = 0.f, u01 = 0.f, u10 = 0.f, u11 = 0.f;
-            for (int q = 0; q <= t + 1; ++q) {
-                const float b0 = Bs[q] * Xs[q * kSl + j], b1 = Bs[q] * Xs[q * kSl + j + 1];
-                const float i0 = Ti[t * kTP + q], i1 = Ti[(t + 1) * kTP + q];
-                u00 += i0 * b0; u01 += i0 * b1; u10 += i1 * b0; u11 += i1 * b1;
-            }
-            Us[t * kSl + j] = u00; Us[t * kSl + j + 1] = u01;
-            Us[(t + 1) * kSl + j] = u10; Us[(t + 1) * kSl + j + 1] = u11;
+        if (wave < kC / 16) {
+            const int R = 16 * wave;
+            const f32x4 acc = tile_product(0, R + 16, [&](int k) { return Ti[(R + li) * kTP + k]; },
+                                           [&](int k) { return Bs[k] * Xs[k * kSl + li]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Us[(R + 4 * l4 + r) * kSl + li] = acc[r];
         }
         __syncthreads();
-        // S <- eE S + Kt^T U  (2 x 2 tiles of (c, j))
-        if (tid < DK * kSl / 4) {
-            const int c = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
-            float s00 = eE[c] * Ss[c * kSl + j], s01 = eE[c] * Ss[c * kSl + j + 1];
-            float s10 = eE[c + 1] * Ss[(c + 1) * kSl + j], s11 = eE[c + 1] * Ss[(c + 1) * kSl + j + 1];
-#pragma unroll 4
-            for (int t = 0; t < kC; ++t) {
-                const float k0 = Kt[t * KP + c], k1 = Kt[t * KP + c + 1];
-                const float u0 = Us[t * kSl + j], u1 = Us[t * kSl + j + 1];
-                s00 += k0 * u0; s01 += k0 * u1; s10 += k1 * u0; s11 += k1 * u1;
+        // S <- eE S + Kt^T U
+        if (wave < DK / 16) {
+            const int R = 16 * wave;
+            const f32x4 acc = tile_product(0, kC, [&](int k) { return Kt[k * KP + R + li]; },
+                                           [&](int k) { return Us[k * kSl + li]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int c = R + 4 * l4 + r;
+                Ss[c * kSl + li] = eE[c] * Ss[c * kSl + li] + acc[r];
             }
-            Ss[c * kSl + j] = s00; Ss[c * kSl + j + 1] = s01;
-            Ss[(c + 1) * kSl + j] = s10; Ss[(c + 1) * kSl + j + 1] = s11;
         }
     }
 }
@@ -361,49 +374,38 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
             Os[i] = t < n ? ld(dO + r * a.DV + j0 + j) : 0.f;
         }
         __syncthreads();
-        // U = Tinv diag(beta) Xr;  dU = scale P^T dO + Kt dS_end  (2 x 2 tiles;
-        // Tinv and P are zero above their diagonals)
-        if (tid < kC * kSl / 4) {
-            const int t = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
-            float u00 = 0.f, u01 = 0.f, u10 = 0.f, u11 = 0.f;
-            for (int q = 0; q <= t + 1; ++q) {
-                const float b0 = Bs[q] * Xs[q * kSl + j], b1 = Bs[q] * Xs[q * kSl + j + 1];
-                const float i0 = Ti[t * kTP + q], i1 = Ti[(t + 1) * kTP + q];
-                u00 += i0 * b0; u01 += i0 * b1; u10 += i1 * b0; u11 += i1 * b1;
-            }
-            Us[t * kSl + j] = u00; Us[t * kSl + j + 1] = u01;
-            Us[(t + 1) * kSl + j] = u10; Us[(t + 1) * kSl + j + 1] = u11;
-            float d00 = 0.f, d01 = 0.f, d10 = 0.f, d11 = 0.f;
-            for (int r = t; r < kC; ++r) {
-                const float p0 = Ps[r * kTP + t], p1 = Ps[r * kTP + t + 1];
-                const float o0 = Os[r * kSl + j], o1 = Os[r * kSl + j + 1];
-                d00 += p0 * o0; d01 += p0 * o1; d10 += p1 * o0; d11 += p1 * o1;
-            }
-            d00 *= a.scale; d01 *= a.scale; d10 *= a.scale; d11 *= a.scale;
-#pragma unroll 4
-            for (int c = 0; c < DK; ++c) {
-                const float k0 = Kt[t * KP + c], k1 = Kt[(t + 1) * KP + c];
-                const float s0 = dS[c * kSl + j], s1 = dS[c * kSl + j + 1];
-                d00 += k0 * s0; d01 += k0 * s1; d10 += k1 * s0; d11 += k1 * s1;
-            }
-            dU[t * kSl + j] = d00; dU[t * kSl + j + 1] = d01;
-            dU[(t + 1) * kSl + j] = d10; dU[(t + 1) * kSl + j + 1] = d11;
+        // Matrix-core phases (wave w: 16-row tile of a product; li = the
+        // slice's value column).  U = Tinv diag(beta) Xr on waves 0-3,
+        // dU = scale P^T dO + Kt dS_end on waves 4-7 (Tinv, P zero above
+        // their diagonals).
+        const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+        if (wave < 4) {
+            const int R = 16 * wave;
+            const f32x4 acc = tile_product(0, R + 16, [&](int k) { return Ti[(R + li) * kTP + k]; },
+                                           [&](int k) { return Bs[k] * Xs[k * kSl + li]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Us[(R + 4 * l4 + r) * kSl + li] = acc[r];
+        } else if (wave < 8) {
+            const int R = 16 * (wave - 4);
+            const f32x4 ap = tile_product(R, kC, [&](int k) { return Ps[k * kTP + R + li]; },
+                                          [&](int k) { return Os[k * kSl + li]; });
+            const f32x4 ak = tile_product(0, DK, [&](int k) { return Kt[(R + li) * KP + k]; },
+                                          [&](int k) { return dS[k * kSl + li]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dU[(R + 4 * l4 + r) * kSl + li] = a.scale * ap[r] + ak[r];
         }
         __syncthreads();
         // dX = Tinv^T dU, kept in registers until every tile has read dU
-        float x00 = 0.f, x01 = 0.f, x10 = 0.f, x11 = 0.f;
-        const int xt = 2 * (tid / (kSl / 2)), xj = 2 * (tid % (kSl / 2));
-        if (tid < kC * kSl / 4) {
-            for (int r = xt; r < kC; ++r) {
-                const float i0 = Ti[r * kTP + xt], i1 = Ti[r * kTP + xt + 1];
-                const float g0 = dU[r * kSl + xj], g1 = dU[r * kSl + xj + 1];
-                x00 += i0 * g0; x01 += i0 * g1; x10 += i1 * g0; x11 += i1 * g1;
-            }
+        f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
+        if (wave < 4) {
+            const int R = 16 * wave;
+            xacc = tile_product(R, kC, [&](int k) { return Ti[k * kTP + R + li]; },
+                                [&](int k) { return dU[k * kSl + li]; });
         }
         __syncthreads();
-        if (tid < kC * kSl / 4) {
-            dU[xt * kSl + xj] = x00; dU[xt * kSl + xj + 1] = x01;
-            dU[(xt + 1) * kSl + xj] = x10; dU[(xt + 1) * kSl + xj + 1] = x11;
+        if (wave < 4) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dU[(16 * wave + 4 * l4 + r) * kSl + li] = xacc[r];
         }
         __syncthreads();
         float* dX = dU;
@@ -424,26 +426,18 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
                 a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok] = acc;
             }
         }
-        // dS <- eE dS + scale Q0^T dO - K0^T diag(beta) dX  (2 x 2 tiles of (c, j))
-        if (tid < DK * kSl / 4) {
-            const int c = 2 * (tid / (kSl / 2)), j = 2 * (tid % (kSl / 2));
-            float q00 = 0.f, q01 = 0.f, q10 = 0.f, q11 = 0.f;
-            float k00 = 0.f, k01 = 0.f, k10 = 0.f, k11 = 0.f;
-#pragma unroll 4
-            for (int t = 0; t < kC; ++t) {
-                const float qa = Q0[t * KP + c], qb = Q0[t * KP + c + 1];
-                const float ka = K0[t * KP + c], kb = K0[t * KP + c + 1];
-                const float o0 = Os[t * kSl + j], o1 = Os[t * kSl + j + 1];
-                const float bt = Bs[t];
-                const float g0 = bt * dX[t * kSl + j], g1 = bt * dX[t * kSl + j + 1];
-                q00 += qa * o0; q01 += qa * o1; q10 += qb * o0; q11 += qb * o1;
-                k00 += ka * g0; k01 += ka * g1; k10 += kb * g0; k11 += kb * g1;
+        // dS <- eE dS + scale Q0^T dO - K0^T diag(beta) dX  (wave w: rows c of tile w)
+        if (wave < DK / 16) {
+            const int R = 16 * wave;
+            const f32x4 aq = tile_product(0, kC, [&](int k) { return Q0[k * KP + R + li]; },
+                                          [&](int k) { return Os[k * kSl + li]; });
+            const f32x4 ak = tile_product(0, kC, [&](int k) { return K0[k * KP + R + li]; },
+                                          [&](int k) { return Bs[k] * dX[k * kSl + li]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int c = R + 4 * l4 + r;
+                dS[c * kSl + li] = eE[c] * dS[c * kSl + li] + a.scale * aq[r] - ak[r];
             }
-            const float sc = a.scale;
-            dS[c * kSl + j] = eE[c] * dS[c * kSl + j] + sc * q00 - k00;
-            dS[c * kSl + j + 1] = eE[c] * dS[c * kSl + j + 1] + sc * q01 - k01;
-            dS[(c + 1) * kSl + j] = eE[c + 1] * dS[(c + 1) * kSl + j] + sc * q10 - k10;
-            dS[(c + 1) * kSl + j + 1] = eE[c + 1] * dS[(c + 1) * kSl + j + 1] + sc * q11 - k11;
         }
     }
     __syncthreads();
