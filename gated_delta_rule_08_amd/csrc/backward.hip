@@ -71,7 +71,7 @@ __device__ __forceinline__ f32x4 tile_product(int k0, int k1, FA fa, FB fb) {
     const int lk = (threadIdx.x & 63) >> 4;
     f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
     int k = k0;
-#pragma unroll 2
+#pragma nounroll
     for (; k + 8 <= k1; k += 8) {
         c0 = mma4(fa(k + lk), fb(k + lk), c0);
         c1 = mma4(fa(k + 4 + lk), fb(k + 4 + lk), c1);
@@ -450,21 +450,18 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
 }
 
 // ---------------------------------------------------------------- bwd_local
-// Thread tiles: of the [64 x DK] gradients, RT rows from t0 = RT (tid % NRG)
-// and CW columns from c0 = CW (tid / NRG) (NRG = 64 / RT row groups); of the
-// [64 x 64] ones, rows tb .. tb+1 and columns s0 .. s0+1 (tb = 2 (tid % 32),
-// s0 = 2 (tid / 32)).
+// Matrix-core mapping: wave w owns row tile T = 16 (w % 4) of every
+// [64 x DK] gradient and column tiles 16 (g + 4 i) (g = w / 4) of them, and
+// the (T, 16 g) tile of the [64 x 64] ones; a lane holds rows T + 4 (l / 16)
+// + r (r = 0..3), column (tile start) + l % 16 of each.
 template <int DK, bool KDA, typename InT>
 __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     constexpr int KP = DK + 1;
     constexpr int GW = KDA ? DK : 1;
     constexpr int GP = GW + 1;
-    constexpr int PER = kC * DK / kNT;              // [64 x DK] elements per thread
-    constexpr int RT = PER >= 4 ? 4 : PER;          // rows of the tile
-    constexpr int CW = PER / RT;                    // columns of the tile
-    constexpr int NRG = kC / RT;
-    static_assert(RT * CW * kNT == kC * DK && (kNT / NRG) * CW == DK, "tile mapping");
-    constexpr int CB = 16;             // value columns per block
+    constexpr int NCTILE = DK / 16;          // 16-column tiles of the [64 x DK] gradients
+    constexpr int NCT = (NCTILE + 3) / 4;    // of them per wave
+    constexpr int CB = 16;                   // value columns per staged block
     constexpr int SP = CB + 1;
     extern __shared__ float sm[];
     float* Ks = sm;                    // [64][KP]  raw k; later dG
@@ -477,8 +474,8 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     float* Ub = Db + DK * SP;          // [64][SP]  U
     float* Xb = Ub + kC * SP;          // [64][SP]  dX
     float* Ob = Xb + kC * SP;          // [64][SP]  dO
-    float* Mm = X;                     // [64][kTP] M = beta dA
-    float* Nm = Mm + kC * kTP;         // [64][kTP] N = dP
+    float* Mm = X;                     // [64][kTP] M = beta dA  (GDN: then M o E)
+    float* Nm = Mm + kC * kTP;         // [64][kTP] N = dP       (GDN: then N o E)
     constexpr int UNION = (2 * DK * SP + 3 * kC * SP) > 2 * kC * kTP ? (2 * DK * SP + 3 * kC * SP) : 2 * kC * kTP;
     float* Bs = X + UNION;             // [64] beta
     float* dB = Bs + kC;               // [64] dbeta
@@ -523,22 +520,19 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         eE[tid] = __expf(acc);  // acc = G_end
     }
 
-    const int t0 = RT * (tid % NRG);
-    const int c0 = CW * (tid / NRG);
-    const int tb = 2 * (tid & 31);
-    const int s0 = 2 * (tid >> 5);
-    float aQ[RT][CW], aK[RT][CW], aT[RT][CW], aA[2][2], aP[2][2];
+    const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+    const int T = 16 * (wave & 3), g = wave >> 2;
+    auto has_ct = [&](int i) { return g + 4 * i < NCTILE; };
+    auto ct = [&](int i) { return 16 * (g + 4 * i); };
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 aQ[NCT], aK[NCT], aT[NCT], aA = z4, aP = z4;
 #pragma unroll
-    for (int x = 0; x < RT; ++x)
-#pragma unroll
-        for (int y = 0; y < CW; ++y) aQ[x][y] = aK[x][y] = aT[x][y] = 0.f;
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) aA[x][y] = aP[x][y] = 0.f;
+    for (int i = 0; i < NCT; ++i) aQ[i] = aK[i] = aT[i] = z4;
     float ge = 0.f;  // tid < DK: sum_j dS_end S of channel tid
     const float* Sg = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
     const float* Dg = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    // Contractions over the value columns, block by block:
+    //   dQ0' = dO S^T, dK0' = dX S^T, dKt = U dS_end^T, dA' = dX U^T, dP' = dO U^T
     for (int jb = 0; jb < a.DV; jb += CB) {
         __syncthreads();  // previous block consumed (first pass: staging above done)
         for (int i = tid; i < DK * CB; i += kNT) {
@@ -555,41 +549,22 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
             Ob[t * SP + j] = ok ? ld(dO + r) : 0.f;
         }
         __syncthreads();
-        for (int j = 0; j < CB; ++j) {
-            float o[RT], x[RT], u[RT], sv[CW], dv[CW], ob[2], xb[2], us[2];
 #pragma unroll
-            for (int m = 0; m < RT; ++m) {
-                o[m] = Ob[(t0 + m) * SP + j];
-                x[m] = Xb[(t0 + m) * SP + j];
-                u[m] = Ub[(t0 + m) * SP + j];
+        for (int kk = 0; kk < CB; kk += 4) {
+            const int j = kk + l4;
+            const float o = Ob[(T + li) * SP + j], x = Xb[(T + li) * SP + j], u = Ub[(T + li) * SP + j];
+            const float us = Ub[(16 * g + li) * SP + j];
+            aA = mma4(x, us, aA);
+            aP = mma4(o, us, aP);
+#pragma unroll
+            for (int i = 0; i < NCT; ++i) {
+                if (!has_ct(i)) continue;
+                const int c = ct(i) + li;
+                const float sv = Sb[c * SP + j], dv = Db[c * SP + j];
+                aQ[i] = mma4(o, sv, aQ[i]);
+                aK[i] = mma4(x, sv, aK[i]);
+                aT[i] = mma4(u, dv, aT[i]);
             }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                ob[m] = Ob[(tb + m) * SP + j];
-                xb[m] = Xb[(tb + m) * SP + j];
-                us[m] = Ub[(s0 + m) * SP + j];
-            }
-#pragma unroll
-            for (int y = 0; y < CW; ++y) {
-                sv[y] = Sb[(c0 + y) * SP + j];
-                dv[y] = Db[(c0 + y) * SP + j];
-            }
-#pragma unroll
-            for (int m = 0; m < RT; ++m) {
-#pragma unroll
-                for (int y = 0; y < CW; ++y) {
-                    aQ[m][y] += o[m] * sv[y];
-                    aK[m][y] += x[m] * sv[y];
-                    aT[m][y] += u[m] * dv[y];
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    aA[m][y] += xb[m] * us[y];
-                    aP[m][y] += ob[m] * us[y];
-                }
         }
         if (tid < DK) {
             for (int j = 0; j < CB; ++j) ge += Db[tid * SP + j] * Sb[tid * SP + j];
@@ -599,118 +574,125 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     // dA = -dX U^T (s < t), M = beta dA;  dP = scale dO U^T (s <= t);
     // dbeta_t += sum_s dA_ts Ahat_ts
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int t = tb + m;
-        float db = 0.f;
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            const int s = s0 + y;
-            const float dA = s < t ? -aA[m][y] : 0.f;
-            db += dA * Ah[t * kTP + s];
-            Mm[t * kTP + s] = Bs[t] * dA;
-            Nm[t * kTP + s] = s <= t ? a.scale * aP[m][y] : 0.f;
-        }
-        atomicAdd(&dB[t], db);
+    for (int r = 0; r < 4; ++r) {
+        const int t = T + 4 * l4 + r, s2 = 16 * g + li;
+        const float dA = s2 < t ? -aA[r] : 0.f;
+        Mm[t * kTP + s2] = Bs[t] * dA;
+        Nm[t * kTP + s2] = s2 <= t ? a.scale * aP[r] : 0.f;
+        atomicAdd(&dB[t], dA * Ah[t * kTP + s2]);
     }
     if (tid < DK) {
         if (KDA) dGe[tid] = eE[tid] * ge;
         else atomicAdd(&dGe[0], eE[0] * ge);
     }
     __syncthreads();
-    // the four gate-weighted sums of the thread's tile, s outermost so that
-    // each LDS value feeds the whole tile.  G decreases along the chunk, so
-    // G_t - G_s <= 0 exactly where M_ts, N_ts can be nonzero (s <= t) and
-    // G_s - G_t <= 0 where M_st, N_st can (s >= t); clamping the exponents
-    // at 0 leaves the other products at 0 * 1.
-    float a1[RT][CW], a2[RT][CW], a3[RT][CW], a4[RT][CW], gt[RT][CW];
+    // The four gate-weighted sums of the lane's outputs:
+    //   a1 = sum_{s<t} M_ts k_sc E(t,s,c),   a2 = sum_{s<=t} N_ts k_sc E(t,s,c),
+    //   a3 = sum_{r>t} M_rt k_rc E(r,t,c),   a4 = sum_{r>=t} N_rt q_rc E(r,t,c).
+    f32x4 a1[NCT], a2[NCT], a3[NCT], a4[NCT];
 #pragma unroll
-    for (int m = 0; m < RT; ++m)
-#pragma unroll
-        for (int y = 0; y < CW; ++y) {
-            a1[m][y] = a2[m][y] = a3[m][y] = a4[m][y] = 0.f;
-            gt[m][y] = Gs[(t0 + m) * GP + (KDA ? c0 + y : 0)];
+    for (int i = 0; i < NCT; ++i) a1[i] = a2[i] = a3[i] = a4[i] = z4;
+    if constexpr (!KDA) {
+        // scalar gate: E(t,s) is one matrix, folded into M and N, after which
+        // the sums are four matrix products (M E) K, (N E) K, (M E)^T K,
+        // (N E)^T Q.  G decreases along the chunk, so the exponent is <= 0
+        // wherever M or N can be nonzero; clamping it leaves 0 * 1 elsewhere.
+        for (int i = tid; i < kC * kC; i += kNT) {
+            const int t = i >> 6, s2 = i & 63;
+            const float e = __expf(fminf(Gs[t * GP] - Gs[s2 * GP], 0.f));
+            Mm[t * kTP + s2] *= e;
+            Nm[t * kTP + s2] *= e;
         }
+        __syncthreads();
 #pragma unroll 2
-    for (int s = 0; s < kC; ++s) {
-        float mts[RT], nts[RT], mst[RT], nst[RT], ks[CW], qs[CW], gs[CW];
+        for (int kk = 0; kk < kC; kk += 4) {
+            const int s2 = kk + l4;
+            const float m1 = Mm[(T + li) * kTP + s2], n1 = Nm[(T + li) * kTP + s2];
+            const float m3 = Mm[s2 * kTP + T + li], n3 = Nm[s2 * kTP + T + li];
 #pragma unroll
-        for (int m = 0; m < RT; ++m) {
-            mts[m] = Mm[(t0 + m) * kTP + s];
-            nts[m] = Nm[(t0 + m) * kTP + s];
-            mst[m] = Mm[s * kTP + t0 + m];
-            nst[m] = Nm[s * kTP + t0 + m];
+            for (int i = 0; i < NCT; ++i) {
+                if (!has_ct(i)) continue;
+                const float kv = Ks[s2 * KP + ct(i) + li], qv = Qs[s2 * KP + ct(i) + li];
+                a1[i] = mma4(m1, kv, a1[i]);
+                a2[i] = mma4(n1, kv, a2[i]);
+                a3[i] = mma4(m3, kv, a3[i]);
+                a4[i] = mma4(n3, qv, a4[i]);
+            }
         }
+    } else {
+        // channel gate: E depends on c, so the sums run on the vector ALUs
+        // over the lane's own outputs (rows T + 4 l4 + r, columns ct(i) + li).
+        for (int s2 = 0; s2 < kC; ++s2) {
+            float mts[4], nts[4], mst[4], nst[4];
 #pragma unroll
-        for (int y = 0; y < CW; ++y) {
-            ks[y] = Ks[s * KP + c0 + y];
-            qs[y] = Qs[s * KP + c0 + y];
-            gs[y] = Gs[s * GP + (KDA ? c0 + y : 0)];
-        }
-#pragma unroll
-        for (int m = 0; m < RT; ++m) {
-            float e1g = 0.f, e2g = 0.f;
-            if constexpr (!KDA) {
-                e1g = __expf(fminf(gt[m][0] - gs[0], 0.f));
-                e2g = __expf(fminf(gs[0] - gt[m][0], 0.f));
+            for (int r = 0; r < 4; ++r) {
+                const int t = T + 4 * l4 + r;
+                mts[r] = Mm[t * kTP + s2];
+                nts[r] = Nm[t * kTP + s2];
+                mst[r] = Mm[s2 * kTP + t];
+                nst[r] = Nm[s2 * kTP + t];
             }
 #pragma unroll
-            for (int y = 0; y < CW; ++y) {
-                const float e1 = KDA ? __expf(fminf(gt[m][y] - gs[y], 0.f)) : e1g;
-                const float e2 = KDA ? __expf(fminf(gs[y] - gt[m][y], 0.f)) : e2g;
-                const float k1 = ks[y] * e1, k2 = ks[y] * e2;
-                a1[m][y] += mts[m] * k1;
-                a2[m][y] += nts[m] * k1;
-                a3[m][y] += mst[m] * k2;
-                a4[m][y] += nst[m] * qs[y] * e2;
+            for (int i = 0; i < NCT; ++i) {
+                if (!has_ct(i)) continue;
+                const int c = ct(i) + li;
+                const float ks = Ks[s2 * KP + c], qs = Qs[s2 * KP + c], gs = Gs[s2 * GP + c];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float gt = Gs[(T + 4 * l4 + r) * GP + c];
+                    const float e1 = __expf(fminf(gt - gs, 0.f)), e2 = __expf(fminf(gs - gt, 0.f));
+                    a1[i][r] += mts[r] * ks * e1;
+                    a2[i][r] += nts[r] * ks * e1;
+                    a3[i][r] += mst[r] * ks * e2;
+                    a4[i][r] += nst[r] * qs * e2;
+                }
             }
         }
     }
-    float dq[RT][CW], dk[RT][CW], dg[RT][CW];
+    // gradients of the lane's outputs
+    float dq[NCT][4], dk[NCT][4], dg[NCT][4];
 #pragma unroll
-    for (int m = 0; m < RT; ++m) {
-        const int t = t0 + m;
+    for (int i = 0; i < NCT; ++i) {
 #pragma unroll
-        for (int y = 0; y < CW; ++y) {
-            const int c = c0 + y;
-            const float e0 = __expf(gt[m][y]);
-            const float ek = __expf(Gs[(kC - 1) * GP + (KDA ? c : 0)] - gt[m][y]);  // exp(G_end - G_t) <= 1
+        for (int r = 0; r < 4; ++r) {
+            dq[i][r] = dk[i][r] = dg[i][r] = 0.f;
+            if (!has_ct(i)) continue;
+            const int t = T + 4 * l4 + r, c = ct(i) + li;
+            const float gt = Gs[t * GP + (KDA ? c : 0)];
+            const float e0 = __expf(gt);
+            const float ek = __expf(Gs[(kC - 1) * GP + (KDA ? c : 0)] - gt);  // exp(G_end - G_t) <= 1
             const float kv = Ks[t * KP + c], qv = Qs[t * KP + c];
-            const float dQ0 = a.scale * aQ[m][y], dK0 = -Bs[t] * aK[m][y], dKt = aT[m][y];
-            dq[m][y] = dQ0 * e0 + a2[m][y];
-            dk[m][y] = dK0 * e0 + dKt * ek + a1[m][y] + a3[m][y] + a4[m][y];
-            dg[m][y] = qv * (dQ0 * e0 + a2[m][y]) + kv * (dK0 * e0 - dKt * ek + a1[m][y] - a3[m][y] - a4[m][y]);
+            const float dQ0 = a.scale * aQ[i][r], dK0 = -Bs[t] * aK[i][r], dKt = aT[i][r];
+            dq[i][r] = dQ0 * e0 + a2[i][r];
+            dk[i][r] = dK0 * e0 + dKt * ek + a1[i][r] + a3[i][r] + a4[i][r];
+            dg[i][r] = qv * (dQ0 * e0 + a2[i][r]) + kv * (dK0 * e0 - dKt * ek + a1[i][r] - a3[i][r] - a4[i][r]);
             // G_end = G_{n-1}: its gradient through Kt (and, above, eE)
-            const float ge_t = dKt * kv * ek;
-            if (KDA) atomicAdd(&dGe[c], ge_t);
-            else atomicAdd(&dGe[0], ge_t);
+            atomicAdd(&dGe[KDA ? c : 0], dKt * kv * ek);
         }
     }
     __syncthreads();  // k, q no longer read: dG goes where k was
     float* dG = Ks;
-    if constexpr (KDA) {
 #pragma unroll
-        for (int m = 0; m < RT; ++m)
+    for (int i = 0; i < NCT; ++i) {
+        if (!has_ct(i)) continue;
 #pragma unroll
-            for (int y = 0; y < CW; ++y) dG[(t0 + m) * KP + c0 + y] = dg[m][y];
-    } else {
-#pragma unroll
-        for (int m = 0; m < RT; ++m) {
-            float s = 0.f;
-#pragma unroll
-            for (int y = 0; y < CW; ++y) s += dg[m][y];
-            atomicAdd(&dGt[t0 + m], s);
+        for (int r = 0; r < 4; ++r) {
+            const int t = T + 4 * l4 + r;
+            if constexpr (KDA) dG[t * KP + ct(i) + li] = dg[i][r];
+            else atomicAdd(&dGt[t], dg[i][r]);
         }
     }
     InT* dqo = static_cast<InT*>(a.dq);
     InT* dko = static_cast<InT*>(a.dk);
 #pragma unroll
-    for (int m = 0; m < RT; ++m) {
-        const int t = t0 + m;
-        if (t < n) {
+    for (int i = 0; i < NCT; ++i) {
+        if (!has_ct(i)) continue;
 #pragma unroll
-            for (int y = 0; y < CW; ++y) {
-                Elem<InT>::store(dqo + tok(t) * DK + c0 + y, dq[m][y]);
-                Elem<InT>::store(dko + tok(t) * DK + c0 + y, dk[m][y]);
+        for (int r = 0; r < 4; ++r) {
+            const int t = T + 4 * l4 + r;
+            if (t < n) {
+                Elem<InT>::store(dqo + tok(t) * DK + ct(i) + li, dq[i][r]);
+                Elem<InT>::store(dko + tok(t) * DK + ct(i) + li, dk[i][r]);
             }
         }
     }
