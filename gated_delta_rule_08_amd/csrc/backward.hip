@@ -176,21 +176,52 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
     }
     __syncthreads();
     float* img = a.ws + Ws(a.B, a.T, a.H, DK, a.DV).img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-    for (int i = tid; i < kC * kC; i += kNT) {
-        const int t = i >> 6, s = i & 63;
-        float sa = 0.f, sp = 0.f;
-        if (s <= t) {
-            for (int c = 0; c < DK; ++c) {
-                const float e = __expf(Gs[t * GP + (KDA ? c : 0)] - Gs[s * GP + (KDA ? c : 0)]);
-                const float kse = Ks[s * KP + c] * e;
-                sa += Ks[t * KP + c] * kse;
-                sp += Qs[t * KP + c] * kse;
+    if constexpr (!KDA) {
+        // scalar gate: Ahat = (K K^T) o E and P = (Q K^T) o E with one decay
+        // E_ts = exp(G_t - G_s) per pair, so both are matrix products on the
+        // matrix cores (wave w: the 16 x 16 tile (w / 4, w % 4)).
+        const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+        const int T = 16 * (wave >> 2), S = 16 * (wave & 3);
+        if (S <= T) {
+            const f32x4 ka = tile_product(0, DK, [&](int k) { return Ks[(T + li) * KP + k]; },
+                                          [&](int k) { return Ks[(S + li) * KP + k]; });
+            const f32x4 qa = tile_product(0, DK, [&](int k) { return Qs[(T + li) * KP + k]; },
+                                          [&](int k) { return Ks[(S + li) * KP + k]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = T + 4 * l4 + r, s = S + li;
+                const float e = __expf(fminf(Gs[t * GP] - Gs[s * GP], 0.f));
+                const float sa = s < t ? ka[r] * e : 0.f, sp = s <= t ? qa[r] * e : 0.f;
+                img[iA + t * kC + s] = sa;
+                img[iP + t * kC + s] = sp;
+                As[t * kTP + s] = Bs[t] * sa;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = T + 4 * l4 + r, s = S + li;
+                img[iA + t * kC + s] = 0.f;
+                img[iP + t * kC + s] = 0.f;
+                As[t * kTP + s] = 0.f;
             }
         }
-        if (s == t) sa = 0.f;
-        img[iA + i] = sa;
-        img[iP + i] = sp;
-        As[t * kTP + s] = Bs[t] * sa;
+    } else {
+        for (int i = tid; i < kC * kC; i += kNT) {
+            const int t = i >> 6, s = i & 63;
+            float sa = 0.f, sp = 0.f;
+            if (s <= t) {
+                for (int c = 0; c < DK; ++c) {
+                    const float e = __expf(Gs[t * GP + c] - Gs[s * GP + c]);
+                    const float kse = Ks[s * KP + c] * e;
+                    sa += Ks[t * KP + c] * kse;
+                    sp += Qs[t * KP + c] * kse;
+                }
+            }
+            if (s == t) sa = 0.f;
+            img[iA + i] = sa;
+            img[iP + i] = sp;
+            As[t * kTP + s] = Bs[t] * sa;
+        }
     }
     for (int i = tid; i < kC * DK; i += kNT) {
         const int t = i / DK, c = i - t * DK;
