@@ -1,5 +1,7 @@
 // Backward pass of the chunked gated delta rule (dq, dk, dv, dalpha, dbeta,
-// dS_0 from dO and dS_T), in fp32 on the vector ALUs.
+// dS_0 from dO and dS_T), all arithmetic in fp32: the products on the fp32
+// matrix cores, the element-wise work (and KDA's channel-dependent decays) on
+// the vector ALUs.
 //
 // The mixers ("Super Apriel: One Checkpoint, Many Speeds", §2.A: GDN and KDA,
 // recurrent mixers with scalar and channel-wise gates) are trained in the
@@ -31,7 +33,8 @@
 //
 // Kernels (one head per (b, h); 16-column value slices where the work
 // separates by value column):
-//   bwd_prep   (b, h, chunk)  Ahat, P and Tinv of every chunk -> image
+//   bwd_prep   (b, h, chunk)  Ahat, P, Tinv and the factored rows
+//                             k e0, k ek, q e0, eE of every chunk -> image
 //   bwd_fwd    (b, h, slice)  forward chain: S at every chunk start
 //                             (checkpoints) and Xr
 //   bwd_chain  (b, h, slice)  reverse chain: dS_end of every chunk, U, dX,
