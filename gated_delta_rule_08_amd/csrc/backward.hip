@@ -237,24 +237,43 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
     }
     for (int i = tid; i < kC * kC; i += kNT) Tl[(i >> 6) * kTP + (i & 63)] = (i >> 6) == (i & 63) ? 1.f : 0.f;
     __syncthreads();
-    // Tinv = (I + A)^{-1}, unit lower triangular, row by row: row t is
-    // -sum_{r<t} A_tr Tinv_r (Tinv_r zero right of its diagonal, so every
-    // lane s runs the same r range and A_tr is a broadcast read).  One wave.
-    // Each lane reads and writes only its own column.
+    // Tinv = (I + A)^{-1}, unit lower triangular, by 16 x 16 blocks: the four
+    // diagonal blocks D_b = (I + A_bb)^{-1} row by row (one wave, lane =
+    // block and column; Tinv starts as I, so every lane runs the same range),
+    // then the blocks below them by their distance d from the diagonal,
+    //   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj,
+    // as fp32 matrix-core products (wave j takes block (j + d, j)).
     if (tid < kC) {
-        const int s = tid;
-        for (int t = 1; t < kC; ++t) {
-            float v0 = 0.f, v1 = 0.f;
-            int r = 0;
-            for (; r + 1 < t; r += 2) {
-                v0 -= As[t * kTP + r] * Tl[r * kTP + s];
-                v1 -= As[t * kTP + r + 1] * Tl[(r + 1) * kTP + s];
-            }
-            if (r < t) v0 -= As[t * kTP + r] * Tl[r * kTP + s];
-            if (s < t) Tl[t * kTP + s] = v0 + v1;
+        const int o = 16 * (tid >> 4), s = tid & 15;
+        for (int t = 1; t < 16; ++t) {
+            float v = 0.f;
+            for (int r = 0; r < t; ++r) v -= As[(o + t) * kTP + o + r] * Tl[(o + r) * kTP + o + s];
+            if (s < t) Tl[(o + t) * kTP + o + s] = v;
         }
     }
     __syncthreads();
+    {
+        constexpr int YP = 17;
+        float* Ys = Qs;  // q is written out already: 3 tiles of [16][YP] scratch
+        const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+        for (int d = 1; d < 4; ++d) {
+            const int J = 16 * wave, I = J + 16 * d;
+            if (wave < 4 - d) {
+                const f32x4 y = tile_product(J, I, [&](int k) { return As[(I + li) * kTP + k]; },
+                                             [&](int k) { return Tl[k * kTP + J + li]; });
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Ys[wave * 16 * YP + (4 * l4 + r) * YP + li] = y[r];
+            }
+            __syncthreads();
+            if (wave < 4 - d) {
+                const f32x4 t = tile_product(0, 16, [&](int k) { return Tl[(I + li) * kTP + I + k]; },
+                                             [&](int k) { return Ys[wave * 16 * YP + k * YP + li]; });
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tl[(I + 4 * l4 + r) * kTP + J + li] = -t[r];
+            }
+            __syncthreads();
+        }
+    }
     for (int i = tid; i < kC * kC; i += kNT) img[iT + i] = Tl[(i >> 6) * kTP + (i & 63)];
 }
 
