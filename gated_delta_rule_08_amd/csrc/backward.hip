@@ -209,21 +209,53 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
             }
         }
     } else {
-        for (int i = tid; i < kC * kC; i += kNT) {
-            const int t = i >> 6, s = i & 63;
+        // channel gate: tiles below the diagonal blocks factor the decay at
+        // the column block's last token (exp(G_t - G_g) exp(G_g - G_s), both
+        // <= 1) and run on the matrix cores; the four diagonal tiles use
+        // exact exponentials on the vector ALUs.
+        const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+        const int T = 16 * (wave >> 2), S = 16 * (wave & 3);
+        if (S < T) {
+            f32x4 ka = {0.f, 0.f, 0.f, 0.f}, qa = {0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < DK; kk += 4) {
+                const int c = kk + l4;
+                const float gg = Gs[(S + 15) * GP + c];
+                const float bk = Ks[(S + li) * KP + c] * __expf(gg - Gs[(S + li) * GP + c]);
+                const float et = __expf(Gs[(T + li) * GP + c] - gg);
+                ka = mma4(Ks[(T + li) * KP + c] * et, bk, ka);
+                qa = mma4(Qs[(T + li) * KP + c] * et, bk, qa);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = T + 4 * l4 + r, s2 = S + li;
+                img[iA + t * kC + s2] = ka[r];
+                img[iP + t * kC + s2] = qa[r];
+                As[t * kTP + s2] = Bs[t] * ka[r];
+            }
+        } else if (S > T) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = T + 4 * l4 + r, s2 = S + li;
+                img[iA + t * kC + s2] = 0.f;
+                img[iP + t * kC + s2] = 0.f;
+                As[t * kTP + s2] = 0.f;
+            }
+        }
+        for (int i = tid; i < 4 * 16 * 16; i += kNT) {  // the diagonal tiles
+            const int blk = i >> 8, t = 16 * blk + ((i >> 4) & 15), s2 = 16 * blk + (i & 15);
             float sa = 0.f, sp = 0.f;
-            if (s <= t) {
+            if (s2 <= t) {
                 for (int c = 0; c < DK; ++c) {
-                    const float e = __expf(Gs[t * GP + c] - Gs[s * GP + c]);
-                    const float kse = Ks[s * KP + c] * e;
+                    const float e = __expf(Gs[t * GP + c] - Gs[s2 * GP + c]);
+                    const float kse = Ks[s2 * KP + c] * e;
                     sa += Ks[t * KP + c] * kse;
                     sp += Qs[t * KP + c] * kse;
                 }
             }
-            if (s == t) sa = 0.f;
-            img[iA + i] = sa;
-            img[iP + i] = sp;
-            As[t * kTP + s] = Bs[t] * sa;
+            if (s2 == t) sa = 0.f;
+            img[iA + t * kC + s2] = sa;
+            img[iP + t * kC + s2] = sp;
+            As[t * kTP + s2] = Bs[t] * sa;
         }
     }
     for (int i = tid; i < kC * DK; i += kNT) {
@@ -673,31 +705,64 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
             }
         }
     } else {
-        // channel gate: E depends on c, so the sums run on the vector ALUs
-        // over the lane's own outputs (rows T + 4 l4 + r, columns ct(i) + li).
-        for (int s2 = 0; s2 < kC; ++s2) {
-            float mts[4], nts[4], mst[4], nst[4];
+        // channel gate: E(t,s,c) depends on c.  Across 16-token blocks it
+        // factors through the cumulative gate at a block boundary into two
+        // factors that are each <= 1 (G decreases along the chunk):
+        //   s < T <= t:        E = exp(G_t - G_{T-1}) exp(G_{T-1} - G_s),
+        //   t <= T+15 < r:     E = exp(G_r - G_{T+15}) exp(G_{T+15} - G_t),
+        // so the parts of a1, a2 (s before the row block) and a3, a4 (r after
+        // it) are matrix products with the second factor in the B operand and
+        // the first applied to the output; the row block's own 16 tokens run
+        // on the vector ALUs with exact exponentials.
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = T + 4 * l4 + r;
-                mts[r] = Mm[t * kTP + s2];
-                nts[r] = Nm[t * kTP + s2];
-                mst[r] = Mm[s2 * kTP + t];
-                nst[r] = Nm[s2 * kTP + t];
+        for (int i = 0; i < NCT; ++i) {
+            if (!has_ct(i)) continue;
+            const int c = ct(i) + li;
+            if (T > 0) {
+                const float gr = Gs[(T - 1) * GP + c];
+                f32x4 c1 = z4, c2 = z4;
+                for (int kk = 0; kk < T; kk += 4) {
+                    const int s2 = kk + l4;
+                    const float bk = Ks[s2 * KP + c] * __expf(gr - Gs[s2 * GP + c]);
+                    c1 = mma4(Mm[(T + li) * kTP + s2], bk, c1);
+                    c2 = mma4(Nm[(T + li) * kTP + s2], bk, c2);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float f = __expf(Gs[(T + 4 * l4 + r) * GP + c] - gr);
+                    a1[i][r] = c1[r] * f;
+                    a2[i][r] = c2[r] * f;
+                }
             }
+            if (T + 16 < kC) {
+                const float gr = Gs[(T + 15) * GP + c];
+                f32x4 c3 = z4, c4 = z4;
+                for (int kk = T + 16; kk < kC; kk += 4) {
+                    const int r2 = kk + l4;
+                    const float e = __expf(Gs[r2 * GP + c] - gr);
+                    c3 = mma4(Mm[r2 * kTP + T + li], Ks[r2 * KP + c] * e, c3);
+                    c4 = mma4(Nm[r2 * kTP + T + li], Qs[r2 * KP + c] * e, c4);
+                }
 #pragma unroll
-            for (int i = 0; i < NCT; ++i) {
-                if (!has_ct(i)) continue;
-                const int c = ct(i) + li;
+                for (int r = 0; r < 4; ++r) {
+                    const float f = __expf(gr - Gs[(T + 4 * l4 + r) * GP + c]);
+                    a3[i][r] = c3[r] * f;
+                    a4[i][r] = c4[r] * f;
+                }
+            }
+            // the row block itself (masks come from the zeros of M and N; the
+            // exponents are clamped at 0 where the products vanish)
+            for (int s2 = T; s2 < T + 16; ++s2) {
                 const float ks = Ks[s2 * KP + c], qs = Qs[s2 * KP + c], gs = Gs[s2 * GP + c];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float gt = Gs[(T + 4 * l4 + r) * GP + c];
+                    const int t = T + 4 * l4 + r;
+                    const float gt = Gs[t * GP + c];
                     const float e1 = __expf(fminf(gt - gs, 0.f)), e2 = __expf(fminf(gs - gt, 0.f));
-                    a1[i][r] += mts[r] * ks * e1;
-                    a2[i][r] += nts[r] * ks * e1;
-                    a3[i][r] += mst[r] * ks * e2;
-                    a4[i][r] += nst[r] * qs * e2;
+                    a1[i][r] += Mm[t * kTP + s2] * ks * e1;
+                    a2[i][r] += Nm[t * kTP + s2] * ks * e1;
+                    a3[i][r] += Mm[s2 * kTP + t] * ks * e2;
+                    a4[i][r] += Nm[s2 * kTP + t] * qs * e2;
                 }
             }
         }
