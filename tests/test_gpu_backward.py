@@ -133,3 +133,40 @@ def test_backward_gdn_full_size():
 
 def test_backward_kda_full_size():
     _full_size("kda", "kda_prefill_b1_t32768_h32_d128", [(0, 7)])
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_backward_zero_gate_token(gate):
+    """alpha = 0 at one token (the state is reset there).  The kernels take
+    log(alpha) floored at -40, so the gate's own gradient is 0 at that token
+    (the floor is active); every other gradient, and dalpha elsewhere, match
+    the oracle."""
+    inp, do, dst = _case(gate, "f32", B=1, T=100, H=2, dk=32, dv=32, seed=12)
+    inp["alpha"][:, 70] = 0.0
+    announce("backward %s alpha=0 at t=70" % gate)
+    got = _run(gate, "f32", inp, do, dst, 0.9)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["s0"], do, dst, scale=0.9)
+    for key in ("dq", "dk", "dv", "dbeta", "ds0"):
+        assert_close(got[key], ref[key], TOL["f32"], key)
+    assert np.all(got["dalpha"][:, 70] == 0.0)
+    keep = np.ones(100, dtype=bool)
+    keep[70] = False
+    assert_close(got["dalpha"][:, keep], ref["dalpha"][:, keep], TOL["f32"], "dalpha elsewhere")
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_backward_zero_beta_and_single_token(gate):
+    """beta = 0 on half the tokens (no write there), and a one-token sequence."""
+    inp, do, dst = _case(gate, "f32", B=2, T=90, H=2, dk=16, dv=16, seed=13)
+    inp["beta"][:, ::2] = 0.0
+    announce("backward %s beta=0 on even tokens" % gate)
+    got = _run(gate, "f32", inp, do, dst, 1.0)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["s0"], do, dst)
+    for key in ("dq", "dk", "dv", "dalpha", "dbeta", "ds0"):
+        assert_close(got[key], ref[key], TOL["f32"], key)
+    one, do1, dst1 = _case(gate, "f32", B=1, T=1, H=3, dk=64, dv=32, seed=14)
+    announce("backward %s T=1" % gate)
+    got = _run(gate, "f32", one, do1, dst1, 0.5)
+    ref = oracle.backward(one["q"], one["k"], one["v"], one["alpha"], one["beta"], one["s0"], do1, dst1, scale=0.5)
+    for key in ("dq", "dk", "dv", "dalpha", "dbeta", "ds0"):
+        assert_close(got[key], ref[key], TOL["f32"], key)
