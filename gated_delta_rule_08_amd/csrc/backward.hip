@@ -327,81 +327,83 @@ __device__ __forceinline__ void load_factors(const Args& a, const float* im, int
 }
 
 // ---------------------------------------------------------------- bwd_fwd
-template <int DK, bool KDA, typename InT>
+// FS value columns per workgroup: 32 when that still puts a workgroup on
+// every CU (the kernel's LDS has room for them, and a wider slice reads each
+// chunk image for more columns), else 16.
+template <int DK, bool KDA, typename InT, int FS>
 __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
     constexpr int KP = DK + 1;
+    constexpr int NCT = FS / 16;     // 16-column tiles of the slice
     extern __shared__ float sm[];
     float* K0 = sm;                  // [64][KP]
     float* Kt = K0 + kC * KP;        // [64][KP]
     float* Ti = Kt + kC * KP;        // [64][kTP]
-    float* Ss = Ti + kC * kTP;       // [DK][kSl]
-    float* Xs = Ss + DK * kSl;       // [64][kSl]  Xr
-    float* Us = Xs + kC * kSl;       // [64][kSl]
-    float* eE = Us + kC * kSl;       // [DK]
+    float* Ss = Ti + kC * kTP;       // [DK][FS]
+    float* Xs = Ss + DK * FS;        // [64][FS]  Xr
+    float* Us = Xs + kC * FS;        // [64][FS]
+    float* eE = Us + kC * FS;        // [DK]
     float* Bs = eE + DK;             // [64]
     const int tid = threadIdx.x;
-    const int nsl = a.DV / kSl;
+    const int nsl = a.DV / FS;
     int bh, sl;
     slice_of(a, nsl, bh, sl);
     if (bh >= a.B * a.H) return;  // padding of the grid (whole block, before any barrier)
     const int b = bh / a.H, h = bh - b * a.H;
-    const int j0 = sl * kSl;
+    const int j0 = sl * FS;
     const Ws W(a.B, a.T, a.H, DK, a.DV);
     const InT* v = static_cast<const InT*>(a.v);
-    for (int i = tid; i < DK * kSl; i += kNT) {
-        const int c = i / kSl, j = i - c * kSl;
+    for (int i = tid; i < DK * FS; i += kNT) {
+        const int c = i / FS, j = i - c * FS;
         Ss[i] = a.s0 ? a.s0[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
     }
+    // Matrix-core tiles: wave w takes row tile w / NCT and column tile w % NCT
+    // of each product (rows t for Xr and U, rows c for S); a lane's column
+    // is 16 (w % NCT) + lane % 16.
+    const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+    const int R = 16 * (wave / NCT), col = 16 * (wave % NCT) + li;
     for (int ch = 0; ch < a.nch; ++ch) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();  // the previous chunk is done with every buffer
         float* ck = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
-        for (int i = tid; i < DK * kSl; i += kNT) {
-            const int c = i / kSl, j = i - c * kSl;
+        for (int i = tid; i < DK * FS; i += kNT) {
+            const int c = i / FS, j = i - c * FS;
             ck[static_cast<size_t>(c) * a.DV + j0 + j] = Ss[i];
         }
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
         load_factors<DK>(a, im, b, h, t0, n, K0, Kt, nullptr, eE, Bs);
         for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
         __syncthreads();
-        // Matrix-core phases: wave w takes 16-row tile w of each product
-        // (rows t for Xr and U, rows c for S); li = lane % 16 is the value
-        // column of the slice.
-        const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
         // Xr = V - K0 S
-        if (wave < kC / 16) {
-            const int R = 16 * wave;
+        if (R < kC) {
             const f32x4 acc = tile_product(0, DK, [&](int k) { return K0[(R + li) * KP + k]; },
-                                           [&](int k) { return Ss[k * kSl + li]; });
+                                           [&](int k) { return Ss[k * FS + col]; });
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = R + 4 * l4 + r;
                 const size_t row = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
                 const bool ok = t < n;
-                const float x = ok ? ld(v + row * a.DV + j0 + li) - acc[r] : 0.f;
-                Xs[t * kSl + li] = x;
-                if (ok) a.ws[W.xr + row * a.DV + j0 + li] = x;
+                const float x = ok ? ld(v + row * a.DV + j0 + col) - acc[r] : 0.f;
+                Xs[t * FS + col] = x;
+                if (ok) a.ws[W.xr + row * a.DV + j0 + col] = x;
             }
         }
         __syncthreads();
         // U = Tinv diag(beta) Xr  (Tinv is zero above its diagonal)
-        if (wave < kC / 16) {
-            const int R = 16 * wave;
+        if (R < kC) {
             const f32x4 acc = tile_product(0, R + 16, [&](int k) { return Ti[(R + li) * kTP + k]; },
-                                           [&](int k) { return Bs[k] * Xs[k * kSl + li]; });
+                                           [&](int k) { return Bs[k] * Xs[k * FS + col]; });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Us[(R + 4 * l4 + r) * kSl + li] = acc[r];
+            for (int r = 0; r < 4; ++r) Us[(R + 4 * l4 + r) * FS + col] = acc[r];
         }
         __syncthreads();
         // S <- eE S + Kt^T U
-        if (wave < DK / 16) {
-            const int R = 16 * wave;
+        if (R < DK) {
             const f32x4 acc = tile_product(0, kC, [&](int k) { return Kt[k * KP + R + li]; },
-                                           [&](int k) { return Us[k * kSl + li]; });
+                                           [&](int k) { return Us[k * FS + col]; });
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int c = R + 4 * l4 + r;
-                Ss[c * kSl + li] = eE[c] * Ss[c * kSl + li] + acc[r];
+                Ss[c * FS + col] = eE[c] * Ss[c * FS + col] + acc[r];
             }
         }
     }
@@ -844,8 +846,8 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
 
 template <int DK, bool KDA>
 constexpr int prep_lds() { return 4 * (2 * kC * (DK + 1) + kC * ((KDA ? DK : 1) + 1) + 2 * kC * kTP + kC); }
-template <int DK>
-constexpr int fwd_lds() { return 4 * (2 * kC * (DK + 1) + kC * kTP + DK * kSl + 2 * kC * kSl + DK + kC); }
+template <int DK, int FS>
+constexpr int fwd_lds() { return 4 * (2 * kC * (DK + 1) + kC * kTP + DK * FS + 2 * kC * FS + DK + kC); }
 template <int DK>
 constexpr int chain_lds() { return 4 * (3 * kC * (DK + 1) + 2 * kC * kTP + DK * kSl + 4 * kC * kSl + DK + kC); }
 template <int DK, bool KDA>
@@ -858,21 +860,32 @@ constexpr int local_lds() {
 template <int DK, bool KDA, typename InT>
 hipError_t run(const Args& a, hipStream_t s) {
     static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK>() <= 160 * 1024 &&
-                  prep_lds<DK, KDA>() <= 160 * 1024, "LDS budget");
+                  prep_lds<DK, KDA>() <= 160 * 1024 && fwd_lds<DK, 32>() <= 160 * 1024, "LDS budget");
     auto set = [](const void* f, int bytes) {
         return bytes > 64 * 1024 ? hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
                                  : hipSuccess;
     };
     hipError_t e;
+    const unsigned heads8 = static_cast<unsigned>((a.B * a.H + 7) / 8 * 8);  // slice grids: whole groups of 8 heads
     const unsigned per_chunk = static_cast<unsigned>(a.B * a.H * a.nch);
-    const unsigned per_slice = static_cast<unsigned>((a.B * a.H + 7) / 8 * 8 * (a.DV / kSl));
+    const unsigned per_slice = heads8 * static_cast<unsigned>(a.DV / kSl);
+    // the forward chain's 32-column slices, when they still give every CU a workgroup
+    const bool wide = a.DV >= 32 && static_cast<long long>(a.B) * a.H * (a.DV / 32) >= 256;
+    const void* fwd = wide ? reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 32>)
+                           : reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 16>);
+    const int fwd_bytes = wide ? fwd_lds<DK, 32>() : fwd_lds<DK, 16>();
     if ((e = set(reinterpret_cast<const void*>(bwd_prep<DK, KDA, InT>), prep_lds<DK, KDA>())) != hipSuccess) return e;
-    if ((e = set(reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT>), fwd_lds<DK>())) != hipSuccess) return e;
+    if ((e = set(fwd, fwd_bytes)) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT>), chain_lds<DK>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_local<DK, KDA, InT>), local_lds<DK, KDA>())) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (prep_lds<DK, KDA>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT>), dim3(per_slice), dim3(kNT), fwd_lds<DK>(), s, a);
+    if (wide) {
+        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 32>), dim3(heads8 * static_cast<unsigned>(a.DV / 32)), dim3(kNT),
+                           (fwd_lds<DK, 32>()), s, a);
+    } else {
+        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 16>), dim3(per_slice), dim3(kNT), (fwd_lds<DK, 16>()), s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_chain<DK, KDA, InT>), dim3(per_slice), dim3(kNT), chain_lds<DK>(), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -170,3 +170,20 @@ def test_backward_zero_beta_and_single_token(gate):
     ref = oracle.backward(one["q"], one["k"], one["v"], one["alpha"], one["beta"], one["s0"], do1, dst1, scale=0.5)
     for key in ("dq", "dk", "dv", "dalpha", "dbeta", "ds0"):
         assert_close(got[key], ref[key], TOL["f32"], key)
+
+
+@pytest.mark.parametrize("gate,dk,dv", [("gdn", 64, 32), ("kda", 16, 64)])
+def test_backward_many_heads_wide_slices(gate, dk, dv):
+    """Enough heads that the forward chain takes 32-column slices (one
+    workgroup per CU still); the oracle on sampled heads."""
+    inp, do, dst = _case(gate, "f32", B=8, T=70, H=32, dk=dk, dv=dv, seed=15)
+    announce("backward %s wide slices B=8 H=32 dk=%d dv=%d" % (gate, dk, dv))
+    got = _run(gate, "f32", inp, do, dst, 1.0)
+    for (b, h) in [(0, 0), (5, 17), (7, 31)]:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+        ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]), sl(inp["beta"]),
+                              np.ascontiguousarray(inp["s0"][b:b + 1, h:h + 1]), sl(do),
+                              np.ascontiguousarray(dst[b:b + 1, h:h + 1]))
+        for key in ("dq", "dk", "dv", "dalpha", "dbeta"):
+            assert_close(got[key][b:b + 1, :, h:h + 1], ref[key], TOL["f32"], "%s[%d,%d]" % (key, b, h))
+        assert_close(got["ds0"][b:b + 1, h:h + 1], ref["ds0"], TOL["f32"], "ds0[%d,%d]" % (b, h))
