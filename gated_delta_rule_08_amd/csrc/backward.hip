@@ -37,6 +37,8 @@
 //                             k e0, k ek, q e0, eE of every chunk -> image
 //   bwd_fwd    (b, h, slice)  forward chain: S at every chunk start
 //                             (checkpoints) and Xr
+//   bwd_dout   (b, h, chunk)  the reverse chain's state-free terms
+//                             scale P^T dO and scale (q e0)^T dO
 //   bwd_chain  (b, h, slice)  reverse chain: dS_end of every chunk, U, dX,
 //                             dV and the Xr.dX part of dbeta
 //   bwd_local  (b, h, chunk)  the contractions over all value columns and
@@ -90,7 +92,7 @@ __host__ __device__ constexpr size_t img_floats(int dk) { return 3 * kC * kC + 3
 
 // Workspace layout (floats), shared by the host sizing and the kernels.
 struct Ws {
-    size_t img, ck, dck, xr, u, dx, dbp, total;
+    size_t img, ck, dck, xr, u, dx, dbp, pd, hq, total;
     __host__ __device__ Ws(int B, int T, int H, int dk, int dv) {
         const size_t bh = static_cast<size_t>(B) * H;
         const size_t nch = (static_cast<size_t>(T) + kC - 1) / kC;
@@ -102,12 +104,15 @@ struct Ws {
         u = xr + tok * dv;
         dx = u + tok * dv;
         dbp = dx + tok * dv;                      // [dv/16][B,T,H]
-        total = dbp + tok * (dv / kSl);
+        pd = dbp + tok * (dv / kSl);              // [B,T,H,dv]: scale P^T dO
+        hq = pd + tok * dv;                       // [bh][chunk][dk][dv]: scale (q e0)^T dO
+        total = hq + bh * nch * dk * dv;
     }
 };
 
 struct Args {
     int B, T, H, DV, nch;
+    int nsl_chain;  // value slices of the reverse chain (parts of sum_j Xr dX per token)
     float scale;
     const void* q;
     const void* k;
@@ -409,95 +414,152 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
     }
 }
 
-// ---------------------------------------------------------------- bwd_chain
+// ---------------------------------------------------------------- bwd_dout
+// The reverse chain's terms that do not depend on its state, per (b, h,
+// chunk) and all value columns: Pd = scale P^T dO [64 x dv] and
+// Hq = scale (q e0)^T dO [dk x dv], on the matrix cores.
 template <int DK, bool KDA, typename InT>
+__global__ __launch_bounds__(kNT) void bwd_dout(Args a) {
+    constexpr int KP = DK + 1;
+    constexpr int HW = 64;           // dO columns staged at a time (two workgroups fit a CU)
+    constexpr int OP = HW + 1;
+    extern __shared__ float sm[];
+    float* Q0 = sm;                  // [64][KP]
+    float* Ps = Q0 + kC * KP;        // [64][kTP]
+    float* Os = Ps + kC * kTP;       // [64][OP]
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int t0 = ch * kC, n = min(kC, a.T - t0);
+    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    const InT* dO = static_cast<const InT*>(a.dO);
+    const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+    float* hq = a.ws + W.hq + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    for (int i = tid; i < kC * DK; i += kNT) Q0[(i / DK) * KP + i % DK] = im[iK0 + 2 * kC * DK + i];
+    for (int i = tid; i < kC * kC; i += kNT) Ps[(i >> 6) * kTP + (i & 63)] = im[iP + i];
+    const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+    for (int j0 = 0; j0 < a.DV; j0 += HW) {
+        const int w = min(HW, a.DV - j0);
+        __syncthreads();  // (first pass: Q0, P staged; later: the previous half consumed)
+        for (int i = tid; i < kC * w; i += kNT) {
+            const int t = i / w, j = i - t * w;
+            Os[t * OP + j] = t < n ? ld(dO + ((static_cast<size_t>(b) * a.T + t0 + t) * a.H + h) * a.DV + j0 + j) : 0.f;
+        }
+        __syncthreads();
+        const int nct = w / 16;
+        // tiles: 4 row tiles of Pd and DK/16 of Hq, times nct column tiles
+        for (int tile = wave; tile < (4 + DK / 16) * nct; tile += kNT / 64) {
+            const int rt = tile / nct, C = 16 * (tile - rt * nct);
+            if (rt < 4) {
+                const int R = 16 * rt;
+                const f32x4 acc = tile_product(R, kC, [&](int k) { return Ps[k * kTP + R + li]; },
+                                               [&](int k) { return Os[k * OP + C + li]; });
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = R + 4 * l4 + r;
+                    if (t < n)
+                        a.ws[W.pd + ((static_cast<size_t>(b) * a.T + t0 + t) * a.H + h) * a.DV + j0 + C + li] =
+                            a.scale * acc[r];
+                }
+            } else {
+                const int R = 16 * (rt - 4);
+                const f32x4 acc = tile_product(0, kC, [&](int k) { return Q0[k * KP + R + li]; },
+                                               [&](int k) { return Os[k * OP + C + li]; });
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    hq[static_cast<size_t>(R + 4 * l4 + r) * a.DV + j0 + C + li] = a.scale * acc[r];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bwd_chain
+// FS value columns per workgroup (32 when that still fills every CU).
+template <int DK, bool KDA, typename InT, int FS>
 __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
     constexpr int KP = DK + 1;
+    constexpr int NCT = FS / 16;
     extern __shared__ float sm[];
     float* K0 = sm;                  // [64][KP]
     float* Kt = K0 + kC * KP;        // [64][KP]
-    float* Q0 = Kt + kC * KP;        // [64][KP]
-    float* Ti = Q0 + kC * KP;        // [64][kTP]
-    float* Ps = Ti + kC * kTP;       // [64][kTP]
-    float* dS = Ps + kC * kTP;       // [DK][kSl]
-    float* Xs = dS + DK * kSl;       // [64][kSl]  Xr
-    float* Os = Xs + kC * kSl;       // [64][kSl]  dO
-    float* Us = Os + kC * kSl;       // [64][kSl]  U
-    float* dU = Us + kC * kSl;       // [64][kSl]  dU, then dX
-    float* eE = dU + kC * kSl;       // [DK]
+    float* Ti = Kt + kC * KP;        // [64][kTP]
+    float* dS = Ti + kC * kTP;       // [DK][FS]
+    float* Hq = dS + DK * FS;        // [DK][FS]  scale (q e0)^T dO
+    float* Xs = Hq + DK * FS;        // [64][FS]  Xr
+    float* Pd = Xs + kC * FS;        // [64][FS]  scale P^T dO
+    float* Us = Pd + kC * FS;        // [64][FS]  U
+    float* dU = Us + kC * FS;        // [64][FS]  dU, then dX
+    float* eE = dU + kC * FS;        // [DK]
     float* Bs = eE + DK;             // [64]
     const int tid = threadIdx.x;
-    const int nsl = a.DV / kSl;
+    const int nsl = a.DV / FS;
     int bh, sl;
     slice_of(a, nsl, bh, sl);
     if (bh >= a.B * a.H) return;  // padding of the grid (whole block, before any barrier)
     const int b = bh / a.H, h = bh - b * a.H;
-    const int j0 = sl * kSl;
+    const int j0 = sl * FS;
     const Ws W(a.B, a.T, a.H, DK, a.DV);
-    const InT* dO = static_cast<const InT*>(a.dO);
     InT* dv = static_cast<InT*>(a.dv);
-    for (int i = tid; i < DK * kSl; i += kNT) {
-        const int c = i / kSl, j = i - c * kSl;
+    for (int i = tid; i < DK * FS; i += kNT) {
+        const int c = i / FS, j = i - c * FS;
         dS[i] = a.dsT ? a.dsT[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
     }
+    // Matrix-core tiles: wave w takes row tile w / NCT, column tile w % NCT
+    // (a lane's column: 16 (w % NCT) + lane % 16).
+    const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
+    const int R = 16 * (wave / NCT), col = 16 * (wave % NCT) + li;
     for (int ch = a.nch - 1; ch >= 0; --ch) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();
         float* dck = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
-        for (int i = tid; i < DK * kSl; i += kNT) {
-            const int c = i / kSl, j = i - c * kSl;
+        const float* hq = a.ws + W.hq + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+        for (int i = tid; i < DK * FS; i += kNT) {
+            const int c = i / FS, j = i - c * FS;
             dck[static_cast<size_t>(c) * a.DV + j0 + j] = dS[i];
+            Hq[i] = hq[static_cast<size_t>(c) * a.DV + j0 + j];
         }
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, Q0, eE, Bs);
-        for (int i = tid; i < kC * kC; i += kNT) {
-            Ps[(i >> 6) * kTP + (i & 63)] = im[iP + i];
-            Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
-        }
-        for (int i = tid; i < kC * kSl; i += kNT) {
-            const int t = i / kSl, j = i - t * kSl;
+        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, nullptr, eE, Bs);
+        for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
+        for (int i = tid; i < kC * FS; i += kNT) {
+            const int t = i / FS, j = i - t * FS;
             const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
             Xs[i] = t < n ? a.ws[W.xr + r * a.DV + j0 + j] : 0.f;
-            Os[i] = t < n ? ld(dO + r * a.DV + j0 + j) : 0.f;
+            Pd[i] = t < n ? a.ws[W.pd + r * a.DV + j0 + j] : 0.f;
         }
         __syncthreads();
-        // Matrix-core phases (wave w: 16-row tile of a product; li = the
-        // slice's value column).  U = Tinv diag(beta) Xr on waves 0-3,
-        // dU = scale P^T dO + Kt dS_end on waves 4-7 (Tinv, P zero above
-        // their diagonals).
-        const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
-        if (wave < 4) {
-            const int R = 16 * wave;
+        // U = Tinv diag(beta) Xr (Tinv zero above its diagonal) on the first
+        // 4 NCT waves; dU = Pd + Kt dS_end on the next 4 NCT.
+        if (wave < 4 * NCT) {
             const f32x4 acc = tile_product(0, R + 16, [&](int k) { return Ti[(R + li) * kTP + k]; },
-                                           [&](int k) { return Bs[k] * Xs[k * kSl + li]; });
+                                           [&](int k) { return Bs[k] * Xs[k * FS + col]; });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Us[(R + 4 * l4 + r) * kSl + li] = acc[r];
-        } else if (wave < 8) {
-            const int R = 16 * (wave - 4);
-            const f32x4 ap = tile_product(R, kC, [&](int k) { return Ps[k * kTP + R + li]; },
-                                          [&](int k) { return Os[k * kSl + li]; });
-            const f32x4 ak = tile_product(0, DK, [&](int k) { return Kt[(R + li) * KP + k]; },
-                                          [&](int k) { return dS[k * kSl + li]; });
+            for (int r = 0; r < 4; ++r) Us[(R + 4 * l4 + r) * FS + col] = acc[r];
+        } else if (wave < 8 * NCT) {
+            const int R2 = R - 64;
+            const f32x4 ak = tile_product(0, DK, [&](int k) { return Kt[(R2 + li) * KP + k]; },
+                                          [&](int k) { return dS[k * FS + col]; });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dU[(R + 4 * l4 + r) * kSl + li] = a.scale * ap[r] + ak[r];
+            for (int r = 0; r < 4; ++r) {
+                const int t = R2 + 4 * l4 + r;
+                dU[t * FS + col] = Pd[t * FS + col] + ak[r];
+            }
         }
         __syncthreads();
         // dX = Tinv^T dU, kept in registers until every tile has read dU
         f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
-        if (wave < 4) {
-            const int R = 16 * wave;
+        if (wave < 4 * NCT)
             xacc = tile_product(R, kC, [&](int k) { return Ti[k * kTP + R + li]; },
-                                [&](int k) { return dU[k * kSl + li]; });
-        }
+                                [&](int k) { return dU[k * FS + col]; });
         __syncthreads();
-        if (wave < 4) {
+        if (wave < 4 * NCT) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dU[(16 * wave + 4 * l4 + r) * kSl + li] = xacc[r];
+            for (int r = 0; r < 4; ++r) dU[(R + 4 * l4 + r) * FS + col] = xacc[r];
         }
         __syncthreads();
         float* dX = dU;
-        for (int i = tid; i < kC * kSl; i += kNT) {
-            const int t = i / kSl, j = i - t * kSl;
+        for (int i = tid; i < kC * FS; i += kNT) {
+            const int t = i / FS, j = i - t * FS;
             if (t < n) {
                 const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
                 Elem<InT>::store(dv + r * a.DV + j0 + j, Bs[t] * dX[i]);
@@ -507,30 +569,27 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
         }
         if (tid < kC) {  // this slice's part of sum_j Xr dX
             float acc = 0.f;
-            for (int j = 0; j < kSl; ++j) acc += Xs[tid * kSl + j] * dX[tid * kSl + j];
+            for (int j = 0; j < FS; ++j) acc += Xs[tid * FS + j] * dX[tid * FS + j];
             if (tid < n) {
                 const size_t tok = (static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h;
                 a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok] = acc;
             }
         }
-        // dS <- eE dS + scale Q0^T dO - K0^T diag(beta) dX  (wave w: rows c of tile w)
-        if (wave < DK / 16) {
-            const int R = 16 * wave;
-            const f32x4 aq = tile_product(0, kC, [&](int k) { return Q0[k * KP + R + li]; },
-                                          [&](int k) { return Os[k * kSl + li]; });
+        // dS <- eE dS + Hq - K0^T diag(beta) dX
+        if (R < DK) {
             const f32x4 ak = tile_product(0, kC, [&](int k) { return K0[k * KP + R + li]; },
-                                          [&](int k) { return Bs[k] * dX[k * kSl + li]; });
+                                          [&](int k) { return Bs[k] * dX[k * FS + col]; });
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int c = R + 4 * l4 + r;
-                dS[c * kSl + li] = eE[c] * dS[c * kSl + li] + a.scale * aq[r] - ak[r];
+                dS[c * FS + col] = eE[c] * dS[c * FS + col] + Hq[c * FS + col] - ak[r];
             }
         }
     }
     __syncthreads();
     if (a.ds0) {
-        for (int i = tid; i < DK * kSl; i += kNT) {
-            const int c = i / kSl, j = i - c * kSl;
+        for (int i = tid; i < DK * FS; i += kNT) {
+            const int c = i / FS, j = i - c * FS;
             a.ds0[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] = dS[i];
         }
     }
@@ -838,8 +897,7 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     }
     if (tid < n) {
         float db = dB[tid];
-        const int nsl = a.DV / kSl;
-        for (int sl = 0; sl < nsl; ++sl) db += a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok(tid)];
+        for (int sl = 0; sl < a.nsl_chain; ++sl) db += a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok(tid)];
         a.dbeta[tok(tid)] = db;
     }
 }
@@ -848,8 +906,10 @@ template <int DK, bool KDA>
 constexpr int prep_lds() { return 4 * (2 * kC * (DK + 1) + kC * ((KDA ? DK : 1) + 1) + 2 * kC * kTP + kC); }
 template <int DK, int FS>
 constexpr int fwd_lds() { return 4 * (2 * kC * (DK + 1) + kC * kTP + DK * FS + 2 * kC * FS + DK + kC); }
+template <int DK, int FS>
+constexpr int chain_lds() { return 4 * (2 * kC * (DK + 1) + kC * kTP + 2 * DK * FS + 4 * kC * FS + DK + kC); }
 template <int DK>
-constexpr int chain_lds() { return 4 * (3 * kC * (DK + 1) + 2 * kC * kTP + DK * kSl + 4 * kC * kSl + DK + kC); }
+constexpr int dout_lds() { return 4 * (kC * (DK + 1) + kC * kTP + kC * 65); }
 template <int DK, bool KDA>
 constexpr int local_lds() {
     constexpr int SP = 17;
@@ -858,9 +918,10 @@ constexpr int local_lds() {
 }
 
 template <int DK, bool KDA, typename InT>
-hipError_t run(const Args& a, hipStream_t s) {
-    static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK>() <= 160 * 1024 &&
-                  prep_lds<DK, KDA>() <= 160 * 1024 && fwd_lds<DK, 32>() <= 160 * 1024, "LDS budget");
+hipError_t run(Args a, hipStream_t s) {
+    static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK, 32>() <= 160 * 1024 &&
+                  prep_lds<DK, KDA>() <= 160 * 1024 && fwd_lds<DK, 32>() <= 160 * 1024 &&
+                  dout_lds<DK>() <= 160 * 1024, "LDS budget");
     auto set = [](const void* f, int bytes) {
         return bytes > 64 * 1024 ? hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
                                  : hipSuccess;
@@ -868,26 +929,33 @@ hipError_t run(const Args& a, hipStream_t s) {
     hipError_t e;
     const unsigned heads8 = static_cast<unsigned>((a.B * a.H + 7) / 8 * 8);  // slice grids: whole groups of 8 heads
     const unsigned per_chunk = static_cast<unsigned>(a.B * a.H * a.nch);
-    const unsigned per_slice = heads8 * static_cast<unsigned>(a.DV / kSl);
-    // the forward chain's 32-column slices, when they still give every CU a workgroup
+    // the chains take 32-column slices when that still puts a workgroup on every CU
     const bool wide = a.DV >= 32 && static_cast<long long>(a.B) * a.H * (a.DV / 32) >= 256;
+    const int FSW = wide ? 32 : 16;
+    a.nsl_chain = a.DV / FSW;
+    const unsigned per_slice = heads8 * static_cast<unsigned>(a.DV / FSW);
     const void* fwd = wide ? reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 32>)
                            : reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 16>);
-    const int fwd_bytes = wide ? fwd_lds<DK, 32>() : fwd_lds<DK, 16>();
+    const void* chain = wide ? reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT, 32>)
+                             : reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT, 16>);
     if ((e = set(reinterpret_cast<const void*>(bwd_prep<DK, KDA, InT>), prep_lds<DK, KDA>())) != hipSuccess) return e;
-    if ((e = set(fwd, fwd_bytes)) != hipSuccess) return e;
-    if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT>), chain_lds<DK>())) != hipSuccess) return e;
+    if ((e = set(reinterpret_cast<const void*>(bwd_dout<DK, KDA, InT>), dout_lds<DK>())) != hipSuccess) return e;
+    if ((e = set(fwd, wide ? fwd_lds<DK, 32>() : fwd_lds<DK, 16>())) != hipSuccess) return e;
+    if ((e = set(chain, wide ? chain_lds<DK, 32>() : chain_lds<DK, 16>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_local<DK, KDA, InT>), local_lds<DK, KDA>())) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (prep_lds<DK, KDA>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dout<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (dout_lds<DK>()), s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (wide) {
-        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 32>), dim3(heads8 * static_cast<unsigned>(a.DV / 32)), dim3(kNT),
-                           (fwd_lds<DK, 32>()), s, a);
+        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 32>), dim3(per_slice), dim3(kNT), (fwd_lds<DK, 32>()), s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_chain<DK, KDA, InT, 32>), dim3(per_slice), dim3(kNT), (chain_lds<DK, 32>()), s, a);
     } else {
         hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 16>), dim3(per_slice), dim3(kNT), (fwd_lds<DK, 16>()), s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_chain<DK, KDA, InT, 16>), dim3(per_slice), dim3(kNT), (chain_lds<DK, 16>()), s, a);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chain<DK, KDA, InT>), dim3(per_slice), dim3(kNT), chain_lds<DK>(), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_local<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (local_lds<DK, KDA>()), s, a);
     return hipGetLastError();
