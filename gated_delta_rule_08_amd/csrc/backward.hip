@@ -314,18 +314,17 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
     for (int i = tid; i < kC * kC; i += kNT) img[iT + i] = Tl[(i >> 6) * kTP + (i & 63)];
 }
 
-// The factored rows, eE and beta of one chunk from its image (all threads,
-// coalesced).  Q0 is skipped when null.
+// The factored rows K0 = k e0 and Kt = k ek, eE and beta of one chunk, from
+// its image (all threads, coalesced).
 template <int DK>
 __device__ __forceinline__ void load_factors(const Args& a, const float* im, int b, int h, int t0, int n,
-                                             float* K0, float* Kt, float* Q0, float* eE, float* Bs) {
+                                             float* K0, float* Kt, float* eE, float* Bs) {
     constexpr int KP = DK + 1;
     const int tid = threadIdx.x;
     for (int i = tid; i < kC * DK; i += kNT) {
         const int t = i / DK, c = i - t * DK;
         K0[t * KP + c] = im[iK0 + i];
         Kt[t * KP + c] = im[iK0 + kC * DK + i];
-        if (Q0) Q0[t * KP + c] = im[iK0 + 2 * kC * DK + i];
     }
     if (tid < DK) eE[tid] = im[iK0 + 3 * kC * DK + tid];
     if (tid < kC) Bs[tid] = tid < n ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
@@ -375,7 +374,7 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
             ck[static_cast<size_t>(c) * a.DV + j0 + j] = Ss[i];
         }
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, nullptr, eE, Bs);
+        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, eE, Bs);
         for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
         __syncthreads();
         // Xr = V - K0 S
@@ -519,7 +518,7 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
             Hq[i] = hq[static_cast<size_t>(c) * a.DV + j0 + j];
         }
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, nullptr, eE, Bs);
+        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, eE, Bs);
         for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
         for (int i = tid; i < kC * FS; i += kNT) {
             const int t = i / FS, j = i - t * FS;
