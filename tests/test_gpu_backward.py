@@ -187,3 +187,52 @@ def test_backward_many_heads_wide_slices(gate, dk, dv):
         for key in ("dq", "dk", "dv", "dalpha", "dbeta"):
             assert_close(got[key][b:b + 1, :, h:h + 1], ref[key], TOL["f32"], "%s[%d,%d]" % (key, b, h))
         assert_close(got["ds0"][b:b + 1, h:h + 1], ref["ds0"], TOL["f32"], "ds0[%d,%d]" % (b, h))
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_backward_graph_replays_match_eager(gate):
+    """The backward (five launches, workspace passed in) captured in a HIP
+    graph and replayed several times with eager work in between: every replay
+    matches an eager call (bitwise where the kernels are deterministic; dalpha
+    and dbeta sum a few terms with LDS atomics, so to 1e-6 of their scale)."""
+    inp, do, dst = _case(gate, "bf16", B=2, T=150, H=4, dk=64, dv=64, seed=16)
+    d = {key: to_dev(val, "bf16" if key in ("q", "k", "v") else "f32") for key, val in inp.items()}
+    g_o, g_st = to_dev(do, "bf16"), to_dev(dst, "f32")
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[-1]
+    need = gdr.gdr_chunk_backward_workspace_bytes(gate, torch.bfloat16, B, T, H, dk, dv)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def outputs():
+        return [torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
+                torch.empty_like(d["alpha"]), torch.empty_like(d["beta"]),
+                torch.empty(B, H, dk, dv, device="cuda")]
+
+    def call(out):
+        gdr.gdr_chunk_backward(gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["s0"], g_o, g_st,
+                               *out, workspace=ws)
+
+    og, oe = outputs(), outputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(outputs())
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(og)
+    announce("backward %s graph replays" % gate)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        call(oe)
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(og, oe)):
+            if i in (3, 4):
+                scale = float(y.abs().max())
+                assert float((x - y).abs().max()) <= 1e-6 * max(scale, 1e-30), (rep, i)
+            else:
+                assert torch.equal(x, y), (rep, i)
+        junk = torch.randn(4096, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del junk
