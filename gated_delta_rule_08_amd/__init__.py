@@ -21,6 +21,7 @@ __all__ = [
     "gdr_chunk_prefill_varlen_workspace_bytes", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
     "gdr_abi_version", "EXPORTED_SYMBOLS", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
     "PRO_L2NORM_QK", "PRO_SIGMOID", "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
+    "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,7 @@ _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 PRO_L2NORM_QK = 1
 PRO_SIGMOID = 2
 EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
+                    "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex",
                     "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
                     "gdr_decode_multi", "gdr_chunk_prefill",
                     "gdr_chunk_prefill_varlen", "gdr_chunk_prefill_varlen_workspace_bytes",
@@ -70,6 +72,10 @@ def load_library():
     lib.gdr_chunk_backward.restype = i
     lib.gdr_chunk_backward_workspace_bytes.argtypes = [i] * 8
     lib.gdr_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdr_decode_multi_ex.argtypes = [i] * 8 + [f] + [vp] * 9
+    lib.gdr_decode_multi_ex.restype = i
+    lib.gdr_chunk_prefill_varlen_ex.argtypes = [i] * 10 + [f] + [vp] * 9 + [i, vp, vp, ctypes.c_size_t, vp]
+    lib.gdr_chunk_prefill_varlen_ex.restype = i
     lib.gdr_decode_multi.argtypes = [i] * 7 + [f] + [vp] * 9
     lib.gdr_decode_multi.restype = i
     lib.gdr_chunk_prefill.argtypes = [i] * 8 + [f] + [vp] * 9 + [ctypes.c_size_t, vp]
@@ -169,6 +175,13 @@ def _decode_step(flags, gate, q, k, v, alpha, beta, state, o, scale, stream):
                                       *ptrs))
 
 
+def gdr_decode_multi_ex(gate: str, q, k, v, alpha, beta, state, o, states=None, flags: int = 0,
+                        scale: float = 1.0, stream=None) -> None:
+    """:func:`gdr_decode_multi` with an input prologue (``flags`` as in
+    :func:`gdr_decode_step_ex`), applied to every token."""
+    _decode_multi(int(flags), gate, q, k, v, alpha, beta, state, o, states, scale, stream)
+
+
 def gdr_decode_multi(gate: str, q, k, v, alpha, beta, state, o, states=None,
                      scale: float = 1.0, stream=None) -> None:
     """T decode steps per head (the verify step of speculative decoding).
@@ -178,6 +191,10 @@ def gdr_decode_multi(gate: str, q, k, v, alpha, beta, state, o, states=None,
     read as S_0 and overwritten with S_T.  ``states`` (optional, fp32
     [B,T,H,dk,dv]) receives the state after every token.  T <= 64.
     """
+    _decode_multi(None, gate, q, k, v, alpha, beta, state, o, states, scale, stream)
+
+
+def _decode_multi(flags, gate, q, k, v, alpha, beta, state, o, states, scale, stream):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape != (B, T, H, dv) or o.shape != (B, T, H, dv):
@@ -193,9 +210,13 @@ def gdr_decode_multi(gate: str, q, k, v, alpha, beta, state, o, states=None,
     if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
         raise ValueError("alpha and beta must be fp32")
     _same_device(q, k, v, alpha, beta, state, o, states)
-    _check(load_library().gdr_decode_multi(
-        GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
-        _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _ptr(states), _stream(stream)))
+    lib = load_library()
+    rest = (B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+            _ptr(state), _ptr(o), _ptr(states), _stream(stream))
+    if flags is None:
+        _check(lib.gdr_decode_multi(GATES[gate], _DTYPES[q.dtype], *rest))
+    else:
+        _check(lib.gdr_decode_multi_ex(GATES[gate], _DTYPES[q.dtype], flags, *rest))
 
 
 def gdr_chunk_prefill_workspace_bytes(gate: str, dtype, B: int, T: int, H: int, dk: int,
@@ -264,6 +285,16 @@ def gdr_chunk_prefill_varlen_workspace_bytes(gate: str, dtype, N: int, max_T: in
         GATES[gate], _DTYPES[dtype], N, max_T, H, dk, dv, chunk))
 
 
+def gdr_chunk_prefill_varlen_ex(gate: str, q, k, v, alpha, beta, cu_seqlens, state_slots, states,
+                                o, has_state=None, max_seqlen: Optional[int] = None, flags: int = 0,
+                                scale: float = 1.0, workspace=None, chunk: int = CHUNK,
+                                stream=None) -> None:
+    """:func:`gdr_chunk_prefill_varlen` with an input prologue (``flags`` as
+    in :func:`gdr_chunk_prefill_ex`)."""
+    _prefill_varlen(int(flags), gate, q, k, v, alpha, beta, cu_seqlens, state_slots, states, o,
+                    has_state, max_seqlen, scale, workspace, chunk, stream)
+
+
 def gdr_chunk_prefill_varlen(gate: str, q, k, v, alpha, beta, cu_seqlens, state_slots, states, o,
                              has_state=None, max_seqlen: Optional[int] = None, scale: float = 1.0,
                              workspace=None, chunk: int = CHUNK, stream=None) -> None:
@@ -276,6 +307,12 @@ def gdr_chunk_prefill_varlen(gate: str, q, k, v, alpha, beta, cu_seqlens, state_
     place.  max_seqlen bounds every sequence length; if None it is read from
     cu_seqlens (one device-to-host copy).
     """
+    _prefill_varlen(None, gate, q, k, v, alpha, beta, cu_seqlens, state_slots, states, o,
+                    has_state, max_seqlen, scale, workspace, chunk, stream)
+
+
+def _prefill_varlen(flags, gate, q, k, v, alpha, beta, cu_seqlens, state_slots, states, o,
+                    has_state, max_seqlen, scale, workspace, chunk, stream):
     total_T, H, dk = q.shape
     dv = v.shape[-1]
     N = cu_seqlens.numel() - 1
@@ -303,11 +340,14 @@ def gdr_chunk_prefill_varlen(gate: str, q, k, v, alpha, beta, cu_seqlens, state_
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().gdr_chunk_prefill_varlen(
-        GATES[gate], _DTYPES[q.dtype], N, total_T, int(max_seqlen), H, dk, dv, chunk, float(scale),
-        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), _ptr(state_slots),
-        _ptr(has_state), _ptr(states), states.shape[0], _ptr(o), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+    lib = load_library()
+    rest = (N, total_T, int(max_seqlen), H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k), _ptr(v),
+            _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), _ptr(state_slots), _ptr(has_state),
+            _ptr(states), states.shape[0], _ptr(o), _ptr(workspace), ws_bytes, _stream(stream))
+    if flags is None:
+        _check(lib.gdr_chunk_prefill_varlen(GATES[gate], _DTYPES[q.dtype], *rest))
+    else:
+        _check(lib.gdr_chunk_prefill_varlen_ex(GATES[gate], _DTYPES[q.dtype], flags, *rest))
 
 
 def gdr_chunk_backward_workspace_bytes(gate: str, dtype, B: int, T: int, H: int, dk: int, dv: int,

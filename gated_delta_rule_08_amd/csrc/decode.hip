@@ -227,7 +227,7 @@ template <int DK, int DV, typename InT, bool KDA, bool SAVE>
 __global__ __launch_bounds__(256) void decode_multi_kernel(
     int n_units, int T, int H, float scale, const InT* __restrict__ q, const InT* __restrict__ k,
     const InT* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
-    float* __restrict__ state, InT* __restrict__ o, float* __restrict__ states) {
+    float* __restrict__ state, InT* __restrict__ o, float* __restrict__ states, int pro) {
     constexpr int COLS = DV < 32 ? DV : 32;
     constexpr int NSLICE = DV / COLS;
     constexpr int LPR = COLS / 4;
@@ -272,10 +272,16 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
         x.b = beta[tok];
         x.vv = load4<InT>(v + tok * DV + col);
     };
+    const bool sig = (pro & GDR_PRO_SIGMOID) != 0, nrm = (pro & GDR_PRO_L2NORM_QK) != 0;
     In cur, nxt;
     load_in(0, cur);
     for (int t = 0; t < T; ++t) {
         load_in(t + 1 < T ? t + 1 : t, nxt);  // the next token's inputs (the last one reloads)
+        if (sig) {  // gates given as logits
+            cur.b = sigmoid_f(cur.b);
+#pragma unroll
+            for (int m = 0; m < (KDA ? NI : 1); ++m) cur.av[m] = sigmoid_f(cur.av[m]);
+        }
         float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
         float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
         float kq = 0.f;
@@ -295,11 +301,31 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
             r2 += __shfl_xor(r2, off); r3 += __shfl_xor(r3, off);
             kq += __shfl_xor(kq, off);
         }
+        float ik = 1.f;  // raw q, k: rescale the sums as the decode step does
+        if (nrm) {
+            float kk = 0.f, qq = 0.f;
+#pragma unroll
+            for (int m = 0; m < NI; ++m) {
+                kk += cur.kv[m] * cur.kv[m];
+                qq += cur.qv[m] * cur.qv[m];
+            }
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1) {
+                kk += __shfl_xor(kk, off);
+                qq += __shfl_xor(qq, off);
+            }
+            ik = inv_norm(kk);
+            const float iq = inv_norm(qq);
+            p0 *= ik; p1 *= ik; p2 *= ik; p3 *= ik;
+            r0 *= iq; r1 *= iq; r2 *= iq; r3 *= iq;
+            kq *= ik * iq;
+        }
         const float e0 = cur.vv.x - p0, e1 = cur.vv.y - p1, e2 = cur.vv.z - p2, e3 = cur.vv.w - p3;
         const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
+        const float bn = cur.b * ik;
 #pragma unroll
         for (int m = 0; m < NI; ++m) {
-            const float bk = cur.b * cur.kv[m];
+            const float bk = bn * cur.kv[m];
             s[m].x += bk * e0; s[m].y += bk * e1; s[m].z += bk * e2; s[m].w += bk * e3;
             if constexpr (SAVE)
                 st_state(states + tok * DK * DV + col + static_cast<size_t>(m * RPI + rg) * DV, s[m]);
@@ -318,18 +344,18 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
 template <int DK, int DV, typename InT, bool KDA>
 hipError_t launch_multi(int n_units, int T, int H, float scale, const void* q, const void* k,
                         const void* v, const float* alpha, const float* beta, float* state,
-                        void* o, float* states, hipStream_t s) {
+                        void* o, float* states, hipStream_t s, int pro) {
     constexpr int COLS = DV < 32 ? DV : 32;
     const long long waves = static_cast<long long>(n_units) * (DV / COLS);
     const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
     if (states) {
         hipLaunchKernelGGL((decode_multi_kernel<DK, DV, InT, KDA, true>), dim3(blocks), dim3(256), 0, s,
                            n_units, T, H, scale, static_cast<const InT*>(q), static_cast<const InT*>(k),
-                           static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o), states);
+                           static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o), states, pro);
     } else {
         hipLaunchKernelGGL((decode_multi_kernel<DK, DV, InT, KDA, false>), dim3(blocks), dim3(256), 0, s,
                            n_units, T, H, scale, static_cast<const InT*>(q), static_cast<const InT*>(k),
-                           static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o), states);
+                           static_cast<const InT*>(v), alpha, beta, state, static_cast<InT*>(o), states, pro);
     }
     return hipGetLastError();
 }
@@ -337,24 +363,24 @@ hipError_t launch_multi(int n_units, int T, int H, float scale, const void* q, c
 template <int DK, int DV>
 hipError_t multi_type(int kda, int dtype, int n, int T, int H, float scale, const void* q,
                       const void* k, const void* v, const float* alpha, const float* beta,
-                      float* state, void* o, float* states, hipStream_t s) {
+                      float* state, void* o, float* states, hipStream_t s, int pro) {
     if (dtype == GDR_DTYPE_BF16) {
-        return kda ? launch_multi<DK, DV, bf16_t, true>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s)
-                   : launch_multi<DK, DV, bf16_t, false>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        return kda ? launch_multi<DK, DV, bf16_t, true>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro)
+                   : launch_multi<DK, DV, bf16_t, false>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
     }
-    return kda ? launch_multi<DK, DV, float, true>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s)
-               : launch_multi<DK, DV, float, false>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+    return kda ? launch_multi<DK, DV, float, true>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro)
+               : launch_multi<DK, DV, float, false>(n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
 }
 
 template <int DK>
 hipError_t multi_dv(int kda, int dtype, int dv, int n, int T, int H, float scale, const void* q,
                     const void* k, const void* v, const float* alpha, const float* beta,
-                    float* state, void* o, float* states, hipStream_t s) {
+                    float* state, void* o, float* states, hipStream_t s, int pro) {
     switch (dv) {
-        case 16: return multi_type<DK, 16>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
-        case 32: return multi_type<DK, 32>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
-        case 64: return multi_type<DK, 64>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
-        default: return multi_type<DK, 128>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        case 16: return multi_type<DK, 16>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
+        case 32: return multi_type<DK, 32>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
+        case 64: return multi_type<DK, 64>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
+        default: return multi_type<DK, 128>(kda, dtype, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
     }
 }
 
@@ -375,13 +401,13 @@ hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float
 hipError_t launch_decode_multi(int kda, int dtype, int B, int T, int H, int dk, int dv,
                                float scale, const void* q, const void* k, const void* v,
                                const float* alpha, const float* beta, float* state, void* o,
-                               float* states, hipStream_t s) {
+                               float* states, hipStream_t s, int pro) {
     const int n = B * H;
     switch (dk) {
-        case 16: return multi_dv<16>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
-        case 32: return multi_dv<32>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
-        case 64: return multi_dv<64>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
-        default: return multi_dv<128>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s);
+        case 16: return multi_dv<16>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
+        case 32: return multi_dv<32>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
+        case 64: return multi_dv<64>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
+        default: return multi_dv<128>(kda, dtype, dv, n, T, H, scale, q, k, v, alpha, beta, state, o, states, s, pro);
     }
 }
 

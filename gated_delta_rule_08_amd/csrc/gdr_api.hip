@@ -48,6 +48,12 @@ inline bool sizes_ok(long long B, long long T, long long H, long long dk, long l
 }
 
 inline bool flags_ok(int flags) { return (flags & ~(GDR_PRO_L2NORM_QK | GDR_PRO_SIGMOID)) == 0; }
+// The bf16 prefill schedules normalise q, k where the chunk-local products
+// are formed: the fused GDN kernel and the split KDA kernels.
+inline bool norm_supported(int flags, int gate, int dtype) {
+    return !(flags & GDR_PRO_L2NORM_QK) || dtype != GDR_DTYPE_BF16 ||
+           gdr::prefill_bf16_split(gate == GDR_GATE_KDA) == (gate == GDR_GATE_KDA);
+}
 
 int check_enums(int gate, int dtype) {
     if (gate != GDR_GATE_GDN && gate != GDR_GATE_KDA) return GDR_ERR_BAD_ENUM;
@@ -108,8 +114,17 @@ int gdr_decode_step_ex(int gate, int dtype, int flags, int B, int H, int dk, int
 int gdr_decode_multi(int gate, int dtype, int B, int T, int H, int dk, int dv, float scale,
                      const void* q, const void* k, const void* v, const float* alpha,
                      const float* beta, float* state, void* o, float* states, void* stream) {
+    return gdr_decode_multi_ex(gate, dtype, 0, B, T, H, dk, dv, scale, q, k, v, alpha, beta, state,
+                               o, states, stream);
+}
+
+int gdr_decode_multi_ex(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
+                        float scale, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, float* state, void* o,
+                        float* states, void* stream) {
     int st = check_enums(gate, dtype);
     if (st != GDR_OK) return st;
+    if (!flags_ok(flags)) return GDR_ERR_BAD_ENUM;
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || T > kMaxMultiTokens) return GDR_ERR_UNSUPPORTED;
     if (!sizes_ok(B, T, H, dk, dv) || static_cast<long long>(B) * T * H * dk * dv > (1LL << 40))
@@ -129,7 +144,8 @@ int gdr_decode_multi(int gate, int dtype, int B, int T, int H, int dk, int dv, f
         if (a0 < b0 + lb && b0 < a0 + la) return GDR_ERR_ALIAS;
     }
     hipError_t e = gdr::launch_decode_multi(kda, dtype, B, T, H, dk, dv, scale, q, k, v, alpha,
-                                            beta, state, o, states, static_cast<hipStream_t>(stream));
+                                            beta, state, o, states, static_cast<hipStream_t>(stream),
+                                            flags);
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
@@ -163,11 +179,7 @@ int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, in
     if (!flags_ok(flags)) return GDR_ERR_BAD_ENUM;
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
-    // the bf16 schedules normalise q, k where the chunk-local products are
-    // formed: the fused GDN kernel and the split KDA kernels
-    if ((flags & GDR_PRO_L2NORM_QK) && dtype == GDR_DTYPE_BF16 &&
-        gdr::prefill_bf16_split(gate == GDR_GATE_KDA) != (gate == GDR_GATE_KDA))
-        return GDR_ERR_UNSUPPORTED;
+    if (!norm_supported(flags, gate, dtype)) return GDR_ERR_UNSUPPORTED;
     if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
     const size_t need = gdr_chunk_prefill_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
@@ -217,10 +229,23 @@ int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T,
                              const int* cu_seqlens, const int* state_slots, const int* has_state,
                              float* states, int n_slots, void* o, void* workspace,
                              size_t workspace_bytes, void* stream) {
+    return gdr_chunk_prefill_varlen_ex(gate, dtype, 0, N, total_T, max_T, H, dk, dv, chunk, scale, q,
+                                       k, v, alpha, beta, cu_seqlens, state_slots, has_state, states,
+                                       n_slots, o, workspace, workspace_bytes, stream);
+}
+
+int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total_T, int max_T,
+                                int H, int dk, int dv, int chunk, float scale, const void* q,
+                                const void* k, const void* v, const float* alpha,
+                                const float* beta, const int* cu_seqlens, const int* state_slots,
+                                const int* has_state, float* states, int n_slots, void* o,
+                                void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_enums(gate, dtype);
     if (st != GDR_OK) return st;
+    if (!flags_ok(flags)) return GDR_ERR_BAD_ENUM;
     if (N < 0 || total_T < 0 || max_T < 0 || H < 0 || n_slots < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
+    if (!norm_supported(flags, gate, dtype)) return GDR_ERR_UNSUPPORTED;
     if (!sizes_ok(1, total_T, H, dk, dv) || !sizes_ok(N, max_T, H, dk, dv) ||
         !sizes_ok(n_slots, 1, H, dk, dv))
         return GDR_ERR_BAD_SHAPE;
@@ -242,6 +267,7 @@ int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T,
     vl.has = has_state;
     vl.n_slots = n_slots;
     vl.total = total_T;
+    vl.pro = flags;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == GDR_DTYPE_F32) {

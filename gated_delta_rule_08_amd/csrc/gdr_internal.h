@@ -73,7 +73,7 @@ hipError_t launch_decode(int kda, int dtype, int B, int H, int dk, int dv, float
 hipError_t launch_decode_multi(int kda, int dtype, int B, int T, int H, int dk, int dv,
                                float scale, const void* q, const void* k, const void* v,
                                const float* alpha, const float* beta, float* state, void* o,
-                               float* states, hipStream_t s);
+                               float* states, hipStream_t s, int pro = 0);
 
 hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, float scale,
                               const float* q, const float* k, const float* v,

@@ -143,6 +143,15 @@ int gdr_decode_multi(int gate, int dtype, int B, int T, int H, int dk, int dv, f
                      float* state, void* o, float* states, void* stream);
 
 /*
+ * gdr_decode_multi with an input prologue (flags: GDR_PRO_*), applied to
+ * every token.  flags == 0 is gdr_decode_multi exactly.
+ */
+int gdr_decode_multi_ex(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
+                        float scale, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        float* state, void* o, float* states, void* stream);
+
+/*
  * Chunked prefill of T tokens for B x H independent heads (the prompt pass
  * of the same recurrence), in chunks of `chunk` = 64 tokens; T need not be a
  * multiple of the chunk.
@@ -223,6 +232,19 @@ int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T,
                              const int* cu_seqlens, const int* state_slots, const int* has_state,
                              float* states, int n_slots, void* o,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdr_chunk_prefill_varlen with an input prologue (flags: GDR_PRO_*), with
+ * the same support as gdr_chunk_prefill_ex.  flags == 0 is
+ * gdr_chunk_prefill_varlen exactly.
+ */
+int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total_T, int max_T,
+                                int H, int dk, int dv, int chunk, float scale,
+                                const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const int* cu_seqlens, const int* state_slots,
+                                const int* has_state, float* states, int n_slots, void* o,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace gdr_chunk_prefill_varlen needs (0 when the arguments are
  * invalid or no scratch is needed). */

@@ -295,3 +295,23 @@ def test_backward_validation(lib):
     bad[8] = ctypes.c_void_p(0x10008)                         # grad_q misaligned
     assert bwd(ptrs=bad, ws=ws, ws_bytes=need) == MISAL
     assert bwd(B=0, ptrs=nul) == OK                           # empty batch: no-op
+
+
+def test_prologue_ex_variants_validation(lib, monkeypatch):
+    """The verify and packed variable-length calls take the same flags."""
+    p9 = [P[i] for i in range(9)]
+    assert lib.gdr_decode_multi_ex(0, 1, 4, 2, 3, 4, 128, 128, 1.0, *p9) == ENUM
+    assert lib.gdr_decode_multi_ex(0, 1, 3, 2, 65, 4, 128, 128, 1.0, *p9) == UNSUP
+    assert lib.gdr_decode_multi_ex(0, 1, 3, 2, 0, 4, 128, 128, 1.0, *([None] * 9)) == OK
+
+    def vl(flags, gate=0, dtype=1):
+        return lib.gdr_chunk_prefill_varlen_ex(gate, dtype, flags, 2, 100, 70, 3, 128, 128, 64, 1.0,
+                                               *([None] * 9), 4, None, None, 0, None)
+
+    assert vl(8) == ENUM
+    monkeypatch.setenv("GDR_PREFILL_PATH", "split")
+    assert vl(1) == UNSUP            # GDN normalises only in the fused kernel
+    monkeypatch.setenv("GDR_PREFILL_PATH", "fused")
+    assert vl(1, gate=1) == UNSUP    # KDA normalises only in the split kernels
+    monkeypatch.delenv("GDR_PREFILL_PATH")
+    assert vl(3) == NULL and vl(3, dtype=0) == NULL

@@ -203,3 +203,74 @@ def test_prefill_prologue_full_size(gate, name, heads):
         o_ref, s_ref = oracle.recurrent(q, k, sl(raw["v"]), a, bt, s0, scale=0.75)
         assert_close(o[b:b + 1, :, h:h + 1], o_ref, TOL["bf16"], "o[b=%d,h=%d]" % (b, h))
         assert_close(s[b:b + 1, h:h + 1], s_ref, TOL["bf16"], "S_T[b=%d,h=%d]" % (b, h))
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_multi_prologue_matches_stepped_oracle(gate, dtype):
+    """The verify step on raw inputs: every token's prologue, then the
+    float64 recurrence token by token; flags 0 is the plain call bitwise."""
+    w = _workload("decode", gate, dtype, 64, 64)
+    T = 5
+    raw = _raw(w, NORM | SIG, B=3, T=T, H=4, seed=19, zero_rows=True)
+    d = _dev(raw, dtype)
+    state = d["s0"].clone()
+    o = torch.empty(3, T, 4, 64, device="cuda", dtype=d["q"].dtype)
+    states = torch.empty(3, T, 4, 64, 64, device="cuda")
+    announce("decode_multi prologue %s %s" % (gate, dtype))
+    gdr.gdr_decode_multi_ex(gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], state, o, states,
+                            flags=NORM | SIG, scale=0.5)
+    torch.cuda.synchronize()
+    q, k, a, b = _reference_inputs(raw, NORM | SIG)
+    s = raw["s0"]
+    for t in range(T):
+        sl = slice(t, t + 1)
+        o_ref, s = oracle.recurrent(q[:, sl], k[:, sl], raw["v"][:, sl], a[:, sl], b[:, sl], s, scale=0.5)
+        assert_close(to_host64(o)[:, t], o_ref[:, 0], TOL[dtype], "o_%d" % t)
+        assert_close(to_host64(states)[:, t], s, TOL[dtype], "S_%d" % (t + 1))
+    assert_close(to_host64(state), s, TOL[dtype], "S_T")
+    # flags 0: bitwise the plain call
+    plain = _dev(synth.make_inputs(w, B=3, T=T, H=4, seed=19, s0="normal"), dtype)
+    s1, s2 = plain["s0"].clone(), plain["s0"].clone()
+    o1, o2 = torch.empty_like(o), torch.empty_like(o)
+    gdr.gdr_decode_multi(gate, plain["q"], plain["k"], plain["v"], plain["alpha"], plain["beta"], s1, o1)
+    gdr.gdr_decode_multi_ex(gate, plain["q"], plain["k"], plain["v"], plain["alpha"], plain["beta"], s2, o2,
+                            flags=0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_prefill_varlen_prologue_matches_oracle(gate):
+    """Packed prompts on raw inputs: each sequence against the float64
+    recurrence on its own prologue'd inputs, from its pool row."""
+    w = _workload("prefill", gate, "bf16", 64, 64)
+    lens, slots, has = [1, 70, 0, 130], [2, 0, 3, 1], [1, 0, 1, 1]
+    H = 3
+    seqs = [_raw(w, NORM | SIG, B=1, T=max(n, 1), H=H, seed=50 + i) for i, n in enumerate(lens)]
+    cat = lambda key: np.ascontiguousarray(np.concatenate([sq[key][0, :n] for sq, n in zip(seqs, lens)], axis=0))
+    packed = {key: cat(key) for key in ("q", "k", "v", "alpha", "beta")}
+    pool0 = (0.02 * np.random.default_rng(3).standard_normal((4, H, 64, 64))).astype(np.float32)
+    d = _dev(packed, "bf16")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    pool = torch.from_numpy(pool0.copy()).cuda()
+    o = torch.zeros(sum(lens), H, 64, device="cuda", dtype=torch.bfloat16)
+    announce("prefill varlen prologue %s" % gate)
+    gdr.gdr_chunk_prefill_varlen_ex(gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], cu,
+                                    torch.tensor(slots, dtype=torch.int32, device="cuda"), pool, o,
+                                    has_state=torch.tensor(has, dtype=torch.int32, device="cuda"),
+                                    flags=NORM | SIG)
+    torch.cuda.synchronize()
+    o, pool = to_host64(o), to_host64(pool)
+    off = np.concatenate([[0], np.cumsum(lens)])
+    for i, n in enumerate(lens):
+        r = slots[i]
+        if n == 0:
+            assert np.array_equal(pool[r], pool0[r])
+            continue
+        sl = slice(off[i], off[i + 1])
+        q, k, a, b = oracle.prologue(packed["q"][sl][None], packed["k"][sl][None], packed["alpha"][sl][None],
+                                     packed["beta"][sl][None])
+        o_ref, s_ref = oracle.recurrent(q, k, packed["v"][sl][None], a, b, pool0[r][None] if has[i] else None)
+        assert_close(o[sl], o_ref[0], TOL["bf16"], "o of sequence %d" % i)
+        assert_close(pool[r], s_ref[0], TOL["bf16"], "state of sequence %d" % i)
