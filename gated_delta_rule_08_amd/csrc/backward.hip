@@ -678,21 +678,43 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     const float* Dg = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
     // Contractions over the value columns, block by block:
     //   dQ0' = dO S^T, dK0' = dX S^T, dKt = U dS_end^T, dA' = dX U^T, dP' = dO U^T
+    // The next block's values are loaded into registers (each thread a fixed
+    // set of elements per array) while the current block is multiplied.
+    constexpr int NS = (DK * CB + kNT - 1) / kNT;   // S / dS_end elements per thread
+    static_assert(kC * CB == kNT, "one U, dX, dO element per thread");
+    float ps[NS], pd[NS], pu, px, po;
+    const int ut = tid / CB, uj = tid - (tid / CB) * CB;
+    auto fetch = [&](int jb) {
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const int i = tid + m * kNT;
+            const int c = i / CB, j = i - c * CB;
+            const bool ok = i < DK * CB;
+            ps[m] = ok ? Sg[static_cast<size_t>(c) * a.DV + jb + j] : 0.f;
+            pd[m] = ok ? Dg[static_cast<size_t>(c) * a.DV + jb + j] : 0.f;
+        }
+        const bool ok = ut < n;
+        const size_t r = tok(ut) * a.DV + jb + uj;
+        pu = ok ? a.ws[W.u + r] : 0.f;
+        px = ok ? a.ws[W.dx + r] : 0.f;
+        po = ok ? ld(dO + r) : 0.f;
+    };
+    fetch(0);
     for (int jb = 0; jb < a.DV; jb += CB) {
         __syncthreads();  // previous block consumed (first pass: staging above done)
-        for (int i = tid; i < DK * CB; i += kNT) {
-            const int c = i / CB, j = i - c * CB;
-            Sb[c * SP + j] = Sg[static_cast<size_t>(c) * a.DV + jb + j];
-            Db[c * SP + j] = Dg[static_cast<size_t>(c) * a.DV + jb + j];
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const int i = tid + m * kNT;
+            if (i < DK * CB) {
+                const int c = i / CB, j = i - c * CB;
+                Sb[c * SP + j] = ps[m];
+                Db[c * SP + j] = pd[m];
+            }
         }
-        for (int i = tid; i < kC * CB; i += kNT) {
-            const int t = i / CB, j = i - t * CB;
-            const bool ok = t < n;
-            const size_t r = tok(t) * a.DV + jb + j;
-            Ub[t * SP + j] = ok ? a.ws[W.u + r] : 0.f;
-            Xb[t * SP + j] = ok ? a.ws[W.dx + r] : 0.f;
-            Ob[t * SP + j] = ok ? ld(dO + r) : 0.f;
-        }
+        Ub[ut * SP + uj] = pu;
+        Xb[ut * SP + uj] = px;
+        Ob[ut * SP + uj] = po;
+        if (jb + CB < a.DV) fetch(jb + CB);
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < CB; kk += 4) {
