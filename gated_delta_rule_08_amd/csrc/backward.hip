@@ -365,6 +365,26 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
     // is 16 (w % NCT) + lane % 16.
     const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
     const int R = 16 * (wave / NCT), col = 16 * (wave % NCT) + li;
+    // The next chunk's image (K0, Kt, Tinv, eE) and beta are loaded into
+    // registers while the current chunk is computed.
+    constexpr int NKF = (kC * DK + kNT - 1) / kNT;
+    constexpr int NTF = kC * kC / kNT;
+    float fk0[NKF], fkt[NKF], fti[NTF], fee = 0.f, fb = 0.f;
+    auto fetch = [&](int ch) {
+        const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+#pragma unroll
+        for (int m = 0; m < NKF; ++m) {
+            const int i = tid + m * kNT;
+            fk0[m] = i < kC * DK ? im[iK0 + i] : 0.f;
+            fkt[m] = i < kC * DK ? im[iK0 + kC * DK + i] : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < NTF; ++m) fti[m] = im[iT + tid + m * kNT];
+        if (tid < DK) fee = im[iK0 + 3 * kC * DK + tid];
+        const int nn = min(kC, a.T - ch * kC);
+        if (tid < kC) fb = tid < nn ? a.beta[(static_cast<size_t>(b) * a.T + ch * kC + tid) * a.H + h] : 0.f;
+    };
+    fetch(0);
     for (int ch = 0; ch < a.nch; ++ch) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();  // the previous chunk is done with every buffer
@@ -373,9 +393,22 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
             const int c = i / FS, j = i - c * FS;
             ck[static_cast<size_t>(c) * a.DV + j0 + j] = Ss[i];
         }
-        const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, eE, Bs);
-        for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
+#pragma unroll
+        for (int m = 0; m < NKF; ++m) {
+            const int i = tid + m * kNT;
+            if (i < kC * DK) {
+                K0[(i / DK) * KP + i % DK] = fk0[m];
+                Kt[(i / DK) * KP + i % DK] = fkt[m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NTF; ++m) {
+            const int i = tid + m * kNT;
+            Ti[(i >> 6) * kTP + (i & 63)] = fti[m];
+        }
+        if (tid < DK) eE[tid] = fee;
+        if (tid < kC) Bs[tid] = fb;
+        if (ch + 1 < a.nch) fetch(ch + 1);
         __syncthreads();
         // Xr = V - K0 S
         if (R < kC) {
