@@ -540,6 +540,25 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
     // (a lane's column: 16 (w % NCT) + lane % 16).
     const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
     const int R = 16 * (wave / NCT), col = 16 * (wave % NCT) + li;
+    // At the narrow slice width the next (earlier) chunk's image rows K0, Kt
+    // and Tinv are loaded into registers while the current chunk is computed
+    // (at the wide width the registers have no room for them).
+    constexpr bool kPf = FS == 16;
+    constexpr int NKF = kPf ? (kC * DK + kNT - 1) / kNT : 1;
+    constexpr int NTF = kPf ? kC * kC / kNT : 1;
+    float fk0[NKF], fkt[NKF], fti[NTF];
+    auto fetch = [&](int ch) {
+        const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+#pragma unroll
+        for (int m = 0; m < NKF; ++m) {
+            const int i = tid + m * kNT;
+            fk0[m] = i < kC * DK ? im[iK0 + i] : 0.f;
+            fkt[m] = i < kC * DK ? im[iK0 + kC * DK + i] : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < NTF; ++m) fti[m] = im[iT + tid + m * kNT];
+    };
+    if constexpr (kPf) fetch(a.nch - 1);
     for (int ch = a.nch - 1; ch >= 0; --ch) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();
@@ -551,14 +570,34 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
             Hq[i] = hq[static_cast<size_t>(c) * a.DV + j0 + j];
         }
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-        load_factors<DK>(a, im, b, h, t0, n, K0, Kt, eE, Bs);
-        for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
+        if constexpr (kPf) {
+#pragma unroll
+            for (int m = 0; m < NKF; ++m) {
+                const int i = tid + m * kNT;
+                if (i < kC * DK) {
+                    K0[(i / DK) * KP + i % DK] = fk0[m];
+                    Kt[(i / DK) * KP + i % DK] = fkt[m];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NTF; ++m) {
+                const int i = tid + m * kNT;
+                Ti[(i >> 6) * kTP + (i & 63)] = fti[m];
+            }
+            if (tid < DK) eE[tid] = im[iK0 + 3 * kC * DK + tid];
+            if (tid < kC) Bs[tid] = tid < n ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
+        } else {
+            load_factors<DK>(a, im, b, h, t0, n, K0, Kt, eE, Bs);
+            for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
+        }
         for (int i = tid; i < kC * FS; i += kNT) {
             const int t = i / FS, j = i - t * FS;
             const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
             Xs[i] = t < n ? a.ws[W.xr + r * a.DV + j0 + j] : 0.f;
             Pd[i] = t < n ? a.ws[W.pd + r * a.DV + j0 + j] : 0.f;
         }
+        if constexpr (kPf)
+            if (ch > 0) fetch(ch - 1);
         __syncthreads();
         // U = Tinv diag(beta) Xr (Tinv zero above its diagonal) on the first
         // 4 NCT waves; dU = Pd + Kt dS_end on the next 4 NCT.
