@@ -85,6 +85,37 @@ __device__ __forceinline__ f32x4 tile_product(int k0, int k1, FA fa, FB fb) {
     return c0 + c1;
 }
 
+// Cross-lane sums and scans (every lane of the wave takes part).
+__device__ __forceinline__ float row16_sum(float v) {  // over the 16 lanes of a row
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+// Inclusive prefix (lanes <= l) and suffix (lanes >= l) sums over the wave.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(v, d);
+        if (l >= d) v += o;
+    }
+    return v;
+}
+__device__ __forceinline__ float wave_suffix_sum(float v) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_down(v, d);
+        if (l + d < 64) v += o;
+    }
+    return v;
+}
+
 // Per-chunk image (floats): Ahat, P, Tinv [64][64] each, then K0 = k e0,
 // Kt = k ek, Q0 = q e0 [64][dk] each, then eE [dk].
 enum { iA = 0, iP = kC * kC, iT = 2 * kC * kC, iK0 = 3 * kC * kC };
@@ -175,12 +206,11 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
     }
     if (tid < kC) Bs[tid] = tid < n ? a.beta[tok(tid)] : 0.f;
     __syncthreads();
-    if (tid < GW) {  // cumulative log-gate (padded tokens add nothing)
-        float acc = 0.f;
-        for (int t = 0; t < kC; ++t) {
-            acc += Gs[t * GP + tid];
-            Gs[t * GP + tid] = acc;
-        }
+    // cumulative log-gate (padded tokens add nothing): a wave per channel,
+    // lane = token
+    for (int c = tid >> 6; c < GW; c += kNT / 64) {
+        const int t = tid & 63;
+        Gs[t * GP + c] = wave_prefix_sum(Gs[t * GP + c]);
     }
     __syncthreads();
     float* img = a.ws + Ws(a.B, a.T, a.H, DK, a.DV).img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
@@ -728,13 +758,11 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
     for (int i = tid; i < kC * kC; i += kNT) Ah[(i >> 6) * kTP + (i & 63)] = im[iA + i];
     __syncthreads();
-    if (tid < GW) {  // cumulative log-gate in place
-        float acc = 0.f;
-        for (int t = 0; t < kC; ++t) {
-            acc += Gs[t * GP + tid];
-            Gs[t * GP + tid] = acc;
-        }
-        eE[tid] = __expf(acc);  // acc = G_end
+    for (int c = tid >> 6; c < GW; c += kNT / 64) {  // cumulative log-gate in place
+        const int t = tid & 63;
+        const float g = wave_prefix_sum(Gs[t * GP + c]);
+        Gs[t * GP + c] = g;
+        if (t == kC - 1) eE[c] = __expf(g);  // G_end
     }
 
     const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
@@ -818,11 +846,14 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         const float dA = s2 < t ? -aA[r] : 0.f;
         Mm[t * kTP + s2] = Bs[t] * dA;
         Nm[t * kTP + s2] = s2 <= t ? a.scale * aP[r] : 0.f;
-        atomicAdd(&dB[t], dA * Ah[t * kTP + s2]);
+        const float db = row16_sum(dA * Ah[t * kTP + s2]);  // over the row's 16 s
+        if (li == 0) atomicAdd(&dB[t], db);
     }
-    if (tid < DK) {
-        if (KDA) dGe[tid] = eE[tid] * ge;
-        else atomicAdd(&dGe[0], eE[0] * ge);
+    if constexpr (KDA) {
+        if (tid < DK) dGe[tid] = eE[tid] * ge;
+    } else if (tid < ((DK + 63) & ~63)) {  // whole waves; ge = 0 beyond DK
+        const float sg = wave_sum(ge);
+        if ((tid & 63) == 0) atomicAdd(&dGe[0], eE[0] * sg);
     }
     __syncthreads();
     // The four gate-weighted sums of the lane's outputs:
@@ -923,6 +954,7 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     }
     // gradients of the lane's outputs
     float dq[NCT][4], dk[NCT][4], dg[NCT][4];
+    float ge_all = 0.f;  // GDN: the lane's part of sum_t dKt k ek (a scalar G_end)
 #pragma unroll
     for (int i = 0; i < NCT; ++i) {
 #pragma unroll
@@ -939,8 +971,13 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
             dk[i][r] = dK0 * e0 + dKt * ek + a1[i][r] + a3[i][r] + a4[i][r];
             dg[i][r] = qv * (dQ0 * e0 + a2[i][r]) + kv * (dK0 * e0 - dKt * ek + a1[i][r] - a3[i][r] - a4[i][r]);
             // G_end = G_{n-1}: its gradient through Kt (and, above, eE)
-            atomicAdd(&dGe[KDA ? c : 0], dKt * kv * ek);
+            if constexpr (KDA) atomicAdd(&dGe[c], dKt * kv * ek);
+            else ge_all += dKt * kv * ek;
         }
+    }
+    if constexpr (!KDA) {
+        const float sg = wave_sum(ge_all);
+        if ((tid & 63) == 0) atomicAdd(&dGe[0], sg);
     }
     __syncthreads();  // k, q no longer read: dG goes where k was
     float* dG = Ks;
@@ -951,7 +988,16 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         for (int r = 0; r < 4; ++r) {
             const int t = T + 4 * l4 + r;
             if constexpr (KDA) dG[t * KP + ct(i) + li] = dg[i][r];
-            else atomicAdd(&dGt[t], dg[i][r]);
+        }
+    }
+    if constexpr (!KDA) {  // dG_t = sum over channels: the lane's tiles, then the row's 16 lanes
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float sg = 0.f;
+#pragma unroll
+            for (int i = 0; i < NCT; ++i) sg += dg[i][r];
+            sg = row16_sum(sg);
+            if (li == 0) atomicAdd(&dGt[T + 4 * l4 + r], sg);
         }
     }
     InT* dqo = static_cast<InT*>(a.dq);
@@ -973,13 +1019,10 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     // the last token); dalpha = dlog alpha / alpha unless the floor is active.
     float* dL = KDA ? dG : dGt;  // dlog alpha, in place
     constexpr int LP = KDA ? KP : 1;
-    if (tid < GW) {
-        const int c = tid;
-        float acc = dGe[c];
-        for (int t = n - 1; t >= 0; --t) {
-            acc += dL[t * LP + c];
-            dL[t * LP + c] = acc;
-        }
+    for (int c = tid >> 6; c < GW; c += kNT / 64) {  // a wave per channel, lane = token
+        const int t = tid & 63;
+        const float x = wave_suffix_sum(t < n ? dL[t * LP + c] : 0.f);
+        if (t < n) dL[t * LP + c] = x + dGe[c];
     }
     __syncthreads();
     for (int i = tid; i < n * GW; i += kNT) {
