@@ -897,8 +897,9 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         //   t <= T+15 < r:     E = exp(G_r - G_{T+15}) exp(G_{T+15} - G_t),
         // so the parts of a1, a2 (s before the row block) and a3, a4 (r after
         // it) are matrix products with the second factor in the B operand and
-        // the first applied to the output; the row block's own 16 tokens run
-        // on the vector ALUs with exact exponentials.
+        // the first applied to the output; inside the row block the same holds
+        // between its 4-token groups, and only pairs within one group take
+        // exact exponentials on the vector ALUs.
 #pragma unroll
         for (int i = 0; i < NCT; ++i) {
             if (!has_ct(i)) continue;
@@ -935,19 +936,71 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
                     a4[i][r] = c4[r] * f;
                 }
             }
-            // the row block itself (masks come from the zeros of M and N; the
-            // exponents are clamped at 0 where the products vanish)
-            for (int s2 = T; s2 < T + 16; ++s2) {
-                const float ks = Ks[s2 * KP + c], qs = Qs[s2 * KP + c], gs = Gs[s2 * GP + c];
+            // The row block itself, in 4-token groups (the lane's four rows
+            // t = T + 4 l4 + r are group l4).  Pairs in different groups factor
+            // through a group boundary as above, a K = 4 matrix product per
+            // group: s in group j < group of t through b = T + 4j + 3, r in
+            // group j > group of t through b = T + 4j - 1; rows outside the
+            // valid groups get zero A operands.
+#pragma nounroll
+            for (int j = 0; j < 3; ++j) {
+                const int s2 = T + 4 * j + l4, bb = T + 4 * j + 3;
+                const float gb = Gs[bb * GP + c];
+                const float bk = Ks[s2 * KP + c] * __expf(gb - Gs[s2 * GP + c]);
+                const bool on = li > 4 * j + 3;
+                const f32x4 d1 = mma4(on ? Mm[(T + li) * kTP + s2] : 0.f, bk, z4);
+                const f32x4 d2 = mma4(on ? Nm[(T + li) * kTP + s2] : 0.f, bk, z4);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = T + 4 * l4 + r;
-                    const float gt = Gs[t * GP + c];
-                    const float e1 = __expf(fminf(gt - gs, 0.f)), e2 = __expf(fminf(gs - gt, 0.f));
-                    a1[i][r] += Mm[t * kTP + s2] * ks * e1;
-                    a2[i][r] += Nm[t * kTP + s2] * ks * e1;
-                    a3[i][r] += Mm[s2 * kTP + t] * ks * e2;
-                    a4[i][r] += Nm[s2 * kTP + t] * qs * e2;
+                    const float f = __expf(fminf(Gs[(T + 4 * l4 + r) * GP + c] - gb, 0.f));
+                    a1[i][r] += d1[r] * f;
+                    a2[i][r] += d2[r] * f;
+                }
+            }
+#pragma nounroll
+            for (int j = 1; j < 4; ++j) {
+                const int r2 = T + 4 * j + l4, bb = T + 4 * j - 1;
+                const float gb = Gs[bb * GP + c];
+                const float e = __expf(Gs[r2 * GP + c] - gb);
+                const bool on = li < 4 * j;
+                const f32x4 d3 = mma4(on ? Mm[r2 * kTP + T + li] : 0.f, Ks[r2 * KP + c] * e, z4);
+                const f32x4 d4 = mma4(on ? Nm[r2 * kTP + T + li] : 0.f, Qs[r2 * KP + c] * e, z4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float f = __expf(fminf(gb - Gs[(T + 4 * l4 + r) * GP + c], 0.f));
+                    a3[i][r] += d3[r] * f;
+                    a4[i][r] += d4[r] * f;
+                }
+            }
+            // pairs inside the lane's own group, exact: E between tokens u < w
+            // of the group is exp(G_w - G_u) for both the lower sums (row w)
+            // and the upper ones (row u)
+            {
+                const int u0 = T + 4 * l4;
+                float gg[4], kg[4], qg[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    gg[r] = Gs[(u0 + r) * GP + c];
+                    kg[r] = Ks[(u0 + r) * KP + c];
+                    qg[r] = Qs[(u0 + r) * KP + c];
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float nd = Nm[(u0 + r) * kTP + u0 + r];
+                    a2[i][r] += nd * kg[r];
+                    a4[i][r] += nd * qg[r];
+                }
+#pragma unroll
+                for (int w = 1; w < 4; ++w) {
+#pragma unroll
+                    for (int u = 0; u < w; ++u) {
+                        const float e = __expf(fminf(gg[w] - gg[u], 0.f));
+                        const float mwu = Mm[(u0 + w) * kTP + u0 + u], nwu = Nm[(u0 + w) * kTP + u0 + u];
+                        a1[i][w] += mwu * kg[u] * e;  // row w, s = u
+                        a2[i][w] += nwu * kg[u] * e;
+                        a3[i][u] += mwu * kg[w] * e;  // row u, r = w
+                        a4[i][u] += nwu * qg[w] * e;
+                    }
                 }
             }
         }
