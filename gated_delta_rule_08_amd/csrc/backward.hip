@@ -344,22 +344,6 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
     for (int i = tid; i < kC * kC; i += kNT) img[iT + i] = Tl[(i >> 6) * kTP + (i & 63)];
 }
 
-// The factored rows K0 = k e0 and Kt = k ek, eE and beta of one chunk, from
-// its image (all threads, coalesced).
-template <int DK>
-__device__ __forceinline__ void load_factors(const Args& a, const float* im, int b, int h, int t0, int n,
-                                             float* K0, float* Kt, float* eE, float* Bs) {
-    constexpr int KP = DK + 1;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < kC * DK; i += kNT) {
-        const int t = i / DK, c = i - t * DK;
-        K0[t * KP + c] = im[iK0 + i];
-        Kt[t * KP + c] = im[iK0 + kC * DK + i];
-    }
-    if (tid < DK) eE[tid] = im[iK0 + 3 * kC * DK + tid];
-    if (tid < kC) Bs[tid] = tid < n ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
-}
-
 // ---------------------------------------------------------------- bwd_fwd
 // FS value columns per workgroup: 32 when that still puts a workgroup on
 // every CU (the kernel's LDS has room for them, and a wider slice reads each
@@ -536,7 +520,7 @@ __global__ __launch_bounds__(kNT) void bwd_dout(Args a) {
 }
 
 // ---------------------------------------------------------------- bwd_chain
-// FS value columns per workgroup (32 when that still fills every CU).
+// FS = 16 value columns per workgroup.
 template <int DK, bool KDA, typename InT, int FS>
 __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
     constexpr int KP = DK + 1;
@@ -570,12 +554,12 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
     // (a lane's column: 16 (w % NCT) + lane % 16).
     const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
     const int R = 16 * (wave / NCT), col = 16 * (wave % NCT) + li;
-    // At the narrow slice width the next (earlier) chunk's image rows K0, Kt
-    // and Tinv are loaded into registers while the current chunk is computed
-    // (at the wide width the registers have no room for them).
-    constexpr bool kPf = FS == 16;
-    constexpr int NKF = kPf ? (kC * DK + kNT - 1) / kNT : 1;
-    constexpr int NTF = kPf ? kC * kC / kNT : 1;
+    // The next (earlier) chunk's image rows K0, Kt and Tinv are loaded into
+    // registers while the current chunk is computed (at 16-column slices the
+    // registers have room for them; at 32 they do not).
+    static_assert(FS == kSl, "the reverse chain runs 16-column slices");
+    constexpr int NKF = (kC * DK + kNT - 1) / kNT;
+    constexpr int NTF = kC * kC / kNT;
     float fk0[NKF], fkt[NKF], fti[NTF];
     auto fetch = [&](int ch) {
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
@@ -588,7 +572,7 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
 #pragma unroll
         for (int m = 0; m < NTF; ++m) fti[m] = im[iT + tid + m * kNT];
     };
-    if constexpr (kPf) fetch(a.nch - 1);
+    fetch(a.nch - 1);
     for (int ch = a.nch - 1; ch >= 0; --ch) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();
@@ -600,34 +584,28 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
             Hq[i] = hq[static_cast<size_t>(c) * a.DV + j0 + j];
         }
         const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-        if constexpr (kPf) {
 #pragma unroll
-            for (int m = 0; m < NKF; ++m) {
-                const int i = tid + m * kNT;
-                if (i < kC * DK) {
-                    K0[(i / DK) * KP + i % DK] = fk0[m];
-                    Kt[(i / DK) * KP + i % DK] = fkt[m];
-                }
+        for (int m = 0; m < NKF; ++m) {
+            const int i = tid + m * kNT;
+            if (i < kC * DK) {
+                K0[(i / DK) * KP + i % DK] = fk0[m];
+                Kt[(i / DK) * KP + i % DK] = fkt[m];
             }
-#pragma unroll
-            for (int m = 0; m < NTF; ++m) {
-                const int i = tid + m * kNT;
-                Ti[(i >> 6) * kTP + (i & 63)] = fti[m];
-            }
-            if (tid < DK) eE[tid] = im[iK0 + 3 * kC * DK + tid];
-            if (tid < kC) Bs[tid] = tid < n ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
-        } else {
-            load_factors<DK>(a, im, b, h, t0, n, K0, Kt, eE, Bs);
-            for (int i = tid; i < kC * kC; i += kNT) Ti[(i >> 6) * kTP + (i & 63)] = im[iT + i];
         }
+#pragma unroll
+        for (int m = 0; m < NTF; ++m) {
+            const int i = tid + m * kNT;
+            Ti[(i >> 6) * kTP + (i & 63)] = fti[m];
+        }
+        if (tid < DK) eE[tid] = im[iK0 + 3 * kC * DK + tid];
+        if (tid < kC) Bs[tid] = tid < n ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
         for (int i = tid; i < kC * FS; i += kNT) {
             const int t = i / FS, j = i - t * FS;
             const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
             Xs[i] = t < n ? a.ws[W.xr + r * a.DV + j0 + j] : 0.f;
             Pd[i] = t < n ? a.ws[W.pd + r * a.DV + j0 + j] : 0.f;
         }
-        if constexpr (kPf)
-            if (ch > 0) fetch(ch - 1);
+        if (ch > 0) fetch(ch - 1);
         __syncthreads();
         // U = Tinv diag(beta) Xr (Tinv zero above its diagonal) on the first
         // 4 NCT waves; dU = Pd + Kt dS_end on the next 4 NCT.
@@ -1108,7 +1086,7 @@ constexpr int local_lds() {
 
 template <int DK, bool KDA, typename InT>
 hipError_t run(Args a, hipStream_t s) {
-    static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK, 32>() <= 160 * 1024 &&
+    static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK, kSl>() <= 160 * 1024 &&
                   prep_lds<DK, KDA>() <= 160 * 1024 && fwd_lds<DK, 32>() <= 160 * 1024 &&
                   dout_lds<DK>() <= 160 * 1024, "LDS budget");
     auto set = [](const void* f, int bytes) {
@@ -1118,33 +1096,31 @@ hipError_t run(Args a, hipStream_t s) {
     hipError_t e;
     const unsigned heads8 = static_cast<unsigned>((a.B * a.H + 7) / 8 * 8);  // slice grids: whole groups of 8 heads
     const unsigned per_chunk = static_cast<unsigned>(a.B * a.H * a.nch);
-    // the chains take 32-column slices when that still puts a workgroup on every CU
+    // The checkpoint chain takes 32-column slices when that still puts a
+    // workgroup on every CU; the reverse chain always takes 16 (at 16 it has
+    // the registers to load the next chunk's image during the current one,
+    // which costs less than the extra rounds of workgroups).
     const bool wide = a.DV >= 32 && static_cast<long long>(a.B) * a.H * (a.DV / 32) >= 256;
-    const int FSW = wide ? 32 : 16;
-    a.nsl_chain = a.DV / FSW;
-    const unsigned per_slice = heads8 * static_cast<unsigned>(a.DV / FSW);
+    a.nsl_chain = a.DV / kSl;
+    const unsigned fwd_slices = heads8 * static_cast<unsigned>(a.DV / (wide ? 32 : 16));
+    const unsigned chain_slices = heads8 * static_cast<unsigned>(a.DV / kSl);
     const void* fwd = wide ? reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 32>)
                            : reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 16>);
-    const void* chain = wide ? reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT, 32>)
-                             : reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT, 16>);
     if ((e = set(reinterpret_cast<const void*>(bwd_prep<DK, KDA, InT>), prep_lds<DK, KDA>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_dout<DK, KDA, InT>), dout_lds<DK>())) != hipSuccess) return e;
     if ((e = set(fwd, wide ? fwd_lds<DK, 32>() : fwd_lds<DK, 16>())) != hipSuccess) return e;
-    if ((e = set(chain, wide ? chain_lds<DK, 32>() : chain_lds<DK, 16>())) != hipSuccess) return e;
+    if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT, kSl>), chain_lds<DK, kSl>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_local<DK, KDA, InT>), local_lds<DK, KDA>())) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (prep_lds<DK, KDA>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dout<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (dout_lds<DK>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (wide) {
-        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 32>), dim3(per_slice), dim3(kNT), (fwd_lds<DK, 32>()), s, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_chain<DK, KDA, InT, 32>), dim3(per_slice), dim3(kNT), (chain_lds<DK, 32>()), s, a);
-    } else {
-        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 16>), dim3(per_slice), dim3(kNT), (fwd_lds<DK, 16>()), s, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_chain<DK, KDA, InT, 16>), dim3(per_slice), dim3(kNT), (chain_lds<DK, 16>()), s, a);
-    }
+    if (wide)
+        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 32>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 32>()), s, a);
+    else
+        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 16>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 16>()), s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_chain<DK, KDA, InT, kSl>), dim3(chain_slices), dim3(kNT), (chain_lds<DK, kSl>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_local<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (local_lds<DK, KDA>()), s, a);
     return hipGetLastError();
