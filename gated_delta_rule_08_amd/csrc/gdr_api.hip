@@ -47,6 +47,12 @@ inline bool sizes_ok(long long B, long long T, long long H, long long dk, long l
     return true;
 }
 
+// The backward runs one 1024-thread workgroup per (b, h, chunk): the
+// dispatch's work-item count has to fit 32 bits.
+inline bool backward_grid_ok(long long B, long long T, long long H) {
+    return B * H * ((T + 63) / 64) < (1LL << 22);
+}
+
 inline bool flags_ok(int flags) { return (flags & ~(GDR_PRO_L2NORM_QK | GDR_PRO_SIGMOID)) == 0; }
 // The bf16 prefill schedules normalise q, k where the chunk-local products
 // are formed: the fused GDN kernel and the split KDA kernels.
@@ -287,7 +293,8 @@ int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total
 size_t gdr_chunk_backward_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
                                           int dv, int chunk) {
     if (check_enums(gate, dtype) != GDR_OK || chunk != 64 || B < 0 || H < 0 || T < 0 ||
-        !head_dim_ok(dk) || !head_dim_ok(dv) || !sizes_ok(B, T, H, dk, dv))
+        !head_dim_ok(dk) || !head_dim_ok(dv) || !sizes_ok(B, T, H, dk, dv) ||
+        !backward_grid_ok(B, T, H))
         return 0;
     if (B == 0 || H == 0 || T == 0) return 0;
     return gdr::backward_workspace_floats(B, T, H, dk, dv) * sizeof(float);
@@ -305,6 +312,7 @@ int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv,
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
     if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
+    if (!backward_grid_ok(B, T, H)) return GDR_ERR_BAD_SHAPE;
     const size_t need = gdr_chunk_backward_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
     if (B == 0 || H == 0) return GDR_OK;

@@ -271,7 +271,9 @@ size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int 
  * to nearest even).  The gate enters through log(alpha), floored at -40 per
  * token as in the fp32 forward: where the floor is active, grad_alpha is 0.
  * T == 0 copies grad_state_out (or zeros) to grad_state_in.  Outputs may not
- * overlap inputs.  Returns a GDR_* status.
+ * overlap inputs.  B * H * ceil(T / 64) must stay below 2^22 (one 1024-thread
+ * workgroup per chunk and head; far beyond what the workspace allows on one
+ * GPU), else GDR_ERR_BAD_SHAPE.  Returns a GDR_* status.
  */
 int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
                        float scale,

@@ -295,6 +295,10 @@ def test_backward_validation(lib):
     bad[8] = ctypes.c_void_p(0x10008)                         # grad_q misaligned
     assert bwd(ptrs=bad, ws=ws, ws_bytes=need) == MISAL
     assert bwd(B=0, ptrs=nul) == OK                           # empty batch: no-op
+    # one workgroup per (b, h, chunk): 2^22 of them would overflow the dispatch
+    assert bwd(B=1, T=64 * (1 << 22), H=1, ptrs=p, ws=ws, ws_bytes=need) == SHAPE
+    assert bwd(B=2, T=64 * (1 << 21), H=1, ptrs=p, ws=ws, ws_bytes=need) == SHAPE
+    assert lib.gdr_chunk_backward_workspace_bytes(0, 1, 1, 64 * (1 << 22), 1, 128, 128, 64) == 0
 
 
 def test_prologue_ex_variants_validation(lib, monkeypatch):
