@@ -1094,8 +1094,11 @@ hipError_t run(Args a, hipStream_t s) {
                                  : hipSuccess;
     };
     hipError_t e;
-    const unsigned heads8 = static_cast<unsigned>((a.B * a.H + 7) / 8 * 8);  // slice grids: whole groups of 8 heads
-    const unsigned per_chunk = static_cast<unsigned>(a.B * a.H * a.nch);
+    const unsigned long long h8 = (static_cast<unsigned long long>(a.B) * a.H + 7) / 8 * 8;
+    if (!grid_fits(static_cast<unsigned long long>(a.B) * a.H * a.nch, kNT) || !grid_fits(h8 * (a.DV / kSl), kNT))
+        return hipErrorInvalidConfiguration;
+    const unsigned heads8 = static_cast<unsigned>(h8);  // slice grids: whole groups of 8 heads
+    const unsigned per_chunk = static_cast<unsigned>(static_cast<unsigned long long>(a.B) * a.H * a.nch);
     // The checkpoint chain takes 32-column slices when that still puts a
     // workgroup on every CU; the reverse chain always takes 16 (at 16 it has
     // the registers to load the next chunk's image during the current one,

@@ -185,6 +185,7 @@ hipError_t launch(int n_units, float scale, const void* q, const void* k, const 
                   int pro) {
     constexpr int COLS = DV < 32 ? DV : 32;
     const long long waves = static_cast<long long>(n_units) * (DV / COLS);
+    if (!grid_fits((waves + 3) / 4, 256)) return hipErrorInvalidConfiguration;
     const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
     hipLaunchKernelGGL((decode_step_kernel<DK, DV, InT, KDA>), dim3(blocks), dim3(256), 0, s,
                        n_units, scale, static_cast<const InT*>(q), static_cast<const InT*>(k),
@@ -347,6 +348,7 @@ hipError_t launch_multi(int n_units, int T, int H, float scale, const void* q, c
                         void* o, float* states, hipStream_t s, int pro) {
     constexpr int COLS = DV < 32 ? DV : 32;
     const long long waves = static_cast<long long>(n_units) * (DV / COLS);
+    if (!grid_fits((waves + 3) / 4, 256)) return hipErrorInvalidConfiguration;
     const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
     if (states) {
         hipLaunchKernelGGL((decode_multi_kernel<DK, DV, InT, KDA, true>), dim3(blocks), dim3(256), 0, s,

@@ -47,10 +47,16 @@ inline bool sizes_ok(long long B, long long T, long long H, long long dk, long l
     return true;
 }
 
-// The backward runs one 1024-thread workgroup per (b, h, chunk): the
-// dispatch's work-item count has to fit 32 bits.
-inline bool backward_grid_ok(long long B, long long T, long long H) {
-    return B * H * ((T + 63) / 64) < (1LL << 22);
+// The backward runs 1024-thread workgroups, one per (b, h, chunk) and one per
+// (b, h, 16 value columns) over whole groups of 8 heads: each dispatch's
+// work-item count has to fit 32 bits.
+inline bool backward_grid_ok(long long B, long long T, long long H, long long dv) {
+    return B * H * ((T + 63) / 64) < (1LL << 22) && (B * H + 7) / 8 * 8 * (dv / 16) < (1LL << 22);
+}
+// A launcher's hipErrorInvalidConfiguration means a grid too large for one
+// dispatch (checked before any HIP call): reported as a shape error.
+inline int status_of(hipError_t e) {
+    return e == hipSuccess ? GDR_OK : e == hipErrorInvalidConfiguration ? GDR_ERR_BAD_SHAPE : GDR_ERR_HIP;
 }
 
 inline bool flags_ok(int flags) { return (flags & ~(GDR_PRO_L2NORM_QK | GDR_PRO_SIGMOID)) == 0; }
@@ -114,7 +120,7 @@ int gdr_decode_step_ex(int gate, int dtype, int flags, int B, int H, int dk, int
         return GDR_ERR_MISALIGNED;
     hipError_t e = gdr::launch_decode(kda, dtype, B, H, dk, dv, scale, q, k, v, alpha, beta,
                                       state, o, static_cast<hipStream_t>(stream), flags);
-    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+    return status_of(e);
 }
 
 int gdr_decode_multi(int gate, int dtype, int B, int T, int H, int dk, int dv, float scale,
@@ -152,7 +158,7 @@ int gdr_decode_multi_ex(int gate, int dtype, int flags, int B, int T, int H, int
     hipError_t e = gdr::launch_decode_multi(kda, dtype, B, T, H, dk, dv, scale, q, k, v, alpha,
                                             beta, state, o, states, static_cast<hipStream_t>(stream),
                                             flags);
-    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+    return status_of(e);
 }
 
 size_t gdr_chunk_prefill_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
@@ -221,7 +227,7 @@ int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, in
                                      static_cast<const gdr::bf16_t*>(v), alpha, beta, state_in,
                                      state_out, static_cast<gdr::bf16_t*>(o), workspace, s, opt);
     }
-    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+    return status_of(e);
 }
 
 size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int max_T, int H,
@@ -287,14 +293,14 @@ int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total
                                      static_cast<const gdr::bf16_t*>(v), alpha, beta, states,
                                      states, static_cast<gdr::bf16_t*>(o), workspace, s, vl);
     }
-    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+    return status_of(e);
 }
 
 size_t gdr_chunk_backward_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
                                           int dv, int chunk) {
     if (check_enums(gate, dtype) != GDR_OK || chunk != 64 || B < 0 || H < 0 || T < 0 ||
         !head_dim_ok(dk) || !head_dim_ok(dv) || !sizes_ok(B, T, H, dk, dv) ||
-        !backward_grid_ok(B, T, H))
+        !backward_grid_ok(B, T, H, dv))
         return 0;
     if (B == 0 || H == 0 || T == 0) return 0;
     return gdr::backward_workspace_floats(B, T, H, dk, dv) * sizeof(float);
@@ -312,7 +318,7 @@ int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv,
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
     if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
-    if (!backward_grid_ok(B, T, H)) return GDR_ERR_BAD_SHAPE;
+    if (!backward_grid_ok(B, T, H, dv)) return GDR_ERR_BAD_SHAPE;
     const size_t need = gdr_chunk_backward_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
     if (B == 0 || H == 0) return GDR_OK;
@@ -339,7 +345,7 @@ int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv,
                                  grad_o, grad_state_out, grad_q, grad_k, grad_v, grad_alpha,
                                  grad_beta, grad_state_in, static_cast<float*>(workspace), s);
     }
-    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+    return status_of(e);
 }
 
 }  // extern "C"

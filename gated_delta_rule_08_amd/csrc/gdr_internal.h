@@ -62,6 +62,13 @@ __device__ __forceinline__ float log2_sigmoid(float z) {
     return -(fmaxf(-z, 0.f) * kLog2e + __log2f(1.f + exp2f(-fabsf(z) * kLog2e)));
 }
 
+// A dispatch's work-item count (workgroups x threads) has to fit 32 bits.
+// Launchers check their grids with this before any HIP call and return
+// hipErrorInvalidConfiguration for a shape that would exceed it.
+inline bool grid_fits(unsigned long long blocks, unsigned long long threads) {
+    return blocks * threads <= 0xFFFFFFFFull;
+}
+
 // Launchers, one per kernel family.  They assume validated arguments and
 // return the hipError_t of the launch.
 // pro: input prologue flags (GDR_PRO_*).

@@ -1650,7 +1650,11 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     using L = Layout<DK, NSW, KDA>;
     const int NS = DV / (16 * NSW);
     const int groups = (B * H + 7) / 8;
-    const unsigned blocks = static_cast<unsigned>(groups) * 8u * static_cast<unsigned>(NS);
+    const unsigned long long blocks64 = static_cast<unsigned long long>(groups) * 8u * NS;
+    if (!grid_fits(blocks64, block_threads<NSW, KDA, kFused>()) ||
+        !grid_fits(blocks64, block_threads<NSW, KDA, kChain>()))
+        return hipErrorInvalidConfiguration;
+    const unsigned blocks = static_cast<unsigned>(blocks64);
     auto set_lds = [](const void* kern, int bytes) {
         return bytes > 64 * 1024 ? hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
                                  : hipSuccess;
@@ -1680,6 +1684,8 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
         // chunks per chunk-local workgroup: about two workgroups per CU
         const int cpw = std::max(1, (B * H * (c1 - c0) + 511) / 512);
         const int groups_per_head = (c1 - c0 + cpw - 1) / cpw;
+        if (!grid_fits(static_cast<unsigned long long>(B) * H * groups_per_head, block_threads<1, KDA, kPrep>()))
+            return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(B * H * groups_per_head)),
                            dim3(block_threads<1, KDA, kPrep>()), LP::pBytes, s, B, T, H, DV, cpw, scale, q, k,
                            v, alpha, beta, s_in, s_out, o, img, c0, c1, vl);

@@ -238,6 +238,7 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const float* q, cons
     using L = F32Smem<DK, DVS, KDA>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
     auto kern = prefill_f32_kernel<DK, DVS, KDA>;
+    if (!grid_fits(static_cast<unsigned long long>(B) * H * (DV / DVS), 256)) return hipErrorInvalidConfiguration;
     if (L::bytes > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,

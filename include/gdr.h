@@ -63,7 +63,8 @@ typedef enum { GDR_DTYPE_F32 = 0, GDR_DTYPE_BF16 = 1 } gdr_dtype_t;
 enum {
     GDR_OK = 0,
     GDR_ERR_NULL_PTR = -1,    /* a required pointer is NULL                 */
-    GDR_ERR_BAD_SHAPE = -2,   /* a size is negative or overflows            */
+    GDR_ERR_BAD_SHAPE = -2,   /* a size is negative or overflows (also: a
+                                 launch would exceed 2^32 work-items)       */
     GDR_ERR_UNSUPPORTED = -3, /* dk, dv or chunk outside the supported set  */
     GDR_ERR_MISALIGNED = -4,  /* a pointer violates the alignment rule      */
     GDR_ERR_WORKSPACE = -5,   /* workspace missing or too small             */
@@ -271,9 +272,10 @@ size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int 
  * to nearest even).  The gate enters through log(alpha), floored at -40 per
  * token as in the fp32 forward: where the floor is active, grad_alpha is 0.
  * T == 0 copies grad_state_out (or zeros) to grad_state_in.  Outputs may not
- * overlap inputs.  B * H * ceil(T / 64) must stay below 2^22 (one 1024-thread
- * workgroup per chunk and head; far beyond what the workspace allows on one
- * GPU), else GDR_ERR_BAD_SHAPE.  Returns a GDR_* status.
+ * overlap inputs.  B * H * ceil(T / 64) and ceil(B * H / 8) * 8 * dv / 16
+ * must stay below 2^22 (1024-thread workgroups per chunk and head, and per 16
+ * value columns of each head), else GDR_ERR_BAD_SHAPE.  Returns a GDR_*
+ * status.
  */
 int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
                        float scale,

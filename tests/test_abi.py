@@ -299,6 +299,16 @@ def test_backward_validation(lib):
     assert bwd(B=1, T=64 * (1 << 22), H=1, ptrs=p, ws=ws, ws_bytes=need) == SHAPE
     assert bwd(B=2, T=64 * (1 << 21), H=1, ptrs=p, ws=ws, ws_bytes=need) == SHAPE
     assert lib.gdr_chunk_backward_workspace_bytes(0, 1, 1, 64 * (1 << 22), 1, 128, 128, 64) == 0
+    # the 16-column slice grids of the chains: 600,000 heads x 8 slices
+    assert bwd(B=600000, T=64, H=1, ptrs=p, ws=ws, ws_bytes=1 << 62) == SHAPE
+
+
+def test_decode_grid_limit(lib):
+    """A decode whose dispatch would exceed 2^32 work-items is a shape error,
+    reported before any device call: 70 M heads of 16 x 16 (one wavefront each)."""
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(7)]
+    assert lib.gdr_decode_step(0, 0, 70_000_000, 1, 16, 16, 1.0, *p, None) == SHAPE
+    assert lib.gdr_decode_step(1, 1, 35_000_000, 2, 16, 16, 1.0, *p, None) == SHAPE
 
 
 def test_prologue_ex_variants_validation(lib, monkeypatch):
