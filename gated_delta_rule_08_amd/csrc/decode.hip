@@ -92,20 +92,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int rg = lane / LPR;
     const int col = slice * COLS + (lane % LPR) * 4;
 
-    float* S = state + static_cast<size_t>(unit) * DK * DV + col;
-    float4 s[NI];
-#pragma unroll
-    for (int m = 0; m < NI; ++m)
-        s[m] = ld_state(S + static_cast<size_t>(m * RPI + rg) * DV);
-
+    // Load order: the small per-head vectors first, then the state rows in
+    // row order (each pinned by a scheduling fence).  Loads complete in
+    // order, so each row is scaled and reduced as soon as it arrives; left
+    // alone, the compiler issued row 0 last and waited for the whole state.
     const InT* qu = q + static_cast<size_t>(unit) * DK;
     const InT* ku = k + static_cast<size_t>(unit) * DK;
-    float qv[NI], kv[NI];
-#pragma unroll
-    for (int m = 0; m < NI; ++m) {
-        qv[m] = Elem<InT>::load(qu + m * RPI + rg);
-        kv[m] = Elem<InT>::load(ku + m * RPI + rg);
-    }
     float av[KDA ? NI : 1];
     if constexpr (KDA) {
 #pragma unroll
@@ -114,7 +106,22 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         av[0] = alpha[unit];
     }
     float b = beta[unit];
+    float qv[NI], kv[NI];
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        kv[m] = Elem<InT>::load(ku + m * RPI + rg);
+        qv[m] = Elem<InT>::load(qu + m * RPI + rg);
+    }
     const float4 vv = load4<InT>(v + static_cast<size_t>(unit) * DV + col);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float* S = state + static_cast<size_t>(unit) * DK * DV + col;
+    float4 s[NI];
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        s[m] = ld_state(S + static_cast<size_t>(m * RPI + rg) * DV);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if (pro & GDR_PRO_SIGMOID) {  // gates given as logits
         b = sigmoid_f(b);
 #pragma unroll
