@@ -73,7 +73,7 @@ __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
 }
 
 template <int DK, int DV, typename InT, bool KDA>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 1 : 4))) void decode_step_kernel(
     int n_units, float scale, const InT* __restrict__ q, const InT* __restrict__ k,
     const InT* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
     float* __restrict__ state, InT* __restrict__ o, int pro) {
@@ -84,60 +84,90 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     constexpr int NI = DK / RPI;             // rows per lane
     static_assert(NI >= 1 && NI * RPI == DK, "head size does not tile the wavefront");
 
+    constexpr int UPW = 4 / NSLICE;          // heads per workgroup
+    constexpr int NL = (UPW * DK + 255) / 256;  // shared elements per thread
+    static_assert(UPW >= 1 && UPW * NSLICE == 4, "the four waves cover whole heads");
+    // q, k and (KDA) the gate of the workgroup's heads, read by every wave
+    // of the head from LDS when a row needs them instead of being held in
+    // registers: GDN then fits 128 VGPRs, four waves per SIMD (measured
+    // 48.8 -> 47.4 us per launch at B=64, H=32, d=128); KDA's extra gate
+    // reads keep it at three (forced to four it spills).
+    __shared__ float qs[UPW][DK], ks[UPW][DK], gs[KDA ? UPW : 1][KDA ? DK : 1];
+
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int unit = wave / NSLICE;
-    if (unit >= n_units) return;  // no barriers below: whole waves retire
+    const int lu = (threadIdx.x >> 6) / NSLICE;  // the wave's head within the workgroup
+    const int u0 = blockIdx.x * UPW;
+    const bool live = unit < n_units;            // padding waves only join the barrier
     const int slice = wave - unit * NSLICE;
     const int rg = lane / LPR;
     const int col = slice * COLS + (lane % LPR) * 4;
 
-    // Load order: the small per-head vectors first, then the state rows in
-    // row order (each pinned by a scheduling fence).  Loads complete in
-    // order, so each row is scaled and reduced as soon as it arrives; left
-    // alone, the compiler issued row 0 last and waited for the whole state.
-    const InT* qu = q + static_cast<size_t>(unit) * DK;
-    const InT* ku = k + static_cast<size_t>(unit) * DK;
-    float av[KDA ? NI : 1];
-    if constexpr (KDA) {
+    // Load order: the small vectors first (shared ones cooperatively), then
+    // the state rows in row order (each pinned by a scheduling fence).  Loads
+    // complete in order, so each row is scaled and reduced as soon as it
+    // arrives; left alone, the compiler issued row 0 last and waited for the
+    // whole state.
+    float tq[NL], tk[NL], tg[NL];
 #pragma unroll
-        for (int m = 0; m < NI; ++m) av[m] = alpha[static_cast<size_t>(unit) * DK + m * RPI + rg];
-    } else {
-        av[0] = alpha[unit];
+    for (int j = 0; j < NL; ++j) {
+        const int i = threadIdx.x + 256 * j, uu = i / DK, c = i - uu * DK;
+        const bool ok = i < UPW * DK && u0 + uu < n_units;
+        const size_t e = static_cast<size_t>(u0 + uu) * DK + c;
+        tq[j] = ok ? Elem<InT>::load(q + e) : 0.f;
+        tk[j] = ok ? Elem<InT>::load(k + e) : 0.f;
+        if constexpr (KDA) tg[j] = ok ? alpha[e] : 0.f;
     }
-    float b = beta[unit];
-    float qv[NI], kv[NI];
-#pragma unroll
-    for (int m = 0; m < NI; ++m) {
-        kv[m] = Elem<InT>::load(ku + m * RPI + rg);
-        qv[m] = Elem<InT>::load(qu + m * RPI + rg);
+    float ag = 0.f, b = 0.f;
+    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+        if constexpr (!KDA) ag = alpha[unit];
+        b = beta[unit];
+        vv = load4<InT>(v + static_cast<size_t>(unit) * DV + col);
     }
-    const float4 vv = load4<InT>(v + static_cast<size_t>(unit) * DV + col);
     __builtin_amdgcn_sched_barrier(0);
 
-    float* S = state + static_cast<size_t>(unit) * DK * DV + col;
+    float* S = state + static_cast<size_t>(live ? unit : 0) * DK * DV + col;
     float4 s[NI];
+    if (live) {
 #pragma unroll
-    for (int m = 0; m < NI; ++m) {
-        s[m] = ld_state(S + static_cast<size_t>(m * RPI + rg) * DV);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int m = 0; m < NI; ++m) {
+            s[m] = ld_state(S + static_cast<size_t>(m * RPI + rg) * DV);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    if (pro & GDR_PRO_SIGMOID) {  // gates given as logits
+    const bool sig = pro & GDR_PRO_SIGMOID;  // gates given as logits
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        if (i < UPW * DK) {
+            const int uu = i / DK, c = i - uu * DK;
+            qs[uu][c] = tq[j];
+            ks[uu][c] = tk[j];
+            if constexpr (KDA) gs[uu][c] = sig ? sigmoid_f(tg[j]) : tg[j];
+        }
+    }
+    __syncthreads();
+    if (!live) return;  // no barriers below
+    if (sig) {
         b = sigmoid_f(b);
-#pragma unroll
-        for (int m = 0; m < (KDA ? NI : 1); ++m) av[m] = sigmoid_f(av[m]);
+        if constexpr (!KDA) ag = sigmoid_f(ag);
     }
+    const float* qv = qs[lu];
+    const float* kv = ks[lu];
 
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
     float kq = 0.f;
 #pragma unroll
     for (int m = 0; m < NI; ++m) {
-        const float a = KDA ? av[m] : av[0];
+        const int row = m * RPI + rg;
+        const float a = KDA ? gs[lu][row] : ag, kr = kv[row], qr = qv[row];
         s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
-        p0 += kv[m] * s[m].x; p1 += kv[m] * s[m].y; p2 += kv[m] * s[m].z; p3 += kv[m] * s[m].w;
-        r0 += qv[m] * s[m].x; r1 += qv[m] * s[m].y; r2 += qv[m] * s[m].z; r3 += qv[m] * s[m].w;
-        kq += kv[m] * qv[m];
+        p0 += kr * s[m].x; p1 += kr * s[m].y; p2 += kr * s[m].z; p3 += kr * s[m].w;
+        r0 += qr * s[m].x; r1 += qr * s[m].y; r2 += qr * s[m].z; r3 += qr * s[m].w;
+        kq += kr * qr;
     }
     // Butterfly over the lanes that hold the same columns (lane bits >= log2(LPR)).
 #pragma unroll
@@ -156,8 +186,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         float kk = 0.f, qq = 0.f;
 #pragma unroll
         for (int m = 0; m < NI; ++m) {
-            kk += kv[m] * kv[m];
-            qq += qv[m] * qv[m];
+            const float kr = kv[m * RPI + rg], qr = qv[m * RPI + rg];
+            kk += kr * kr;
+            qq += qr * qr;
         }
 #pragma unroll
         for (int off = LPR; off < 64; off <<= 1) {
@@ -174,7 +205,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const float bn = b * ik;
 #pragma unroll
     for (int m = 0; m < NI; ++m) {
-        const float bk = bn * kv[m];
+        const float bk = bn * kv[m * RPI + rg];
         s[m].x += bk * e0; s[m].y += bk * e1; s[m].z += bk * e2; s[m].w += bk * e3;
         st_state(S + static_cast<size_t>(m * RPI + rg) * DV, s[m]);
     }
