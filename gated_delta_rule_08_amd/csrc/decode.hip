@@ -283,12 +283,6 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
     const int col = slice * COLS + (lane % LPR) * 4;
     const int b = unit / H, h = unit - (unit / H) * H;
 
-    float* S = state + static_cast<size_t>(unit) * DK * DV + col;
-    float4 s[NI];
-#pragma unroll
-    for (int m = 0; m < NI; ++m)
-        s[m] = ld_state(S + static_cast<size_t>(m * RPI + rg) * DV);
-
     struct In {
         float qv[NI], kv[NI], av[KDA ? NI : 1], b;
         float4 vv;
@@ -312,8 +306,19 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
         x.vv = load4<InT>(v + tok * DV + col);
     };
     const bool sig = (pro & GDR_PRO_SIGMOID) != 0, nrm = (pro & GDR_PRO_L2NORM_QK) != 0;
+    // Load order as in the decode step: the first token's inputs, then the
+    // state rows in row order, so the first token's rows are reduced as they
+    // arrive.
     In cur, nxt;
     load_in(0, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    float* S = state + static_cast<size_t>(unit) * DK * DV + col;
+    float4 s[NI];
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+        s[m] = ld_state(S + static_cast<size_t>(m * RPI + rg) * DV);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int t = 0; t < T; ++t) {
         load_in(t + 1 < T ? t + 1 : t, nxt);  // the next token's inputs (the last one reloads)
         if (sig) {  // gates given as logits
