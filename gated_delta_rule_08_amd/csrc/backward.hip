@@ -447,13 +447,13 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
             for (int r = 0; r < 4; ++r) Us[(R + 4 * l4 + r) * FS + col] = acc[r];
         }
         __syncthreads();
-        // S <- eE S + Kt^T U
-        if (R < DK) {
-            const f32x4 acc = tile_product(0, kC, [&](int k) { return Kt[k * KP + R + li]; },
+        // S <- eE S + Kt^T U  (DK/16 row tiles; at 64 columns a wave takes two)
+        for (int R3 = R; R3 < DK; R3 += 16 * (16 / NCT)) {
+            const f32x4 acc = tile_product(0, kC, [&](int k) { return Kt[k * KP + R3 + li]; },
                                            [&](int k) { return Us[k * FS + col]; });
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int c = R + 4 * l4 + r;
+                const int c = R3 + 4 * l4 + r;
                 Ss[c * FS + col] = eE[c] * Ss[c * FS + col] + acc[r];
             }
         }
@@ -1087,7 +1087,7 @@ constexpr int local_lds() {
 template <int DK, bool KDA, typename InT>
 hipError_t run(Args a, hipStream_t s) {
     static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK, kSl>() <= 160 * 1024 &&
-                  prep_lds<DK, KDA>() <= 160 * 1024 && fwd_lds<DK, 32>() <= 160 * 1024 &&
+                  prep_lds<DK, KDA>() <= 160 * 1024 && fwd_lds<DK, 64>() <= 160 * 1024 &&
                   dout_lds<DK>() <= 160 * 1024, "LDS budget");
     auto set = [](const void* f, int bytes) {
         return bytes > 64 * 1024 ? hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
@@ -1103,22 +1103,27 @@ hipError_t run(Args a, hipStream_t s) {
     // workgroup on every CU; the reverse chain always takes 16 (at 16 it has
     // the registers to load the next chunk's image during the current one,
     // which costs less than the extra rounds of workgroups).
-    const bool wide = a.DV >= 32 && static_cast<long long>(a.B) * a.H * (a.DV / 32) >= 256;
+    const long long BH = static_cast<long long>(a.B) * a.H;
+    const int FSF = a.DV >= 64 && BH * (a.DV / 64) >= 256 ? 64 : a.DV >= 32 && BH * (a.DV / 32) >= 256 ? 32 : 16;
     a.nsl_chain = a.DV / kSl;
-    const unsigned fwd_slices = heads8 * static_cast<unsigned>(a.DV / (wide ? 32 : 16));
+    const unsigned fwd_slices = heads8 * static_cast<unsigned>(a.DV / FSF);
     const unsigned chain_slices = heads8 * static_cast<unsigned>(a.DV / kSl);
-    const void* fwd = wide ? reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 32>)
-                           : reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 16>);
+    const void* fwd = FSF == 64 ? reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 64>)
+                    : FSF == 32 ? reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 32>)
+                                : reinterpret_cast<const void*>(bwd_fwd<DK, KDA, InT, 16>);
     if ((e = set(reinterpret_cast<const void*>(bwd_prep<DK, KDA, InT>), prep_lds<DK, KDA>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_dout<DK, KDA, InT>), dout_lds<DK>())) != hipSuccess) return e;
-    if ((e = set(fwd, wide ? fwd_lds<DK, 32>() : fwd_lds<DK, 16>())) != hipSuccess) return e;
+    if ((e = set(fwd, FSF == 64 ? fwd_lds<DK, 64>() : FSF == 32 ? fwd_lds<DK, 32>() : fwd_lds<DK, 16>())) != hipSuccess)
+        return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT, kSl>), chain_lds<DK, kSl>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_local<DK, KDA, InT>), local_lds<DK, KDA>())) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (prep_lds<DK, KDA>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dout<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (dout_lds<DK>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (wide)
+    if (FSF == 64)
+        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 64>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 64>()), s, a);
+    else if (FSF == 32)
         hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 32>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 32>()), s, a);
     else
         hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 16>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 16>()), s, a);

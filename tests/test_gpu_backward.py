@@ -174,8 +174,9 @@ def test_backward_zero_beta_and_single_token(gate):
 
 @pytest.mark.parametrize("gate,dk,dv", [("gdn", 64, 32), ("kda", 16, 64)])
 def test_backward_many_heads_wide_slices(gate, dk, dv):
-    """Enough heads that the forward chain takes 32-column slices (one
-    workgroup per CU still); the oracle on sampled heads."""
+    """Enough heads that the forward chain takes wide slices (32 columns for
+    dv = 32, 64 for dv = 64; one workgroup per CU still); the oracle on
+    sampled heads."""
     inp, do, dst = _case(gate, "f32", B=8, T=70, H=32, dk=dk, dv=dv, seed=15)
     announce("backward %s wide slices B=8 H=32 dk=%d dv=%d" % (gate, dk, dv))
     got = _run(gate, "f32", inp, do, dst, 1.0)
