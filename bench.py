@@ -17,7 +17,9 @@ replayed, so the timed region holds GPU work only.  Roofline: algorithmic
 bytes (or flops) per launch divided by the average launch duration, from HIP
 events recorded around the timed region on the stream the kernels run on
 (GPU time / launches in the region).  ``cpu_baseline`` times the float64 CPU oracle on a
-bounded sample of the headline workload.
+bounded sample of the headline workload; the KDA decode, the small fp32 case
+and both prefills carry their own ``cpu_baseline``: the oracle's full run on
+the same inputs, with the host's core count and CPU model.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
        [--no-cpu-baseline] [--launches N]
@@ -93,6 +95,34 @@ def load_traffic(kernel_key, sha):
     except (OSError, ValueError):
         pass
     return None
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the oracle figures."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def oracle_baseline(run, units, unit, sample, gpu_rate, reps=1):
+    """Times ``run(nthreads)`` (the float64 oracle on the workload's own
+    inputs, ``reps`` times) on every host core visible to the process; the
+    rate is ``units`` per run per second.  A baseline, not a target."""
+    import oracle
+    nt = oracle.default_threads()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run(nt)
+    dt = (time.perf_counter() - t0) / reps
+    v = units / dt
+    return {"value": round(v, 3), "unit": unit, "cores": nt, "kind": "oracle", "sample": sample,
+            "seconds": round(dt, 6), "cpu": cpu_model(),
+            "gpu_over_oracle": round(gpu_rate / v, 1) if gpu_rate else None}
 
 
 def c_decode_call(torch, gdr, gate, d, scale=1.0):
@@ -221,11 +251,11 @@ def cpu_baseline_decode(torch, synth, w, layers, budget_s=12.0):
         "sample": "%d of %d layers, one decode step each (B=%d, H=%d, d=%d), float64" % (
             done, w.layers, w.B, w.H, w.dk),
         "seconds": round(t_total, 3),
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
     }
 
 
-def bench_kda_decode(torch, gdr, synth, steps, warmup):
+def bench_kda_decode(torch, gdr, synth, steps, warmup, want_cpu=False):
     w = synth.WORKLOADS["kda_decode_b256_h32_d128"]
     B, H, dk, dv = w.B, w.H, w.dk, w.dv
     inp = synth.make_inputs(w, s0="zero")
@@ -237,6 +267,7 @@ def bench_kda_decode(torch, gdr, synth, steps, warmup):
         for k in ("q", "k", "v", "alpha", "beta")}
     d["state"] = state
     d["o"] = torch.empty(B, H, dv, device="cuda", dtype=torch.bfloat16)
+    s_host = state.double().cpu().numpy() if want_cpu else None
     call = c_decode_call(torch, gdr, "kda", d)
     for _ in range(warmup):
         call()
@@ -244,10 +275,58 @@ def bench_kda_decode(torch, gdr, synth, steps, warmup):
     elapsed, gpu_s = timed_region(torch, n, call)
     launch_ms = 1e3 * gpu_s / n
     per_launch = B * H * decode_bytes_per_head("kda", dk, dv)
-    return {"workload": w.name, "steps": n, "ms_per_step": 1e3 * elapsed / n,
-            "gbs": per_launch * n / elapsed / 1e9, "tokens_per_s": B * n / elapsed,
-            "roofline": roofline_hbm(per_launch, launch_ms,
-                                     load_traffic("decode_kda", src_hash("decode.hip")))}
+    res = {"workload": w.name, "steps": n, "ms_per_step": 1e3 * elapsed / n,
+           "gbs": per_launch * n / elapsed / 1e9, "tokens_per_s": B * n / elapsed,
+           "roofline": roofline_hbm(per_launch, launch_ms,
+                                    load_traffic("decode_kda", src_hash("decode.hip")))}
+    if want_cpu:
+        import oracle
+        x = {k: inp[k][:, 0] for k in ("q", "k", "v", "alpha", "beta")}
+        res["cpu_baseline"] = oracle_baseline(
+            lambda nt: oracle.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], s_host,
+                                          nthreads=nt),
+            per_launch / 1e9, "GB/s", "full run: one decode step of all %d heads, float64" % (B * H),
+            per_launch / (launch_ms / 1e3) / 1e9)
+    return res
+
+
+def bench_tiny(torch, gdr, synth, steps, warmup, want_cpu=False):
+    """The small fp32 GDN case (B=1, H=2, T=64, d=16): one chunked prefill,
+    and the same 64 tokens as 64 decode steps.  Latency-bound: times only,
+    no roofline fraction."""
+    w = synth.WORKLOADS["gdn_tiny_f32"]
+    inp = synth.make_inputs(w)
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    d = {k: (None if v is None else torch.from_numpy(v).cuda()) for k, v in inp.items()}
+    s_out = torch.empty(B, H, dk, dv, device="cuda")
+    o = torch.empty(B, T, H, dv, device="cuda")
+    pre = lambda: gdr.gdr_chunk_prefill("gdn", d["q"], d["k"], d["v"], d["alpha"], d["beta"], None,
+                                        s_out, o)
+    steps_in = [{k: d[k][:, t].contiguous() for k in ("q", "k", "v", "alpha", "beta")} for t in range(T)]
+    state = torch.zeros(B, H, dk, dv, device="cuda")
+    o1 = torch.empty(B, H, dv, device="cuda")
+    calls = [c_decode_call(torch, gdr, "gdn", dict(x, state=state, o=o1)) for x in steps_in]
+
+    def dec():
+        for c in calls:
+            c()
+    n = max(steps, 20)
+    res = {"workload": w.name, "steps": n}
+    for tag, fn in (("prefill", pre), ("decode_x64", dec)):
+        for _ in range(warmup):
+            fn()
+        elapsed, gpu_s = timed_region(torch, n, fn)
+        res[tag + "_ms"] = 1e3 * gpu_s / n
+        res[tag + "_tokens_per_s"] = B * T * n / elapsed
+    res["roofline"] = None
+    if want_cpu:
+        import oracle
+        res["cpu_baseline"] = oracle_baseline(
+            lambda nt: oracle.recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None,
+                                        nthreads=nt),
+            B * T, "tokens/s", "full run (all %d tokens of both heads), float64, mean of 200" % T,
+            res["prefill_tokens_per_s"], reps=200)
+    return res
 
 
 def bench_decode_prologue(torch, gdr, synth, steps, warmup, gate="gdn"):
@@ -437,18 +516,21 @@ def bench_backward(torch, gdr, synth, name, steps, warmup):
                     "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
 
 
-def bench_prefill(torch, gdr, synth, name, steps, warmup, flags=0):
+def bench_prefill(torch, gdr, synth, name, steps, warmup, flags=0, want_cpu=False):
     """One chunked prefill per step; with ``flags`` the inputs are raw (q, k
-    not normalised, gate logits) and the kernels run the input prologue."""
+    not normalised, gate logits) and the kernels run the input prologue.
+    ``want_cpu``: the float64 oracle runs the whole workload on the same
+    inputs afterwards."""
     w = synth.WORKLOADS[name]
     inp = synth.make_raw_inputs(w) if flags else synth.make_inputs(w)
     B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
     d = {k: (None if v is None else torch.from_numpy(v).to(
         torch.bfloat16 if k in ("q", "k", "v") else torch.float32).cuda()) for k, v in inp.items()}
-    del inp
+    if not want_cpu:
+        del inp
     s_out = torch.empty(B, H, dk, dv, device="cuda")
     o = torch.empty(B, T, H, dv, device="cuda", dtype=torch.bfloat16)
-    need = gdr.gdr_chunk_prefill_workspace_bytes(w.gate, torch.bfloat16, B, T, H, dk, dv)
+    need = gdr.gdr_chunk_prefill_workspace_bytes(w.gate, torch.bfloat16, B, T, H, dk, dv, flags=flags)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     call = lambda: gdr.gdr_chunk_prefill_ex(w.gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
                                             d["s0"], s_out, o, flags=flags, workspace=ws)
@@ -459,7 +541,16 @@ def bench_prefill(torch, gdr, synth, name, steps, warmup, flags=0):
     nbytes = prefill_bytes(w.gate, B, T, H, dk, dv, d["s0"] is not None)
     flops = prefill_flops(B, T, H, dk, dv)
     sec = launch_ms / 1e3
-    return {
+    cpu = None
+    if want_cpu:
+        import oracle
+        cpu = oracle_baseline(
+            lambda nt: oracle.recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["s0"],
+                                        nthreads=nt),
+            B * T, "tokens/s", "full run (all %d heads, %d tokens each), float64" % (B * H, T),
+            B * T / sec)
+        del inp
+    res = {
         "workload": name + ("_prologue" if flags else ""), "steps": steps,
         "ms_per_step": 1e3 * elapsed / steps,
         "tokens_per_s": B * T * steps / elapsed,
@@ -475,6 +566,9 @@ def bench_prefill(torch, gdr, synth, name, steps, warmup, flags=0):
                  "algorithmic_flops": flops},
         "algorithmic_bytes": nbytes,
     }
+    if cpu:
+        res["cpu_baseline"] = cpu
+    return res
 
 
 def roofline_hbm(per_launch_bytes, launch_ms, traffic=None):
@@ -489,7 +583,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None,
-                    help="gdn_decode | kda_decode | gdn_verify | gdn_prefill | gdn_varlen | kda_prefill | backward | prologue | copy")
+                    help="gdn_decode | kda_decode | tiny | gdn_verify | gdn_prefill | gdn_varlen | kda_prefill | "
+                         "backward | prologue | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -518,22 +613,27 @@ def main():
     if only in (None, "gdn_decode"):
         head = bench_gdn_decode(torch, gdr, synth, args.steps, args.warmup,
                                 want_cpu=(only is None and not args.no_cpu_baseline))
+    want_cpu = only is None and not args.no_cpu_baseline
     if only in (None, "kda_decode"):
         extra["kda_decode_b256_h32_d128"] = bench_kda_decode(torch, gdr, synth, args.steps,
-                                                             args.warmup)
+                                                             args.warmup, want_cpu)
+    if only in (None, "tiny"):
+        extra["gdn_tiny_f32"] = bench_tiny(torch, gdr, synth, args.steps, args.warmup, want_cpu)
     if only in (None, "gdn_verify"):
         for save in (True, False):
             r = bench_gdn_verify(torch, gdr, synth, args.steps, args.warmup, T=4, save=save)
             extra[r["workload"]] = r
     if only in (None, "gdn_prefill"):
         extra["gdn_prefill_b4_t8192_h32_d128"] = bench_prefill(
-            torch, gdr, synth, "gdn_prefill_b4_t8192_h32_d128", max(5, args.steps // 2), 2)
+            torch, gdr, synth, "gdn_prefill_b4_t8192_h32_d128", max(5, args.steps // 2), 2,
+            want_cpu=want_cpu)
     if only in (None, "gdn_varlen"):
         r = bench_gdn_varlen(torch, gdr, synth, args.steps, 2)
         extra[r["workload"]] = r
     if only in (None, "kda_prefill"):
         extra["kda_prefill_b1_t32768_h32_d128"] = bench_prefill(
-            torch, gdr, synth, "kda_prefill_b1_t32768_h32_d128", max(5, args.steps // 2), 2)
+            torch, gdr, synth, "kda_prefill_b1_t32768_h32_d128", max(5, args.steps // 2), 2,
+            want_cpu=want_cpu)
     if only in (None, "backward"):
         for name in ("gdn_prefill_b4_t8192_h32_d128", "kda_prefill_b1_t32768_h32_d128"):
             r = bench_backward(torch, gdr, synth, name, max(3, args.steps // 4), 1)

@@ -21,7 +21,7 @@ __all__ = [
     "gdr_chunk_prefill_varlen_workspace_bytes", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
     "gdr_abi_version", "EXPORTED_SYMBOLS", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
     "PRO_L2NORM_QK", "PRO_SIGMOID", "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
-    "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex",
+    "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex", "SCHED_FUSED", "SCHED_SPLIT",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,7 +30,13 @@ _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 # input prologue flags of the *_ex calls (include/gdr.h: GDR_PRO_*)
 PRO_L2NORM_QK = 1
 PRO_SIGMOID = 2
+# schedule of the bf16 chunked prefill (include/gdr.h: GDR_SCHED_*); neither
+# bit = the default (fused for GDN, split for KDA)
+SCHED_FUSED = 4
+SCHED_SPLIT = 8
 EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
+                    "gdr_chunk_prefill_workspace_bytes_ex",
+                    "gdr_chunk_prefill_varlen_workspace_bytes_ex",
                     "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex",
                     "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
                     "gdr_decode_multi", "gdr_chunk_prefill",
@@ -86,6 +92,10 @@ def load_library():
     lib.gdr_chunk_prefill_varlen.restype = i
     lib.gdr_chunk_prefill_varlen_workspace_bytes.argtypes = [i] * 8
     lib.gdr_chunk_prefill_varlen_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdr_chunk_prefill_workspace_bytes_ex.argtypes = [i] * 9
+    lib.gdr_chunk_prefill_workspace_bytes_ex.restype = ctypes.c_size_t
+    lib.gdr_chunk_prefill_varlen_workspace_bytes_ex.argtypes = [i] * 9
+    lib.gdr_chunk_prefill_varlen_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.gdr_status_string.argtypes = [i]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_abi_version.argtypes = []
@@ -117,6 +127,24 @@ def _stream(stream) -> ctypes.c_void_p:
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _workspace(need: int, device, stream):
+    """A workspace of `need` bytes for one call launched on `stream`.
+
+    The caching allocator ties a block to the stream current at allocation
+    and may hand it out again once the tensor is freed, so a block used by a
+    launch on another stream is recorded on that stream: it is not reused
+    before the launch's work there has completed.
+    """
+    if not need:
+        return None
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+        if s.cuda_stream != torch.cuda.current_stream(device).cuda_stream:
+            ws.record_stream(s)
+    return ws
 
 
 def _same_device(*ts):
@@ -220,9 +248,11 @@ def _decode_multi(flags, gate, q, k, v, alpha, beta, state, o, states, scale, st
 
 
 def gdr_chunk_prefill_workspace_bytes(gate: str, dtype, B: int, T: int, H: int, dk: int,
-                                      dv: int, chunk: int = CHUNK) -> int:
-    return int(load_library().gdr_chunk_prefill_workspace_bytes(
-        GATES[gate], _DTYPES[dtype], B, T, H, dk, dv, chunk))
+                                      dv: int, chunk: int = CHUNK, flags: int = 0) -> int:
+    """Workspace bytes of a chunked prefill with these prologue and schedule
+    ``flags`` (0: the default schedule)."""
+    return int(load_library().gdr_chunk_prefill_workspace_bytes_ex(
+        GATES[gate], _DTYPES[dtype], int(flags), B, T, H, dk, dv, chunk))
 
 
 def gdr_chunk_prefill(gate: str, q, k, v, alpha, beta, state_in, state_out, o,
@@ -242,8 +272,9 @@ def gdr_chunk_prefill(gate: str, q, k, v, alpha, beta, state_in, state_out, o,
 def gdr_chunk_prefill_ex(gate: str, q, k, v, alpha, beta, state_in, state_out, o, flags: int = 0,
                          scale: float = 1.0, workspace=None, chunk: int = CHUNK,
                          stream=None) -> None:
-    """:func:`gdr_chunk_prefill` with an input prologue (``flags`` as in
-    :func:`gdr_decode_step_ex`)."""
+    """:func:`gdr_chunk_prefill` with an input prologue and a schedule choice:
+    ``flags`` ORs the PRO_* bits of :func:`gdr_decode_step_ex` with at most
+    one of SCHED_FUSED, SCHED_SPLIT (bf16 only)."""
     _chunk_prefill(int(flags), gate, q, k, v, alpha, beta, state_in, state_out, o, scale,
                    workspace, chunk, stream)
 
@@ -265,9 +296,8 @@ def _chunk_prefill(flags, gate, q, k, v, alpha, beta, state_in, state_out, o, sc
         raise ValueError("alpha and beta must be fp32")
     _same_device(q, k, v, alpha, beta, state_in, state_out, o, workspace)
     if workspace is None:  # allocate what this call needs (callers that time or capture pass their own)
-        need = gdr_chunk_prefill_workspace_bytes(gate, q.dtype, B, T, H, dk, dv, chunk)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(gdr_chunk_prefill_workspace_bytes(gate, q.dtype, B, T, H, dk, dv, chunk,
+                                                                 flags or 0), q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
     rest = (float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
@@ -280,9 +310,10 @@ def _chunk_prefill(flags, gate, q, k, v, alpha, beta, state_in, state_out, o, sc
 
 
 def gdr_chunk_prefill_varlen_workspace_bytes(gate: str, dtype, N: int, max_T: int, H: int,
-                                             dk: int, dv: int, chunk: int = CHUNK) -> int:
-    return int(load_library().gdr_chunk_prefill_varlen_workspace_bytes(
-        GATES[gate], _DTYPES[dtype], N, max_T, H, dk, dv, chunk))
+                                             dk: int, dv: int, chunk: int = CHUNK,
+                                             flags: int = 0) -> int:
+    return int(load_library().gdr_chunk_prefill_varlen_workspace_bytes_ex(
+        GATES[gate], _DTYPES[dtype], int(flags), N, max_T, H, dk, dv, chunk))
 
 
 def gdr_chunk_prefill_varlen_ex(gate: str, q, k, v, alpha, beta, cu_seqlens, state_slots, states,
@@ -336,9 +367,8 @@ def _prefill_varlen(flags, gate, q, k, v, alpha, beta, cu_seqlens, state_slots, 
         cu = cu_seqlens.cpu()
         max_seqlen = int((cu[1:] - cu[:-1]).max()) if N > 0 else 0
     if workspace is None:
-        need = gdr_chunk_prefill_varlen_workspace_bytes(gate, q.dtype, N, max_seqlen, H, dk, dv, chunk)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(gdr_chunk_prefill_varlen_workspace_bytes(
+            gate, q.dtype, N, max_seqlen, H, dk, dv, chunk, flags or 0), q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
     rest = (N, total_T, int(max_seqlen), H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k), _ptr(v),
@@ -385,9 +415,8 @@ def gdr_chunk_backward(gate: str, q, k, v, alpha, beta, state_in, grad_o, grad_s
     _same_device(q, k, v, alpha, beta, state_in, grad_o, grad_state_out, grad_q, grad_k, grad_v,
                  grad_alpha, grad_beta, grad_state_in, workspace)
     if workspace is None:
-        need = gdr_chunk_backward_workspace_bytes(gate, q.dtype, B, T, H, dk, dv, chunk)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(gdr_chunk_backward_workspace_bytes(gate, q.dtype, B, T, H, dk, dv, chunk),
+                               q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().gdr_chunk_backward(
         GATES[gate], _DTYPES[q.dtype], B, T, H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k), _ptr(v),

@@ -59,12 +59,26 @@ inline int status_of(hipError_t e) {
     return e == hipSuccess ? GDR_OK : e == hipErrorInvalidConfiguration ? GDR_ERR_BAD_SHAPE : GDR_ERR_HIP;
 }
 
-inline bool flags_ok(int flags) { return (flags & ~(GDR_PRO_L2NORM_QK | GDR_PRO_SIGMOID)) == 0; }
-// The bf16 prefill schedules normalise q, k where the chunk-local products
-// are formed: the fused GDN kernel and the split KDA kernels.
-inline bool norm_supported(int flags, int gate, int dtype) {
-    return !(flags & GDR_PRO_L2NORM_QK) || dtype != GDR_DTYPE_BF16 ||
-           gdr::prefill_bf16_split(gate == GDR_GATE_KDA) == (gate == GDR_GATE_KDA);
+constexpr int kProFlags = GDR_PRO_L2NORM_QK | GDR_PRO_SIGMOID;
+constexpr int kSchedFlags = GDR_SCHED_FUSED | GDR_SCHED_SPLIT;
+// decode calls: prologue bits only
+inline bool flags_ok(int flags) { return (flags & ~kProFlags) == 0; }
+// prefill calls: prologue bits and at most one schedule bit
+inline bool prefill_flags_ok(int flags) {
+    return (flags & ~(kProFlags | kSchedFlags)) == 0 && (flags & kSchedFlags) != kSchedFlags;
+}
+// The schedule bits against the dtype and gate, and the prologue against the
+// schedule that runs: only bf16 has two schedules, KDA runs split only, and
+// the bf16 schedules normalise q, k where the kernel forming the chunk-local
+// products stages them itself (GDN fused, KDA split).
+int schedule_status(int flags, int gate, int dtype) {
+    const int sched = flags & kSchedFlags;
+    if (dtype != GDR_DTYPE_BF16) return sched ? GDR_ERR_UNSUPPORTED : GDR_OK;
+    const int kda = gate == GDR_GATE_KDA;
+    if (kda && (sched & GDR_SCHED_FUSED)) return GDR_ERR_UNSUPPORTED;
+    if ((flags & GDR_PRO_L2NORM_QK) && !kda && gdr::prefill_bf16_split(kda, flags))
+        return GDR_ERR_UNSUPPORTED;
+    return GDR_OK;
 }
 
 int check_enums(int gate, int dtype) {
@@ -89,7 +103,7 @@ const char* gdr_status_string(int status) {
         case GDR_ERR_MISALIGNED:
             return "GDR_ERR_MISALIGNED: tensors need 16-byte alignment (beta and GDN alpha 4-byte)";
         case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace missing or too small";
-        case GDR_ERR_BAD_ENUM: return "GDR_ERR_BAD_ENUM: unknown gate mode, dtype or prologue flag";
+        case GDR_ERR_BAD_ENUM: return "GDR_ERR_BAD_ENUM: unknown gate mode, dtype or flag";
         case GDR_ERR_HIP: return "GDR_ERR_HIP: the HIP runtime rejected a launch";
         case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: two state buffers (partially) overlap";
         default: return "unknown gdr status";
@@ -163,13 +177,19 @@ int gdr_decode_multi_ex(int gate, int dtype, int flags, int B, int T, int H, int
 
 size_t gdr_chunk_prefill_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
                                          int dv, int chunk) {
-    if (check_enums(gate, dtype) != GDR_OK || chunk != 64 || B < 0 || H < 0 || T < 0 ||
+    return gdr_chunk_prefill_workspace_bytes_ex(gate, dtype, 0, B, T, H, dk, dv, chunk);
+}
+
+size_t gdr_chunk_prefill_workspace_bytes_ex(int gate, int dtype, int flags, int B, int T, int H,
+                                            int dk, int dv, int chunk) {
+    if (check_enums(gate, dtype) != GDR_OK || !prefill_flags_ok(flags) ||
+        schedule_status(flags, gate, dtype) != GDR_OK || chunk != 64 || B < 0 || H < 0 || T < 0 ||
         !head_dim_ok(dk) || !head_dim_ok(dv) || !sizes_ok(B, T, H, dk, dv))
         return 0;
-    // The fp32 path keeps its intermediates on chip; the bf16 path may stage
-    // per-chunk images of its chunk-local products.
+    // The fp32 path keeps its intermediates on chip; the bf16 path's split
+    // schedule stages per-chunk images of its chunk-local products.
     if (dtype != GDR_DTYPE_BF16) return 0;
-    return gdr::prefill_bf16_workspace(gate == GDR_GATE_KDA, B, T, H, dk);
+    return gdr::prefill_bf16_workspace(gate == GDR_GATE_KDA, flags, B, T, H, dk);
 }
 
 int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
@@ -188,12 +208,12 @@ int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, in
                          void* stream) {
     int st = check_enums(gate, dtype);
     if (st != GDR_OK) return st;
-    if (!flags_ok(flags)) return GDR_ERR_BAD_ENUM;
+    if (!prefill_flags_ok(flags)) return GDR_ERR_BAD_ENUM;
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
-    if (!norm_supported(flags, gate, dtype)) return GDR_ERR_UNSUPPORTED;
+    if ((st = schedule_status(flags, gate, dtype)) != GDR_OK) return st;
     if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
-    const size_t need = gdr_chunk_prefill_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk);
+    const size_t need = gdr_chunk_prefill_workspace_bytes_ex(gate, dtype, flags, B, T, H, dk, dv, chunk);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
     if (B == 0 || H == 0) return GDR_OK;
     if (!state_out) return GDR_ERR_NULL_PTR;
@@ -212,7 +232,7 @@ int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, in
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     gdr::Opts opt;
-    opt.pro = flags;
+    opt.pro = flags & kProFlags;
     hipError_t e;
     if (T == 0) {
         e = gdr::launch_state_copy(state_in, state_out, n_state, s);
@@ -225,14 +245,20 @@ int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, in
                                      static_cast<const gdr::bf16_t*>(q),
                                      static_cast<const gdr::bf16_t*>(k),
                                      static_cast<const gdr::bf16_t*>(v), alpha, beta, state_in,
-                                     state_out, static_cast<gdr::bf16_t*>(o), workspace, s, opt);
+                                     state_out, static_cast<gdr::bf16_t*>(o), workspace, s, flags,
+                                     opt);
     }
     return status_of(e);
 }
 
 size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int max_T, int H,
                                                 int dk, int dv, int chunk) {
-    return gdr_chunk_prefill_workspace_bytes(gate, dtype, N, max_T, H, dk, dv, chunk);
+    return gdr_chunk_prefill_workspace_bytes_ex(gate, dtype, 0, N, max_T, H, dk, dv, chunk);
+}
+
+size_t gdr_chunk_prefill_varlen_workspace_bytes_ex(int gate, int dtype, int flags, int N,
+                                                   int max_T, int H, int dk, int dv, int chunk) {
+    return gdr_chunk_prefill_workspace_bytes_ex(gate, dtype, flags, N, max_T, H, dk, dv, chunk);
 }
 
 int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T, int H, int dk,
@@ -254,14 +280,15 @@ int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total
                                 void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_enums(gate, dtype);
     if (st != GDR_OK) return st;
-    if (!flags_ok(flags)) return GDR_ERR_BAD_ENUM;
+    if (!prefill_flags_ok(flags)) return GDR_ERR_BAD_ENUM;
     if (N < 0 || total_T < 0 || max_T < 0 || H < 0 || n_slots < 0) return GDR_ERR_BAD_SHAPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
-    if (!norm_supported(flags, gate, dtype)) return GDR_ERR_UNSUPPORTED;
+    if ((st = schedule_status(flags, gate, dtype)) != GDR_OK) return st;
     if (!sizes_ok(1, total_T, H, dk, dv) || !sizes_ok(N, max_T, H, dk, dv) ||
         !sizes_ok(n_slots, 1, H, dk, dv))
         return GDR_ERR_BAD_SHAPE;
-    const size_t need = gdr_chunk_prefill_varlen_workspace_bytes(gate, dtype, N, max_T, H, dk, dv, chunk);
+    const size_t need =
+        gdr_chunk_prefill_varlen_workspace_bytes_ex(gate, dtype, flags, N, max_T, H, dk, dv, chunk);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
     if (N == 0 || H == 0) return GDR_OK;
     if (!cu_seqlens || !state_slots || !states) return GDR_ERR_NULL_PTR;
@@ -279,7 +306,7 @@ int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total
     vl.has = has_state;
     vl.n_slots = n_slots;
     vl.total = total_T;
-    vl.pro = flags;
+    vl.pro = flags & kProFlags;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == GDR_DTYPE_F32) {
@@ -291,7 +318,7 @@ int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total
                                      static_cast<const gdr::bf16_t*>(q),
                                      static_cast<const gdr::bf16_t*>(k),
                                      static_cast<const gdr::bf16_t*>(v), alpha, beta, states,
-                                     states, static_cast<gdr::bf16_t*>(o), workspace, s, vl);
+                                     states, static_cast<gdr::bf16_t*>(o), workspace, s, flags, vl);
     }
     return status_of(e);
 }

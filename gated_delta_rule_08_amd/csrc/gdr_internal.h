@@ -87,15 +87,17 @@ hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, floa
                               const float* alpha, const float* beta, const float* state_in,
                               float* state_out, float* o, hipStream_t s, const Opts& vl = Opts());
 
-// The bf16 prefill uses `workspace` (at least prefill_bf16_workspace(...)
-// bytes) when its split schedule is selected, and ignores it otherwise.
+// The bf16 prefill runs its split schedule (chunk-local kernel, then chain
+// kernel, `workspace` of at least prefill_bf16_workspace(...) bytes) when
+// prefill_bf16_split(kda, flags) holds, else the fused kernel (no
+// workspace).  flags: the GDR_SCHED_* bits of the call (validated).
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
                                float* state_out, bf16_t* o, void* workspace, hipStream_t s,
-                               const Opts& vl = Opts());
-bool prefill_bf16_split(int kda);
-size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk);
+                               int flags, const Opts& vl = Opts());
+bool prefill_bf16_split(int kda, int flags);
+size_t prefill_bf16_workspace(int kda, int flags, int B, int T, int H, int dk);
 
 // Backward of the chunked recurrence (fp32 arithmetic; q, k, v, d_o, dq, dk,
 // dv in the element type `dtype`).  ws: backward_workspace_floats(...) floats.

@@ -45,8 +45,6 @@
 // that step is read in the same k order, which keeps every product exact
 // without any register shuffle.
 #include <algorithm>
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "gdr_internal.h"
@@ -1660,7 +1658,9 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
                                  : hipSuccess;
     };
     hipError_t e;
-    if (!img) {
+    if constexpr (KDA) {
+        if (!img) return hipErrorInvalidValue;  // KDA runs the split schedule only
+    } else if (!img) {
         auto kern = prefill_bf16_kernel<DK, NSW, KDA, kFused>;
         constexpr int fused_lds = L::fBytes(KDA) + (L::vstage(kFused, KDA) ? NSW * L::VST : 0);
         if ((e = set_lds(reinterpret_cast<const void*>(kern), fused_lds)) != hipSuccess) return e;
@@ -1736,19 +1736,15 @@ int prefill_bf16_slice_width(int B, int H, int dv) {
 }
 
 // Which bf16 prefill schedule runs: the split one (chunk-local kernel + chain
-// kernel, needs a workspace) or the fused one.  GDR_PREFILL_PATH=fused|split
-// overrides the default, which is split for KDA (its chunk-local work is the
-// expensive part, and the fused kernel would repeat it for every value
-// slice) and fused for GDN.
-bool prefill_bf16_split(int kda) {
-    const char* env = getenv("GDR_PREFILL_PATH");
-    if (env && !strcmp(env, "fused")) return false;
-    if (env && !strcmp(env, "split")) return true;
-    return kda != 0;
+// kernel, needs a workspace) or the fused one.  KDA always runs split (its
+// chunk-local work is the expensive part, and a fused kernel would repeat it
+// for every value slice); GDN runs fused unless GDR_SCHED_SPLIT asks.
+bool prefill_bf16_split(int kda, int flags) {
+    return kda != 0 || (flags & GDR_SCHED_SPLIT) != 0;
 }
 
-size_t prefill_bf16_workspace(int kda, int B, int T, int H, int dk) {
-    if (!prefill_bf16_split(kda) || T <= 0 || B <= 0 || H <= 0) return 0;
+size_t prefill_bf16_workspace(int kda, int flags, int B, int T, int H, int dk) {
+    if (!prefill_bf16_split(kda, flags) || T <= 0 || B <= 0 || H <= 0) return 0;
     size_t img;
     switch (dk) {
         case 16: img = image_bytes<16>(kda); break;
@@ -1764,9 +1760,9 @@ hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, flo
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
                                float* state_out, bf16_t* o, void* workspace, hipStream_t s,
-                               const Opts& vl) {
+                               int flags, const Opts& vl) {
     const int dvs = prefill_bf16_slice_width(B, H, dv);
-    unsigned char* img = prefill_bf16_split(kda) ? static_cast<unsigned char*>(workspace) : nullptr;
+    unsigned char* img = prefill_bf16_split(kda, flags) ? static_cast<unsigned char*>(workspace) : nullptr;
     switch (dk) {
         case 16: return dispatch_gate<16>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
         case 32: return dispatch_gate<32>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 /* Gate mode: scalar gate (Gated DeltaNet) or channel-wise gate (Kimi Delta
  * Attention), the two mixers of the pages' §2.A. */
@@ -102,9 +102,32 @@ int gdr_decode_step(int gate, int dtype, int B, int H, int dk, int dv, float sca
  *                       sigmoid(alpha) and sigmoid(beta) (the chunked paths
  *                       take log2 sigmoid(alpha) directly, so very negative
  *                       logits keep their size instead of underflowing).
- * Other bits return GDR_ERR_BAD_ENUM.
+ * Other bits (apart from the prefill calls' GDR_SCHED_* bits below) return
+ * GDR_ERR_BAD_ENUM.
  */
 enum { GDR_PRO_L2NORM_QK = 1, GDR_PRO_SIGMOID = 2 };
+
+/*
+ * Schedule flags of the bf16 chunked prefill (gdr_chunk_prefill_ex,
+ * gdr_chunk_prefill_varlen_ex and their workspace queries; OR-ed with the
+ * GDR_PRO_* bits).  With dtype BF16 the prefill has two schedules:
+ *   GDR_SCHED_FUSED  one kernel per (head, value slice) that forms each
+ *                    chunk's local products itself while it advances the
+ *                    state; no workspace.  GDN only.
+ *   GDR_SCHED_SPLIT  a chunk-local kernel per (head, chunk) writes each
+ *                    chunk's products to the workspace, then a chain kernel
+ *                    per (head, value slice) runs the state through them.
+ * Neither bit: the default, FUSED for GDN and SPLIT for KDA (the channel
+ * gate makes the chunk-local work the expensive part, which the fused kernel
+ * would repeat for every value slice).  Prologue support: GDR_PRO_SIGMOID
+ * runs in both schedules; GDR_PRO_L2NORM_QK runs in GDN FUSED and KDA SPLIT
+ * (where the kernel that forms the chunk-local products stages q and k
+ * itself) and returns GDR_ERR_UNSUPPORTED with GDN SPLIT.  Both bits set is
+ * GDR_ERR_BAD_ENUM; GDR_SCHED_FUSED with KDA, or either bit with dtype F32
+ * (one schedule), is GDR_ERR_UNSUPPORTED.  The decode calls take no schedule
+ * bits (GDR_ERR_BAD_ENUM).
+ */
+enum { GDR_SCHED_FUSED = 4, GDR_SCHED_SPLIT = 8 };
 
 /*
  * gdr_decode_step with an input prologue (flags: GDR_PRO_*): the same step
@@ -185,13 +208,17 @@ int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, 
 size_t gdr_chunk_prefill_workspace_bytes(int gate, int dtype, int B, int T, int H,
                                          int dk, int dv, int chunk);
 
+/* Bytes of workspace gdr_chunk_prefill_ex needs with these flags (0 when the
+ * arguments or flags are invalid, or no scratch is needed). */
+size_t gdr_chunk_prefill_workspace_bytes_ex(int gate, int dtype, int flags, int B, int T, int H,
+                                            int dk, int dv, int chunk);
+
 /*
- * gdr_chunk_prefill with an input prologue (flags: GDR_PRO_*), same
- * arguments and workspace.  flags == 0 is gdr_chunk_prefill exactly.
- * GDR_PRO_SIGMOID runs in every schedule; GDR_PRO_L2NORM_QK runs in the fp32
- * path and in the default bf16 schedules (the fused GDN kernel, the split KDA
- * kernels), and returns GDR_ERR_UNSUPPORTED when GDR_PREFILL_PATH selects
- * the other bf16 schedule.
+ * gdr_chunk_prefill with an input prologue and a schedule choice (flags:
+ * GDR_PRO_* | GDR_SCHED_*), taking a workspace of at least
+ * gdr_chunk_prefill_workspace_bytes_ex(..., flags, ...) bytes.  flags == 0
+ * is gdr_chunk_prefill exactly.  Both prologue flags run in the fp32 path;
+ * the bf16 schedules support them as listed with GDR_SCHED_*.
  */
 int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
                          int chunk, float scale,
@@ -235,9 +262,11 @@ int gdr_chunk_prefill_varlen(int gate, int dtype, int N, int total_T, int max_T,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * gdr_chunk_prefill_varlen with an input prologue (flags: GDR_PRO_*), with
- * the same support as gdr_chunk_prefill_ex.  flags == 0 is
- * gdr_chunk_prefill_varlen exactly.
+ * gdr_chunk_prefill_varlen with an input prologue and a schedule choice
+ * (flags: GDR_PRO_* | GDR_SCHED_*), with the same support as
+ * gdr_chunk_prefill_ex and a workspace of at least
+ * gdr_chunk_prefill_varlen_workspace_bytes_ex(..., flags, ...) bytes.
+ * flags == 0 is gdr_chunk_prefill_varlen exactly.
  */
 int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total_T, int max_T,
                                 int H, int dk, int dv, int chunk, float scale,
@@ -251,6 +280,11 @@ int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total
  * invalid or no scratch is needed). */
 size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int max_T, int H,
                                                 int dk, int dv, int chunk);
+
+/* Bytes of workspace gdr_chunk_prefill_varlen_ex needs with these flags (0
+ * when the arguments or flags are invalid, or no scratch is needed). */
+size_t gdr_chunk_prefill_varlen_workspace_bytes_ex(int gate, int dtype, int flags, int N,
+                                                   int max_T, int H, int dk, int dv, int chunk);
 
 /*
  * Backward pass of the chunked prefill (the training step of the mixers; the

@@ -179,8 +179,8 @@ def varlen(lib, gate=0, dtype=1, N=3, total_T=100, max_T=64, H=2, dk=64, dv=64, 
                                         *p[:9], n_slots, p[9], ws, ws_bytes, None)
 
 
-def test_prefill_varlen_validation(lib, monkeypatch):
-    monkeypatch.setenv("GDR_PREFILL_PATH", "fused")  # no workspace needed for GDN bf16
+def test_prefill_varlen_validation(lib):
+    # GDN bf16 runs the fused schedule by default: no workspace needed
     assert varlen(lib, gate=5) == ENUM
     assert varlen(lib, N=-1) == SHAPE
     assert varlen(lib, max_T=-1) == SHAPE
@@ -198,7 +198,6 @@ def test_prefill_varlen_validation(lib, monkeypatch):
     ptrs[8] = ctypes.c_void_p(P[8].value + 4)  # states: 16-byte alignment
     assert varlen(lib, ptrs=ptrs) == MISAL
     assert varlen(lib, N=0, ptrs=[None] * 10) == OK
-    monkeypatch.setenv("GDR_PREFILL_PATH", "split")
     import torch
     need = gdr.gdr_chunk_prefill_varlen_workspace_bytes("kda", torch.bfloat16, 3, 64, 2, 64, 64)
     assert need > 0
@@ -206,10 +205,9 @@ def test_prefill_varlen_validation(lib, monkeypatch):
     assert varlen(lib, gate=1, ws=ctypes.c_void_p(0x100000), ws_bytes=need - 1) == WS
 
 
-def test_workspace(lib, monkeypatch):
+def test_workspace(lib):
     import torch
-    monkeypatch.delenv("GDR_PREFILL_PATH", raising=False)
-    # GDN bf16 and every fp32 prefill keep their intermediates on chip
+    # GDN bf16 (default schedule) and every fp32 prefill keep their intermediates on chip
     assert lib.gdr_chunk_prefill_workspace_bytes(0, 1, 4, 8192, 32, 128, 128, 64) == 0
     assert lib.gdr_chunk_prefill_workspace_bytes(1, 0, 1, 256, 2, 128, 128, 64) == 0
     # KDA bf16 stages one image per (b, h, chunk) of a range of chunks; a range
@@ -225,13 +223,47 @@ def test_workspace(lib, monkeypatch):
     # a missing or short workspace is rejected before any device work
     assert prefill(lib, gate=1) == WS
     assert prefill(lib, gate=1, ws=P[8], ws_bytes=1024) == WS
-    # the schedule can be forced either way
-    monkeypatch.setenv("GDR_PREFILL_PATH", "fused")
-    assert gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 64, 1, 128, 128) == 0
-    monkeypatch.setenv("GDR_PREFILL_PATH", "split")
+    # the schedule is an argument: GDN can run split; KDA runs split only
+    SF, SS = gdr.SCHED_FUSED, gdr.SCHED_SPLIT
+    wsx = lib.gdr_chunk_prefill_workspace_bytes_ex
+    assert wsx(1, 1, SS, 1, 64, 1, 128, 128, 64) == n1
+    assert wsx(1, 1, SF, 1, 64, 1, 128, 128, 64) == 0          # KDA fused: unsupported
+    assert wsx(0, 1, SF, 1, 64, 1, 128, 128, 64) == 0
     # GDN's image holds only the chunk's small tiles and gate factors
-    g1 = gdr.gdr_chunk_prefill_workspace_bytes("gdn", torch.bfloat16, 1, 64, 1, 128, 128)
+    g1 = gdr.gdr_chunk_prefill_workspace_bytes("gdn", torch.bfloat16, 1, 64, 1, 128, 128, flags=SS)
     assert 0 < g1 < n1 // 3 and g1 % 16 == 0
+    assert wsx(0, 1, SS | 2, 1, 64, 1, 128, 128, 64) == g1      # with the sigmoid prologue
+    assert wsx(0, 1, SS | 1, 1, 64, 1, 128, 128, 64) == 0       # GDN split cannot normalise
+    assert wsx(0, 1, SS | SF, 1, 64, 1, 128, 128, 64) == 0      # both schedules: invalid
+    assert wsx(0, 0, SS, 1, 64, 1, 128, 128, 64) == 0           # fp32: one schedule
+    assert lib.gdr_chunk_prefill_varlen_workspace_bytes_ex(1, 1, SS, 1, 64, 1, 128, 128, 64) == n1
+    assert lib.gdr_chunk_prefill_varlen_workspace_bytes_ex(0, 1, SS, 1, 64, 1, 128, 128, 64) == g1
+
+
+def test_schedule_flag_validation(lib):
+    """The schedule bits of the prefill calls, checked before the device."""
+    SF, SS = gdr.SCHED_FUSED, gdr.SCHED_SPLIT
+
+    def pre(gate, dtype, flags, ws=None, ws_bytes=0):
+        return lib.gdr_chunk_prefill_ex(gate, dtype, flags, 2, 70, 3, 128, 128, 64, 1.0,
+                                        *([None] * 8), ws, ws_bytes, None)
+
+    assert pre(0, 1, SF | SS) == ENUM
+    assert pre(0, 1, 16) == ENUM
+    assert pre(1, 1, SF) == UNSUP          # KDA has no fused schedule
+    assert pre(0, 0, SF) == UNSUP          # fp32 has one schedule
+    assert pre(1, 0, SS) == UNSUP
+    assert pre(0, 1, SF) == NULL           # valid, inputs missing
+    assert pre(0, 1, SS) == WS             # the split schedule needs its workspace
+    need = lib.gdr_chunk_prefill_workspace_bytes_ex(0, 1, SS, 2, 70, 3, 128, 128, 64)
+    assert pre(0, 1, SS, ws=P[9], ws_bytes=need) == NULL
+    assert pre(1, 1, SS) == WS and pre(1, 1, 0) == WS
+    # the decode calls take no schedule bits
+    p = list(P[:8])
+    assert lib.gdr_decode_step_ex(0, 1, SF, 2, 3, 128, 128, 1.0, *p) == ENUM
+    assert lib.gdr_decode_multi_ex(0, 1, SS, 2, 3, 4, 128, 128, 1.0, *[P[i] for i in range(9)]) == ENUM
+    assert lib.gdr_chunk_prefill_varlen_ex(1, 1, SF, 2, 100, 70, 3, 128, 128, 64, 1.0, *([None] * 9), 4,
+                                           None, None, 0, None) == UNSUP
 
 
 def test_binding_rejects_cpu_tensors():
@@ -242,7 +274,7 @@ def test_binding_rejects_cpu_tensors():
                             torch.zeros(1, 1, 16, 16), torch.zeros(1, 1, 16))
 
 
-def test_prologue_flag_validation(lib, monkeypatch):
+def test_prologue_flag_validation(lib):
     """Unknown prologue bits are BAD_ENUM; the normalising prologue in a bf16
     schedule that does not form the chunk-local products itself is
     UNSUPPORTED; everything is checked before the device is touched."""
@@ -256,15 +288,13 @@ def test_prologue_flag_validation(lib, monkeypatch):
         return lib.gdr_chunk_prefill_ex(gate, dtype, flags, 2, T, 3, 128, 128, 64, 1.0,
                                         *([None] * 8), None, 0, None)
 
-    assert pre(0, 1, 8) == ENUM
-    for path in ("fused", "split"):
-        monkeypatch.setenv("GDR_PREFILL_PATH", path)
-        # GDN normalises in the fused kernel, KDA in the split one
-        assert pre(0, 1, 1) == (NULL if path == "fused" else UNSUP)
-        assert pre(1, 1, 1) == (UNSUP if path == "fused" else WS)
-        assert pre(0, 1, 2) in (NULL, WS)  # the sigmoid runs in every schedule
-        assert pre(1, 0, 3) == NULL        # fp32 path: both
-    monkeypatch.delenv("GDR_PREFILL_PATH")
+    assert pre(0, 1, 16) == ENUM
+    SF, SS = gdr.SCHED_FUSED, gdr.SCHED_SPLIT
+    # GDN normalises in the fused kernel, KDA in the split one
+    assert pre(0, 1, 1 | SF) == NULL and pre(0, 1, 1 | SS) == UNSUP
+    assert pre(1, 1, 1 | SS) == WS and pre(1, 1, 1 | SF) == UNSUP
+    assert pre(0, 1, 2 | SF) == NULL and pre(0, 1, 2 | SS) == WS  # the sigmoid runs in every schedule
+    assert pre(1, 0, 3) == NULL        # fp32 path: both
     assert pre(0, 1, 3) == NULL and pre(1, 1, 3) == WS
 
 
@@ -311,7 +341,7 @@ def test_decode_grid_limit(lib):
     assert lib.gdr_decode_step(1, 1, 35_000_000, 2, 16, 16, 1.0, *p, None) == SHAPE
 
 
-def test_prologue_ex_variants_validation(lib, monkeypatch):
+def test_prologue_ex_variants_validation(lib):
     """The verify and packed variable-length calls take the same flags."""
     p9 = [P[i] for i in range(9)]
     assert lib.gdr_decode_multi_ex(0, 1, 4, 2, 3, 4, 128, 128, 1.0, *p9) == ENUM
@@ -322,10 +352,7 @@ def test_prologue_ex_variants_validation(lib, monkeypatch):
         return lib.gdr_chunk_prefill_varlen_ex(gate, dtype, flags, 2, 100, 70, 3, 128, 128, 64, 1.0,
                                                *([None] * 9), 4, None, None, 0, None)
 
-    assert vl(8) == ENUM
-    monkeypatch.setenv("GDR_PREFILL_PATH", "split")
-    assert vl(1) == UNSUP            # GDN normalises only in the fused kernel
-    monkeypatch.setenv("GDR_PREFILL_PATH", "fused")
-    assert vl(1, gate=1) == UNSUP    # KDA normalises only in the split kernels
-    monkeypatch.delenv("GDR_PREFILL_PATH")
+    assert vl(16) == ENUM
+    assert vl(1 | gdr.SCHED_SPLIT) == UNSUP            # GDN normalises only in the fused kernel
+    assert vl(1 | gdr.SCHED_FUSED, gate=1) == UNSUP    # KDA has no fused schedule
     assert vl(3) == NULL and vl(3, dtype=0) == NULL

@@ -107,8 +107,8 @@ def test_backward_t0_copies_the_state_gradient():
 
 def _full_size(gate, name, heads, seed=31):
     """The backward at the prefill workload's full shape, in the launch
-    configuration the benchmark times; the oracle runs on sampled heads over
-    the whole length."""
+    configuration the benchmark times; the oracle runs on the listed heads
+    (stacked along its batch axis, one call) over the whole length."""
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w)
     B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
@@ -117,22 +117,27 @@ def _full_size(gate, name, heads, seed=31):
     dst = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
     announce("backward %s bf16 full size %s" % (gate, name))
     got = _run(gate, "bf16", inp, do, dst, 1.0)
-    for (b, h) in heads:
-        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
-        s0 = None if inp["s0"] is None else np.ascontiguousarray(inp["s0"][b:b + 1, h:h + 1])
-        ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]), sl(inp["beta"]),
-                              s0, sl(do), np.ascontiguousarray(dst[b:b + 1, h:h + 1]))
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    pick = lambda x: np.ascontiguousarray(x[bs, :, hs][:, :, None])       # [P, T, 1, ...]
+    pick_s = lambda x: np.ascontiguousarray(x[bs, hs][:, None])          # [P, 1, dk, dv]
+    ref = oracle.backward(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(inp["alpha"]),
+                          pick(inp["beta"]), None if inp["s0"] is None else pick_s(inp["s0"]),
+                          pick(do), pick_s(dst))
+    for i, (b, h) in enumerate(heads):
         for key in ("dq", "dk", "dv", "dalpha", "dbeta"):
-            assert_close(got[key][b:b + 1, :, h:h + 1], ref[key], TOL["bf16"], "%s[b=%d,h=%d]" % (key, b, h))
-        assert_close(got["ds0"][b:b + 1, h:h + 1], ref["ds0"], TOL["bf16"], "ds0[b=%d,h=%d]" % (b, h))
+            assert_close(got[key][b, :, h], ref[key][i, :, 0], TOL["bf16"], "%s[b=%d,h=%d]" % (key, b, h))
+        assert_close(got["ds0"][b, h], ref["ds0"][i, 0], TOL["bf16"], "ds0[b=%d,h=%d]" % (b, h))
 
 
 def test_backward_gdn_full_size():
-    _full_size("gdn", "gdn_prefill_b4_t8192_h32_d128", [(0, 0), (3, 31)])
+    """Two heads of every batch entry, the last head of each among them."""
+    _full_size("gdn", "gdn_prefill_b4_t8192_h32_d128",
+               [(0, 0), (0, 31), (1, 13), (1, 31), (2, 22), (2, 31), (3, 5), (3, 31)])
 
 
 def test_backward_kda_full_size():
-    _full_size("kda", "kda_prefill_b1_t32768_h32_d128", [(0, 7)])
+    _full_size("kda", "kda_prefill_b1_t32768_h32_d128", [(0, 0), (0, 7), (0, 19), (0, 31)])
 
 
 @pytest.mark.parametrize("gate", ["gdn", "kda"])

@@ -40,7 +40,7 @@ def _packed_inputs(w, lens, H, seed):
     return {k: cat(k) for k in ("q", "k", "v", "alpha", "beta")}
 
 
-def _run(gate, dtype, inp, lens, slots, has, pool0, max_T=None):
+def _run(gate, dtype, inp, lens, slots, has, pool0, max_T=None, flags=0):
     dev = {k: to_dev(v, dtype if k in ("q", "k", "v") else "f32") for k, v in inp.items()}
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
     sl = torch.tensor(slots, dtype=torch.int32, device="cuda")
@@ -49,18 +49,18 @@ def _run(gate, dtype, inp, lens, slots, has, pool0, max_T=None):
     total_T, H = inp["beta"].shape
     dv = inp["v"].shape[-1]
     o = torch.full((total_T, H, dv), 7.0, device="cuda", dtype=dev["q"].dtype)
-    gdr.gdr_chunk_prefill_varlen(gate, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], cu, sl,
-                                 states, o, has_state=hs, max_seqlen=max_T)
+    gdr.gdr_chunk_prefill_varlen_ex(gate, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], cu, sl,
+                                    states, o, has_state=hs, max_seqlen=max_T, flags=flags)
     torch.cuda.synchronize()
     return to_host64(o), to_host64(states)
 
 
-def _check(gate, dtype, H=3, dk=64, dv=64, lens=LENS, slots=SLOTS, has=HAS):
+def _check(gate, dtype, H=3, dk=64, dv=64, lens=LENS, slots=SLOTS, has=HAS, flags=0):
     w = _workload(gate, dtype, dk, dv)
     inp = _packed_inputs(w, lens, H, seed=40)
     rng = np.random.default_rng(5)
     pool0 = (0.02 * rng.standard_normal((9, H, dk, dv))).astype(np.float32)
-    o, pool = _run(gate, dtype, inp, lens, slots, has, pool0)
+    o, pool = _run(gate, dtype, inp, lens, slots, has, pool0, flags=flags)
     tol = TOL[dtype]
     off = np.concatenate([[0], np.cumsum(lens)])
     for n, L in enumerate(lens):
@@ -78,12 +78,10 @@ def _check(gate, dtype, H=3, dk=64, dv=64, lens=LENS, slots=SLOTS, has=HAS):
         assert np.array_equal(pool[r], pool0[r]), "unused row %d changed" % r
 
 
-@pytest.mark.parametrize("gate", ["gdn", "kda"])
-@pytest.mark.parametrize("path", ["fused", "split"])
-def test_varlen_bf16_matches_oracle(gate, path, monkeypatch):
-    monkeypatch.setenv("GDR_PREFILL_PATH", path)
-    announce("prefill varlen %s bf16 %s" % (gate, path))
-    _check(gate, "bf16")
+@pytest.mark.parametrize("gate,sched", [("gdn", "fused"), ("gdn", "split"), ("kda", "split")])
+def test_varlen_bf16_matches_oracle(gate, sched):
+    announce("prefill varlen %s bf16 %s" % (gate, sched))
+    _check(gate, "bf16", flags={"fused": gdr.SCHED_FUSED, "split": gdr.SCHED_SPLIT}[sched])
 
 
 @pytest.mark.parametrize("gate", ["gdn", "kda"])

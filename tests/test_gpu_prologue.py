@@ -151,16 +151,22 @@ def test_prefill_f32_prologue_matches_oracle(gate):
     _check_prefill(gate, "f32", NORM | SIG, 64, 32, T=130)
 
 
-def test_prefill_sigmoid_in_the_split_gdn_schedule(monkeypatch):
-    monkeypatch.setenv("GDR_PREFILL_PATH", "split")
+def test_prefill_sigmoid_in_the_split_gdn_schedule():
     announce("prefill prologue bf16 gdn split sigmoid")
-    _check_prefill("gdn", "bf16", SIG, 128, 128)
+    _check_prefill("gdn", "bf16", SIG | gdr.SCHED_SPLIT, 128, 128)
 
 
-def test_prefill_sigmoid_in_the_fused_kda_schedule(monkeypatch):
-    monkeypatch.setenv("GDR_PREFILL_PATH", "fused")
-    announce("prefill prologue bf16 kda fused sigmoid")
-    _check_prefill("kda", "bf16", SIG, 64, 64)
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_prefill_prologue_with_explicit_default_schedule(gate):
+    """Naming the default schedule explicitly gives the default call bitwise."""
+    sched = gdr.SCHED_FUSED if gate == "gdn" else gdr.SCHED_SPLIT
+    w = _workload("prefill", gate, "bf16", 64, 64)
+    raw = _raw(w, NORM | SIG, B=2, T=150, H=3, seed=21)
+    d = _dev(raw, "bf16")
+    announce("prefill prologue bf16 %s explicit schedule" % gate)
+    a = _prefill(gate, "bf16", d, NORM | SIG, 2, 150, 3, 64)
+    b = _prefill(gate, "bf16", d, NORM | SIG | sched, 2, 150, 3, 64)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 def test_prefill_gdn_long_sequence_prologue():
