@@ -23,11 +23,21 @@
 //
 // Gates inside the contractions.  GDN: one scalar per token, so the MFMAs run
 // on raw q and k and the factors 2^(G_t - G_j) <= 1, 2^G_t, 2^(G_end - G_t)
-// scale their outputs.  KDA: the decay differs per channel and is folded into
-// the operands around a per-channel reference R = G_end / 2, so every factor
-// stays within 2^(|G_end| / 2); S is scaled by 2^R where it is rounded to bf16.
-// log2(alpha) is floored at -115.4 (alpha ~ e^-80), so alpha == 0 is legal;
-// KDA needs the total log-decay of a channel within one chunk above about -170.
+// scale their outputs; log2(alpha) is floored at -115.4 (alpha ~ e^-80), so
+// alpha == 0 is legal.  KDA: the decay differs per channel, so it has to sit
+// inside the operands.  The state-side operands carry factors <= 1 only:
+// Khat_t = k_t 2^G_t, Qhat_t = q_t 2^G_t, Ktil_t = k_t 2^(G_end - G_t).  A and
+// P factor every pair through the middle of the 16-token block of row t,
+// m_r = G at token 16 r + 7 of the chunk:
+//     2^(G_t - G_j) = 2^(G_t - m_r) 2^(m_r - G_j),
+// with left rows k_t 2^(G_t - m_r) (q_t for P) and, per row block r, right
+// rows k_j 2^(m_r - G_j) for every j up to the end of block r.  alpha is
+// raised to at least 2^-15 per token and channel, so a factor is at most
+// 2^(15 * 8) = 2^120 (t or j at most 8 tokens from the middle of its block)
+// and nothing overflows for any gate; for j before block r the right factor
+// is <= 1, and where it underflows the exact product is below 2^-21.  The
+// floor changes each step's decay by at most 2^-15 of the state (alpha = 0
+// forgets all but 3e-5 of it), below the bf16 rounding of the operands.
 //
 // Mapping.  One workgroup per (b, h, slice of 16*NSW value columns); the value
 // columns of S are independent, so the slices of a head run on different CUs
@@ -74,7 +84,9 @@ constexpr int kPrepWaves = 4;
 // once per value slice, and run it at full occupancy.
 enum : int { kFused = 0, kPrep = 1, kChain = 2 };
 constexpr float kLog2Floor = -115.4f;  // GDN: log2(alpha) floor, alpha ~ e^-80
-constexpr float kMinGate = 3.7252903e-09f;  // KDA: alpha floor 2^-28 (4-token products stay normal)
+constexpr float kKdaMinGate = 3.0517578125e-05f;  // KDA: alpha floor 2^-15 (factors within 2^+-120)
+constexpr int kRR = 160;  // KDA right-operand rows: block r keeps rows 0 .. 16 r + 15 (16 + 32 + 48 + 64)
+__device__ __forceinline__ constexpr int rr_row0(int r) { return 8 * r * (r + 1); }  // first row of block r's set
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
 // but leaves global loads in flight (a full __syncthreads also drains vmcnt,
@@ -157,6 +169,11 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+// Value of lane N of this lane's DPP row (row_share).
+template <int N>
+__device__ __forceinline__ float row_share(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
 template <int N>
 __device__ __forceinline__ float lane_group_sum(float x) {
     x += dpp_f<0xB1>(x);                         // quad_perm [1, 0, 3, 2]
@@ -194,8 +211,7 @@ struct Layout {
     static constexpr int oEg = oBeta + kC * 4;            // GDN 2^G_t [64]
     static constexpr int oEk = oEg + kC * 4;              // GDN 2^(G_end - G_t) [64]
     static constexpr int oGend = oEk + kC * 4;            // 2^G_end per channel (GDN: [0])
-    static constexpr int oSref = oGend + DK * 4;          // KDA 2^R per channel
-    static constexpr int BUF = ((oSref + DK * 4) + 15) / 16 * 16;
+    static constexpr int BUF = ((oGend + DK * 4) + 15) / 16 * 16;
     static constexpr int IMG = (BUF + 1023) / 1024 * 1024;  // image stride (1 KB per copy instruction)
     // prep-private
     static constexpr int oKc = 2 * BUF;                   // KDA Kcheck [64][PK]
@@ -204,12 +220,15 @@ struct Layout {
     static constexpr int oScr = oG + kC * 4;              // fp32 diagonal tiles [4][16][PS]
     static constexpr int bytes = oScr + kPrepWaves * 16 * PS * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
-    // kPrep: only what the A/P products and the inverses read stays in LDS
+    // kPrep: only what the A/P products and the inverses read stays in LDS.
+    // KDA: pKh / pQh hold the left rows k_t 2^(G_t - m_r), q_t 2^(G_t - m_r)
+    // and pKc the right rows of the four row blocks (kRR rows; the image gets
+    // Khat and Qhat instead).
     static constexpr int pKh = 0;
     static constexpr int pQh = kC * PK * 2;
     static constexpr int pBeta = 2 * kC * PK * 2;
     static constexpr int pKc = pBeta + kC * 4;
-    static constexpr int pG = pKc + (KDA ? kC * PK * 2 : 0);
+    static constexpr int pG = pKc + (KDA ? kRR * PK * 2 : 0);
     static constexpr int pScr = pG + kC * 4;
     static constexpr int pA = pScr + kPrepWaves * 16 * PS * 4;  // -A_rk tiles (6)
     static constexpr int pD = pA + 6 * TILE;                     // D_r^{-1} tiles (4)
@@ -410,7 +429,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         if constexpr (MODE == kPrep) return reinterpret_cast<float*>(imgp(c) + off - (LITE ? L::oP : 0));
         else return f32p(c, off);
     };
-    bf16_t* Kc = reinterpret_cast<bf16_t*>(smem + (MODE == kPrep ? L::pKc : L::oKc));  // KDA only
+    bf16_t* Kc = reinterpret_cast<bf16_t*>(smem + (MODE == kPrep ? L::pKc : L::oKc));  // KDA right rows
     // G_t of the chunk being gated / formed (ONEBAR: one per operand set)
     auto sGp = [&](int c) {
         if constexpr (ONEBAR) return reinterpret_cast<float*>(smem + (c % 3) * L::OPS + L::uG);
@@ -426,7 +445,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             const int t = r / W, col = ONEBAR ? perm_pos(DK + r % W) : DK + r % W;
             prep_lds_b(c, L::oKh, L::pKh)[t * L::PK + col] = 0;
             prep_lds_b(c, L::oQh, L::pQh)[t * L::PK + col] = 0;
-            if (KDA && c == 0) Kc[t * L::PK + col] = 0;
+        }
+        if constexpr (KDA && MODE == kPrep) {
+            for (int idx = tid; idx < kRR * W; idx += blockDim.x)
+                Kc[(idx / W) * L::PK + DK + idx % W] = 0;
         }
     }
     // kPrep: the same padding in the image of chunk c, which the chain reads
@@ -581,57 +603,95 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 qz[u] = valid[u] ? R.qr[u] : make_uint4(0, 0, 0, 0);
             }
             if constexpr (KDA) {
-                // Pass 1, per channel: product of this lane's 4 gates, its log2
-                // scanned across the 16 lanes, and the lane's base factor
-                // 2^(off - R) with R = G_end / 2.  Pass 2 walks the tokens with
-                // a running product (2^(G_t - R)) and writes each row at once.
-                float run[8], ce[8], ga[NA];
+                // Lane = one 4-token group (tokens 4 tg .. 4 tg + 3) of 8
+                // channels; the 16 groups of the chunk are one DPP row.
+                // Pass 1, per channel: the product of the lane's 4 gates, its
+                // log2 scanned across the row (G at each group's end, inc),
+                // and the lane's factors from X = inc - log2(product) (G
+                // before the group): 2^X, 2^(X - m_b) (b = the lane's block),
+                // 2^(G_end - inc) and 2^(m_r - inc) for the blocks r >= b.
+                // Pass 2 walks the tokens forward with the running product
+                // 2^(G_t - X) (Khat, Qhat, left rows), pass 3 backward with
+                // 2^(inc - G_t) (Ktil, right rows).  Every factor lies within
+                // 2^+-120 (see the file header).
+                // The two halves of the octet (4 channels each) run one after
+                // the other to bound the live factors (rows go out as 8-byte
+                // pieces).
+                const int blk = tg >> 2;
 #pragma unroll
-                for (int i = 0; i < NA; ++i) ga[i] = fmaxf(sig ? sigmoid_f(R.a[i]) : R.a[i], kMinGate);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int cc = c8 + 4 * hh;
+                    float ga[4][4], cK[4], cD[4], cT[4], cR[4][4];  // [token][channel], [.][channel]
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float p = 1.f;
+                    for (int u = 0; u < 4; ++u)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) p *= valid[u] ? ga[8 * u + e] : 1.f;
-                    const float tot = lg2(p);
-                    const float inc = row_scan(tot);
-                    const float end = __shfl(inc, 15, 16);
-                    run[e] = ex2(inc - tot - 0.5f * end);
-                    ce[e] = ex2(0.5f * end);  // 2^(G_end - R) = 2^R
-                    if (tg == 0) {
-                        prep_out_f(c, L::oGend)[c8 + e] = ex2(end);
-                        prep_out_f(c, L::oSref)[c8 + e] = ce[e];
+                        for (int e = 0; e < 4; ++e) {
+                            const float a = R.a[8 * u + 4 * hh + e];
+                            ga[u][e] = valid[u] ? fmaxf(sig ? sigmoid_f(a) : a, kKdaMinGate) : 1.f;
+                        }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float tot = lg2(ga[0][e] * ga[1][e] * ga[2][e] * ga[3][e]);
+                        const float inc = row_scan(tot);
+                        const float X = inc - tot;
+                        const float gend = row_share<15>(inc);
+                        const float m0 = row_share<1>(inc), m1 = row_share<5>(inc);
+                        const float m2 = row_share<9>(inc), m3 = row_share<13>(inc);
+                        const float mb = blk == 0 ? m0 : blk == 1 ? m1 : blk == 2 ? m2 : m3;
+                        cK[e] = ex2(X);
+                        cD[e] = ex2(X - mb);
+                        cT[e] = ex2(gend - inc);
+                        cR[0][e] = blk == 0 ? ex2(m0 - inc) : 0.f;
+                        cR[1][e] = blk <= 1 ? ex2(m1 - inc) : 0.f;
+                        cR[2][e] = blk <= 2 ? ex2(m2 - inc) : 0.f;
+                        cR[3][e] = ex2(m3 - inc);
+                        if (tg == 0) prep_out_f(c, L::oGend)[cc + e] = ex2(gend);
                     }
+                    auto kval = [&](int u, int e) { return bf_at(kz[u], 4 * hh + e) * nk[u]; };
+                    auto qval = [&](int u, int e) { return bf_at(qz[u], 4 * hh + e) * nq[u]; };
+                    float run[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int t = 4 * tg + u;
+                        bf16x4 kh, qh, dl, dq;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            run[e] = u == 0 ? ga[0][e] : run[e] * ga[u][e];  // 2^(G_t - X)
+                            const float kp = kval(u, e) * run[e], qp = qval(u, e) * run[e];
+                            kh[e] = static_cast<__bf16>(kp * cK[e]);
+                            qh[e] = static_cast<__bf16>(qp * cK[e]);
+                            dl[e] = static_cast<__bf16>(kp * cD[e]);
+                            dq[e] = static_cast<__bf16>(qp * cD[e]);
+                        }
+                        *reinterpret_cast<bf16x4*>(Kh + t * L::PK + cc) = dl;
+                        *reinterpret_cast<bf16x4*>(Qh + t * L::PK + cc) = dq;
+                        *reinterpret_cast<bf16x4*>(KhI + t * L::PK + cc) = kh;
+                        *reinterpret_cast<bf16x4*>(QhI + t * L::PK + cc) = qh;
+                    }
+                    uint32_t ktw[4][2];
+                    float rev[4];
+#pragma unroll
+                    for (int u = 3; u >= 0; --u) {
+                        const int t = 4 * tg + u;
+                        bf16x4 rr[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            rev[e] = u == 3 ? 1.f : rev[e] * ga[u + 1][e];  // 2^(inc - G_t)
+                            const float ks = kval(u, e) * rev[e];
+                            const uint32_t kt = bf_bits(ks * cT[e]);
+                            if (u & 1) ktw[e][u >> 1] = kt << 16;
+                            else ktw[e][u >> 1] |= kt;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) rr[r][e] = static_cast<__bf16>(ks * cR[r][e]);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (r >= blk) *reinterpret_cast<bf16x4*>(Kc + (rr_row0(r) + t) * L::PK + cc) = rr[r];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        *reinterpret_cast<uint2*>(Kt + (cc + e) * L::PT + 4 * tg) = make_uint2(ktw[e][0], ktw[e][1]);
                 }
-                uint32_t ktw[8][2];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int t = 4 * tg + u;
-                    bf16x8 kh, qh, kc;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        run[e] *= valid[u] ? ga[8 * u + e] : 1.f;  // 2^(G_t - R)
-                        const float kv = bf_at(kz[u], e) * nk[u], qv = bf_at(qz[u], e) * nq[u];
-                        const float dn = __builtin_amdgcn_rcpf(run[e]);
-                        kh[e] = static_cast<__bf16>(kv * run[e]);
-                        qh[e] = static_cast<__bf16>(qv * run[e]);
-                        const float kcv = kv * dn;
-                        kc[e] = static_cast<__bf16>(kcv);
-                        const uint32_t kt = bf_bits(kcv * ce[e]);
-                        if (u & 1) ktw[e][u >> 1] |= kt << 16;
-                        else ktw[e][u >> 1] = kt;
-                    }
-                    *reinterpret_cast<bf16x8*>(Kh + t * L::PK + c8) = kh;
-                    *reinterpret_cast<bf16x8*>(Qh + t * L::PK + c8) = qh;
-                    *reinterpret_cast<bf16x8*>(Kc + t * L::PK + c8) = kc;
-                    if constexpr (MODE == kPrep) {
-                        *reinterpret_cast<bf16x8*>(KhI + t * L::PK + c8) = kh;
-                        *reinterpret_cast<bf16x8*>(QhI + t * L::PK + c8) = qh;
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *reinterpret_cast<uint2*>(Kt + (c8 + e) * L::PT + 4 * tg) = make_uint2(ktw[e][0], ktw[e][1]);
             } else {
                 if (wave == kScanWave) {
                     // scalar gates: token t = lane; inclusive scan of log2 alpha
@@ -776,7 +836,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     auto prep_ap = [&](int c) {
         const bf16_t* Kh = prep_lds_b(c, L::oKh, L::pKh);
         const bf16_t* Qh = prep_lds_b(c, L::oQh, L::pQh);
-        const bf16_t* Kr = KDA ? Kc : Kh;  // right factor (j side)
+        // right factor (j side); KDA: the right rows of the row block's set
+        const bf16_t* Kr = Kh;
+        const bf16_t* KrB = Kh;
+        if constexpr (KDA) {
+            Kr = Kc + rr_row0(wave < 2 ? 3 : 2) * L::PK;
+            KrB = Kc + rr_row0(wave < 2 ? 0 : 1) * L::PK;
+        }
         const float* sb = reinterpret_cast<const float*>(prep_lds_b(c, L::oBeta, L::pBeta));
         bf16_t* Pt = prep_out_b(c, L::oP);
         // kPrep keeps -A and D_r^{-1} in LDS: the image gets (I + A)^{-1} instead
@@ -913,10 +979,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         f32x4 accB[2] = {zero4(), zero4()};
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-            bf16x8 kr[4];
+            bf16x8 kr[4], krb[2];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
                 if (ct <= rA) kr[ct] = lds8(Kr + (16 * ct + lr) * L::PK + 32 * s + 8 * lg);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                if (ct <= rB) krb[ct] = KDA ? lds8(KrB + (16 * ct + lr) * L::PK + 32 * s + 8 * lg) : kr[ct];
             const bf16x8 mA = lds8(M + (16 * rA + lr) * L::PK + 32 * s + 8 * lg);
             const bf16x8 mB = lds8(M + (16 * rB + lr) * L::PK + 32 * s + 8 * lg);
 #pragma unroll
@@ -924,7 +993,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 if (ct <= rA) accA[ct] = mfma32(kr[ct], mA, accA[ct]);
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                if (ct <= rB) accB[ct] = mfma32(kr[ct], mB, accB[ct]);
+                if (ct <= rB) accB[ct] = mfma32(krb[ct], mB, accB[ct]);
         }
         auto epilogue = [&](int rt, int ct, const f32x4& acc, float bt, float gt) {
             const int t = 16 * rt + lr;
@@ -1082,7 +1151,6 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     typedef bf16x8 KFrag[4][NKS];
     struct OpsA {
         KFrag kf;                     // Khat rows 16 rt + lr, permuted k
-        float4 sr[KDA ? NRT : 1];     // KDA: 2^R of S rows 16 r + 4 lg + i
         float4 b4[4], e4[4];          // beta_t, GDN 2^G_t, rows t = 16 rt + 4 lg + i
         bf16x4 Df[4], Af[6];          // kFused: D_r^{-1} and -A_rk; kChain: blocks of (I + A)^{-1}
     };
@@ -1125,11 +1193,6 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             for (int s = 0; s < NKS; ++s)
                 A.kf[rt][s] = ONEBAR ? lds8(Kh + (16 * rt + lr) * L::PK + 32 * s + 8 * lg)  // permuted rows
                                      : lds_perm(Kh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
-        if constexpr (KDA) {
-            const float* sr = f32p(c, L::oSref);
-#pragma unroll
-            for (int r = 0; r < NRT; ++r) A.sr[r] = *reinterpret_cast<const float4*>(sr + 16 * r + 4 * lg);
-        }
     };
     auto load_a2 = [&](int c, OpsA& A) {
         const float* sb = f32p(c, L::oBeta);
@@ -1211,20 +1274,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         }
     };
 
-    // phase 1: Khat S (the B operands are S rounded to bf16; KDA: rows scaled by 2^R)
+    // phase 1: Khat S (the B operands are S rounded to bf16)
     auto phase_ks = [&](const OpsA& A, f32x4 (&acc)[4]) {
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-            f32x4 lo = S[2 * s];
-            f32x4 hi = (2 * s + 1 < NRT) ? S[2 * s + 1] : zero4();
-            if constexpr (KDA) {
-                const float4 f0 = A.sr[2 * s];
-                lo[0] *= f0.x; lo[1] *= f0.y; lo[2] *= f0.z; lo[3] *= f0.w;
-                if (2 * s + 1 < NRT) {
-                    const float4 f1 = A.sr[2 * s + 1 < NRT ? 2 * s + 1 : 0];
-                    hi[0] *= f1.x; hi[1] *= f1.y; hi[2] *= f1.z; hi[3] *= f1.w;
-                }
-            }
+            const f32x4 lo = S[2 * s];
+            const f32x4 hi = (2 * s + 1 < NRT) ? S[2 * s + 1] : zero4();
             bS[s] = cat8(cvt4(lo), cvt4(hi));
         }
 #pragma unroll

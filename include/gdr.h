@@ -191,10 +191,12 @@ int gdr_decode_multi_ex(int gate, int dtype, int flags, int B, int T, int H, int
  *
  * T == 0 copies state_in (or zeros) to state_out.  With dtype BF16 the
  * contractions run on bf16 matrix cores with fp32 accumulation and an fp32
- * state; with dtype F32 every operation is fp32.  KDA with bf16 inputs
- * requires the cumulative log-gate inside any chunk to stay above -80 per
- * channel (exp of its half-range must not overflow); GDN and the F32 path
- * have no such limit.  Returns a GDR_* status.
+ * state; with dtype F32 every operation is fp32.  Any gate in [0, 1] is
+ * valid.  Gates near zero are raised to a floor per token (and channel):
+ * KDA with BF16 to 2^-15, which changes a state or output by at most 2^-15
+ * of the state's magnitude, below the bf16 rounding of the operands; GDN
+ * with BF16 to e^-80 and the F32 path to e^-40 (no visible change).
+ * Returns a GDR_* status.
  */
 int gdr_chunk_prefill(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
                       float scale,

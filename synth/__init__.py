@@ -134,13 +134,15 @@ def make_state(rng: np.random.Generator, B: int, H: int, dk: int, dv: int) -> np
 
 def make_inputs(w: Workload, layer: int = 0, *, B: Optional[int] = None,
                 T: Optional[int] = None, H: Optional[int] = None,
-                seed: Optional[int] = None, s0: Optional[str] = None) -> dict:
+                seed: Optional[int] = None, s0: Optional[str] = None,
+                alpha_mean: float = 2.0) -> dict:
     """Draw one layer's inputs for workload ``w``.
 
     Token tensors use the layout [B, T, H, d]; decode workloads (T == 1) use
     the same arrays, which are also valid as [B, H, d].  ``B``, ``T``, ``H``,
     ``seed`` and ``s0`` override the workload's values (used to draw smaller
-    cases with the same distributions).
+    cases with the same distributions); ``alpha_mean`` moves the mean of the
+    gate logits (2.0 for every workload; -2.0 gives fast-forgetting gates).
 
     Returns a dict with float32 arrays ``q, k`` [B,T,H,dk], ``v`` [B,T,H,dv],
     ``alpha`` [B,T,H] (gdn) or [B,T,H,dk] (kda), ``beta`` [B,T,H], and
@@ -160,7 +162,7 @@ def make_inputs(w: Workload, layer: int = 0, *, B: Optional[int] = None,
     if w.dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     ashape = (B, T, H) if w.gate == "gdn" else (B, T, H, dk)
-    alpha = _sigmoid(2.0 + 0.5 * ra.standard_normal(ashape, dtype=np.float32))
+    alpha = _sigmoid(np.float32(alpha_mean) + 0.5 * ra.standard_normal(ashape, dtype=np.float32))
     beta = _sigmoid(rb.standard_normal((B, T, H), dtype=np.float32))
     s0 = make_state(rs, B, H, dk, dv) if s0_kind == "normal" else None
     return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta, "s0": s0}
@@ -169,7 +171,7 @@ def make_inputs(w: Workload, layer: int = 0, *, B: Optional[int] = None,
 def make_raw_inputs(w: Workload, layer: int = 0, *, B: Optional[int] = None,
                     T: Optional[int] = None, H: Optional[int] = None,
                     seed: Optional[int] = None, s0: Optional[str] = None,
-                    round_bf16: bool = True) -> dict:
+                    round_bf16: bool = True, alpha_mean: float = 2.0) -> dict:
     """The same draws as :func:`make_inputs` before its two transforms: q and
     k are the raw normal draws (not normalised) and ``alpha``, ``beta`` are the
     logits (before the sigmoid).  With a bf16 workload and ``round_bf16`` the
@@ -187,7 +189,7 @@ def make_raw_inputs(w: Workload, layer: int = 0, *, B: Optional[int] = None,
     if w.dtype == "bf16" and round_bf16:
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     ashape = (B, T, H) if w.gate == "gdn" else (B, T, H, dk)
-    alpha = (2.0 + 0.5 * ra.standard_normal(ashape, dtype=np.float32)).astype(np.float32)
+    alpha = (np.float32(alpha_mean) + 0.5 * ra.standard_normal(ashape, dtype=np.float32)).astype(np.float32)
     beta = rb.standard_normal((B, T, H), dtype=np.float32)
     s0 = make_state(rs, B, H, dk, dv) if s0_kind == "normal" else None
     return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta, "s0": s0}

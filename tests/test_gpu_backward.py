@@ -24,10 +24,11 @@ def _built():
     ensure_built()
 
 
-def _case(gate, dtype, B, T, H, dk, dv, seed, s0=True, dst=True):
+def _case(gate, dtype, B, T, H, dk, dv, seed, s0=True, dst=True, alpha_mean=2.0):
     base = synth.WORKLOADS["gdn_prefill_b4_t8192_h32_d128" if gate == "gdn" else "kda_prefill_b1_t32768_h32_d128"]
     w = replace(base, dtype=dtype, dk=dk, dv=dv)
-    inp = synth.make_inputs(w, B=B, T=T, H=H, seed=seed, s0="normal" if s0 else "zero")
+    inp = synth.make_inputs(w, B=B, T=T, H=H, seed=seed, s0="normal" if s0 else "zero",
+                            alpha_mean=alpha_mean)
     rng = np.random.default_rng(seed + 100)
     do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
     if dtype == "bf16":
@@ -53,8 +54,8 @@ def _run(gate, dtype, inp, do, dst, scale, want_ds0=True):
     return {key: (None if val is None else to_host64(val)) for key, val in out.items()}
 
 
-def _check(gate, dtype, B, T, H, dk, dv, seed=1, s0=True, dst=True, scale=0.8):
-    inp, do, dst_arr = _case(gate, dtype, B, T, H, dk, dv, seed, s0, dst)
+def _check(gate, dtype, B, T, H, dk, dv, seed=1, s0=True, dst=True, scale=0.8, alpha_mean=2.0):
+    inp, do, dst_arr = _case(gate, dtype, B, T, H, dk, dv, seed, s0, dst, alpha_mean)
     got = _run(gate, dtype, inp, do, dst_arr, scale)
     ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["s0"], do,
                           dst_arr, scale=scale)
@@ -89,6 +90,14 @@ def test_backward_without_states(gate):
 def test_backward_exact_chunks_bf16_d128(gate):
     announce("backward %s bf16 T=256 d=128" % gate)
     _check(gate, "bf16", B=1, T=256, H=2, dk=128, dv=128, seed=8)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_strong_decay(gate, dtype):
+    """Fast-forgetting gates, alpha = sigmoid(N(-2, 0.5)) (per channel for KDA)."""
+    announce("backward %s %s strong decay" % (gate, dtype))
+    _check(gate, dtype, B=1, T=200, H=2, dk=64, dv=64, seed=12, alpha_mean=-2.0)
 
 
 def test_backward_t0_copies_the_state_gradient():

@@ -179,6 +179,32 @@ def test_zero_gate_inside_chunk(gate):
     check(gate, "f32", synth.make_inputs(w32, B=1, T=128, H=2, seed=8) | {"alpha": inp2["alpha"]})
 
 
+@pytest.mark.parametrize("dk,dv,T", [(128, 128, 1000), (64, 32, 333), (32, 64, 200), (16, 128, 130),
+                                     (128, 16, 65)])
+def test_kda_strong_channel_decay(dk, dv, T):
+    """Fast-forgetting channel gates, alpha = sigmoid(N(-2, 0.5)): about -3
+    in log2 per token, about -200 over a chunk, in every channel."""
+    w = replace(synth.WORKLOADS["kda_prefill_b1_t32768_h32_d128"], dk=dk, dv=dv)
+    inp = synth.make_inputs(w, B=2, T=T, H=3, seed=50 + dk, s0="normal", alpha_mean=-2.0)
+    announce("prefill kda strong decay dk=%d dv=%d T=%d" % (dk, dv, T))
+    check("kda", "bf16", inp, scale=0.9)
+
+
+def test_kda_zero_channels():
+    """Whole channels at alpha = 0 for whole chunks and across chunk
+    boundaries, every channel at one token, and tiny nonzero gates."""
+    w = synth.WORKLOADS["kda_prefill_b1_t32768_h32_d128"]
+    inp = synth.make_inputs(w, B=1, T=400, H=5, seed=51, s0="normal")
+    a = inp["alpha"]
+    a[0, 64:128, 0, :32] = 0.0        # 32 channels of head 0 over all of chunk 1
+    a[0, :, 1, 5] = 0.0               # channel 5 of head 1 at every token
+    a[0, 100:300, 2, 64:] = 0.0       # half the channels of head 2 across three chunk boundaries
+    a[0, 150, 3, :] = 0.0             # every channel of head 3 at one token
+    a[0, 200:216, 4, ::2] = 1e-30     # tiny, nonzero
+    announce("prefill kda zero channels")
+    check("kda", "bf16", inp)
+
+
 def test_prefill_deterministic():
     w = synth.WORKLOADS["kda_prefill_b1_t32768_h32_d128"]
     inp = synth.make_inputs(w, B=1, T=256, H=8, seed=12)

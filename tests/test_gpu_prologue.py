@@ -39,8 +39,8 @@ def _reference_inputs(raw, flags):
     return q, k, a, b
 
 
-def _raw(w, flags, B, T, H, seed, zero_rows=False):
-    raw = synth.make_raw_inputs(w, B=B, T=T, H=H, seed=seed, s0="normal")
+def _raw(w, flags, B, T, H, seed, zero_rows=False, alpha_mean=2.0):
+    raw = synth.make_raw_inputs(w, B=B, T=T, H=H, seed=seed, s0="normal", alpha_mean=alpha_mean)
     if not flags & NORM:  # q, k given normalised (raw ones would make the recurrence diverge)
         normed = synth.make_inputs(w, B=B, T=T, H=H, seed=seed, s0="normal")
         raw["q"], raw["k"] = normed["q"], normed["k"]
@@ -118,9 +118,9 @@ def _prefill(gate, dtype, d, flags, B, T, H, dv):
     return to_host64(o), to_host64(s_out)
 
 
-def _check_prefill(gate, dtype, flags, dk, dv, B=2, T=200, H=3, seed=17, zero_rows=True):
+def _check_prefill(gate, dtype, flags, dk, dv, B=2, T=200, H=3, seed=17, zero_rows=True, alpha_mean=2.0):
     w = _workload("prefill", gate, dtype, dk, dv)
-    raw = _raw(w, flags, B=B, T=T, H=H, seed=seed, zero_rows=zero_rows)
+    raw = _raw(w, flags, B=B, T=T, H=H, seed=seed, zero_rows=zero_rows, alpha_mean=alpha_mean)
     o, s = _prefill(gate, dtype, _dev(raw, dtype), flags, B, T, H, dv)
     q, k, a, b = _reference_inputs(raw, flags)
     o_ref, s_ref = oracle.recurrent(q, k, raw["v"], a, b, raw["s0"], scale=0.75)
@@ -167,6 +167,14 @@ def test_prefill_prologue_with_explicit_default_schedule(gate):
     a = _prefill(gate, "bf16", d, NORM | SIG, 2, 150, 3, 64)
     b = _prefill(gate, "bf16", d, NORM | SIG | sched, 2, 150, 3, 64)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_prefill_sigmoid_very_negative_logits(gate):
+    """Gate logits around -6 (some below -8): the chunked paths take
+    log2 sigmoid of the logit directly."""
+    announce("prefill prologue bf16 %s negative logits" % gate)
+    _check_prefill(gate, "bf16", NORM | SIG, 128, 128, T=300, alpha_mean=-6.0)
 
 
 def test_prefill_gdn_long_sequence_prologue():
