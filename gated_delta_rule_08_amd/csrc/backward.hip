@@ -28,8 +28,11 @@
 //   dq = dQ0 e0 + a2,   dk = dK0 e0 + dKt ek + a1 + a3 + a4,
 //   dG = q (dQ0 e0 + a2) + k (dK0 e0 - dKt ek + a1 - a3 - a4),
 //   dG_end = eE sum_j dS_end S + sum_t dKt k ek   (added to the last token),
-// dlog alpha_s = sum_{t >= s} dG_t inside the chunk, dalpha = dlog alpha / alpha
-// (zero where the floor is active).
+// dlog alpha_s = sum_{t >= s} dG_t inside the chunk, dalpha = dlog alpha / alpha.
+// Where the floor is active (alpha ~ 0) dlog alpha_m is ~alpha_m times the
+// true dalpha_m and comes out of a sum whose other terms cancel, so it is not
+// divided there: bwd_floor sums the terms that carry alpha_m directly, with
+// alpha_m taken out of their exponents (see that kernel).
 //
 // Kernels (one head per (b, h); 16-column value slices where the work
 // separates by value column):
@@ -43,6 +46,8 @@
 //                             dV and the Xr.dX part of dbeta
 //   bwd_local  (b, h, chunk)  the contractions over all value columns and
 //                             everything that maps back to q, k, beta, alpha
+//   bwd_floor  (b, h, chunk)  dalpha where the log-gate floor is active (only
+//                             chunks bwd_local flags do any work)
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -123,7 +128,7 @@ __host__ __device__ constexpr size_t img_floats(int dk) { return 3 * kC * kC + 3
 
 // Workspace layout (floats), shared by the host sizing and the kernels.
 struct Ws {
-    size_t img, ck, dck, xr, u, dx, dbp, pd, hq, total;
+    size_t img, ck, dck, xr, u, dx, dbp, pd, hq, fl, total;
     __host__ __device__ Ws(int B, int T, int H, int dk, int dv) {
         const size_t bh = static_cast<size_t>(B) * H;
         const size_t nch = (static_cast<size_t>(T) + kC - 1) / kC;
@@ -137,7 +142,8 @@ struct Ws {
         dbp = dx + tok * dv;                      // [dv/16][B,T,H]
         pd = dbp + tok * (dv / kSl);              // [B,T,H,dv]: scale P^T dO
         hq = pd + tok * dv;                       // [bh][chunk][dk][dv]: scale (q e0)^T dO
-        total = hq + bh * nch * dk * dv;
+        fl = hq + bh * nch * dk * dv;             // [bh][chunk] int: a floored gate in the chunk
+        total = fl + bh * nch;
     }
 };
 
@@ -707,6 +713,11 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     float* eE = dB + kC;               // [DK]
     float* dGe = eE + DK;              // [DK] dG_end
     float* dGt = dGe + DK;             // [64] GDN: dG per token
+    // partial sums, added in a fixed order (the results do not depend on
+    // which wave finishes first)
+    float* dBp = dGt + kC;             // [4][64] dbeta by column group
+    float* dGtp = dBp + 4 * kC;        // [4][64] GDN: dG by column group
+    float* gep = dGtp + 4 * kC;        // [2][16] GDN: dG_end by wave (through eE; through Kt)
 
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
@@ -723,9 +734,12 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         Ks[t * KP + c] = t < n ? ld(k + tok(t) * DK + c) : 0.f;
         Qs[t * KP + c] = t < n ? ld(q + tok(t) * DK + c) : 0.f;
     }
+    int floored = 0;  // a gate of this chunk at the log floor (bwd_floor's flag)
     for (int i = tid; i < kC * GW; i += kNT) {
         const int t = i / GW, c = i - t * GW;
-        Gs[t * GP + c] = t < n ? log_gate(KDA ? a.alpha[tok(t) * DK + c] : a.alpha[tok(t)]) : 0.f;
+        const float lg = t < n ? __logf(KDA ? a.alpha[tok(t) * DK + c] : a.alpha[tok(t)]) : 0.f;
+        floored |= !(lg > kFloor);
+        Gs[t * GP + c] = fmaxf(lg, kFloor);
     }
     if (tid < kC) {
         Bs[tid] = tid < n ? a.beta[tok(tid)] : 0.f;
@@ -735,7 +749,8 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     if (tid < DK) dGe[tid] = 0.f;
     const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
     for (int i = tid; i < kC * kC; i += kNT) Ah[(i >> 6) * kTP + (i & 63)] = im[iA + i];
-    __syncthreads();
+    floored = __syncthreads_or(floored);
+    if (tid == 0) reinterpret_cast<int*>(a.ws + W.fl)[static_cast<size_t>(bh) * a.nch + ch] = floored;
     for (int c = tid >> 6; c < GW; c += kNT / 64) {  // cumulative log-gate in place
         const int t = tid & 63;
         const float g = wave_prefix_sum(Gs[t * GP + c]);
@@ -825,13 +840,13 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         Mm[t * kTP + s2] = Bs[t] * dA;
         Nm[t * kTP + s2] = s2 <= t ? a.scale * aP[r] : 0.f;
         const float db = row16_sum(dA * Ah[t * kTP + s2]);  // over the row's 16 s
-        if (li == 0) atomicAdd(&dB[t], db);
+        if (li == 0) dBp[g * kC + t] = db;
     }
     if constexpr (KDA) {
         if (tid < DK) dGe[tid] = eE[tid] * ge;
     } else if (tid < ((DK + 63) & ~63)) {  // whole waves; ge = 0 beyond DK
         const float sg = wave_sum(ge);
-        if ((tid & 63) == 0) atomicAdd(&dGe[0], eE[0] * sg);
+        if ((tid & 63) == 0) gep[tid >> 6] = sg;
     }
     __syncthreads();
     // The four gate-weighted sums of the lane's outputs:
@@ -985,12 +1000,13 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     }
     // gradients of the lane's outputs
     float dq[NCT][4], dk[NCT][4], dg[NCT][4];
+    float gk[NCT][4];    // KDA: dKt k ek, G_end's gradient through Kt (summed per channel below)
     float ge_all = 0.f;  // GDN: the lane's part of sum_t dKt k ek (a scalar G_end)
 #pragma unroll
     for (int i = 0; i < NCT; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            dq[i][r] = dk[i][r] = dg[i][r] = 0.f;
+            dq[i][r] = dk[i][r] = dg[i][r] = gk[i][r] = 0.f;
             if (!has_ct(i)) continue;
             const int t = T + 4 * l4 + r, c = ct(i) + li;
             const float gt = Gs[t * GP + (KDA ? c : 0)];
@@ -1002,23 +1018,27 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
             dk[i][r] = dK0 * e0 + dKt * ek + a1[i][r] + a3[i][r] + a4[i][r];
             dg[i][r] = qv * (dQ0 * e0 + a2[i][r]) + kv * (dK0 * e0 - dKt * ek + a1[i][r] - a3[i][r] - a4[i][r]);
             // G_end = G_{n-1}: its gradient through Kt (and, above, eE)
-            if constexpr (KDA) atomicAdd(&dGe[c], dKt * kv * ek);
+            if constexpr (KDA) gk[i][r] = dKt * kv * ek;
             else ge_all += dKt * kv * ek;
         }
     }
     if constexpr (!KDA) {
         const float sg = wave_sum(ge_all);
-        if ((tid & 63) == 0) atomicAdd(&dGe[0], sg);
+        if ((tid & 63) == 0) gep[16 + (tid >> 6)] = sg;
     }
-    __syncthreads();  // k, q no longer read: dG goes where k was
+    __syncthreads();  // k, q no longer read: dG goes where k was (KDA: dKt k ek where q was)
     float* dG = Ks;
+    float* gK = Qs;
 #pragma unroll
     for (int i = 0; i < NCT; ++i) {
         if (!has_ct(i)) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = T + 4 * l4 + r;
-            if constexpr (KDA) dG[t * KP + ct(i) + li] = dg[i][r];
+            if constexpr (KDA) {
+                dG[t * KP + ct(i) + li] = dg[i][r];
+                gK[t * KP + ct(i) + li] = gk[i][r];
+            }
         }
     }
     if constexpr (!KDA) {  // dG_t = sum over channels: the lane's tiles, then the row's 16 lanes
@@ -1028,7 +1048,7 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
 #pragma unroll
             for (int i = 0; i < NCT; ++i) sg += dg[i][r];
             sg = row16_sum(sg);
-            if (li == 0) atomicAdd(&dGt[T + 4 * l4 + r], sg);
+            if (li == 0) dGtp[g * kC + T + 4 * l4 + r] = sg;
         }
     }
     InT* dqo = static_cast<InT*>(a.dq);
@@ -1046,14 +1066,26 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         }
     }
     __syncthreads();
+    if constexpr (!KDA) {  // the partial sums, in a fixed order
+        if (tid < kC) dGt[tid] = ((dGtp[tid] + dGtp[kC + tid]) + dGtp[2 * kC + tid]) + dGtp[3 * kC + tid];
+        if (tid == 0) {
+            float a1 = 0.f, a2 = 0.f;
+            for (int w = 0; w < (DK + 63) / 64; ++w) a1 += gep[w];
+            for (int w = 0; w < kNT / 64; ++w) a2 += gep[16 + w];
+            dGe[0] = eE[0] * a1 + a2;
+        }
+        __syncthreads();
+    }
     // dlog alpha_s = sum_{t >= s} dG_t inside the chunk (G_end's gradient on
-    // the last token); dalpha = dlog alpha / alpha unless the floor is active.
+    // the last token); dalpha = dlog alpha / alpha unless the floor is active
+    // (there bwd_floor writes it).
     float* dL = KDA ? dG : dGt;  // dlog alpha, in place
     constexpr int LP = KDA ? KP : 1;
     for (int c = tid >> 6; c < GW; c += kNT / 64) {  // a wave per channel, lane = token
         const int t = tid & 63;
+        const float gke = KDA ? wave_sum(gK[t * KP + c]) : 0.f;  // G_end's gradient through Kt
         const float x = wave_suffix_sum(t < n ? dL[t * LP + c] : 0.f);
-        if (t < n) dL[t * LP + c] = x + dGe[c];
+        if (t < n) dL[t * LP + c] = x + dGe[c] + gke;
     }
     __syncthreads();
     for (int i = tid; i < n * GW; i += kNT) {
@@ -1063,9 +1095,267 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         a.dalpha[r] = __logf(al) > kFloor ? dL[t * LP + c] / al : 0.f;
     }
     if (tid < n) {
-        float db = dB[tid];
+        float db = ((dBp[tid] + dBp[kC + tid]) + dBp[2 * kC + tid]) + dBp[3 * kC + tid];
         for (int sl = 0; sl < a.nsl_chain; ++sl) db += a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok(tid)];
         a.dbeta[tok(tid)] = db;
+    }
+}
+
+// ---------------------------------------------------------------- bwd_floor
+// dalpha where the log floor is active (alpha_m ~ 0).  Every term of
+// dlog alpha_m that depends on alpha_m carries it as a factor: the pairs
+// s < m <= t (through E(t,s,c)), the state terms of the tokens t >= m
+// (through e0) and t < m (through ek), and eE.  bwd_local's per-token sums
+// also hold terms free of alpha_m, which cancel in dlog alpha_m but leave
+// rounding that a division by alpha_m would magnify.  Here the terms that
+// carry alpha_m are summed directly, each with alpha_m taken out of its
+// exponent (every exponent stays <= 0), per channel c (g = floored log-gate):
+//   dalpha_mc = sum_{t>=m} exp(G_tc - G_mc) sum_{s<m} (M_ts k_tc + N_ts q_tc) k_sc exp(G_{m-1},c - G_sc)
+//             + exp(-g_mc) [ sum_{t>=m} (dK0_tc k_tc + dQ0_tc q_tc) e0_tc
+//                            + sum_{t<m} dKt_tc k_tc ek_tc + (sum_j dS_end[c,j] S[c,j]) eE_c ]
+// (GDN sums it over the channels).  The bracket's terms all carry exp(g_mc),
+// so exp(-g_mc) restores them (where e0 or ek underflowed the restored term
+// is below e^-47).  One workgroup per (b, h, chunk); chunks without a floored
+// gate return at once.  All sums run in a fixed order (deterministic).
+constexpr int kFT = 1024;  // threads of bwd_floor (few accumulators per thread)
+constexpr int kJB = 16;   // value columns per staged block
+template <int DK>
+constexpr int floor_cb() { return DK < 64 ? DK : 64; }  // channels per pass
+template <int DK>
+constexpr int floor_stage() {
+    constexpr int SP = kJB + 1, CP = floor_cb<DK>() + 1;
+    return (3 * kC * SP + 2 * floor_cb<DK>() * SP) > kC * CP ? (3 * kC * SP + 2 * floor_cb<DK>() * SP) : kC * CP;
+}
+template <int DK>
+constexpr int floor_lds() {
+    constexpr int CB = floor_cb<DK>(), CP = CB + 1;
+    return 4 * (2 * kC * kTP + floor_stage<DK>() + 5 * kC * CP + 3 * CB + 3 * kC);
+}
+template <int DK, bool KDA, typename InT>
+__global__ __launch_bounds__(kFT) void bwd_floor(Args a) {
+    constexpr int CB = floor_cb<DK>(), CP = CB + 1, SP = kJB + 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
+    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    if (reinterpret_cast<const int*>(a.ws + W.fl)[static_cast<size_t>(bh) * a.nch + ch] == 0) return;
+    extern __shared__ float sm[];
+    float* Mm = sm;                          // [64][kTP] beta dA (s < t)
+    float* Nm = Mm + kC * kTP;               // [64][kTP] dP (s <= t)
+    float* Ust = Nm + kC * kTP;              // staging: U, dX, dO [64][SP]; S, dS_end [CB][SP]
+    float* Xst = Ust + kC * SP;
+    float* Ost = Xst + kC * SP;
+    float* Sst = Ost + kC * SP;
+    float* Dst = Sst + CB * SP;
+    float* F2 = Ust;                         // [64][CP] after the staging: the ek terms, then k exp(...)
+    float* Kb = Ust + floor_stage<DK>();     // [64][CP] k of the pass's channels
+    float* Qb = Kb + kC * CP;                // [64][CP] q
+    float* Gb = Qb + kC * CP;                // [64][CP] cumulative log-gate
+    float* gb = Gb + kC * CP;                // [64][CP] log-gate (floored)
+    float* F1 = gb + kC * CP;                // [64][CP] the e0 terms, then the bracket
+    float* dE = F1 + kC * CP;                // [CB] sum_j dS_end S
+    float* eE = dE + CB;                     // [CB] exp(G_end)
+    float* vv = eE + CB;                     // [CB] GDN: one token's terms per channel
+    float* Bs = vv + CB;                     // [64] beta
+    float* dA = Bs + kC;                     // [64] GDN: dalpha per token
+    int* mrow = reinterpret_cast<int*>(dA + kC);  // [64] a floored gate in row m (this pass)
+
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int t0c = ch * kC, n = min(kC, a.T - t0c);
+    const InT* q = static_cast<const InT*>(a.q);
+    const InT* k = static_cast<const InT*>(a.k);
+    const InT* dO = static_cast<const InT*>(a.dO);
+    auto tok = [&](int t) { return (static_cast<size_t>(b) * a.T + t0c + t) * a.H + h; };
+    const float* Sg = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    const float* Dg = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    if (tid < kC) {
+        Bs[tid] = tid < n ? a.beta[tok(tid)] : 0.f;
+        dA[tid] = 0.f;
+    }
+    auto stage_tok = [&](int jb) {  // U, dX, dO of the chunk's rows, columns jb .. jb + 15
+        for (int i = tid; i < kC * kJB; i += kFT) {
+            const int t = i / kJB, j = i - t * kJB;
+            float u = 0.f, x = 0.f, o = 0.f;
+            if (t < n) {
+                const size_t r = tok(t) * a.DV + jb + j;
+                u = a.ws[W.u + r];
+                x = a.ws[W.dx + r];
+                o = ld(dO + r);
+            }
+            Ust[t * SP + j] = u;
+            Xst[t * SP + j] = x;
+            Ost[t * SP + j] = o;
+        }
+    };
+    // M = beta dA = -beta dX U^T (s < t), N = dP = scale dO U^T (s <= t)
+    constexpr int PPT = kC * kC / kFT;
+    float am[PPT], an[PPT];
+#pragma unroll
+    for (int x = 0; x < PPT; ++x) am[x] = an[x] = 0.f;
+    for (int jb = 0; jb < a.DV; jb += kJB) {
+        __syncthreads();
+        stage_tok(jb);
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < PPT; ++x) {
+            const int p = tid + x * kFT, t = p >> 6, s2 = p & 63;
+#pragma unroll 4
+            for (int j = 0; j < kJB; ++j) {
+                const float us = Ust[s2 * SP + j];
+                am[x] += Xst[t * SP + j] * us;
+                an[x] += Ost[t * SP + j] * us;
+            }
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < PPT; ++x) {
+        const int p = tid + x * kFT, t = p >> 6, s2 = p & 63;
+        Mm[t * kTP + s2] = s2 < t ? -Bs[t] * am[x] : 0.f;
+        Nm[t * kTP + s2] = s2 <= t ? a.scale * an[x] : 0.f;
+    }
+    constexpr int EPT = (kC * CB + kFT - 1) / kFT;
+    for (int cb = 0; cb < DK; cb += CB) {
+        __syncthreads();  // the previous pass is done with every array
+        if (tid < kC) mrow[tid] = 0;
+        for (int i = tid; i < kC * CB; i += kFT) {
+            const int t = i / CB, c = i - t * CB;
+            float kv = 0.f, qv = 0.f, lg = 0.f;
+            if (t < n) {
+                const size_t r = tok(t);
+                kv = ld(k + r * DK + cb + c);
+                qv = ld(q + r * DK + cb + c);
+                lg = fmaxf(__logf(KDA ? a.alpha[r * DK + cb + c] : a.alpha[r]), kFloor);
+            }
+            Kb[t * CP + c] = kv;
+            Qb[t * CP + c] = qv;
+            gb[t * CP + c] = lg;
+        }
+        __syncthreads();
+        for (int i = tid; i < kC * CB; i += kFT) {
+            const int t = i / CB, c = i - t * CB;
+            if (t < n && gb[t * CP + c] == kFloor) mrow[t] = 1;
+        }
+        for (int c = wave; c < CB; c += kFT / 64) {  // cumulative log-gate: a wave per channel, lane = token
+            const float g = wave_prefix_sum(gb[lane * CP + c]);
+            Gb[lane * CP + c] = g;
+            if (lane == kC - 1) eE[c] = __expf(g);
+        }
+        // dQ0 = scale dO S^T, dK0 = -beta dX S^T, dKt = U dS_end^T of the pass's channels
+        float aq[EPT], ak[EPT], at[EPT];
+#pragma unroll
+        for (int x = 0; x < EPT; ++x) aq[x] = ak[x] = at[x] = 0.f;
+        float de = 0.f;
+        for (int jb = 0; jb < a.DV; jb += kJB) {
+            __syncthreads();
+            stage_tok(jb);
+            for (int i = tid; i < CB * kJB; i += kFT) {
+                const int c = i / kJB, j = i - c * kJB;
+                Sst[c * SP + j] = Sg[static_cast<size_t>(cb + c) * a.DV + jb + j];
+                Dst[c * SP + j] = Dg[static_cast<size_t>(cb + c) * a.DV + jb + j];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < EPT; ++x) {
+                const int p = tid + x * kFT;
+                if (p >= kC * CB) break;
+                const int t = p / CB, c = p - t * CB;
+#pragma unroll 4
+                for (int j = 0; j < kJB; ++j) {
+                    const float sv = Sst[c * SP + j], dv = Dst[c * SP + j];
+                    aq[x] += Ost[t * SP + j] * sv;
+                    ak[x] += Xst[t * SP + j] * sv;
+                    at[x] += Ust[t * SP + j] * dv;
+                }
+            }
+            if (tid < CB) {
+#pragma unroll 4
+                for (int j = 0; j < kJB; ++j) de += Dst[tid * SP + j] * Sst[tid * SP + j];
+            }
+        }
+        __syncthreads();  // the staging is consumed: F2 takes its place
+#pragma unroll
+        for (int x = 0; x < EPT; ++x) {
+            const int p = tid + x * kFT;
+            if (p >= kC * CB) break;
+            const int t = p / CB, c = p - t * CB;
+            const float kv = Kb[t * CP + c], qv = Qb[t * CP + c], G = Gb[t * CP + c];
+            const float dQ0 = a.scale * aq[x], dK0 = -Bs[t] * ak[x], dKt = at[x];
+            F1[t * CP + c] = (dK0 * kv + dQ0 * qv) * __expf(G);
+            F2[t * CP + c] = dKt * kv * __expf(Gb[(kC - 1) * CP + c] - G);
+        }
+        if (tid < CB) dE[tid] = de;
+        __syncthreads();
+        // bracket[m] = sum_{t >= m} F1 + sum_{t < m} F2 + dE eE (the ek sum
+        // runs over the lanes before m only: no term of row m enters it)
+        for (int c = wave; c < CB; c += kFT / 64) {
+            const float f1 = F1[lane * CP + c];
+            const float f2 = __shfl_up(F2[lane * CP + c], 1);
+            const float v = wave_suffix_sum(f1) + wave_prefix_sum(lane > 0 ? f2 : 0.f) + dE[c] * eE[c];
+            F1[lane * CP + c] = v;
+        }
+        __syncthreads();
+        for (int m = 0; m < n; ++m) {
+            if (!mrow[m]) continue;  // uniform: LDS value, read after a barrier
+            // F2 <- k_sc exp(G_{m-1},c - G_sc) for s < m (each factor <= 1)
+            for (int i = tid; i < kC * CB; i += kFT) {
+                const int s2 = i / CB, c = i - s2 * CB;
+                const float gm1 = m > 0 ? Gb[(m - 1) * CP + c] : 0.f;
+                F2[s2 * CP + c] = s2 < m ? Kb[s2 * CP + c] * __expf(gm1 - Gb[s2 * CP + c]) : 0.f;
+            }
+            __syncthreads();
+            // channels c = wave + NW x per wave, lane = t >= m
+            constexpr int NW = kFT / 64;
+            constexpr int CPW = (CB + NW - 1) / NW;
+            float accm[CPW], accn[CPW];
+#pragma unroll
+            for (int x = 0; x < CPW; ++x) accm[x] = accn[x] = 0.f;
+            const int t = lane;
+            if (t >= m && t < n) {
+#pragma unroll 2
+                for (int s2 = 0; s2 < m; ++s2) {
+                    const float mts = Mm[t * kTP + s2], nts = Nm[t * kTP + s2];
+#pragma unroll
+                    for (int x = 0; x < CPW; ++x) {
+                        const int c = wave + NW * x;
+                        if (c < CB) {
+                            const float as = F2[s2 * CP + c];
+                            accm[x] += mts * as;
+                            accn[x] += nts * as;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < CPW; ++x) {
+                const int c = wave + NW * x;
+                if (c >= CB) continue;
+                float y = 0.f;
+                if (t >= m && t < n)
+                    y = __expf(Gb[t * CP + c] - Gb[m * CP + c]) * (Kb[t * CP + c] * accm[x] + Qb[t * CP + c] * accn[x]);
+                y = wave_sum(y);
+                if (lane == 0) {
+                    const float gm = gb[m * CP + c];
+                    const float v = y + __expf(-gm) * F1[m * CP + c];
+                    if constexpr (KDA) {
+                        if (gm == kFloor) a.dalpha[tok(m) * DK + cb + c] = v;
+                    } else {
+                        vv[c] = v;
+                    }
+                }
+            }
+            __syncthreads();
+            if constexpr (!KDA) {
+                if (tid == 0) {
+                    float sum = dA[m];
+                    for (int c = 0; c < CB; ++c) sum += vv[c];
+                    dA[m] = sum;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if constexpr (!KDA) {
+        __syncthreads();
+        if (tid < n && mrow[tid]) a.dalpha[tok(tid)] = dA[tid];
     }
 }
 
@@ -1081,14 +1371,14 @@ template <int DK, bool KDA>
 constexpr int local_lds() {
     constexpr int SP = 17;
     constexpr int un = (2 * DK * SP + 3 * kC * SP) > 2 * kC * kTP ? (2 * DK * SP + 3 * kC * SP) : 2 * kC * kTP;
-    return 4 * (2 * kC * (DK + 1) + kC * ((KDA ? DK : 1) + 1) + kC * kTP + un + 3 * kC + 2 * DK);
+    return 4 * (2 * kC * (DK + 1) + kC * ((KDA ? DK : 1) + 1) + kC * kTP + un + 3 * kC + 2 * DK + 8 * kC + 32);
 }
 
 template <int DK, bool KDA, typename InT>
 hipError_t run(Args a, hipStream_t s) {
     static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK, kSl>() <= 160 * 1024 &&
                   prep_lds<DK, KDA>() <= 160 * 1024 && fwd_lds<DK, 64>() <= 160 * 1024 &&
-                  dout_lds<DK>() <= 160 * 1024, "LDS budget");
+                  dout_lds<DK>() <= 160 * 1024 && floor_lds<DK>() <= 160 * 1024, "LDS budget");
     auto set = [](const void* f, int bytes) {
         return bytes > 64 * 1024 ? hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
                                  : hipSuccess;
@@ -1117,6 +1407,7 @@ hipError_t run(Args a, hipStream_t s) {
         return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT, kSl>), chain_lds<DK, kSl>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_local<DK, KDA, InT>), local_lds<DK, KDA>())) != hipSuccess) return e;
+    if ((e = set(reinterpret_cast<const void*>(bwd_floor<DK, KDA, InT>), floor_lds<DK>())) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (prep_lds<DK, KDA>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dout<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (dout_lds<DK>()), s, a);
@@ -1131,6 +1422,8 @@ hipError_t run(Args a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_chain<DK, KDA, InT, kSl>), dim3(chain_slices), dim3(kNT), (chain_lds<DK, kSl>()), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_local<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (local_lds<DK, KDA>()), s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_floor<DK, KDA, InT>), dim3(per_chunk), dim3(kFT), (floor_lds<DK>()), s, a);
     return hipGetLastError();
 }
 

@@ -306,7 +306,10 @@ size_t gdr_chunk_prefill_varlen_workspace_bytes_ex(int gate, int dtype, int flag
  *
  * Every product runs in fp32 (bf16 inputs are widened, bf16 gradients rounded
  * to nearest even).  The gate enters through log(alpha), floored at -40 per
- * token as in the fp32 forward: where the floor is active, grad_alpha is 0.
+ * token as in the fp32 forward; where the floor is active (alpha <= e^-40,
+ * alpha = 0 included) grad_alpha is formed from the terms that carry alpha
+ * as a factor, i.e. its value at alpha = 0 up to terms of order e^-40.
+ * Every sum runs in a fixed order: repeated calls give identical gradients.
  * T == 0 copies grad_state_out (or zeros) to grad_state_in.  Outputs may not
  * overlap inputs.  B * H * ceil(T / 64) and ceil(B * H / 8) * 8 * dv / 16
  * must stay below 2^22 (1024-thread workgroups per chunk and head, and per 16
