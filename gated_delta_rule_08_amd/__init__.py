@@ -22,6 +22,7 @@ __all__ = [
     "gdr_abi_version", "EXPORTED_SYMBOLS", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
     "PRO_L2NORM_QK", "PRO_SIGMOID", "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
     "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex", "SCHED_FUSED", "SCHED_SPLIT",
+    "gdr_chunk_prefill_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +36,7 @@ PRO_SIGMOID = 2
 SCHED_FUSED = 4
 SCHED_SPLIT = 8
 EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
+                    "gdr_chunk_prefill_noalloc",
                     "gdr_chunk_prefill_workspace_bytes_ex",
                     "gdr_chunk_prefill_varlen_workspace_bytes_ex",
                     "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex",
@@ -74,6 +76,8 @@ def load_library():
     lib.gdr_decode_step_ex.restype = i
     lib.gdr_chunk_prefill_ex.argtypes = [i] * 9 + [f] + [vp] * 9 + [ctypes.c_size_t, vp]
     lib.gdr_chunk_prefill_ex.restype = i
+    lib.gdr_chunk_prefill_noalloc.argtypes = [i] * 9 + [f] + [vp] * 9
+    lib.gdr_chunk_prefill_noalloc.restype = i
     lib.gdr_chunk_backward.argtypes = [i] * 8 + [f] + [vp] * 15 + [ctypes.c_size_t, vp]
     lib.gdr_chunk_backward.restype = i
     lib.gdr_chunk_backward_workspace_bytes.argtypes = [i] * 8
@@ -279,8 +283,17 @@ def gdr_chunk_prefill_ex(gate: str, q, k, v, alpha, beta, state_in, state_out, o
                    workspace, chunk, stream)
 
 
+def gdr_chunk_prefill_noalloc(gate: str, q, k, v, alpha, beta, state_in, state_out, o, flags: int = 0,
+                              scale: float = 1.0, chunk: int = CHUNK, stream=None) -> None:
+    """:func:`gdr_chunk_prefill_ex` without a workspace: the split schedule
+    uses the library's fixed 96 MiB device scratch (one per GPU), so the call
+    allocates nothing.  Calls overlapping in time on one GPU race on it."""
+    _chunk_prefill(int(flags), gate, q, k, v, alpha, beta, state_in, state_out, o, scale, None,
+                   chunk, stream, noalloc=True)
+
+
 def _chunk_prefill(flags, gate, q, k, v, alpha, beta, state_in, state_out, o, scale, workspace,
-                   chunk, stream):
+                   chunk, stream, noalloc=False):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape != (B, T, H, dv) or o.shape != (B, T, H, dv):
@@ -295,6 +308,11 @@ def _chunk_prefill(flags, gate, q, k, v, alpha, beta, state_in, state_out, o, sc
     if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
         raise ValueError("alpha and beta must be fp32")
     _same_device(q, k, v, alpha, beta, state_in, state_out, o, workspace)
+    if noalloc:
+        _check(load_library().gdr_chunk_prefill_noalloc(
+            GATES[gate], _DTYPES[q.dtype], flags, B, T, H, dk, dv, chunk, float(scale), _ptr(q), _ptr(k),
+            _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream)))
+        return
     if workspace is None:  # allocate what this call needs (callers that time or capture pass their own)
         workspace = _workspace(gdr_chunk_prefill_workspace_bytes(gate, q.dtype, B, T, H, dk, dv, chunk,
                                                                  flags or 0), q.device, stream)

@@ -87,6 +87,66 @@ int check_enums(int gate, int dtype) {
     return GDR_OK;
 }
 
+// Everything gdr_chunk_prefill_ex checks apart from the workspace, in order,
+// after the enums, flags and sizes (done by the caller).
+int prefill_pointer_checks(int gate, int B, int T, int H, int dk, int dv, const void* q,
+                           const void* k, const void* v, const float* alpha, const float* beta,
+                           const float* state_in, const float* state_out, const void* o) {
+    if (!state_out) return GDR_ERR_NULL_PTR;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !o)) return GDR_ERR_NULL_PTR;
+    const int kda = gate == GDR_GATE_KDA;
+    if (!aligned(state_out, 16) || (state_in && !aligned(state_in, 16))) return GDR_ERR_MISALIGNED;
+    if (T > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+                  !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4)))
+        return GDR_ERR_MISALIGNED;
+    if (state_in && state_in != state_out) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(state_in);
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(state_out);
+        const uintptr_t len = static_cast<size_t>(B) * H * dk * dv * sizeof(float);
+        if (a0 < b0 + len && b0 < a0 + len) return GDR_ERR_ALIAS;
+    }
+    return GDR_OK;
+}
+
+// Enums, flags, shapes and schedule of a chunked prefill call.
+int prefill_arg_checks(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
+                       int chunk) {
+    int st = check_enums(gate, dtype);
+    if (st != GDR_OK) return st;
+    if (!prefill_flags_ok(flags)) return GDR_ERR_BAD_ENUM;
+    if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
+    if ((st = schedule_status(flags, gate, dtype)) != GDR_OK) return st;
+    if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
+    return GDR_OK;
+}
+
+// The launch of a validated prefill call (T == 0: the state copy).
+int prefill_launch(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
+                   float scale, const void* q, const void* k, const void* v, const float* alpha,
+                   const float* beta, const float* state_in, float* state_out, void* o,
+                   void* workspace, size_t workspace_bytes, hipStream_t s) {
+    const int kda = gate == GDR_GATE_KDA;
+    gdr::Opts opt;
+    opt.pro = flags & kProFlags;
+    hipError_t e;
+    if (T == 0) {
+        e = gdr::launch_state_copy(state_in, state_out, static_cast<size_t>(B) * H * dk * dv, s);
+    } else if (dtype == GDR_DTYPE_F32) {
+        e = gdr::launch_prefill_f32(kda, B, T, H, dk, dv, scale, static_cast<const float*>(q),
+                                    static_cast<const float*>(k), static_cast<const float*>(v),
+                                    alpha, beta, state_in, state_out, static_cast<float*>(o), s, opt);
+    } else {
+        e = gdr::launch_prefill_bf16(kda, B, T, H, dk, dv, scale,
+                                     static_cast<const gdr::bf16_t*>(q),
+                                     static_cast<const gdr::bf16_t*>(k),
+                                     static_cast<const gdr::bf16_t*>(v), alpha, beta, state_in,
+                                     state_out, static_cast<gdr::bf16_t*>(o), workspace,
+                                     workspace_bytes, s, flags, opt);
+    }
+    return status_of(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +166,9 @@ const char* gdr_status_string(int status) {
         case GDR_ERR_BAD_ENUM: return "GDR_ERR_BAD_ENUM: unknown gate mode, dtype or flag";
         case GDR_ERR_HIP: return "GDR_ERR_HIP: the HIP runtime rejected a launch";
         case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: two state buffers (partially) overlap";
+        case GDR_ERR_SCRATCH:
+            return "GDR_ERR_SCRATCH: one chunk of every head needs more than the 96 MiB fixed scratch of "
+                   "gdr_chunk_prefill_noalloc";
         default: return "unknown gdr status";
     }
 }
@@ -206,49 +269,38 @@ int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, in
                          const float* alpha, const float* beta, const float* state_in,
                          float* state_out, void* o, void* workspace, size_t workspace_bytes,
                          void* stream) {
-    int st = check_enums(gate, dtype);
+    int st = prefill_arg_checks(gate, dtype, flags, B, T, H, dk, dv, chunk);
     if (st != GDR_OK) return st;
-    if (!prefill_flags_ok(flags)) return GDR_ERR_BAD_ENUM;
-    if (B < 0 || H < 0 || T < 0) return GDR_ERR_BAD_SHAPE;
-    if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
-    if ((st = schedule_status(flags, gate, dtype)) != GDR_OK) return st;
-    if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
     const size_t need = gdr_chunk_prefill_workspace_bytes_ex(gate, dtype, flags, B, T, H, dk, dv, chunk);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
     if (B == 0 || H == 0) return GDR_OK;
-    if (!state_out) return GDR_ERR_NULL_PTR;
-    if (T > 0 && (!q || !k || !v || !alpha || !beta || !o)) return GDR_ERR_NULL_PTR;
-    const int kda = gate == GDR_GATE_KDA;
-    if (!aligned(state_out, 16) || (state_in && !aligned(state_in, 16))) return GDR_ERR_MISALIGNED;
-    if (T > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-                  !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4)))
-        return GDR_ERR_MISALIGNED;
-    const size_t n_state = static_cast<size_t>(B) * H * dk * dv;
-    if (state_in && state_in != state_out) {
-        const uintptr_t a0 = reinterpret_cast<uintptr_t>(state_in);
-        const uintptr_t b0 = reinterpret_cast<uintptr_t>(state_out);
-        const uintptr_t len = n_state * sizeof(float);
-        if (a0 < b0 + len && b0 < a0 + len) return GDR_ERR_ALIAS;
-    }
+    if ((st = prefill_pointer_checks(gate, B, T, H, dk, dv, q, k, v, alpha, beta, state_in, state_out,
+                                     o)) != GDR_OK)
+        return st;
+    return prefill_launch(gate, dtype, flags, B, T, H, dk, dv, scale, q, k, v, alpha, beta, state_in,
+                          state_out, o, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int gdr_chunk_prefill_noalloc(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
+                              int chunk, float scale, const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta, const float* state_in,
+                              float* state_out, void* o, void* stream) {
+    int st = prefill_arg_checks(gate, dtype, flags, B, T, H, dk, dv, chunk);
+    if (st != GDR_OK) return st;
+    if (B == 0 || H == 0) return GDR_OK;
+    const bool split = dtype == GDR_DTYPE_BF16 && T > 0 && gdr::prefill_bf16_split(gate == GDR_GATE_KDA, flags);
+    // the images of one chunk of every head have to fit the fixed scratch
+    if (split && static_cast<size_t>(B) * H * gdr::prefill_bf16_image_bytes(gate == GDR_GATE_KDA, dk) >
+                     gdr::kNoallocScratchBytes)
+        return GDR_ERR_SCRATCH;
+    if ((st = prefill_pointer_checks(gate, B, T, H, dk, dv, q, k, v, alpha, beta, state_in, state_out,
+                                     o)) != GDR_OK)
+        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    gdr::Opts opt;
-    opt.pro = flags & kProFlags;
-    hipError_t e;
-    if (T == 0) {
-        e = gdr::launch_state_copy(state_in, state_out, n_state, s);
-    } else if (dtype == GDR_DTYPE_F32) {
-        e = gdr::launch_prefill_f32(kda, B, T, H, dk, dv, scale, static_cast<const float*>(q),
-                                    static_cast<const float*>(k), static_cast<const float*>(v),
-                                    alpha, beta, state_in, state_out, static_cast<float*>(o), s, opt);
-    } else {
-        e = gdr::launch_prefill_bf16(kda, B, T, H, dk, dv, scale,
-                                     static_cast<const gdr::bf16_t*>(q),
-                                     static_cast<const gdr::bf16_t*>(k),
-                                     static_cast<const gdr::bf16_t*>(v), alpha, beta, state_in,
-                                     state_out, static_cast<gdr::bf16_t*>(o), workspace, s, flags,
-                                     opt);
-    }
-    return status_of(e);
+    void* scratch = nullptr;
+    if (split && gdr::noalloc_scratch(s, &scratch) != hipSuccess) return GDR_ERR_HIP;
+    return prefill_launch(gate, dtype, flags, B, T, H, dk, dv, scale, q, k, v, alpha, beta, state_in,
+                          state_out, o, scratch, split ? gdr::kNoallocScratchBytes : 0, s);
 }
 
 size_t gdr_chunk_prefill_varlen_workspace_bytes(int gate, int dtype, int N, int max_T, int H,
@@ -318,7 +370,8 @@ int gdr_chunk_prefill_varlen_ex(int gate, int dtype, int flags, int N, int total
                                      static_cast<const gdr::bf16_t*>(q),
                                      static_cast<const gdr::bf16_t*>(k),
                                      static_cast<const gdr::bf16_t*>(v), alpha, beta, states,
-                                     states, static_cast<gdr::bf16_t*>(o), workspace, s, flags, vl);
+                                     states, static_cast<gdr::bf16_t*>(o), workspace, workspace_bytes,
+                                     s, flags, vl);
     }
     return status_of(e);
 }

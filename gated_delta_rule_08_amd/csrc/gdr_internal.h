@@ -91,13 +91,23 @@ hipError_t launch_prefill_f32(int kda, int B, int T, int H, int dk, int dv, floa
 // kernel, `workspace` of at least prefill_bf16_workspace(...) bytes) when
 // prefill_bf16_split(kda, flags) holds, else the fused kernel (no
 // workspace).  flags: the GDR_SCHED_* bits of the call (validated).
+// workspace_bytes caps the split schedule's ranges of chunks (each range's
+// images must fit); at least prefill_bf16_workspace(...) or B*H image bytes.
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, bf16_t* o, void* workspace, hipStream_t s,
-                               int flags, const Opts& vl = Opts());
+                               float* state_out, bf16_t* o, void* workspace, size_t workspace_bytes,
+                               hipStream_t s, int flags, const Opts& vl = Opts());
 bool prefill_bf16_split(int kda, int flags);
 size_t prefill_bf16_workspace(int kda, int flags, int B, int T, int H, int dk);
+// Bytes of one (head, chunk) image of the split schedule.
+size_t prefill_bf16_image_bytes(int kda, int dk);
+
+// Fixed scratch of gdr_chunk_prefill_noalloc: a file-scope device array per
+// GPU (noalloc.hip).  noalloc_scratch returns its address on the device of
+// `stream` (the current device for the null stream), looked up on first use.
+constexpr size_t kNoallocScratchBytes = size_t(96) << 20;
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 
 // Backward of the chunked recurrence (fp32 arithmetic; q, k, v, d_o, dq, dk,
 // dv in the element type `dtype`).  ws: backward_workspace_floats(...) floats.

@@ -1699,7 +1699,8 @@ inline int split_range_chunks(int BH, int nch, size_t img_bytes) {
 template <int DK, int NSW, bool KDA>
 hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, const bf16_t* k,
                   const bf16_t* v, const float* alpha, const float* beta, const float* s_in,
-                  float* s_out, bf16_t* o, unsigned char* img, hipStream_t s, const Opts& vl) {
+                  float* s_out, bf16_t* o, unsigned char* img, size_t img_cap, hipStream_t s,
+                  const Opts& vl) {
     using L = Layout<DK, NSW, KDA>;
     const int NS = DV / (16 * NSW);
     const int groups = (B * H + 7) / 8;
@@ -1733,7 +1734,9 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     if ((e = set_lds(reinterpret_cast<const void*>(prep), LP::pBytes)) != hipSuccess) return e;
     if ((e = set_lds(reinterpret_cast<const void*>(chain), chain_lds)) != hipSuccess) return e;
     const int nch = (T + kC - 1) / kC;
-    const int rc = split_range_chunks(B * H, nch, KDA ? L::IMG : L::TIMG);
+    const size_t head_chunk = static_cast<size_t>(B) * H * (KDA ? L::IMG : L::TIMG);  // one chunk, all heads
+    const int rc = std::max(1, std::min(split_range_chunks(B * H, nch, KDA ? L::IMG : L::TIMG),
+                                        static_cast<int>(std::min<size_t>(nch, img_cap / head_chunk))));
     for (int c0 = 0; c0 < nch; c0 += rc) {
         const int c1 = std::min(nch, c0 + rc);
         // chunks per chunk-local workgroup: about two workgroups per CU
@@ -1756,12 +1759,12 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
 template <int DK, bool KDA>
 hipError_t dispatch_dvs(int dvs, int B, int T, int H, int DV, float scale, const bf16_t* q,
                         const bf16_t* k, const bf16_t* v, const float* alpha, const float* beta,
-                        const float* s_in, float* s_out, bf16_t* o, unsigned char* img,
+                        const float* s_in, float* s_out, bf16_t* o, unsigned char* img, size_t cap,
                         hipStream_t s, const Opts& vl) {
     switch (dvs) {
-        case 16: return launch<DK, 1, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
-        case 32: return launch<DK, 2, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
-        default: return launch<DK, 4, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
+        case 16: return launch<DK, 1, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, cap, s, vl);
+        case 32: return launch<DK, 2, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, cap, s, vl);
+        default: return launch<DK, 4, KDA>(B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, cap, s, vl);
     }
 }
 
@@ -1769,9 +1772,9 @@ template <int DK>
 hipError_t dispatch_gate(int kda, int dvs, int B, int T, int H, int DV, float scale,
                          const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* alpha,
                          const float* beta, const float* s_in, float* s_out, bf16_t* o,
-                         unsigned char* img, hipStream_t s, const Opts& vl) {
-    return kda ? dispatch_dvs<DK, true>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl)
-               : dispatch_dvs<DK, false>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, s, vl);
+                         unsigned char* img, size_t cap, hipStream_t s, const Opts& vl) {
+    return kda ? dispatch_dvs<DK, true>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, cap, s, vl)
+               : dispatch_dvs<DK, false>(dvs, B, T, H, DV, scale, q, k, v, alpha, beta, s_in, s_out, o, img, cap, s, vl);
 }
 
 template <int DK>
@@ -1798,15 +1801,18 @@ bool prefill_bf16_split(int kda, int flags) {
     return kda != 0 || (flags & GDR_SCHED_SPLIT) != 0;
 }
 
+size_t prefill_bf16_image_bytes(int kda, int dk) {
+    switch (dk) {
+        case 16: return image_bytes<16>(kda);
+        case 32: return image_bytes<32>(kda);
+        case 64: return image_bytes<64>(kda);
+        default: return image_bytes<128>(kda);
+    }
+}
+
 size_t prefill_bf16_workspace(int kda, int flags, int B, int T, int H, int dk) {
     if (!prefill_bf16_split(kda, flags) || T <= 0 || B <= 0 || H <= 0) return 0;
-    size_t img;
-    switch (dk) {
-        case 16: img = image_bytes<16>(kda); break;
-        case 32: img = image_bytes<32>(kda); break;
-        case 64: img = image_bytes<64>(kda); break;
-        default: img = image_bytes<128>(kda); break;
-    }
+    const size_t img = prefill_bf16_image_bytes(kda, dk);
     const int nch = (T + kC - 1) / kC;
     return static_cast<size_t>(B) * H * split_range_chunks(B * H, nch, img) * img;
 }
@@ -1814,15 +1820,16 @@ size_t prefill_bf16_workspace(int kda, int flags, int B, int T, int H, int dk) {
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
                                const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, bf16_t* o, void* workspace, hipStream_t s,
-                               int flags, const Opts& vl) {
+                               float* state_out, bf16_t* o, void* workspace, size_t workspace_bytes,
+                               hipStream_t s, int flags, const Opts& vl) {
     const int dvs = prefill_bf16_slice_width(B, H, dv);
     unsigned char* img = prefill_bf16_split(kda, flags) ? static_cast<unsigned char*>(workspace) : nullptr;
+    const size_t cap = workspace_bytes;
     switch (dk) {
-        case 16: return dispatch_gate<16>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
-        case 32: return dispatch_gate<32>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
-        case 64: return dispatch_gate<64>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
-        default: return dispatch_gate<128>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, s, vl);
+        case 16: return dispatch_gate<16>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, cap, s, vl);
+        case 32: return dispatch_gate<32>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, cap, s, vl);
+        case 64: return dispatch_gate<64>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, cap, s, vl);
+        default: return dispatch_gate<128>(kda, dvs, B, T, H, dv, scale, q, k, v, alpha, beta, state_in, state_out, o, img, cap, s, vl);
     }
 }
 

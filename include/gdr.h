@@ -23,8 +23,9 @@
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer to a dense, row-major buffer
  *    owned by the caller.  The library allocates and frees nothing and keeps
- *    no mutable global state; concurrent calls on different streams are safe
- *    as long as their output buffers do not overlap.
+ *    no mutable global state (apart from gdr_chunk_prefill_noalloc's fixed
+ *    scratch, see there); concurrent calls on different streams are safe as
+ *    long as their output buffers do not overlap.
  *  - q, k, v, o share one element type, selected by `dtype`: GDR_DTYPE_F32
  *    (IEEE fp32) or GDR_DTYPE_BF16 (bfloat16, outputs rounded to nearest
  *    even).  alpha, beta and the state are always fp32.
@@ -70,7 +71,9 @@ enum {
     GDR_ERR_WORKSPACE = -5,   /* workspace missing or too small             */
     GDR_ERR_BAD_ENUM = -6,    /* gate, dtype or flags not known             */
     GDR_ERR_HIP = -7,         /* the HIP runtime rejected a launch          */
-    GDR_ERR_ALIAS = -8        /* two state buffers (partially) overlap      */
+    GDR_ERR_ALIAS = -8,       /* two state buffers (partially) overlap      */
+    GDR_ERR_SCRATCH = -9      /* gdr_chunk_prefill_noalloc: the problem
+                                 needs more than its fixed scratch          */
 };
 
 /*
@@ -228,6 +231,30 @@ int gdr_chunk_prefill_ex(int gate, int dtype, int flags, int B, int T, int H, in
                          const float* alpha, const float* beta,
                          const float* state_in, float* state_out, void* o,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdr_chunk_prefill_ex without a workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, flags, support and results as
+ * gdr_chunk_prefill_ex (bitwise: the same kernels and arithmetic).  The split
+ * schedule's chunk images go to a fixed scratch buffer of 96 MiB that the
+ * library holds as a device array, one per GPU: it is set up on the first
+ * call on a device (the address lookup loads it there) and kept until the
+ * process ends; the call itself allocates and frees nothing.  Ranges of
+ * chunks are sized so one range's images fit the buffer; a problem whose
+ * single chunk of all B * H heads does not fit (B * H * 68 KiB > 96 MiB for
+ * KDA at dk = 128, i.e. more than 1445 heads) returns GDR_ERR_SCRATCH before
+ * any device work.  Every call on a GPU shares that GPU's buffer, so calls
+ * that overlap in time on one GPU (on different streams, or from different
+ * host threads) race; calls ordered on one stream do not.  Nothing in the
+ * buffer needs to start at zero (each range writes its images before reading
+ * them).  The stream's device (the current device for the null stream) must
+ * be one of the first 64.  Returns a GDR_* status.
+ */
+int gdr_chunk_prefill_noalloc(int gate, int dtype, int flags, int B, int T, int H, int dk, int dv,
+                              int chunk, float scale, const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta, const float* state_in,
+                              float* state_out, void* o, void* stream);
 
 /*
  * Chunked prefill of N packed variable-length sequences whose states live in

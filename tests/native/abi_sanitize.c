@@ -132,6 +132,13 @@ int main(void) {
     }
     EXPECT(gdr_chunk_prefill(0, 1, 2, 0, 3, 128, 128, 64, 1.f, 0, 0, 0, 0, 0, 0, p[7], 0, 0, 0, 0),
            GDR_ERR_HIP); /* T == 0: the state copy kernel */
+    /* the call without a workspace: its scratch lookup fails without a GPU */
+    EXPECT(gdr_chunk_prefill_noalloc(1, 1, 0, 2, 70, 3, 128, 128, 64, 1.f, p[0], p[1], p[2], fa, fb,
+                                     0, p[7], p[8], 0),
+           GDR_ERR_HIP);
+    EXPECT(gdr_chunk_prefill_noalloc(1, 1, 0, 1, 70, 1446, 128, 128, 64, 1.f, p[0], p[1], p[2], fa,
+                                     fb, 0, p[7], p[8], 0),
+           GDR_ERR_SCRATCH);
     {
         const size_t need = gdr_chunk_backward_workspace_bytes(1, 0, 1, 130, 2, 64, 64, 64);
         EXPECT(gdr_chunk_backward(1, 0, 1, 130, 2, 64, 64, 64, 1.f, p[0], p[1], p[2], fa, fb, 0,

@@ -15,7 +15,7 @@ import gated_delta_rule_08_amd as gdr
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr.h")
 
-OK, NULL, SHAPE, UNSUP, MISAL, WS, ENUM, HIP, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, UNSUP, MISAL, WS, ENUM, HIP, ALIAS, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 @pytest.fixture(scope="module")
@@ -54,7 +54,7 @@ def test_abi_version(lib):
 def test_status_strings(lib):
     for code, tag in [(OK, "GDR_OK"), (NULL, "NULL_PTR"), (SHAPE, "BAD_SHAPE"),
                       (UNSUP, "UNSUPPORTED"), (MISAL, "MISALIGNED"), (WS, "WORKSPACE"),
-                      (ENUM, "BAD_ENUM"), (HIP, "GDR_ERR_HIP"), (ALIAS, "ALIAS")]:
+                      (ENUM, "BAD_ENUM"), (HIP, "GDR_ERR_HIP"), (ALIAS, "ALIAS"), (SCRATCH, "SCRATCH")]:
         assert tag in gdr.gdr_status_string(code)
     assert gdr.gdr_status_string(12345) == "unknown gdr status"
 
@@ -356,3 +356,35 @@ def test_prologue_ex_variants_validation(lib):
     assert vl(1 | gdr.SCHED_SPLIT) == UNSUP            # GDN normalises only in the fused kernel
     assert vl(1 | gdr.SCHED_FUSED, gate=1) == UNSUP    # KDA has no fused schedule
     assert vl(3) == NULL and vl(3, dtype=0) == NULL
+
+
+def test_noalloc_validation(lib):
+    """gdr_chunk_prefill_noalloc: the checks of gdr_chunk_prefill_ex, no
+    workspace, and a clear error where one chunk of every head would not fit
+    its fixed 96 MiB scratch -- all before any device call."""
+    def na(gate=1, dtype=1, flags=0, B=2, T=70, H=3, dk=128, dv=128, chunk=64, ptrs=None):
+        p = list(P[:8]) if ptrs is None else ptrs
+        return lib.gdr_chunk_prefill_noalloc(gate, dtype, flags, B, T, H, dk, dv, chunk, 1.0, *p, None)
+
+    assert na(gate=2) == ENUM
+    assert na(flags=gdr.SCHED_FUSED | gdr.SCHED_SPLIT) == ENUM
+    assert na(flags=gdr.SCHED_FUSED) == UNSUP                 # KDA: split only
+    assert na(chunk=32) == UNSUP
+    assert na(B=-1) == SHAPE
+    assert na(B=0, ptrs=[None] * 8) == OK
+    ptrs = list(P[:8])
+    ptrs[0] = None
+    assert na(ptrs=ptrs) == NULL
+    # 68 KiB images: 1445 heads fit the scratch, 1446 do not (KDA, dk = 128)
+    img = gdr.gdr_chunk_prefill_workspace_bytes("kda", _torch().bfloat16, 1, 64, 1, 128, 128)
+    assert 1445 * img <= (96 << 20) < 1446 * img
+    assert na(B=1, H=1446) == SCRATCH
+    assert na(B=2, H=723) == SCRATCH
+    assert na(B=1, H=1446, T=0) != SCRATCH                    # T == 0 needs no scratch
+    assert na(gate=0, B=1, H=1446) != SCRATCH                 # GDN fused needs none
+    assert na(gate=0, flags=gdr.SCHED_SPLIT, B=1, H=1446) != SCRATCH  # the small GDN image fits
+
+
+def _torch():
+    import torch
+    return torch
