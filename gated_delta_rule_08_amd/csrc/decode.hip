@@ -73,7 +73,7 @@ __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
 }
 
 template <int DK, int DV, typename InT, bool KDA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 1 : 4))) void decode_step_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_step_kernel(
     int n_units, float scale, const InT* __restrict__ q, const InT* __restrict__ k,
     const InT* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
     float* __restrict__ state, InT* __restrict__ o, int pro) {
@@ -89,9 +89,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 1 : 4
     static_assert(UPW >= 1 && UPW * NSLICE == 4, "the four waves cover whole heads");
     // q, k and (KDA) the gate of the workgroup's heads, read by every wave
     // of the head from LDS when a row needs them instead of being held in
-    // registers: GDN then fits 128 VGPRs, four waves per SIMD (measured
-    // 48.8 -> 47.4 us per launch at B=64, H=32, d=128); KDA's extra gate
-    // reads keep it at three (forced to four it spills).
+    // registers: both gates then fit 128 VGPRs, four waves per SIMD (GDN
+    // measured 48.8 -> 47.4 us per launch at B=64, H=32, d=128; KDA, whose
+    // three reads per row the compiler would otherwise hoist for all 16 rows
+    // (129 VGPRs, three waves), takes them 8 rows at a time: 203 -> 195 us
+    // at B=256).
     __shared__ float qs[UPW][DK], ks[UPW][DK], gs[KDA ? UPW : 1][KDA ? DK : 1];
 
     const int lane = threadIdx.x & 63;
@@ -162,6 +164,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 1 : 4
     float kq = 0.f;
 #pragma unroll
     for (int m = 0; m < NI; ++m) {
+        if (KDA && (m & 7) == 0) __builtin_amdgcn_sched_barrier(0);  // the next 8 rows' reads
         const int row = m * RPI + rg;
         const float a = KDA ? gs[lu][row] : ag, kr = kv[row], qr = qv[row];
         s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;

@@ -87,6 +87,12 @@ constexpr float kLog2Floor = -115.4f;  // GDN: log2(alpha) floor, alpha ~ e^-80
 constexpr float kKdaMinGate = 3.0517578125e-05f;  // KDA: alpha floor 2^-15 (factors within 2^+-120)
 constexpr int kRR = 160;  // KDA right-operand rows: block r keeps rows 0 .. 16 r + 15 (16 + 32 + 48 + 64)
 __device__ __forceinline__ constexpr int rr_row0(int r) { return 8 * r * (r + 1); }  // first row of block r's set
+// KDA chunk-local rows in LDS (left rows, right rows): the 16-byte unit j of
+// row R sits at unit j ^ ((R / 8) mod U) (U units per row).  A gating store
+// writes 16 rows four apart at one unit, which would otherwise meet on two
+// bank groups; the matrix-core reads apply the same map.
+template <int U>
+__device__ __forceinline__ int kswz(int row, int unit) { return unit ^ ((row >> 3) & (U - 1)); }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
 // but leaves global loads in flight (a full __syncthreads also drains vmcnt,
@@ -306,7 +312,9 @@ constexpr int block_threads() {
 // so each wave may use the whole register file.
 template <int NSW, bool KDA, int MODE>
 constexpr int waves_per_simd() {
-    return (MODE == kChain && load_waves<NSW, KDA>() + NSW <= 4) ? 1 : 2;
+    // (KDA's chunk-local kernel: its LDS keeps it at one workgroup per CU,
+    // one wave per SIMD, so it may use the whole register file too)
+    return (MODE == kChain && load_waves<NSW, KDA>() + NSW <= 4) || (MODE == kPrep && KDA) ? 1 : 2;
 }
 
 __device__ __forceinline__ int ptile(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }  // ct <= rt
@@ -437,18 +445,23 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     };
     float* scr0 = reinterpret_cast<float*>(smem + (MODE == kPrep ? L::pScr : ONEBAR ? L::uScr : L::oScr));
 
+    // KDA chunk-local rows: element position of (row, col) under the unit map
+    constexpr bool KSW = KDA && MODE == kPrep;
+    auto kpos = [](int row, int col) {
+        return KSW ? (kswz<L::DKP / 8>(row, col >> 3) << 3) | (col & 7) : col;
+    };
     if constexpr (L::DKP != DK && MODE != kChain) {  // zero the contraction padding
         constexpr int W = L::DKP - DK;
         constexpr int NB = MODE == kPrep ? 1 : ONEBAR ? 3 : 2;
         for (int idx = tid; idx < NB * kC * W; idx += blockDim.x) {
             const int c = idx / (kC * W), r = idx % (kC * W);
-            const int t = r / W, col = ONEBAR ? perm_pos(DK + r % W) : DK + r % W;
+            const int t = r / W, col = ONEBAR ? perm_pos(DK + r % W) : kpos(r / W, DK + r % W);
             prep_lds_b(c, L::oKh, L::pKh)[t * L::PK + col] = 0;
             prep_lds_b(c, L::oQh, L::pQh)[t * L::PK + col] = 0;
         }
-        if constexpr (KDA && MODE == kPrep) {
+        if constexpr (KSW) {
             for (int idx = tid; idx < kRR * W; idx += blockDim.x)
-                Kc[(idx / W) * L::PK + DK + idx % W] = 0;
+                Kc[(idx / W) * L::PK + kpos(idx / W, DK + idx % W)] = 0;
         }
     }
     // kPrep: the same padding in the image of chunk c, which the chain reads
@@ -614,84 +627,76 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 // 2^(G_t - X) (Khat, Qhat, left rows), pass 3 backward with
                 // 2^(inc - G_t) (Ktil, right rows).  Every factor lies within
                 // 2^+-120 (see the file header).
-                // The two halves of the octet (4 channels each) run one after
-                // the other to bound the live factors (rows go out as 8-byte
-                // pieces).
                 const int blk = tg >> 2;
+                float ga[NA], cK[8], cD[8], cT[8], cR[4][8];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int cc = c8 + 4 * hh;
-                    float ga[4][4], cK[4], cD[4], cT[4], cR[4][4];  // [token][channel], [.][channel]
+                for (int i = 0; i < NA; ++i)
+                    ga[i] = valid[i >> 3] ? fmaxf(sig ? sigmoid_f(R.a[i]) : R.a[i], kKdaMinGate) : 1.f;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float a = R.a[8 * u + 4 * hh + e];
-                            ga[u][e] = valid[u] ? fmaxf(sig ? sigmoid_f(a) : a, kKdaMinGate) : 1.f;
-                        }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float tot = lg2(ga[0][e] * ga[1][e] * ga[2][e] * ga[3][e]);
-                        const float inc = row_scan(tot);
-                        const float X = inc - tot;
-                        const float gend = row_share<15>(inc);
-                        const float m0 = row_share<1>(inc), m1 = row_share<5>(inc);
-                        const float m2 = row_share<9>(inc), m3 = row_share<13>(inc);
-                        const float mb = blk == 0 ? m0 : blk == 1 ? m1 : blk == 2 ? m2 : m3;
-                        cK[e] = ex2(X);
-                        cD[e] = ex2(X - mb);
-                        cT[e] = ex2(gend - inc);
-                        cR[0][e] = blk == 0 ? ex2(m0 - inc) : 0.f;
-                        cR[1][e] = blk <= 1 ? ex2(m1 - inc) : 0.f;
-                        cR[2][e] = blk <= 2 ? ex2(m2 - inc) : 0.f;
-                        cR[3][e] = ex2(m3 - inc);
-                        if (tg == 0) prep_out_f(c, L::oGend)[cc + e] = ex2(gend);
-                    }
-                    auto kval = [&](int u, int e) { return bf_at(kz[u], 4 * hh + e) * nk[u]; };
-                    auto qval = [&](int u, int e) { return bf_at(qz[u], 4 * hh + e) * nq[u]; };
-                    float run[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int t = 4 * tg + u;
-                        bf16x4 kh, qh, dl, dq;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            run[e] = u == 0 ? ga[0][e] : run[e] * ga[u][e];  // 2^(G_t - X)
-                            const float kp = kval(u, e) * run[e], qp = qval(u, e) * run[e];
-                            kh[e] = static_cast<__bf16>(kp * cK[e]);
-                            qh[e] = static_cast<__bf16>(qp * cK[e]);
-                            dl[e] = static_cast<__bf16>(kp * cD[e]);
-                            dq[e] = static_cast<__bf16>(qp * cD[e]);
-                        }
-                        *reinterpret_cast<bf16x4*>(Kh + t * L::PK + cc) = dl;
-                        *reinterpret_cast<bf16x4*>(Qh + t * L::PK + cc) = dq;
-                        *reinterpret_cast<bf16x4*>(KhI + t * L::PK + cc) = kh;
-                        *reinterpret_cast<bf16x4*>(QhI + t * L::PK + cc) = qh;
-                    }
-                    uint32_t ktw[4][2];
-                    float rev[4];
-#pragma unroll
-                    for (int u = 3; u >= 0; --u) {
-                        const int t = 4 * tg + u;
-                        bf16x4 rr[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            rev[e] = u == 3 ? 1.f : rev[e] * ga[u + 1][e];  // 2^(inc - G_t)
-                            const float ks = kval(u, e) * rev[e];
-                            const uint32_t kt = bf_bits(ks * cT[e]);
-                            if (u & 1) ktw[e][u >> 1] = kt << 16;
-                            else ktw[e][u >> 1] |= kt;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) rr[r][e] = static_cast<__bf16>(ks * cR[r][e]);
-                        }
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (r >= blk) *reinterpret_cast<bf16x4*>(Kc + (rr_row0(r) + t) * L::PK + cc) = rr[r];
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        *reinterpret_cast<uint2*>(Kt + (cc + e) * L::PT + 4 * tg) = make_uint2(ktw[e][0], ktw[e][1]);
+                for (int e = 0; e < 8; ++e) {
+                    const float tot = lg2(ga[e] * ga[8 + e] * ga[16 + e] * ga[24 + e]);
+                    const float inc = row_scan(tot);
+                    const float X = inc - tot;
+                    const float gend = row_share<15>(inc);
+                    const float m0 = row_share<1>(inc), m1 = row_share<5>(inc);
+                    const float m2 = row_share<9>(inc), m3 = row_share<13>(inc);
+                    const float mb = blk == 0 ? m0 : blk == 1 ? m1 : blk == 2 ? m2 : m3;
+                    cK[e] = ex2(X);
+                    cD[e] = ex2(X - mb);
+                    cT[e] = ex2(gend - inc);
+                    cR[0][e] = blk == 0 ? ex2(m0 - inc) : 0.f;
+                    cR[1][e] = blk <= 1 ? ex2(m1 - inc) : 0.f;
+                    cR[2][e] = blk <= 2 ? ex2(m2 - inc) : 0.f;
+                    cR[3][e] = ex2(m3 - inc);
+                    if (tg == 0) prep_out_f(c, L::oGend)[c8 + e] = ex2(gend);
                 }
+                float run[8];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int t = 4 * tg + u;
+                    bf16x8 kh, qh, dl, dq;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        run[e] = u == 0 ? ga[e] : run[e] * ga[8 * u + e];  // 2^(G_t - X)
+                        const float kp = bf_at(kz[u], e) * nk[u] * run[e];
+                        const float qp = bf_at(qz[u], e) * nq[u] * run[e];
+                        kh[e] = static_cast<__bf16>(kp * cK[e]);
+                        qh[e] = static_cast<__bf16>(qp * cK[e]);
+                        dl[e] = static_cast<__bf16>(kp * cD[e]);
+                        dq[e] = static_cast<__bf16>(qp * cD[e]);
+                    }
+                    const int pos = kpos(t, c8);
+                    *reinterpret_cast<bf16x8*>(Kh + t * L::PK + pos) = dl;
+                    *reinterpret_cast<bf16x8*>(Qh + t * L::PK + pos) = dq;
+                    *reinterpret_cast<bf16x8*>(KhI + t * L::PK + c8) = kh;
+                    *reinterpret_cast<bf16x8*>(QhI + t * L::PK + c8) = qh;
+                }
+                uint32_t ktw[8][2];
+                float rev[8];
+#pragma unroll
+                for (int u = 3; u >= 0; --u) {
+                    const int t = 4 * tg + u;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        bf16x8 rr;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            if (r == 0) rev[e] = u == 3 ? 1.f : rev[e] * ga[8 * (u + 1) + e];  // 2^(inc - G_t)
+                            const float ks = bf_at(kz[u], e) * nk[u] * rev[e];
+                            if (r == 0) {
+                                const uint32_t kt = bf_bits(ks * cT[e]);
+                                if (u & 1) ktw[e][u >> 1] = kt << 16;
+                                else ktw[e][u >> 1] |= kt;
+                            }
+                            rr[e] = static_cast<__bf16>(ks * cR[r][e]);
+                        }
+                        const int row = rr_row0(r) + t;
+                        if (r >= blk) *reinterpret_cast<bf16x8*>(Kc + row * L::PK + kpos(row, c8)) = rr;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<uint2*>(Kt + (c8 + e) * L::PT + 4 * tg) = make_uint2(ktw[e][0], ktw[e][1]);
             } else {
                 if (wave == kScanWave) {
                     // scalar gates: token t = lane; inclusive scan of log2 alpha
@@ -977,17 +982,22 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         }
         f32x4 accA[4] = {zero4(), zero4(), zero4(), zero4()};
         f32x4 accB[2] = {zero4(), zero4()};
+        // KDA rows sit under the unit map (kpos); rA0 / rB0: first absolute
+        // right row of the row blocks' sets
+        const int rA0 = KDA ? rr_row0(rA) : 0, rB0 = KDA ? rr_row0(rB) : 0;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             bf16x8 kr[4], krb[2];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
-                if (ct <= rA) kr[ct] = lds8(Kr + (16 * ct + lr) * L::PK + 32 * s + 8 * lg);
+                if (ct <= rA) kr[ct] = lds8(Kr + (16 * ct + lr) * L::PK + kpos(rA0 + 16 * ct + lr, 32 * s + 8 * lg));
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                if (ct <= rB) krb[ct] = KDA ? lds8(KrB + (16 * ct + lr) * L::PK + 32 * s + 8 * lg) : kr[ct];
-            const bf16x8 mA = lds8(M + (16 * rA + lr) * L::PK + 32 * s + 8 * lg);
-            const bf16x8 mB = lds8(M + (16 * rB + lr) * L::PK + 32 * s + 8 * lg);
+                if (ct <= rB)
+                    krb[ct] = KDA ? lds8(KrB + (16 * ct + lr) * L::PK + kpos(rB0 + 16 * ct + lr, 32 * s + 8 * lg))
+                                  : kr[ct];
+            const bf16x8 mA = lds8(M + (16 * rA + lr) * L::PK + kpos(16 * rA + lr, 32 * s + 8 * lg));
+            const bf16x8 mB = lds8(M + (16 * rB + lr) * L::PK + kpos(16 * rB + lr, 32 * s + 8 * lg));
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
                 if (ct <= rA) accA[ct] = mfma32(kr[ct], mA, accA[ct]);
@@ -1066,7 +1076,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     };
 
     // kPrep: the 16x16 blocks of T = (I + A)^{-1} from -A and the D_r^{-1}
-    // (one wave):  T_rr = D_r^{-1},  T_rk = D_r^{-1} sum_{k<=m<r} (-A_rm) T_mk.
+    // (one wave, after the barrier that follows prep_ap):
+    //   T_rr = D_r^{-1},  T_rk = D_r^{-1} sum_{k<=m<r} (-A_rm) T_mk.
     // Z = sum_m (-A_rm) T_mk is formed in the accumulator layout, which is
     // the A-operand layout of Z^T, so the second product gives (D_r^{-1} Z)^T,
     // whose accumulator layout is the row-fragment layout the chain reads.
@@ -1435,8 +1446,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         // A few consecutive chunks of one head per workgroup; the inputs of
         // chunk c+1 are loaded into registers while chunk c is gated and
         // multiplied, and the outputs go straight to the image.  prep_t of
-        // chunk c (wave 0) only touches its own LDS tiles, which the next
-        // chunk's products overwrite after the next barrier.
+        // chunk c only touches its own LDS tiles, which the next chunk's
+        // products overwrite after the next barrier.  It runs on wave 1,
+        // which forms P tiles only (waves 0 and 2 also invert the diagonal
+        // blocks), so the waves reach the next barrier together.
         PrepIn pin;
         // (a packed sequence may end before this workgroup's chunks begin)
         if (pc < pc_end) prep_load(pc, pin);
@@ -1447,7 +1460,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             lds_barrier();
             prep_ap(c);
             lds_barrier();
-            if (wave == 0) prep_t(c);
+            if (wave == 1) prep_t(c);
         }
     } else if constexpr (MODE == kChain) {
         if (wave < kLoad) {
@@ -1739,8 +1752,10 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
                                         static_cast<int>(std::min<size_t>(nch, img_cap / head_chunk))));
     for (int c0 = 0; c0 < nch; c0 += rc) {
         const int c1 = std::min(nch, c0 + rc);
-        // chunks per chunk-local workgroup: about two workgroups per CU
-        const int cpw = std::max(1, (B * H * (c1 - c0) + 511) / 512);
+        // chunks per chunk-local workgroup: about two workgroups per CU (KDA:
+        // one, its LDS allows one per CU)
+        constexpr int kPrepGroups = KDA ? 256 : 512;
+        const int cpw = std::max(1, (B * H * (c1 - c0) + kPrepGroups - 1) / kPrepGroups);
         const int groups_per_head = (c1 - c0 + cpw - 1) / cpw;
         if (!grid_fits(static_cast<unsigned long long>(B) * H * groups_per_head, block_threads<1, KDA, kPrep>()))
             return hipErrorInvalidConfiguration;
