@@ -1300,9 +1300,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(A.kf[rt][s], bS[s], acc[rt]);
     };
-    // phase 2: X = diag(beta) (V - Khat S), U = (I + A)^{-1} X
-    auto phase_u = [&](const OpsA& A, const f32x4 (&acc)[4], const VIn& V) {
-        float vv[4][4];  // v[16 rt + 4 lg + i][col0 + lr]
+    // v of the chunk in the accumulator layout, vv[rt][i] = v[16 rt + 4 lg + i][col0 + lr]
+    // (staged: through the wave's LDS tile)
+    auto v_regs = [&](const VIn& V, float (&vv)[4][4]) {
         if constexpr (VSTAGE) {
             typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
             unsigned char* vt = smem + L::vbase(MODE, KDA) + sw * L::VST;
@@ -1325,6 +1325,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 for (int i = 0; i < 4; ++i)
                     vv[rt][i] = (lr & 1) ? bf_hi(V[4 * rt + i]) : bf_lo(V[4 * rt + i]);
         }
+    };
+    // phase 2: X = diag(beta) (V - Khat S), U = (I + A)^{-1} X
+    auto phase_u = [&](const OpsA& A, const f32x4 (&acc)[4], const float (&vv)[4][4]) {
         f32x4 X[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -1568,9 +1571,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                 __builtin_amdgcn_sched_barrier(0);
                 load_a2(i, A);
                 phase_ks(A, acc);
+                // v's LDS round trip before the next phase's operand reads:
+                // LDS requests complete in order, so X would otherwise wait
+                // for all of them
+                float vv[4][4];
+                v_regs(vr, vv);
                 __builtin_amdgcn_sched_barrier(0);
                 load_b1(i, Bo);
-                phase_u(A, acc, vr);
+                phase_u(A, acc, vv);
                 if (i + 1 < nch) serial_vload(i + 1, vr);
                 __builtin_amdgcn_sched_barrier(0);
                 load_b2(i, Bo);
@@ -1632,10 +1640,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             {
                 OpsA A;
                 f32x4 acc[4];
+                float vv[4][4];
                 load_a1(i, A);
                 load_a2(i, A);
                 phase_ks(A, acc);
-                phase_u(A, acc, cur);
+                v_regs(cur, vv);
+                phase_u(A, acc, vv);
             }
             __builtin_amdgcn_sched_barrier(0);
             {
@@ -1669,10 +1679,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             {
                 OpsA A;
                 f32x4 acc[4];
+                float vv[4][4];
                 load_a1(i, A);
                 load_a2(i, A);
                 phase_ks(A, acc);
-                phase_u(A, acc, cur);
+                v_regs(cur, vv);
+                phase_u(A, acc, vv);
             }
             lds_barrier();
             {
