@@ -202,7 +202,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <int DK, int NSW, bool KDA>
 struct Layout {
     static constexpr int DKP = DK < 32 ? 32 : DK;  // contraction pad (dk = 16)
-    static constexpr int PK = DKP + 8;             // pitch of [token][channel] tiles (bf16)
+    // pitch of [token][channel] tiles (bf16).  KDA reads row fragments as
+    // two 8-byte pieces (conflict-free at DKP + 8); GDN reads them as one
+    // 16-byte piece, and 16-byte reads of lanes 8b..8b+7 share an LDS cycle
+    // with lanes 8(b^7)..: a pitch of DKP + 16 puts rows r and r + 8 on
+    // disjoint banks (and halves the conflicts of the transposing reads).
+    static constexpr int PK = DKP + (KDA ? 8 : 16);
     static constexpr int PT = kC + 4;              // pitch of [channel][token] tiles (bf16)
     static constexpr int PD = 16 + 8;              // pitch of packed 16x16 tiles (bf16)
     static constexpr int TILE = 16 * PD * 2;       // bytes of one packed tile
