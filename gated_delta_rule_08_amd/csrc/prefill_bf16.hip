@@ -492,7 +492,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     constexpr int OPR = DK / 8;  // octets per row
     const int oct = KDA ? tid >> 4 : tid % OPR;
     const int tg = KDA ? tid & 15 : tid / OPR;
-    const bool gater = tid < 2 * DK;  // DK/8 octets x 16 token runs
+    // DK/8 octets x 16 token runs (GDN kFused, dk = 128: every prep lane)
+    const bool gater = (ONEBAR && 2 * DK >= kPrepWaves * 64) || tid < 2 * DK;
     const int c8 = 8 * oct;           // first channel of this lane's octet
     constexpr int NA = KDA ? 32 : 4;  // gate values per lane
     // GDN: the wave that scans the scalar gates (one with a light tile load:
@@ -505,12 +506,38 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     };
     const size_t tok0 = tseq * H + h;  // token (b, 0, h)
     auto prep_load = [&](int c, PrepIn& R) {
+        // ONEBAR: R was gated this step; the other register set's 10 loads
+        // (one step younger) may still be in flight.  Every older load has
+        // landed, which the wait states explicitly: otherwise the register
+        // reuse below is guarded by waits that also drain the younger set.
+        if constexpr (ONEBAR) __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
         const int t0 = c * kC, nn = min(kC, T - t0);
         const size_t rb = tok0 + static_cast<size_t>(t0) * H;  // row of token t0 (uniform)
         const bf16_t* kb = k + rb * DK;
         const bf16_t* qb = q + rb * DK;
         const float* ab = KDA ? alpha + rb * DK : alpha + rb;
         const float* bb = beta + rb;
+        if constexpr (ONEBAR) {
+            // range-checked loads: rows past the chunk's end (and every row
+            // of a chunk past the sequence's end) read zero
+            const uint32_t nr = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(max(nn, 0)));  // uniform
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, nr * H * DK * 2);
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, nr * H * DK * 2);
+            if (gater) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t off = static_cast<uint32_t>(((4 * tg + u) * H * DK + c8) * 2);
+                    R.kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                    R.qr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+                }
+            }
+            // gates, token = lane (used by the scan wave; every wave loads
+            // them, so every wave has the same 10 loads in flight per set)
+            const uint32_t off = static_cast<uint32_t>(lane * H * 4);
+            R.a[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(ab, nr * H * 4), off, 0, 0));
+            R.bt[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(bb, nr * H * 4), off, 0, 0));
+            return;
+        }
         if (gater) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -1608,14 +1635,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             // while the serial waves run chunk i; nch + 2 barriers in all.
             // The inputs alternate between two register sets (even / odd
             // chunks) and are loaded two steps ahead.
+            // Every step issues its loads (past the end: zeros), so the
+            // loads come in the same order on every path.
             PrepIn pin2;
-            if (nch > 0) prep_load(0, pin);
-            if (nch > 1) prep_load(1, pin2);
+            prep_load(0, pin);
+            prep_load(1, pin2);
             auto step = [&](int i, PrepIn& cur) {  // cur holds chunk i + 2
-                if (i + 2 < nch) {
-                    prep_gate(i + 2, cur);
-                    if (i + 4 < nch) prep_load(i + 4, cur);
-                }
+                if (i + 2 < nch) prep_gate(i + 2, cur);
+                prep_load(i + 4, cur);
                 if (i + 1 >= 0 && i + 1 < nch) prep_ap(i + 1);
                 lds_barrier();
             };
