@@ -496,9 +496,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     const bool gater = (ONEBAR && 2 * DK >= kPrepWaves * 64) || tid < 2 * DK;
     const int c8 = 8 * oct;           // first channel of this lane's octet
     constexpr int NA = KDA ? 32 : 4;  // gate values per lane
-    // GDN: the wave that scans the scalar gates (one with a light tile load:
-    // see the tile lists of prep_ap)
-    constexpr int kScanWave = ONEBAR ? 2 : 1;
+    // GDN: the wave that scans the scalar gates (kFused: one that inverts no
+    // diagonal block; see the tile lists of prep_ap)
+    constexpr int kScanWave = ONEBAR ? 3 : 1;
     struct PrepIn {
         uint4 kr[4], qr[4];
         float a[NA];
