@@ -264,7 +264,8 @@ struct Layout {
     static constexpr int uU = uGend + 16;   // [64] row factors
     static constexpr int uW = uU + kC * 4;  // [64] column factors
     static constexpr int uC = uW + kC * 4;  // [4][4] block-pair factors (r > c)
-    static constexpr int OPS = (uC + 64 + 15) / 16 * 16;  // operand set stride
+    static constexpr int uEs = uC + 64;     // [64] scale 2^G_t (the output's row factor)
+    static constexpr int OPS = (uEs + kC * 4 + 15) / 16 * 16;  // operand set stride
     static constexpr int uTB = 3 * OPS;                      // first tile set
     static constexpr int TLS = 20 * TILE;                    // tile set: P (10), -A (6), D (4)
     static constexpr int uScr = uTB + 2 * TLS;
@@ -755,6 +756,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                             const int br = lane >> 2, bc = lane & 3;
                             ops[L::uC / 4 + lane] = br > bc ? ex2(gb(br - 1) - gb(bc)) : 0.f;
                         }
+                        ops[L::uEs / 4 + lane] = ex2(x) * scale;
                     }
                     sGp(c)[lane] = x;
                     prep_out_f(c, L::oEg)[lane] = ex2(x);
@@ -968,7 +970,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     if (cl < r) {
                         const float4 w = wj[cl];
                         const float cf = cl == 0 ? cr[r].x : cl == 1 ? cr[r].y : cr[r].z;
-                        const float f = ut[r] * cf;
+                        // P tiles carry the output scale
+                        const float f = tP_ ? ut[r] * cf * scale : ut[r] * cf;
                         const float wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
@@ -982,7 +985,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                         for (int i = 0; i < 4; ++i) {
                             const int j = 16 * cl + 4 * lg + i;
                             const float xx = acc[x][i] * ex2(fminf(gt[r] - gv[i], 0.f));
-                            val[i] = tP_ ? (j <= t ? xx : 0.f) : (j < t ? bt[r] * xx : 0.f);
+                            val[i] = tP_ ? (j <= t ? xx * scale : 0.f) : (j < t ? bt[r] * xx : 0.f);
                         }
                     }
                     if (tP_) {
@@ -1256,6 +1259,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         const bf16_t* Qh = bfp(c, L::oQh);
         const bf16_t* Pt = bfp(c, L::oP);
         const float* eg = f32p(c, L::oEg);
+        const float* es = ONEBAR ? reinterpret_cast<const float*>(smem + (c % 3) * L::OPS + L::uEs) : eg;
         const bf16x4 z4 = cvt4(zero4());
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -1265,7 +1269,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
                     ? perm_frag(stg(c, L::lQ), 16 * rt + lr, 32 * s + 4 * lg)
                     : ONEBAR ? lds8(Qh + (16 * rt + lr) * L::PK + 32 * s + 8 * lg)  // permuted rows
                              : lds_perm(Qh + (16 * rt + lr) * L::PK + 32 * s + 4 * lg);
-            Bo.egt[rt] = KDA ? 1.f : eg[16 * rt + lr];
+            // GDN 2^G_t (ONEBAR: scale 2^G_t; P carries the scale too)
+            Bo.egt[rt] = KDA ? 1.f : ONEBAR ? es[16 * rt + lr] : eg[16 * rt + lr];
         }
         // P pieces: (rt, s) for 2 s <= rt -> 6 pieces
 #pragma unroll
@@ -1412,7 +1417,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             if (rt >= 2) oacc[rt] = mfma32(u23, Bo.pf[x++], oacc[rt]);
             const int t = 16 * rt + lr;
             const uint32_t off = t < n ? static_cast<uint32_t>((t * H * DV + 4 * lg) * 2) : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(oacc[rt] * scale)), ors,
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(ONEBAR ? oacc[rt] : oacc[rt] * scale)), ors,
                                                   off, 0, 0);
         }
     };
