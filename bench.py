@@ -511,7 +511,8 @@ def bench_backward(torch, gdr, synth, name, steps, warmup):
             "tokens_per_s": B * T * steps / elapsed, "workspace_bytes": need,
             "roofline": {"bound": "alu", "achieved": round(flops / sec / 1e12, 2), "peak": FP32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(flops / sec / 1e12 / FP32_PEAK_TFLOPS, 4),
-                         "traffic": None, "algorithmic_flops": flops},
+                         "traffic": load_traffic("backward_" + w.gate, src_hash("backward.hip")),
+                         "algorithmic_flops": flops},
             "hbm": {"achieved": round(nbytes / sec / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
 
