@@ -42,13 +42,13 @@
 // Mapping.  One workgroup per (b, h, slice of 16*NSW value columns); the value
 // columns of S are independent, so the slices of a head run on different CUs
 // (their block ids are congruent mod 8: one XCD, shared L2).  Waves 0..3 are
-// "prep" waves, waves 4.. are "serial" waves owning 16 value columns each:
-//   iteration i, phase 1: prep gates chunk i+1 into LDS buffer (i+1)&1 and
-//                         prefetches chunk i+2; serial computes Khat S, X and
-//                         U for chunk i from buffer i&1;
-//   phase 2:              prep forms A, P and the D_r^{-1} of chunk i+1;
-//                         serial forms O and updates S for chunk i.
-// Two workgroup barriers per chunk.  The serial chain keeps S, X and U in
+// "prep" waves, waves 4.. are "serial" waves owning 16 value columns each.
+// GDN (kFused), one workgroup barrier per step: in step i the prep waves gate
+// chunk i+2 and form A, P and the D_r^{-1} of chunk i+1 while the serial waves
+// compute Khat S, X, U, O and the new S of chunk i, so LDS holds three sets
+// of gated operands and two sets of tiles.  KDA runs the same prep work once
+// per (head, chunk) in kPrep and the serial work in kChain (below).  The
+// serial chain keeps S, X and U in
 // MFMA registers: an fp32 accumulator tile holds rows 4g..4g+3 of column l%16
 // in lane l (g = l/16), so two row tiles together are the B operand of a
 // K=32 step whose k order is {4g..4g+3, 16+4g..16+4g+3}; the LDS operand of
