@@ -351,9 +351,9 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
 }
 
 // ---------------------------------------------------------------- bwd_fwd
-// FS value columns per workgroup: 32 when that still puts a workgroup on
-// every CU (the kernel's LDS has room for them, and a wider slice reads each
-// chunk image for more columns), else 16.
+// FS value columns per workgroup: the widest of 64, 32 and 16 that still
+// puts a workgroup on every CU (the kernel's LDS has room for them, and a
+// wider slice reads each chunk image for more columns).
 template <int DK, bool KDA, typename InT, int FS>
 __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
     constexpr int KP = DK + 1;
@@ -1389,8 +1389,9 @@ hipError_t run(Args a, hipStream_t s) {
         return hipErrorInvalidConfiguration;
     const unsigned heads8 = static_cast<unsigned>(h8);  // slice grids: whole groups of 8 heads
     const unsigned per_chunk = static_cast<unsigned>(static_cast<unsigned long long>(a.B) * a.H * a.nch);
-    // The checkpoint chain takes 32-column slices when that still puts a
-    // workgroup on every CU; the reverse chain always takes 16 (at 16 it has
+    // The checkpoint chain takes the widest slices (64, 32 or 16 columns)
+    // that still put a workgroup on every CU; the reverse chain always takes
+    // 16 (at 16 it has
     // the registers to load the next chunk's image during the current one,
     // which costs less than the extra rounds of workgroups).
     const long long BH = static_cast<long long>(a.B) * a.H;
