@@ -55,6 +55,7 @@
 // that step is read in the same k order, which keeps every product exact
 // without any register shuffle.
 #include <algorithm>
+#include <numeric>
 #include <type_traits>
 
 #include "gdr_internal.h"
@@ -1752,10 +1753,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
 // stay within about 96 MiB, well inside the 256 MB last-level cache, so the
 // chain kernel reads what the chunk-local kernel has just written from cache.
 constexpr size_t kRangeBytes = size_t(96) << 20;
-inline int split_range_chunks(int BH, int nch, size_t img_bytes) {
+// Chunk-local workgroups of one range (about two per CU; KDA: one, its LDS
+// allows one per CU).
+constexpr int prep_groups(bool kda) { return kda ? 256 : 512; }
+inline int split_range_chunks(int BH, int nch, size_t img_bytes, bool kda) {
     const size_t per_chunk = static_cast<size_t>(BH) * img_bytes;
     const size_t r = per_chunk ? kRangeBytes / per_chunk : 0;
-    return static_cast<int>(std::max<size_t>(1, std::min<size_t>(static_cast<size_t>(nch), r)));
+    int rc = static_cast<int>(std::max<size_t>(1, std::min<size_t>(static_cast<size_t>(nch), r)));
+    // A range of a multiple of `unit` chunks gives every chunk-local
+    // workgroup the same number of chunks (KDA workload: 40-chunk ranges, 5
+    // chunks per workgroup, instead of 45 with 6 for most and 3 for some).
+    const int unit = prep_groups(kda) / std::gcd(prep_groups(kda), std::max(BH, 1));
+    if (rc < nch && rc > unit) rc = rc / unit * unit;
+    return rc;
 }
 
 template <int DK, int NSW, bool KDA>
@@ -1797,13 +1807,12 @@ hipError_t launch(int B, int T, int H, int DV, float scale, const bf16_t* q, con
     if ((e = set_lds(reinterpret_cast<const void*>(chain), chain_lds)) != hipSuccess) return e;
     const int nch = (T + kC - 1) / kC;
     const size_t head_chunk = static_cast<size_t>(B) * H * (KDA ? L::IMG : L::TIMG);  // one chunk, all heads
-    const int rc = std::max(1, std::min(split_range_chunks(B * H, nch, KDA ? L::IMG : L::TIMG),
+    const int rc = std::max(1, std::min(split_range_chunks(B * H, nch, KDA ? L::IMG : L::TIMG, KDA),
                                         static_cast<int>(std::min<size_t>(nch, img_cap / head_chunk))));
     for (int c0 = 0; c0 < nch; c0 += rc) {
         const int c1 = std::min(nch, c0 + rc);
-        // chunks per chunk-local workgroup: about two workgroups per CU (KDA:
-        // one, its LDS allows one per CU)
-        constexpr int kPrepGroups = KDA ? 256 : 512;
+        // chunks per chunk-local workgroup
+        constexpr int kPrepGroups = prep_groups(KDA);
         const int cpw = std::max(1, (B * H * (c1 - c0) + kPrepGroups - 1) / kPrepGroups);
         const int groups_per_head = (c1 - c0 + cpw - 1) / cpw;
         if (!grid_fits(static_cast<unsigned long long>(B) * H * groups_per_head, block_threads<1, KDA, kPrep>()))
@@ -1878,7 +1887,7 @@ size_t prefill_bf16_workspace(int kda, int flags, int B, int T, int H, int dk) {
     if (!prefill_bf16_split(kda, flags) || T <= 0 || B <= 0 || H <= 0) return 0;
     const size_t img = prefill_bf16_image_bytes(kda, dk);
     const int nch = (T + kC - 1) / kC;
-    return static_cast<size_t>(B) * H * split_range_chunks(B * H, nch, img) * img;
+    return static_cast<size_t>(B) * H * split_range_chunks(B * H, nch, img, kda != 0) * img;
 }
 
 hipError_t launch_prefill_bf16(int kda, int B, int T, int H, int dk, int dv, float scale,
