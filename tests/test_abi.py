@@ -211,13 +211,13 @@ def test_workspace(lib):
     assert lib.gdr_chunk_prefill_workspace_bytes(0, 1, 4, 8192, 32, 128, 128, 64) == 0
     assert lib.gdr_chunk_prefill_workspace_bytes(1, 0, 1, 256, 2, 128, 128, 64) == 0
     # KDA bf16 stages one image per (b, h, chunk) of a range of chunks; a range
-    # keeps all heads' images within 96 MiB, its chunk count rounded down to a
-    # multiple of 256 / gcd(256, B H) (every chunk-local workgroup of the
+    # keeps all heads' images within 136 MiB, its chunk count rounded down to
+    # a multiple of 256 / gcd(256, B H) (every chunk-local workgroup of the
     # 256 takes the same number of chunks)
     n = gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 32768, 32, 128, 128)
     n1 = gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 64, 1, 128, 128)
     assert n1 > 0 and n1 % 1024 == 0
-    rc = min(512, (96 << 20) // (32 * n1))
+    rc = min(512, (136 << 20) // (32 * n1))
     assert n == 32 * (rc // 8 * 8) * n1
     assert gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 65, 1, 128, 128) == 2 * n1
     assert gdr.gdr_chunk_prefill_workspace_bytes("kda", torch.bfloat16, 1, 0, 1, 128, 128) == 0
