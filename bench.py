@@ -503,12 +503,25 @@ def bench_backward(torch, gdr, synth, name, steps, warmup):
         call()
     elapsed, gpu_s = timed_region(torch, steps, call)
     launch_ms = 1e3 * gpu_s / steps
+    # the same in chunk ranges, with a workspace of at most 2 GB
+    nch = (T + CHUNK - 1) // CHUNK
+    rc = next((c for c in range(nch - 1, 0, -1)
+               if gdr.gdr_chunk_backward_workspace_bytes_ranged(w.gate, torch.bfloat16, B, T, H, dk, dv, c)
+               <= 2 * 10 ** 9), 1)
+    need_r = gdr.gdr_chunk_backward_workspace_bytes_ranged(w.gate, torch.bfloat16, B, T, H, dk, dv, rc)
+    del ws
+    ws_r = torch.empty(need_r, dtype=torch.uint8, device="cuda")
+    call_r = lambda: gdr.gdr_chunk_backward(w.gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], s0, do,
+                                            dst, *out, workspace=ws_r)
+    call_r()
+    _, gpu_r = timed_region(torch, steps, call_r)
     flops = backward_flops(B, T, H, dk, dv)
     nbytes = backward_bytes(w.gate, B, T, H, dk, dv)
     sec = launch_ms / 1e3
     return {"workload": name.replace("prefill", "backward"), "steps": steps,
             "ms_per_step": 1e3 * elapsed / steps, "launch_ms": launch_ms,
             "tokens_per_s": B * T * steps / elapsed, "workspace_bytes": need,
+            "ranged": {"range_chunks": rc, "workspace_bytes": need_r, "launch_ms": 1e3 * gpu_r / steps},
             "roofline": {"bound": "alu", "achieved": round(flops / sec / 1e12, 2), "peak": FP32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(flops / sec / 1e12 / FP32_PEAK_TFLOPS, 4),
                          "traffic": load_traffic("backward_" + w.gate, src_hash("backward.hip")),

@@ -21,6 +21,7 @@ __all__ = [
     "gdr_chunk_prefill_varlen_workspace_bytes", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
     "gdr_abi_version", "EXPORTED_SYMBOLS", "gdr_decode_step_ex", "gdr_chunk_prefill_ex",
     "PRO_L2NORM_QK", "PRO_SIGMOID", "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
+    "gdr_chunk_backward_workspace_bytes_ranged",
     "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex", "SCHED_FUSED", "SCHED_SPLIT",
     "gdr_chunk_prefill_noalloc",
 ]
@@ -41,6 +42,7 @@ EXPORTED_SYMBOLS = ("gdr_decode_step", "gdr_decode_step_ex", "gdr_chunk_prefill_
                     "gdr_chunk_prefill_varlen_workspace_bytes_ex",
                     "gdr_decode_multi_ex", "gdr_chunk_prefill_varlen_ex",
                     "gdr_chunk_backward", "gdr_chunk_backward_workspace_bytes",
+                    "gdr_chunk_backward_workspace_bytes_ranged",
                     "gdr_decode_multi", "gdr_chunk_prefill",
                     "gdr_chunk_prefill_varlen", "gdr_chunk_prefill_varlen_workspace_bytes",
                     "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
@@ -82,6 +84,8 @@ def load_library():
     lib.gdr_chunk_backward.restype = i
     lib.gdr_chunk_backward_workspace_bytes.argtypes = [i] * 8
     lib.gdr_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdr_chunk_backward_workspace_bytes_ranged.argtypes = [i] * 9
+    lib.gdr_chunk_backward_workspace_bytes_ranged.restype = ctypes.c_size_t
     lib.gdr_decode_multi_ex.argtypes = [i] * 8 + [f] + [vp] * 9
     lib.gdr_decode_multi_ex.restype = i
     lib.gdr_chunk_prefill_varlen_ex.argtypes = [i] * 10 + [f] + [vp] * 9 + [i, vp, vp, ctypes.c_size_t, vp]
@@ -404,6 +408,15 @@ def gdr_chunk_backward_workspace_bytes(gate: str, dtype, B: int, T: int, H: int,
         GATES[gate], _DTYPES[dtype], B, T, H, dk, dv, chunk))
 
 
+def gdr_chunk_backward_workspace_bytes_ranged(gate: str, dtype, B: int, T: int, H: int, dk: int,
+                                              dv: int, range_chunks: int, chunk: int = CHUNK) -> int:
+    """Workspace with which the backward runs in ranges of ``range_chunks``
+    chunks (any workspace from the one-chunk size up is accepted; the widest
+    ranges that fit are taken)."""
+    return int(load_library().gdr_chunk_backward_workspace_bytes_ranged(
+        GATES[gate], _DTYPES[dtype], B, T, H, dk, dv, chunk, range_chunks))
+
+
 def gdr_chunk_backward(gate: str, q, k, v, alpha, beta, state_in, grad_o, grad_state_out,
                        grad_q, grad_k, grad_v, grad_alpha, grad_beta, grad_state_in=None,
                        scale: float = 1.0, workspace=None, chunk: int = CHUNK, stream=None) -> None:
@@ -411,7 +424,9 @@ def gdr_chunk_backward(gate: str, q, k, v, alpha, beta, state_in, grad_o, grad_s
     chunked prefill, written into grad_* (shapes and dtypes of the inputs;
     grad_alpha, grad_beta, grad_state_in fp32).  state_in, grad_state_out and
     grad_state_in may be None.  workspace: a device tensor of at least
-    gdr_chunk_backward_workspace_bytes bytes, or None to allocate one."""
+    gdr_chunk_backward_workspace_bytes bytes (one pass) or of fewer, down to
+    gdr_chunk_backward_workspace_bytes_ranged(..., 1) (chunk ranges), or None
+    to allocate the one-pass size."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape != (B, T, H, dv) or grad_o.shape != (B, T, H, dv):

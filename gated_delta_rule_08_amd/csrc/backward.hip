@@ -48,6 +48,8 @@
 //                             everything that maps back to q, k, beta, alpha
 //   bwd_floor  (b, h, chunk)  dalpha where the log-gate floor is active (only
 //                             chunks bwd_local flags do any work)
+#include <algorithm>
+
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -149,6 +151,14 @@ struct Ws {
 
 struct Args {
     int B, T, H, DV, nch;
+    // Chunks c0 .. c0 + nr - 1 run in this launch.  The workspace holds them
+    // only: per-chunk items at wc(bh, ch), token rows at wt(b, t, h) (Tw =
+    // T for the whole sequence at once, nr * 64 for a range of chunks).
+    int c0, nr, Tw;
+    const float* s_in;     // state at chunk c0 (NULL: zeros)
+    float* s_end;          // checkpoint chain: the state after the range (or NULL)
+    const float* ds_end;   // state gradient after the range (NULL: zeros)
+    float* ds_start;       // reverse chain: the gradient at chunk c0 (or NULL)
     int nsl_chain;  // value slices of the reverse chain (parts of sum_j Xr dX per token)
     float scale;
     const void* q;
@@ -166,6 +176,10 @@ struct Args {
     float* dbeta;
     float* ds0;
     float* ws;
+    __host__ __device__ size_t wc(int bh, int ch) const { return static_cast<size_t>(bh) * nr + (ch - c0); }
+    __host__ __device__ size_t wt(int b, int t, int h) const {
+        return (static_cast<size_t>(b) * Tw + (t - c0 * kC)) * H + h;
+    }
 };
 
 // Workgroup -> (head, value slice) of the two chains.  Consecutive workgroups
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
     float* Tl = As + kC * kTP;      // [64][kTP]  Tinv
     float* Bs = Tl + kC * kTP;      // [64]
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
+    const int bh = blockIdx.x / a.nr, ch = a.c0 + static_cast<int>(blockIdx.x - bh * a.nr);
     const int b = bh / a.H, h = bh - b * a.H;
     const int t0 = ch * kC, n = min(kC, a.T - t0);
     const InT* q = static_cast<const InT*>(a.q);
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(kNT) void bwd_prep(Args a) {
         Gs[t * GP + c] = wave_prefix_sum(Gs[t * GP + c]);
     }
     __syncthreads();
-    float* img = a.ws + Ws(a.B, a.T, a.H, DK, a.DV).img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+    float* img = a.ws + Ws(a.B, a.Tw, a.H, DK, a.DV).img + a.wc(bh, ch) * img_floats(DK);
     if constexpr (!KDA) {
         // scalar gate: Ahat = (K K^T) o E and P = (Q K^T) o E with one decay
         // E_ts = exp(G_t - G_s) per pair, so both are matrix products on the
@@ -374,11 +388,11 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
     if (bh >= a.B * a.H) return;  // padding of the grid (whole block, before any barrier)
     const int b = bh / a.H, h = bh - b * a.H;
     const int j0 = sl * FS;
-    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    const Ws W(a.B, a.Tw, a.H, DK, a.DV);
     const InT* v = static_cast<const InT*>(a.v);
     for (int i = tid; i < DK * FS; i += kNT) {
         const int c = i / FS, j = i - c * FS;
-        Ss[i] = a.s0 ? a.s0[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
+        Ss[i] = a.s_in ? a.s_in[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
     }
     // Matrix-core tiles: wave w takes row tile w / NCT and column tile w % NCT
     // of each product (rows t for Xr and U, rows c for S); a lane's column
@@ -391,7 +405,7 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
     constexpr int NTF = kC * kC / kNT;
     float fk0[NKF], fkt[NKF], fti[NTF], fee = 0.f, fb = 0.f;
     auto fetch = [&](int ch) {
-        const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+        const float* im = a.ws + W.img + a.wc(bh, ch) * img_floats(DK);
 #pragma unroll
         for (int m = 0; m < NKF; ++m) {
             const int i = tid + m * kNT;
@@ -404,11 +418,12 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
         const int nn = min(kC, a.T - ch * kC);
         if (tid < kC) fb = tid < nn ? a.beta[(static_cast<size_t>(b) * a.T + ch * kC + tid) * a.H + h] : 0.f;
     };
-    fetch(0);
-    for (int ch = 0; ch < a.nch; ++ch) {
+    const int ce = a.c0 + a.nr;
+    fetch(a.c0);
+    for (int ch = a.c0; ch < ce; ++ch) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();  // the previous chunk is done with every buffer
-        float* ck = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+        float* ck = a.ws + W.ck + a.wc(bh, ch) * DK * a.DV;
         for (int i = tid; i < DK * FS; i += kNT) {
             const int c = i / FS, j = i - c * FS;
             ck[static_cast<size_t>(c) * a.DV + j0 + j] = Ss[i];
@@ -428,7 +443,7 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
         }
         if (tid < DK) eE[tid] = fee;
         if (tid < kC) Bs[tid] = fb;
-        if (ch + 1 < a.nch) fetch(ch + 1);
+        if (ch + 1 < ce) fetch(ch + 1);
         __syncthreads();
         // Xr = V - K0 S
         if (R < kC) {
@@ -441,7 +456,7 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
                 const bool ok = t < n;
                 const float x = ok ? ld(v + row * a.DV + j0 + col) - acc[r] : 0.f;
                 Xs[t * FS + col] = x;
-                if (ok) a.ws[W.xr + row * a.DV + j0 + col] = x;
+                if (ok) a.ws[W.xr + a.wt(b, t0 + t, h) * a.DV + j0 + col] = x;
             }
         }
         __syncthreads();
@@ -464,6 +479,13 @@ __global__ __launch_bounds__(kNT) void bwd_fwd(Args a) {
             }
         }
     }
+    if (a.s_end) {  // the state after the range, where the next range starts
+        __syncthreads();
+        for (int i = tid; i < DK * FS; i += kNT) {
+            const int c = i / FS, j = i - c * FS;
+            a.s_end[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] = Ss[i];
+        }
+    }
 }
 
 // ---------------------------------------------------------------- bwd_dout
@@ -480,13 +502,13 @@ __global__ __launch_bounds__(kNT) void bwd_dout(Args a) {
     float* Ps = Q0 + kC * KP;        // [64][kTP]
     float* Os = Ps + kC * kTP;       // [64][OP]
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
+    const int bh = blockIdx.x / a.nr, ch = a.c0 + static_cast<int>(blockIdx.x - bh * a.nr);
     const int b = bh / a.H, h = bh - b * a.H;
     const int t0 = ch * kC, n = min(kC, a.T - t0);
-    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    const Ws W(a.B, a.Tw, a.H, DK, a.DV);
     const InT* dO = static_cast<const InT*>(a.dO);
-    const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
-    float* hq = a.ws + W.hq + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    const float* im = a.ws + W.img + a.wc(bh, ch) * img_floats(DK);
+    float* hq = a.ws + W.hq + a.wc(bh, ch) * DK * a.DV;
     for (int i = tid; i < kC * DK; i += kNT) Q0[(i / DK) * KP + i % DK] = im[iK0 + 2 * kC * DK + i];
     for (int i = tid; i < kC * kC; i += kNT) Ps[(i >> 6) * kTP + (i & 63)] = im[iP + i];
     const int wave = tid >> 6, li = tid & 15, l4 = (tid & 63) >> 4;
@@ -510,8 +532,7 @@ __global__ __launch_bounds__(kNT) void bwd_dout(Args a) {
                 for (int r = 0; r < 4; ++r) {
                     const int t = R + 4 * l4 + r;
                     if (t < n)
-                        a.ws[W.pd + ((static_cast<size_t>(b) * a.T + t0 + t) * a.H + h) * a.DV + j0 + C + li] =
-                            a.scale * acc[r];
+                        a.ws[W.pd + a.wt(b, t0 + t, h) * a.DV + j0 + C + li] = a.scale * acc[r];
                 }
             } else {
                 const int R = 16 * (rt - 4);
@@ -550,11 +571,11 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
     if (bh >= a.B * a.H) return;  // padding of the grid (whole block, before any barrier)
     const int b = bh / a.H, h = bh - b * a.H;
     const int j0 = sl * FS;
-    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    const Ws W(a.B, a.Tw, a.H, DK, a.DV);
     InT* dv = static_cast<InT*>(a.dv);
     for (int i = tid; i < DK * FS; i += kNT) {
         const int c = i / FS, j = i - c * FS;
-        dS[i] = a.dsT ? a.dsT[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
+        dS[i] = a.ds_end ? a.ds_end[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] : 0.f;
     }
     // Matrix-core tiles: wave w takes row tile w / NCT, column tile w % NCT
     // (a lane's column: 16 (w % NCT) + lane % 16).
@@ -568,7 +589,7 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
     constexpr int NTF = kC * kC / kNT;
     float fk0[NKF], fkt[NKF], fti[NTF];
     auto fetch = [&](int ch) {
-        const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+        const float* im = a.ws + W.img + a.wc(bh, ch) * img_floats(DK);
 #pragma unroll
         for (int m = 0; m < NKF; ++m) {
             const int i = tid + m * kNT;
@@ -578,18 +599,18 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
 #pragma unroll
         for (int m = 0; m < NTF; ++m) fti[m] = im[iT + tid + m * kNT];
     };
-    fetch(a.nch - 1);
-    for (int ch = a.nch - 1; ch >= 0; --ch) {
+    fetch(a.c0 + a.nr - 1);
+    for (int ch = a.c0 + a.nr - 1; ch >= a.c0; --ch) {
         const int t0 = ch * kC, n = min(kC, a.T - t0);
         __syncthreads();
-        float* dck = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
-        const float* hq = a.ws + W.hq + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+        float* dck = a.ws + W.dck + a.wc(bh, ch) * DK * a.DV;
+        const float* hq = a.ws + W.hq + a.wc(bh, ch) * DK * a.DV;
         for (int i = tid; i < DK * FS; i += kNT) {
             const int c = i / FS, j = i - c * FS;
             dck[static_cast<size_t>(c) * a.DV + j0 + j] = dS[i];
             Hq[i] = hq[static_cast<size_t>(c) * a.DV + j0 + j];
         }
-        const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+        const float* im = a.ws + W.img + a.wc(bh, ch) * img_floats(DK);
 #pragma unroll
         for (int m = 0; m < NKF; ++m) {
             const int i = tid + m * kNT;
@@ -607,11 +628,11 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
         if (tid < kC) Bs[tid] = tid < n ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
         for (int i = tid; i < kC * FS; i += kNT) {
             const int t = i / FS, j = i - t * FS;
-            const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
+            const size_t r = a.wt(b, t0 + t, h);
             Xs[i] = t < n ? a.ws[W.xr + r * a.DV + j0 + j] : 0.f;
             Pd[i] = t < n ? a.ws[W.pd + r * a.DV + j0 + j] : 0.f;
         }
-        if (ch > 0) fetch(ch - 1);
+        if (ch > a.c0) fetch(ch - 1);
         __syncthreads();
         // U = Tinv diag(beta) Xr (Tinv zero above its diagonal) on the first
         // 4 NCT waves; dU = Pd + Kt dS_end on the next 4 NCT.
@@ -647,18 +668,16 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
             const int t = i / FS, j = i - t * FS;
             if (t < n) {
                 const size_t r = (static_cast<size_t>(b) * a.T + t0 + t) * a.H + h;
+                const size_t rw = a.wt(b, t0 + t, h);
                 Elem<InT>::store(dv + r * a.DV + j0 + j, Bs[t] * dX[i]);
-                a.ws[W.u + r * a.DV + j0 + j] = Us[i];
-                a.ws[W.dx + r * a.DV + j0 + j] = dX[i];
+                a.ws[W.u + rw * a.DV + j0 + j] = Us[i];
+                a.ws[W.dx + rw * a.DV + j0 + j] = dX[i];
             }
         }
         if (tid < kC) {  // this slice's part of sum_j Xr dX
             float acc = 0.f;
             for (int j = 0; j < FS; ++j) acc += Xs[tid * FS + j] * dX[tid * FS + j];
-            if (tid < n) {
-                const size_t tok = (static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h;
-                a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok] = acc;
-            }
+            if (tid < n) a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.Tw * a.H + a.wt(b, t0 + tid, h)] = acc;
         }
         // dS <- eE dS + Hq - K0^T diag(beta) dX
         if (R < DK) {
@@ -672,10 +691,10 @@ __global__ __launch_bounds__(kNT) void bwd_chain(Args a) {
         }
     }
     __syncthreads();
-    if (a.ds0) {
+    if (a.ds_start) {
         for (int i = tid; i < DK * FS; i += kNT) {
             const int c = i / FS, j = i - c * FS;
-            a.ds0[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] = dS[i];
+            a.ds_start[(static_cast<size_t>(bh) * DK + c) * a.DV + j0 + j] = dS[i];
         }
     }
 }
@@ -720,14 +739,15 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     float* gep = dGtp + 4 * kC;        // [2][16] GDN: dG_end by wave (through eE; through Kt)
 
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
+    const int bh = blockIdx.x / a.nr, ch = a.c0 + static_cast<int>(blockIdx.x - bh * a.nr);
     const int b = bh / a.H, h = bh - b * a.H;
     const int t0c = ch * kC, n = min(kC, a.T - t0c);
-    const Ws W(a.B, a.T, a.H, DK, a.DV);
+    const Ws W(a.B, a.Tw, a.H, DK, a.DV);
     const InT* q = static_cast<const InT*>(a.q);
     const InT* k = static_cast<const InT*>(a.k);
     const InT* dO = static_cast<const InT*>(a.dO);
     auto tok = [&](int t) { return (static_cast<size_t>(b) * a.T + t0c + t) * a.H + h; };
+    auto wtok = [&](int t) { return a.wt(b, t0c + t, h); };  // workspace row
 
     for (int i = tid; i < kC * DK; i += kNT) {
         const int t = i / DK, c = i - t * DK;
@@ -747,10 +767,10 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
         dGt[tid] = 0.f;
     }
     if (tid < DK) dGe[tid] = 0.f;
-    const float* im = a.ws + W.img + (static_cast<size_t>(bh) * a.nch + ch) * img_floats(DK);
+    const float* im = a.ws + W.img + a.wc(bh, ch) * img_floats(DK);
     for (int i = tid; i < kC * kC; i += kNT) Ah[(i >> 6) * kTP + (i & 63)] = im[iA + i];
     floored = __syncthreads_or(floored);
-    if (tid == 0) reinterpret_cast<int*>(a.ws + W.fl)[static_cast<size_t>(bh) * a.nch + ch] = floored;
+    if (tid == 0) reinterpret_cast<int*>(a.ws + W.fl)[a.wc(bh, ch)] = floored;
     for (int c = tid >> 6; c < GW; c += kNT / 64) {  // cumulative log-gate in place
         const int t = tid & 63;
         const float g = wave_prefix_sum(Gs[t * GP + c]);
@@ -767,8 +787,8 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
 #pragma unroll
     for (int i = 0; i < NCT; ++i) aQ[i] = aK[i] = aT[i] = z4;
     float ge = 0.f;  // tid < DK: sum_j dS_end S of channel tid
-    const float* Sg = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
-    const float* Dg = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    const float* Sg = a.ws + W.ck + a.wc(bh, ch) * DK * a.DV;
+    const float* Dg = a.ws + W.dck + a.wc(bh, ch) * DK * a.DV;
     // Contractions over the value columns, block by block:
     //   dQ0' = dO S^T, dK0' = dX S^T, dKt = U dS_end^T, dA' = dX U^T, dP' = dO U^T
     // The next block's values are loaded into registers (each thread a fixed
@@ -787,10 +807,10 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
             pd[m] = ok ? Dg[static_cast<size_t>(c) * a.DV + jb + j] : 0.f;
         }
         const bool ok = ut < n;
-        const size_t r = tok(ut) * a.DV + jb + uj;
+        const size_t r = wtok(ut) * a.DV + jb + uj;  // workspace row
         pu = ok ? a.ws[W.u + r] : 0.f;
         px = ok ? a.ws[W.dx + r] : 0.f;
-        po = ok ? ld(dO + r) : 0.f;
+        po = ok ? ld(dO + tok(ut) * a.DV + jb + uj) : 0.f;
     };
     fetch(0);
     for (int jb = 0; jb < a.DV; jb += CB) {
@@ -1096,7 +1116,7 @@ __global__ __launch_bounds__(kNT) void bwd_local(Args a) {
     }
     if (tid < n) {
         float db = ((dBp[tid] + dBp[kC + tid]) + dBp[2 * kC + tid]) + dBp[3 * kC + tid];
-        for (int sl = 0; sl < a.nsl_chain; ++sl) db += a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.T * a.H + tok(tid)];
+        for (int sl = 0; sl < a.nsl_chain; ++sl) db += a.ws[W.dbp + static_cast<size_t>(sl) * a.B * a.Tw * a.H + wtok(tid)];
         a.dbeta[tok(tid)] = db;
     }
 }
@@ -1135,9 +1155,9 @@ template <int DK, bool KDA, typename InT>
 __global__ __launch_bounds__(kFT) void bwd_floor(Args a) {
     constexpr int CB = floor_cb<DK>(), CP = CB + 1, SP = kJB + 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bh = blockIdx.x / a.nch, ch = blockIdx.x - (blockIdx.x / a.nch) * a.nch;
-    const Ws W(a.B, a.T, a.H, DK, a.DV);
-    if (reinterpret_cast<const int*>(a.ws + W.fl)[static_cast<size_t>(bh) * a.nch + ch] == 0) return;
+    const int bh = blockIdx.x / a.nr, ch = a.c0 + static_cast<int>(blockIdx.x - bh * a.nr);
+    const Ws W(a.B, a.Tw, a.H, DK, a.DV);
+    if (reinterpret_cast<const int*>(a.ws + W.fl)[a.wc(bh, ch)] == 0) return;
     extern __shared__ float sm[];
     float* Mm = sm;                          // [64][kTP] beta dA (s < t)
     float* Nm = Mm + kC * kTP;               // [64][kTP] dP (s <= t)
@@ -1165,8 +1185,8 @@ __global__ __launch_bounds__(kFT) void bwd_floor(Args a) {
     const InT* k = static_cast<const InT*>(a.k);
     const InT* dO = static_cast<const InT*>(a.dO);
     auto tok = [&](int t) { return (static_cast<size_t>(b) * a.T + t0c + t) * a.H + h; };
-    const float* Sg = a.ws + W.ck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
-    const float* Dg = a.ws + W.dck + (static_cast<size_t>(bh) * a.nch + ch) * DK * a.DV;
+    const float* Sg = a.ws + W.ck + a.wc(bh, ch) * DK * a.DV;
+    const float* Dg = a.ws + W.dck + a.wc(bh, ch) * DK * a.DV;
     if (tid < kC) {
         Bs[tid] = tid < n ? a.beta[tok(tid)] : 0.f;
         dA[tid] = 0.f;
@@ -1176,10 +1196,10 @@ __global__ __launch_bounds__(kFT) void bwd_floor(Args a) {
             const int t = i / kJB, j = i - t * kJB;
             float u = 0.f, x = 0.f, o = 0.f;
             if (t < n) {
-                const size_t r = tok(t) * a.DV + jb + j;
+                const size_t r = a.wt(b, t0c + t, h) * a.DV + jb + j;  // workspace row
                 u = a.ws[W.u + r];
                 x = a.ws[W.dx + r];
-                o = ld(dO + r);
+                o = ld(dO + tok(t) * a.DV + jb + j);
             }
             Ust[t * SP + j] = u;
             Xst[t * SP + j] = x;
@@ -1375,7 +1395,7 @@ constexpr int local_lds() {
 }
 
 template <int DK, bool KDA, typename InT>
-hipError_t run(Args a, hipStream_t s) {
+hipError_t run(Args a, hipStream_t s, int rc) {
     static_assert(local_lds<DK, KDA>() <= 160 * 1024 && chain_lds<DK, kSl>() <= 160 * 1024 &&
                   prep_lds<DK, KDA>() <= 160 * 1024 && fwd_lds<DK, 64>() <= 160 * 1024 &&
                   dout_lds<DK>() <= 160 * 1024 && floor_lds<DK>() <= 160 * 1024, "LDS budget");
@@ -1388,12 +1408,10 @@ hipError_t run(Args a, hipStream_t s) {
     if (!grid_fits(static_cast<unsigned long long>(a.B) * a.H * a.nch, kNT) || !grid_fits(h8 * (a.DV / kSl), kNT))
         return hipErrorInvalidConfiguration;
     const unsigned heads8 = static_cast<unsigned>(h8);  // slice grids: whole groups of 8 heads
-    const unsigned per_chunk = static_cast<unsigned>(static_cast<unsigned long long>(a.B) * a.H * a.nch);
     // The checkpoint chain takes the widest slices (64, 32 or 16 columns)
     // that still put a workgroup on every CU; the reverse chain always takes
-    // 16 (at 16 it has
-    // the registers to load the next chunk's image during the current one,
-    // which costs less than the extra rounds of workgroups).
+    // 16 (at 16 it has the registers to load the next chunk's image during
+    // the current one, which costs less than the extra rounds of workgroups).
     const long long BH = static_cast<long long>(a.B) * a.H;
     const int FSF = a.DV >= 64 && BH * (a.DV / 64) >= 256 ? 64 : a.DV >= 32 && BH * (a.DV / 32) >= 256 ? 32 : 16;
     a.nsl_chain = a.DV / kSl;
@@ -1409,30 +1427,66 @@ hipError_t run(Args a, hipStream_t s) {
     if ((e = set(reinterpret_cast<const void*>(bwd_chain<DK, KDA, InT, kSl>), chain_lds<DK, kSl>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_local<DK, KDA, InT>), local_lds<DK, KDA>())) != hipSuccess) return e;
     if ((e = set(reinterpret_cast<const void*>(bwd_floor<DK, KDA, InT>), floor_lds<DK>())) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (prep_lds<DK, KDA>()), s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dout<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (dout_lds<DK>()), s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (FSF == 64)
-        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 64>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 64>()), s, a);
-    else if (FSF == 32)
-        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 32>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 32>()), s, a);
-    else
-        hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 16>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 16>()), s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chain<DK, KDA, InT, kSl>), dim3(chain_slices), dim3(kNT), (chain_lds<DK, kSl>()), s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_local<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (local_lds<DK, KDA>()), s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_floor<DK, KDA, InT>), dim3(per_chunk), dim3(kFT), (floor_lds<DK>()), s, a);
-    return hipGetLastError();
+    // the chunk-local forward work of a range (prep, and the checkpoint chain)
+    auto forward = [&](const Args& r) {
+        const unsigned per_chunk = static_cast<unsigned>(static_cast<unsigned long long>(r.B) * r.H * r.nr);
+        hipLaunchKernelGGL((bwd_prep<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (prep_lds<DK, KDA>()), s, r);
+        if (FSF == 64)
+            hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 64>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 64>()), s, r);
+        else if (FSF == 32)
+            hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 32>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 32>()), s, r);
+        else
+            hipLaunchKernelGGL((bwd_fwd<DK, KDA, InT, 16>), dim3(fwd_slices), dim3(kNT), (fwd_lds<DK, 16>()), s, r);
+        return hipGetLastError();
+    };
+    // the gradient work of a range whose forward work is in the workspace
+    auto reverse = [&](const Args& r) {
+        const unsigned per_chunk = static_cast<unsigned>(static_cast<unsigned long long>(r.B) * r.H * r.nr);
+        hipLaunchKernelGGL((bwd_dout<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (dout_lds<DK>()), s, r);
+        hipLaunchKernelGGL((bwd_chain<DK, KDA, InT, kSl>), dim3(chain_slices), dim3(kNT), (chain_lds<DK, kSl>()), s, r);
+        hipLaunchKernelGGL((bwd_local<DK, KDA, InT>), dim3(per_chunk), dim3(kNT), (local_lds<DK, KDA>()), s, r);
+        hipLaunchKernelGGL((bwd_floor<DK, KDA, InT>), dim3(per_chunk), dim3(kFT), (floor_lds<DK>()), s, r);
+        return hipGetLastError();
+    };
+    if (rc >= a.nch) {  // the whole sequence at once
+        a.c0 = 0; a.nr = a.nch; a.Tw = a.T;
+        a.s_in = a.s0; a.s_end = nullptr; a.ds_end = a.dsT; a.ds_start = a.ds0;
+        if ((e = forward(a)) != hipSuccess) return e;
+        return reverse(a);
+    }
+    // Ranges of rc chunks: the workspace holds one range.  A forward pass
+    // keeps only the state at each range start; the reverse pass then runs
+    // the ranges from the last, each from its start state (the last range's
+    // forward work is still in the workspace), carrying the state gradient
+    // from range to range.
+    const int R = (a.nch + rc - 1) / rc;
+    const size_t state = static_cast<size_t>(BH) * DK * a.DV;
+    float* starts = a.ws + Ws(a.B, rc * kC, a.H, DK, a.DV).total;  // R - 1 states: ranges 1 .. R-1
+    float* dcarry = starts + (R - 1) * state;                      // the state gradient between ranges
+    auto range = [&](int r) {
+        Args x = a;
+        x.c0 = r * rc; x.nr = std::min(rc, a.nch - x.c0); x.Tw = rc * kC;
+        x.s_in = r == 0 ? a.s0 : starts + (r - 1) * state;
+        x.s_end = r + 1 < R ? starts + r * state : nullptr;
+        x.ds_end = r + 1 == R ? a.dsT : dcarry;
+        x.ds_start = r == 0 ? a.ds0 : dcarry;
+        return x;
+    };
+    for (int r = 0; r < R; ++r)
+        if ((e = forward(range(r))) != hipSuccess) return e;
+    for (int r = R - 1; r >= 0; --r) {
+        const Args x = range(r);
+        if (r + 1 < R && (e = forward(x)) != hipSuccess) return e;
+        if ((e = reverse(x)) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int DK>
-hipError_t run_dk(int kda, int dtype, const Args& a, hipStream_t s) {
+hipError_t run_dk(int kda, int dtype, const Args& a, hipStream_t s, int rc) {
     if (dtype == GDR_DTYPE_BF16)
-        return kda ? run<DK, true, bf16_t>(a, s) : run<DK, false, bf16_t>(a, s);
-    return kda ? run<DK, true, float>(a, s) : run<DK, false, float>(a, s);
+        return kda ? run<DK, true, bf16_t>(a, s, rc) : run<DK, false, bf16_t>(a, s, rc);
+    return kda ? run<DK, true, float>(a, s, rc) : run<DK, false, float>(a, s, rc);
 }
 
 }  // namespace
@@ -1441,11 +1495,28 @@ size_t backward_workspace_floats(int B, int T, int H, int dk, int dv) {
     return Ws(B, T, H, dk, dv).total;
 }
 
+size_t backward_workspace_floats_ranged(int B, int T, int H, int dk, int dv, int rc) {
+    const int nch = (T + kC - 1) / kC;
+    if (rc >= nch) return Ws(B, T, H, dk, dv).total;
+    const size_t state = static_cast<size_t>(B) * H * dk * dv;
+    const int R = (nch + rc - 1) / rc;
+    return Ws(B, rc * kC, H, dk, dv).total + static_cast<size_t>(R) * state;  // R - 1 starts + the carry
+}
+
 hipError_t launch_backward(int kda, int dtype, int B, int T, int H, int dk, int dv, float scale,
                            const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* state_in, const void* d_o,
                            const float* d_state_out, void* dq, void* dkk, void* dvv, float* dalpha,
-                           float* dbeta, float* d_state_in, float* ws, hipStream_t s) {
+                           float* dbeta, float* d_state_in, float* ws, size_t ws_floats, hipStream_t s) {
+    // the widest chunk range the workspace holds (the whole sequence if it can)
+    const int nch = (T + kC - 1) / kC;
+    int rc = nch;
+    if (ws_floats < Ws(B, T, H, dk, dv).total) {
+        rc = 0;
+        for (int c = nch - 1; c >= 1 && rc == 0; --c)
+            if (backward_workspace_floats_ranged(B, T, H, dk, dv, c) <= ws_floats) rc = c;
+        if (rc == 0) return hipErrorInvalidValue;
+    }
     Args a;
     a.B = B; a.T = T; a.H = H; a.DV = dv; a.nch = (T + kC - 1) / kC;
     a.scale = scale;
@@ -1454,10 +1525,10 @@ hipError_t launch_backward(int kda, int dtype, int B, int T, int H, int dk, int 
     a.dq = dq; a.dk = dkk; a.dv = dvv; a.dalpha = dalpha; a.dbeta = dbeta; a.ds0 = d_state_in;
     a.ws = ws;
     switch (dk) {
-        case 16: return run_dk<16>(kda, dtype, a, s);
-        case 32: return run_dk<32>(kda, dtype, a, s);
-        case 64: return run_dk<64>(kda, dtype, a, s);
-        default: return run_dk<128>(kda, dtype, a, s);
+        case 16: return run_dk<16>(kda, dtype, a, s, rc);
+        case 32: return run_dk<32>(kda, dtype, a, s, rc);
+        case 64: return run_dk<64>(kda, dtype, a, s, rc);
+        default: return run_dk<128>(kda, dtype, a, s, rc);
     }
 }
 

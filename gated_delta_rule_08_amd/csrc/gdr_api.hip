@@ -386,6 +386,13 @@ size_t gdr_chunk_backward_workspace_bytes(int gate, int dtype, int B, int T, int
     return gdr::backward_workspace_floats(B, T, H, dk, dv) * sizeof(float);
 }
 
+size_t gdr_chunk_backward_workspace_bytes_ranged(int gate, int dtype, int B, int T, int H, int dk,
+                                                 int dv, int chunk, int range_chunks) {
+    if (range_chunks < 1) return 0;
+    if (gdr_chunk_backward_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk) == 0) return 0;
+    return gdr::backward_workspace_floats_ranged(B, T, H, dk, dv, range_chunks) * sizeof(float);
+}
+
 int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv, int chunk,
                        float scale, const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, const float* state_in,
@@ -399,7 +406,9 @@ int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv,
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64) return GDR_ERR_UNSUPPORTED;
     if (!sizes_ok(B, T, H, dk, dv)) return GDR_ERR_BAD_SHAPE;
     if (!backward_grid_ok(B, T, H, dv)) return GDR_ERR_BAD_SHAPE;
-    const size_t need = gdr_chunk_backward_workspace_bytes(gate, dtype, B, T, H, dk, dv, chunk);
+    // the smallest workspace: ranges of one chunk (the whole sequence runs at
+    // once from gdr_chunk_backward_workspace_bytes on)
+    const size_t need = gdr_chunk_backward_workspace_bytes_ranged(gate, dtype, B, T, H, dk, dv, chunk, 1);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDR_ERR_WORKSPACE;
     if (B == 0 || H == 0) return GDR_OK;
     const int kda = gate == GDR_GATE_KDA;
@@ -423,7 +432,8 @@ int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv,
     } else {
         e = gdr::launch_backward(kda, dtype, B, T, H, dk, dv, scale, q, k, v, alpha, beta, state_in,
                                  grad_o, grad_state_out, grad_q, grad_k, grad_v, grad_alpha,
-                                 grad_beta, grad_state_in, static_cast<float*>(workspace), s);
+                                 grad_beta, grad_state_in, static_cast<float*>(workspace),
+                                 workspace_bytes / sizeof(float), s);
     }
     return status_of(e);
 }

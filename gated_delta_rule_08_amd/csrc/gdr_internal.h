@@ -110,13 +110,18 @@ constexpr size_t kNoallocScratchBytes = size_t(96) << 20;
 hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 
 // Backward of the chunked recurrence (fp32 arithmetic; q, k, v, d_o, dq, dk,
-// dv in the element type `dtype`).  ws: backward_workspace_floats(...) floats.
+// dv in the element type `dtype`).  ws: ws_floats floats, at least
+// backward_workspace_floats_ranged(..., 1); with backward_workspace_floats(...)
+// the whole sequence runs at once, with less it runs in the widest chunk
+// ranges that fit (a forward pass for the range start states, then the
+// ranges from the last).
 size_t backward_workspace_floats(int B, int T, int H, int dk, int dv);
+size_t backward_workspace_floats_ranged(int B, int T, int H, int dk, int dv, int range_chunks);
 hipError_t launch_backward(int kda, int dtype, int B, int T, int H, int dk, int dv, float scale,
                            const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* state_in, const void* d_o,
                            const float* d_state_out, void* dq, void* dkk, void* dvv, float* dalpha,
-                           float* dbeta, float* d_state_in, float* ws, hipStream_t s);
+                           float* dbeta, float* d_state_in, float* ws, size_t ws_floats, hipStream_t s);
 
 // state_out <- state_in (or zeros when state_in is NULL), n floats.
 hipError_t launch_state_copy(const float* state_in, float* state_out, size_t n, hipStream_t s);

@@ -329,7 +329,10 @@ size_t gdr_chunk_prefill_varlen_workspace_bytes_ex(int gate, int dtype, int flag
  *   grad_alpha [B, T, H] (GDN) or [B, T, H, dk] (KDA) fp32
  *   grad_beta  [B, T, H] fp32
  *   grad_state_in [B, H, dk, dv] fp32, or NULL (not wanted)
- *   workspace  device scratch of at least gdr_chunk_backward_workspace_bytes
+ *   workspace  device scratch: gdr_chunk_backward_workspace_bytes runs the
+ *              sequence in one pass, down to
+ *              gdr_chunk_backward_workspace_bytes_ranged(..., 1) it runs in
+ *              chunk ranges (below); less is GDR_ERR_WORKSPACE
  *
  * Every product runs in fp32 (bf16 inputs are widened, bf16 gradients rounded
  * to nearest even).  The gate enters through log(alpha), floored at -40 per
@@ -352,10 +355,24 @@ int gdr_chunk_backward(int gate, int dtype, int B, int T, int H, int dk, int dv,
                        float* grad_alpha, float* grad_beta, float* grad_state_in,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace gdr_chunk_backward needs (0 when the arguments are
- * invalid). */
+/* Bytes of workspace with which gdr_chunk_backward runs the whole sequence
+ * at once (0 when the arguments are invalid). */
 size_t gdr_chunk_backward_workspace_bytes(int gate, int dtype, int B, int T, int H, int dk,
                                           int dv, int chunk);
+
+/* Bytes of workspace with which gdr_chunk_backward runs the sequence in
+ * ranges of range_chunks chunks of 64 tokens (0 when the arguments are
+ * invalid or range_chunks < 1; the whole-sequence size when range_chunks
+ * covers the sequence).  A range holds every head's chunk images, states and
+ * per-token terms of its chunks; the rest is one state per range start and
+ * one state gradient.  gdr_chunk_backward accepts any workspace of at least
+ * the one-chunk size: it takes the widest ranges that fit.  In ranges it
+ * runs a forward pass that keeps only each range's start state, then the
+ * ranges from the last, each from its start state (the chunk-local forward
+ * work of every range but the last runs twice); the gradients are bitwise
+ * the same as in one pass. */
+size_t gdr_chunk_backward_workspace_bytes_ranged(int gate, int dtype, int B, int T, int H, int dk,
+                                                 int dv, int chunk, int range_chunks);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* gdr_status_string(int status);

@@ -112,6 +112,9 @@ int main(void) {
                               p[11], (size_t)1 << 40, 0),
            GDR_ERR_BAD_SHAPE);
     if (gdr_chunk_backward_workspace_bytes(0, 1, INT_MAX, INT_MAX, 1, 128, 128, 64) != 0) ++failures;
+    if (gdr_chunk_backward_workspace_bytes_ranged(0, 1, INT_MAX, INT_MAX, 1, 128, 128, 64, 1) != 0)
+        ++failures;
+    if (gdr_chunk_backward_workspace_bytes_ranged(0, 1, 1, 130, 2, 64, 64, 64, 0) != 0) ++failures;
 
     /* valid calls on a host without a GPU: the runtime rejects them */
     EXPECT(gdr_decode_step(0, 1, 2, 3, 128, 128, 1.f, p[0], p[1], p[2], fa, fb, p[5], p[6], 0),
@@ -144,6 +147,13 @@ int main(void) {
         EXPECT(gdr_chunk_backward(1, 0, 1, 130, 2, 64, 64, 64, 1.f, p[0], p[1], p[2], fa, fb, 0,
                                   p[5], 0, p[6], p[7], p[8], (float*)p[9], (float*)p[10], 0,
                                   p[11], need, 0),
+               GDR_ERR_HIP);
+        /* the same in ranges of one chunk (the ranged host driver) */
+        const size_t one = gdr_chunk_backward_workspace_bytes_ranged(1, 0, 1, 130, 2, 64, 64, 64, 1);
+        if (!(one > 0 && one < need)) ++failures;
+        EXPECT(gdr_chunk_backward(1, 0, 1, 130, 2, 64, 64, 64, 1.f, p[0], p[1], p[2], fa, fb, 0,
+                                  p[5], 0, p[6], p[7], p[8], (float*)p[9], (float*)p[10], 0,
+                                  p[11], one, 0),
                GDR_ERR_HIP);
     }
     if (failures) {

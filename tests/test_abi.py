@@ -334,6 +334,22 @@ def test_backward_validation(lib):
     assert lib.gdr_chunk_backward_workspace_bytes(0, 1, 1, 64 * (1 << 22), 1, 128, 128, 64) == 0
     # the 16-column slice grids of the chains: 600,000 heads x 8 slices
     assert bwd(B=600000, T=64, H=1, ptrs=p, ws=ws, ws_bytes=1 << 62) == SHAPE
+    # a workspace below the one-pass size runs in chunk ranges: the smallest
+    # accepted is the one-chunk-range size
+    rng = lib.gdr_chunk_backward_workspace_bytes_ranged
+    rng.restype = ctypes.c_size_t
+    one = rng(0, 1, 2, 70, 3, 128, 128, 64, 1)
+    assert 0 < one < need
+    assert rng(0, 1, 2, 70, 3, 128, 128, 64, 2) == need      # two chunks: the whole sequence
+    assert rng(0, 1, 2, 70, 3, 128, 128, 64, 0) == 0         # invalid range
+    assert rng(0, 1, 2, 70, 3, 96, 128, 64, 1) == 0          # invalid arguments
+    assert bwd(ptrs=bad, ws=ws, ws_bytes=one) == MISAL        # accepted size, then pointer checks
+    assert bwd(ptrs=bad, ws=ws, ws_bytes=one - 4) == WS
+    T = 64 * 512
+    full = lib.gdr_chunk_backward_workspace_bytes(1, 1, 1, T, 32, 128, 128, 64)
+    r128 = rng(1, 1, 1, T, 32, 128, 128, 64, 128)
+    assert r128 < full and r128 <= 2 * 10 ** 9                 # the KDA workload in 2 GB
+    assert rng(0, 1, 4, 64 * 128, 32, 128, 128, 64, 32) <= 2 * 10 ** 9  # and the GDN one
 
 
 def test_decode_grid_limit(lib):

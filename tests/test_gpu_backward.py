@@ -37,7 +37,7 @@ def _case(gate, dtype, B, T, H, dk, dv, seed, s0=True, dst=True, alpha_mean=2.0)
     return inp, do, dst_arr
 
 
-def _run(gate, dtype, inp, do, dst, scale, want_ds0=True):
+def _run(gate, dtype, inp, do, dst, scale, want_ds0=True, ws_bytes=None):
     d = {key: to_dev(val, dtype if key in ("q", "k", "v") else "f32") for key, val in inp.items()}
     g_o = to_dev(do, dtype)
     g_st = None if dst is None else to_dev(dst, "f32")
@@ -47,9 +47,12 @@ def _run(gate, dtype, inp, do, dst, scale, want_ds0=True):
     B, T, H, dk = inp["q"].shape
     dv = inp["v"].shape[-1]
     out["ds0"] = torch.full((B, H, dk, dv), 7.0, device="cuda") if want_ds0 else None
+    # an explicit workspace of ws_bytes (a ranged one below the one-pass size),
+    # filled with garbage first
+    ws = None if ws_bytes is None else torch.full((ws_bytes // 4,), float("nan"), device="cuda")
     gdr.gdr_chunk_backward(gate, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["s0"], g_o, g_st,
                            out["dq"], out["dk"], out["dv"], out["dalpha"], out["dbeta"], out["ds0"],
-                           scale=scale)
+                           scale=scale, workspace=ws)
     torch.cuda.synchronize()
     return {key: (None if val is None else to_host64(val)) for key, val in out.items()}
 
@@ -282,3 +285,56 @@ def test_backward_graph_replays_match_eager(gate):
         junk = torch.randn(4096, device="cuda").sum()  # unrelated eager work between replays
         torch.cuda.synchronize()
         del junk
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_ranges_bitwise(gate, dtype):
+    """A workspace below the one-pass size runs the sequence in chunk ranges
+    (a forward pass for each range's start state, then the ranges from the
+    last): every gradient is bitwise the one-pass result, for ranges of 1, 2
+    and 3 chunks over a ragged 5-chunk sequence with a zero gate, with and
+    without S0 and dS_T."""
+    B, T, H, dk, dv = 2, 300, 3, 64, 32
+    inp, do, dst = _case(gate, dtype, B, T, H, dk, dv, seed=31)
+    inp["alpha"][:, 150] = 0.0
+    announce("backward %s %s ranges" % (gate, dtype))
+    ref = _run(gate, dtype, inp, do, dst, 0.9)
+    full = gdr.gdr_chunk_backward_workspace_bytes(gate, torch.float32 if dtype == "f32" else torch.bfloat16,
+                                                  B, T, H, dk, dv)
+    for rc in (1, 2, 3):
+        need = gdr.gdr_chunk_backward_workspace_bytes_ranged(
+            gate, torch.float32 if dtype == "f32" else torch.bfloat16, B, T, H, dk, dv, rc)
+        assert 0 < need < full
+        got = _run(gate, dtype, inp, do, dst, 0.9, ws_bytes=need)
+        for key in ref:
+            assert np.array_equal(got[key], ref[key]), (rc, key)
+    inp0, do0, _ = _case(gate, dtype, B, T, H, dk, dv, seed=32, s0=False, dst=False)
+    ref0 = _run(gate, dtype, inp0, do0, None, 0.9, want_ds0=False)
+    need = gdr.gdr_chunk_backward_workspace_bytes_ranged(
+        gate, torch.float32 if dtype == "f32" else torch.bfloat16, B, T, H, dk, dv, 2)
+    got0 = _run(gate, dtype, inp0, do0, None, 0.9, want_ds0=False, ws_bytes=need)
+    for key in ref0:
+        if ref0[key] is not None:
+            assert np.array_equal(got0[key], ref0[key]), key
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_backward_ranges_full_size(gate):
+    """At the prefill workload's shape, a workspace of at most 2 GB (GDN: 32
+    chunks per range, KDA: 128) gives the one-pass gradients bitwise, every
+    head and token."""
+    name = "gdn_prefill_b4_t8192_h32_d128" if gate == "gdn" else "kda_prefill_b1_t32768_h32_d128"
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    rng = np.random.default_rng(77)
+    do = synth.bf16_round(rng.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32))
+    dst = (0.1 * rng.standard_normal((w.B, w.H, w.dk, w.dv))).astype(np.float32)
+    rc = 32 if gate == "gdn" else 128
+    need = gdr.gdr_chunk_backward_workspace_bytes_ranged(gate, torch.bfloat16, w.B, w.T, w.H, w.dk, w.dv, rc)
+    assert need <= 2 * 10 ** 9
+    announce("backward %s full size, ranged workspace %.2f GB" % (gate, need / 1e9))
+    ref = _run(gate, "bf16", inp, do, dst, 1.0)
+    got = _run(gate, "bf16", inp, do, dst, 1.0, ws_bytes=need)
+    for key in ref:
+        assert np.array_equal(got[key], ref[key]), key
