@@ -866,32 +866,23 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     };
 
     // A, P and the diagonal-block inverses of chunk c (buffer c & 1).  The
-    // tile products run transposed, C^T = Kr M^T, so a lane ends up with 4
-    // consecutive j of one row t and stores 8 bytes.  Tiles per wave (row
-    // tile rt of M = Khat for A, Qhat for P; column tiles ct <= rt of Kr):
-    //   wave 0: A rows 3 and 0;  wave 1: P rows 3 and 0;
-    //   wave 2: A rows 2 and 1;  wave 3: P rows 2 and 1     (5 tiles each),
-    // so each K step loads the Kr fragments once for both rows.  Waves 0 and
-    // 2 hold the diagonal A tiles and invert them, two blocks per wave.
+    // tile products run transposed, C^T = Kr M^T (M = Khat rows for A, Qhat
+    // rows for P, Kr the right rows), so a lane ends up with 4 consecutive j
+    // of one row t and stores 8 bytes.  Waves 0 and 2 hold the diagonal A
+    // tiles of blocks 3, 0 and 2, 1 and invert them; the tile lists per wave
+    // are below.
     auto prep_ap = [&](int c) {
         const bf16_t* Kh = prep_lds_b(c, L::oKh, L::pKh);
         const bf16_t* Qh = prep_lds_b(c, L::oQh, L::pQh);
-        // right factor (j side); KDA: the right rows of the row block's set
-        const bf16_t* Kr = Kh;
-        const bf16_t* KrB = Kh;
-        if constexpr (KDA) {
-            Kr = Kc + rr_row0(wave < 2 ? 3 : 2) * L::PK;
-            KrB = Kc + rr_row0(wave < 2 ? 0 : 1) * L::PK;
-        }
+        const bf16_t* Kr = Kh;  // right factor (j side) of the fused GDN products
         const float* sb = reinterpret_cast<const float*>(prep_lds_b(c, L::oBeta, L::pBeta));
         bf16_t* Pt = prep_out_b(c, L::oP);
         // kPrep keeps -A and D_r^{-1} in LDS: the image gets (I + A)^{-1} instead
         bf16_t* At = MODE == kPrep ? reinterpret_cast<bf16_t*>(smem + L::pA) : prep_out_b(c, L::oA);
         bf16_t* Dt = MODE == kPrep ? reinterpret_cast<bf16_t*>(smem + L::pD) : prep_out_b(c, L::oD);
         const bool isP = wave & 1;
-        const int rA = wave < 2 ? 3 : 2;  // first row tile: ct = 0..rA
-        const int rB = wave < 2 ? 0 : 1;  // second row tile: ct = 0..rB
-        const bf16_t* M = isP ? Qh : Kh;
+        const int rA = wave < 2 ? 3 : 2;  // diagonal blocks inverted by waves 0 and 2
+        const int rB = wave < 2 ? 0 : 1;
         if constexpr (ONEBAR) {
             // GDN fused: per-wave tile lists.  Waves 0 and 2 also invert the
             // diagonal blocks (3, 0) and (2, 1), so they form only those A
@@ -1005,72 +996,111 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             else if (wave == 2) run(Tiles<tA(2, 2), tA(1, 1), tA(2, 1)>{});
             else run(Tiles<tP(2, 0), tP(2, 1), tP(2, 2), tP(1, 0), tP(1, 1), tA(2, 0), tA(1, 0)>{});
         } else {
-        // scalars of the epilogues, read before the products
-        const float btA = sb[16 * rA + lr], btB = sb[16 * rB + lr];
-        float gtA = 0.f, gtB = 0.f;
-        float4 gj4[4];
-        if constexpr (!KDA) {
+            // Per-wave tile lists (code = 16 isP + 4 row + column): waves 0
+            // and 2 form only the diagonal A tiles of the blocks they invert
+            // (3, 0 and 2, 1), waves 1 and 3 the other 16 tiles, so that the
+            // inversions run beside the larger share of the products.  Each
+            // wave loads every right-hand fragment (KDA: from the row block's
+            // own set of right rows) and left-hand fragment it needs once per
+            // K step.
             const float* sG = sGp(c);
-            gtA = sG[16 * rA + lr];
-            gtB = sG[16 * rB + lr];
+            auto run = [&](auto tag) {
+                using TL = decltype(tag);
+                constexpr int NT = TL::n;
+                auto uses_rc = [&](int rr, int cc) {  // right fragment: row block rr's set (KDA), column tile cc
+                    bool u = false;
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) gj4[ct] = *reinterpret_cast<const float4*>(sG + 16 * ct + 4 * lg);
-        }
-        f32x4 accA[4] = {zero4(), zero4(), zero4(), zero4()};
-        f32x4 accB[2] = {zero4(), zero4()};
-        // KDA rows sit under the unit map (kpos); rA0 / rB0: first absolute
-        // right row of the row blocks' sets
-        const int rA0 = KDA ? rr_row0(rA) : 0, rB0 = KDA ? rr_row0(rB) : 0;
+                    for (int x = 0; x < NT; ++x) {
+                        const int cd = TL::code[x], r = (cd >> 2) & 3, cl = cd & 3;
+                        u |= cl == cc && (!KDA || r == rr);
+                    }
+                    return u;
+                };
+                auto uses_row = [&](int rr, int what) {  // what: 0 any tile, 1 A tile
+                    bool u = false;
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            bf16x8 kr[4], krb[2];
+                    for (int x = 0; x < NT; ++x) {
+                        const int cd = TL::code[x], r = (cd >> 2) & 3;
+                        u |= r == rr && (what == 0 || cd < 16);
+                    }
+                    return u;
+                };
+                auto uses_m = [&](int key) {  // key = 4 isP + row
+                    bool u = false;
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                if (ct <= rA) kr[ct] = lds8(Kr + (16 * ct + lr) * L::PK + kpos(rA0 + 16 * ct + lr, 32 * s + 8 * lg));
+                    for (int x = 0; x < NT; ++x) u |= (TL::code[x] >> 2) == key;
+                    return u;
+                };
+                // epilogue scalars, read before the products
+                float bt[4], gt[4];
+                float4 gj[4];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-                if (ct <= rB)
-                    krb[ct] = KDA ? lds8(KrB + (16 * ct + lr) * L::PK + kpos(rB0 + 16 * ct + lr, 32 * s + 8 * lg))
-                                  : kr[ct];
-            const bf16x8 mA = lds8(M + (16 * rA + lr) * L::PK + kpos(16 * rA + lr, 32 * s + 8 * lg));
-            const bf16x8 mB = lds8(M + (16 * rB + lr) * L::PK + kpos(16 * rB + lr, 32 * s + 8 * lg));
+                for (int r = 0; r < 4; ++r) {
+                    if (uses_row(r, 1)) bt[r] = sb[16 * r + lr];
+                    if (!KDA && uses_row(r, 0)) gt[r] = sG[16 * r + lr];
+                }
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                if (ct <= rA) accA[ct] = mfma32(kr[ct], mA, accA[ct]);
+                for (int cc = 0; cc < 4; ++cc)
+                    if (!KDA && uses_rc(0, cc)) gj[cc] = *reinterpret_cast<const float4*>(sG + 16 * cc + 4 * lg);
+                f32x4 acc[NT];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-                if (ct <= rB) accB[ct] = mfma32(krb[ct], mB, accB[ct]);
-        }
-        auto epilogue = [&](int rt, int ct, const f32x4& acc, float bt, float gt) {
-            const int t = 16 * rt + lr;
-            float gj[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (!KDA) {
-                gj[0] = gj4[ct].x; gj[1] = gj4[ct].y; gj[2] = gj4[ct].z; gj[3] = gj4[ct].w;
-            }
-            f32x4 val;
+                for (int x = 0; x < NT; ++x) acc[x] = zero4();
+                constexpr int NR = KDA ? 4 : 1;  // right-row sets
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 16 * ct + 4 * lg + i;
-                float x = acc[i];
-                if constexpr (!KDA) x *= ex2(fminf(gt - gj[i], 0.f));
-                val[i] = isP ? (j <= t ? x : 0.f) : (j < t ? bt * x : 0.f);
-            }
-            if (isP) {
-                st4(Pt + ptile(rt, ct) * 16 * L::PD + lr * L::PD + 4 * lg, val);
-            } else if (ct < rt) {
-                st4(At + atile(rt, ct) * 16 * L::PD + lr * L::PD + 4 * lg, -val);
-            } else {  // diagonal tile, stored transposed: scr[j][t] = A[t][j]
-                float* scr = scr0 + rt * 16 * L::PS;
+                for (int s = 0; s < NKS; ++s) {
+                    bf16x8 kr[NR][4], mf[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) scr[(4 * lg + i) * L::PS + lr] = val[i];
-            }
-        };
+                    for (int rr = 0; rr < NR; ++rr)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-            if (ct <= rA) epilogue(rA, ct, accA[ct], btA, gtA);
+                        for (int cc = 0; cc < 4; ++cc)
+                            if (uses_rc(rr, cc)) {
+                                const int row = (KDA ? rr_row0(rr) : 0) + 16 * cc + lr;  // row of Kc (KDA) / Khat
+                                kr[rr][cc] = lds8((KDA ? Kc : Kh) + row * L::PK + kpos(row, 32 * s + 8 * lg));
+                            }
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-            if (ct <= rB) epilogue(rB, ct, accB[ct], btB, gtB);
+                    for (int key = 0; key < 8; ++key)
+                        if (uses_m(key)) {
+                            const int row = 16 * (key & 3) + lr;
+                            mf[key] = lds8((key >= 4 ? Qh : Kh) + row * L::PK + kpos(row, 32 * s + 8 * lg));
+                        }
+#pragma unroll
+                    for (int x = 0; x < NT; ++x) {
+                        const int cd = TL::code[x];
+                        acc[x] = mfma32(kr[KDA ? (cd >> 2) & 3 : 0][cd & 3], mf[cd >> 2], acc[x]);
+                    }
+                }
+#pragma unroll
+                for (int x = 0; x < NT; ++x) {
+                    const int cd = TL::code[x], tP_ = cd >> 4, r = (cd >> 2) & 3, cl = cd & 3;
+                    const int t = 16 * r + lr;
+                    float gv[4] = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (!KDA) {
+                        gv[0] = gj[cl].x; gv[1] = gj[cl].y; gv[2] = gj[cl].z; gv[3] = gj[cl].w;
+                    }
+                    f32x4 val;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = 16 * cl + 4 * lg + i;
+                        float xx = acc[x][i];
+                        if constexpr (!KDA) xx *= ex2(fminf(gt[r] - gv[i], 0.f));
+                        val[i] = tP_ ? (j <= t ? xx : 0.f) : (j < t ? bt[r] * xx : 0.f);
+                    }
+                    if (tP_) {
+                        st4(Pt + ptile(r, cl) * 16 * L::PD + lr * L::PD + 4 * lg, val);
+                    } else if (cl < r) {
+                        st4(At + atile(r, cl) * 16 * L::PD + lr * L::PD + 4 * lg, -val);
+                    } else {  // diagonal tile, stored transposed: scr[j][t] = A[t][j]
+                        float* scr = scr0 + r * 16 * L::PS;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) scr[(4 * lg + i) * L::PS + lr] = val[i];
+                    }
+                }
+            };
+            if (wave == 0) run(Tiles<tA(3, 3), tA(0, 0)>{});
+            else if (wave == 2) run(Tiles<tA(2, 2), tA(1, 1)>{});
+            else if (wave == 1)
+                run(Tiles<tP(3, 0), tP(3, 1), tP(3, 2), tP(3, 3), tP(0, 0), tA(3, 0), tA(3, 1), tA(3, 2)>{});
+            else run(Tiles<tP(2, 0), tP(2, 1), tP(2, 2), tP(1, 0), tP(1, 1), tA(2, 0), tA(2, 1), tA(1, 0)>{});
         }
         // D_r^{-1} = (I + A_rr)^{-1}: lanes 0..15 invert block rA, lanes 16..31
         // block rB; lane c solves column c by right-looking forward
@@ -1112,12 +1142,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
     };
 
     // kPrep: the 16x16 blocks of T = (I + A)^{-1} from -A and the D_r^{-1}
-    // (one wave, after the barrier that follows prep_ap):
+    // (after the barrier that follows prep_ap):
     //   T_rr = D_r^{-1},  T_rk = D_r^{-1} sum_{k<=m<r} (-A_rm) T_mk.
+    // Each column k of blocks depends only on its own blocks above, so the
+    // columns are independent chains: part 0 forms column 0 (T_10, T_20,
+    // T_30), part 1 columns 1 and 2 (T_21, T_31, T_32) and copies the T_rr.
     // Z = sum_m (-A_rm) T_mk is formed in the accumulator layout, which is
     // the A-operand layout of Z^T, so the second product gives (D_r^{-1} Z)^T,
     // whose accumulator layout is the row-fragment layout the chain reads.
-    auto prep_t = [&](int c) {
+    auto prep_t = [&](int c, int part) {
         const bf16_t* Ab = reinterpret_cast<const bf16_t*>(smem + L::pA);
         const bf16_t* Dl = reinterpret_cast<const bf16_t*>(smem + L::pD);
         bf16_t* Tl = reinterpret_cast<bf16_t*>(smem + L::pT);
@@ -1129,15 +1162,18 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             const bf16_t* p = t + (4 * lg + (lr >> 2)) * L::PD + 4 * (lr & 3);
             return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
         };
+        if (part == 1) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<uint2*>(Di + r * 16 * L::PD + lr * L::PD + 4 * lg) =
-                *reinterpret_cast<const uint2*>(Dl + r * 16 * L::PD + lr * L::PD + 4 * lg);
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<uint2*>(Di + r * 16 * L::PD + lr * L::PD + 4 * lg) =
+                    *reinterpret_cast<const uint2*>(Dl + r * 16 * L::PD + lr * L::PD + 4 * lg);
+        }
 #pragma unroll
         for (int r = 1; r < 4; ++r) {
             const bf16x4 dr = row_frag(Dl + r * 16 * L::PD);
 #pragma unroll
             for (int kk = 0; kk < r; ++kk) {
+                if ((kk == 0) != (part == 0)) continue;
                 f32x4 z = zero4();
 #pragma unroll
                 for (int m = kk; m < r; ++m) {
@@ -1488,9 +1524,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
         // chunk c+1 are loaded into registers while chunk c is gated and
         // multiplied, and the outputs go straight to the image.  prep_t of
         // chunk c only touches its own LDS tiles, which the next chunk's
-        // products overwrite after the next barrier.  It runs on wave 1,
-        // which forms P tiles only (waves 0 and 2 also invert the diagonal
-        // blocks), so the waves reach the next barrier together.
+        // products overwrite after the next barrier.  It runs on waves 1 and
+        // 3 (one column chain each side), which invert nothing.
         PrepIn pin;
         // (a packed sequence may end before this workgroup's chunks begin)
         if (pc < pc_end) prep_load(pc, pin);
@@ -1501,7 +1536,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             lds_barrier();
             prep_ap(c);
             lds_barrier();
-            if (wave == 1) prep_t(c);
+            if (wave & 1) prep_t(c, wave >> 1);
         }
     } else if constexpr (MODE == kChain) {
         if (wave < kLoad) {
