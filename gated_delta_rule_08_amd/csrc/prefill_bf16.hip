@@ -630,9 +630,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             }
         }
         if (KDA && !gater) return;
-        // a full chunk (every chunk but a ragged last one) needs no row masks
-        auto body = [&](auto full_tag) {
+        // a full chunk (every chunk but a ragged last one) needs no row masks;
+        // KDA full chunks without the norm prologue skip the unit factors
+        auto body = [&](auto full_tag, auto nrm_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
+            constexpr bool NRM = decltype(nrm_tag)::value;  // false: nk = nq = 1
             bool valid[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) valid[u] = FULL || 4 * tg + u < n;
@@ -692,8 +694,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         run[e] = u == 0 ? ga[e] : run[e] * ga[8 * u + e];  // 2^(G_t - X)
-                        const float kp = bf_at(kz[u], e) * nk[u] * run[e];
-                        const float qp = bf_at(qz[u], e) * nq[u] * run[e];
+                        const float kp = bf_at(kz[u], e) * (NRM ? nk[u] : 1.f) * run[e];
+                        const float qp = bf_at(qz[u], e) * (NRM ? nq[u] : 1.f) * run[e];
                         kh[e] = static_cast<__bf16>(kp * cK[e]);
                         qh[e] = static_cast<__bf16>(qp * cK[e]);
                         dl[e] = static_cast<__bf16>(kp * cD[e]);
@@ -716,7 +718,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             if (r == 0) rev[e] = u == 3 ? 1.f : rev[e] * ga[8 * (u + 1) + e];  // 2^(inc - G_t)
-                            const float ks = bf_at(kz[u], e) * nk[u] * rev[e];
+                            const float ks = bf_at(kz[u], e) * (NRM ? nk[u] : 1.f) * rev[e];
                             if (r == 0) {
                                 const uint32_t kt = bf_bits(ks * cT[e]);
                                 if (u & 1) ktw[e][u >> 1] = kt << 16;
@@ -861,8 +863,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<NSW, KDA, MODE>(), waves_per_s
             }
     
         };
-        if (n == kC) body(std::true_type{});
-        else body(std::false_type{});
+        if (n != kC) body(std::false_type{}, std::true_type{});
+        else if (!KDA || nrm) body(std::true_type{}, std::true_type{});
+        else body(std::true_type{}, std::false_type{});
     };
 
     // A, P and the diagonal-block inverses of chunk c (buffer c & 1).  The
