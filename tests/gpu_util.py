@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import gated_delta_rule_08_amd as gdr
+from oracle_pool import rel_err
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
@@ -35,18 +36,6 @@ def to_dev(x, dtype: str, dev="cuda"):
 
 def to_host64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
-
-
-def rel_err(got, ref) -> float:
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    if ref.size == 0:
-        return 0.0
-    denom = float(np.abs(ref).max())
-    err = float(np.abs(got - ref).max())
-    if not np.isfinite(err):
-        return float("inf")
-    return err / denom if denom > 0 else err
 
 
 def assert_close(got, ref, tol, what=""):
