@@ -217,18 +217,15 @@ def test_backward_zero_beta_and_single_token(gate):
 def test_backward_many_heads_wide_slices(gate, dk, dv):
     """Enough heads that the forward chain takes wide slices (32 columns for
     dv = 32, 64 for dv = 64; one workgroup per CU still); the oracle on
-    sampled heads."""
+    every head."""
     inp, do, dst = _case(gate, "f32", B=8, T=70, H=32, dk=dk, dv=dv, seed=15)
     announce("backward %s wide slices B=8 H=32 dk=%d dv=%d" % (gate, dk, dv))
     got = _run(gate, "f32", inp, do, dst, 1.0)
-    for (b, h) in [(0, 0), (5, 17), (7, 31)]:
-        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
-        ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]), sl(inp["beta"]),
-                              np.ascontiguousarray(inp["s0"][b:b + 1, h:h + 1]), sl(do),
-                              np.ascontiguousarray(dst[b:b + 1, h:h + 1]))
-        for key in ("dq", "dk", "dv", "dalpha", "dbeta"):
-            assert_close(got[key][b:b + 1, :, h:h + 1], ref[key], TOL["f32"], "%s[%d,%d]" % (key, b, h))
-        assert_close(got["ds0"][b:b + 1, h:h + 1], ref["ds0"], TOL["f32"], "ds0[%d,%d]" % (b, h))
+    errs = backward_errors_every_head(inp, do, dst, got)
+    assert len(errs) == 8 * 32
+    for (b, h), e in sorted(errs.items()):
+        for key, val in e.items():
+            assert val <= TOL["f32"], "%s[%d,%d]: max|err| / max|ref| = %.3e > %.1e" % (key, b, h, val, TOL["f32"])
 
 
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
